@@ -1,0 +1,139 @@
+"""fp64 CPU oracle for the selective scan (TEST INFRASTRUCTURE).
+
+Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of bench.py may
+import this package.  The product path (the HIP library and its Python
+binding) never does, and the two share no code: the oracle is the plain C file
+ssm_oracle.c next to this file, compiled with gcc, wrapped here with ctypes.
+
+Functions take numpy arrays of any float dtype (bf16 values arrive widened to
+fp32 by the caller) and compute in fp64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssm_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ssm_oracle.c into liboracle.so (gcc -O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.oracle_selective_scan_f64.restype = ctypes.c_int
+        lib.oracle_selective_scan_f64.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, P, P,
+                                                  ctypes.c_int, P, P, P, ctypes.c_int]
+        lib.oracle_state_update_f64.restype = ctypes.c_int
+        lib.oracle_state_update_f64.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, P,
+                                                ctypes.c_int, P, ctypes.c_int]
+        lib.oracle_softplus.restype = ctypes.c_double
+        lib.oracle_softplus.argtypes = [ctypes.c_double]
+        lib.oracle_silu.restype = ctypes.c_double
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        _lib = lib
+    return _lib
+
+
+class use_library:
+    """Context manager: run the oracle functions against another build of
+    ssm_oracle.c (used by the test that plants mistakes in the oracle)."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = _load()
+        _lib = None
+        lib = ctypes.CDLL(self.path)
+        for name in ("oracle_selective_scan_f64", "oracle_state_update_f64", "oracle_softplus",
+                     "oracle_silu"):
+            src = getattr(self.saved, name)
+            dst = getattr(lib, name)
+            dst.restype, dst.argtypes = src.restype, src.argtypes
+        _lib = lib
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def _f64(x):
+    if x is None:
+        return None
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def softplus(x: float) -> float:
+    return _load().oracle_softplus(float(x))
+
+
+def silu(x: float) -> float:
+    return _load().oracle_silu(float(x))
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                   h0=None, return_last_state=False, nthreads=0):
+    """out[b,d,t] (and last_state[b,d,n]) in fp64.
+
+    u, delta, z: (batch, dim, L); B, C: (batch, N, L); A: (dim, N);
+    D, delta_bias: (dim,); h0: (batch, dim, N)."""
+    lib = _load()
+    u, delta, z, B, C, A, D, delta_bias, h0 = map(_f64, (u, delta, z, B, C, A, D, delta_bias, h0))
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    assert N <= 1024
+    assert delta.shape == u.shape and (z is None or z.shape == u.shape)
+    assert B.shape == (batch, N, L) and C.shape == (batch, N, L) and A.shape == (dim, N)
+    out = np.empty_like(u)
+    last = np.empty((batch, dim, N)) if return_last_state else None
+    used = lib.oracle_selective_scan_f64(batch, dim, L, N, _ptr(u), _ptr(delta), _ptr(z),
+                                         _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(delta_bias),
+                                         int(bool(delta_softplus)), _ptr(h0), _ptr(out),
+                                         _ptr(last), int(nthreads))
+    selective_scan.last_threads = used
+    return (out, last) if return_last_state else out
+
+
+def state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True,
+                 nthreads=0):
+    """One decode token.  Returns (out (batch, dim), new_state (batch, dim, N));
+    the input state is not modified."""
+    lib = _load()
+    s = np.array(state, dtype=np.float64, copy=True, order="C")
+    x, dt, z, B, C, A, D, dt_bias = map(_f64, (x, dt, z, B, C, A, D, dt_bias))
+    batch, dim, N = s.shape
+    assert x.shape == (batch, dim) and dt.shape == (batch, dim)
+    assert B.shape == (batch, N) and C.shape == (batch, N) and A.shape == (dim, N)
+    out = np.empty((batch, dim))
+    used = lib.oracle_state_update_f64(batch, dim, N, _ptr(s), _ptr(x), _ptr(dt), _ptr(z),
+                                       _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(dt_bias),
+                                       int(bool(dt_softplus)), _ptr(out), int(nthreads))
+    state_update.last_threads = used
+    return out, s

@@ -1,0 +1,172 @@
+/*
+ * ssm_oracle.c -- plain fp64 CPU oracle for the Mamba-1 selective scan and its
+ * single-token state update.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this library.  The GPU product path
+ * never calls it, and it shares no code, header or constant with the HIP
+ * sources.
+ *
+ * What it computes (sources are the five pages on Mamba; cited by page title
+ * and section):
+ *   - "Mamba模型笔记" (Mamba model notes), section 2.2: discrete SSM
+ *     h_t = Abar h_{t-1} + Bbar x_t,  y_t = C h_t + D x_t.
+ *   - same page, section 4.4: one independent SSM per channel, so the state
+ *     of channel d is a vector over the state index n and A is diagonal per
+ *     channel (A[d,n]); exp is elementwise.
+ *   - same page, section 4.1: B, C and the step size Delta depend on the
+ *     input token; here they are given per (batch, n, t) and per (batch, d, t).
+ *   - Mamba paper notes (0539edu.com), section 2.3: zero-order-hold
+ *     discretisation as used in practice: Abar = exp(Delta*A), Bbar = Delta*B,
+ *     Cbar = C, with Delta kept positive by a softplus.
+ *   - Mamba training/inference guide (zhouruolin.cn), FAQ item 2: the
+ *     projection bias places Delta in a target range -> Delta =
+ *     softplus(dt + bias[d]).
+ *   - Mamba model notes, section 4.3: the gate branch multiplies the SSM
+ *     output; gate = silu(z) applied after the D skip term.
+ *   - Mamba paper notes, section 4.3: recurrent inference keeps only a
+ *     fixed-size state per (batch, channel) and updates it once per token
+ *     (the decode form below).
+ *   - Mamba paper notes, section 5.5: the state starts at zero.
+ *
+ * Readings where the pages are silent (listed in the design notes too):
+ *   softplus is exact (max(x,0) + log1p(exp(-|x|))), no threshold; the
+ *   initial state is h0 when given, else zero; out = (sum_n C h + D u) * silu(z).
+ *
+ * Parity pins live in tests/test_oracle_pins.py (LTI convolution, Delta -> 0,
+ * L = 1 closed form, split sequence, decode == scan, reset, A = 0 prefix sum,
+ * linearity, unrolled-sum brute force in fp64 and 40-digit decimal).
+ *
+ * Layouts (all contiguous, row-major):
+ *   u, delta, z, out : (batch, dim, seqlen)
+ *   Bm, Cm           : (batch, dstate, seqlen)
+ *   A                : (dim, dstate)
+ *   Dv, bias         : (dim)
+ *   h0, last_state   : (batch, dim, dstate)
+ * Decode: state (batch, dim, dstate); x, dt, z, out (batch, dim);
+ *         Bm, Cm (batch, dstate).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+double oracle_softplus(double x) {
+  /* log(1 + e^x) written so that neither branch overflows or cancels */
+  return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));
+}
+
+double oracle_silu(double z) { return z / (1.0 + exp(-z)); }
+
+static double step_size(double dt, const double* bias, int64_t d, int softplus) {
+  double x = dt + (bias ? bias[d] : 0.0);
+  return softplus ? oracle_softplus(x) : x;
+}
+
+/* One (batch, channel) row of the prefill scan, strictly sequential in t. */
+static void scan_row(int64_t b, int64_t d, int64_t dim, int64_t L, int64_t N,
+                     const double* u, const double* delta, const double* z,
+                     const double* Bm, const double* Cm, const double* A,
+                     const double* Dv, const double* bias, int softplus,
+                     const double* h0, double* out, double* last_state, double* h) {
+  const int64_t row = (b * dim + d) * L;
+  const double* Bb = Bm + b * N * L;
+  const double* Cb = Cm + b * N * L;
+  for (int64_t n = 0; n < N; ++n) h[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    const double ut = u[row + t];
+    const double dl = step_size(delta[row + t], bias, d, softplus);
+    double y = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      const double abar = exp(dl * A[d * N + n]);      /* Abar = exp(Delta*A)   */
+      const double bbar_u = dl * Bb[n * L + t] * ut;    /* Bbar*u = Delta*B*u    */
+      h[n] = abar * h[n] + bbar_u;
+      y += Cb[n * L + t] * h[n];                        /* C_t . h_t             */
+    }
+    if (Dv) y += Dv[d] * ut;                            /* skip term D*u         */
+    if (z) y *= oracle_silu(z[row + t]);                /* gate, after the skip  */
+    out[row + t] = y;
+  }
+  if (last_state)
+    for (int64_t n = 0; n < N; ++n) last_state[(b * dim + d) * N + n] = h[n];
+}
+
+/* Prefill: runs every (batch, channel) row; rows are independent, so they are
+ * spread over OpenMP threads (nthreads <= 0 means the runtime default). The
+ * recurrence over t inside a row stays sequential. Returns the thread count. */
+int oracle_selective_scan_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
+                              const double* u, const double* delta, const double* z,
+                              const double* Bm, const double* Cm, const double* A,
+                              const double* Dv, const double* bias, int softplus,
+                              const double* h0, double* out, double* last_state,
+                              int nthreads) {
+  int used = 1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+  {
+#pragma omp single
+    used = omp_get_num_threads();
+    double h[1024];
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < batch * dim; ++r)
+      scan_row(r / dim, r % dim, dim, seqlen, dstate, u, delta, z, Bm, Cm, A, Dv, bias,
+               softplus, h0, out, last_state, h);
+  }
+#else
+  (void)nthreads;
+  double h[1024];
+  for (int64_t r = 0; r < batch * dim; ++r)
+    scan_row(r / dim, r % dim, dim, seqlen, dstate, u, delta, z, Bm, Cm, A, Dv, bias,
+             softplus, h0, out, last_state, h);
+#endif
+  return used;
+}
+
+/* Decode: one token per (batch, channel); state updated in place.  Written as
+ * its own loop body (not a call into scan_row) so that "decode equals scan" is
+ * a real check between two pieces of code. */
+static void update_row(int64_t r, int64_t dim, int64_t N, double* state,
+                       const double* x, const double* dt, const double* z,
+                       const double* Bm, const double* Cm, const double* A,
+                       const double* Dv, const double* bias, int softplus, double* out) {
+  const int64_t b = r / dim, d = r % dim;
+  const double xt = x[r];
+  double dl = dt[r] + (bias ? bias[d] : 0.0);
+  if (softplus) dl = oracle_softplus(dl);
+  double* s = state + r * N;
+  double y = 0.0;
+  for (int64_t n = 0; n < N; ++n) {
+    s[n] = exp(dl * A[d * N + n]) * s[n] + dl * Bm[b * N + n] * xt;
+    y += Cm[b * N + n] * s[n];
+  }
+  if (Dv) y += Dv[d] * xt;
+  if (z) y *= oracle_silu(z[r]);
+  out[r] = y;
+}
+
+int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, double* state,
+                            const double* x, const double* dt, const double* z,
+                            const double* Bm, const double* Cm, const double* A,
+                            const double* Dv, const double* bias, int softplus,
+                            double* out, int nthreads) {
+  int used = 1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+  {
+#pragma omp single
+    used = omp_get_num_threads();
+#pragma omp for schedule(static)
+    for (int64_t r = 0; r < batch * dim; ++r)
+      update_row(r, dim, dstate, state, x, dt, z, Bm, Cm, A, Dv, bias, softplus, out);
+  }
+#else
+  (void)nthreads;
+  for (int64_t r = 0; r < batch * dim; ++r)
+    update_row(r, dim, dstate, state, x, dt, z, Bm, Cm, A, Dv, bias, softplus, out);
+#endif
+  return used;
+}

@@ -1,0 +1,231 @@
+"""Seeded synthetic inputs for the selective scan and the decode update.
+
+This module only draws random numbers and rounds them to the IO dtype; it holds
+none of the scan's arithmetic.  Both the HIP path (through the tests and the
+bench) and the fp64 oracle consume the arrays it returns.
+
+Input recipe (the pages use trained language models, which are out of reach, so
+seeded data with the layer shapes stands in for them):
+  u, z ~ N(0, 1);  dt ~ 0.1 * N(0, 1);  B, C ~ N(0, 1) of shape (batch, N, L),
+  shared by every channel of a batch row;
+  per-channel bias = inverse softplus of Delta0, Delta0 log-uniform in
+  [1e-3, 1e-1] (the Mamba training/inference guide, FAQ item 2: the projection
+  bias is initialised so that Delta starts in a target range);
+  A[d, n] = -(n + 1), a real diagonal structured initialisation (Mamba model
+  notes, section 3.3: A is given a special structure so the state keeps long
+  history);  D = 1.
+Draw order for one seed: u, z, dt, B, C, then the per-channel Delta0.
+bf16 inputs are the fp32 draws rounded to nearest-even.
+
+Small and mid-size configs are drawn with numpy PCG64 (deterministic on every
+machine).  The two configs whose inputs run to gigabytes (the 1M-token scan and
+the 1000-step decode) are drawn on the device with torch's Philox generator;
+the oracle then reads the sampled rows back from those same tensors.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+DSTATE = 16
+
+
+@dataclasses.dataclass(frozen=True)
+class ScanConfig:
+    name: str
+    batch: int
+    dim: int
+    seqlen: int
+    dstate: int
+    io_dtype: str  # "f32" or "bf16"
+    seed: int
+    last_state: bool = True
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    batch: int
+    dim: int
+    dstate: int
+    io_dtype: str
+    steps: int
+    seed: int
+
+
+# The five workloads: four prefill scans and one decode run.
+SCAN_CONFIGS = {
+    0: ScanConfig("tiny-f32", 2, 32, 64, DSTATE, "f32", 0),
+    1: ScanConfig("mamba130m-layer-f32", 8, 1536, 2048, DSTATE, "f32", 1),
+    2: ScanConfig("mamba2.8b-layer-bf16", 4, 5120, 4096, DSTATE, "bf16", 2),
+    3: ScanConfig("long-context-bf16", 1, 1536, 1 << 20, DSTATE, "bf16", 3),
+}
+DECODE_CONFIG = DecodeConfig("decode-b256-d5120-bf16", 256, 5120, DSTATE, "bf16", 1000, 4)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bfloat16 (nearest-even) and return them as fp32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    rounded = ((bits + 0x7FFF + lsb) >> 16) << 16
+    nan = np.isnan(x)
+    out = rounded.astype(np.uint32).view(np.float32).copy()
+    out[nan] = np.float32(np.nan)
+    return out
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of fp32 values that are already bf16-representable."""
+    return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _to_io(x: np.ndarray, io_dtype: str) -> np.ndarray:
+    return bf16_round(x) if io_dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
+
+
+def delta_bias_from_delta0(delta0: np.ndarray) -> np.ndarray:
+    """Bias b with softplus(b) = delta0 (recipe input, computed in fp64)."""
+    d0 = np.asarray(delta0, dtype=np.float64)
+    return (d0 + np.log(-np.expm1(-d0))).astype(np.float32)
+
+
+def channel_params(dim: int, dstate: int, rng: np.random.Generator):
+    """A (dim, dstate), D (dim), bias (dim) in fp32."""
+    lo, hi = math.log(1e-3), math.log(1e-1)
+    delta0 = np.exp(rng.uniform(lo, hi, size=dim))
+    A = -np.tile(np.arange(1, dstate + 1, dtype=np.float32), (dim, 1))
+    D = np.ones(dim, dtype=np.float32)
+    return A, D, delta_bias_from_delta0(delta0)
+
+
+def scan_inputs(batch: int, dim: int, seqlen: int, dstate: int = DSTATE,
+                io_dtype: str = "f32", seed: int = 0) -> dict:
+    """Host (numpy) inputs for one prefill scan; IO tensors are fp32 arrays
+    whose values are exact in io_dtype."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((batch, dim, seqlen), dtype=np.float32)
+    z = rng.standard_normal((batch, dim, seqlen), dtype=np.float32)
+    dt = np.float32(0.1) * rng.standard_normal((batch, dim, seqlen), dtype=np.float32)
+    B = rng.standard_normal((batch, dstate, seqlen), dtype=np.float32)
+    C = rng.standard_normal((batch, dstate, seqlen), dtype=np.float32)
+    A, D, bias = channel_params(dim, dstate, rng)
+    return dict(u=_to_io(u, io_dtype), z=_to_io(z, io_dtype), delta=_to_io(dt, io_dtype),
+                B=_to_io(B, io_dtype), C=_to_io(C, io_dtype), A=A, D=D, delta_bias=bias,
+                io_dtype=io_dtype)
+
+
+def scan_inputs_for(cfg: ScanConfig) -> dict:
+    return scan_inputs(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, cfg.io_dtype, cfg.seed)
+
+
+def torch_io_dtype(io_dtype: str):
+    import torch
+    return torch.bfloat16 if io_dtype == "bf16" else torch.float32
+
+
+def to_torch(inputs: dict, device="cpu") -> dict:
+    """numpy inputs -> torch tensors: IO arrays in the IO dtype, parameters fp32."""
+    import torch
+    io = torch_io_dtype(inputs["io_dtype"])
+    out = {}
+    for k, v in inputs.items():
+        if k == "io_dtype":
+            continue
+        t = torch.from_numpy(np.ascontiguousarray(v))
+        if k in ("u", "z", "delta", "B", "C", "x", "dt", "h0", "state"):
+            if k in ("h0", "state"):
+                t = t.to(torch.float32)
+            else:
+                t = t.to(io)
+        out[k] = t.to(device)
+    return out
+
+
+def scan_inputs_device(cfg: ScanConfig, device="cuda", chunk: int = 1 << 22) -> dict:
+    """Device-drawn inputs (torch Philox) for configs too large for host numpy.
+
+    Parameters (A, D, bias) still come from numpy so that they are identical
+    on every machine.  IO tensors are drawn in fp32 chunks of the flattened
+    (batch, dim, L) index space and rounded to the IO dtype.
+    """
+    import torch
+    io = torch_io_dtype(cfg.io_dtype)
+    g = torch.Generator(device=device)
+    g.manual_seed(cfg.seed)
+
+    def draw(shape, scale=1.0):
+        t = torch.empty(shape, dtype=io, device=device)
+        flat = t.view(-1)
+        for s in range(0, flat.numel(), chunk):
+            e = min(flat.numel(), s + chunk)
+            x = torch.randn(e - s, generator=g, device=device, dtype=torch.float32)
+            if scale != 1.0:
+                x.mul_(scale)
+            flat[s:e].copy_(x)
+        return t
+
+    shp = (cfg.batch, cfg.dim, cfg.seqlen)
+    u = draw(shp)
+    z = draw(shp)
+    dt = draw(shp, 0.1)
+    B = draw((cfg.batch, cfg.dstate, cfg.seqlen))
+    C = draw((cfg.batch, cfg.dstate, cfg.seqlen))
+    rng = np.random.default_rng(cfg.seed)
+    A, D, bias = channel_params(cfg.dim, cfg.dstate, rng)
+    return dict(u=u, z=z, delta=dt, B=B, C=C, A=torch.from_numpy(A).to(device),
+                D=torch.from_numpy(D).to(device), delta_bias=torch.from_numpy(bias).to(device))
+
+
+def decode_inputs_device(cfg: DecodeConfig, steps: int | None = None, device="cuda") -> dict:
+    """Per-step decode inputs for `steps` consecutive tokens, drawn on device.
+
+    x, dt, z: (steps, batch, dim); B, C: (steps, batch, dstate); io dtype.
+    The fp32 state starts at zero (the pages: the state is zero right after
+    initialisation)."""
+    import torch
+    steps = cfg.steps if steps is None else steps
+    io = torch_io_dtype(cfg.io_dtype)
+    g = torch.Generator(device=device)
+    g.manual_seed(cfg.seed)
+
+    def draw(shape, scale=1.0):
+        out = torch.empty(shape, dtype=io, device=device)
+        for s in range(shape[0]):
+            x = torch.randn(shape[1:], generator=g, device=device, dtype=torch.float32)
+            if scale != 1.0:
+                x.mul_(scale)
+            out[s].copy_(x)
+        return out
+
+    x = draw((steps, cfg.batch, cfg.dim))
+    z = draw((steps, cfg.batch, cfg.dim))
+    dt = draw((steps, cfg.batch, cfg.dim), 0.1)
+    B = draw((steps, cfg.batch, cfg.dstate))
+    C = draw((steps, cfg.batch, cfg.dstate))
+    rng = np.random.default_rng(cfg.seed)
+    A, D, bias = channel_params(cfg.dim, cfg.dstate, rng)
+    return dict(x=x, z=z, dt=dt, B=B, C=C, A=torch.from_numpy(A).to(device),
+                D=torch.from_numpy(D).to(device), dt_bias=torch.from_numpy(bias).to(device))
+
+
+def decode_inputs_host(batch: int, dim: int, dstate: int = DSTATE, io_dtype: str = "bf16",
+                       steps: int = 1, seed: int = 0, random_state: bool = False) -> dict:
+    """Small host-drawn decode inputs (numpy), for parity tests.
+
+    x, dt, z: (steps, batch, dim); B, C: (steps, batch, dstate).  With
+    random_state the initial state is N(0, 1), else zero."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((steps, batch, dim), dtype=np.float32)
+    z = rng.standard_normal((steps, batch, dim), dtype=np.float32)
+    dt = np.float32(0.1) * rng.standard_normal((steps, batch, dim), dtype=np.float32)
+    B = rng.standard_normal((steps, batch, dstate), dtype=np.float32)
+    C = rng.standard_normal((steps, batch, dstate), dtype=np.float32)
+    A, D, bias = channel_params(dim, dstate, rng)
+    state = (rng.standard_normal((batch, dim, dstate), dtype=np.float32) if random_state
+             else np.zeros((batch, dim, dstate), dtype=np.float32))
+    return dict(x=_to_io(x, io_dtype), z=_to_io(z, io_dtype), dt=_to_io(dt, io_dtype),
+                B=_to_io(B, io_dtype), C=_to_io(C, io_dtype), A=A, D=D, dt_bias=bias,
+                state=state, io_dtype=io_dtype)

@@ -1,0 +1,61 @@
+"""Plants mistakes in copies of the oracle's C source (on the CPU) and checks
+that the pins in test_oracle_pins.py catch every one of them."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ssm_oracle.c")
+
+PINS = [pins.test_lti_convolution, pins.test_unrolled_sum_fp64, pins.test_delta_zero_keeps_state_exactly,
+        pins.test_single_token_closed_form, pins.test_single_token_zero_state,
+        pins.test_split_sequence_bit_exact, pins.test_decode_equals_scan_bit_exact,
+        pins.test_reset_when_decay_underflows, pins.test_zero_A_is_prefix_sum,
+        pins.test_softplus_identities_and_bias]
+
+# (name, text in ssm_oracle.c, replacement)
+MUTANTS = [
+    ("decay-sign", "exp(dl * A[d * N + n]);", "exp(-dl * A[d * N + n]);"),
+    ("drop-skip-term", "if (Dv) y += Dv[d] * ut;", ";"),
+    ("swap-B-C", "dl * Bb[n * L + t] * ut", "dl * Cb[n * L + t] * ut"),
+    ("gate-before-skip", "    if (Dv) y += Dv[d] * ut;                            /* skip term D*u         */\n"
+     "    if (z) y *= oracle_silu(z[row + t]);",
+     "    if (z) y *= oracle_silu(z[row + t]);\n    if (Dv) y += Dv[d] * ut;"),
+    ("no-softplus", "return softplus ? oracle_softplus(x) : x;", "return x;"),
+    ("no-bias", "double x = dt + (bias ? bias[d] : 0.0);", "double x = dt;"),
+    ("readout-before-update", "      h[n] = abar * h[n] + bbar_u;\n      y += Cb[n * L + t] * h[n];",
+     "      y += Cb[n * L + t] * h[n];\n      h[n] = abar * h[n] + bbar_u;"),
+    ("ignore-h0", "h[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;", "h[n] = 0.0;"),
+    ("exact-zoh-B", "const double bbar_u = dl * Bb[n * L + t] * ut;",
+     "const double bbar_u = (A[d * N + n] != 0.0 ? (abar - 1.0) / A[d * N + n] : dl) * Bb[n * L + t] * ut;"),
+    ("softplus-sign", "return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));",
+     "return (x > 0.0 ? x : 0.0) + log1p(exp(fabs(x)));"),
+    ("silu-sign", "return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    ("decode-drop-input", "s[n] = exp(dl * A[d * N + n]) * s[n] + dl * Bm[b * N + n] * xt;",
+     "s[n] = exp(dl * A[d * N + n]) * s[n];"),
+]
+
+
+def _fails(fn):
+    args = {"test_lti_convolution": {"with_h0": True}, "test_split_sequence_bit_exact": {"cut": 13}}
+    try:
+        fn(**args.get(fn.__name__, {}))
+    except AssertionError:
+        return True
+    return False
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(name, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(lib), str(path), "-lm"])
+    with oracle.use_library(str(lib)):
+        caught = [fn.__name__ for fn in PINS if _fails(fn)]
+    assert caught, f"no pin caught mutant {name}"
