@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 selective scan.
+
+Headline: the Mamba-130m-like layer scan (batch 8, d_inner 1536, L 2048,
+d_state 16, fp32 IO, silu gate, last_state returned).  One step = one full
+prefill scan over the batch with inputs already resident in HBM.  Throughput is
+algorithmic bytes per second (every input element read once, B and C once per
+(batch, token), every output written once, the state never touching HBM) and
+channel*tokens per second; the HBM fraction is against MI355X's 8 TB/s.
+
+Also measured (secondary, same JSON line): the bf16 2.8b-like layer scan and
+the 1000-step decode update; with --all also the 1M-token scan.
+
+Prints ONE JSON line on stdout.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+METRIC = "selective-scan GB/s and channel·tokens/s (1 GPU); % of HBM roofline"
+SCAN_KERNEL_SRC = ["selective_state_space_74_amd/csrc/scan_fwd.hip",
+                   "selective_state_space_74_amd/csrc/ssm_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_fwd_mamba130m_f32_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def scan_bytes(batch, dim, L, N, esz, last_state=True, h0=False, gate=True):
+    """Algorithmic bytes of one prefill scan."""
+    io = batch * dim * L * esz * (3 + (1 if gate else 0))   # u, delta, out (+ z)
+    bc = 2 * batch * N * L * esz                            # B, C once per (batch, token)
+    params = dim * N * 4 + 2 * dim * 4                      # A, D, bias
+    st = batch * dim * N * 4 * ((1 if last_state else 0) + (1 if h0 else 0))
+    return io + bc + params + st
+
+
+def decode_bytes(batch, dim, N, esz):
+    """Algorithmic bytes of one decode step."""
+    state = 2 * batch * dim * N * 4                         # read + write
+    io = 4 * batch * dim * esz                              # x, dt, z, out
+    bc = 2 * batch * N * esz
+    params = dim * N * 4 + 2 * dim * 4
+    return state + io + bc + params
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for rel in SCAN_KERNEL_SRC:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the scan kernel from the committed rocprofv3
+    counter runs, or None when the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def timed_launches(fn, iters, torch):
+    """Average kernel duration with HIP events on the launching stream."""
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    for i in range(iters):
+        starts[i].record(stream)
+        fn(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return float(np.mean(ms)), float(np.min(ms))
+
+
+def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2):
+    """Times `steps` full scans; returns a dict of measurements."""
+    dev = "cuda"
+    sets = []
+    for r in range(rotate):
+        if cfg.seqlen * cfg.dim * cfg.batch > 200_000_000:
+            t = si.scan_inputs_device(cfg, dev)
+        else:
+            t = si.to_torch(si.scan_inputs_for(cfg), dev)
+        sets.append(t)
+        if r == 0 and rotate > 1 and cfg.seqlen * cfg.dim * cfg.batch > 1_000_000_000:
+            break   # the long config alone exceeds every cache; one set is enough
+    io = sets[0]["u"].dtype
+    outs = [torch.empty_like(s["u"]) for s in sets]
+    lasts = [torch.empty((cfg.batch, cfg.dim, cfg.dstate), device=dev) for _ in sets]
+
+    def step(i):
+        k = i % len(sets)
+        s = sets[k]
+        ssm.selective_scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
+                               delta_bias=s["delta_bias"], out=outs[k], last_state=lasts[k])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms, kern_min = timed_launches(step, max(10, min(steps, 200)), torch)
+    esz = 2 if io == torch.bfloat16 else 4
+    nbytes = scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, esz)
+    ms_step = wall / steps * 1e3
+    res = dict(ms_per_step=ms_step, kernel_ms=kern_ms, kernel_ms_min=kern_min, bytes=nbytes,
+               gbps=nbytes / (ms_step * 1e-3) / 1e9,
+               kernel_gbps=nbytes / (kern_ms * 1e-3) / 1e9,
+               channel_tokens_per_s=cfg.batch * cfg.dim * cfg.seqlen / (ms_step * 1e-3),
+               io_dtype="bf16" if esz == 2 else "f32")
+    res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBS
+    del sets, outs, lasts
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(cfg, torch, ssm, si, warmup=20):
+    """1000 consecutive decode steps with per-step inputs pre-resident."""
+    dev = "cuda"
+    d = si.decode_inputs_device(cfg, device=dev)
+    state = torch.zeros((cfg.batch, cfg.dim, cfg.dstate), device=dev)
+    out = torch.empty((cfg.steps, cfg.batch, cfg.dim), dtype=d["x"].dtype, device=dev)
+
+    def step(s):
+        ssm.selective_state_update(state, d["x"][s], d["dt"][s], d["A"], d["B"][s], d["C"][s],
+                                   D=d["D"], z=d["z"][s], dt_bias=d["dt_bias"], out=out[s])
+
+    for s in range(warmup):
+        step(s)
+    state.zero_()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(cfg.steps):
+        step(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms, kern_min = timed_launches(step, 200, torch)
+    esz = 2 if d["x"].dtype == torch.bfloat16 else 4
+    nbytes = decode_bytes(cfg.batch, cfg.dim, cfg.dstate, esz)
+    ms_step = wall / cfg.steps * 1e3
+    res = dict(steps=cfg.steps, ms_total=wall * 1e3, ms_per_step=ms_step, kernel_ms=kern_ms,
+               kernel_ms_min=kern_min, bytes_per_step=nbytes,
+               gbps=nbytes / (ms_step * 1e-3) / 1e9,
+               kernel_gbps=nbytes / (kern_ms * 1e-3) / 1e9,
+               channel_tokens_per_s=cfg.batch * cfg.dim / (ms_step * 1e-3))
+    res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBS
+    del d, out, state
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(cfg, si, max_s=30.0):
+    """The fp64 oracle, as it stands, on the host cores, over the headline
+    workload (whole batch rows at full length).  It runs batch row 0 first and
+    adds further batch rows while the projected total stays under max_s."""
+    import oracle
+    inp = si.scan_inputs_for(cfg)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
+
+    def run(k):
+        t0 = time.perf_counter()
+        oracle.selective_scan(inp["u"][:k], inp["delta"][:k], inp["A"], inp["B"][:k],
+                              inp["C"][:k], D=inp["D"], z=inp["z"][:k],
+                              delta_bias=inp["delta_bias"], nthreads=threads,
+                              return_last_state=True)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    k = int(max(1, min(cfg.batch, max_s / max(t1, 1e-9))))
+    dt = run(k) if k > 1 else t1
+    used = oracle.selective_scan.last_threads
+    rows = k * cfg.dim
+    nbytes = scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, 4) * k / cfg.batch
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
+            "channel_tokens_per_s": rows * cfg.seqlen / dt, "seconds": round(dt, 3),
+            "sample": f"{k} of {cfg.batch} batch rows ({rows} channel rows) of the headline "
+                      f"workload at full L={cfg.seqlen}; fp64 oracle with {used} OpenMP threads"}
+
+
+def profile_run(cfg, torch, ssm, si, launches=10):
+    """Headline scan launches plus a plain copy kernel of known size (reads
+    1 GiB, writes 1 GiB) so that FETCH_SIZE / WRITE_SIZE can be scaled."""
+    t = si.to_torch(si.scan_inputs_for(cfg), "cuda")
+    out = torch.empty_like(t["u"])
+    last = torch.empty((cfg.batch, cfg.dim, cfg.dstate), device="cuda")
+    for i in range(launches):
+        ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                               delta_bias=t["delta_bias"], out=out, last_state=last)
+    torch.cuda.synchronize()
+    n = (1 << 30) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for i in range(launches):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"[profile] {launches} scan launches ({scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, 4)}"
+        f" algorithmic bytes each) and {launches} copy launches (1 GiB read + 1 GiB write)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--all", action="store_true", help="also time the 1M-token scan")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="only the headline scan (10 launches) and a 1 GiB copy kernel "
+                         "(10 launches) that calibrates the HBM byte counters; for rocprofv3")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the scan shards by batch/channel with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_74_amd as ssm
+    import synth_inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    ssm.lib()
+    torch.cuda.init()
+
+    head = si.SCAN_CONFIGS[1]
+    if args.profile:
+        profile_run(head, torch, ssm, si)
+        return
+    log(f"[bench] headline {head.name}: warmup {args.warmup}, steps {args.steps}")
+    r = bench_scan(head, args.steps, args.warmup, torch, ssm, si)
+    log(f"[bench] headline {r['gbps']:.1f} GB/s, kernel {r['kernel_ms'] * 1e3:.1f} us")
+
+    secondary = {}
+    if not args.no_secondary:
+        c2 = si.SCAN_CONFIGS[2]
+        log(f"[bench] secondary {c2.name}")
+        secondary[c2.name] = bench_scan(c2, max(20, args.steps // 4), 5, torch, ssm, si)
+        log(f"[bench] {c2.name} {secondary[c2.name]['gbps']:.1f} GB/s")
+        log(f"[bench] secondary {si.DECODE_CONFIG.name}")
+        secondary[si.DECODE_CONFIG.name] = bench_decode(si.DECODE_CONFIG, torch, ssm, si)
+        log(f"[bench] decode {secondary[si.DECODE_CONFIG.name]['gbps']:.1f} GB/s")
+        if args.all:
+            c3 = si.SCAN_CONFIGS[3]
+            log(f"[bench] secondary {c3.name}")
+            secondary[c3.name] = bench_scan(c3, 3, 1, torch, ssm, si, rotate=1)
+            log(f"[bench] {c3.name} {secondary[c3.name]['gbps']:.1f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle)")
+        cpu = cpu_baseline(head, si)
+        log(f"[bench] cpu baseline {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
+
+    traffic = measured_traffic()
+    achieved = r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(r["gbps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy PCG64: u,z~N(0,1), dt~0.1N(0,1), B,C~N(0,1), "
+                "bias=inv-softplus(logU[1e-3,1e-1]), A=-(n+1), D=1)",
+        "config": {"workload": "selective scan fwd, mamba-130m-like layer: batch 8, d_inner 1536, "
+                               "L 2048, d_state 16, fp32 IO, silu gate, last_state",
+                   "batch": head.batch, "dim": head.dim, "seqlen": head.seqlen,
+                   "dstate": head.dstate},
+        "channel_tokens_per_s": r["channel_tokens_per_s"],
+        "hbm_frac": round(r["hbm_frac"], 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "scan_fwd_kernel<float>",
+                     "kernel_ms": round(r["kernel_ms"], 5),
+                     "algorithmic_bytes_per_launch": r["bytes"]},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

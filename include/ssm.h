@@ -1,0 +1,153 @@
+/*
+ * ssm.h -- C ABI of libssm.so, the gfx950 (MI355X) selective-scan library.
+ *
+ * Two operations, both from the Mamba pages (cited by page title and section):
+ *
+ *   ssm_selective_scan_fwd  -- prefill.  For every batch row b, channel d and
+ *     state index n, with Delta_t = softplus(delta_t + bias[d]) (Mamba paper
+ *     notes, 0539edu.com, section 2.3; Mamba training/inference guide, FAQ 2):
+ *         h_t[n] = exp(Delta_t * A[d,n]) * h_{t-1}[n] + Delta_t * B[b,n,t] * u_t
+ *         y_t    = sum_n C[b,n,t] * h_t[n] + D[d] * u_t
+ *         out_t  = y_t * silu(z_t)
+ *     starting from h_{-1} = h0 (or 0), and optionally returning h_{L-1}.
+ *     The discrete recurrence and readout are section 2.2 of the Mamba model
+ *     notes; the per-channel diagonal SSM is section 4.4 there; B, C and
+ *     Delta depending on the token is section 4.1; the gate is the block's
+ *     gate branch (section 4.3).
+ *
+ *   ssm_selective_state_update -- decode: the same recurrence for a single
+ *     token, reading and writing a resident fp32 state (Mamba paper notes,
+ *     section 4.3: inference keeps one fixed-size state and updates it once
+ *     per generated token).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, never frees and holds no global state.
+ *   - Strides are in ELEMENTS and must be >= 0.  The innermost (time, or
+ *     state for decode) stride is implicitly 1.
+ *   - io_dtype (SSM_F32 or SSM_BF16) is the dtype of u/delta/z/B/C/out in the
+ *     scan and of x/dt/z/B/C/out in decode.  A, D, the Delta bias, h0,
+ *     last_state and the decode state are always fp32.
+ *   - All arithmetic is fp32; bf16 inputs are widened exactly; fp32 results
+ *     are rounded to bf16 to nearest-even when io_dtype is SSM_BF16.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *     stream).  The return value covers host-side validation and the launch
+ *     itself; a device fault shows up at the caller's next synchronisation.
+ *   - No exception crosses the ABI; errors are ssm_status codes, explained by
+ *     ssm_status_string().  On any error nothing is launched.
+ *   - The library is re-entrant and thread-safe (no mutable global state).
+ */
+#ifndef SSM_H_
+#define SSM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef enum ssm_status {
+  SSM_OK = 0,
+  SSM_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  SSM_ERR_SHAPE = 2,       /* negative size, or dstate < 1                     */
+  SSM_ERR_STRIDE = 3,      /* negative stride                                  */
+  SSM_ERR_DTYPE = 4,       /* io_dtype is not SSM_F32 / SSM_BF16               */
+  SSM_ERR_ALIGN = 5,       /* pointer not aligned to its element size          */
+  SSM_ERR_ALIAS = 6,       /* an output overlaps an input it must not overlap  */
+  SSM_ERR_UNSUPPORTED = 7, /* valid but not built: dstate != 16                */
+  SSM_ERR_HIP = 8          /* the HIP runtime rejected the launch              */
+} ssm_status;
+
+typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
+
+/* Arguments of the prefill scan.
+ *   u, delta, z, out : (batch, dim, seqlen), time stride 1; element (b, d, t)
+ *                      at ptr[b * *_batch_stride + d * *_dim_stride + t].
+ *   B, C             : (batch, dstate, seqlen), time stride 1; shared by all
+ *                      channels of a batch row; element (b, n, t) at
+ *                      ptr[b * *_batch_stride + n * *_state_stride + t].
+ *   A                : (dim, dstate) fp32, element (d, n) at
+ *                      A[d * A_dim_stride + n * A_state_stride].
+ *   D, delta_bias    : (dim) fp32, contiguous.  NULL means 0.
+ *   h0, last_state   : (batch, dim, dstate) fp32, contiguous.  h0 NULL means a
+ *                      zero initial state; last_state NULL means "not wanted".
+ *   z NULL           : no gate (out = y).
+ *   delta_softplus   : nonzero applies softplus to delta + bias.
+ * Sizes: batch, dim, seqlen >= 0 (zero sizes are a no-op, except that
+ * seqlen == 0 with last_state set copies h0, or zeros, into last_state);
+ * dstate must be 16.
+ * Aliasing: out must not overlap u, delta, z, B or C; last_state must not
+ * overlap any input except that it may be exactly h0 (in-place carry). */
+typedef struct ssm_scan_args {
+  int64_t batch, dim, seqlen, dstate;
+  int32_t io_dtype;       /* ssm_dtype */
+  int32_t delta_softplus; /* bool */
+  const void* u;      int64_t u_batch_stride, u_dim_stride;
+  const void* delta;  int64_t delta_batch_stride, delta_dim_stride;
+  const void* z;      int64_t z_batch_stride, z_dim_stride;
+  const void* B;      int64_t B_batch_stride, B_state_stride;
+  const void* C;      int64_t C_batch_stride, C_state_stride;
+  const float* A;     int64_t A_dim_stride, A_state_stride;
+  const float* D;
+  const float* delta_bias;
+  const float* h0;
+  float* last_state;
+  void* out;          int64_t out_batch_stride, out_dim_stride;
+} ssm_scan_args;
+
+/* Arguments of the single-token decode update.
+ *   state            : (batch, dim, dstate) fp32, state stride 1, element
+ *                      (b, d, n) at state[b * state_batch_stride +
+ *                      d * state_dim_stride + n]; updated IN PLACE.
+ *   x, dt, z, out    : (batch, dim), dim stride 1.  z NULL means no gate.
+ *   B, C             : (batch, dstate), state stride 1.
+ *   A                : (dim, dstate) fp32, state stride 1.
+ *   D, dt_bias       : (dim) fp32, contiguous, NULL means 0.
+ * Sizes: batch, dim >= 0 (zero is a no-op); dstate must be 16.
+ * Aliasing: out must not overlap state or any input; state must not overlap
+ * any input. */
+typedef struct ssm_update_args {
+  int64_t batch, dim, dstate;
+  int32_t io_dtype;    /* ssm_dtype */
+  int32_t dt_softplus; /* bool */
+  float* state;       int64_t state_batch_stride, state_dim_stride;
+  const void* x;      int64_t x_batch_stride;
+  const void* dt;     int64_t dt_batch_stride;
+  const void* z;      int64_t z_batch_stride;
+  const void* B;      int64_t B_batch_stride;
+  const void* C;      int64_t C_batch_stride;
+  const float* A;     int64_t A_dim_stride;
+  const float* D;
+  const float* dt_bias;
+  void* out;          int64_t out_batch_stride;
+} ssm_update_args;
+
+/* ABI version of the loaded library (SSM_ABI_VERSION at build time). */
+int ssm_abi_version(void);
+
+/* sizeof the argument structs, for bindings that mirror them. */
+size_t ssm_scan_args_size(void);
+size_t ssm_update_args_size(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* ssm_status_string(int status);
+
+/* Pure host checks of an argument block: no HIP call, no device access, so
+ * they run on a machine without a GPU.  Returns the first failing status. */
+int ssm_validate_scan(const ssm_scan_args* args);
+int ssm_validate_update(const ssm_update_args* args);
+
+/* Prefill scan (see ssm_scan_args).  Validates, then launches on `stream`. */
+int ssm_selective_scan_fwd(const ssm_scan_args* args, void* stream);
+
+/* Decode update (see ssm_update_args).  Validates, then launches on `stream`. */
+int ssm_selective_state_update(const ssm_update_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H_ */

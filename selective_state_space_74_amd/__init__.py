@@ -1,0 +1,279 @@
+"""MI355X (gfx950) selective scan: Python binding over libssm.so.
+
+This module only marshals arguments: it checks tensor placement and dtypes,
+allocates outputs through torch, fills the C argument blocks declared in
+include/ssm.h and calls the library on torch's current HIP stream.  Every step
+of the computation runs in the HIP kernels of libssm.so; there is no Python or
+CPU fallback, and importing a missing library raises.
+
+    selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                       delta_softplus=True, h0=None, return_last_state=False)
+        -> out, or (out, last_state)
+    selective_state_update(state, x, dt, A, B, C, D=None, z=None,
+                           dt_bias=None, dt_softplus=True) -> out  (state updated in place)
+
+Shapes: u, delta, z (batch, dim, L) with time stride 1; B, C (batch, 16, L)
+with time stride 1; A (dim, 16) fp32; D, delta_bias (dim,) fp32; h0 and
+last_state (batch, dim, 16) fp32.  Decode: state (batch, dim, 16) fp32 with
+state stride 1; x, dt, z (batch, dim); B, C (batch, 16).  IO tensors are
+float32 or bfloat16 (all of one dtype).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssm.so")
+
+SSM_ABI_VERSION = 1
+SSM_F32, SSM_BF16 = 0, 1
+STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_STRIDE",
+          4: "SSM_ERR_DTYPE", 5: "SSM_ERR_ALIGN", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_UNSUPPORTED",
+          8: "SSM_ERR_HIP"}
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+
+
+class ScanArgs(ctypes.Structure):
+    """Mirror of ssm_scan_args."""
+    _fields_ = [("batch", _I64), ("dim", _I64), ("seqlen", _I64), ("dstate", _I64),
+                ("io_dtype", _I32), ("delta_softplus", _I32),
+                ("u", _P), ("u_batch_stride", _I64), ("u_dim_stride", _I64),
+                ("delta", _P), ("delta_batch_stride", _I64), ("delta_dim_stride", _I64),
+                ("z", _P), ("z_batch_stride", _I64), ("z_dim_stride", _I64),
+                ("B", _P), ("B_batch_stride", _I64), ("B_state_stride", _I64),
+                ("C", _P), ("C_batch_stride", _I64), ("C_state_stride", _I64),
+                ("A", _P), ("A_dim_stride", _I64), ("A_state_stride", _I64),
+                ("D", _P), ("delta_bias", _P), ("h0", _P), ("last_state", _P),
+                ("out", _P), ("out_batch_stride", _I64), ("out_dim_stride", _I64)]
+
+
+class UpdateArgs(ctypes.Structure):
+    """Mirror of ssm_update_args."""
+    _fields_ = [("batch", _I64), ("dim", _I64), ("dstate", _I64),
+                ("io_dtype", _I32), ("dt_softplus", _I32),
+                ("state", _P), ("state_batch_stride", _I64), ("state_dim_stride", _I64),
+                ("x", _P), ("x_batch_stride", _I64),
+                ("dt", _P), ("dt_batch_stride", _I64),
+                ("z", _P), ("z_batch_stride", _I64),
+                ("B", _P), ("B_batch_stride", _I64),
+                ("C", _P), ("C_batch_stride", _I64),
+                ("A", _P), ("A_dim_stride", _I64),
+                ("D", _P), ("dt_bias", _P),
+                ("out", _P), ("out_batch_stride", _I64)]
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libssm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libssm.so not found at {LIB_PATH}; build it with "
+                              "`python -m selective_state_space_74_amd._build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.ssm_abi_version.restype = ctypes.c_int
+        L.ssm_scan_args_size.restype = ctypes.c_size_t
+        L.ssm_update_args_size.restype = ctypes.c_size_t
+        L.ssm_status_string.restype = ctypes.c_char_p
+        L.ssm_status_string.argtypes = [ctypes.c_int]
+        for name, T in (("ssm_validate_scan", ScanArgs), ("ssm_validate_update", UpdateArgs)):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.POINTER(T)]
+        L.ssm_selective_scan_fwd.restype = ctypes.c_int
+        L.ssm_selective_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _P]
+        L.ssm_selective_state_update.restype = ctypes.c_int
+        L.ssm_selective_state_update.argtypes = [ctypes.POINTER(UpdateArgs), _P]
+        if L.ssm_abi_version() != SSM_ABI_VERSION:
+            raise ImportError(f"libssm.so ABI {L.ssm_abi_version()} != {SSM_ABI_VERSION}")
+        if (L.ssm_scan_args_size() != ctypes.sizeof(ScanArgs)
+                or L.ssm_update_args_size() != ctypes.sizeof(UpdateArgs)):
+            raise ImportError("libssm.so argument struct layout differs from the binding")
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ssm_status_string(int(status)).decode()
+
+
+def validate_scan(args: ScanArgs) -> int:
+    return lib().ssm_validate_scan(ctypes.byref(args))
+
+
+def validate_update(args: UpdateArgs) -> int:
+    return lib().ssm_validate_update(ctypes.byref(args))
+
+
+def scan_fwd_raw(args: ScanArgs, stream: int = 0) -> int:
+    return lib().ssm_selective_scan_fwd(ctypes.byref(args), _P(stream or None))
+
+
+def state_update_raw(args: UpdateArgs, stream: int = 0) -> int:
+    return lib().ssm_selective_state_update(ctypes.byref(args), _P(stream or None))
+
+
+# ---------------------------------------------------------------------------
+# torch-level wrappers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _io_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SSM_F32
+    if t.dtype == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError(f"IO tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check_dev(name, t, device, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _contig_f32(name, t, shape):
+    if t is None:
+        return None
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
+                       h0=None, return_last_state=False, out=None, last_state=None, stream=None):
+    """Prefill selective scan on the GPU (see the module docstring)."""
+    torch = _torch()
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, L)")
+    batch, dim, L = u.shape
+    N = A.shape[1] if A.dim() == 2 else -1
+    dev = u.device
+    io = u.dtype
+    code = _io_code(u)
+    for name, t in (("delta", delta), ("z", z), ("B", B), ("C", C)):
+        _check_dev(name, t, dev, io)
+    for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias), ("h0", h0),
+                    ("last_state", last_state)):
+        _check_dev(name, t, dev, torch.float32)
+    if tuple(delta.shape) != (batch, dim, L) or (z is not None and tuple(z.shape) != (batch, dim, L)):
+        raise ValueError("delta and z must match u's shape")
+    if tuple(B.shape) != (batch, N, L) or tuple(C.shape) != (batch, N, L):
+        raise ValueError("B and C must be (batch, dstate, L)")
+    if tuple(A.shape) != (dim, N):
+        raise ValueError("A must be (dim, dstate)")
+    for name, t in (("u", u), ("delta", delta), ("z", z), ("B", B), ("C", C)):
+        if t is not None and L > 1 and t.stride(2) != 1:
+            raise ValueError(f"{name} must have time stride 1")
+    _contig_f32("D", D, (dim,))
+    _contig_f32("delta_bias", delta_bias, (dim,))
+    _contig_f32("h0", h0, (batch, dim, N))
+    if out is None:
+        out = torch.empty((batch, dim, L), dtype=io, device=dev)
+    _check_dev("out", out, dev, io)
+    if tuple(out.shape) != (batch, dim, L) or (L > 1 and out.stride(2) != 1):
+        raise ValueError("out must be (batch, dim, L) with time stride 1")
+    if return_last_state and last_state is None:
+        last_state = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    if last_state is not None:
+        _contig_f32("last_state", last_state, (batch, dim, N))
+    a = ScanArgs()
+    a.batch, a.dim, a.seqlen, a.dstate = batch, dim, L, N
+    a.io_dtype, a.delta_softplus = code, int(bool(delta_softplus))
+    a.u, (a.u_batch_stride, a.u_dim_stride) = _ptr(u), u.stride()[:2]
+    a.delta, (a.delta_batch_stride, a.delta_dim_stride) = _ptr(delta), delta.stride()[:2]
+    if z is not None:
+        a.z, (a.z_batch_stride, a.z_dim_stride) = _ptr(z), z.stride()[:2]
+    a.B, (a.B_batch_stride, a.B_state_stride) = _ptr(B), B.stride()[:2]
+    a.C, (a.C_batch_stride, a.C_state_stride) = _ptr(C), C.stride()[:2]
+    a.A, (a.A_dim_stride, a.A_state_stride) = _ptr(A), A.stride()
+    a.D, a.delta_bias, a.h0 = _ptr(D), _ptr(delta_bias), _ptr(h0)
+    a.last_state = _ptr(last_state)
+    a.out, (a.out_batch_stride, a.out_dim_stride) = _ptr(out), out.stride()[:2]
+    st = scan_fwd_raw(a, _stream(stream))
+    if st != 0:
+        raise SSMError(st, "ssm_selective_scan_fwd")
+    return (out, last_state) if return_last_state else out
+
+
+def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True,
+                           out=None, stream=None):
+    """Single-token decode update on the GPU; `state` is updated in place."""
+    torch = _torch()
+    if state.dim() != 3:
+        raise ValueError("state must be (batch, dim, dstate)")
+    batch, dim, N = state.shape
+    dev = state.device
+    io = x.dtype
+    code = _io_code(x)
+    _check_dev("state", state, dev, torch.float32)
+    for name, t in (("x", x), ("dt", dt), ("z", z), ("B", B), ("C", C)):
+        _check_dev(name, t, dev, io)
+    for name, t in (("A", A), ("D", D), ("dt_bias", dt_bias)):
+        _check_dev(name, t, dev, torch.float32)
+    for name, t in (("x", x), ("dt", dt), ("z", z)):
+        if t is not None and (tuple(t.shape) != (batch, dim) or (dim > 1 and t.stride(1) != 1)):
+            raise ValueError(f"{name} must be (batch, dim) with dim stride 1")
+    for name, t in (("B", B), ("C", C)):
+        if tuple(t.shape) != (batch, N) or (N > 1 and t.stride(1) != 1):
+            raise ValueError(f"{name} must be (batch, dstate) with state stride 1")
+    if tuple(A.shape) != (dim, N) or (N > 1 and A.stride(1) != 1):
+        raise ValueError("A must be (dim, dstate) with state stride 1")
+    if N > 1 and state.stride(2) != 1:
+        raise ValueError("state must have state stride 1")
+    _contig_f32("D", D, (dim,))
+    _contig_f32("dt_bias", dt_bias, (dim,))
+    if out is None:
+        out = torch.empty((batch, dim), dtype=io, device=dev)
+    _check_dev("out", out, dev, io)
+    if tuple(out.shape) != (batch, dim) or (dim > 1 and out.stride(1) != 1):
+        raise ValueError("out must be (batch, dim) with dim stride 1")
+    a = UpdateArgs()
+    a.batch, a.dim, a.dstate = batch, dim, N
+    a.io_dtype, a.dt_softplus = code, int(bool(dt_softplus))
+    a.state, (a.state_batch_stride, a.state_dim_stride) = _ptr(state), state.stride()[:2]
+    a.x, a.x_batch_stride = _ptr(x), x.stride(0)
+    a.dt, a.dt_batch_stride = _ptr(dt), dt.stride(0)
+    if z is not None:
+        a.z, a.z_batch_stride = _ptr(z), z.stride(0)
+    a.B, a.B_batch_stride = _ptr(B), B.stride(0)
+    a.C, a.C_batch_stride = _ptr(C), C.stride(0)
+    a.A, a.A_dim_stride = _ptr(A), A.stride(0)
+    a.D, a.dt_bias = _ptr(D), _ptr(dt_bias)
+    a.out, a.out_batch_stride = _ptr(out), out.stride(0)
+    st = state_update_raw(a, _stream(stream))
+    if st != 0:
+        raise SSMError(st, "ssm_selective_state_update")
+    return out

@@ -1,0 +1,163 @@
+// ssm_abi.hip -- the extern "C" surface of libssm.so: host-side validation
+// and dispatch to the gfx950 kernels.  Validation is pure host code (no HIP
+// call) so it can be exercised on a machine without a GPU.
+#include <stdint.h>
+#include <string.h>
+
+#include "ssm_internal.h"
+
+namespace {
+
+struct Span {  // byte range [lo, hi)
+  uintptr_t lo = 0, hi = 0;
+  bool empty() const { return hi <= lo; }
+};
+
+bool overlap(const Span& a, const Span& b) {
+  return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+// Bytes touched by a (n0, n1, n2) tensor with strides (s0, s1, 1).
+Span span3(const void* p, int64_t n0, int64_t s0, int64_t n1, int64_t s1, int64_t n2,
+           int64_t esz) {
+  Span s;
+  if (!p || n0 <= 0 || n1 <= 0 || n2 <= 0) return s;
+  s.lo = reinterpret_cast<uintptr_t>(p);
+  s.hi = s.lo + static_cast<uintptr_t>(((n0 - 1) * s0 + (n1 - 1) * s1 + n2) * esz);
+  return s;
+}
+
+Span span1(const void* p, int64_t n, int64_t esz) { return span3(p, 1, 0, 1, 0, n, esz); }
+
+bool misaligned(const void* p, int64_t align) {
+  return p && (reinterpret_cast<uintptr_t>(p) % static_cast<uintptr_t>(align)) != 0;
+}
+
+int64_t io_size(int32_t dt) { return dt == SSM_BF16 ? 2 : 4; }
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+size_t ssm_scan_args_size(void) { return sizeof(ssm_scan_args); }
+size_t ssm_update_args_size(void) { return sizeof(ssm_update_args); }
+
+const char* ssm_status_string(int status) {
+  switch (status) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL: return "a required pointer is NULL";
+    case SSM_ERR_SHAPE: return "invalid size (negative, or dstate < 1)";
+    case SSM_ERR_STRIDE: return "invalid stride (negative)";
+    case SSM_ERR_DTYPE: return "io_dtype must be SSM_F32 or SSM_BF16";
+    case SSM_ERR_ALIGN: return "pointer not aligned to its element size";
+    case SSM_ERR_ALIAS: return "an output overlaps an input";
+    case SSM_ERR_UNSUPPORTED: return "unsupported configuration (dstate must be 16)";
+    case SSM_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int ssm_validate_scan(const ssm_scan_args* a) {
+  if (!a) return SSM_ERR_NULL;
+  if (a->batch < 0 || a->dim < 0 || a->seqlen < 0 || a->dstate < 1) return SSM_ERR_SHAPE;
+  if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (a->dstate != 16) return SSM_ERR_UNSUPPORTED;
+  if (a->batch == 0 || a->dim == 0) return SSM_OK;
+  const int64_t B = a->batch, Dm = a->dim, L = a->seqlen, N = a->dstate;
+  const int64_t esz = io_size(a->io_dtype);
+  if (L > 0) {
+    if (!a->u || !a->delta || !a->B || !a->C || !a->A || !a->out) return SSM_ERR_NULL;
+    const int64_t strides[] = {a->u_batch_stride, a->u_dim_stride, a->delta_batch_stride,
+                               a->delta_dim_stride, a->B_batch_stride, a->B_state_stride,
+                               a->C_batch_stride, a->C_state_stride, a->A_dim_stride,
+                               a->A_state_stride, a->out_batch_stride, a->out_dim_stride,
+                               a->z ? a->z_batch_stride : 0, a->z ? a->z_dim_stride : 0};
+    for (int64_t s : strides)
+      if (s < 0) return SSM_ERR_STRIDE;
+    if (misaligned(a->u, esz) || misaligned(a->delta, esz) || misaligned(a->z, esz) ||
+        misaligned(a->B, esz) || misaligned(a->C, esz) || misaligned(a->out, esz))
+      return SSM_ERR_ALIGN;
+  }
+  if (misaligned(a->A, 4) || misaligned(a->D, 4) || misaligned(a->delta_bias, 4) ||
+      misaligned(a->h0, 4) || misaligned(a->last_state, 4))
+    return SSM_ERR_ALIGN;
+
+  const Span su = span3(a->u, B, a->u_batch_stride, Dm, a->u_dim_stride, L, esz);
+  const Span sdl = span3(a->delta, B, a->delta_batch_stride, Dm, a->delta_dim_stride, L, esz);
+  const Span sz = span3(a->z, B, a->z_batch_stride, Dm, a->z_dim_stride, L, esz);
+  const Span sB = span3(a->B, B, a->B_batch_stride, N, a->B_state_stride, L, esz);
+  const Span sC = span3(a->C, B, a->C_batch_stride, N, a->C_state_stride, L, esz);
+  const Span sA = L > 0 ? span3(a->A, 1, 0, Dm, a->A_dim_stride, 1, 4) : Span{};
+  Span sA_full = sA;
+  if (L > 0 && a->A) sA_full.hi += static_cast<uintptr_t>((N - 1) * a->A_state_stride * 4);
+  const Span sD = span1(a->D, Dm, 4), sbias = span1(a->delta_bias, Dm, 4);
+  const Span sh0 = span1(a->h0, B * Dm * N, 4);
+  const Span sout = span3(a->out, B, a->out_batch_stride, Dm, a->out_dim_stride, L, esz);
+  const Span sls = span1(a->last_state, B * Dm * N, 4);
+  const Span inputs[] = {su, sdl, sz, sB, sC, sA_full, sD, sbias, sh0};
+  for (const Span& s : inputs)
+    if (overlap(sout, s)) return SSM_ERR_ALIAS;
+  for (int i = 0; i < 8; ++i)
+    if (overlap(sls, inputs[i])) return SSM_ERR_ALIAS;
+  if (overlap(sls, sout)) return SSM_ERR_ALIAS;
+  if (overlap(sls, sh0) && a->last_state != a->h0) return SSM_ERR_ALIAS;
+  return SSM_OK;
+}
+
+int ssm_validate_update(const ssm_update_args* a) {
+  if (!a) return SSM_ERR_NULL;
+  if (a->batch < 0 || a->dim < 0 || a->dstate < 1) return SSM_ERR_SHAPE;
+  if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (a->dstate != 16) return SSM_ERR_UNSUPPORTED;
+  if (a->batch == 0 || a->dim == 0) return SSM_OK;
+  if (!a->state || !a->x || !a->dt || !a->B || !a->C || !a->A || !a->out) return SSM_ERR_NULL;
+  const int64_t strides[] = {a->state_batch_stride, a->state_dim_stride, a->x_batch_stride,
+                             a->dt_batch_stride, a->z ? a->z_batch_stride : 0,
+                             a->B_batch_stride, a->C_batch_stride, a->A_dim_stride,
+                             a->out_batch_stride};
+  for (int64_t s : strides)
+    if (s < 0) return SSM_ERR_STRIDE;
+  const int64_t esz = io_size(a->io_dtype);
+  const int64_t B = a->batch, Dm = a->dim, N = a->dstate;
+  if (misaligned(a->x, esz) || misaligned(a->dt, esz) || misaligned(a->z, esz) ||
+      misaligned(a->B, esz) || misaligned(a->C, esz) || misaligned(a->out, esz))
+    return SSM_ERR_ALIGN;
+  if (misaligned(a->state, 4) || misaligned(a->A, 4) || misaligned(a->D, 4) ||
+      misaligned(a->dt_bias, 4))
+    return SSM_ERR_ALIGN;
+  const Span sst = span3(a->state, B, a->state_batch_stride, Dm, a->state_dim_stride, N, 4);
+  const Span sx = span3(a->x, 1, 0, B, a->x_batch_stride, Dm, esz);
+  const Span sdt = span3(a->dt, 1, 0, B, a->dt_batch_stride, Dm, esz);
+  const Span sz = span3(a->z, 1, 0, B, a->z_batch_stride, Dm, esz);
+  const Span sB = span3(a->B, 1, 0, B, a->B_batch_stride, N, esz);
+  const Span sC = span3(a->C, 1, 0, B, a->C_batch_stride, N, esz);
+  const Span sA = span3(a->A, 1, 0, Dm, a->A_dim_stride, N, 4);
+  const Span sD = span1(a->D, Dm, 4), sbias = span1(a->dt_bias, Dm, 4);
+  const Span sout = span3(a->out, 1, 0, B, a->out_batch_stride, Dm, esz);
+  const Span inputs[] = {sx, sdt, sz, sB, sC, sA, sD, sbias};
+  for (const Span& s : inputs)
+    if (overlap(sout, s) || overlap(sst, s)) return SSM_ERR_ALIAS;
+  if (overlap(sout, sst)) return SSM_ERR_ALIAS;
+  return SSM_OK;
+}
+
+int ssm_selective_scan_fwd(const ssm_scan_args* a, void* stream) {
+  const int st = ssm_validate_scan(a);
+  if (st != SSM_OK) return st;
+  if (a->batch == 0 || a->dim == 0) return SSM_OK;
+  if (ssm::launch_scan_fwd(*a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SSM_ERR_HIP;
+  return SSM_OK;
+}
+
+int ssm_selective_state_update(const ssm_update_args* a, void* stream) {
+  const int st = ssm_validate_update(a);
+  if (st != SSM_OK) return st;
+  if (a->batch == 0 || a->dim == 0) return SSM_OK;
+  if (ssm::launch_state_update(*a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SSM_ERR_HIP;
+  return SSM_OK;
+}
+
+}  // extern "C"
