@@ -57,7 +57,8 @@ typedef enum ssm_status {
   SSM_ERR_DTYPE = 4,       /* io_dtype is not SSM_F32 / SSM_BF16               */
   SSM_ERR_ALIGN = 5,       /* pointer not aligned to its element size          */
   SSM_ERR_ALIAS = 6,       /* an output overlaps an input it must not overlap  */
-  SSM_ERR_UNSUPPORTED = 7, /* valid but not built: dstate != 16                */
+  SSM_ERR_UNSUPPORTED = 7, /* valid but not built: dstate != 16, or seqlen too
+                              large for 32-bit token indices (>= 2^31 - 64)    */
   SSM_ERR_HIP = 8          /* the HIP runtime rejected the launch              */
 } ssm_status;
 
@@ -78,9 +79,14 @@ typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  *   delta_softplus   : nonzero applies softplus to delta + bias.
  * Sizes: batch, dim, seqlen >= 0 (zero sizes are a no-op, except that
  * seqlen == 0 with last_state set copies h0, or zeros, into last_state);
- * dstate must be 16.
+ * dstate must be 16; seqlen must be below 2^31 - 64.
  * Aliasing: out must not overlap u, delta, z, B or C; last_state must not
- * overlap any input except that it may be exactly h0 (in-place carry). */
+ * overlap any input except that it may be exactly h0 (in-place carry).
+ * Workspace: device scratch owned by the caller, 4-byte aligned, of at least
+ * ssm_scan_workspace_size() bytes, not overlapping any tensor.  The library
+ * uses it to cut long sequences with few channels into segments scanned in
+ * parallel; with workspace NULL or too small the scan still runs, correctly,
+ * as a single segment per sequence.  Its contents are scratch on return. */
 typedef struct ssm_scan_args {
   int64_t batch, dim, seqlen, dstate;
   int32_t io_dtype;       /* ssm_dtype */
@@ -96,6 +102,7 @@ typedef struct ssm_scan_args {
   const float* h0;
   float* last_state;
   void* out;          int64_t out_batch_stride, out_dim_stride;
+  void* workspace;    size_t workspace_bytes;
 } ssm_scan_args;
 
 /* Arguments of the single-token decode update.
@@ -131,6 +138,10 @@ int ssm_abi_version(void);
 /* sizeof the argument structs, for bindings that mirror them. */
 size_t ssm_scan_args_size(void);
 size_t ssm_update_args_size(void);
+
+/* Workspace bytes the scan can use for this argument block (0 when it would
+ * run single-segment anyway).  Reads only sizes; pure host code. */
+size_t ssm_scan_workspace_size(const ssm_scan_args* args);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* ssm_status_string(int status);

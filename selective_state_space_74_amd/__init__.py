@@ -48,7 +48,8 @@ class ScanArgs(ctypes.Structure):
                 ("C", _P), ("C_batch_stride", _I64), ("C_state_stride", _I64),
                 ("A", _P), ("A_dim_stride", _I64), ("A_state_stride", _I64),
                 ("D", _P), ("delta_bias", _P), ("h0", _P), ("last_state", _P),
-                ("out", _P), ("out_batch_stride", _I64), ("out_dim_stride", _I64)]
+                ("out", _P), ("out_batch_stride", _I64), ("out_dim_stride", _I64),
+                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class UpdateArgs(ctypes.Structure):
@@ -92,6 +93,8 @@ def lib():
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.POINTER(T)]
+        L.ssm_scan_workspace_size.restype = ctypes.c_size_t
+        L.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs)]
         L.ssm_selective_scan_fwd.restype = ctypes.c_int
         L.ssm_selective_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _P]
         L.ssm_selective_state_update.restype = ctypes.c_int
@@ -115,6 +118,10 @@ def validate_scan(args: ScanArgs) -> int:
 
 def validate_update(args: UpdateArgs) -> int:
     return lib().ssm_validate_update(ctypes.byref(args))
+
+
+def scan_workspace_size(args: ScanArgs) -> int:
+    return lib().ssm_scan_workspace_size(ctypes.byref(args))
 
 
 def scan_fwd_raw(args: ScanArgs, stream: int = 0) -> int:
@@ -173,8 +180,13 @@ def _stream(stream):
 
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
-                       h0=None, return_last_state=False, out=None, last_state=None, stream=None):
-    """Prefill selective scan on the GPU (see the module docstring)."""
+                       h0=None, return_last_state=False, out=None, last_state=None, stream=None,
+                       workspace=None):
+    """Prefill selective scan on the GPU (see the module docstring).
+
+    `workspace` (optional): a device tensor reused across calls; when None,
+    one of the size the library asks for is allocated through torch; False
+    passes no workspace (the scan then runs each sequence as one segment)."""
     torch = _torch()
     if u.dim() != 3:
         raise ValueError("u must be (batch, dim, L)")
@@ -222,6 +234,12 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     a.D, a.delta_bias, a.h0 = _ptr(D), _ptr(delta_bias), _ptr(h0)
     a.last_state = _ptr(last_state)
     a.out, (a.out_batch_stride, a.out_dim_stride) = _ptr(out), out.stride()[:2]
+    need = scan_workspace_size(a) if workspace is not False else 0
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        _check_dev("workspace", workspace, dev)
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     st = scan_fwd_raw(a, _stream(stream))
     if st != 0:
         raise SSMError(st, "ssm_selective_scan_fwd")

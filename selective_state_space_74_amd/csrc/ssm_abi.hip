@@ -35,6 +35,9 @@ bool misaligned(const void* p, int64_t align) {
 
 int64_t io_size(int32_t dt) { return dt == SSM_BF16 ? 2 : 4; }
 
+// Token indices are 32-bit inside the scan kernel.
+constexpr int64_t kMaxSeqlen = (int64_t{1} << 31) - 64;
+
 }  // namespace
 
 extern "C" {
@@ -42,6 +45,11 @@ extern "C" {
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 size_t ssm_scan_args_size(void) { return sizeof(ssm_scan_args); }
 size_t ssm_update_args_size(void) { return sizeof(ssm_update_args); }
+
+size_t ssm_scan_workspace_size(const ssm_scan_args* a) {
+  if (!a || a->dstate != 16 || a->seqlen > kMaxSeqlen) return 0;
+  return ssm::scan_workspace_bytes(*a);
+}
 
 const char* ssm_status_string(int status) {
   switch (status) {
@@ -52,7 +60,7 @@ const char* ssm_status_string(int status) {
     case SSM_ERR_DTYPE: return "io_dtype must be SSM_F32 or SSM_BF16";
     case SSM_ERR_ALIGN: return "pointer not aligned to its element size";
     case SSM_ERR_ALIAS: return "an output overlaps an input";
-    case SSM_ERR_UNSUPPORTED: return "unsupported configuration (dstate must be 16)";
+    case SSM_ERR_UNSUPPORTED: return "unsupported configuration (dstate must be 16, seqlen < 2^31 - 64)";
     case SSM_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
   }
@@ -63,6 +71,7 @@ int ssm_validate_scan(const ssm_scan_args* a) {
   if (a->batch < 0 || a->dim < 0 || a->seqlen < 0 || a->dstate < 1) return SSM_ERR_SHAPE;
   if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (a->dstate != 16) return SSM_ERR_UNSUPPORTED;
+  if (a->seqlen > kMaxSeqlen) return SSM_ERR_UNSUPPORTED;
   if (a->batch == 0 || a->dim == 0) return SSM_OK;
   const int64_t B = a->batch, Dm = a->dim, L = a->seqlen, N = a->dstate;
   const int64_t esz = io_size(a->io_dtype);
@@ -80,7 +89,7 @@ int ssm_validate_scan(const ssm_scan_args* a) {
       return SSM_ERR_ALIGN;
   }
   if (misaligned(a->A, 4) || misaligned(a->D, 4) || misaligned(a->delta_bias, 4) ||
-      misaligned(a->h0, 4) || misaligned(a->last_state, 4))
+      misaligned(a->h0, 4) || misaligned(a->last_state, 4) || misaligned(a->workspace, 4))
     return SSM_ERR_ALIGN;
 
   const Span su = span3(a->u, B, a->u_batch_stride, Dm, a->u_dim_stride, L, esz);
@@ -102,6 +111,10 @@ int ssm_validate_scan(const ssm_scan_args* a) {
     if (overlap(sls, inputs[i])) return SSM_ERR_ALIAS;
   if (overlap(sls, sout)) return SSM_ERR_ALIAS;
   if (overlap(sls, sh0) && a->last_state != a->h0) return SSM_ERR_ALIAS;
+  const Span sws = span1(a->workspace, static_cast<int64_t>(a->workspace_bytes), 1);
+  for (const Span& s : inputs)
+    if (overlap(sws, s)) return SSM_ERR_ALIAS;
+  if (overlap(sws, sout) || overlap(sws, sls)) return SSM_ERR_ALIAS;
   return SSM_OK;
 }
 

@@ -10,6 +10,7 @@ namespace ssm {
 
 // Launches; arguments already validated by the ABI layer.
 hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream);
+size_t scan_workspace_bytes(const ssm_scan_args& a);
 hipError_t launch_state_update(const ssm_update_args& a, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
@@ -39,15 +40,25 @@ template <> struct io<uint16_t> {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// softplus(x) = log(1 + e^x); above 20 the correction e^-x < 2.1e-9 is below
-// fp32 resolution of x, so x itself is returned.
+constexpr float kLn2 = 0.6931471805599453f;
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|), on the hardware
+// exp2/log2/rcp.  log1p(y) for y in (0, 1] uses the exact-rounding correction
+// log1p(y) = log(1 + y) * y / ((1 + y) - 1), which keeps full relative accuracy
+// for small y (Delta around 1e-3 sits there); when 1 + y rounds to 1 the
+// answer is y itself.
 __device__ __forceinline__ float softplus_f32(float x) {
-  return x > 20.0f ? x : log1pf(expf(x));
+  const float y = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+  const float u = 1.0f + y;
+  const float d = u - 1.0f;
+  const float l = __builtin_amdgcn_logf(u) * kLn2;
+  const float lp = d == 0.0f ? y : l * (y * __builtin_amdgcn_rcpf(d));
+  return fmaxf(x, 0.0f) + lp;
 }
 
-// silu(z) = z * sigmoid(z)
+// silu(z) = z * sigmoid(z) = z / (1 + 2^(-z log2 e))
 __device__ __forceinline__ float silu_f32(float z) {
-  return z / (1.0f + expf(-z));
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
