@@ -113,7 +113,8 @@ typedef struct ssm_scan_args {
  *   B, C             : (batch, dstate), state stride 1.
  *   A                : (dim, dstate) fp32, state stride 1.
  *   D, dt_bias       : (dim) fp32, contiguous, NULL means 0.
- * Sizes: batch, dim >= 0 (zero is a no-op); dstate must be 16.
+ * Sizes: batch, dim >= 0 (zero is a no-op); dstate must be 16; batch at most
+ * 65535.
  * Aliasing: out must not overlap state or any input; state must not overlap
  * any input. */
 typedef struct ssm_update_args {

@@ -123,6 +123,7 @@ int ssm_validate_update(const ssm_update_args* a) {
   if (a->batch < 0 || a->dim < 0 || a->dstate < 1) return SSM_ERR_SHAPE;
   if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (a->dstate != 16) return SSM_ERR_UNSUPPORTED;
+  if (a->batch > 65535) return SSM_ERR_UNSUPPORTED;
   if (a->batch == 0 || a->dim == 0) return SSM_OK;
   if (!a->state || !a->x || !a->dt || !a->B || !a->C || !a->A || !a->out) return SSM_ERR_NULL;
   const int64_t strides[] = {a->state_batch_stride, a->state_dim_stride, a->x_batch_stride,
