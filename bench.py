@@ -200,8 +200,9 @@ def cpu_baseline(cfg, si, max_s=30.0):
 
 
 def profile_run(cfg, torch, ssm, si, launches=10):
-    """Headline scan launches plus a plain copy kernel of known size (reads
-    1 GiB, writes 1 GiB) so that FETCH_SIZE / WRITE_SIZE can be scaled."""
+    """Headline scan launches, decode steps on the decode workload, and a plain
+    copy kernel of known size (reads 1 GiB, writes 1 GiB) so that the
+    FETCH_SIZE / WRITE_SIZE counters can be scaled to bytes."""
     t = si.to_torch(si.scan_inputs_for(cfg), "cuda")
     out = torch.empty_like(t["u"])
     last = torch.empty((cfg.batch, cfg.dim, cfg.dstate), device="cuda")
@@ -209,6 +210,16 @@ def profile_run(cfg, torch, ssm, si, launches=10):
         ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                                delta_bias=t["delta_bias"], out=out, last_state=last)
     torch.cuda.synchronize()
+    del t, out, last
+    dc = si.DECODE_CONFIG
+    d = si.decode_inputs_device(dc, steps=launches, device="cuda")
+    state = torch.zeros((dc.batch, dc.dim, dc.dstate), device="cuda")
+    dout = torch.empty((dc.batch, dc.dim), dtype=d["x"].dtype, device="cuda")
+    for s in range(launches):
+        ssm.selective_state_update(state, d["x"][s], d["dt"][s], d["A"], d["B"][s], d["C"][s],
+                                   D=d["D"], z=d["z"][s], dt_bias=d["dt_bias"], out=dout)
+    torch.cuda.synchronize()
+    del d, state, dout
     n = (1 << 30) // 4
     src = torch.ones(n, device="cuda")
     dst = torch.empty_like(src)
@@ -216,7 +227,9 @@ def profile_run(cfg, torch, ssm, si, launches=10):
         torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
     log(f"[profile] {launches} scan launches ({scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, 4)}"
-        f" algorithmic bytes each) and {launches} copy launches (1 GiB read + 1 GiB write)")
+        f" algorithmic bytes each), {launches} decode steps "
+        f"({decode_bytes(dc.batch, dc.dim, dc.dstate, 2)} bytes each), {launches} copy launches "
+        f"(1 GiB read + 1 GiB write)")
 
 
 def main():
