@@ -57,8 +57,10 @@ typedef enum ssm_status {
   SSM_ERR_DTYPE = 4,       /* io_dtype is not SSM_F32 / SSM_BF16               */
   SSM_ERR_ALIGN = 5,       /* pointer not aligned to its element size          */
   SSM_ERR_ALIAS = 6,       /* an output overlaps an input it must not overlap  */
-  SSM_ERR_UNSUPPORTED = 7, /* valid but not built: dstate != 16, or seqlen too
-                              large for 32-bit token indices (>= 2^31 - 64)    */
+  SSM_ERR_UNSUPPORTED = 7, /* valid but not built: dstate != 16, seqlen too
+                              large for 32-bit token indices (>= 2^31 - 64),
+                              or row spans past the 32-bit windows (see
+                              ssm_scan_args)                                   */
   SSM_ERR_HIP = 8          /* the HIP runtime rejected the launch              */
 } ssm_status;
 
@@ -79,7 +81,12 @@ typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  *   delta_softplus   : nonzero applies softplus to delta + bias.
  * Sizes: batch, dim, seqlen >= 0 (zero sizes are a no-op, except that
  * seqlen == 0 with last_state set copies h0, or zeros, into last_state);
- * dstate must be 16; seqlen must be below 2^31 - 64.
+ * dstate must be 16; seqlen must be below 2^31 - 64.  The kernel reads each
+ * group of 4 channels, and the 16 state rows of B and C, through 32-bit byte
+ * windows: (3 * dim_stride + seqlen) * element size for u, delta, z and out,
+ * and (15 * state_stride + seqlen) * element size for B and C, must stay
+ * below 2^32 (for contiguous fp32 B/C: seqlen below 2^26).  Larger spans
+ * return SSM_ERR_UNSUPPORTED.
  * Aliasing: out must not overlap u, delta, z, B or C; last_state must not
  * overlap any input except that it may be exactly h0 (in-place carry).
  * Workspace: device scratch owned by the caller, 4-byte aligned, of at least

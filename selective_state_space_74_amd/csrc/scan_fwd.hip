@@ -6,20 +6,27 @@
 //   h_t[n]  = exp(Delta_t A[d,n]) h_{t-1}[n] + Delta_t B[b,n,t] u_t
 //   out_t   = (sum_n C[b,n,t] h_t[n] + D[d] u_t) * silu(z_t)
 //
-// Work decomposition.  One workgroup = 16 channels of one batch row x 16
-// states (256 lanes, 4 wavefronts), walking its token range in blocks of 16:
-//   scan role   lane (n = tid/16, c = tid%16) owns the fp32 state h[n] of
-//               channel d0+c.  The state never leaves the register file.
-//   owner role  lane (c = tid/16, j = tid%16) owns token t0+j of channel d0+c:
-//               it loads u/delta/z, computes Delta and Delta*u once, and one
-//               block later reduces the readout over n, applies the skip term
-//               and the gate, and stores out.
-// B and C depend on (b, n, t) only, so each 16-lane row (one state n) needs the
-// same 16 values per block: lane j of the row loads token t0+j and a DPP
-// row_newbcast hands it to every lane of the row inside the consuming VALU op.
-// Delta and Delta*u travel from owners to scan lanes through LDS, and so do
-// the per-state readout partials on their way back to the owners.  The state
-// recurrence is sequential per lane: one exp per (t, n), nothing recomputed.
+// Work decomposition.  A workgroup is 4 wavefronts; a wavefront is 4
+// channels of one batch row, each a 16-lane row whose lane n holds the fp32
+// state h[n] in a register for the whole sequence.  The workgroup walks its
+// token range in blocks of 16:
+//   owner role  lane (row c, col j) loads u/delta/z of token t0+j of channel c
+//               and computes Delta and Delta*u once; a DPP row_newbcast:j
+//               inside the consuming VALU op hands them to the 16 state lanes
+//               of the same row.
+//   stage role  B and C depend on (b, n, t) only.  Every 2 blocks the
+//               workgroup loads the next 16 x 32 tile of each (one state row
+//               per 16 lanes, coalesced) into a double-buffered LDS tile and
+//               synchronises once; every lane then reads back the 16 values
+//               of its state n for each block.
+//   readout     each state lane leaves C_n h_n per token in its wavefront's
+//               LDS; one block later the owner of the token sums the 16
+//               partials, adds D*u, applies the gate and stores.
+// Apart from the B/C tile, LDS is private to a wavefront, whose LDS operations
+// complete in issue order, so the per-block exchange needs no barrier.  Every
+// global access goes through a buffer descriptor whose window ends where the
+// wavefront's data ends: lanes of a partial last block that reach past it
+// read zero instead of touching memory, so no lane clamps its address.
 //
 // Long sequences with few channels.  The recurrence is linear in the state
 // (Mamba paper notes, sections 5.3/5.4: a long input can be cut into chunks
@@ -39,12 +46,20 @@
 namespace ssm {
 namespace {
 
-constexpr int kN = 16;              // states per channel = rows of the workgroup
-constexpr int kCh = 16;             // channels per workgroup = lanes per row
+constexpr int kN = 16;              // states per channel = lanes per row
+constexpr int kRows = 4;            // channels per wavefront
+constexpr int kWaves = 4;           // wavefronts per workgroup
+constexpr int kCh = kRows * kWaves; // channels per workgroup
+constexpr int kThreads = 64 * kWaves;
 constexpr int kT = 16;              // tokens per block
-constexpr int kThreads = kN * kCh;  // 256
-constexpr int kPitch = 20;          // LDS row pitch in floats: b128 accesses hit distinct banks
-constexpr int kAggStride = kN + 1;  // floats per (row, segment) aggregate: b[16], S
+constexpr int kGB = 2;              // blocks per B/C staging group
+constexpr int kGT = kT * kGB;       // tokens per group
+static_assert(4 % kGB == 0, "the steady-state loop runs four blocks at a time");
+constexpr int kGPitch = kGT + 4;    // LDS pitch (floats) of one state's group of B / C
+constexpr int kPitch = 20;          // LDS pitch (floats) of one state's readout partials
+constexpr int kPartRow = kN * kPitch + 16;  // floats per channel of readout partials
+constexpr int kAggStride = kN + 1;  // floats per (channel, segment) aggregate: b[16], S
+constexpr int kRsrcWord3 = 0x00020000;      // raw buffer, 32-bit dwords (gfx9 family)
 
 enum class Mode { kScan, kAggregate };
 
@@ -64,227 +79,340 @@ struct ScanParams {
   int64_t usb, usd, dsb, dsd, zsb, zsd, Bsb, Bsn, Csb, Csn, Asd, Asn, osb, osd;
   int64_t batch, dim;
   int L;
-  int seg_len;     // tokens per segment (multiple of kT)
+  int seg_len;     // tokens per segment (multiple of kGT)
   int nseg;        // segments per sequence
-  int64_t dgroups; // ceil(dim / kCh)
-  int softplus;
+  int64_t cgroups; // ceil(dim / kCh)
 };
 
-// Raw inputs of one block as one lane sees them: the owner role's u, delta, z
-// for its (channel, token) and the scan role's B, C for (its state, token).
-struct BlockIn {
-  float u, dt, z, b, c;
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kSize = 4;
+  __device__ static __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  __device__ static __forceinline__ float f32(uint32_t v) { return __uint_as_float(v); }
+  __device__ static __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+  }
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int kSize = 2;
+  __device__ static __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  }
+  __device__ static __forceinline__ float f32(uint32_t v) { return __uint_as_float(v << 16); }
+  __device__ static __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
+  }
 };
 
-// Per-lane constants and pointers shared by every block.
-template <typename T>
-struct Lane {
-  const T* u;   // owner row of u (channel clamped into range)
-  const T* dl;  // owner row of delta
-  const T* z;   // owner row of z (u's row when there is no gate: loaded, never used)
-  const T* B;   // scan row of B (state n)
-  const T* C;   // scan row of C
-  T* out;       // owner row of out
-  float a2;     // A[d, n] * log2(e)
-  float bias, Dd;
-  bool vO;      // owner channel exists
-  bool gate;    // z given
+// A wavefront-uniform byte window [base, base + bytes) of one tensor.  Host
+// validation keeps every window below 4 GiB, so all offsets are 32-bit.
+struct Window {
+  const char* base;
+  uint32_t bytes;
+  // The window moved `skip` bytes forward; skip never exceeds bytes (block
+  // starts stay inside the sequence).
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t at(uint32_t skip) const {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + skip), 0,
+                                             static_cast<int>(bytes - skip), kRsrcWord3);
+  }
 };
 
-// Pipeline of one workgroup over blocks of kT tokens of its segment
-// [t_beg, t_end).  Block j's raw inputs are loaded two iterations before the
-// scan uses them, its step sizes are published one iteration before, and it is
-// finished (readout, skip, gate, store) one iteration after its scan.  Four
-// register buffers rotate with the iteration index; the loop is unrolled by
-// four so every buffer is a fixed set of registers and no load result is
-// copied while still in flight.
-template <typename T, Mode M>
-struct Pipe {
+// Owner role raw inputs of one block: token t0 + col of the lane's channel
+// (bit patterns, widened where they are used).
+struct Raw {
+  uint32_t u, dt, z;
+};
+
+// Stage role raw inputs of one group: B and C of state 4w + row at tokens
+// tg + col + 16 i.
+struct GroupRaw {
+  uint32_t b[kGB], c[kGB];
+};
+
+template <typename T, Mode M, bool kSoftplus>
+struct Wave {
   const ScanParams& p;
-  const Lane<T>& ln;
-  int row, col;
-  int t_beg, t_end;
-  int nblk;
-  float (*s_dl)[kCh][kPitch];
-  float (*s_du)[kCh][kPitch];
-  float (*s_part)[kN][kCh][kPitch];
-  double* ssum;  // aggregate mode: this owner lane's running sum of Delta
+  int wave, row, col;
+  int t_beg, t_end, nblk, ngrp;
+  Window wu, wdt, wz, wB, wC, wout;
+  uint32_t ou, odt, oz, oB, oC, oout;  // per-lane byte offsets inside the windows
+  float a2, bias, Dd;
+  float (*sB)[kN][kGPitch];   // [2][kN][kGPitch], shared by the workgroup
+  float (*sC)[kN][kGPitch];
+  float (*sP)[kPartRow];      // this wavefront's [kRows][kPartRow]
 
-  __device__ __forceinline__ int tok(int k) const { return t_beg + k * kT + col; }
+  static constexpr int E = Elem<T>::kSize;
 
-  __device__ __forceinline__ BlockIn load(int k) const {
-    // Clamped token index: every address is in bounds; values of tokens past
-    // the segment end are masked where they are consumed.
-    const int t = min(tok(k), t_end - 1);
-    BlockIn in;
-    in.b = io<T>::load(ln.B + t);
-    in.c = M == Mode::kScan ? io<T>::load(ln.C + t) : 0.0f;
-    in.u = io<T>::load(ln.u + t);
-    in.dt = io<T>::load(ln.dl + t);
-    in.z = M == Mode::kScan ? io<T>::load(ln.z + t) : 0.0f;
-    return in;
+  __device__ __forceinline__ uint32_t skip(int k) const {
+    return static_cast<uint32_t>(t_beg + k * kT) * E;
   }
 
-  __device__ __forceinline__ bool owns(int k) const { return ln.vO && tok(k) < t_end; }
-
-  // Owner: Delta and Delta*u of block k into LDS slot k & 1 (zero past the end).
-  __device__ __forceinline__ void publish(int k, const BlockIn& in) const {
-    const float x = in.dt + ln.bias;
-    const float dl = p.softplus ? softplus_f32(x) : x;
-    const bool own = owns(k);
-    s_dl[k & 1][row][col] = own ? dl : 0.0f;
-    s_du[k & 1][row][col] = own ? dl * in.u : 0.0f;
-    if (M == Mode::kAggregate && own) *ssum += static_cast<double>(dl);
+  // Owner raw inputs of block k; blocks past the last one reload the last one
+  // (the pipeline prefetches two blocks ahead and never uses those).
+  __device__ __forceinline__ Raw load(int k) const {
+    Raw r;
+    const uint32_t s = skip(min(k, nblk - 1));
+    r.u = Elem<T>::load(wu.at(s), ou);
+    r.dt = Elem<T>::load(wdt.at(s), odt);
+    // without a gate the z window is u's: the load is a cache hit, never used
+    r.z = M == Mode::kScan ? Elem<T>::load(wz.at(s), oz) : 0u;
+    return r;
   }
 
-  // Owner: readout of block k from the partials, skip term, gate, store.
-  __device__ __forceinline__ void finish(int k, const BlockIn& in, const float (&part)[kN]) const {
-    float y = 0.0f;
+  // Stage raw inputs of group g (clamped to the last group like load()).
+  __device__ __forceinline__ GroupRaw load_group(int g) const {
+    GroupRaw r;
+    const uint32_t s = skip(min(g, ngrp - 1) * kGB);
+    const __amdgpu_buffer_rsrc_t rb = wB.at(s);
 #pragma unroll
-    for (int n = 0; n < kN; ++n) y += part[n];
-    y = fmaf(ln.Dd, in.u, y);
-    if (ln.gate) y *= silu_f32(in.z);
-    if (owns(k)) io<T>::store(ln.out + tok(k), y);
+    for (int i = 0; i < kGB; ++i) r.b[i] = Elem<T>::load(rb, oB + i * kT * E);
+    if (M == Mode::kScan) {
+      const __amdgpu_buffer_rsrc_t rc = wC.at(s);
+#pragma unroll
+      for (int i = 0; i < kGB; ++i) r.c[i] = Elem<T>::load(rc, oC + i * kT * E);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kGB; ++i) r.c[i] = 0u;
+    }
+    return r;
+  }
+
+  // Stage role: group g's B (and C) into LDS buffer g & 1.  B of tokens past
+  // the end is zeroed so that a non-finite value read from beyond a row
+  // cannot reach h.
+  __device__ __forceinline__ void stage(int g, const GroupRaw& r) const {
+    const int st = kRows * wave + row;
+    const int t = t_beg + g * kGT + col;
+#pragma unroll
+    for (int i = 0; i < kGB; ++i) {
+      const float bv = Elem<T>::f32(r.b[i]);
+      sB[g & 1][st][col + i * kT] = t + i * kT < t_end ? bv : 0.0f;
+      if (M == Mode::kScan) sC[g & 1][st][col + i * kT] = Elem<T>::f32(r.c[i]);
+    }
+  }
+
+  // Owner role: readout of block k (y = the sum of its 16 partials), skip
+  // term, gate, store.  Rows past dim repeat the last channel bit for bit, so in full
+  // blocks every lane may store (duplicates write identical values); with
+  // kMask only tokens before the end are stored.
+  template <bool kMask>
+  __device__ __forceinline__ void finish(int k, const Raw& r, float y) const {
+    const float uv = Elem<T>::f32(r.u);
+    y = fmaf(Dd, uv, y);
+    const float g = silu_f32(Elem<T>::f32(r.z));
+    y *= p.z ? g : 1.0f;  // a select, not a branch
+    const __amdgpu_buffer_rsrc_t ro = wout.at(skip(k));
+    if (!kMask || t_beg + k * kT + col < t_end) Elem<T>::store(ro, oout, y);
   }
 
   // Iteration k.  Buffers: P = block k-1 (finish), Q = block k (scan),
-  // R = block k+1 (publish), S = block k+2 (load target).
-  __device__ __forceinline__ void iter(int k, float& h, const BlockIn& P, const BlockIn& Q,
-                                       const BlockIn& R, BlockIn& S) const {
-    const int slot = k & 1;
-    // LDS reads first: this block's step sizes and the previous block's partials.
-    float dlr[kT], dur[kT], part[kN];
+  // S = block k+2 (load target); G holds the next group's B/C.
+  // kMask = false is the steady state, valid when blocks k-1 and k are full:
+  // it has no branch, so the scan's DPP broadcasts stay fused into the ops
+  // that use them.  kEnd (steady state only) marks the last block of a group,
+  // after which the next group is staged and the workgroup synchronises; in
+  // the masked form that is decided at run time.
+  template <bool kMask, bool kEnd>
+  __device__ __forceinline__ void iter(int k, float& h, double& ssum, const Raw& P, const Raw& Q,
+                                       Raw& S, GroupRaw& G) const {
+    // LDS reads first: B/C of this block and the previous block's partials.
+    const int buf = (k / kGB) & 1;
+    const int tb = (k % kGB) * kT;
+    float bv[kT], cv[kT], part[kN];
 #pragma unroll
     for (int q = 0; q < kT / 4; ++q) {
-      const float4 a = *reinterpret_cast<const float4*>(&s_dl[slot][col][4 * q]);
-      const float4 c = *reinterpret_cast<const float4*>(&s_du[slot][col][4 * q]);
-      dlr[4 * q + 0] = a.x; dlr[4 * q + 1] = a.y; dlr[4 * q + 2] = a.z; dlr[4 * q + 3] = a.w;
-      dur[4 * q + 0] = c.x; dur[4 * q + 1] = c.y; dur[4 * q + 2] = c.z; dur[4 * q + 3] = c.w;
+      const float4 x = *reinterpret_cast<const float4*>(&sB[buf][col][tb + 4 * q]);
+      bv[4 * q] = x.x; bv[4 * q + 1] = x.y; bv[4 * q + 2] = x.z; bv[4 * q + 3] = x.w;
+      if (M == Mode::kScan) {
+        const float4 y = *reinterpret_cast<const float4*>(&sC[buf][col][tb + 4 * q]);
+        cv[4 * q] = y.x; cv[4 * q + 1] = y.y; cv[4 * q + 2] = y.z; cv[4 * q + 3] = y.w;
+      }
     }
+    float ysum = 0.0f;
     if (M == Mode::kScan) {
-      // unconditional: at k = 0 the values are never used
+      // unconditional: at k = 0 the value is never used; summed right away so
+      // that one register, not sixteen, lives across the scan
 #pragma unroll
-      for (int n = 0; n < kN; ++n) part[n] = s_part[slot ^ 1][n][row][col];
+      for (int n = 0; n < kN; ++n) part[n] = sP[row][n * kPitch + col];
+#pragma unroll
+      for (int n = 0; n < kN; ++n) ysum += part[n];
     }
-    S = load(k + 2);   // unconditional: past the end the clamped index stays in bounds
+    S = load(k + 2);
 
-    // scan role: 16 sequential steps of this lane's state
-    const float bv = tok(k) < t_end ? Q.b : 0.0f;
-    const float cv = Q.c;
-    float pk[kT];
+    // owner role: Delta and Delta*u of this block (zero past the end)
+    const float x = Elem<T>::f32(Q.dt) + bias;
+    float dl = kSoftplus ? softplus_f32(x) : x;
+    float du = dl * Elem<T>::f32(Q.u);
+    if (kMask) {
+      const bool own = t_beg + k * kT + col < t_end;
+      dl = own ? dl : 0.0f;
+      du = own ? du : 0.0f;
+    }
+    if (M == Mode::kAggregate) ssum += static_cast<double>(dl);
+
+    // state role: 16 sequential steps of this lane's state; the readout
+    // partials C_n h_n go to LDS four tokens at a time
+    float pk[4];
     static_for<0, kT>([&](auto J) {
       constexpr int j = decltype(J)::value;
-      const float e = __builtin_amdgcn_exp2f(dlr[j] * ln.a2);   // Abar = exp(Delta A)
-      const float w = dur[j] * row_bcast<j>(bv);               // Bbar u = Delta u B
+      const float e = __builtin_amdgcn_exp2f(row_bcast<j>(dl) * a2);  // Abar = exp(Delta A)
+      const float w = row_bcast<j>(du) * bv[j];                       // Bbar u = Delta u B
       h = fmaf(e, h, w);
-      if (M == Mode::kScan) pk[j] = row_bcast<j>(cv) * h;      // C_n h_n
+      if (M == Mode::kScan) {
+        pk[j % 4] = cv[j] * h;                                        // C_n h_n
+        if (j % 4 == 3)
+          *reinterpret_cast<float4*>(&sP[row][col * kPitch + j - 3]) =
+              make_float4(pk[0], pk[1], pk[2], pk[3]);
+      }
     });
     if (M == Mode::kScan) {
-#pragma unroll
-      for (int q = 0; q < kT / 4; ++q)
-        *reinterpret_cast<float4*>(&s_part[slot][row][col][4 * q]) =
-            make_float4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]);
-      if (k > 0) finish(k - 1, P, part);
+      if (!kMask) finish<false>(k - 1, P, ysum);
+      else if (k > 0) finish<true>(k - 1, P, ysum);
     }
-    if (k + 1 < nblk) publish(k + 1, R);
-    __syncthreads();
+    // Compiler-only fence: keep this block's LDS traffic in program order with
+    // the next block's (the hardware already keeps one wavefront's in order).
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    if (kMask ? (k % kGB == kGB - 1 && k + 1 < nblk) : kEnd) {
+      // Group (k+1)/kGB into the other buffer.  Every wavefront finished
+      // reading that buffer before the previous barrier.
+      const int g = k / kGB + 1;
+      stage(g, G);
+      __syncthreads();
+      G = load_group(g + 1);
+    }
   }
 };
 
-template <typename T, Mode M>
+template <typename T, Mode M, bool kSoftplus>
 __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
-  // Double-buffered by block parity, so one barrier per block is enough.
-  __shared__ __align__(16) float s_dl[2][kCh][kPitch];
-  __shared__ __align__(16) float s_du[2][kCh][kPitch];
-  __shared__ __align__(16) float s_part[M == Mode::kScan ? 2 : 1][kN][kCh][kPitch];
-  __shared__ double s_sum[kCh][kCh];
+  __shared__ __align__(16) float sB[2][kN][kGPitch];
+  __shared__ __align__(16) float sC[M == Mode::kScan ? 2 : 1][kN][kGPitch];
+  __shared__ __align__(16) float sP[M == Mode::kScan ? kWaves : 1][kRows][kPartRow];
+  __shared__ double sSum[M == Mode::kScan ? 1 : kWaves][kRows][kT];
 
-  const int tid = threadIdx.x;
-  const int row = tid >> 4;
-  const int col = tid & 15;
-  // blockIdx.x = (b * dgroups + dg) * nseg_grid + g; the aggregate pass skips
+  // wavefront index, made visibly uniform so that windows stay in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = (threadIdx.x >> 4) & 3;
+  const int col = threadIdx.x & 15;
+  // blockIdx.x = (b * cgroups + cg) * nseg_grid + g; the aggregate pass skips
   // the last segment (its end state is never needed by a later segment)
   const int nseg_grid = M == Mode::kScan ? p.nseg : p.nseg - 1;
   const int g = static_cast<int>(blockIdx.x % nseg_grid);
-  const int64_t bd = blockIdx.x / nseg_grid;
-  const int64_t b = bd / p.dgroups;
-  const int64_t d0 = (bd % p.dgroups) * kCh;
-  const int t_beg = g * p.seg_len;
-  const int t_end = min(p.L, t_beg + p.seg_len);
-  const int nblk = (t_end - t_beg + kT - 1) / kT;
+  const int64_t bc = blockIdx.x / nseg_grid;
+  const int64_t b = bc / p.cgroups;
+  const int64_t d = (bc % p.cgroups) * kCh + kRows * wave + row;
+  const bool vrow = d < p.dim;
+  // rows past dim repeat the last channel exactly (same inputs, same state)
+  const int64_t dc = vrow ? d : p.dim - 1;
+  // this wavefront's first and last (clamped) rows
+  const int64_t dw0 = std::min<int64_t>((bc % p.cgroups) * kCh + kRows * wave, p.dim - 1);
+  const int64_t dw3 = std::min<int64_t>(dw0 + kRows - 1, p.dim - 1);
 
-  Lane<T> ln;
-  // scan role: state n = row of channel d0 + col
-  const int64_t dS = d0 + col;
-  const bool vS = dS < p.dim;
-  const int64_t dSc = vS ? dS : p.dim - 1;
-  ln.a2 = p.A[dSc * p.Asd + row * p.Asn] * kLog2e;
-  ln.B = static_cast<const T*>(p.B) + b * p.Bsb + row * p.Bsn;
-  ln.C = static_cast<const T*>(p.C) + b * p.Csb + row * p.Csn;
-  // owner role: token t0 + col of channel d0 + row
-  const int64_t dO = d0 + row;
-  ln.vO = dO < p.dim;
-  const int64_t dOc = ln.vO ? dO : p.dim - 1;
-  ln.bias = p.bias ? p.bias[dOc] : 0.0f;
-  ln.Dd = p.D ? p.D[dOc] : 0.0f;
-  ln.u = static_cast<const T*>(p.u) + b * p.usb + dOc * p.usd;
-  ln.dl = static_cast<const T*>(p.delta) + b * p.dsb + dOc * p.dsd;
-  ln.gate = p.z != nullptr;
-  ln.z = ln.gate ? static_cast<const T*>(p.z) + b * p.zsb + dOc * p.zsd : ln.u;
-  ln.out = static_cast<T*>(p.out) + b * p.osb + dOc * p.osd;
+  constexpr int E = Elem<T>::kSize;
+  Wave<T, M, kSoftplus> w{p};
+  w.wave = wave; w.row = row; w.col = col;
+  w.t_beg = g * p.seg_len;
+  w.t_end = std::min(p.L, w.t_beg + p.seg_len);
+  w.nblk = (w.t_end - w.t_beg + kT - 1) / kT;
+  w.ngrp = (w.nblk + kGB - 1) / kGB;
+
+  // Windows run from this wavefront's first row to the end of its last row.
+  auto rows_window = [&](const void* base, int64_t sb, int64_t sd, uint32_t& off) {
+    off = static_cast<uint32_t>(((dc - dw0) * sd + col) * E);
+    return Window{static_cast<const char*>(base) + (b * sb + dw0 * sd) * E,
+                  static_cast<uint32_t>(((dw3 - dw0) * sd + p.L) * E)};
+  };
+  w.wu = rows_window(p.u, p.usb, p.usd, w.ou);
+  w.wdt = rows_window(p.delta, p.dsb, p.dsd, w.odt);
+  if (p.z) {
+    w.wz = rows_window(p.z, p.zsb, p.zsd, w.oz);
+  } else {
+    w.wz = w.wu;
+    w.oz = w.ou;
+  }
+  w.wout = rows_window(p.out, p.osb, p.osd, w.oout);
+  // B/C: the workgroup's 16 state rows; this lane stages state 4 wave + row
+  const int st = kRows * wave + row;
+  w.oB = static_cast<uint32_t>((st * p.Bsn + col) * E);
+  w.wB = Window{static_cast<const char*>(p.B) + b * p.Bsb * E,
+                static_cast<uint32_t>(((kN - 1) * p.Bsn + p.L) * E)};
+  w.oC = static_cast<uint32_t>((st * p.Csn + col) * E);
+  w.wC = Window{static_cast<const char*>(p.C) + b * p.Csb * E,
+                static_cast<uint32_t>(((kN - 1) * p.Csn + p.L) * E)};
+
+  w.a2 = p.A[dc * p.Asd + col * p.Asn] * kLog2e;
+  w.bias = p.bias ? p.bias[dc] : 0.0f;
+  w.Dd = p.D ? p.D[dc] : 0.0f;
+  w.sB = sB; w.sC = sC; w.sP = sP[M == Mode::kScan ? wave : 0];
 
   // Initial state: zero for an aggregate segment; otherwise h0 (or zero) carried
   // through the aggregates of every earlier segment.
   float h = 0.0f;
   if (M == Mode::kScan) {
-    h = (vS && p.h0) ? p.h0[(b * p.dim + dS) * kN + row] : 0.0f;
+    h = p.h0 ? p.h0[(b * p.dim + dc) * kN + col] : 0.0f;
     if (g > 0) {
-      const float* ag = p.agg + ((b * p.dim + dSc) * (p.nseg - 1)) * kAggStride;
+      const float* ag = p.agg + ((b * p.dim + dc) * (p.nseg - 1)) * kAggStride;
       for (int i = 0; i < g; ++i) {
-        const float decay = __builtin_amdgcn_exp2f(ln.a2 * ag[i * kAggStride + kN]);
-        h = fmaf(decay, h, ag[i * kAggStride + row]);
+        const float decay = __builtin_amdgcn_exp2f(w.a2 * ag[i * kAggStride + kN]);
+        h = fmaf(decay, h, ag[i * kAggStride + col]);
       }
     }
   }
 
   double ssum = 0.0;
-  Pipe<T, M> pp{p, ln, row, col, t_beg, t_end, nblk, s_dl, s_du, s_part, &ssum};
-  // block j lives in buffer j % 4; iteration k loads block k + 2
-  BlockIn buf0 = pp.load(0), buf1 = pp.load(1), buf2 = buf0, buf3 = buf0;
-  pp.publish(0, buf0);
+  // group 0 staged before the loop, group 1 in flight; block j's owner inputs
+  // live in buffer j % 4 and iteration k loads block k + 2
+  GroupRaw grp = w.load_group(0);
+  Raw buf0 = w.load(0), buf1 = w.load(1), buf2 = buf0, buf3 = buf0;
+  w.stage(0, grp);
+  grp = w.load_group(1);
   __syncthreads();
 
-  int k = 0;
-  for (; k + 4 <= nblk; k += 4) {
-    pp.iter(k + 0, h, buf3, buf0, buf1, buf2);
-    pp.iter(k + 1, h, buf0, buf1, buf2, buf3);
-    pp.iter(k + 2, h, buf1, buf2, buf3, buf0);
-    pp.iter(k + 3, h, buf2, buf3, buf0, buf1);
+  // Steady state: iterations 1 .. nfull-1 (blocks k-1 and k full), four at a
+  // time so that buffer j % 4 is a fixed set of registers; a group ends at
+  // k % kGB == kGB - 1.  The first iteration and the last few take the masked
+  // form.
+  const int nblk = w.nblk;
+  const int nfull = (w.t_end - w.t_beg) / kT;
+  w.template iter<true, false>(0, h, ssum, buf3, buf0, buf2, grp);
+  int k = 1;
+  for (; k + 4 <= nfull; k += 4) {
+    // k % 4 == 1 here, and 4 is a multiple of kGB
+    w.template iter<false, (1 % kGB == kGB - 1)>(k + 0, h, ssum, buf0, buf1, buf3, grp);
+    w.template iter<false, (2 % kGB == kGB - 1)>(k + 1, h, ssum, buf1, buf2, buf0, grp);
+    w.template iter<false, (3 % kGB == kGB - 1)>(k + 2, h, ssum, buf2, buf3, buf1, grp);
+    w.template iter<false, (4 % kGB == kGB - 1)>(k + 3, h, ssum, buf3, buf0, buf2, grp);
   }
-  if (k < nblk) pp.iter(k, h, buf3, buf0, buf1, buf2);
-  if (k + 1 < nblk) pp.iter(k + 1, h, buf0, buf1, buf2, buf3);
-  if (k + 2 < nblk) pp.iter(k + 2, h, buf1, buf2, buf3, buf0);
+  if (k < nblk) w.template iter<true, false>(k, h, ssum, buf0, buf1, buf3, grp);
+  if (k + 1 < nblk) w.template iter<true, false>(k + 1, h, ssum, buf1, buf2, buf0, grp);
+  if (k + 2 < nblk) w.template iter<true, false>(k + 2, h, ssum, buf2, buf3, buf1, grp);
+  if (k + 3 < nblk) w.template iter<true, false>(k + 3, h, ssum, buf3, buf0, buf2, grp);
 
   if (M == Mode::kScan) {
-    // finish the last block: its partials are in slot (nblk - 1) & 1
+    // finish the last block: its partials are in LDS, its raw inputs in buffer
+    // (nblk - 1) % 4
     const int kl = nblk - 1;
     const int r = kl & 3;
-    const BlockIn last = r == 0 ? buf0 : r == 1 ? buf1 : r == 2 ? buf2 : buf3;
-    float part[kN];
+    const Raw last = r == 0 ? buf0 : r == 1 ? buf1 : r == 2 ? buf2 : buf3;
+    float ysum = 0.0f;
 #pragma unroll
-    for (int n = 0; n < kN; ++n) part[n] = s_part[kl & 1][n][row][col];
-    pp.finish(kl, last, part);
-    if (vS && p.last_state && g == p.nseg - 1) p.last_state[(b * p.dim + dS) * kN + row] = h;
+    for (int n = 0; n < kN; ++n) ysum += w.sP[row][n * kPitch + col];
+    w.template finish<true>(kl, last, ysum);
+    if (vrow && p.last_state && g == p.nseg - 1) p.last_state[(b * p.dim + d) * kN + col] = h;
   } else {
     // segment aggregate: end state from zero and the step-size sum (fp64 partial
     // sums of the 16 owner lanes of each channel, added in a fixed order)
-    s_sum[row][col] = ssum;
-    __syncthreads();
-    float* ag = p.agg + ((b * p.dim + dSc) * (p.nseg - 1) + g) * kAggStride;
-    if (vS) ag[row] = h;
-    if (vS && row == 0) {
+    sSum[wave][row][col] = ssum;
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    float* ag = p.agg + ((b * p.dim + dc) * (p.nseg - 1) + g) * kAggStride;
+    if (vrow) ag[col] = h;
+    if (vrow && col == 0) {
       double s = 0.0;
-      for (int j = 0; j < kCh; ++j) s += s_sum[col][j];
+      for (int j = 0; j < kT; ++j) s += sSum[wave][row][j];
       ag[kN] = static_cast<float>(s);
     }
   }
@@ -297,9 +425,9 @@ __global__ void copy_state_kernel(const float* h0, float* last, int64_t n) {
 }
 
 // Segments per sequence: cut only when the batch x channel groups alone leave
-// the machine short of workgroups, and keep segments long enough that the
+// the machine short of wavefronts, and keep segments long enough that the
 // extra aggregate pass and the fold stay small.
-constexpr int64_t kTargetGroups = 768;    // 3 workgroups per CU on 256 CUs
+constexpr int64_t kTargetGroups = 768;    // 3 wavefronts per SIMD on 256 CUs
 constexpr int64_t kMinSegLen = 8192;
 constexpr int kMaxSeg = 64;
 
@@ -310,7 +438,33 @@ int choose_segments(int64_t groups, int64_t L) {
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(g, kMaxSeg)));
 }
 
+template <Mode M>
+void launch(bool bf16, bool softplus, dim3 grid, const ScanParams& p, hipStream_t stream) {
+  const dim3 block(kThreads);
+  if (bf16) {
+    if (softplus) scan_fwd_kernel<uint16_t, M, true><<<grid, block, 0, stream>>>(p);
+    else scan_fwd_kernel<uint16_t, M, false><<<grid, block, 0, stream>>>(p);
+  } else {
+    if (softplus) scan_fwd_kernel<float, M, true><<<grid, block, 0, stream>>>(p);
+    else scan_fwd_kernel<float, M, false><<<grid, block, 0, stream>>>(p);
+  }
+}
+
 }  // namespace
+
+bool scan_windows_fit(const ssm_scan_args& a) {
+  // Per-wavefront byte windows (and the lane offsets inside them) are 32-bit.
+  const int64_t esz = a.io_dtype == SSM_BF16 ? 2 : 4;
+  const int64_t rows = std::min<int64_t>(kRows, a.dim) - 1;
+  const int64_t lim = int64_t{1} << 32;
+  auto fits = [&](int64_t span) { return span * esz < lim; };
+  bool ok = fits(rows * a.u_dim_stride + a.seqlen) && fits(rows * a.delta_dim_stride + a.seqlen) &&
+            fits(rows * a.out_dim_stride + a.seqlen) &&
+            fits((kN - 1) * a.B_state_stride + a.seqlen) &&
+            fits((kN - 1) * a.C_state_stride + a.seqlen);
+  if (a.z) ok = ok && fits(rows * a.z_dim_stride + a.seqlen);
+  return ok;
+}
 
 size_t scan_workspace_bytes(const ssm_scan_args& a) {
   if (a.batch <= 0 || a.dim <= 0 || a.seqlen <= 0) return 0;
@@ -340,33 +494,26 @@ hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {
   p.Asd = a.A_dim_stride; p.Asn = a.A_state_stride;
   p.osb = a.out_batch_stride; p.osd = a.out_dim_stride;
   p.batch = a.batch; p.dim = a.dim; p.L = static_cast<int>(a.seqlen);
-  p.dgroups = (a.dim + kCh - 1) / kCh;
-  p.softplus = a.delta_softplus ? 1 : 0;
+  p.cgroups = (a.dim + kCh - 1) / kCh;
 
   // Segmenting needs the caller's workspace; without enough of it the whole
   // sequence runs as one segment (same result, less parallelism).
-  const int64_t groups = a.batch * p.dgroups;
+  const int64_t groups = a.batch * p.cgroups;
   const size_t need = scan_workspace_bytes(a);
   int nseg = 1;
   if (need > 0 && a.workspace && a.workspace_bytes >= need)
     nseg = choose_segments(groups, a.seqlen);
   const int64_t seg = (a.seqlen + nseg - 1) / nseg;
-  p.seg_len = static_cast<int>((seg + kT - 1) / kT * kT);
+  p.seg_len = static_cast<int>((seg + kGT - 1) / kGT * kGT);
   p.nseg = static_cast<int>((a.seqlen + p.seg_len - 1) / p.seg_len);
   p.agg = p.nseg > 1 ? static_cast<float*>(a.workspace) : nullptr;
 
   if (p.nseg > 1) {
     const dim3 g1((unsigned)(groups * (p.nseg - 1)));
-    if (a.io_dtype == SSM_BF16)
-      scan_fwd_kernel<uint16_t, Mode::kAggregate><<<g1, dim3(kThreads), 0, stream>>>(p);
-    else
-      scan_fwd_kernel<float, Mode::kAggregate><<<g1, dim3(kThreads), 0, stream>>>(p);
+    launch<Mode::kAggregate>(a.io_dtype == SSM_BF16, a.delta_softplus != 0, g1, p, stream);
   }
   const dim3 g2((unsigned)(groups * p.nseg));
-  if (a.io_dtype == SSM_BF16)
-    scan_fwd_kernel<uint16_t, Mode::kScan><<<g2, dim3(kThreads), 0, stream>>>(p);
-  else
-    scan_fwd_kernel<float, Mode::kScan><<<g2, dim3(kThreads), 0, stream>>>(p);
+  launch<Mode::kScan>(a.io_dtype == SSM_BF16, a.delta_softplus != 0, g2, p, stream);
   return hipGetLastError();
 }
 

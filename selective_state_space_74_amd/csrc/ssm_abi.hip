@@ -60,7 +60,7 @@ const char* ssm_status_string(int status) {
     case SSM_ERR_DTYPE: return "io_dtype must be SSM_F32 or SSM_BF16";
     case SSM_ERR_ALIGN: return "pointer not aligned to its element size";
     case SSM_ERR_ALIAS: return "an output overlaps an input";
-    case SSM_ERR_UNSUPPORTED: return "unsupported configuration (dstate must be 16, seqlen < 2^31 - 64)";
+    case SSM_ERR_UNSUPPORTED: return "unsupported configuration (dstate != 16, or a size past the limits in ssm.h)";
     case SSM_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
   }
@@ -87,6 +87,7 @@ int ssm_validate_scan(const ssm_scan_args* a) {
     if (misaligned(a->u, esz) || misaligned(a->delta, esz) || misaligned(a->z, esz) ||
         misaligned(a->B, esz) || misaligned(a->C, esz) || misaligned(a->out, esz))
       return SSM_ERR_ALIGN;
+    if (!ssm::scan_windows_fit(*a)) return SSM_ERR_UNSUPPORTED;
   }
   if (misaligned(a->A, 4) || misaligned(a->D, 4) || misaligned(a->delta_bias, 4) ||
       misaligned(a->h0, 4) || misaligned(a->last_state, 4) || misaligned(a->workspace, 4))

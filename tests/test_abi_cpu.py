@@ -131,6 +131,25 @@ def test_scan_bad_fields(field, value, code):
     assert ssm.validate_scan(a) == code
 
 
+def test_scan_window_limits():
+    """The kernel reads 4 channel rows (u/delta/z/out) and 16 state rows (B/C)
+    through 32-bit byte windows; spans past 2^32 bytes are unsupported."""
+    L = 64
+    for field, rows in (("u_dim_stride", 3), ("delta_dim_stride", 3), ("z_dim_stride", 3),
+                        ("out_dim_stride", 3), ("B_state_stride", 15), ("C_state_stride", 15)):
+        limit = ((1 << 32) // 4 - L) // rows        # largest stride whose span fits (fp32)
+        a = good_scan(L=L)
+        setattr(a, field, limit + 1)
+        assert ssm.validate_scan(a) == UNSUP, field
+        a = good_scan(L=L)
+        setattr(a, field, limit - 1)
+        assert ssm.validate_scan(a) != UNSUP, field
+    # bf16 halves the bytes: the same stride fits
+    a = good_scan(L=L, io=1)
+    a.B_state_stride = ((1 << 32) // 4 - L) // 15 + 1
+    assert ssm.validate_scan(a) != UNSUP
+
+
 def test_scan_empty_sizes_are_noops():
     for field in ("batch", "dim"):
         a = good_scan()

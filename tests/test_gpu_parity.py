@@ -55,6 +55,15 @@ def test_ragged_shapes(batch, dim, L, io):
     check_scan(inp, io, label=f"ragged b{batch} d{dim} L{L} {io}")
 
 
+@pytest.mark.parametrize("batch,dim,L,io", [(1, 37, 50, "f32"), (2, 13, 3 * 8192 + 5, "bf16")])
+def test_ragged_channels_with_initial_state(batch, dim, L, io):
+    """Channel counts that leave a partial last channel group, with h0 and
+    last_state (the second case is also cut into segments)."""
+    inp = si.scan_inputs(batch, dim, L, io_dtype=io, seed=dim + L)
+    h0 = np.random.default_rng(dim).standard_normal((batch, dim, 16)).astype(np.float32)
+    check_scan(inp, io, h0=h0, label=f"ragged h0 b{batch} d{dim} L{L} {io}")
+
+
 def test_initial_state_and_split_sequence():
     inp = si.scan_inputs(2, 32, 200, io_dtype="f32", seed=7)
     rng = np.random.default_rng(7)
