@@ -46,6 +46,9 @@ def _load():
         lib.oracle_state_update_f64.restype = ctypes.c_int
         lib.oracle_state_update_f64.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, P,
                                                 ctypes.c_int, P, ctypes.c_int]
+        lib.oracle_selective_scan_bwd_f64.restype = ctypes.c_int
+        lib.oracle_selective_scan_bwd_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [
+            ctypes.c_int] + [P] * 12 + [ctypes.c_int]
         lib.oracle_softplus.restype = ctypes.c_double
         lib.oracle_softplus.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
@@ -66,8 +69,8 @@ class use_library:
         self.saved = _load()
         _lib = None
         lib = ctypes.CDLL(self.path)
-        for name in ("oracle_selective_scan_f64", "oracle_state_update_f64", "oracle_softplus",
-                     "oracle_silu"):
+        for name in ("oracle_selective_scan_f64", "oracle_state_update_f64",
+                     "oracle_selective_scan_bwd_f64", "oracle_softplus", "oracle_silu"):
             src = getattr(self.saved, name)
             dst = getattr(lib, name)
             dst.restype, dst.argtypes = src.restype, src.argtypes
@@ -137,3 +140,31 @@ def state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplu
                                        int(bool(dt_softplus)), _ptr(out), int(nthreads))
     state_update.last_threads = used
     return out, s
+
+
+def selective_scan_bwd(dout, u, delta, A, B, C, D=None, z=None, delta_bias=None,
+                       delta_softplus=True, h0=None, dlast=None, nthreads=0):
+    """Gradients of the prefill scan in fp64 for the upstream gradient dout
+    (batch, dim, L) on out and, optionally, dlast (batch, dim, N) on
+    last_state.  Returns a dict with du, ddelta, dB, dC, dA and, when the
+    matching input is given, dz, dD, ddelta_bias, dh0."""
+    lib = _load()
+    dout, dlast = _f64(dout), _f64(dlast)
+    u, delta, z, B, C, A, D, delta_bias, h0 = map(_f64, (u, delta, z, B, C, A, D, delta_bias, h0))
+    batch, dim, L = u.shape
+    N = A.shape[1]
+    assert dout.shape == u.shape and (dlast is None or dlast.shape == (batch, dim, N))
+    assert B.shape == (batch, N, L) and C.shape == (batch, N, L) and A.shape == (dim, N)
+    g = dict(du=np.empty_like(u), ddelta=np.empty_like(u), dB=np.empty((batch, N, L)),
+             dC=np.empty((batch, N, L)), dA=np.empty((dim, N)))
+    g["dz"] = np.empty_like(u) if z is not None else None
+    g["dD"] = np.empty(dim) if D is not None else None
+    g["ddelta_bias"] = np.empty(dim) if delta_bias is not None else None
+    g["dh0"] = np.empty((batch, dim, N)) if h0 is not None else None
+    used = lib.oracle_selective_scan_bwd_f64(
+        batch, dim, L, N, _ptr(u), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
+        _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(dout), _ptr(dlast),
+        _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dz"]), _ptr(g["dB"]), _ptr(g["dC"]),
+        _ptr(g["dA"]), _ptr(g["dD"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), int(nthreads))
+    selective_scan_bwd.last_threads = used
+    return {k: v for k, v in g.items() if v is not None}

@@ -35,7 +35,10 @@
  *
  * Parity pins live in tests/test_oracle_pins.py (LTI convolution, Delta -> 0,
  * L = 1 closed form, split sequence, decode == scan, reset, A = 0 prefix sum,
- * linearity, unrolled-sum brute force in fp64 and 40-digit decimal).
+ * linearity, unrolled-sum brute force in fp64 and 40-digit decimal) and, for
+ * the backward, in tests/test_oracle_bwd_pins.py (exact Jacobian-vector
+ * products of the forward for the inputs it is linear in, central
+ * differences of the forward for the others).
  *
  * Layouts (all contiguous, row-major):
  *   u, delta, z, out : (batch, dim, seqlen)
@@ -49,6 +52,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -168,5 +172,169 @@ int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, double* 
   for (int64_t r = 0; r < batch * dim; ++r)
     update_row(r, dim, dstate, state, x, dt, z, Bm, Cm, A, Dv, bias, softplus, out);
 #endif
+  return used;
+}
+
+/* ------------------------------------------------------------------------ *
+ * Backward of the prefill scan (reverse-mode derivative of the loop in
+ * scan_row), for one upstream gradient dout on out and, optionally, dlast on
+ * last_state.  Chain rule through each step, in fp64:
+ *   gate     out = y s(z) z,  s = logistic:  dy = dout * silu(z),
+ *            dz = dout * y * s (1 + z (1 - s))
+ *   readout  y = sum_n C h_t + D u:  dC += dy h_t,  dD += dy u,  du += dy D,
+ *            adjoint of h_t gains dy C
+ *   step     h_t = e_t h_{t-1} + Delta B u,  e_t = exp(Delta A):
+ *            with g the adjoint of h_t,
+ *            dB += g Delta u,  du += g Delta B,
+ *            dDelta += g (B u + A e_t h_{t-1}),  dA += g Delta e_t h_{t-1},
+ *            adjoint of h_{t-1} = e_t g
+ *   Delta    Delta = softplus(x), x = delta + bias:  dx = dDelta s(x)
+ *            (dx = dDelta without softplus);  ddelta = dx,  dbias += dx
+ *   h0       dh0 = adjoint of h_{-1}
+ * Rows (b, d) run on OpenMP threads into per-row slots; the sums over rows
+ * (dB and dC over d, dA/dD/dbias over b and t) are then added in a fixed
+ * order, so the result does not depend on the thread count.
+ * ------------------------------------------------------------------------ */
+static double logistic(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+static void scan_row_bwd(int64_t b, int64_t d, int64_t dim, int64_t L, int64_t N,
+                         const double* u, const double* delta, const double* z,
+                         const double* Bm, const double* Cm, const double* A,
+                         const double* Dv, const double* bias, int softplus,
+                         const double* h0, const double* dout, const double* dlast,
+                         double* du, double* ddelta, double* dz,
+                         double* dBrow, double* dCrow, double* dArow, double* dDrow,
+                         double* dbrow, double* dh0, double* hs, double* es, double* g) {
+  const int64_t row = (b * dim + d) * L;
+  const double* Bb = Bm + b * N * L;
+  const double* Cb = Cm + b * N * L;
+  /* forward again, keeping every h_t and e_t (hs[(t+1)*N + n] = h_t, hs[n] = h_{-1}) */
+  for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    const double xt = delta[row + t] + (bias ? bias[d] : 0.0);
+    const double step = softplus ? oracle_softplus(xt) : xt;
+    for (int64_t n = 0; n < N; ++n) {
+      const double decay = exp(step * A[d * N + n]);
+      es[t * N + n] = decay;
+      hs[(t + 1) * N + n] = decay * hs[t * N + n] + step * Bb[n * L + t] * u[row + t];
+    }
+  }
+  for (int64_t n = 0; n < N; ++n) {
+    g[n] = dlast ? dlast[(b * dim + d) * N + n] : 0.0;
+    dArow[n] = 0.0;
+  }
+  double sumD = 0.0, sumbias = 0.0;
+  for (int64_t t = L - 1; t >= 0; --t) {
+    const double ut = u[row + t];
+    const double xt = delta[row + t] + (bias ? bias[d] : 0.0);
+    const double step = softplus ? oracle_softplus(xt) : xt;
+    /* y_t again (before the gate), for dz */
+    double yt = 0.0;
+    for (int64_t n = 0; n < N; ++n) yt += Cb[n * L + t] * hs[(t + 1) * N + n];
+    if (Dv) yt += Dv[d] * ut;
+    double dy = dout[row + t];
+    if (z) {
+      const double zt = z[row + t], sg = logistic(zt);
+      dz[row + t] = dy * yt * sg * (1.0 + zt * (1.0 - sg));
+      dy *= zt * sg;
+    }
+    double dut = Dv ? dy * Dv[d] : 0.0;
+    sumD += dy * ut;
+    double dstep = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      const double ht = hs[(t + 1) * N + n], hp = hs[t * N + n], et = es[t * N + n];
+      dCrow[n * L + t] = dy * ht;
+      const double adj = g[n] + dy * Cb[n * L + t];      /* adjoint of h_t */
+      dBrow[n * L + t] = adj * step * ut;
+      dut += adj * step * Bb[n * L + t];
+      dstep += adj * (Bb[n * L + t] * ut + A[d * N + n] * et * hp);
+      dArow[n] += adj * step * et * hp;
+      g[n] = et * adj;                                    /* adjoint of h_{t-1} */
+    }
+    const double dx = softplus ? dstep * logistic(xt) : dstep;
+    du[row + t] = dut;
+    ddelta[row + t] = dx;
+    sumbias += dx;
+  }
+  *dDrow = sumD;
+  *dbrow = sumbias;
+  if (dh0)
+    for (int64_t n = 0; n < N; ++n) dh0[(b * dim + d) * N + n] = g[n];
+}
+
+/* Gradients of the prefill scan.  Outputs: du, ddelta (batch, dim, L); dz
+ * (when z is given); dB, dC (batch, N, L); dA (dim, N); dD, dbias (dim; when
+ * D / bias are given); dh0 (batch, dim, N; when h0 is given).  dlast may be
+ * NULL (no gradient on last_state).  Returns the thread count used. */
+int oracle_selective_scan_bwd_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
+                                  const double* u, const double* delta, const double* z,
+                                  const double* Bm, const double* Cm, const double* A,
+                                  const double* Dv, const double* bias, int softplus,
+                                  const double* h0, const double* dout, const double* dlast,
+                                  double* du, double* ddelta, double* dz, double* dB,
+                                  double* dC, double* dA, double* dD, double* dbias,
+                                  double* dh0, int nthreads) {
+  const int64_t L = seqlen, N = dstate, rows = batch * dim;
+  double* dBrows = (double*)calloc((size_t)(rows * N * L > 0 ? rows * N * L : 1), sizeof(double));
+  double* dCrows = (double*)calloc((size_t)(rows * N * L > 0 ? rows * N * L : 1), sizeof(double));
+  double* dArows = (double*)calloc((size_t)(rows * N > 0 ? rows * N : 1), sizeof(double));
+  double* dDrows = (double*)calloc((size_t)(rows > 0 ? rows : 1), sizeof(double));
+  double* dbrows = (double*)calloc((size_t)(rows > 0 ? rows : 1), sizeof(double));
+  int used = 1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+  {
+#pragma omp single
+    used = omp_get_num_threads();
+    double* hs = (double*)malloc(sizeof(double) * (size_t)((L + 1) * N));
+    double* es = (double*)malloc(sizeof(double) * (size_t)(L * N + 1));
+    double* g = (double*)malloc(sizeof(double) * (size_t)N);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r)
+      scan_row_bwd(r / dim, r % dim, dim, L, N, u, delta, z, Bm, Cm, A, Dv, bias, softplus, h0,
+                   dout, dlast, du, ddelta, dz, dBrows + r * N * L, dCrows + r * N * L,
+                   dArows + r * N, dDrows + r, dbrows + r, dh0, hs, es, g);
+    free(hs); free(es); free(g);
+  }
+#else
+  (void)nthreads;
+  {
+    double* hs = (double*)malloc(sizeof(double) * (size_t)((L + 1) * N));
+    double* es = (double*)malloc(sizeof(double) * (size_t)(L * N + 1));
+    double* g = (double*)malloc(sizeof(double) * (size_t)N);
+    for (int64_t r = 0; r < rows; ++r)
+      scan_row_bwd(r / dim, r % dim, dim, L, N, u, delta, z, Bm, Cm, A, Dv, bias, softplus, h0,
+                   dout, dlast, du, ddelta, dz, dBrows + r * N * L, dCrows + r * N * L,
+                   dArows + r * N, dDrows + r, dbrows + r, dh0, hs, es, g);
+    free(hs); free(es); free(g);
+  }
+#endif
+  /* sums over rows, in a fixed order */
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t i = 0; i < N * L; ++i) {
+      double sb = 0.0, sc = 0.0;
+      for (int64_t d = 0; d < dim; ++d) {
+        sb += dBrows[(b * dim + d) * N * L + i];
+        sc += dCrows[(b * dim + d) * N * L + i];
+      }
+      dB[b * N * L + i] = sb;
+      dC[b * N * L + i] = sc;
+    }
+  for (int64_t d = 0; d < dim; ++d) {
+    double sD = 0.0, sb = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      double sA = 0.0;
+      for (int64_t b = 0; b < batch; ++b) sA += dArows[(b * dim + d) * N + n];
+      dA[d * N + n] = sA;
+    }
+    for (int64_t b = 0; b < batch; ++b) {
+      sD += dDrows[b * dim + d];
+      sb += dbrows[b * dim + d];
+    }
+    if (dD) dD[d] = sD;
+    if (dbias) dbias[d] = sb;
+  }
+  free(dBrows); free(dCrows); free(dArows); free(dDrows); free(dbrows);
   return used;
 }

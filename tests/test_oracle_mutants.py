@@ -59,3 +59,54 @@ def test_pins_catch_planted_mistake(name, old, new, tmp_path):
     with oracle.use_library(str(lib)):
         caught = [fn.__name__ for fn in PINS if _fails(fn)]
     assert caught, f"no pin caught mutant {name}"
+
+
+# Planted mistakes in the backward (scan_row_bwd), each to be caught by a pin
+# in test_oracle_bwd_pins.py.
+import test_oracle_bwd_pins as bpins  # noqa: E402
+
+BWD_PINS = [
+    lambda: [bpins.test_linear_inputs_exact_jvp(n, True) for n in bpins.LINEAR],
+    lambda: [bpins.test_nonlinear_inputs_central_difference(n, True) for n in bpins.NONLINEAR],
+    lambda: [bpins.test_nonlinear_inputs_central_difference(n, False) for n in bpins.NONLINEAR],
+    bpins.test_every_element_of_du_by_unit_directions,
+    bpins.test_last_state_gradient_wrt_h0_is_the_total_decay,
+    bpins.test_single_token_du_closed_form,
+]
+
+BWD_MUTANTS = [
+    ("bwd-carry-without-decay", "g[n] = et * adj;", "g[n] = adj;"),
+    ("bwd-dz-drops-term", "dz[row + t] = dy * yt * sg * (1.0 + zt * (1.0 - sg));",
+     "dz[row + t] = dy * yt * sg;"),
+    ("bwd-dC-previous-state", "dCrow[n * L + t] = dy * ht;", "dCrow[n * L + t] = dy * hp;"),
+    ("bwd-ddelta-drops-decay-term", "dstep += adj * (Bb[n * L + t] * ut + A[d * N + n] * et * hp);",
+     "dstep += adj * Bb[n * L + t] * ut;"),
+    ("bwd-no-softplus-derivative", "const double dx = softplus ? dstep * logistic(xt) : dstep;",
+     "const double dx = dstep;"),
+    ("bwd-dA-drops-step", "dArow[n] += adj * step * et * hp;", "dArow[n] += adj * et * hp;"),
+    ("bwd-dB-readout-only", "dBrow[n * L + t] = adj * step * ut;", "dBrow[n * L + t] = dy * step * ut;"),
+    ("bwd-ignores-dlast", "g[n] = dlast ? dlast[(b * dim + d) * N + n] : 0.0;", "g[n] = 0.0;"),
+    ("bwd-du-drops-skip", "double dut = Dv ? dy * Dv[d] : 0.0;", "double dut = 0.0;"),
+    ("bwd-du-sign", "dut += adj * step * Bb[n * L + t];", "dut -= adj * step * Bb[n * L + t];"),
+]
+
+
+def _fails_call(fn):
+    try:
+        fn()
+    except AssertionError:
+        return True
+    return False
+
+
+@pytest.mark.parametrize("name,old,new", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
+def test_backward_pins_catch_planted_mistake(name, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(lib), str(path), "-lm"])
+    with oracle.use_library(str(lib)):
+        caught = [i for i, fn in enumerate(BWD_PINS) if _fails_call(fn)]
+    assert caught, f"no pin caught mutant {name}"
