@@ -8,8 +8,9 @@ algorithmic bytes per second (every input element read once, B and C once per
 (batch, token), every output written once, the state never touching HBM) and
 channel*tokens per second; the HBM fraction is against MI355X's 8 TB/s.
 
-Also measured (secondary, same JSON line): the bf16 2.8b-like layer scan and
-the 1000-step decode update; with --all also the 1M-token scan.
+Also measured (secondary, same JSON line): the bf16 2.8b-like layer scan, the
+1000-step decode update and the scan backward on the two layer shapes; with
+--all also the 1M-token scan.
 
 Prints ONE JSON line on stdout.  Progress goes to stderr.
 """
@@ -132,6 +133,45 @@ def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2):
                io_dtype="bf16" if esz == 2 else "f32")
     res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBS
     del sets, outs, lasts
+    torch.cuda.empty_cache()
+    return res
+
+
+def scan_bwd_bytes(batch, dim, L, N, esz, gate=True):
+    """Algorithmic bytes of one scan backward: u, delta, dout (+ z) and B, C
+    read once, the forward's checkpoints read once, du, ddelta (+ dz) written
+    once, dB, dC (fp32) written once, parameters and their gradients."""
+    io = batch * dim * L * esz * (5 + (2 if gate else 0))   # u, delta, dout, du, ddelta (+ z, dz)
+    bc = 2 * batch * N * L * esz + 2 * batch * N * L * 4    # B, C in; dB, dC out
+    ck = batch * dim * ((L + 15) // 16) * N * 4
+    params = 2 * (dim * N * 4 + 2 * dim * 4)                # A, D, bias and their gradients
+    return io + bc + ck + params
+
+
+def bench_bwd(cfg, steps, torch, ssm, si):
+    """Times the scan backward (from the forward's checkpoints)."""
+    dev = "cuda"
+    t = si.to_torch(si.scan_inputs_for(cfg), dev)
+    ck = torch.empty(ssm.checkpoint_shape(cfg.batch, cfg.dim, cfg.seqlen), dtype=torch.float32,
+                     device=dev)
+    kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"])
+    ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], checkpoints=ck, **kw)
+    dout = torch.randn_like(t["u"], dtype=torch.float32).to(t["u"].dtype)
+
+    def step(i):
+        ssm.selective_scan_bwd(dout, t["u"], t["delta"], t["A"], t["B"], t["C"], ck, **kw)
+
+    for i in range(5):
+        step(i)
+    torch.cuda.synchronize()
+    kern_ms, kern_min = timed_launches(step, steps, torch)
+    esz = 2 if t["u"].dtype == torch.bfloat16 else 4
+    nbytes = scan_bwd_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, esz)
+    res = dict(kernel_ms=kern_ms, kernel_ms_min=kern_min, bytes=nbytes,
+               gbps=nbytes / (kern_ms * 1e-3) / 1e9,
+               channel_tokens_per_s=cfg.batch * cfg.dim * cfg.seqlen / (kern_ms * 1e-3))
+    res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBS
+    del t, ck, dout
     torch.cuda.empty_cache()
     return res
 
@@ -277,6 +317,13 @@ def main():
         log(f"[bench] secondary {si.DECODE_CONFIG.name}")
         secondary[si.DECODE_CONFIG.name] = bench_decode(si.DECODE_CONFIG, torch, ssm, si)
         log(f"[bench] decode {secondary[si.DECODE_CONFIG.name]['gbps']:.1f} GB/s")
+        for cid in (1, 2):
+            cb = si.SCAN_CONFIGS[cid]
+            key = f"{cb.name}-backward"
+            log(f"[bench] secondary {key}")
+            secondary[key] = bench_bwd(cb, 20, torch, ssm, si)
+            log(f"[bench] {key} {secondary[key]['gbps']:.1f} GB/s, "
+                f"{secondary[key]['kernel_ms'] * 1e3:.1f} us")
         if args.all:
             c3 = si.SCAN_CONFIGS[3]
             log(f"[bench] secondary {c3.name}")

@@ -1,7 +1,7 @@
 /*
  * ssm.h -- C ABI of libssm.so, the gfx950 (MI355X) selective-scan library.
  *
- * Two operations, both from the Mamba pages (cited by page title and section):
+ * Three operations, all from the Mamba pages (cited by page title and section):
  *
  *   ssm_selective_scan_fwd  -- prefill.  For every batch row b, channel d and
  *     state index n, with Delta_t = softplus(delta_t + bias[d]) (Mamba paper
@@ -14,6 +14,12 @@
  *     notes; the per-channel diagonal SSM is section 4.4 there; B, C and
  *     Delta depending on the token is section 4.1; the gate is the block's
  *     gate branch (section 4.3).
+ *
+ *   ssm_selective_scan_bwd -- the gradients of the prefill scan, i.e. its
+ *     reverse-mode derivative.  Back-propagation needs the state at every
+ *     step; as the Mamba paper notes advise (section 5.4: gradient
+ *     checkpointing, state passed at chunk edges), the forward keeps only one
+ *     state per 16-token chunk and the backward recomputes the steps between.
  *
  *   ssm_selective_state_update -- decode: the same recurrence for a single
  *     token, reading and writing a resident fp32 state (Mamba paper notes,
@@ -47,7 +53,10 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
+
+/* Tokens between two state checkpoints (see ssm_scan_args.checkpoints). */
+#define SSM_CHECKPOINT_TOKENS 16
 
 typedef enum ssm_status {
   SSM_OK = 0,
@@ -93,7 +102,12 @@ typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  * ssm_scan_workspace_size() bytes, not overlapping any tensor.  The library
  * uses it to cut long sequences with few channels into segments scanned in
  * parallel; with workspace NULL or too small the scan still runs, correctly,
- * as a single segment per sequence.  Its contents are scratch on return. */
+ * as a single segment per sequence.  Its contents are scratch on return.
+ * Checkpoints (optional output, for ssm_selective_scan_bwd): fp32
+ * (batch, dim, ceil(seqlen / SSM_CHECKPOINT_TOKENS), dstate), contiguous;
+ * element (b, d, k, n) is the state h[n] entering token
+ * k * SSM_CHECKPOINT_TOKENS (so k = 0 holds h0, or zeros).  NULL: none
+ * written.  Must not overlap any other tensor. */
 typedef struct ssm_scan_args {
   int64_t batch, dim, seqlen, dstate;
   int32_t io_dtype;       /* ssm_dtype */
@@ -110,7 +124,56 @@ typedef struct ssm_scan_args {
   float* last_state;
   void* out;          int64_t out_batch_stride, out_dim_stride;
   void* workspace;    size_t workspace_bytes;
+  float* checkpoints;
 } ssm_scan_args;
+
+/* Arguments of the scan backward.  The forward inputs (u, delta, z, B, C, A,
+ * D, delta_bias, h0, delta_softplus) keep their meaning, layout and strides
+ * from ssm_scan_args and must be the ones the forward ran with;
+ * `checkpoints` (required) is what that forward wrote.
+ *   dout            : (batch, dim, seqlen), io_dtype, time stride 1: the
+ *                     gradient on out.
+ *   dlast           : (batch, dim, dstate) fp32, contiguous: the gradient on
+ *                     last_state.  NULL means 0.
+ * Outputs (device memory owned by the caller, fully overwritten):
+ *   du, ddelta      : (batch, dim, seqlen), io_dtype, time stride 1.
+ *   dz              : the same, required when z is given, else ignored.
+ *   dB, dC          : (batch, dstate, seqlen) fp32, contiguous (summed over
+ *                     channels).
+ *   dA              : (dim, dstate) fp32, contiguous (summed over batch, time).
+ *   dD, ddelta_bias : (dim) fp32 (summed over batch, time); NULL: not wanted.
+ *   dh0             : (batch, dim, dstate) fp32, contiguous; NULL: not wanted.
+ * The sums over channels (dB, dC) and over batch rows (dA, dD, ddelta_bias)
+ * are accumulated with device atomics, so their last bits can vary from run
+ * to run; every other output is deterministic.  Outputs must not overlap
+ * each other or any input.  The backward runs every sequence as one segment
+ * (no workspace). */
+typedef struct ssm_scan_bwd_args {
+  int64_t batch, dim, seqlen, dstate;
+  int32_t io_dtype;       /* ssm_dtype */
+  int32_t delta_softplus; /* bool */
+  const void* u;      int64_t u_batch_stride, u_dim_stride;
+  const void* delta;  int64_t delta_batch_stride, delta_dim_stride;
+  const void* z;      int64_t z_batch_stride, z_dim_stride;
+  const void* B;      int64_t B_batch_stride, B_state_stride;
+  const void* C;      int64_t C_batch_stride, C_state_stride;
+  const float* A;     int64_t A_dim_stride, A_state_stride;
+  const float* D;
+  const float* delta_bias;
+  const float* h0;
+  const float* checkpoints;
+  const void* dout;   int64_t dout_batch_stride, dout_dim_stride;
+  const float* dlast;
+  void* du;           int64_t du_batch_stride, du_dim_stride;
+  void* ddelta;       int64_t ddelta_batch_stride, ddelta_dim_stride;
+  void* dz;           int64_t dz_batch_stride, dz_dim_stride;
+  float* dB;
+  float* dC;
+  float* dA;
+  float* dD;
+  float* ddelta_bias;
+  float* dh0;
+} ssm_scan_bwd_args;
 
 /* Arguments of the single-token decode update.
  *   state            : (batch, dim, dstate) fp32, state stride 1, element
@@ -145,6 +208,7 @@ int ssm_abi_version(void);
 
 /* sizeof the argument structs, for bindings that mirror them. */
 size_t ssm_scan_args_size(void);
+size_t ssm_scan_bwd_args_size(void);
 size_t ssm_update_args_size(void);
 
 /* Workspace bytes the scan can use for this argument block (0 when it would
@@ -157,10 +221,15 @@ const char* ssm_status_string(int status);
 /* Pure host checks of an argument block: no HIP call, no device access, so
  * they run on a machine without a GPU.  Returns the first failing status. */
 int ssm_validate_scan(const ssm_scan_args* args);
+int ssm_validate_scan_bwd(const ssm_scan_bwd_args* args);
 int ssm_validate_update(const ssm_update_args* args);
 
 /* Prefill scan (see ssm_scan_args).  Validates, then launches on `stream`. */
 int ssm_selective_scan_fwd(const ssm_scan_args* args, void* stream);
+
+/* Scan backward (see ssm_scan_bwd_args).  Validates, then launches on
+ * `stream`. */
+int ssm_selective_scan_bwd(const ssm_scan_bwd_args* args, void* stream);
 
 /* Decode update (see ssm_update_args).  Validates, then launches on `stream`. */
 int ssm_selective_state_update(const ssm_update_args* args, void* stream);

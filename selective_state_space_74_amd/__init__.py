@@ -7,8 +7,13 @@ of the computation runs in the HIP kernels of libssm.so; there is no Python or
 CPU fallback, and importing a missing library raises.
 
     selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None,
-                       delta_softplus=True, h0=None, return_last_state=False)
+                       delta_softplus=True, h0=None, return_last_state=False,
+                       checkpoints=None)
         -> out, or (out, last_state)
+    selective_scan_bwd(dout, u, delta, A, B, C, checkpoints, D=None, z=None,
+                       delta_bias=None, delta_softplus=True, h0=None, dlast=None)
+        -> dict of gradients (du, ddelta, dB, dC, dA and dz, dD,
+           ddelta_bias, dh0 for the inputs that were given)
     selective_state_update(state, x, dt, A, B, C, D=None, z=None,
                            dt_bias=None, dt_softplus=True) -> out  (state updated in place)
 
@@ -26,7 +31,8 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssm.so")
 
-SSM_ABI_VERSION = 1
+SSM_ABI_VERSION = 2
+CHECKPOINT_TOKENS = 16
 SSM_F32, SSM_BF16 = 0, 1
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_STRIDE",
           4: "SSM_ERR_DTYPE", 5: "SSM_ERR_ALIGN", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_UNSUPPORTED",
@@ -49,7 +55,28 @@ class ScanArgs(ctypes.Structure):
                 ("A", _P), ("A_dim_stride", _I64), ("A_state_stride", _I64),
                 ("D", _P), ("delta_bias", _P), ("h0", _P), ("last_state", _P),
                 ("out", _P), ("out_batch_stride", _I64), ("out_dim_stride", _I64),
-                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+                ("checkpoints", _P)]
+
+
+class ScanBwdArgs(ctypes.Structure):
+    """Mirror of ssm_scan_bwd_args."""
+    _fields_ = [("batch", _I64), ("dim", _I64), ("seqlen", _I64), ("dstate", _I64),
+                ("io_dtype", _I32), ("delta_softplus", _I32),
+                ("u", _P), ("u_batch_stride", _I64), ("u_dim_stride", _I64),
+                ("delta", _P), ("delta_batch_stride", _I64), ("delta_dim_stride", _I64),
+                ("z", _P), ("z_batch_stride", _I64), ("z_dim_stride", _I64),
+                ("B", _P), ("B_batch_stride", _I64), ("B_state_stride", _I64),
+                ("C", _P), ("C_batch_stride", _I64), ("C_state_stride", _I64),
+                ("A", _P), ("A_dim_stride", _I64), ("A_state_stride", _I64),
+                ("D", _P), ("delta_bias", _P), ("h0", _P), ("checkpoints", _P),
+                ("dout", _P), ("dout_batch_stride", _I64), ("dout_dim_stride", _I64),
+                ("dlast", _P),
+                ("du", _P), ("du_batch_stride", _I64), ("du_dim_stride", _I64),
+                ("ddelta", _P), ("ddelta_batch_stride", _I64), ("ddelta_dim_stride", _I64),
+                ("dz", _P), ("dz_batch_stride", _I64), ("dz_dim_stride", _I64),
+                ("dB", _P), ("dC", _P), ("dA", _P), ("dD", _P), ("ddelta_bias", _P),
+                ("dh0", _P)]
 
 
 class UpdateArgs(ctypes.Structure):
@@ -86,10 +113,12 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.ssm_abi_version.restype = ctypes.c_int
         L.ssm_scan_args_size.restype = ctypes.c_size_t
+        L.ssm_scan_bwd_args_size.restype = ctypes.c_size_t
         L.ssm_update_args_size.restype = ctypes.c_size_t
         L.ssm_status_string.restype = ctypes.c_char_p
         L.ssm_status_string.argtypes = [ctypes.c_int]
-        for name, T in (("ssm_validate_scan", ScanArgs), ("ssm_validate_update", UpdateArgs)):
+        for name, T in (("ssm_validate_scan", ScanArgs), ("ssm_validate_update", UpdateArgs),
+                        ("ssm_validate_scan_bwd", ScanBwdArgs)):
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.POINTER(T)]
@@ -97,11 +126,14 @@ def lib():
         L.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs)]
         L.ssm_selective_scan_fwd.restype = ctypes.c_int
         L.ssm_selective_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _P]
+        L.ssm_selective_scan_bwd.restype = ctypes.c_int
+        L.ssm_selective_scan_bwd.argtypes = [ctypes.POINTER(ScanBwdArgs), _P]
         L.ssm_selective_state_update.restype = ctypes.c_int
         L.ssm_selective_state_update.argtypes = [ctypes.POINTER(UpdateArgs), _P]
         if L.ssm_abi_version() != SSM_ABI_VERSION:
             raise ImportError(f"libssm.so ABI {L.ssm_abi_version()} != {SSM_ABI_VERSION}")
         if (L.ssm_scan_args_size() != ctypes.sizeof(ScanArgs)
+                or L.ssm_scan_bwd_args_size() != ctypes.sizeof(ScanBwdArgs)
                 or L.ssm_update_args_size() != ctypes.sizeof(UpdateArgs)):
             raise ImportError("libssm.so argument struct layout differs from the binding")
         _lib = L
@@ -116,6 +148,10 @@ def validate_scan(args: ScanArgs) -> int:
     return lib().ssm_validate_scan(ctypes.byref(args))
 
 
+def validate_scan_bwd(args: ScanBwdArgs) -> int:
+    return lib().ssm_validate_scan_bwd(ctypes.byref(args))
+
+
 def validate_update(args: UpdateArgs) -> int:
     return lib().ssm_validate_update(ctypes.byref(args))
 
@@ -126,6 +162,15 @@ def scan_workspace_size(args: ScanArgs) -> int:
 
 def scan_fwd_raw(args: ScanArgs, stream: int = 0) -> int:
     return lib().ssm_selective_scan_fwd(ctypes.byref(args), _P(stream or None))
+
+
+def scan_bwd_raw(args: ScanBwdArgs, stream: int = 0) -> int:
+    return lib().ssm_selective_scan_bwd(ctypes.byref(args), _P(stream or None))
+
+
+def checkpoint_shape(batch: int, dim: int, seqlen: int, dstate: int = 16):
+    """Shape of the fp32 state checkpoints the forward writes for the backward."""
+    return (batch, dim, (seqlen + CHECKPOINT_TOKENS - 1) // CHECKPOINT_TOKENS, dstate)
 
 
 def state_update_raw(args: UpdateArgs, stream: int = 0) -> int:
@@ -181,12 +226,14 @@ def _stream(stream):
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
                        h0=None, return_last_state=False, out=None, last_state=None, stream=None,
-                       workspace=None):
+                       workspace=None, checkpoints=None):
     """Prefill selective scan on the GPU (see the module docstring).
 
     `workspace` (optional): a device tensor reused across calls; when None,
     one of the size the library asks for is allocated through torch; False
-    passes no workspace (the scan then runs each sequence as one segment)."""
+    passes no workspace (the scan then runs each sequence as one segment).
+    `checkpoints` (optional): an fp32 tensor of checkpoint_shape(...) that
+    receives the state entering every 16-token block, for the backward."""
     torch = _torch()
     if u.dim() != 3:
         raise ValueError("u must be (batch, dim, L)")
@@ -234,6 +281,10 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     a.D, a.delta_bias, a.h0 = _ptr(D), _ptr(delta_bias), _ptr(h0)
     a.last_state = _ptr(last_state)
     a.out, (a.out_batch_stride, a.out_dim_stride) = _ptr(out), out.stride()[:2]
+    if checkpoints is not None:
+        _contig_f32("checkpoints", checkpoints, checkpoint_shape(batch, dim, L, N))
+        _check_dev("checkpoints", checkpoints, dev, torch.float32)
+        a.checkpoints = _ptr(checkpoints)
     need = scan_workspace_size(a) if workspace is not False else 0
     if need:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -295,3 +346,75 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, 
     if st != 0:
         raise SSMError(st, "ssm_selective_state_update")
     return out
+
+
+def selective_scan_bwd(dout, u, delta, A, B, C, checkpoints, D=None, z=None, delta_bias=None,
+                       delta_softplus=True, h0=None, dlast=None, stream=None):
+    """Gradients of selective_scan_fwd for the upstream gradient dout on out
+    (and dlast on last_state), from the checkpoints that forward wrote.
+    Returns a dict: du, ddelta (IO dtype, shaped like u), dB, dC (fp32, like
+    B), dA (fp32, like A) and, for the inputs that were given, dz, dD,
+    ddelta_bias, dh0 (fp32).  dB, dC, dA, dD and ddelta_bias are summed with
+    device atomics (their last bits may vary between runs)."""
+    torch = _torch()
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, L)")
+    batch, dim, L = u.shape
+    N = A.shape[1] if A.dim() == 2 else -1
+    dev, io = u.device, u.dtype
+    code = _io_code(u)
+    for name, t in (("delta", delta), ("z", z), ("B", B), ("C", C), ("dout", dout)):
+        _check_dev(name, t, dev, io)
+    for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias), ("h0", h0),
+                    ("checkpoints", checkpoints), ("dlast", dlast)):
+        _check_dev(name, t, dev, torch.float32)
+    for name, t in (("delta", delta), ("z", z), ("dout", dout)):
+        if t is not None and tuple(t.shape) != (batch, dim, L):
+            raise ValueError(f"{name} must match u's shape")
+    if tuple(B.shape) != (batch, N, L) or tuple(C.shape) != (batch, N, L):
+        raise ValueError("B and C must be (batch, dstate, L)")
+    if tuple(A.shape) != (dim, N):
+        raise ValueError("A must be (dim, dstate)")
+    for name, t in (("u", u), ("delta", delta), ("z", z), ("B", B), ("C", C), ("dout", dout)):
+        if t is not None and L > 1 and t.stride(2) != 1:
+            raise ValueError(f"{name} must have time stride 1")
+    _contig_f32("D", D, (dim,))
+    _contig_f32("delta_bias", delta_bias, (dim,))
+    _contig_f32("h0", h0, (batch, dim, N))
+    _contig_f32("dlast", dlast, (batch, dim, N))
+    _contig_f32("checkpoints", checkpoints, checkpoint_shape(batch, dim, L, N))
+    g = dict(du=torch.empty((batch, dim, L), dtype=io, device=dev),
+             ddelta=torch.empty((batch, dim, L), dtype=io, device=dev),
+             dB=torch.empty((batch, N, L), dtype=torch.float32, device=dev),
+             dC=torch.empty((batch, N, L), dtype=torch.float32, device=dev),
+             dA=torch.empty((dim, N), dtype=torch.float32, device=dev))
+    if z is not None:
+        g["dz"] = torch.empty((batch, dim, L), dtype=io, device=dev)
+    if D is not None:
+        g["dD"] = torch.empty(dim, dtype=torch.float32, device=dev)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty(dim, dtype=torch.float32, device=dev)
+    if h0 is not None:
+        g["dh0"] = torch.empty((batch, dim, N), dtype=torch.float32, device=dev)
+    a = ScanBwdArgs()
+    a.batch, a.dim, a.seqlen, a.dstate = batch, dim, L, N
+    a.io_dtype, a.delta_softplus = code, int(bool(delta_softplus))
+    a.u, (a.u_batch_stride, a.u_dim_stride) = _ptr(u), u.stride()[:2]
+    a.delta, (a.delta_batch_stride, a.delta_dim_stride) = _ptr(delta), delta.stride()[:2]
+    if z is not None:
+        a.z, (a.z_batch_stride, a.z_dim_stride) = _ptr(z), z.stride()[:2]
+        a.dz, (a.dz_batch_stride, a.dz_dim_stride) = _ptr(g["dz"]), g["dz"].stride()[:2]
+    a.B, (a.B_batch_stride, a.B_state_stride) = _ptr(B), B.stride()[:2]
+    a.C, (a.C_batch_stride, a.C_state_stride) = _ptr(C), C.stride()[:2]
+    a.A, (a.A_dim_stride, a.A_state_stride) = _ptr(A), A.stride()
+    a.D, a.delta_bias, a.h0 = _ptr(D), _ptr(delta_bias), _ptr(h0)
+    a.checkpoints, a.dlast = _ptr(checkpoints), _ptr(dlast)
+    a.dout, (a.dout_batch_stride, a.dout_dim_stride) = _ptr(dout), dout.stride()[:2]
+    a.du, (a.du_batch_stride, a.du_dim_stride) = _ptr(g["du"]), g["du"].stride()[:2]
+    a.ddelta, (a.ddelta_batch_stride, a.ddelta_dim_stride) = _ptr(g["ddelta"]), g["ddelta"].stride()[:2]
+    a.dB, a.dC, a.dA = _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dA"])
+    a.dD, a.ddelta_bias, a.dh0 = _ptr(g.get("dD")), _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0"))
+    st = scan_bwd_raw(a, _stream(stream))
+    if st != 0:
+        raise SSMError(st, "ssm_selective_scan_bwd")
+    return g

@@ -59,7 +59,6 @@ constexpr int kGPitch = kGT + 4;    // LDS pitch (floats) of one state's group o
 constexpr int kPitch = 20;          // LDS pitch (floats) of one state's readout partials
 constexpr int kPartRow = kN * kPitch + 16;  // floats per channel of readout partials
 constexpr int kAggStride = kN + 1;  // floats per (channel, segment) aggregate: b[16], S
-constexpr int kRsrcWord3 = 0x00020000;      // raw buffer, 32-bit dwords (gfx9 family)
 
 enum class Mode { kScan, kAggregate };
 
@@ -76,47 +75,14 @@ struct ScanParams {
   float* last_state;
   void* out;
   float* agg;      // [batch * dim][nseg - 1][kAggStride] segment aggregates (nseg > 1)
+  float* ckpt;     // [batch][dim][nbk][kN] states entering each block, or NULL
   int64_t usb, usd, dsb, dsd, zsb, zsd, Bsb, Bsn, Csb, Csn, Asd, Asn, osb, osd;
   int64_t batch, dim;
   int L;
   int seg_len;     // tokens per segment (multiple of kGT)
   int nseg;        // segments per sequence
+  int nbk;         // blocks per sequence, ceil(L / kT)
   int64_t cgroups; // ceil(dim / kCh)
-};
-
-template <typename T> struct Elem;
-template <> struct Elem<float> {
-  static constexpr int kSize = 4;
-  __device__ static __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-  }
-  __device__ static __forceinline__ float f32(uint32_t v) { return __uint_as_float(v); }
-  __device__ static __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
-  }
-};
-template <> struct Elem<uint16_t> {
-  static constexpr int kSize = 2;
-  __device__ static __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-  }
-  __device__ static __forceinline__ float f32(uint32_t v) { return __uint_as_float(v << 16); }
-  __device__ static __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
-    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
-  }
-};
-
-// A wavefront-uniform byte window [base, base + bytes) of one tensor.  Host
-// validation keeps every window below 4 GiB, so all offsets are 32-bit.
-struct Window {
-  const char* base;
-  uint32_t bytes;
-  // The window moved `skip` bytes forward; skip never exceeds bytes (block
-  // starts stay inside the sequence).
-  __device__ __forceinline__ __amdgpu_buffer_rsrc_t at(uint32_t skip) const {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + skip), 0,
-                                             static_cast<int>(bytes - skip), kRsrcWord3);
-  }
 };
 
 // Owner role raw inputs of one block: token t0 + col of the lane's channel
@@ -136,8 +102,10 @@ struct Wave {
   const ScanParams& p;
   int wave, row, col;
   int t_beg, t_end, nblk, ngrp;
-  Window wu, wdt, wz, wB, wC, wout;
-  uint32_t ou, odt, oz, oB, oC, oout;  // per-lane byte offsets inside the windows
+  Window wu, wdt, wz, wB, wC, wout, wck;
+  uint32_t ou, odt, oz, oB, oC, oout, ock;  // per-lane byte offsets inside the windows
+  uint32_t ckstep;    // checkpoint bytes per block of a channel row (0: none kept)
+  int blk0;           // global index of this segment's first block
   float a2, bias, Dd;
   float (*sB)[kN][kGPitch];   // [2][kN][kGPitch], shared by the workgroup
   float (*sC)[kN][kGPitch];
@@ -252,6 +220,11 @@ struct Wave {
     }
     if (M == Mode::kAggregate) ssum += static_cast<double>(dl);
 
+    // checkpoint: the state entering this block (an empty window when none
+    // are kept, so the store is dropped without a branch)
+    if (M == Mode::kScan)
+      Elem<float>::store(wck.at((blk0 + k) * ckstep), ock, h);
+
     // state role: 16 sequential steps of this lane's state; the readout
     // partials C_n h_n go to LDS four tokens at a time
     float pk[4];
@@ -334,6 +307,13 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
     w.oz = w.ou;
   }
   w.wout = rows_window(p.out, p.osb, p.osd, w.oout);
+  // checkpoints: rows of nbk * kN floats, [b][d][block][n]
+  const int64_t ckrow = static_cast<int64_t>(p.nbk) * kN;
+  w.blk0 = w.t_beg / kT;
+  w.ckstep = p.ckpt ? kN * 4 : 0;
+  w.ock = static_cast<uint32_t>(((dc - dw0) * ckrow + col) * 4);
+  w.wck = Window{reinterpret_cast<const char*>(p.ckpt ? p.ckpt + (b * p.dim + dw0) * ckrow : nullptr),
+                 p.ckpt ? static_cast<uint32_t>((dw3 - dw0 + 1) * ckrow * 4) : 0u};
   // B/C: the workgroup's 16 state rows; this lane stages state 4 wave + row
   const int st = kRows * wave + row;
   w.oB = static_cast<uint32_t>((st * p.Bsn + col) * E);
@@ -507,6 +487,8 @@ hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {
   p.seg_len = static_cast<int>((seg + kGT - 1) / kGT * kGT);
   p.nseg = static_cast<int>((a.seqlen + p.seg_len - 1) / p.seg_len);
   p.agg = p.nseg > 1 ? static_cast<float*>(a.workspace) : nullptr;
+  p.ckpt = a.checkpoints;
+  p.nbk = static_cast<int>((a.seqlen + kT - 1) / kT);
 
   if (p.nseg > 1) {
     const dim3 g1((unsigned)(groups * (p.nseg - 1)));

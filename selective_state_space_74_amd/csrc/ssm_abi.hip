@@ -37,6 +37,7 @@ int64_t io_size(int32_t dt) { return dt == SSM_BF16 ? 2 : 4; }
 
 // Token indices are 32-bit inside the scan kernel.
 constexpr int64_t kMaxSeqlen = (int64_t{1} << 31) - 64;
+constexpr int64_t kCkptTokens = SSM_CHECKPOINT_TOKENS;
 
 }  // namespace
 
@@ -44,6 +45,7 @@ extern "C" {
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 size_t ssm_scan_args_size(void) { return sizeof(ssm_scan_args); }
+size_t ssm_scan_bwd_args_size(void) { return sizeof(ssm_scan_bwd_args); }
 size_t ssm_update_args_size(void) { return sizeof(ssm_update_args); }
 
 size_t ssm_scan_workspace_size(const ssm_scan_args* a) {
@@ -116,6 +118,77 @@ int ssm_validate_scan(const ssm_scan_args* a) {
   for (const Span& s : inputs)
     if (overlap(sws, s)) return SSM_ERR_ALIAS;
   if (overlap(sws, sout) || overlap(sws, sls)) return SSM_ERR_ALIAS;
+  if (misaligned(a->checkpoints, 4)) return SSM_ERR_ALIGN;
+  const Span sck = span1(a->checkpoints, B * Dm * ((L + kCkptTokens - 1) / kCkptTokens) * N, 4);
+  for (const Span& s : inputs)
+    if (overlap(sck, s)) return SSM_ERR_ALIAS;
+  if (overlap(sck, sout) || overlap(sck, sls) || overlap(sck, sws)) return SSM_ERR_ALIAS;
+  return SSM_OK;
+}
+
+int ssm_validate_scan_bwd(const ssm_scan_bwd_args* a) {
+  if (!a) return SSM_ERR_NULL;
+  if (a->batch < 0 || a->dim < 0 || a->seqlen < 0 || a->dstate < 1) return SSM_ERR_SHAPE;
+  if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (a->dstate != 16) return SSM_ERR_UNSUPPORTED;
+  if (a->seqlen > kMaxSeqlen) return SSM_ERR_UNSUPPORTED;
+  if (a->batch == 0 || a->dim == 0) return SSM_OK;
+  if (!a->A || !a->dA) return SSM_ERR_NULL;
+  const int64_t B = a->batch, Dm = a->dim, L = a->seqlen, N = a->dstate;
+  const int64_t esz = io_size(a->io_dtype);
+  if (L > 0) {
+    if (!a->u || !a->delta || !a->B || !a->C || !a->checkpoints || !a->dout || !a->du ||
+        !a->ddelta || !a->dB || !a->dC || (a->z && !a->dz))
+      return SSM_ERR_NULL;
+    const int64_t strides[] = {a->u_batch_stride, a->u_dim_stride, a->delta_batch_stride,
+                               a->delta_dim_stride, a->B_batch_stride, a->B_state_stride,
+                               a->C_batch_stride, a->C_state_stride, a->A_dim_stride,
+                               a->A_state_stride, a->dout_batch_stride, a->dout_dim_stride,
+                               a->du_batch_stride, a->du_dim_stride, a->ddelta_batch_stride,
+                               a->ddelta_dim_stride, a->z ? a->z_batch_stride : 0,
+                               a->z ? a->z_dim_stride : 0, a->z ? a->dz_batch_stride : 0,
+                               a->z ? a->dz_dim_stride : 0};
+    for (int64_t s : strides)
+      if (s < 0) return SSM_ERR_STRIDE;
+    if (misaligned(a->u, esz) || misaligned(a->delta, esz) || misaligned(a->z, esz) ||
+        misaligned(a->B, esz) || misaligned(a->C, esz) || misaligned(a->dout, esz) ||
+        misaligned(a->du, esz) || misaligned(a->ddelta, esz) || (a->z && misaligned(a->dz, esz)))
+      return SSM_ERR_ALIGN;
+    if (!ssm::scan_bwd_windows_fit(*a)) return SSM_ERR_UNSUPPORTED;
+  }
+  if (misaligned(a->A, 4) || misaligned(a->D, 4) || misaligned(a->delta_bias, 4) ||
+      misaligned(a->h0, 4) || misaligned(a->checkpoints, 4) || misaligned(a->dlast, 4) ||
+      misaligned(a->dB, 4) || misaligned(a->dC, 4) || misaligned(a->dA, 4) ||
+      misaligned(a->dD, 4) || misaligned(a->ddelta_bias, 4) || misaligned(a->dh0, 4))
+    return SSM_ERR_ALIGN;
+  const int64_t nbk = (L + kCkptTokens - 1) / kCkptTokens;
+  const Span inputs[] = {
+      span3(a->u, B, a->u_batch_stride, Dm, a->u_dim_stride, L, esz),
+      span3(a->delta, B, a->delta_batch_stride, Dm, a->delta_dim_stride, L, esz),
+      span3(a->z, B, a->z_batch_stride, Dm, a->z_dim_stride, L, esz),
+      span3(a->B, B, a->B_batch_stride, N, a->B_state_stride, L, esz),
+      span3(a->C, B, a->C_batch_stride, N, a->C_state_stride, L, esz),
+      L > 0 ? Span{reinterpret_cast<uintptr_t>(a->A),
+                   reinterpret_cast<uintptr_t>(a->A) +
+                       static_cast<uintptr_t>(((Dm - 1) * a->A_dim_stride +
+                                               (N - 1) * a->A_state_stride + 1) * 4)}
+            : Span{},
+      span1(a->D, Dm, 4), span1(a->delta_bias, Dm, 4), span1(a->h0, B * Dm * N, 4),
+      span1(a->checkpoints, B * Dm * nbk * N, 4),
+      span3(a->dout, B, a->dout_batch_stride, Dm, a->dout_dim_stride, L, esz),
+      span1(a->dlast, B * Dm * N, 4)};
+  const Span outputs[] = {
+      span3(a->du, B, a->du_batch_stride, Dm, a->du_dim_stride, L, esz),
+      span3(a->ddelta, B, a->ddelta_batch_stride, Dm, a->ddelta_dim_stride, L, esz),
+      a->z ? span3(a->dz, B, a->dz_batch_stride, Dm, a->dz_dim_stride, L, esz) : Span{},
+      span1(a->dB, B * N * L, 4), span1(a->dC, B * N * L, 4), span1(a->dA, Dm * N, 4),
+      span1(a->dD, Dm, 4), span1(a->ddelta_bias, Dm, 4), span1(a->dh0, B * Dm * N, 4)};
+  for (const Span& o : outputs) {
+    for (const Span& i : inputs)
+      if (overlap(o, i)) return SSM_ERR_ALIAS;
+    for (const Span& o2 : outputs)
+      if (&o2 != &o && overlap(o, o2)) return SSM_ERR_ALIAS;
+  }
   return SSM_OK;
 }
 
@@ -162,6 +235,15 @@ int ssm_selective_scan_fwd(const ssm_scan_args* a, void* stream) {
   if (st != SSM_OK) return st;
   if (a->batch == 0 || a->dim == 0) return SSM_OK;
   if (ssm::launch_scan_fwd(*a, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return SSM_ERR_HIP;
+  return SSM_OK;
+}
+
+int ssm_selective_scan_bwd(const ssm_scan_bwd_args* a, void* stream) {
+  const int st = ssm_validate_scan_bwd(a);
+  if (st != SSM_OK) return st;
+  if (a->batch == 0 || a->dim == 0) return SSM_OK;
+  if (ssm::launch_scan_bwd(*a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return SSM_ERR_HIP;
   return SSM_OK;
 }

@@ -14,6 +14,8 @@ size_t scan_workspace_bytes(const ssm_scan_args& a);
 // The scan addresses each wavefront's rows through 32-bit byte windows.
 bool scan_windows_fit(const ssm_scan_args& a);
 hipError_t launch_state_update(const ssm_update_args& a, hipStream_t stream);
+hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream);
+bool scan_bwd_windows_fit(const ssm_scan_bwd_args& a);
 
 // ---------------------------------------------------------------------------
 // Device helpers.
@@ -77,5 +79,48 @@ template <int J>
 __device__ __forceinline__ float row_bcast(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + J, 0xf, 0xf, true));
 }
+
+
+// ---------------------------------------------------------------------------
+// Buffer-descriptor access (raw buffers, gfx9 family descriptor word 3).
+
+constexpr int kRsrcWord3 = 0x00020000;
+
+// One IO element through a buffer descriptor: loads return the raw bits
+// (widened later), stores round to the IO type.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kSize = 4;
+  __device__ static __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  __device__ static __forceinline__ float f32(uint32_t v) { return __uint_as_float(v); }
+  __device__ static __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+  }
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int kSize = 2;
+  __device__ static __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  }
+  __device__ static __forceinline__ float f32(uint32_t v) { return __uint_as_float(v << 16); }
+  __device__ static __forceinline__ void store(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
+  }
+};
+
+// A wavefront-uniform byte window [base, base + bytes) of one tensor.  Host
+// validation keeps every window below 4 GiB, so all offsets are 32-bit.
+struct Window {
+  const char* base;
+  uint32_t bytes;
+  // The window moved `skip` bytes forward; skip never exceeds bytes (block
+  // starts stay inside the sequence).
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t at(uint32_t skip) const {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + skip), 0,
+                                             static_cast<int>(bytes - skip), kRsrcWord3);
+  }
+};
 
 }  // namespace ssm

@@ -36,11 +36,13 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_struct_layout():
     L = ssm.lib()
-    assert L.ssm_abi_version() == ssm.SSM_ABI_VERSION == 1
+    assert L.ssm_abi_version() == ssm.SSM_ABI_VERSION == 2
     assert L.ssm_scan_args_size() == ctypes.sizeof(ssm.ScanArgs)
+    assert L.ssm_scan_bwd_args_size() == ctypes.sizeof(ssm.ScanBwdArgs)
     assert L.ssm_update_args_size() == ctypes.sizeof(ssm.UpdateArgs)
     header = open(HEADER).read()
-    assert "#define SSM_ABI_VERSION 1" in header
+    assert "#define SSM_ABI_VERSION 2" in header
+    assert f"#define SSM_CHECKPOINT_TOKENS {ssm.CHECKPOINT_TOKENS}" in header
 
 
 def test_status_strings():
@@ -253,3 +255,76 @@ def test_product_path_has_no_cpu_fallback():
     for fn in os.listdir(os.path.join(ROOT, "selective_state_space_74_amd", "csrc")):
         assert "oracle" not in open(os.path.join(ROOT, "selective_state_space_74_amd", "csrc",
                                                  fn)).read().lower()
+
+
+def good_bwd(batch=2, dim=32, L=64, N=16, io=0, z=True):
+    a = ssm.ScanBwdArgs()
+    a.batch, a.dim, a.seqlen, a.dstate = batch, dim, L, N
+    a.io_dtype, a.delta_softplus = io, 1
+    names = ["u", "delta", "dout", "du", "ddelta"] + (["z", "dz"] if z else [])
+    for i, name in enumerate(names):
+        setattr(a, name, addr(i))
+        setattr(a, f"{name}_batch_stride", dim * L)
+        setattr(a, f"{name}_dim_stride", L)
+    for i, name in enumerate(("B", "C")):
+        setattr(a, name, addr(8 + i))
+        setattr(a, f"{name}_batch_stride", N * L)
+        setattr(a, f"{name}_state_stride", L)
+    a.A, a.A_dim_stride, a.A_state_stride = addr(10), N, 1
+    a.D, a.delta_bias, a.h0, a.checkpoints, a.dlast = addr(11), addr(12), addr(13), addr(14), addr(15)
+    a.dB, a.dC, a.dA, a.dD, a.ddelta_bias, a.dh0 = (addr(16), addr(17), addr(18), addr(19),
+                                                    addr(20), addr(21))
+    return a
+
+
+def test_bwd_valid_block_passes():
+    assert ssm.validate_scan_bwd(good_bwd()) == OK
+    assert ssm.validate_scan_bwd(good_bwd(io=1)) == OK
+    assert ssm.validate_scan_bwd(good_bwd(z=False)) == OK
+
+
+@pytest.mark.parametrize("field", ["u", "delta", "B", "C", "A", "checkpoints", "dout", "du",
+                                   "ddelta", "dB", "dC", "dA", "dz"])
+def test_bwd_required_pointers(field):
+    a = good_bwd()
+    setattr(a, field, None)
+    assert ssm.validate_scan_bwd(a) == NULL
+
+
+@pytest.mark.parametrize("field", ["D", "delta_bias", "h0", "dlast", "dD", "ddelta_bias", "dh0"])
+def test_bwd_optional_pointers(field):
+    a = good_bwd()
+    setattr(a, field, None)
+    assert ssm.validate_scan_bwd(a) == OK
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("dstate", 8, UNSUP), ("io_dtype", 3, DTYPE), ("seqlen", -2, SHAPE),
+    ("dout_dim_stride", -1, STRIDE), ("du_batch_stride", -1, STRIDE),
+])
+def test_bwd_bad_fields(field, value, code):
+    a = good_bwd()
+    setattr(a, field, value)
+    assert ssm.validate_scan_bwd(a) == code
+
+
+def test_bwd_outputs_must_not_alias():
+    a = good_bwd()
+    a.du = a.u                       # output onto an input
+    assert ssm.validate_scan_bwd(a) == ALIAS
+    a = good_bwd()
+    a.dC = a.dB                      # two outputs
+    assert ssm.validate_scan_bwd(a) == ALIAS
+    a = good_bwd()
+    a.dA = a.checkpoints
+    assert ssm.validate_scan_bwd(a) == ALIAS
+
+
+def test_forward_checkpoints_validated():
+    a = good_scan()
+    a.checkpoints = addr(11)
+    assert ssm.validate_scan(a) == OK
+    a.checkpoints = a.u               # overlaps an input
+    assert ssm.validate_scan(a) == ALIAS
+    a.checkpoints = addr(11) + 2      # misaligned
+    assert ssm.validate_scan(a) == ALIGN
