@@ -27,10 +27,10 @@
 //      by DPP row broadcast);
 //   3. state lanes run the adjoint from token 15 down to 0, accumulating dA in
 //      a register and leaving per-token terms in LDS: g B and g A e h_{t-1}
-//      (summed over n by the owners into du and ddelta), g Delta u and dy h_t
-//      (summed over the workgroup's 16 channels, then added to dB and dC with
-//      one device atomic per (n, t) and workgroup);
-//   4. owners finish du, ddelta and store them.
+//      (summed over n by the owners, who finish du and ddelta), g Delta u and
+//      dy h_t (summed over the workgroup's 16 channels, then added to dB and
+//      dC with one device atomic per (n, t) and workgroup); this runs in two
+//      halves of 8 tokens so that the LDS holds half a block of terms.
 // dA, dD and the bias gradient are summed over batch rows with device atomics
 // at the end.  B/C tiles are staged as in the forward (16 states x 32 tokens,
 // double buffered), walking backwards.
@@ -104,9 +104,9 @@ struct BwdWave {
   int nvalid;         // channels of this workgroup below dim
   float (*sB)[kN][kGPitch];   // [2][kN][kGPitch], shared
   float (*sC)[kN][kGPitch];
-  float (*sX)[kPartRow];      // this wavefront's [kRows][kPartRow]: readout, then g B
-  float (*sY)[kPartRow];      // this wavefront's [kRows][kPartRow]: g A e h_{t-1}
-  float (*sR)[kN][kT];        // [2 * kCh][kN][kT], shared: dB and dC terms per channel
+  float (*sX)[kPartRow];      // this wavefront's [kRows][kPartRow]: readout, then the
+                              // per-state du/ddelta terms of half a block
+  float (*sR)[kCh][kN][kT / 2];  // [2][kCh][kN][kT/2], shared: dB, dC terms per channel
 
   static constexpr int E = Elem<T>::kSize;
 
@@ -164,13 +164,16 @@ struct BwdWave {
     const float hck = Elem<float>::f32(
         __builtin_amdgcn_raw_buffer_load_b32(wck.at(static_cast<uint32_t>(k) * kN * 4), ock, 0, 0));
 
-    // owner: Delta, Delta u (zero past the end, so those steps are identities)
+    // owner: Delta, Delta u (zero past the end, so those steps are identities).
+    // The mask is applied to the inputs (softplus(-inf) = 0) so that Delta
+    // and Delta u, the DPP broadcast sources, come from arithmetic, not from
+    // a select: that keeps the broadcasts foldable into their consumers.
     const bool own = t0 + col < p.L;
-    const float uv = Elem<T>::f32(Q.u);
+    const float uv = own ? Elem<T>::f32(Q.u) : 0.0f;
     const float x = Elem<T>::f32(Q.dt) + bias;
-    float dl = kSoftplus ? softplus_f32(x) : x;
-    dl = own ? dl : 0.0f;
-    const float du = own ? dl * uv : 0.0f;
+    const float xm = own ? x : (kSoftplus ? -__builtin_inff() : 0.0f);
+    const float dl = kSoftplus ? softplus_f32(xm) : xm;
+    const float du = dl * uv;
 
     // 1. forward again from the checkpoint; readout terms to LDS
     float e[kT], hs[kT];
@@ -205,67 +208,75 @@ struct BwdWave {
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
 
-    // 3. adjoint, token 15 down to 0
+    // 3. adjoint, token 15 down to 0, in two halves of 8 tokens (second
+    // broadcasts of Delta, Delta u and dy go through opaque copies so that
+    // each broadcast folds into its one consumer).  After each half: the
+    // owners of its 8 tokens finish du/ddelta from the per-state terms, and
+    // the workgroup's 256 threads sum the dB/dC terms over its channels.
+    const float dl2 = opaque_copy(dl), du2 = opaque_copy(du), dy2 = opaque_copy(dy);
+    float sxm = 0.0f;  // softplus'(x) for this owner's token
+    if (kSoftplus) sxm = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
     float s1[4], s2[4], rb[4], rc[4];
     static_for<0, kT>([&](auto J) {
       constexpr int j = kT - 1 - decltype(J)::value;
+      constexpr int h8 = j / 8;          // which half
+      constexpr int jj = j % 8;          // token within the half
       const float dyb = row_bcast<j>(dy);
       const float adj = fmaf(dyb, cv[j], g);                       // adjoint of h_t
       const float hp = j > 0 ? hs[j > 0 ? j - 1 : 0] : hck;        // h_{t-1}
       const float q = adj * (e[j] * hp);
       s1[j % 4] = adj * bv[j];                                     // -> du, ddelta
       s2[j % 4] = q * a;                                           // -> ddelta
-      rb[j % 4] = row_bcast<j>(du) * adj;                          // -> dB
-      rc[j % 4] = dyb * hs[j];                                     // -> dC
-      dA = fmaf(row_bcast<j>(dl), q, dA);
+      rb[j % 4] = row_bcast<j>(du2) * adj;                         // -> dB
+      rc[j % 4] = row_bcast<j>(dy2) * hs[j];                       // -> dC
+      dA = fmaf(row_bcast<j>(dl2), q, dA);
       g = e[j] * adj;                                              // adjoint of h_{t-1}
-      if (j % 4 == 0) {
-        *reinterpret_cast<float4*>(&sX[row][col * kPitch + j]) = make_float4(s1[0], s1[1], s1[2], s1[3]);
-        *reinterpret_cast<float4*>(&sY[row][col * kPitch + j]) = make_float4(s2[0], s2[1], s2[2], s2[3]);
-        *reinterpret_cast<float4*>(&sR[kRows * wave + row][col][j]) =
+      if constexpr (j % 4 == 0) {
+        // per-wave region: [c][n][0..7] g B, [c][n][8..15] g A e h_{t-1}
+        *reinterpret_cast<float4*>(&sX[row][col * kPitch + jj]) = make_float4(s1[0], s1[1], s1[2], s1[3]);
+        *reinterpret_cast<float4*>(&sX[row][col * kPitch + 8 + jj]) =
+            make_float4(s2[0], s2[1], s2[2], s2[3]);
+        *reinterpret_cast<float4*>(&sR[0][kRows * wave + row][col][jj]) =
             make_float4(rb[0], rb[1], rb[2], rb[3]);
-        *reinterpret_cast<float4*>(&sR[kCh + kRows * wave + row][col][j]) =
+        *reinterpret_cast<float4*>(&sR[1][kRows * wave + row][col][jj]) =
             make_float4(rc[0], rc[1], rc[2], rc[3]);
       }
-    });
-    __syncthreads();
-
-    // 4. owner: du, ddelta
-    float S1 = 0.0f, S2 = 0.0f;
+      if constexpr (jj == 0) {
+        __syncthreads();
+        // owners of tokens 8 h8 .. 8 h8 + 7: du, ddelta (lanes of the other
+        // half compute and discard)
+        const int tj = col - 8 * h8;
+        const bool mine = own && tj >= 0 && tj < 8;
+        const int ti = tj & 7;
+        float S1 = 0.0f, S2 = 0.0f;
 #pragma unroll
-    for (int n = 0; n < kN; ++n) {
-      S1 += sX[row][n * kPitch + col];
-      S2 += sY[row][n * kPitch + col];
-    }
-    const float duv = fmaf(dl, S1, dy * Dd);
-    float dx = fmaf(uv, S1, S2);
-    if (kSoftplus) dx *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
-    dx = own ? dx : 0.0f;
-    dbs += dx;
-    if (own) {
-      Elem<T>::store(wdu.at(skip(k)), odu, duv);
-      Elem<T>::store(wdd.at(skip(k)), odd, dx);
-      // without a gate the dz window is empty and stays at offset 0, so the
-      // store is dropped
-      Elem<T>::store(wdz.at(gate ? skip(k) : 0u), odz, dzv);
-    }
-
-    // dB, dC: thread (n, t) of the workgroup sums the 16 channels' terms and
-    // adds the sum to global memory (tokens past the end add exact zeros or
-    // fall outside the window)
-    {
-      const int tid = threadIdx.x;
-      const int n = tid >> 4, t = tid & 15;
-      float sb = 0.0f, sc = 0.0f;
-      for (int c = 0; c < nvalid; ++c) {   // rows past dim are repeats: left out
-        sb += sR[c][n][t];
-        sc += sR[kCh + c][n][t];
+        for (int n = 0; n < kN; ++n) {
+          S1 += sX[row][n * kPitch + ti];
+          S2 += sX[row][n * kPitch + 8 + ti];
+        }
+        const float duv = fmaf(dl, S1, dy * Dd);
+        float dx = fmaf(uv, S1, S2);
+        if (kSoftplus) dx *= sxm;
+        dx = mine ? dx : 0.0f;
+        dbs += dx;
+        if (mine) {
+          Elem<T>::store(wdu.at(skip(k)), odu, duv);
+          Elem<T>::store(wdd.at(skip(k)), odd, dx);
+          // without a gate the dz window is empty and stays at offset 0, so
+          // the store is dropped
+          Elem<T>::store(wdz.at(gate ? skip(k) : 0u), odz, dzv);
+        }
+        // dB, dC: thread (tensor, n, t) sums the workgroup's channels (tokens
+        // past the end add exact zeros or fall outside the window)
+        const int tid = threadIdx.x;
+        const int ten = tid >> 7, n = (tid >> 3) & 15, t = tid & 7;
+        float sum = 0.0f;
+        for (int c = 0; c < nvalid; ++c) sum += sR[ten][c][n][t];  // rows past dim: repeats
+        const uint32_t off = static_cast<uint32_t>((n * p.L + t0 + 8 * h8 + t) * 4);
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(sum, ten ? wdC.at(0) : wdB.at(0), off, 0, 0);
+        __syncthreads();
       }
-      const uint32_t off = static_cast<uint32_t>((n * p.L + t0 + t) * 4);
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(sb, wdB.at(0), off, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(sc, wdC.at(0), off, 0, 0);
-    }
-    __syncthreads();
+    });
   }
 };
 
@@ -274,8 +285,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   __shared__ __align__(16) float sB[2][kN][kGPitch];
   __shared__ __align__(16) float sC[2][kN][kGPitch];
   __shared__ __align__(16) float sX[kWaves][kRows][kPartRow];
-  __shared__ __align__(16) float sY[kWaves][kRows][kPartRow];
-  __shared__ __align__(16) float sR[2 * kCh][kN][kT];
+  __shared__ __align__(16) float sR[2][kCh][kN][kT / 2];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = (threadIdx.x >> 4) & 3;
@@ -333,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   w.a2 = w.a * kLog2e;
   w.bias = p.bias ? p.bias[dc] : 0.0f;
   w.Dd = p.D ? p.D[dc] : 0.0f;
-  w.sB = sB; w.sC = sC; w.sX = sX[wave]; w.sY = sY[wave]; w.sR = sR;
+  w.sB = sB; w.sC = sC; w.sX = sX[wave]; w.sR = sR;
 
   float g = p.dlast ? p.dlast[(b * p.dim + dc) * kN + col] : 0.0f;
   float dA = 0.0f, dDs = 0.0f, dbs = 0.0f;

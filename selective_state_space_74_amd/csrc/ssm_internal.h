@@ -80,6 +80,14 @@ __device__ __forceinline__ float row_bcast(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + J, 0xf, 0xf, true));
 }
 
+// An opaque register copy.  Broadcasting the copy instead of the original
+// keeps the compiler from merging two broadcasts of one value (which would
+// leave a separate DPP move, live across everything between its two uses).
+__device__ __forceinline__ float opaque_copy(float v) {
+  float r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
 
 // ---------------------------------------------------------------------------
 // Buffer-descriptor access (raw buffers, gfx9 family descriptor word 3).
