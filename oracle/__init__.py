@@ -49,6 +49,11 @@ def _load():
         lib.oracle_selective_scan_bwd_f64.restype = ctypes.c_int
         lib.oracle_selective_scan_bwd_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [
             ctypes.c_int] + [P] * 12 + [ctypes.c_int]
+        lib.oracle_causal_conv1d_f64.restype = ctypes.c_int
+        lib.oracle_causal_conv1d_f64.argtypes = [I64, I64, I64, I64, P, P, P, P, ctypes.c_int,
+                                                 P, P, ctypes.c_int]
+        lib.oracle_conv_state_update_f64.restype = ctypes.c_int
+        lib.oracle_conv_state_update_f64.argtypes = [I64, I64, I64, P, P, P, P, ctypes.c_int, P]
         lib.oracle_softplus.restype = ctypes.c_double
         lib.oracle_softplus.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
@@ -70,7 +75,8 @@ class use_library:
         _lib = None
         lib = ctypes.CDLL(self.path)
         for name in ("oracle_selective_scan_f64", "oracle_state_update_f64",
-                     "oracle_selective_scan_bwd_f64", "oracle_softplus", "oracle_silu"):
+                     "oracle_selective_scan_bwd_f64", "oracle_causal_conv1d_f64",
+                     "oracle_conv_state_update_f64", "oracle_softplus", "oracle_silu"):
             src = getattr(self.saved, name)
             dst = getattr(lib, name)
             dst.restype, dst.argtypes = src.restype, src.argtypes
@@ -168,3 +174,36 @@ def selective_scan_bwd(dout, u, delta, A, B, C, D=None, z=None, delta_bias=None,
         _ptr(g["dA"]), _ptr(g["dD"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), int(nthreads))
     selective_scan_bwd.last_threads = used
     return {k: v for k, v in g.items() if v is not None}
+
+
+def causal_conv1d(x, weight, bias=None, state=None, silu=True, return_state=False, nthreads=0):
+    """Causal depthwise conv of the block's conv branch, in fp64.
+    x: (batch, dim, L); weight: (dim, K); bias: (dim,); state: (batch, dim,
+    K) holding x[-K .. -1] (zeros when None).  Returns u (batch, dim, L) and,
+    with return_state, the last K inputs (batch, dim, K)."""
+    lib = _load()
+    x, weight, bias, state = map(_f64, (x, weight, bias, state))
+    batch, dim, L = x.shape
+    K = weight.shape[1]
+    assert weight.shape == (dim, K) and (state is None or state.shape == (batch, dim, K))
+    u = np.empty_like(x)
+    st = np.empty((batch, dim, K)) if return_state else None
+    used = lib.oracle_causal_conv1d_f64(batch, dim, L, K, _ptr(x), _ptr(weight), _ptr(bias),
+                                        _ptr(state), int(bool(silu)), _ptr(u), _ptr(st),
+                                        int(nthreads))
+    causal_conv1d.last_threads = used
+    return (u, st) if return_state else u
+
+
+def conv_state_update(state, x, weight, bias=None, silu=True):
+    """One decode token of the conv branch.  Returns (u (batch, dim),
+    new_state (batch, dim, K)); the input state is not modified."""
+    lib = _load()
+    s = np.array(state, dtype=np.float64, copy=True, order="C")
+    x, weight, bias = map(_f64, (x, weight, bias))
+    batch, dim, K = s.shape
+    assert x.shape == (batch, dim) and weight.shape == (dim, K)
+    u = np.empty((batch, dim))
+    lib.oracle_conv_state_update_f64(batch, dim, K, _ptr(s), _ptr(x), _ptr(weight), _ptr(bias),
+                                     int(bool(silu)), _ptr(u))
+    return u, s

@@ -338,3 +338,71 @@ int oracle_selective_scan_bwd_f64(int64_t batch, int64_t dim, int64_t seqlen, in
   free(dBrows); free(dCrows); free(dArows); free(dDrows); free(dbrows);
   return used;
 }
+
+/* ------------------------------------------------------------------------ *
+ * Causal depthwise convolution of the Mamba block's conv branch (Mamba model
+ * notes, section 4.3: the branch feeding the SSM passes a local convolution
+ * first; the block's printed parameter count holds d_inner x d_conv weights
+ * plus a bias per channel), optionally followed by SiLU:
+ *   pre[b,d,t] = bias[d] + sum_{k=0}^{K-1} w[d,k] * x[b,d,t-(K-1)+k]
+ *   u[b,d,t]   = silu(pre) (or pre)
+ * x before t = 0 comes from the conv state: state[b,d,k] = x[b,d,k-K] for
+ * k = 0..K-1 (zeros when no state is given).  state_out receives the last K
+ * inputs, x[L-K .. L-1], in the same layout.
+ * ------------------------------------------------------------------------ */
+int oracle_causal_conv1d_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t K,
+                             const double* x, const double* w, const double* bias,
+                             const double* state_in, int silu, double* u, double* state_out,
+                             int nthreads) {
+  int used = 1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+  {
+#pragma omp single
+    used = omp_get_num_threads();
+#pragma omp for schedule(static)
+#else
+  (void)nthreads;
+#endif
+    for (int64_t r = 0; r < batch * dim; ++r) {
+      const int64_t d = r % dim;
+      const double* xr = x + r * seqlen;
+      for (int64_t t = 0; t < seqlen; ++t) {
+        double acc = bias ? bias[d] : 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+          const int64_t s = t - (K - 1) + k;           /* input index */
+          const double xv = s >= 0 ? xr[s] : (state_in ? state_in[r * K + K + s] : 0.0);
+          acc += w[d * K + k] * xv;
+        }
+        u[r * seqlen + t] = silu ? oracle_silu(acc) : acc;
+      }
+      if (state_out)
+        for (int64_t k = 0; k < K; ++k) {
+          const int64_t s = seqlen - K + k;
+          state_out[r * K + k] = s >= 0 ? xr[s] : (state_in ? state_in[r * K + K + s] : 0.0);
+        }
+    }
+#ifdef _OPENMP
+  }
+#endif
+  return used;
+}
+
+/* One decode token of the conv branch: shift the state left by one, append
+ * x, and form the output from the new state (written as its own loop so that
+ * "decode equals prefill" is a check between two pieces of code). */
+int oracle_conv_state_update_f64(int64_t batch, int64_t dim, int64_t K, double* state,
+                                 const double* x, const double* w, const double* bias, int silu,
+                                 double* u) {
+  for (int64_t r = 0; r < batch * dim; ++r) {
+    const int64_t d = r % dim;
+    double* s = state + r * K;
+    for (int64_t k = 0; k + 1 < K; ++k) s[k] = s[k + 1];
+    s[K - 1] = x[r];
+    double acc = bias ? bias[d] : 0.0;
+    for (int64_t k = 0; k < K; ++k) acc += w[d * K + k] * s[k];
+    u[r] = silu ? oracle_silu(acc) : acc;
+  }
+  return 1;
+}

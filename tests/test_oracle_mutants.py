@@ -110,3 +110,43 @@ def test_backward_pins_catch_planted_mistake(name, old, new, tmp_path):
     with oracle.use_library(str(lib)):
         caught = [i for i, fn in enumerate(BWD_PINS) if _fails_call(fn)]
     assert caught, f"no pin caught mutant {name}"
+
+
+# Planted mistakes in the conv branch oracle, each to be caught by a pin in
+# test_oracle_conv_pins.py.
+import test_oracle_conv_pins as cpins  # noqa: E402
+
+CONV_PINS = [
+    lambda: [cpins.test_zero_state_is_a_truncated_full_convolution(K) for K in (1, 2, 4)],
+    cpins.test_impulse_reads_the_kernel_back,
+    cpins.test_causality,
+    lambda: [cpins.test_split_with_state_is_bit_exact(c) for c in (1, 3, 9)],
+    cpins.test_returned_state_is_the_last_inputs,
+    cpins.test_decode_steps_equal_prefill_bit_exact,
+    cpins.test_width_one_is_pointwise,
+]
+
+CONV_MUTANTS = [
+    ("conv-reversed-kernel", "acc += w[d * K + k] * xv;", "acc += w[d * K + (K - 1 - k)] * xv;"),
+    ("conv-off-by-one", "const int64_t s = t - (K - 1) + k;           /* input index */",
+     "const int64_t s = t - K + k;           /* input index */"),
+    ("conv-ignores-state", "const double xv = s >= 0 ? xr[s] : (state_in ? state_in[r * K + K + s] : 0.0);",
+     "const double xv = s >= 0 ? xr[s] : 0.0;"),
+    ("conv-no-bias", "double acc = bias ? bias[d] : 0.0;\n        for (int64_t k = 0; k < K; ++k) {",
+     "double acc = 0.0;\n        for (int64_t k = 0; k < K; ++k) {"),
+    ("conv-state-out-shifted", "const int64_t s = seqlen - K + k;", "const int64_t s = seqlen - K + k - 1;"),
+    ("conv-decode-no-shift", "for (int64_t k = 0; k + 1 < K; ++k) s[k] = s[k + 1];", ";"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", CONV_MUTANTS, ids=[m[0] for m in CONV_MUTANTS])
+def test_conv_pins_catch_planted_mistake(name, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(lib), str(path), "-lm"])
+    with oracle.use_library(str(lib)):
+        caught = [i for i, fn in enumerate(CONV_PINS) if _fails_call(fn)]
+    assert caught, f"no pin caught mutant {name}"
