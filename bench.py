@@ -9,8 +9,9 @@ algorithmic bytes per second (every input element read once, B and C once per
 channel*tokens per second; the HBM fraction is against MI355X's 8 TB/s.
 
 Also measured (secondary, same JSON line): the bf16 2.8b-like layer scan, the
-1000-step decode update and the scan backward on the two layer shapes; with
---all also the 1M-token scan.
+1000-step decode update, the headline scan with the width-4 causal conv of the
+block's conv branch fused in front, and the scan backward on the two layer
+shapes; with --all also the 1M-token scan.
 
 Prints ONE JSON line on stdout.  Progress goes to stderr.
 """
@@ -92,7 +93,7 @@ def timed_launches(fn, iters, torch):
     return float(np.mean(ms)), float(np.min(ms))
 
 
-def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2):
+def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2, conv=0):
     """Times `steps` full scans; returns a dict of measurements."""
     dev = "cuda"
     sets = []
@@ -108,11 +109,20 @@ def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2):
     outs = [torch.empty_like(s["u"]) for s in sets]
     lasts = [torch.empty((cfg.batch, cfg.dim, cfg.dstate), device=dev) for _ in sets]
 
+    ckw = {}
+    if conv:
+        # the fused conv branch: u is the conv input, weights (dim, conv)
+        g = torch.Generator(device=dev)
+        g.manual_seed(cfg.seed)
+        ckw = dict(conv_weight=torch.randn(cfg.dim, conv, device=dev, generator=g) / conv ** 0.5,
+                   conv_bias=torch.zeros(cfg.dim, device=dev))
+
     def step(i):
         k = i % len(sets)
         s = sets[k]
         ssm.selective_scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
-                               delta_bias=s["delta_bias"], out=outs[k], last_state=lasts[k])
+                               delta_bias=s["delta_bias"], out=outs[k], last_state=lasts[k],
+                               **ckw)
 
     for i in range(warmup):
         step(i)
@@ -125,6 +135,8 @@ def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2):
     kern_ms, kern_min = timed_launches(step, max(10, min(steps, 200)), torch)
     esz = 2 if io == torch.bfloat16 else 4
     nbytes = scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, esz)
+    if conv:
+        nbytes += cfg.dim * conv * 4 + cfg.dim * 4              # conv weights and bias
     ms_step = wall / steps * 1e3
     res = dict(ms_per_step=ms_step, kernel_ms=kern_ms, kernel_ms_min=kern_min, bytes=nbytes,
                gbps=nbytes / (ms_step * 1e-3) / 1e9,
@@ -176,16 +188,22 @@ def bench_bwd(cfg, steps, torch, ssm, si):
     return res
 
 
-def bench_decode(cfg, torch, ssm, si, warmup=20):
-    """1000 consecutive decode steps with per-step inputs pre-resident."""
+def bench_decode(cfg, torch, ssm, si, warmup=20, conv=0):
+    """1000 consecutive decode steps with per-step inputs pre-resident (with
+    conv > 0 the conv branch's state update of that width is fused in)."""
     dev = "cuda"
     d = si.decode_inputs_device(cfg, device=dev)
     state = torch.zeros((cfg.batch, cfg.dim, cfg.dstate), device=dev)
     out = torch.empty((cfg.steps, cfg.batch, cfg.dim), dtype=d["x"].dtype, device=dev)
+    ckw = {}
+    if conv:
+        ckw = dict(conv_state=torch.zeros((cfg.batch, cfg.dim, conv), device=dev),
+                   conv_weight=torch.full((cfg.dim, conv), 1.0 / conv, device=dev),
+                   conv_bias=torch.zeros(cfg.dim, device=dev))
 
     def step(s):
         ssm.selective_state_update(state, d["x"][s], d["dt"][s], d["A"], d["B"][s], d["C"][s],
-                                   D=d["D"], z=d["z"][s], dt_bias=d["dt_bias"], out=out[s])
+                                   D=d["D"], z=d["z"][s], dt_bias=d["dt_bias"], out=out[s], **ckw)
 
     for s in range(warmup):
         step(s)
@@ -199,6 +217,8 @@ def bench_decode(cfg, torch, ssm, si, warmup=20):
     kern_ms, kern_min = timed_launches(step, 200, torch)
     esz = 2 if d["x"].dtype == torch.bfloat16 else 4
     nbytes = decode_bytes(cfg.batch, cfg.dim, cfg.dstate, esz)
+    if conv:
+        nbytes += 2 * cfg.batch * cfg.dim * conv * 4 + cfg.dim * (conv + 1) * 4
     ms_step = wall / cfg.steps * 1e3
     res = dict(steps=cfg.steps, ms_total=wall * 1e3, ms_per_step=ms_step, kernel_ms=kern_ms,
                kernel_ms_min=kern_min, bytes_per_step=nbytes,
@@ -317,6 +337,16 @@ def main():
         log(f"[bench] secondary {si.DECODE_CONFIG.name}")
         secondary[si.DECODE_CONFIG.name] = bench_decode(si.DECODE_CONFIG, torch, ssm, si)
         log(f"[bench] decode {secondary[si.DECODE_CONFIG.name]['gbps']:.1f} GB/s")
+        key = f"{si.DECODE_CONFIG.name}-conv4-fused"
+        log(f"[bench] secondary {key}")
+        secondary[key] = bench_decode(si.DECODE_CONFIG, torch, ssm, si, conv=4)
+        log(f"[bench] {key} {secondary[key]['gbps']:.1f} GB/s")
+        c1 = si.SCAN_CONFIGS[1]
+        key = f"{c1.name}-conv4-fused"
+        log(f"[bench] secondary {key}")
+        secondary[key] = bench_scan(c1, max(20, args.steps // 4), 5, torch, ssm, si, conv=4)
+        log(f"[bench] {key} {secondary[key]['gbps']:.1f} GB/s, "
+            f"kernel {secondary[key]['kernel_ms'] * 1e3:.1f} us")
         for cid in (1, 2):
             cb = si.SCAN_CONFIGS[cid]
             key = f"{cb.name}-backward"

@@ -53,10 +53,13 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 /* Tokens between two state checkpoints (see ssm_scan_args.checkpoints). */
 #define SSM_CHECKPOINT_TOKENS 16
+
+/* Largest width of the fused causal conv (see ssm_scan_args.conv_weight). */
+#define SSM_MAX_CONV 8
 
 typedef enum ssm_status {
   SSM_OK = 0,
@@ -107,7 +110,24 @@ typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  * (batch, dim, ceil(seqlen / SSM_CHECKPOINT_TOKENS), dstate), contiguous;
  * element (b, d, k, n) is the state h[n] entering token
  * k * SSM_CHECKPOINT_TOKENS (so k = 0 holds h0, or zeros).  NULL: none
- * written.  Must not overlap any other tensor. */
+ * written.  Must not overlap any other tensor.
+ * Fused conv branch (Mamba model notes, section 4.3: the branch that feeds
+ * the SSM first passes a local causal convolution).  With conv_weight set,
+ * `u` is the conv input x and the SSM input is computed per token as
+ *     u_t = act(conv_bias[d] + sum_{k<d_conv} conv_weight[d,k] x_{t-(d_conv-1)+k})
+ * with act = SiLU when conv_silu is nonzero, else identity:
+ *   conv_weight     : (dim, d_conv) fp32, contiguous; 1 <= d_conv <= SSM_MAX_CONV.
+ *   conv_bias       : (dim) fp32; NULL means 0.
+ *   conv_state_in   : (batch, dim, d_conv) fp32, contiguous, holding the inputs
+ *                     before the sequence (element k = x_{k-d_conv}); NULL
+ *                     means zeros.
+ *   conv_state_out  : same layout, receives the last d_conv inputs
+ *                     x_{seqlen-d_conv} .. x_{seqlen-1} (from conv_state_in
+ *                     where seqlen < d_conv); NULL: not wanted.  It is the
+ *                     conv_state the decode update continues from.
+ *   conv_out        : (batch, dim, seqlen), io_dtype, time stride 1: receives
+ *                     the SSM input u (e.g. for the backward); NULL: not wanted.
+ *   None of them may overlap any other tensor. */
 typedef struct ssm_scan_args {
   int64_t batch, dim, seqlen, dstate;
   int32_t io_dtype;       /* ssm_dtype */
@@ -125,6 +145,13 @@ typedef struct ssm_scan_args {
   void* out;          int64_t out_batch_stride, out_dim_stride;
   void* workspace;    size_t workspace_bytes;
   float* checkpoints;
+  const float* conv_weight;
+  const float* conv_bias;
+  const float* conv_state_in;
+  float* conv_state_out;
+  void* conv_out;     int64_t conv_out_batch_stride, conv_out_dim_stride;
+  int32_t d_conv;
+  int32_t conv_silu;  /* bool */
 } ssm_scan_args;
 
 /* Arguments of the scan backward.  The forward inputs (u, delta, z, B, C, A,
@@ -183,10 +210,15 @@ typedef struct ssm_scan_bwd_args {
  *   B, C             : (batch, dstate), state stride 1.
  *   A                : (dim, dstate) fp32, state stride 1.
  *   D, dt_bias       : (dim) fp32, contiguous, NULL means 0.
+ * Fused conv branch (as in ssm_scan_args): with conv_weight set, x is the
+ * conv input; conv_state (batch, dim, d_conv) fp32, contiguous, holds the
+ * previous d_conv inputs and is shifted in place (oldest dropped, x appended);
+ * the SSM input is act(conv_bias + sum_k conv_weight[d,k] conv_state[k]) of
+ * the updated conv_state.  1 <= d_conv <= SSM_MAX_CONV.
  * Sizes: batch, dim >= 0 (zero is a no-op); dstate must be 16; batch at most
  * 65535.
- * Aliasing: out must not overlap state or any input; state must not overlap
- * any input. */
+ * Aliasing: out must not overlap state or any input; state and conv_state
+ * must not overlap any input or each other. */
 typedef struct ssm_update_args {
   int64_t batch, dim, dstate;
   int32_t io_dtype;    /* ssm_dtype */
@@ -201,6 +233,11 @@ typedef struct ssm_update_args {
   const float* D;
   const float* dt_bias;
   void* out;          int64_t out_batch_stride;
+  float* conv_state;
+  const float* conv_weight;
+  const float* conv_bias;
+  int32_t d_conv;
+  int32_t conv_silu;  /* bool */
 } ssm_update_args;
 
 /* ABI version of the loaded library (SSM_ABI_VERSION at build time). */

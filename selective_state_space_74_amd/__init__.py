@@ -31,8 +31,9 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssm.so")
 
-SSM_ABI_VERSION = 2
+SSM_ABI_VERSION = 3
 CHECKPOINT_TOKENS = 16
+MAX_CONV = 8
 SSM_F32, SSM_BF16 = 0, 1
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_STRIDE",
           4: "SSM_ERR_DTYPE", 5: "SSM_ERR_ALIGN", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_UNSUPPORTED",
@@ -56,7 +57,11 @@ class ScanArgs(ctypes.Structure):
                 ("D", _P), ("delta_bias", _P), ("h0", _P), ("last_state", _P),
                 ("out", _P), ("out_batch_stride", _I64), ("out_dim_stride", _I64),
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
-                ("checkpoints", _P)]
+                ("checkpoints", _P),
+                ("conv_weight", _P), ("conv_bias", _P), ("conv_state_in", _P),
+                ("conv_state_out", _P),
+                ("conv_out", _P), ("conv_out_batch_stride", _I64), ("conv_out_dim_stride", _I64),
+                ("d_conv", _I32), ("conv_silu", _I32)]
 
 
 class ScanBwdArgs(ctypes.Structure):
@@ -91,7 +96,9 @@ class UpdateArgs(ctypes.Structure):
                 ("C", _P), ("C_batch_stride", _I64),
                 ("A", _P), ("A_dim_stride", _I64),
                 ("D", _P), ("dt_bias", _P),
-                ("out", _P), ("out_batch_stride", _I64)]
+                ("out", _P), ("out_batch_stride", _I64),
+                ("conv_state", _P), ("conv_weight", _P), ("conv_bias", _P),
+                ("d_conv", _I32), ("conv_silu", _I32)]
 
 
 class SSMError(RuntimeError):
@@ -226,14 +233,21 @@ def _stream(stream):
 
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
                        h0=None, return_last_state=False, out=None, last_state=None, stream=None,
-                       workspace=None, checkpoints=None):
+                       workspace=None, checkpoints=None, conv_weight=None, conv_bias=None,
+                       conv_state_in=None, conv_state_out=None, conv_out=None, conv_silu=True):
     """Prefill selective scan on the GPU (see the module docstring).
 
     `workspace` (optional): a device tensor reused across calls; when None,
     one of the size the library asks for is allocated through torch; False
     passes no workspace (the scan then runs each sequence as one segment).
     `checkpoints` (optional): an fp32 tensor of checkpoint_shape(...) that
-    receives the state entering every 16-token block, for the backward."""
+    receives the state entering every 16-token block, for the backward.
+    Fused conv branch: with conv_weight (dim, d_conv) fp32, `u` is the conv
+    input x and the SSM input is silu(conv_bias + causal depthwise conv of
+    x) (no SiLU with conv_silu=False).  conv_state_in (batch, dim, d_conv)
+    fp32 holds the inputs before the sequence; conv_state_out (same shape,
+    filled with the last d_conv inputs) and conv_out (like u, the SSM
+    input) are optional output tensors."""
     torch = _torch()
     if u.dim() != 3:
         raise ValueError("u must be (batch, dim, L)")
@@ -285,6 +299,26 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
         _contig_f32("checkpoints", checkpoints, checkpoint_shape(batch, dim, L, N))
         _check_dev("checkpoints", checkpoints, dev, torch.float32)
         a.checkpoints = _ptr(checkpoints)
+    if conv_weight is not None:
+        if conv_weight.dim() != 2 or conv_weight.shape[0] != dim:
+            raise ValueError("conv_weight must be (dim, d_conv)")
+        K = conv_weight.shape[1]
+        _check_dev("conv_weight", conv_weight, dev, torch.float32)
+        _contig_f32("conv_weight", conv_weight, (dim, K))
+        for name, t, shp in (("conv_bias", conv_bias, (dim,)),
+                             ("conv_state_in", conv_state_in, (batch, dim, K)),
+                             ("conv_state_out", conv_state_out, (batch, dim, K))):
+            _check_dev(name, t, dev, torch.float32)
+            _contig_f32(name, t, shp)
+        a.conv_weight, a.conv_bias = _ptr(conv_weight), _ptr(conv_bias)
+        a.conv_state_in, a.conv_state_out = _ptr(conv_state_in), _ptr(conv_state_out)
+        a.d_conv, a.conv_silu = K, int(bool(conv_silu))
+        if conv_out is not None:
+            _check_dev("conv_out", conv_out, dev, io)
+            if tuple(conv_out.shape) != (batch, dim, L) or (L > 1 and conv_out.stride(2) != 1):
+                raise ValueError("conv_out must be (batch, dim, L) with time stride 1")
+            a.conv_out = _ptr(conv_out)
+            a.conv_out_batch_stride, a.conv_out_dim_stride = conv_out.stride()[:2]
     need = scan_workspace_size(a) if workspace is not False else 0
     if need:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -298,8 +332,11 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
 
 
 def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True,
-                           out=None, stream=None):
-    """Single-token decode update on the GPU; `state` is updated in place."""
+                           out=None, stream=None, conv_state=None, conv_weight=None,
+                           conv_bias=None, conv_silu=True):
+    """Single-token decode update on the GPU; `state` is updated in place.
+    With conv_weight (dim, d_conv), x is the conv input and conv_state
+    (batch, dim, d_conv) fp32 is shifted in place (the fused conv branch)."""
     torch = _torch()
     if state.dim() != 3:
         raise ValueError("state must be (batch, dim, dstate)")
@@ -342,6 +379,18 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, 
     a.A, a.A_dim_stride = _ptr(A), A.stride(0)
     a.D, a.dt_bias = _ptr(D), _ptr(dt_bias)
     a.out, a.out_batch_stride = _ptr(out), out.stride(0)
+    if conv_weight is not None:
+        if conv_weight.dim() != 2 or conv_weight.shape[0] != dim:
+            raise ValueError("conv_weight must be (dim, d_conv)")
+        K = conv_weight.shape[1]
+        if conv_state is None:
+            raise ValueError("conv_state is required with conv_weight")
+        for name, t, shp in (("conv_weight", conv_weight, (dim, K)), ("conv_bias", conv_bias, (dim,)),
+                             ("conv_state", conv_state, (batch, dim, K))):
+            _check_dev(name, t, dev, torch.float32)
+            _contig_f32(name, t, shp)
+        a.conv_state, a.conv_weight, a.conv_bias = _ptr(conv_state), _ptr(conv_weight), _ptr(conv_bias)
+        a.d_conv, a.conv_silu = K, int(bool(conv_silu))
     st = state_update_raw(a, _stream(stream))
     if st != 0:
         raise SSMError(st, "ssm_selective_state_update")

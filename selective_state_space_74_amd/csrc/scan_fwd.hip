@@ -76,7 +76,14 @@ struct ScanParams {
   void* out;
   float* agg;      // [batch * dim][nseg - 1][kAggStride] segment aggregates (nseg > 1)
   float* ckpt;     // [batch][dim][nbk][kN] states entering each block, or NULL
-  int64_t usb, usd, dsb, dsd, zsb, zsd, Bsb, Bsn, Csb, Csn, Asd, Asn, osb, osd;
+  const float* conv_w;      // [dim][K] conv weights (the conv path only)
+  const float* conv_b;      // [dim] or NULL
+  const float* conv_in;     // [batch][dim][K] inputs before the sequence, or NULL
+  float* conv_stout;        // [batch][dim][K] last K inputs, or NULL
+  void* conv_out;           // (batch, dim, L) SSM input u, or NULL
+  int64_t usb, usd, dsb, dsd, zsb, zsd, Bsb, Bsn, Csb, Csn, Asd, Asn, osb, osd, cosb, cosd;
+  int K;                    // conv width
+  int conv_silu;
   int64_t batch, dim;
   int L;
   int seg_len;     // tokens per segment (multiple of kGT)
@@ -86,7 +93,8 @@ struct ScanParams {
 };
 
 // Owner role raw inputs of one block: token t0 + col of the lane's channel
-// (bit patterns, widened where they are used).
+// (bit patterns, widened where they are used); with the conv path, u holds
+// the conv input x.
 struct Raw {
   uint32_t u, dt, z;
 };
@@ -97,7 +105,13 @@ struct GroupRaw {
   uint32_t b[kGB], c[kGB];
 };
 
-template <typename T, Mode M, bool kSoftplus>
+// Lane (J - m) mod 16 of the 16-lane row (DPP row_ror:m).
+template <int M>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + M, 0xf, 0xf, true));
+}
+
+template <typename T, Mode M, bool kSoftplus, int KP>
 struct Wave {
   const ScanParams& p;
   int wave, row, col;
@@ -107,6 +121,12 @@ struct Wave {
   uint32_t ckstep;    // checkpoint bytes per block of a channel row (0: none kept)
   int blk0;           // global index of this segment's first block
   float a2, bias, Dd;
+  // conv path (KP > 0: the width padded to KP): tap weights by lag m,
+  // wl[m] multiplies x_{t-m} (zero past the real width), and the bias
+  float wl[KP > 0 ? KP : 1], cb;
+  bool silu_in;
+  Window wco;                 // conv_out window (empty when not wanted)
+  uint32_t oco;
   float (*sB)[kN][kGPitch];   // [2][kN][kGPitch], shared by the workgroup
   float (*sC)[kN][kGPitch];
   float (*sP)[kPartRow];      // this wavefront's [kRows][kPartRow]
@@ -161,13 +181,12 @@ struct Wave {
     }
   }
 
-  // Owner role: readout of block k (y = the sum of its 16 partials), skip
-  // term, gate, store.  Rows past dim repeat the last channel bit for bit, so in full
+  // Owner role: readout of block k (y = the sum of its 16 partials, uv its
+  // SSM input), skip term, gate, store.  Rows past dim repeat the last channel bit for bit, so in full
   // blocks every lane may store (duplicates write identical values); with
   // kMask only tokens before the end are stored.
   template <bool kMask>
-  __device__ __forceinline__ void finish(int k, const Raw& r, float y) const {
-    const float uv = Elem<T>::f32(r.u);
+  __device__ __forceinline__ void finish(int k, const Raw& r, float uv, float y) const {
     y = fmaf(Dd, uv, y);
     const float g = silu_f32(Elem<T>::f32(r.z));
     y *= p.z ? g : 1.0f;  // a select, not a branch
@@ -184,7 +203,7 @@ struct Wave {
   // the masked form that is decided at run time.
   template <bool kMask, bool kEnd>
   __device__ __forceinline__ void iter(int k, float& h, double& ssum, const Raw& P, const Raw& Q,
-                                       Raw& S, GroupRaw& G) const {
+                                       Raw& S, GroupRaw& G, float& uprev, float& xprev) const {
     // LDS reads first: B/C of this block and the previous block's partials.
     const int buf = (k / kGB) & 1;
     const int tb = (k % kGB) * kT;
@@ -209,10 +228,30 @@ struct Wave {
     }
     S = load(k + 2);
 
-    // owner role: Delta and Delta*u of this block (zero past the end)
+    // owner role: the SSM input u of this token (through the causal conv on
+    // the conv path), Delta and Delta*u (zero past the end)
+    float uv;
+    if constexpr (KP > 0) {
+      // x_{t-m} is lane col-m of this block for m <= col, else lane col-m+16
+      // of the previous one: a DPP row rotation of each and a select
+      const float xc = Elem<T>::f32(Q.u);
+      float pre = fmaf(wl[0], xc, cb);
+      static_for<1, KP>([&](auto Mm) {
+        constexpr int m = decltype(Mm)::value;
+        const float xcur = row_ror<m>(xc), xold = row_ror<m>(xprev);
+        pre = fmaf(wl[m], col >= m ? xcur : xold, pre);
+      });
+      const float act = silu_f32(pre);
+      uv = silu_in ? act : pre;  // a select, not a branch
+      xprev = xc;
+      if (M == Mode::kScan && (!kMask || t_beg + k * kT + col < t_end))
+        Elem<T>::store(wco.at(p.conv_out ? skip(k) : 0u), oco, uv);
+    } else {
+      uv = Elem<T>::f32(Q.u);
+    }
     const float x = Elem<T>::f32(Q.dt) + bias;
     float dl = kSoftplus ? softplus_f32(x) : x;
-    float du = dl * Elem<T>::f32(Q.u);
+    float du = dl * uv;
     if (kMask) {
       const bool own = t_beg + k * kT + col < t_end;
       dl = own ? dl : 0.0f;
@@ -241,9 +280,10 @@ struct Wave {
       }
     });
     if (M == Mode::kScan) {
-      if (!kMask) finish<false>(k - 1, P, ysum);
-      else if (k > 0) finish<true>(k - 1, P, ysum);
+      if (!kMask) finish<false>(k - 1, P, uprev, ysum);
+      else if (k > 0) finish<true>(k - 1, P, uprev, ysum);
     }
+    uprev = uv;
     // Compiler-only fence: keep this block's LDS traffic in program order with
     // the next block's (the hardware already keeps one wavefront's in order).
     __builtin_amdgcn_wave_barrier();
@@ -259,7 +299,7 @@ struct Wave {
   }
 };
 
-template <typename T, Mode M, bool kSoftplus>
+template <typename T, Mode M, bool kSoftplus, int KP>
 __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   __shared__ __align__(16) float sB[2][kN][kGPitch];
   __shared__ __align__(16) float sC[M == Mode::kScan ? 2 : 1][kN][kGPitch];
@@ -285,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   const int64_t dw3 = std::min<int64_t>(dw0 + kRows - 1, p.dim - 1);
 
   constexpr int E = Elem<T>::kSize;
-  Wave<T, M, kSoftplus> w{p};
+  Wave<T, M, kSoftplus, KP> w{p};
   w.wave = wave; w.row = row; w.col = col;
   w.t_beg = g * p.seg_len;
   w.t_end = std::min(p.L, w.t_beg + p.seg_len);
@@ -328,6 +368,31 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   w.Dd = p.D ? p.D[dc] : 0.0f;
   w.sB = sB; w.sC = sC; w.sP = sP[M == Mode::kScan ? wave : 0];
 
+  // conv path: tap weights by lag, bias, the inputs just before this
+  // segment (x_{t_beg-16+col}: from the conv state at the sequence start,
+  // else from x itself), and the conv_out window
+  float xprev = 0.0f;
+  if constexpr (KP > 0) {
+    const int K = p.K;
+#pragma unroll
+    for (int m = 0; m < KP; ++m) w.wl[m] = m < K ? p.conv_w[dc * K + (K - 1 - m)] : 0.0f;
+    w.cb = p.conv_b ? p.conv_b[dc] : 0.0f;
+    w.silu_in = p.conv_silu != 0;
+    if (w.t_beg == 0) {
+      const int t = col - kT;  // token index before the sequence, -16 .. -1
+      xprev = (p.conv_in && t >= -K) ? p.conv_in[(b * p.dim + dc) * K + K + t] : 0.0f;
+    } else {
+      xprev = Elem<T>::f32(Elem<T>::load(w.wu.at(static_cast<uint32_t>(w.t_beg - kT) * E), w.ou));
+    }
+    if (p.conv_out) {
+      w.wco = rows_window(p.conv_out, p.cosb, p.cosd, w.oco);
+    } else {
+      w.wco = Window{nullptr, 0u};
+      w.oco = 0;
+    }
+  }
+  float uprev = 0.0f;
+
   // Initial state: zero for an aggregate segment; otherwise h0 (or zero) carried
   // through the aggregates of every earlier segment.
   float h = 0.0f;
@@ -357,19 +422,19 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   // form.
   const int nblk = w.nblk;
   const int nfull = (w.t_end - w.t_beg) / kT;
-  w.template iter<true, false>(0, h, ssum, buf3, buf0, buf2, grp);
+  w.template iter<true, false>(0, h, ssum, buf3, buf0, buf2, grp, uprev, xprev);
   int k = 1;
   for (; k + 4 <= nfull; k += 4) {
     // k % 4 == 1 here, and 4 is a multiple of kGB
-    w.template iter<false, (1 % kGB == kGB - 1)>(k + 0, h, ssum, buf0, buf1, buf3, grp);
-    w.template iter<false, (2 % kGB == kGB - 1)>(k + 1, h, ssum, buf1, buf2, buf0, grp);
-    w.template iter<false, (3 % kGB == kGB - 1)>(k + 2, h, ssum, buf2, buf3, buf1, grp);
-    w.template iter<false, (4 % kGB == kGB - 1)>(k + 3, h, ssum, buf3, buf0, buf2, grp);
+    w.template iter<false, (1 % kGB == kGB - 1)>(k + 0, h, ssum, buf0, buf1, buf3, grp, uprev, xprev);
+    w.template iter<false, (2 % kGB == kGB - 1)>(k + 1, h, ssum, buf1, buf2, buf0, grp, uprev, xprev);
+    w.template iter<false, (3 % kGB == kGB - 1)>(k + 2, h, ssum, buf2, buf3, buf1, grp, uprev, xprev);
+    w.template iter<false, (4 % kGB == kGB - 1)>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev);
   }
-  if (k < nblk) w.template iter<true, false>(k, h, ssum, buf0, buf1, buf3, grp);
-  if (k + 1 < nblk) w.template iter<true, false>(k + 1, h, ssum, buf1, buf2, buf0, grp);
-  if (k + 2 < nblk) w.template iter<true, false>(k + 2, h, ssum, buf2, buf3, buf1, grp);
-  if (k + 3 < nblk) w.template iter<true, false>(k + 3, h, ssum, buf3, buf0, buf2, grp);
+  if (k < nblk) w.template iter<true, false>(k, h, ssum, buf0, buf1, buf3, grp, uprev, xprev);
+  if (k + 1 < nblk) w.template iter<true, false>(k + 1, h, ssum, buf1, buf2, buf0, grp, uprev, xprev);
+  if (k + 2 < nblk) w.template iter<true, false>(k + 2, h, ssum, buf2, buf3, buf1, grp, uprev, xprev);
+  if (k + 3 < nblk) w.template iter<true, false>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev);
 
   if (M == Mode::kScan) {
     // finish the last block: its partials are in LDS, its raw inputs in buffer
@@ -380,8 +445,23 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
     float ysum = 0.0f;
 #pragma unroll
     for (int n = 0; n < kN; ++n) ysum += w.sP[row][n * kPitch + col];
-    w.template finish<true>(kl, last, ysum);
+    w.template finish<true>(kl, last, uprev, ysum);
     if (vrow && p.last_state && g == p.nseg - 1) p.last_state[(b * p.dim + d) * kN + col] = h;
+    if constexpr (KP > 0) {
+      // the last K inputs, for the decode update to continue from
+      const int K = p.K;
+      if (vrow && p.conv_stout && g == p.nseg - 1 && col < K) {
+        const int t = p.L - K + col;
+        float v;
+        if (t >= 0) {
+          const uint32_t orow = w.ou - static_cast<uint32_t>(col * E);
+          v = Elem<T>::f32(Elem<T>::load(w.wu.at(0), orow + static_cast<uint32_t>(t * E)));
+        } else {
+          v = p.conv_in ? p.conv_in[(b * p.dim + d) * K + K + t] : 0.0f;
+        }
+        p.conv_stout[(b * p.dim + d) * K + col] = v;
+      }
+    }
   } else {
     // segment aggregate: end state from zero and the step-size sum (fp64 partial
     // sums of the 16 owner lanes of each channel, added in a fixed order)
@@ -418,16 +498,24 @@ int choose_segments(int64_t groups, int64_t L) {
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(g, kMaxSeg)));
 }
 
-template <Mode M>
-void launch(bool bf16, bool softplus, dim3 grid, const ScanParams& p, hipStream_t stream) {
+template <Mode M, int KP>
+void launch_kp(bool bf16, bool softplus, dim3 grid, const ScanParams& p, hipStream_t stream) {
   const dim3 block(kThreads);
   if (bf16) {
-    if (softplus) scan_fwd_kernel<uint16_t, M, true><<<grid, block, 0, stream>>>(p);
-    else scan_fwd_kernel<uint16_t, M, false><<<grid, block, 0, stream>>>(p);
+    if (softplus) scan_fwd_kernel<uint16_t, M, true, KP><<<grid, block, 0, stream>>>(p);
+    else scan_fwd_kernel<uint16_t, M, false, KP><<<grid, block, 0, stream>>>(p);
   } else {
-    if (softplus) scan_fwd_kernel<float, M, true><<<grid, block, 0, stream>>>(p);
-    else scan_fwd_kernel<float, M, false><<<grid, block, 0, stream>>>(p);
+    if (softplus) scan_fwd_kernel<float, M, true, KP><<<grid, block, 0, stream>>>(p);
+    else scan_fwd_kernel<float, M, false, KP><<<grid, block, 0, stream>>>(p);
   }
+}
+
+// The conv width is padded to 4 or 8 taps (zero weights), the two kernel sizes.
+template <Mode M>
+void launch(bool bf16, bool softplus, int K, dim3 grid, const ScanParams& p, hipStream_t stream) {
+  if (K == 0) launch_kp<M, 0>(bf16, softplus, grid, p, stream);
+  else if (K <= 4) launch_kp<M, 4>(bf16, softplus, grid, p, stream);
+  else launch_kp<M, 8>(bf16, softplus, grid, p, stream);
 }
 
 }  // namespace
@@ -443,6 +531,7 @@ bool scan_windows_fit(const ssm_scan_args& a) {
             fits((kN - 1) * a.B_state_stride + a.seqlen) &&
             fits((kN - 1) * a.C_state_stride + a.seqlen);
   if (a.z) ok = ok && fits(rows * a.z_dim_stride + a.seqlen);
+  if (a.conv_weight && a.conv_out) ok = ok && fits(rows * a.conv_out_dim_stride + a.seqlen);
   return ok;
 }
 
@@ -456,10 +545,17 @@ size_t scan_workspace_bytes(const ssm_scan_args& a) {
 
 hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {
   if (a.seqlen == 0) {
-    if (!a.last_state || a.last_state == a.h0) return hipSuccess;
-    const int64_t n = a.batch * a.dim * a.dstate;
-    copy_state_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(
-        a.h0, a.last_state, n);
+    // no token: the final states are the initial ones
+    if (a.last_state && a.last_state != a.h0) {
+      const int64_t n = a.batch * a.dim * a.dstate;
+      copy_state_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(
+          a.h0, a.last_state, n);
+    }
+    if (a.conv_weight && a.conv_state_out) {
+      const int64_t n = a.batch * a.dim * a.d_conv;
+      copy_state_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(
+          a.conv_state_in, a.conv_state_out, n);
+    }
     return hipGetLastError();
   }
   ScanParams p;
@@ -488,14 +584,19 @@ hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {
   p.nseg = static_cast<int>((a.seqlen + p.seg_len - 1) / p.seg_len);
   p.agg = p.nseg > 1 ? static_cast<float*>(a.workspace) : nullptr;
   p.ckpt = a.checkpoints;
+  p.K = a.conv_weight ? a.d_conv : 0;
+  p.conv_w = a.conv_weight; p.conv_b = a.conv_bias; p.conv_in = a.conv_state_in;
+  p.conv_stout = a.conv_state_out; p.conv_out = a.conv_out;
+  p.cosb = a.conv_out_batch_stride; p.cosd = a.conv_out_dim_stride;
+  p.conv_silu = a.conv_silu;
   p.nbk = static_cast<int>((a.seqlen + kT - 1) / kT);
 
   if (p.nseg > 1) {
     const dim3 g1((unsigned)(groups * (p.nseg - 1)));
-    launch<Mode::kAggregate>(a.io_dtype == SSM_BF16, a.delta_softplus != 0, g1, p, stream);
+    launch<Mode::kAggregate>(a.io_dtype == SSM_BF16, a.delta_softplus != 0, p.K, g1, p, stream);
   }
   const dim3 g2((unsigned)(groups * p.nseg));
-  launch<Mode::kScan>(a.io_dtype == SSM_BF16, a.delta_softplus != 0, g2, p, stream);
+  launch<Mode::kScan>(a.io_dtype == SSM_BF16, a.delta_softplus != 0, p.K, g2, p, stream);
   return hipGetLastError();
 }
 

@@ -95,34 +95,53 @@ int ssm_validate_scan(const ssm_scan_args* a) {
       misaligned(a->h0, 4) || misaligned(a->last_state, 4) || misaligned(a->workspace, 4))
     return SSM_ERR_ALIGN;
 
-  const Span su = span3(a->u, B, a->u_batch_stride, Dm, a->u_dim_stride, L, esz);
-  const Span sdl = span3(a->delta, B, a->delta_batch_stride, Dm, a->delta_dim_stride, L, esz);
-  const Span sz = span3(a->z, B, a->z_batch_stride, Dm, a->z_dim_stride, L, esz);
-  const Span sB = span3(a->B, B, a->B_batch_stride, N, a->B_state_stride, L, esz);
-  const Span sC = span3(a->C, B, a->C_batch_stride, N, a->C_state_stride, L, esz);
-  const Span sA = L > 0 ? span3(a->A, 1, 0, Dm, a->A_dim_stride, 1, 4) : Span{};
-  Span sA_full = sA;
-  if (L > 0 && a->A) sA_full.hi += static_cast<uintptr_t>((N - 1) * a->A_state_stride * 4);
-  const Span sD = span1(a->D, Dm, 4), sbias = span1(a->delta_bias, Dm, 4);
+  if (misaligned(a->checkpoints, 4) || misaligned(a->conv_weight, 4) ||
+      misaligned(a->conv_bias, 4) || misaligned(a->conv_state_in, 4) ||
+      misaligned(a->conv_state_out, 4))
+    return SSM_ERR_ALIGN;
+  int64_t K = 0;
+  if (a->conv_weight) {
+    K = a->d_conv;
+    if (K < 1) return SSM_ERR_SHAPE;
+    if (K > SSM_MAX_CONV) return SSM_ERR_UNSUPPORTED;
+    if (L > 0 && a->conv_out) {
+      if (a->conv_out_batch_stride < 0 || a->conv_out_dim_stride < 0) return SSM_ERR_STRIDE;
+      if (misaligned(a->conv_out, esz)) return SSM_ERR_ALIGN;
+    }
+  }
+
+  const Span sA = L > 0 ? Span{reinterpret_cast<uintptr_t>(a->A),
+                               reinterpret_cast<uintptr_t>(a->A) +
+                                   static_cast<uintptr_t>(((Dm - 1) * a->A_dim_stride +
+                                                           (N - 1) * a->A_state_stride + 1) * 4)}
+                        : Span{};
   const Span sh0 = span1(a->h0, B * Dm * N, 4);
-  const Span sout = span3(a->out, B, a->out_batch_stride, Dm, a->out_dim_stride, L, esz);
+  const Span inputs[] = {
+      span3(a->u, B, a->u_batch_stride, Dm, a->u_dim_stride, L, esz),
+      span3(a->delta, B, a->delta_batch_stride, Dm, a->delta_dim_stride, L, esz),
+      span3(a->z, B, a->z_batch_stride, Dm, a->z_dim_stride, L, esz),
+      span3(a->B, B, a->B_batch_stride, N, a->B_state_stride, L, esz),
+      span3(a->C, B, a->C_batch_stride, N, a->C_state_stride, L, esz),
+      sA, span1(a->D, Dm, 4), span1(a->delta_bias, Dm, 4), sh0,
+      span1(a->conv_weight, Dm * K, 4), span1(a->conv_bias, Dm, 4),
+      span1(a->conv_state_in, B * Dm * K, 4)};
   const Span sls = span1(a->last_state, B * Dm * N, 4);
-  const Span inputs[] = {su, sdl, sz, sB, sC, sA_full, sD, sbias, sh0};
-  for (const Span& s : inputs)
-    if (overlap(sout, s)) return SSM_ERR_ALIAS;
-  for (int i = 0; i < 8; ++i)
-    if (overlap(sls, inputs[i])) return SSM_ERR_ALIAS;
-  if (overlap(sls, sout)) return SSM_ERR_ALIAS;
-  if (overlap(sls, sh0) && a->last_state != a->h0) return SSM_ERR_ALIAS;
-  const Span sws = span1(a->workspace, static_cast<int64_t>(a->workspace_bytes), 1);
-  for (const Span& s : inputs)
-    if (overlap(sws, s)) return SSM_ERR_ALIAS;
-  if (overlap(sws, sout) || overlap(sws, sls)) return SSM_ERR_ALIAS;
-  if (misaligned(a->checkpoints, 4)) return SSM_ERR_ALIGN;
-  const Span sck = span1(a->checkpoints, B * Dm * ((L + kCkptTokens - 1) / kCkptTokens) * N, 4);
-  for (const Span& s : inputs)
-    if (overlap(sck, s)) return SSM_ERR_ALIAS;
-  if (overlap(sck, sout) || overlap(sck, sls) || overlap(sck, sws)) return SSM_ERR_ALIAS;
+  const Span outputs[] = {
+      span3(a->out, B, a->out_batch_stride, Dm, a->out_dim_stride, L, esz), sls,
+      span1(a->workspace, static_cast<int64_t>(a->workspace_bytes), 1),
+      span1(a->checkpoints, B * Dm * ((L + kCkptTokens - 1) / kCkptTokens) * N, 4),
+      K ? span1(a->conv_state_out, B * Dm * K, 4) : Span{},
+      K ? span3(a->conv_out, B, a->conv_out_batch_stride, Dm, a->conv_out_dim_stride, L, esz)
+        : Span{}};
+  for (const Span& o : outputs) {
+    for (const Span& i : inputs) {
+      // last_state may be exactly h0 (the state carried in place)
+      if (&o == &outputs[1] && &i == &inputs[8] && a->last_state == a->h0) continue;
+      if (overlap(o, i)) return SSM_ERR_ALIAS;
+    }
+    for (const Span& o2 : outputs)
+      if (&o2 != &o && overlap(o, o2)) return SSM_ERR_ALIAS;
+  }
   return SSM_OK;
 }
 
@@ -223,10 +242,23 @@ int ssm_validate_update(const ssm_update_args* a) {
   const Span sA = span3(a->A, 1, 0, Dm, a->A_dim_stride, N, 4);
   const Span sD = span1(a->D, Dm, 4), sbias = span1(a->dt_bias, Dm, 4);
   const Span sout = span3(a->out, 1, 0, B, a->out_batch_stride, Dm, esz);
-  const Span inputs[] = {sx, sdt, sz, sB, sC, sA, sD, sbias};
+  int64_t K = 0;
+  if (a->conv_weight) {
+    K = a->d_conv;
+    if (K < 1) return SSM_ERR_SHAPE;
+    if (K > SSM_MAX_CONV) return SSM_ERR_UNSUPPORTED;
+    if (!a->conv_state) return SSM_ERR_NULL;
+    if (misaligned(a->conv_state, 4) || misaligned(a->conv_weight, 4) ||
+        misaligned(a->conv_bias, 4))
+      return SSM_ERR_ALIGN;
+  }
+  const Span scs = span1(K ? a->conv_state : nullptr, B * Dm * K, 4);
+  const Span inputs[] = {sx, sdt, sz, sB, sC, sA, sD, sbias,
+                         span1(K ? a->conv_weight : nullptr, Dm * K, 4),
+                         span1(K ? a->conv_bias : nullptr, Dm, 4)};
   for (const Span& s : inputs)
-    if (overlap(sout, s) || overlap(sst, s)) return SSM_ERR_ALIAS;
-  if (overlap(sout, sst)) return SSM_ERR_ALIAS;
+    if (overlap(sout, s) || overlap(sst, s) || overlap(scs, s)) return SSM_ERR_ALIAS;
+  if (overlap(sout, sst) || overlap(sout, scs) || overlap(sst, scs)) return SSM_ERR_ALIAS;
   return SSM_OK;
 }
 

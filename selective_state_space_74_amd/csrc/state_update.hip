@@ -24,6 +24,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChannelsPerBlock = kThreads / 4;
+constexpr int kMaxConv = SSM_MAX_CONV;
 
 struct UpdateParams {
   float* state;
@@ -39,6 +40,13 @@ struct UpdateParams {
   int64_t ssb, ssd, xsb, dtsb, zsb, Bsb, Csb, Asd, osb;
   int64_t batch, dim;
   int softplus;
+  // fused conv branch: [batch][dim][K] state shifted in place, [dim][K]
+  // weights, [dim] bias (or NULL)
+  float* conv_state;
+  const float* conv_w;
+  const float* conv_b;
+  int K;
+  int conv_silu;
 };
 
 template <typename T> struct Vec4;
@@ -67,7 +75,12 @@ __device__ __forceinline__ void load4(const T* p, float (&v)[4]) {
 }
 
 // VEC: state rows, A rows and B/C quads are aligned for one vector access each.
-template <typename T, bool VEC>
+// CONV: x is the conv input.  CONV == 1 (width <= 4): lane q of the channel's
+// quad holds conv state element q, takes element q+1 from its neighbour by a
+// DPP quad permute (the newest, x, at q = K-1), and the quad sums the four
+// weighted taps.  CONV == 2 (width 5..8): every lane of the quad forms the
+// whole sum and lane q writes back the elements k = q, q + 4.
+template <typename T, bool VEC, int CONV>
 __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p) {
   const int q = threadIdx.x & 3;
   const int64_t b = blockIdx.y;
@@ -81,7 +94,44 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p) 
   load4<float, VEC>(p.A + d * p.Asd + 4 * q, a);
   load4<T, VEC>(static_cast<const T*>(p.B) + b * p.Bsb + 4 * q, bb);
   load4<T, VEC>(static_cast<const T*>(p.C) + b * p.Csb + 4 * q, cc);
-  const float xv = io<T>::load(static_cast<const T*>(p.x) + b * p.xsb + d);
+  float xv = io<T>::load(static_cast<const T*>(p.x) + b * p.xsb + d);
+  if constexpr (CONV == 1) {
+    // causal conv of the block's conv branch: shift in x, then the weighted
+    // sum of the K newest inputs (Mamba model notes, section 4.3)
+    const int K = p.K;
+    float* cs = p.conv_state + (b * p.dim + d) * K;
+    const int qk = min(q, K - 1);                     // lanes past K stay in the row
+    const float old = cs[qk];
+    const float nb = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(old), 0xF9, 0xf, 0xf, true));
+    const float nv = q == K - 1 ? xv : nb;            // element q of the shifted state
+    float acc = q < K ? p.conv_w[d * K + q] * nv : 0.0f;
+    acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xf, 0xf, true));
+    acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xf, 0xf, true));
+    if (p.conv_b) acc += p.conv_b[d];
+    if (ok && q < K) cs[q] = nv;
+    xv = p.conv_silu ? silu_f32(acc) : acc;
+  } else if constexpr (CONV == 2) {
+    const int K = p.K;
+    float* cs = p.conv_state + (b * p.dim + d) * K;
+    const float* cw = p.conv_w + d * K;
+    float acc = p.conv_b ? p.conv_b[d] : 0.0f;
+    float nv[kMaxConv];
+#pragma unroll
+    for (int k = 0; k < kMaxConv; ++k) {
+      if (k < K) {
+        nv[k] = k + 1 < K ? cs[k + 1] : xv;
+        acc = fmaf(cw[k], nv[k], acc);
+      }
+    }
+    // all four lanes have read the old state before any lane writes
+    __builtin_amdgcn_wave_barrier();
+    if (ok) {
+#pragma unroll
+      for (int k = 0; k < kMaxConv; ++k)
+        if (k < K && (k & 3) == q) cs[k] = nv[k];
+    }
+    xv = p.conv_silu ? silu_f32(acc) : acc;
+  }
   const float dtv = io<T>::load(static_cast<const T*>(p.dt) + b * p.dtsb + d);
   const float zv = p.z ? io<T>::load(static_cast<const T*>(p.z) + b * p.zsb + d) : 0.0f;
 
@@ -113,6 +163,19 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p) 
   }
 }
 
+template <typename T, bool VEC>
+void launch_v(int conv, dim3 grid, dim3 block, const UpdateParams& p, hipStream_t stream) {
+  if (conv == 0) state_update_kernel<T, VEC, 0><<<grid, block, 0, stream>>>(p);
+  else if (conv == 1) state_update_kernel<T, VEC, 1><<<grid, block, 0, stream>>>(p);
+  else state_update_kernel<T, VEC, 2><<<grid, block, 0, stream>>>(p);
+}
+
+template <typename T>
+void launch_t(bool vec, int conv, dim3 grid, dim3 block, const UpdateParams& p, hipStream_t stream) {
+  if (vec) launch_v<T, true>(conv, grid, block, p, stream);
+  else launch_v<T, false>(conv, grid, block, p, stream);
+}
+
 }  // namespace
 
 hipError_t launch_state_update(const ssm_update_args& a, hipStream_t stream) {
@@ -132,17 +195,17 @@ hipError_t launch_state_update(const ssm_update_args& a, hipStream_t stream) {
                    (reinterpret_cast<uintptr_t>(a.B) % (4 * esz) == 0) &&
                    (reinterpret_cast<uintptr_t>(a.C) % (4 * esz) == 0) &&
                    (a.B_batch_stride % 4 == 0) && (a.C_batch_stride % 4 == 0);
+  p.conv_state = a.conv_weight ? a.conv_state : nullptr;
+  p.conv_w = a.conv_weight; p.conv_b = a.conv_bias;
+  p.K = a.conv_weight ? a.d_conv : 0;
+  p.conv_silu = a.conv_silu;
   const int64_t xblocks = (a.dim + kChannelsPerBlock - 1) / kChannelsPerBlock;
   if (xblocks > 0x7fffffff || a.batch > 65535) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(xblocks), static_cast<unsigned>(a.batch));
   const dim3 block(kThreads);
-  if (a.io_dtype == SSM_BF16) {
-    if (vec) state_update_kernel<uint16_t, true><<<grid, block, 0, stream>>>(p);
-    else state_update_kernel<uint16_t, false><<<grid, block, 0, stream>>>(p);
-  } else {
-    if (vec) state_update_kernel<float, true><<<grid, block, 0, stream>>>(p);
-    else state_update_kernel<float, false><<<grid, block, 0, stream>>>(p);
-  }
+  const int conv = a.conv_weight == nullptr ? 0 : (a.d_conv <= 4 ? 1 : 2);
+  if (a.io_dtype == SSM_BF16) launch_t<uint16_t>(vec, conv, grid, block, p, stream);
+  else launch_t<float>(vec, conv, grid, block, p, stream);
   return hipGetLastError();
 }
 

@@ -36,12 +36,13 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_struct_layout():
     L = ssm.lib()
-    assert L.ssm_abi_version() == ssm.SSM_ABI_VERSION == 2
+    assert L.ssm_abi_version() == ssm.SSM_ABI_VERSION == 3
     assert L.ssm_scan_args_size() == ctypes.sizeof(ssm.ScanArgs)
     assert L.ssm_scan_bwd_args_size() == ctypes.sizeof(ssm.ScanBwdArgs)
     assert L.ssm_update_args_size() == ctypes.sizeof(ssm.UpdateArgs)
     header = open(HEADER).read()
-    assert "#define SSM_ABI_VERSION 2" in header
+    assert "#define SSM_ABI_VERSION 3" in header
+    assert f"#define SSM_MAX_CONV {ssm.MAX_CONV}" in header
     assert f"#define SSM_CHECKPOINT_TOKENS {ssm.CHECKPOINT_TOKENS}" in header
 
 
@@ -328,3 +329,29 @@ def test_forward_checkpoints_validated():
     assert ssm.validate_scan(a) == ALIAS
     a.checkpoints = addr(11) + 2      # misaligned
     assert ssm.validate_scan(a) == ALIGN
+
+
+def test_conv_fields_validated():
+    a = good_scan()
+    a.conv_weight, a.d_conv, a.conv_silu = addr(12), 4, 1
+    a.conv_bias, a.conv_state_in, a.conv_state_out = addr(13), addr(14), addr(15)
+    assert ssm.validate_scan(a) == OK
+    a.d_conv = 0
+    assert ssm.validate_scan(a) == SHAPE
+    a.d_conv = 9
+    assert ssm.validate_scan(a) == UNSUP
+    a.d_conv = 4
+    a.conv_state_out = a.conv_state_in            # output onto an input
+    assert ssm.validate_scan(a) == ALIAS
+    a.conv_state_out = addr(15)
+    a.conv_out, a.conv_out_batch_stride, a.conv_out_dim_stride = addr(16), 32 * 64, 64
+    assert ssm.validate_scan(a) == OK
+    a.conv_out = a.out                            # two outputs
+    assert ssm.validate_scan(a) == ALIAS
+    u = good_update()
+    u.conv_weight, u.d_conv = addr(10), 4
+    assert ssm.validate_update(u) == NULL         # conv_state required
+    u.conv_state = addr(11)
+    assert ssm.validate_update(u) == OK
+    u.conv_state = u.state
+    assert ssm.validate_update(u) == ALIAS
