@@ -41,13 +41,13 @@ def _load():
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         lib.oracle_selective_scan_f64.restype = ctypes.c_int
-        lib.oracle_selective_scan_f64.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, P, P,
+        lib.oracle_selective_scan_f64.argtypes = [I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P,
                                                   ctypes.c_int, P, P, P, ctypes.c_int]
         lib.oracle_state_update_f64.restype = ctypes.c_int
-        lib.oracle_state_update_f64.argtypes = [I64, I64, I64, P, P, P, P, P, P, P, P, P,
+        lib.oracle_state_update_f64.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, P, P, P,
                                                 ctypes.c_int, P, ctypes.c_int]
         lib.oracle_selective_scan_bwd_f64.restype = ctypes.c_int
-        lib.oracle_selective_scan_bwd_f64.argtypes = [I64, I64, I64, I64] + [P] * 8 + [
+        lib.oracle_selective_scan_bwd_f64.argtypes = [I64, I64, I64, I64, I64] + [P] * 8 + [
             ctypes.c_int] + [P] * 12 + [ctypes.c_int]
         lib.oracle_causal_conv1d_f64.restype = ctypes.c_int
         lib.oracle_causal_conv1d_f64.argtypes = [I64, I64, I64, I64, P, P, P, P, ctypes.c_int,
@@ -99,6 +99,17 @@ def _ptr(x):
     return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
 
 
+def _groups(B, C, batch, dim, N, tail):
+    """Number of B/C groups from the shape of B: (batch, N, *tail) is one
+    group, (batch, G, N, *tail) is G groups of dim // G channels."""
+    assert B.shape == C.shape
+    if B.shape == (batch, N) + tail:
+        return 1
+    G = B.shape[1]
+    assert B.shape == (batch, G, N) + tail and G >= 1 and dim % G == 0
+    return G
+
+
 def softplus(x: float) -> float:
     return _load().oracle_softplus(float(x))
 
@@ -111,18 +122,20 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
                    h0=None, return_last_state=False, nthreads=0):
     """out[b,d,t] (and last_state[b,d,n]) in fp64.
 
-    u, delta, z: (batch, dim, L); B, C: (batch, N, L); A: (dim, N);
-    D, delta_bias: (dim,); h0: (batch, dim, N)."""
+    u, delta, z: (batch, dim, L); B, C: (batch, N, L), or (batch, G, N, L)
+    with channel d reading group d // (dim // G); A: (dim, N); D, delta_bias:
+    (dim,); h0: (batch, dim, N)."""
     lib = _load()
     u, delta, z, B, C, A, D, delta_bias, h0 = map(_f64, (u, delta, z, B, C, A, D, delta_bias, h0))
     batch, dim, L = u.shape
     N = A.shape[1]
     assert N <= 1024
     assert delta.shape == u.shape and (z is None or z.shape == u.shape)
-    assert B.shape == (batch, N, L) and C.shape == (batch, N, L) and A.shape == (dim, N)
+    G = _groups(B, C, batch, dim, N, (L,))
+    assert A.shape == (dim, N)
     out = np.empty_like(u)
     last = np.empty((batch, dim, N)) if return_last_state else None
-    used = lib.oracle_selective_scan_f64(batch, dim, L, N, _ptr(u), _ptr(delta), _ptr(z),
+    used = lib.oracle_selective_scan_f64(batch, dim, L, N, G, _ptr(u), _ptr(delta), _ptr(z),
                                          _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(delta_bias),
                                          int(bool(delta_softplus)), _ptr(h0), _ptr(out),
                                          _ptr(last), int(nthreads))
@@ -139,9 +152,10 @@ def state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplu
     x, dt, z, B, C, A, D, dt_bias = map(_f64, (x, dt, z, B, C, A, D, dt_bias))
     batch, dim, N = s.shape
     assert x.shape == (batch, dim) and dt.shape == (batch, dim)
-    assert B.shape == (batch, N) and C.shape == (batch, N) and A.shape == (dim, N)
+    G = _groups(B, C, batch, dim, N, ())
+    assert A.shape == (dim, N)
     out = np.empty((batch, dim))
-    used = lib.oracle_state_update_f64(batch, dim, N, _ptr(s), _ptr(x), _ptr(dt), _ptr(z),
+    used = lib.oracle_state_update_f64(batch, dim, N, G, _ptr(s), _ptr(x), _ptr(dt), _ptr(z),
                                        _ptr(B), _ptr(C), _ptr(A), _ptr(D), _ptr(dt_bias),
                                        int(bool(dt_softplus)), _ptr(out), int(nthreads))
     state_update.last_threads = used
@@ -160,15 +174,16 @@ def selective_scan_bwd(dout, u, delta, A, B, C, D=None, z=None, delta_bias=None,
     batch, dim, L = u.shape
     N = A.shape[1]
     assert dout.shape == u.shape and (dlast is None or dlast.shape == (batch, dim, N))
-    assert B.shape == (batch, N, L) and C.shape == (batch, N, L) and A.shape == (dim, N)
-    g = dict(du=np.empty_like(u), ddelta=np.empty_like(u), dB=np.empty((batch, N, L)),
-             dC=np.empty((batch, N, L)), dA=np.empty((dim, N)))
+    G = _groups(B, C, batch, dim, N, (L,))
+    assert A.shape == (dim, N)
+    g = dict(du=np.empty_like(u), ddelta=np.empty_like(u), dB=np.empty(B.shape),
+             dC=np.empty(B.shape), dA=np.empty((dim, N)))
     g["dz"] = np.empty_like(u) if z is not None else None
     g["dD"] = np.empty(dim) if D is not None else None
     g["ddelta_bias"] = np.empty(dim) if delta_bias is not None else None
     g["dh0"] = np.empty((batch, dim, N)) if h0 is not None else None
     used = lib.oracle_selective_scan_bwd_f64(
-        batch, dim, L, N, _ptr(u), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
+        batch, dim, L, N, G, _ptr(u), _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(D),
         _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(dout), _ptr(dlast),
         _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dz"]), _ptr(g["dB"]), _ptr(g["dC"]),
         _ptr(g["dA"]), _ptr(g["dD"]), _ptr(g["ddelta_bias"]), _ptr(g["dh0"]), int(nthreads))

@@ -42,12 +42,14 @@
  *
  * Layouts (all contiguous, row-major):
  *   u, delta, z, out : (batch, dim, seqlen)
- *   Bm, Cm           : (batch, dstate, seqlen)
+ *   Bm, Cm           : (batch, ngroups, dstate, seqlen); channel d reads
+ *                      group d / (dim / ngroups) (ngroups = 1: one B_t, C_t
+ *                      per token shared by every channel, as in the pages)
  *   A                : (dim, dstate)
  *   Dv, bias         : (dim)
  *   h0, last_state   : (batch, dim, dstate)
  * Decode: state (batch, dim, dstate); x, dt, z, out (batch, dim);
- *         Bm, Cm (batch, dstate).
+ *         Bm, Cm (batch, ngroups, dstate).
  */
 #include <math.h>
 #include <stddef.h>
@@ -70,14 +72,15 @@ static double step_size(double dt, const double* bias, int64_t d, int softplus) 
 }
 
 /* One (batch, channel) row of the prefill scan, strictly sequential in t. */
-static void scan_row(int64_t b, int64_t d, int64_t dim, int64_t L, int64_t N,
+static void scan_row(int64_t b, int64_t d, int64_t dim, int64_t L, int64_t N, int64_t G,
                      const double* u, const double* delta, const double* z,
                      const double* Bm, const double* Cm, const double* A,
                      const double* Dv, const double* bias, int softplus,
                      const double* h0, double* out, double* last_state, double* h) {
   const int64_t row = (b * dim + d) * L;
-  const double* Bb = Bm + b * N * L;
-  const double* Cb = Cm + b * N * L;
+  const int64_t grp = b * G + d / (dim / G);           /* this channel's B/C group */
+  const double* Bb = Bm + grp * N * L;
+  const double* Cb = Cm + grp * N * L;
   for (int64_t n = 0; n < N; ++n) h[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;
   for (int64_t t = 0; t < L; ++t) {
     const double ut = u[row + t];
@@ -101,7 +104,7 @@ static void scan_row(int64_t b, int64_t d, int64_t dim, int64_t L, int64_t N,
  * spread over OpenMP threads (nthreads <= 0 means the runtime default). The
  * recurrence over t inside a row stays sequential. Returns the thread count. */
 int oracle_selective_scan_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
-                              const double* u, const double* delta, const double* z,
+                              int64_t ngroups, const double* u, const double* delta, const double* z,
                               const double* Bm, const double* Cm, const double* A,
                               const double* Dv, const double* bias, int softplus,
                               const double* h0, double* out, double* last_state,
@@ -116,14 +119,14 @@ int oracle_selective_scan_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_
     double h[1024];
 #pragma omp for schedule(dynamic, 1)
     for (int64_t r = 0; r < batch * dim; ++r)
-      scan_row(r / dim, r % dim, dim, seqlen, dstate, u, delta, z, Bm, Cm, A, Dv, bias,
+      scan_row(r / dim, r % dim, dim, seqlen, dstate, ngroups, u, delta, z, Bm, Cm, A, Dv, bias,
                softplus, h0, out, last_state, h);
   }
 #else
   (void)nthreads;
   double h[1024];
   for (int64_t r = 0; r < batch * dim; ++r)
-    scan_row(r / dim, r % dim, dim, seqlen, dstate, u, delta, z, Bm, Cm, A, Dv, bias,
+    scan_row(r / dim, r % dim, dim, seqlen, dstate, ngroups, u, delta, z, Bm, Cm, A, Dv, bias,
              softplus, h0, out, last_state, h);
 #endif
   return used;
@@ -132,26 +135,29 @@ int oracle_selective_scan_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_
 /* Decode: one token per (batch, channel); state updated in place.  Written as
  * its own loop body (not a call into scan_row) so that "decode equals scan" is
  * a real check between two pieces of code. */
-static void update_row(int64_t r, int64_t dim, int64_t N, double* state,
+static void update_row(int64_t r, int64_t dim, int64_t N, int64_t G, double* state,
                        const double* x, const double* dt, const double* z,
                        const double* Bm, const double* Cm, const double* A,
                        const double* Dv, const double* bias, int softplus, double* out) {
   const int64_t b = r / dim, d = r % dim;
+  const double* Bt = Bm + (b * G + d / (dim / G)) * N;  /* this channel's group */
+  const double* Ct = Cm + (b * G + d / (dim / G)) * N;
   const double xt = x[r];
   double dl = dt[r] + (bias ? bias[d] : 0.0);
   if (softplus) dl = oracle_softplus(dl);
   double* s = state + r * N;
   double y = 0.0;
   for (int64_t n = 0; n < N; ++n) {
-    s[n] = exp(dl * A[d * N + n]) * s[n] + dl * Bm[b * N + n] * xt;
-    y += Cm[b * N + n] * s[n];
+    s[n] = exp(dl * A[d * N + n]) * s[n] + dl * Bt[n] * xt;
+    y += Ct[n] * s[n];
   }
   if (Dv) y += Dv[d] * xt;
   if (z) y *= oracle_silu(z[r]);
   out[r] = y;
 }
 
-int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, double* state,
+int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, int64_t ngroups,
+                            double* state,
                             const double* x, const double* dt, const double* z,
                             const double* Bm, const double* Cm, const double* A,
                             const double* Dv, const double* bias, int softplus,
@@ -165,12 +171,12 @@ int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, double* 
     used = omp_get_num_threads();
 #pragma omp for schedule(static)
     for (int64_t r = 0; r < batch * dim; ++r)
-      update_row(r, dim, dstate, state, x, dt, z, Bm, Cm, A, Dv, bias, softplus, out);
+      update_row(r, dim, dstate, ngroups, state, x, dt, z, Bm, Cm, A, Dv, bias, softplus, out);
   }
 #else
   (void)nthreads;
   for (int64_t r = 0; r < batch * dim; ++r)
-    update_row(r, dim, dstate, state, x, dt, z, Bm, Cm, A, Dv, bias, softplus, out);
+    update_row(r, dim, dstate, ngroups, state, x, dt, z, Bm, Cm, A, Dv, bias, softplus, out);
 #endif
   return used;
 }
@@ -197,7 +203,7 @@ int oracle_state_update_f64(int64_t batch, int64_t dim, int64_t dstate, double* 
  * ------------------------------------------------------------------------ */
 static double logistic(double x) { return 1.0 / (1.0 + exp(-x)); }
 
-static void scan_row_bwd(int64_t b, int64_t d, int64_t dim, int64_t L, int64_t N,
+static void scan_row_bwd(int64_t b, int64_t d, int64_t dim, int64_t L, int64_t N, int64_t G,
                          const double* u, const double* delta, const double* z,
                          const double* Bm, const double* Cm, const double* A,
                          const double* Dv, const double* bias, int softplus,
@@ -206,8 +212,9 @@ static void scan_row_bwd(int64_t b, int64_t d, int64_t dim, int64_t L, int64_t N
                          double* dBrow, double* dCrow, double* dArow, double* dDrow,
                          double* dbrow, double* dh0, double* hs, double* es, double* g) {
   const int64_t row = (b * dim + d) * L;
-  const double* Bb = Bm + b * N * L;
-  const double* Cb = Cm + b * N * L;
+  const int64_t grp = b * G + d / (dim / G);
+  const double* Bb = Bm + grp * N * L;
+  const double* Cb = Cm + grp * N * L;
   /* forward again, keeping every h_t and e_t (hs[(t+1)*N + n] = h_t, hs[n] = h_{-1}) */
   for (int64_t n = 0; n < N; ++n) hs[n] = h0 ? h0[(b * dim + d) * N + n] : 0.0;
   for (int64_t t = 0; t < L; ++t) {
@@ -263,18 +270,19 @@ static void scan_row_bwd(int64_t b, int64_t d, int64_t dim, int64_t L, int64_t N
 }
 
 /* Gradients of the prefill scan.  Outputs: du, ddelta (batch, dim, L); dz
- * (when z is given); dB, dC (batch, N, L); dA (dim, N); dD, dbias (dim; when
+ * (when z is given); dB, dC (batch, ngroups, N, L), each summed over the
+ * channels of its group; dA (dim, N); dD, dbias (dim; when
  * D / bias are given); dh0 (batch, dim, N; when h0 is given).  dlast may be
  * NULL (no gradient on last_state).  Returns the thread count used. */
 int oracle_selective_scan_bwd_f64(int64_t batch, int64_t dim, int64_t seqlen, int64_t dstate,
-                                  const double* u, const double* delta, const double* z,
+                                  int64_t ngroups, const double* u, const double* delta, const double* z,
                                   const double* Bm, const double* Cm, const double* A,
                                   const double* Dv, const double* bias, int softplus,
                                   const double* h0, const double* dout, const double* dlast,
                                   double* du, double* ddelta, double* dz, double* dB,
                                   double* dC, double* dA, double* dD, double* dbias,
                                   double* dh0, int nthreads) {
-  const int64_t L = seqlen, N = dstate, rows = batch * dim;
+  const int64_t L = seqlen, N = dstate, G = ngroups, rows = batch * dim;
   double* dBrows = (double*)calloc((size_t)(rows * N * L > 0 ? rows * N * L : 1), sizeof(double));
   double* dCrows = (double*)calloc((size_t)(rows * N * L > 0 ? rows * N * L : 1), sizeof(double));
   double* dArows = (double*)calloc((size_t)(rows * N > 0 ? rows * N : 1), sizeof(double));
@@ -292,7 +300,7 @@ int oracle_selective_scan_bwd_f64(int64_t batch, int64_t dim, int64_t seqlen, in
     double* g = (double*)malloc(sizeof(double) * (size_t)N);
 #pragma omp for schedule(dynamic, 1)
     for (int64_t r = 0; r < rows; ++r)
-      scan_row_bwd(r / dim, r % dim, dim, L, N, u, delta, z, Bm, Cm, A, Dv, bias, softplus, h0,
+      scan_row_bwd(r / dim, r % dim, dim, L, N, G, u, delta, z, Bm, Cm, A, Dv, bias, softplus, h0,
                    dout, dlast, du, ddelta, dz, dBrows + r * N * L, dCrows + r * N * L,
                    dArows + r * N, dDrows + r, dbrows + r, dh0, hs, es, g);
     free(hs); free(es); free(g);
@@ -304,23 +312,25 @@ int oracle_selective_scan_bwd_f64(int64_t batch, int64_t dim, int64_t seqlen, in
     double* es = (double*)malloc(sizeof(double) * (size_t)(L * N + 1));
     double* g = (double*)malloc(sizeof(double) * (size_t)N);
     for (int64_t r = 0; r < rows; ++r)
-      scan_row_bwd(r / dim, r % dim, dim, L, N, u, delta, z, Bm, Cm, A, Dv, bias, softplus, h0,
+      scan_row_bwd(r / dim, r % dim, dim, L, N, G, u, delta, z, Bm, Cm, A, Dv, bias, softplus, h0,
                    dout, dlast, du, ddelta, dz, dBrows + r * N * L, dCrows + r * N * L,
                    dArows + r * N, dDrows + r, dbrows + r, dh0, hs, es, g);
     free(hs); free(es); free(g);
   }
 #endif
-  /* sums over rows, in a fixed order */
+  /* sums over rows, in a fixed order: dB, dC over the channels of each group */
+  const int64_t cpg = G > 0 ? dim / G : 0;
   for (int64_t b = 0; b < batch; ++b)
-    for (int64_t i = 0; i < N * L; ++i) {
-      double sb = 0.0, sc = 0.0;
-      for (int64_t d = 0; d < dim; ++d) {
-        sb += dBrows[(b * dim + d) * N * L + i];
-        sc += dCrows[(b * dim + d) * N * L + i];
+    for (int64_t gi = 0; gi < G; ++gi)
+      for (int64_t i = 0; i < N * L; ++i) {
+        double sb = 0.0, sc = 0.0;
+        for (int64_t d = gi * cpg; d < (gi + 1) * cpg; ++d) {
+          sb += dBrows[(b * dim + d) * N * L + i];
+          sc += dCrows[(b * dim + d) * N * L + i];
+        }
+        dB[(b * G + gi) * N * L + i] = sb;
+        dC[(b * G + gi) * N * L + i] = sc;
       }
-      dB[b * N * L + i] = sb;
-      dC[b * N * L + i] = sc;
-    }
   for (int64_t d = 0; d < dim; ++d) {
     double sD = 0.0, sb = 0.0;
     for (int64_t n = 0; n < N; ++n) {

@@ -34,7 +34,7 @@ MUTANTS = [
     ("softplus-sign", "return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));",
      "return (x > 0.0 ? x : 0.0) + log1p(exp(fabs(x)));"),
     ("silu-sign", "return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
-    ("decode-drop-input", "s[n] = exp(dl * A[d * N + n]) * s[n] + dl * Bm[b * N + n] * xt;",
+    ("decode-drop-input", "s[n] = exp(dl * A[d * N + n]) * s[n] + dl * Bt[n] * xt;",
      "s[n] = exp(dl * A[d * N + n]) * s[n];"),
 ]
 
@@ -149,4 +149,43 @@ def test_conv_pins_catch_planted_mistake(name, old, new, tmp_path):
     subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(lib), str(path), "-lm"])
     with oracle.use_library(str(lib)):
         caught = [i for i, fn in enumerate(CONV_PINS) if _fails_call(fn)]
+    assert caught, f"no pin caught mutant {name}"
+
+
+# Planted mistakes in the group lookup and the per-group sums, each to be
+# caught by a pin in test_oracle_general_pins.py.
+import test_oracle_general_pins as gpins  # noqa: E402
+
+GROUP_PINS = [
+    lambda: [gpins.test_unrolled_sum_any_dstate_groups_and_sign(N, G) for N in (8, 33) for G in (2, 4)],
+    gpins.test_group_decomposition_bit_exact,
+    lambda: [gpins.test_decode_equals_scan_grouped(N, G) for N, G in ((8, 2), (64, 4))],
+    lambda: [gpins.test_grouped_backward_exact_jvp(n, 8, 2) for n in ("B", "C", "u", "h0")],
+    gpins.test_grouped_backward_decomposes_by_group,
+]
+
+GROUP_MUTANTS = [
+    ("group-interleaved", "const int64_t grp = b * G + d / (dim / G);           /* this channel's B/C group */",
+     "const int64_t grp = b * G + d % G;"),
+    ("group-ignored", "const int64_t grp = b * G + d / (dim / G);           /* this channel's B/C group */",
+     "const int64_t grp = b * G;"),
+    ("decode-group-interleaved", "const double* Bt = Bm + (b * G + d / (dim / G)) * N;  /* this channel's group */",
+     "const double* Bt = Bm + (b * G + d % G) * N;"),
+    ("bwd-group-sum-all-channels", "for (int64_t d = gi * cpg; d < (gi + 1) * cpg; ++d) {",
+     "for (int64_t d = 0; d < dim; ++d) {"),
+    ("bwd-group-interleaved", "const int64_t grp = b * G + d / (dim / G);\n",
+     "const int64_t grp = b * G + d % G;\n"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", GROUP_MUTANTS, ids=[m[0] for m in GROUP_MUTANTS])
+def test_group_pins_catch_planted_mistake(name, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(lib), str(path), "-lm"])
+    with oracle.use_library(str(lib)):
+        caught = [i for i, fn in enumerate(GROUP_PINS) if _fails_call(fn)]
     assert caught, f"no pin caught mutant {name}"
