@@ -6,9 +6,11 @@
  *   ssm_selective_scan_fwd  -- prefill.  For every batch row b, channel d and
  *     state index n, with Delta_t = softplus(delta_t + bias[d]) (Mamba paper
  *     notes, 0539edu.com, section 2.3; Mamba training/inference guide, FAQ 2):
- *         h_t[n] = exp(Delta_t * A[d,n]) * h_{t-1}[n] + Delta_t * B[b,n,t] * u_t
- *         y_t    = sum_n C[b,n,t] * h_t[n] + D[d] * u_t
+ *         h_t[n] = exp(Delta_t * A[d,n]) * h_{t-1}[n] + Delta_t * B[b,g,n,t] * u_t
+ *         y_t    = sum_n C[b,g,n,t] * h_t[n] + D[d] * u_t
  *         out_t  = y_t * silu(z_t)
+ *     where g is the B/C group of channel d (one group: B_t and C_t shared
+ *     by every channel, the layout of the pages).
  *     starting from h_{-1} = h0 (or 0), and optionally returning h_{L-1}.
  *     The discrete recurrence and readout are section 2.2 of the Mamba model
  *     notes; the per-channel diagonal SSM is section 4.4 there; B, C and
@@ -53,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 
 /* Tokens between two state checkpoints (see ssm_scan_args.checkpoints). */
 #define SSM_CHECKPOINT_TOKENS 16
@@ -61,17 +63,24 @@ extern "C" {
 /* Largest width of the fused causal conv (see ssm_scan_args.conv_weight). */
 #define SSM_MAX_CONV 8
 
+/* Largest state size of the scan and the decode update (the Mamba training
+ * and inference guide's parameter table puts d_state between 8 and 64). */
+#define SSM_MAX_DSTATE 64
+
 typedef enum ssm_status {
   SSM_OK = 0,
   SSM_ERR_NULL = 1,        /* a required pointer is NULL                       */
-  SSM_ERR_SHAPE = 2,       /* negative size, or dstate < 1                     */
+  SSM_ERR_SHAPE = 2,       /* negative size, dstate < 1, or ngroups not
+                              dividing dim                                     */
   SSM_ERR_STRIDE = 3,      /* negative stride                                  */
   SSM_ERR_DTYPE = 4,       /* io_dtype is not SSM_F32 / SSM_BF16               */
   SSM_ERR_ALIGN = 5,       /* pointer not aligned to its element size          */
   SSM_ERR_ALIAS = 6,       /* an output overlaps an input it must not overlap  */
-  SSM_ERR_UNSUPPORTED = 7, /* valid but not built: dstate != 16, seqlen too
-                              large for 32-bit token indices (>= 2^31 - 64),
-                              or row spans past the 32-bit windows (see
+  SSM_ERR_UNSUPPORTED = 7, /* valid but not built: dstate > SSM_MAX_DSTATE
+                              (backward: dstate != 16, or groups that split a
+                              block of 16 channels), seqlen too large for
+                              32-bit token indices (>= 2^31 - 64), or row
+                              spans past the 32-bit windows (see
                               ssm_scan_args)                                   */
   SSM_ERR_HIP = 8          /* the HIP runtime rejected the launch              */
 } ssm_status;
@@ -81,9 +90,12 @@ typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
 /* Arguments of the prefill scan.
  *   u, delta, z, out : (batch, dim, seqlen), time stride 1; element (b, d, t)
  *                      at ptr[b * *_batch_stride + d * *_dim_stride + t].
- *   B, C             : (batch, dstate, seqlen), time stride 1; shared by all
- *                      channels of a batch row; element (b, n, t) at
- *                      ptr[b * *_batch_stride + n * *_state_stride + t].
+ *   B, C             : (batch, ngroups, dstate, seqlen), time stride 1;
+ *                      element (b, g, n, t) at ptr[b * *_batch_stride +
+ *                      g * *_group_stride + n * *_state_stride + t].  Channel
+ *                      d reads group d / (dim / ngroups); ngroups 0 or 1 is
+ *                      one group shared by all channels (group stride
+ *                      unused), ngroups == dim gives every channel its own.
  *   A                : (dim, dstate) fp32, element (d, n) at
  *                      A[d * A_dim_stride + n * A_state_stride].
  *   D, delta_bias    : (dim) fp32, contiguous.  NULL means 0.
@@ -93,11 +105,14 @@ typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
  *   delta_softplus   : nonzero applies softplus to delta + bias.
  * Sizes: batch, dim, seqlen >= 0 (zero sizes are a no-op, except that
  * seqlen == 0 with last_state set copies h0, or zeros, into last_state);
- * dstate must be 16; seqlen must be below 2^31 - 64.  The kernel reads each
- * group of 4 channels, and the 16 state rows of B and C, through 32-bit byte
+ * 1 <= dstate <= SSM_MAX_DSTATE; ngroups (0 or 1 meaning one group) must
+ * divide dim; seqlen must be below 2^31 - 64.  The kernel reads each group
+ * of 4 channels, and the state rows of B and C, through 32-bit byte
  * windows: (3 * dim_stride + seqlen) * element size for u, delta, z and out,
- * and (15 * state_stride + seqlen) * element size for B and C, must stay
- * below 2^32 (for contiguous fp32 B/C: seqlen below 2^26).  Larger spans
+ * and (r * group_stride + (dstate - 1) * state_stride + seqlen) * element
+ * size for B and C, must stay below 2^32, with r = 0 when dim / ngroups is
+ * a multiple of 16 (or one group) and min(3, ngroups - 1) otherwise; with
+ * checkpoints, 4 * ceil(seqlen / 16) * dstate * 4 bytes too.  Larger spans
  * return SSM_ERR_UNSUPPORTED.
  * Aliasing: out must not overlap u, delta, z, B or C; last_state must not
  * overlap any input except that it may be exactly h0 (in-place carry).
@@ -152,6 +167,8 @@ typedef struct ssm_scan_args {
   void* conv_out;     int64_t conv_out_batch_stride, conv_out_dim_stride;
   int32_t d_conv;
   int32_t conv_silu;  /* bool */
+  int64_t ngroups;    /* B/C groups; 0 or 1: one group */
+  int64_t B_group_stride, C_group_stride;
 } ssm_scan_args;
 
 /* Arguments of the scan backward.  The forward inputs (u, delta, z, B, C, A,
@@ -165,8 +182,8 @@ typedef struct ssm_scan_args {
  * Outputs (device memory owned by the caller, fully overwritten):
  *   du, ddelta      : (batch, dim, seqlen), io_dtype, time stride 1.
  *   dz              : the same, required when z is given, else ignored.
- *   dB, dC          : (batch, dstate, seqlen) fp32, contiguous (summed over
- *                     channels).
+ *   dB, dC          : (batch, ngroups, dstate, seqlen) fp32, contiguous
+ *                     (each summed over the channels of its group).
  *   dA              : (dim, dstate) fp32, contiguous (summed over batch, time).
  *   dD, ddelta_bias : (dim) fp32 (summed over batch, time); NULL: not wanted.
  *   dh0             : (batch, dim, dstate) fp32, contiguous; NULL: not wanted.
@@ -174,7 +191,9 @@ typedef struct ssm_scan_args {
  * are accumulated with device atomics, so their last bits can vary from run
  * to run; every other output is deterministic.  Outputs must not overlap
  * each other or any input.  The backward runs every sequence as one segment
- * (no workspace). */
+ * (no workspace).  It is built for dstate == 16 and for B/C groups that
+ * keep each block of 16 consecutive channels in one group (one group, or
+ * dim / ngroups a multiple of 16); other shapes return SSM_ERR_UNSUPPORTED. */
 typedef struct ssm_scan_bwd_args {
   int64_t batch, dim, seqlen, dstate;
   int32_t io_dtype;       /* ssm_dtype */
@@ -200,6 +219,8 @@ typedef struct ssm_scan_bwd_args {
   float* dD;
   float* ddelta_bias;
   float* dh0;
+  int64_t ngroups;    /* B/C groups; 0 or 1: one group */
+  int64_t B_group_stride, C_group_stride;
 } ssm_scan_bwd_args;
 
 /* Arguments of the single-token decode update.
@@ -207,7 +228,9 @@ typedef struct ssm_scan_bwd_args {
  *                      (b, d, n) at state[b * state_batch_stride +
  *                      d * state_dim_stride + n]; updated IN PLACE.
  *   x, dt, z, out    : (batch, dim), dim stride 1.  z NULL means no gate.
- *   B, C             : (batch, dstate), state stride 1.
+ *   B, C             : (batch, ngroups, dstate), state stride 1; element
+ *                      (b, g, n) at ptr[b * *_batch_stride + g * *_group_stride
+ *                      + n]; channel d reads group d / (dim / ngroups).
  *   A                : (dim, dstate) fp32, state stride 1.
  *   D, dt_bias       : (dim) fp32, contiguous, NULL means 0.
  * Fused conv branch (as in ssm_scan_args): with conv_weight set, x is the
@@ -215,8 +238,8 @@ typedef struct ssm_scan_bwd_args {
  * previous d_conv inputs and is shifted in place (oldest dropped, x appended);
  * the SSM input is act(conv_bias + sum_k conv_weight[d,k] conv_state[k]) of
  * the updated conv_state.  1 <= d_conv <= SSM_MAX_CONV.
- * Sizes: batch, dim >= 0 (zero is a no-op); dstate must be 16; batch at most
- * 65535.
+ * Sizes: batch, dim >= 0 (zero is a no-op); 1 <= dstate <= SSM_MAX_DSTATE;
+ * ngroups (0 or 1 meaning one group) must divide dim; batch at most 65535.
  * Aliasing: out must not overlap state or any input; state and conv_state
  * must not overlap any input or each other. */
 typedef struct ssm_update_args {
@@ -238,6 +261,8 @@ typedef struct ssm_update_args {
   const float* conv_bias;
   int32_t d_conv;
   int32_t conv_silu;  /* bool */
+  int64_t ngroups;    /* B/C groups; 0 or 1: one group */
+  int64_t B_group_stride, C_group_stride;
 } ssm_update_args;
 
 /* ABI version of the loaded library (SSM_ABI_VERSION at build time). */

@@ -17,11 +17,12 @@ CPU fallback, and importing a missing library raises.
     selective_state_update(state, x, dt, A, B, C, D=None, z=None,
                            dt_bias=None, dt_softplus=True) -> out  (state updated in place)
 
-Shapes: u, delta, z (batch, dim, L) with time stride 1; B, C (batch, 16, L)
-with time stride 1; A (dim, 16) fp32; D, delta_bias (dim,) fp32; h0 and
-last_state (batch, dim, 16) fp32.  Decode: state (batch, dim, 16) fp32 with
-state stride 1; x, dt, z (batch, dim); B, C (batch, 16).  IO tensors are
-float32 or bfloat16 (all of one dtype).
+Shapes (N = dstate, 1..64): u, delta, z (batch, dim, L) with time stride 1;
+B, C (batch, N, L), or (batch, G, N, L) for G groups of dim // G channels,
+with time stride 1; A (dim, N) fp32; D, delta_bias (dim,) fp32; h0 and
+last_state (batch, dim, N) fp32.  Decode: state (batch, dim, N) fp32 with
+state stride 1; x, dt, z (batch, dim); B, C (batch, N) or (batch, G, N).
+IO tensors are float32 or bfloat16 (all of one dtype).
 """
 from __future__ import annotations
 
@@ -31,7 +32,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssm.so")
 
-SSM_ABI_VERSION = 3
+SSM_ABI_VERSION = 4
 CHECKPOINT_TOKENS = 16
 MAX_CONV = 8
 SSM_F32, SSM_BF16 = 0, 1
@@ -61,7 +62,8 @@ class ScanArgs(ctypes.Structure):
                 ("conv_weight", _P), ("conv_bias", _P), ("conv_state_in", _P),
                 ("conv_state_out", _P),
                 ("conv_out", _P), ("conv_out_batch_stride", _I64), ("conv_out_dim_stride", _I64),
-                ("d_conv", _I32), ("conv_silu", _I32)]
+                ("d_conv", _I32), ("conv_silu", _I32),
+                ("ngroups", _I64), ("B_group_stride", _I64), ("C_group_stride", _I64)]
 
 
 class ScanBwdArgs(ctypes.Structure):
@@ -81,7 +83,8 @@ class ScanBwdArgs(ctypes.Structure):
                 ("ddelta", _P), ("ddelta_batch_stride", _I64), ("ddelta_dim_stride", _I64),
                 ("dz", _P), ("dz_batch_stride", _I64), ("dz_dim_stride", _I64),
                 ("dB", _P), ("dC", _P), ("dA", _P), ("dD", _P), ("ddelta_bias", _P),
-                ("dh0", _P)]
+                ("dh0", _P),
+                ("ngroups", _I64), ("B_group_stride", _I64), ("C_group_stride", _I64)]
 
 
 class UpdateArgs(ctypes.Structure):
@@ -98,7 +101,8 @@ class UpdateArgs(ctypes.Structure):
                 ("D", _P), ("dt_bias", _P),
                 ("out", _P), ("out_batch_stride", _I64),
                 ("conv_state", _P), ("conv_weight", _P), ("conv_bias", _P),
-                ("d_conv", _I32), ("conv_silu", _I32)]
+                ("d_conv", _I32), ("conv_silu", _I32),
+                ("ngroups", _I64), ("B_group_stride", _I64), ("C_group_stride", _I64)]
 
 
 class SSMError(RuntimeError):
@@ -224,6 +228,36 @@ def _contig_f32(name, t, shape):
     return t
 
 
+def _bc_groups(B, C, batch, dim, N, tail):
+    """B/C groups from the shape of B: (batch, N, *tail) is one group shared
+    by every channel, (batch, G, N, *tail) is G groups of dim // G channels."""
+    if tuple(B.shape) != tuple(C.shape):
+        raise ValueError("B and C must have the same shape")
+    if tuple(B.shape) == (batch, N) + tuple(tail):
+        return 0
+    if B.dim() == 3 + len(tail) and tuple(B.shape[2:]) == (N,) + tuple(tail) \
+            and B.shape[0] == batch and B.shape[1] >= 1 and dim % B.shape[1] == 0:
+        return int(B.shape[1])
+    raise ValueError("B and C must be (batch, dstate%s) or (batch, ngroups, dstate%s) with "
+                     "ngroups dividing dim" % ((", L",) * 2 if tail else ("", "")))
+
+
+def _set_bc(a, B, C, G, time):
+    """B/C pointers and strides into an argument block (0 groups: 3-D B/C)."""
+    a.B, a.C, a.ngroups = _ptr(B), _ptr(C), G
+    if time:
+        if G:
+            a.B_batch_stride, a.B_group_stride, a.B_state_stride = B.stride()[:3]
+            a.C_batch_stride, a.C_group_stride, a.C_state_stride = C.stride()[:3]
+        else:
+            a.B_batch_stride, a.B_state_stride = B.stride()[:2]
+            a.C_batch_stride, a.C_state_stride = C.stride()[:2]
+    else:
+        a.B_batch_stride, a.C_batch_stride = B.stride(0), C.stride(0)
+        if G:
+            a.B_group_stride, a.C_group_stride = B.stride(1), C.stride(1)
+
+
 def _stream(stream):
     torch = _torch()
     if stream is None:
@@ -263,12 +297,11 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
         _check_dev(name, t, dev, torch.float32)
     if tuple(delta.shape) != (batch, dim, L) or (z is not None and tuple(z.shape) != (batch, dim, L)):
         raise ValueError("delta and z must match u's shape")
-    if tuple(B.shape) != (batch, N, L) or tuple(C.shape) != (batch, N, L):
-        raise ValueError("B and C must be (batch, dstate, L)")
+    G = _bc_groups(B, C, batch, dim, N, (L,))
     if tuple(A.shape) != (dim, N):
         raise ValueError("A must be (dim, dstate)")
     for name, t in (("u", u), ("delta", delta), ("z", z), ("B", B), ("C", C)):
-        if t is not None and L > 1 and t.stride(2) != 1:
+        if t is not None and L > 1 and t.stride(-1) != 1:
             raise ValueError(f"{name} must have time stride 1")
     _contig_f32("D", D, (dim,))
     _contig_f32("delta_bias", delta_bias, (dim,))
@@ -289,8 +322,7 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     a.delta, (a.delta_batch_stride, a.delta_dim_stride) = _ptr(delta), delta.stride()[:2]
     if z is not None:
         a.z, (a.z_batch_stride, a.z_dim_stride) = _ptr(z), z.stride()[:2]
-    a.B, (a.B_batch_stride, a.B_state_stride) = _ptr(B), B.stride()[:2]
-    a.C, (a.C_batch_stride, a.C_state_stride) = _ptr(C), C.stride()[:2]
+    _set_bc(a, B, C, G, time=True)
     a.A, (a.A_dim_stride, a.A_state_stride) = _ptr(A), A.stride()
     a.D, a.delta_bias, a.h0 = _ptr(D), _ptr(delta_bias), _ptr(h0)
     a.last_state = _ptr(last_state)
@@ -352,9 +384,10 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, 
     for name, t in (("x", x), ("dt", dt), ("z", z)):
         if t is not None and (tuple(t.shape) != (batch, dim) or (dim > 1 and t.stride(1) != 1)):
             raise ValueError(f"{name} must be (batch, dim) with dim stride 1")
+    G = _bc_groups(B, C, batch, dim, N, ())
     for name, t in (("B", B), ("C", C)):
-        if tuple(t.shape) != (batch, N) or (N > 1 and t.stride(1) != 1):
-            raise ValueError(f"{name} must be (batch, dstate) with state stride 1")
+        if N > 1 and t.stride(-1) != 1:
+            raise ValueError(f"{name} must have state stride 1")
     if tuple(A.shape) != (dim, N) or (N > 1 and A.stride(1) != 1):
         raise ValueError("A must be (dim, dstate) with state stride 1")
     if N > 1 and state.stride(2) != 1:
@@ -374,8 +407,7 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, 
     a.dt, a.dt_batch_stride = _ptr(dt), dt.stride(0)
     if z is not None:
         a.z, a.z_batch_stride = _ptr(z), z.stride(0)
-    a.B, a.B_batch_stride = _ptr(B), B.stride(0)
-    a.C, a.C_batch_stride = _ptr(C), C.stride(0)
+    _set_bc(a, B, C, G, time=False)
     a.A, a.A_dim_stride = _ptr(A), A.stride(0)
     a.D, a.dt_bias = _ptr(D), _ptr(dt_bias)
     a.out, a.out_batch_stride = _ptr(out), out.stride(0)
@@ -420,12 +452,11 @@ def selective_scan_bwd(dout, u, delta, A, B, C, checkpoints, D=None, z=None, del
     for name, t in (("delta", delta), ("z", z), ("dout", dout)):
         if t is not None and tuple(t.shape) != (batch, dim, L):
             raise ValueError(f"{name} must match u's shape")
-    if tuple(B.shape) != (batch, N, L) or tuple(C.shape) != (batch, N, L):
-        raise ValueError("B and C must be (batch, dstate, L)")
+    G = _bc_groups(B, C, batch, dim, N, (L,))
     if tuple(A.shape) != (dim, N):
         raise ValueError("A must be (dim, dstate)")
     for name, t in (("u", u), ("delta", delta), ("z", z), ("B", B), ("C", C), ("dout", dout)):
-        if t is not None and L > 1 and t.stride(2) != 1:
+        if t is not None and L > 1 and t.stride(-1) != 1:
             raise ValueError(f"{name} must have time stride 1")
     _contig_f32("D", D, (dim,))
     _contig_f32("delta_bias", delta_bias, (dim,))
@@ -434,8 +465,8 @@ def selective_scan_bwd(dout, u, delta, A, B, C, checkpoints, D=None, z=None, del
     _contig_f32("checkpoints", checkpoints, checkpoint_shape(batch, dim, L, N))
     g = dict(du=torch.empty((batch, dim, L), dtype=io, device=dev),
              ddelta=torch.empty((batch, dim, L), dtype=io, device=dev),
-             dB=torch.empty((batch, N, L), dtype=torch.float32, device=dev),
-             dC=torch.empty((batch, N, L), dtype=torch.float32, device=dev),
+             dB=torch.empty(tuple(B.shape), dtype=torch.float32, device=dev),
+             dC=torch.empty(tuple(C.shape), dtype=torch.float32, device=dev),
              dA=torch.empty((dim, N), dtype=torch.float32, device=dev))
     if z is not None:
         g["dz"] = torch.empty((batch, dim, L), dtype=io, device=dev)
@@ -453,8 +484,7 @@ def selective_scan_bwd(dout, u, delta, A, B, C, checkpoints, D=None, z=None, del
     if z is not None:
         a.z, (a.z_batch_stride, a.z_dim_stride) = _ptr(z), z.stride()[:2]
         a.dz, (a.dz_batch_stride, a.dz_dim_stride) = _ptr(g["dz"]), g["dz"].stride()[:2]
-    a.B, (a.B_batch_stride, a.B_state_stride) = _ptr(B), B.stride()[:2]
-    a.C, (a.C_batch_stride, a.C_state_stride) = _ptr(C), C.stride()[:2]
+    _set_bc(a, B, C, G, time=True)
     a.A, (a.A_dim_stride, a.A_state_stride) = _ptr(A), A.stride()
     a.D, a.delta_bias, a.h0 = _ptr(D), _ptr(delta_bias), _ptr(h0)
     a.checkpoints, a.dlast = _ptr(checkpoints), _ptr(dlast)

@@ -1,10 +1,12 @@
 """Build libssm.so (the gfx950 HIP kernels + C ABI) in-tree with hipcc."""
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -30,10 +32,7 @@ def hipcc():
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every csrc/*.hip into libssm.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-shared", "-o", tmp, *sources()]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,6 +42,19 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(noise))
     if verbose and noise:
         print("\n".join(noise), file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every csrc/*.hip into libssm.so (always recompiles).  The
+    sources compile in parallel into a temporary directory, then link."""
+    tmp = LIB + ".tmp"
+    jobs = max(1, min(len(sources()), os.cpu_count() or 1, 16))
+    with tempfile.TemporaryDirectory(prefix="ssm_build_") as d:
+        objs = [os.path.join(d, os.path.basename(src) + ".o") for src in sources()]
+        with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+            list(ex.map(lambda so: _run([hipcc(), *HIPCC_FLAGS, "-c", "-o", so[1], so[0]], verbose),
+                        zip(sources(), objs)))
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -76,6 +76,8 @@ struct BwdParams {
   float* dh0;
   int64_t usb, usd, dsb, dsd, zsb, zsd, Bsb, Bsn, Csb, Csn, Asd, Asn, gsb, gsd;
   int64_t dusb, dusd, ddsb, ddsd, dzsb, dzsd;
+  int64_t Bsg, Csg;     // B/C group strides
+  int64_t ngroups, cpg; // groups, channels per group (a multiple of kCh, or dim)
   int64_t batch, dim;
   int L;
   int nbk;          // ceil(L / kT)
@@ -323,20 +325,22 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     w.wz = w.wu; w.oz = w.ou;      // loaded, never used
     w.wdz = Window{nullptr, 0u}; w.odz = 0;
   }
+  // the workgroup's 16 channels share one B/C group
+  const int64_t grp = (cg * kCh) / p.cpg;
   const int st = kRows * wave + row;
   w.oB = static_cast<uint32_t>((st * p.Bsn + col) * E);
-  w.wB = Window{static_cast<const char*>(p.B) + b * p.Bsb * E,
+  w.wB = Window{static_cast<const char*>(p.B) + (b * p.Bsb + grp * p.Bsg) * E,
                 static_cast<uint32_t>(((kN - 1) * p.Bsn + p.L) * E)};
   w.oC = static_cast<uint32_t>((st * p.Csn + col) * E);
-  w.wC = Window{static_cast<const char*>(p.C) + b * p.Csb * E,
+  w.wC = Window{static_cast<const char*>(p.C) + (b * p.Csb + grp * p.Csg) * E,
                 static_cast<uint32_t>(((kN - 1) * p.Csn + p.L) * E)};
   const int64_t ckrow = static_cast<int64_t>(p.nbk) * kN;
   w.ock = static_cast<uint32_t>(((dc - dw0) * ckrow + col) * 4);
   w.wck = Window{reinterpret_cast<const char*>(p.ckpt + (b * p.dim + dw0) * ckrow),
                  static_cast<uint32_t>((dw3 - dw0 + 1) * ckrow * 4)};
-  w.wdB = Window{reinterpret_cast<const char*>(p.dB + b * kN * p.L),
+  w.wdB = Window{reinterpret_cast<const char*>(p.dB + (b * p.ngroups + grp) * kN * p.L),
                  static_cast<uint32_t>(kN * p.L * 4)};
-  w.wdC = Window{reinterpret_cast<const char*>(p.dC + b * kN * p.L),
+  w.wdC = Window{reinterpret_cast<const char*>(p.dC + (b * p.ngroups + grp) * kN * p.L),
                  static_cast<uint32_t>(kN * p.L * 4)};
 
   w.a = p.A[dc * p.Asd + col * p.Asn];
@@ -418,7 +422,8 @@ bool scan_bwd_windows_fit(const ssm_scan_bwd_args& a) {
 
 hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
   // zero what the kernel accumulates into
-  const int64_t nbc = a.batch * a.dstate * a.seqlen;
+  const int64_t G = a.ngroups > 1 ? a.ngroups : 1;
+  const int64_t nbc = a.batch * G * a.dstate * a.seqlen;
   const int64_t nmax = std::max<int64_t>(nbc, a.dim * a.dstate);
   zero_kernel<<<dim3(static_cast<unsigned>((nmax + 255) / 256)), dim3(256), 0, stream>>>(
       a.dB, nbc, a.dC, nbc, a.dA, a.dim * a.dstate, a.dD, a.dim, a.ddelta_bias, a.dim);
@@ -445,6 +450,8 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
   p.zsb = a.z_batch_stride; p.zsd = a.z_dim_stride;
   p.Bsb = a.B_batch_stride; p.Bsn = a.B_state_stride;
   p.Csb = a.C_batch_stride; p.Csn = a.C_state_stride;
+  p.Bsg = G > 1 ? a.B_group_stride : 0; p.Csg = G > 1 ? a.C_group_stride : 0;
+  p.ngroups = G; p.cpg = a.dim / G;
   p.Asd = a.A_dim_stride; p.Asn = a.A_state_stride;
   p.gsb = a.dout_batch_stride; p.gsd = a.dout_dim_stride;
   p.dusb = a.du_batch_stride; p.dusd = a.du_dim_stride;

@@ -1,482 +1,18 @@
-// scan_fwd.hip -- prefill selective scan for gfx950.
-//
-// Computes, per batch row b, channel d and state n (Mamba model notes sections
-// 2.2, 4.1 and 4.4; Mamba paper notes section 2.3 for the discretisation):
-//   Delta_t = softplus(delta_t + bias[d])
-//   h_t[n]  = exp(Delta_t A[d,n]) h_{t-1}[n] + Delta_t B[b,n,t] u_t
-//   out_t   = (sum_n C[b,n,t] h_t[n] + D[d] u_t) * silu(z_t)
-//
-// Work decomposition.  A workgroup is 4 wavefronts; a wavefront is 4
-// channels of one batch row, each a 16-lane row whose lane n holds the fp32
-// state h[n] in a register for the whole sequence.  The workgroup walks its
-// token range in blocks of 16:
-//   owner role  lane (row c, col j) loads u/delta/z of token t0+j of channel c
-//               and computes Delta and Delta*u once; a DPP row_newbcast:j
-//               inside the consuming VALU op hands them to the 16 state lanes
-//               of the same row.
-//   stage role  B and C depend on (b, n, t) only.  Every 2 blocks the
-//               workgroup loads the next 16 x 32 tile of each (one state row
-//               per 16 lanes, coalesced) into a double-buffered LDS tile and
-//               synchronises once; every lane then reads back the 16 values
-//               of its state n for each block.
-//   readout     each state lane leaves C_n h_n per token in its wavefront's
-//               LDS; one block later the owner of the token sums the 16
-//               partials, adds D*u, applies the gate and stores.
-// Apart from the B/C tile, LDS is private to a wavefront, whose LDS operations
-// complete in issue order, so the per-block exchange needs no barrier.  Every
-// global access goes through a buffer descriptor whose window ends where the
-// wavefront's data ends: lanes of a partial last block that reach past it
-// read zero instead of touching memory, so no lane clamps its address.
-//
-// Long sequences with few channels.  The recurrence is linear in the state
-// (Mamba paper notes, sections 5.3/5.4: a long input can be cut into chunks
-// with the state handed from one chunk to the next), so the sequence may be
-// cut into G segments processed by different workgroups:
-//   pass 1 (aggregate)  segments 0..G-2 run from a zero state and record their
-//                       end state b_g and the sum of their step sizes S_g;
-//   pass 2 (scan)       segment g starts from
-//                       h_in = fold_{i<g} (exp(A S_i) h + b_i) applied to h0,
-//                       then runs exactly like the single-segment scan.
-// The exact state entering segment g is exp(A S_{g-1}) h_in(g-1) + b_{g-1},
-// so the fold reproduces the sequential result up to fp32 rounding.
+// scan_fwd.hip -- host side of the prefill selective scan: segment choice,
+// B/C mode, workspace, window limits and the launches.  The kernel itself is
+// in scan_fwd_kernel.h (instantiated by scan_fwd_s1/s2/s4.hip).
 #include <algorithm>
 
-#include "ssm_internal.h"
+#include "scan_fwd_kernel.h"
 
 namespace ssm {
 namespace {
 
-constexpr int kN = 16;              // states per channel = lanes per row
-constexpr int kRows = 4;            // channels per wavefront
-constexpr int kWaves = 4;           // wavefronts per workgroup
-constexpr int kCh = kRows * kWaves; // channels per workgroup
-constexpr int kThreads = 64 * kWaves;
-constexpr int kT = 16;              // tokens per block
-constexpr int kGB = 2;              // blocks per B/C staging group
-constexpr int kGT = kT * kGB;       // tokens per group
-static_assert(4 % kGB == 0, "the steady-state loop runs four blocks at a time");
-constexpr int kGPitch = kGT + 4;    // LDS pitch (floats) of one state's group of B / C
-constexpr int kPitch = 20;          // LDS pitch (floats) of one state's readout partials
-constexpr int kPartRow = kN * kPitch + 16;  // floats per channel of readout partials
-constexpr int kAggStride = kN + 1;  // floats per (channel, segment) aggregate: b[16], S
-
-enum class Mode { kScan, kAggregate };
-
-struct ScanParams {
-  const void* u;
-  const void* delta;
-  const void* z;
-  const void* B;
-  const void* C;
-  const float* A;
-  const float* D;
-  const float* bias;
-  const float* h0;
-  float* last_state;
-  void* out;
-  float* agg;      // [batch * dim][nseg - 1][kAggStride] segment aggregates (nseg > 1)
-  float* ckpt;     // [batch][dim][nbk][kN] states entering each block, or NULL
-  const float* conv_w;      // [dim][K] conv weights (the conv path only)
-  const float* conv_b;      // [dim] or NULL
-  const float* conv_in;     // [batch][dim][K] inputs before the sequence, or NULL
-  float* conv_stout;        // [batch][dim][K] last K inputs, or NULL
-  void* conv_out;           // (batch, dim, L) SSM input u, or NULL
-  int64_t usb, usd, dsb, dsd, zsb, zsd, Bsb, Bsn, Csb, Csn, Asd, Asn, osb, osd, cosb, cosd;
-  int K;                    // conv width
-  int conv_silu;
-  int64_t batch, dim;
-  int L;
-  int seg_len;     // tokens per segment (multiple of kGT)
-  int nseg;        // segments per sequence
-  int nbk;         // blocks per sequence, ceil(L / kT)
-  int64_t cgroups; // ceil(dim / kCh)
-};
-
-// Owner role raw inputs of one block: token t0 + col of the lane's channel
-// (bit patterns, widened where they are used); with the conv path, u holds
-// the conv input x.
-struct Raw {
-  uint32_t u, dt, z;
-};
-
-// Stage role raw inputs of one group: B and C of state 4w + row at tokens
-// tg + col + 16 i.
-struct GroupRaw {
-  uint32_t b[kGB], c[kGB];
-};
-
-// Lane (J - m) mod 16 of the 16-lane row (DPP row_ror:m).
-template <int M>
-__device__ __forceinline__ float row_ror(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + M, 0xf, 0xf, true));
-}
-
-template <typename T, Mode M, bool kSoftplus, int KP>
-struct Wave {
-  const ScanParams& p;
-  int wave, row, col;
-  int t_beg, t_end, nblk, ngrp;
-  Window wu, wdt, wz, wB, wC, wout, wck;
-  uint32_t ou, odt, oz, oB, oC, oout, ock;  // per-lane byte offsets inside the windows
-  uint32_t ckstep;    // checkpoint bytes per block of a channel row (0: none kept)
-  int blk0;           // global index of this segment's first block
-  float a2, bias, Dd;
-  // conv path (KP > 0: the width padded to KP): tap weights by lag m,
-  // wl[m] multiplies x_{t-m} (zero past the real width), and the bias
-  float wl[KP > 0 ? KP : 1], cb;
-  bool silu_in;
-  Window wco;                 // conv_out window (empty when not wanted)
-  uint32_t oco;
-  float (*sB)[kN][kGPitch];   // [2][kN][kGPitch], shared by the workgroup
-  float (*sC)[kN][kGPitch];
-  float (*sP)[kPartRow];      // this wavefront's [kRows][kPartRow]
-
-  static constexpr int E = Elem<T>::kSize;
-
-  __device__ __forceinline__ uint32_t skip(int k) const {
-    return static_cast<uint32_t>(t_beg + k * kT) * E;
-  }
-
-  // Owner raw inputs of block k; blocks past the last one reload the last one
-  // (the pipeline prefetches two blocks ahead and never uses those).
-  __device__ __forceinline__ Raw load(int k) const {
-    Raw r;
-    const uint32_t s = skip(min(k, nblk - 1));
-    r.u = Elem<T>::load(wu.at(s), ou);
-    r.dt = Elem<T>::load(wdt.at(s), odt);
-    // without a gate the z window is u's: the load is a cache hit, never used
-    r.z = M == Mode::kScan ? Elem<T>::load(wz.at(s), oz) : 0u;
-    return r;
-  }
-
-  // Stage raw inputs of group g (clamped to the last group like load()).
-  __device__ __forceinline__ GroupRaw load_group(int g) const {
-    GroupRaw r;
-    const uint32_t s = skip(min(g, ngrp - 1) * kGB);
-    const __amdgpu_buffer_rsrc_t rb = wB.at(s);
-#pragma unroll
-    for (int i = 0; i < kGB; ++i) r.b[i] = Elem<T>::load(rb, oB + i * kT * E);
-    if (M == Mode::kScan) {
-      const __amdgpu_buffer_rsrc_t rc = wC.at(s);
-#pragma unroll
-      for (int i = 0; i < kGB; ++i) r.c[i] = Elem<T>::load(rc, oC + i * kT * E);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kGB; ++i) r.c[i] = 0u;
-    }
-    return r;
-  }
-
-  // Stage role: group g's B (and C) into LDS buffer g & 1.  B of tokens past
-  // the end is zeroed so that a non-finite value read from beyond a row
-  // cannot reach h.
-  __device__ __forceinline__ void stage(int g, const GroupRaw& r) const {
-    const int st = kRows * wave + row;
-    const int t = t_beg + g * kGT + col;
-#pragma unroll
-    for (int i = 0; i < kGB; ++i) {
-      const float bv = Elem<T>::f32(r.b[i]);
-      sB[g & 1][st][col + i * kT] = t + i * kT < t_end ? bv : 0.0f;
-      if (M == Mode::kScan) sC[g & 1][st][col + i * kT] = Elem<T>::f32(r.c[i]);
-    }
-  }
-
-  // Owner role: readout of block k (y = the sum of its 16 partials, uv its
-  // SSM input), skip term, gate, store.  Rows past dim repeat the last channel bit for bit, so in full
-  // blocks every lane may store (duplicates write identical values); with
-  // kMask only tokens before the end are stored.
-  template <bool kMask>
-  __device__ __forceinline__ void finish(int k, const Raw& r, float uv, float y) const {
-    y = fmaf(Dd, uv, y);
-    const float g = silu_f32(Elem<T>::f32(r.z));
-    y *= p.z ? g : 1.0f;  // a select, not a branch
-    const __amdgpu_buffer_rsrc_t ro = wout.at(skip(k));
-    if (!kMask || t_beg + k * kT + col < t_end) Elem<T>::store(ro, oout, y);
-  }
-
-  // Iteration k.  Buffers: P = block k-1 (finish), Q = block k (scan),
-  // S = block k+2 (load target); G holds the next group's B/C.
-  // kMask = false is the steady state, valid when blocks k-1 and k are full:
-  // it has no branch, so the scan's DPP broadcasts stay fused into the ops
-  // that use them.  kEnd (steady state only) marks the last block of a group,
-  // after which the next group is staged and the workgroup synchronises; in
-  // the masked form that is decided at run time.
-  template <bool kMask, bool kEnd>
-  __device__ __forceinline__ void iter(int k, float& h, double& ssum, const Raw& P, const Raw& Q,
-                                       Raw& S, GroupRaw& G, float& uprev, float& xprev) const {
-    // LDS reads first: B/C of this block and the previous block's partials.
-    const int buf = (k / kGB) & 1;
-    const int tb = (k % kGB) * kT;
-    float bv[kT], cv[kT], part[kN];
-#pragma unroll
-    for (int q = 0; q < kT / 4; ++q) {
-      const float4 x = *reinterpret_cast<const float4*>(&sB[buf][col][tb + 4 * q]);
-      bv[4 * q] = x.x; bv[4 * q + 1] = x.y; bv[4 * q + 2] = x.z; bv[4 * q + 3] = x.w;
-      if (M == Mode::kScan) {
-        const float4 y = *reinterpret_cast<const float4*>(&sC[buf][col][tb + 4 * q]);
-        cv[4 * q] = y.x; cv[4 * q + 1] = y.y; cv[4 * q + 2] = y.z; cv[4 * q + 3] = y.w;
-      }
-    }
-    float ysum = 0.0f;
-    if (M == Mode::kScan) {
-      // unconditional: at k = 0 the value is never used; summed right away so
-      // that one register, not sixteen, lives across the scan
-#pragma unroll
-      for (int n = 0; n < kN; ++n) part[n] = sP[row][n * kPitch + col];
-#pragma unroll
-      for (int n = 0; n < kN; ++n) ysum += part[n];
-    }
-    S = load(k + 2);
-
-    // owner role: the SSM input u of this token (through the causal conv on
-    // the conv path), Delta and Delta*u (zero past the end)
-    float uv;
-    if constexpr (KP > 0) {
-      // x_{t-m} is lane col-m of this block for m <= col, else lane col-m+16
-      // of the previous one: a DPP row rotation of each and a select
-      const float xc = Elem<T>::f32(Q.u);
-      float pre = fmaf(wl[0], xc, cb);
-      static_for<1, KP>([&](auto Mm) {
-        constexpr int m = decltype(Mm)::value;
-        const float xcur = row_ror<m>(xc), xold = row_ror<m>(xprev);
-        pre = fmaf(wl[m], col >= m ? xcur : xold, pre);
-      });
-      const float act = silu_f32(pre);
-      uv = silu_in ? act : pre;  // a select, not a branch
-      xprev = xc;
-      if (M == Mode::kScan && (!kMask || t_beg + k * kT + col < t_end))
-        Elem<T>::store(wco.at(p.conv_out ? skip(k) : 0u), oco, uv);
-    } else {
-      uv = Elem<T>::f32(Q.u);
-    }
-    const float x = Elem<T>::f32(Q.dt) + bias;
-    float dl = kSoftplus ? softplus_f32(x) : x;
-    float du = dl * uv;
-    if (kMask) {
-      const bool own = t_beg + k * kT + col < t_end;
-      dl = own ? dl : 0.0f;
-      du = own ? du : 0.0f;
-    }
-    if (M == Mode::kAggregate) ssum += static_cast<double>(dl);
-
-    // checkpoint: the state entering this block (an empty window when none
-    // are kept, so the store is dropped without a branch)
-    if (M == Mode::kScan)
-      Elem<float>::store(wck.at((blk0 + k) * ckstep), ock, h);
-
-    // state role: 16 sequential steps of this lane's state; the readout
-    // partials C_n h_n go to LDS four tokens at a time
-    float pk[4];
-    static_for<0, kT>([&](auto J) {
-      constexpr int j = decltype(J)::value;
-      const float e = __builtin_amdgcn_exp2f(row_bcast<j>(dl) * a2);  // Abar = exp(Delta A)
-      const float w = row_bcast<j>(du) * bv[j];                       // Bbar u = Delta u B
-      h = fmaf(e, h, w);
-      if (M == Mode::kScan) {
-        pk[j % 4] = cv[j] * h;                                        // C_n h_n
-        if (j % 4 == 3)
-          *reinterpret_cast<float4*>(&sP[row][col * kPitch + j - 3]) =
-              make_float4(pk[0], pk[1], pk[2], pk[3]);
-      }
-    });
-    if (M == Mode::kScan) {
-      if (!kMask) finish<false>(k - 1, P, uprev, ysum);
-      else if (k > 0) finish<true>(k - 1, P, uprev, ysum);
-    }
-    uprev = uv;
-    // Compiler-only fence: keep this block's LDS traffic in program order with
-    // the next block's (the hardware already keeps one wavefront's in order).
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("" ::: "memory");
-    if (kMask ? (k % kGB == kGB - 1 && k + 1 < nblk) : kEnd) {
-      // Group (k+1)/kGB into the other buffer.  Every wavefront finished
-      // reading that buffer before the previous barrier.
-      const int g = k / kGB + 1;
-      stage(g, G);
-      __syncthreads();
-      G = load_group(g + 1);
-    }
-  }
-};
-
-template <typename T, Mode M, bool kSoftplus, int KP>
-__global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
-  __shared__ __align__(16) float sB[2][kN][kGPitch];
-  __shared__ __align__(16) float sC[M == Mode::kScan ? 2 : 1][kN][kGPitch];
-  __shared__ __align__(16) float sP[M == Mode::kScan ? kWaves : 1][kRows][kPartRow];
-  __shared__ double sSum[M == Mode::kScan ? 1 : kWaves][kRows][kT];
-
-  // wavefront index, made visibly uniform so that windows stay in SGPRs
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row = (threadIdx.x >> 4) & 3;
-  const int col = threadIdx.x & 15;
-  // blockIdx.x = (b * cgroups + cg) * nseg_grid + g; the aggregate pass skips
-  // the last segment (its end state is never needed by a later segment)
-  const int nseg_grid = M == Mode::kScan ? p.nseg : p.nseg - 1;
-  const int g = static_cast<int>(blockIdx.x % nseg_grid);
-  const int64_t bc = blockIdx.x / nseg_grid;
-  const int64_t b = bc / p.cgroups;
-  const int64_t d = (bc % p.cgroups) * kCh + kRows * wave + row;
-  const bool vrow = d < p.dim;
-  // rows past dim repeat the last channel exactly (same inputs, same state)
-  const int64_t dc = vrow ? d : p.dim - 1;
-  // this wavefront's first and last (clamped) rows
-  const int64_t dw0 = std::min<int64_t>((bc % p.cgroups) * kCh + kRows * wave, p.dim - 1);
-  const int64_t dw3 = std::min<int64_t>(dw0 + kRows - 1, p.dim - 1);
-
-  constexpr int E = Elem<T>::kSize;
-  Wave<T, M, kSoftplus, KP> w{p};
-  w.wave = wave; w.row = row; w.col = col;
-  w.t_beg = g * p.seg_len;
-  w.t_end = std::min(p.L, w.t_beg + p.seg_len);
-  w.nblk = (w.t_end - w.t_beg + kT - 1) / kT;
-  w.ngrp = (w.nblk + kGB - 1) / kGB;
-
-  // Windows run from this wavefront's first row to the end of its last row.
-  auto rows_window = [&](const void* base, int64_t sb, int64_t sd, uint32_t& off) {
-    off = static_cast<uint32_t>(((dc - dw0) * sd + col) * E);
-    return Window{static_cast<const char*>(base) + (b * sb + dw0 * sd) * E,
-                  static_cast<uint32_t>(((dw3 - dw0) * sd + p.L) * E)};
-  };
-  w.wu = rows_window(p.u, p.usb, p.usd, w.ou);
-  w.wdt = rows_window(p.delta, p.dsb, p.dsd, w.odt);
-  if (p.z) {
-    w.wz = rows_window(p.z, p.zsb, p.zsd, w.oz);
-  } else {
-    w.wz = w.wu;
-    w.oz = w.ou;
-  }
-  w.wout = rows_window(p.out, p.osb, p.osd, w.oout);
-  // checkpoints: rows of nbk * kN floats, [b][d][block][n]
-  const int64_t ckrow = static_cast<int64_t>(p.nbk) * kN;
-  w.blk0 = w.t_beg / kT;
-  w.ckstep = p.ckpt ? kN * 4 : 0;
-  w.ock = static_cast<uint32_t>(((dc - dw0) * ckrow + col) * 4);
-  w.wck = Window{reinterpret_cast<const char*>(p.ckpt ? p.ckpt + (b * p.dim + dw0) * ckrow : nullptr),
-                 p.ckpt ? static_cast<uint32_t>((dw3 - dw0 + 1) * ckrow * 4) : 0u};
-  // B/C: the workgroup's 16 state rows; this lane stages state 4 wave + row
-  const int st = kRows * wave + row;
-  w.oB = static_cast<uint32_t>((st * p.Bsn + col) * E);
-  w.wB = Window{static_cast<const char*>(p.B) + b * p.Bsb * E,
-                static_cast<uint32_t>(((kN - 1) * p.Bsn + p.L) * E)};
-  w.oC = static_cast<uint32_t>((st * p.Csn + col) * E);
-  w.wC = Window{static_cast<const char*>(p.C) + b * p.Csb * E,
-                static_cast<uint32_t>(((kN - 1) * p.Csn + p.L) * E)};
-
-  w.a2 = p.A[dc * p.Asd + col * p.Asn] * kLog2e;
-  w.bias = p.bias ? p.bias[dc] : 0.0f;
-  w.Dd = p.D ? p.D[dc] : 0.0f;
-  w.sB = sB; w.sC = sC; w.sP = sP[M == Mode::kScan ? wave : 0];
-
-  // conv path: tap weights by lag, bias, the inputs just before this
-  // segment (x_{t_beg-16+col}: from the conv state at the sequence start,
-  // else from x itself), and the conv_out window
-  float xprev = 0.0f;
-  if constexpr (KP > 0) {
-    const int K = p.K;
-#pragma unroll
-    for (int m = 0; m < KP; ++m) w.wl[m] = m < K ? p.conv_w[dc * K + (K - 1 - m)] : 0.0f;
-    w.cb = p.conv_b ? p.conv_b[dc] : 0.0f;
-    w.silu_in = p.conv_silu != 0;
-    if (w.t_beg == 0) {
-      const int t = col - kT;  // token index before the sequence, -16 .. -1
-      xprev = (p.conv_in && t >= -K) ? p.conv_in[(b * p.dim + dc) * K + K + t] : 0.0f;
-    } else {
-      xprev = Elem<T>::f32(Elem<T>::load(w.wu.at(static_cast<uint32_t>(w.t_beg - kT) * E), w.ou));
-    }
-    if (p.conv_out) {
-      w.wco = rows_window(p.conv_out, p.cosb, p.cosd, w.oco);
-    } else {
-      w.wco = Window{nullptr, 0u};
-      w.oco = 0;
-    }
-  }
-  float uprev = 0.0f;
-
-  // Initial state: zero for an aggregate segment; otherwise h0 (or zero) carried
-  // through the aggregates of every earlier segment.
-  float h = 0.0f;
-  if (M == Mode::kScan) {
-    h = p.h0 ? p.h0[(b * p.dim + dc) * kN + col] : 0.0f;
-    if (g > 0) {
-      const float* ag = p.agg + ((b * p.dim + dc) * (p.nseg - 1)) * kAggStride;
-      for (int i = 0; i < g; ++i) {
-        const float decay = __builtin_amdgcn_exp2f(w.a2 * ag[i * kAggStride + kN]);
-        h = fmaf(decay, h, ag[i * kAggStride + col]);
-      }
-    }
-  }
-
-  double ssum = 0.0;
-  // group 0 staged before the loop, group 1 in flight; block j's owner inputs
-  // live in buffer j % 4 and iteration k loads block k + 2
-  GroupRaw grp = w.load_group(0);
-  Raw buf0 = w.load(0), buf1 = w.load(1), buf2 = buf0, buf3 = buf0;
-  w.stage(0, grp);
-  grp = w.load_group(1);
-  __syncthreads();
-
-  // Steady state: iterations 1 .. nfull-1 (blocks k-1 and k full), four at a
-  // time so that buffer j % 4 is a fixed set of registers; a group ends at
-  // k % kGB == kGB - 1.  The first iteration and the last few take the masked
-  // form.
-  const int nblk = w.nblk;
-  const int nfull = (w.t_end - w.t_beg) / kT;
-  w.template iter<true, false>(0, h, ssum, buf3, buf0, buf2, grp, uprev, xprev);
-  int k = 1;
-  for (; k + 4 <= nfull; k += 4) {
-    // k % 4 == 1 here, and 4 is a multiple of kGB
-    w.template iter<false, (1 % kGB == kGB - 1)>(k + 0, h, ssum, buf0, buf1, buf3, grp, uprev, xprev);
-    w.template iter<false, (2 % kGB == kGB - 1)>(k + 1, h, ssum, buf1, buf2, buf0, grp, uprev, xprev);
-    w.template iter<false, (3 % kGB == kGB - 1)>(k + 2, h, ssum, buf2, buf3, buf1, grp, uprev, xprev);
-    w.template iter<false, (4 % kGB == kGB - 1)>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev);
-  }
-  if (k < nblk) w.template iter<true, false>(k, h, ssum, buf0, buf1, buf3, grp, uprev, xprev);
-  if (k + 1 < nblk) w.template iter<true, false>(k + 1, h, ssum, buf1, buf2, buf0, grp, uprev, xprev);
-  if (k + 2 < nblk) w.template iter<true, false>(k + 2, h, ssum, buf2, buf3, buf1, grp, uprev, xprev);
-  if (k + 3 < nblk) w.template iter<true, false>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev);
-
-  if (M == Mode::kScan) {
-    // finish the last block: its partials are in LDS, its raw inputs in buffer
-    // (nblk - 1) % 4
-    const int kl = nblk - 1;
-    const int r = kl & 3;
-    const Raw last = r == 0 ? buf0 : r == 1 ? buf1 : r == 2 ? buf2 : buf3;
-    float ysum = 0.0f;
-#pragma unroll
-    for (int n = 0; n < kN; ++n) ysum += w.sP[row][n * kPitch + col];
-    w.template finish<true>(kl, last, uprev, ysum);
-    if (vrow && p.last_state && g == p.nseg - 1) p.last_state[(b * p.dim + d) * kN + col] = h;
-    if constexpr (KP > 0) {
-      // the last K inputs, for the decode update to continue from
-      const int K = p.K;
-      if (vrow && p.conv_stout && g == p.nseg - 1 && col < K) {
-        const int t = p.L - K + col;
-        float v;
-        if (t >= 0) {
-          const uint32_t orow = w.ou - static_cast<uint32_t>(col * E);
-          v = Elem<T>::f32(Elem<T>::load(w.wu.at(0), orow + static_cast<uint32_t>(t * E)));
-        } else {
-          v = p.conv_in ? p.conv_in[(b * p.dim + d) * K + K + t] : 0.0f;
-        }
-        p.conv_stout[(b * p.dim + d) * K + col] = v;
-      }
-    }
-  } else {
-    // segment aggregate: end state from zero and the step-size sum (fp64 partial
-    // sums of the 16 owner lanes of each channel, added in a fixed order)
-    sSum[wave][row][col] = ssum;
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("" ::: "memory");
-    float* ag = p.agg + ((b * p.dim + dc) * (p.nseg - 1) + g) * kAggStride;
-    if (vrow) ag[col] = h;
-    if (vrow && col == 0) {
-      double s = 0.0;
-      for (int j = 0; j < kT; ++j) s += sSum[wave][row][j];
-      ag[kN] = static_cast<float>(s);
-    }
-  }
-}
+using fwd::kCh;
+using fwd::kGT;
+using fwd::kN;
+using fwd::kRows;
+using fwd::kT;
 
 // seqlen == 0: the final state is the initial one.
 __global__ void copy_state_kernel(const float* h0, float* last, int64_t n) {
@@ -498,40 +34,38 @@ int choose_segments(int64_t groups, int64_t L) {
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(g, kMaxSeg)));
 }
 
-template <Mode M, int KP>
-void launch_kp(bool bf16, bool softplus, dim3 grid, const ScanParams& p, hipStream_t stream) {
-  const dim3 block(kThreads);
-  if (bf16) {
-    if (softplus) scan_fwd_kernel<uint16_t, M, true, KP><<<grid, block, 0, stream>>>(p);
-    else scan_fwd_kernel<uint16_t, M, false, KP><<<grid, block, 0, stream>>>(p);
-  } else {
-    if (softplus) scan_fwd_kernel<float, M, true, KP><<<grid, block, 0, stream>>>(p);
-    else scan_fwd_kernel<float, M, false, KP><<<grid, block, 0, stream>>>(p);
-  }
+int64_t ngroups_of(const ssm_scan_args& a) { return a.ngroups > 1 ? a.ngroups : 1; }
+
+// Shared B/C (one LDS tile per workgroup) needs the workgroup's 16 channels
+// in one group; otherwise each lane reads its own group's rows.
+bool lane_bc(const ssm_scan_args& a) {
+  const int64_t G = ngroups_of(a);
+  return G > 1 && (a.dim / G) % kCh != 0;
 }
 
-// The conv width is padded to 4 or 8 taps (zero weights), the two kernel sizes.
-template <Mode M>
-void launch(bool bf16, bool softplus, int K, dim3 grid, const ScanParams& p, hipStream_t stream) {
-  if (K == 0) launch_kp<M, 0>(bf16, softplus, grid, p, stream);
-  else if (K <= 4) launch_kp<M, 4>(bf16, softplus, grid, p, stream);
-  else launch_kp<M, 8>(bf16, softplus, grid, p, stream);
-}
+// State slots per lane: 16 states per slot.
+int slots(int64_t dstate) { return dstate <= 16 ? 1 : dstate <= 32 ? 2 : 4; }
 
 }  // namespace
 
 bool scan_windows_fit(const ssm_scan_args& a) {
-  // Per-wavefront byte windows (and the lane offsets inside them) are 32-bit.
+  // Per-wavefront byte windows (and the lane offsets inside them) are 32-bit,
+  // with a margin: lanes of padding states address from a window's end.
   const int64_t esz = a.io_dtype == SSM_BF16 ? 2 : 4;
   const int64_t rows = std::min<int64_t>(kRows, a.dim) - 1;
-  const int64_t lim = int64_t{1} << 32;
+  const int64_t lim = (int64_t{1} << 32) - 256;
   auto fits = [&](int64_t span) { return span * esz < lim; };
+  // a wavefront's four rows reach at most four groups in lane mode
+  const int64_t gspan = lane_bc(a) ? std::min<int64_t>(3, ngroups_of(a) - 1) : 0;
   bool ok = fits(rows * a.u_dim_stride + a.seqlen) && fits(rows * a.delta_dim_stride + a.seqlen) &&
             fits(rows * a.out_dim_stride + a.seqlen) &&
-            fits((kN - 1) * a.B_state_stride + a.seqlen) &&
-            fits((kN - 1) * a.C_state_stride + a.seqlen);
+            fits(gspan * a.B_group_stride + (a.dstate - 1) * a.B_state_stride + a.seqlen) &&
+            fits(gspan * a.C_group_stride + (a.dstate - 1) * a.C_state_stride + a.seqlen);
   if (a.z) ok = ok && fits(rows * a.z_dim_stride + a.seqlen);
   if (a.conv_weight && a.conv_out) ok = ok && fits(rows * a.conv_out_dim_stride + a.seqlen);
+  // checkpoints: four rows of ceil(L / 16) * dstate floats
+  if (a.checkpoints)
+    ok = ok && (rows + 1) * ((a.seqlen + kT - 1) / kT) * a.dstate * 4 < lim;
   return ok;
 }
 
@@ -540,7 +74,7 @@ size_t scan_workspace_bytes(const ssm_scan_args& a) {
   const int64_t groups = a.batch * ((a.dim + kCh - 1) / kCh);
   const int nseg = choose_segments(groups, a.seqlen);
   if (nseg <= 1) return 0;
-  return static_cast<size_t>(a.batch * a.dim * (nseg - 1) * kAggStride) * sizeof(float);
+  return static_cast<size_t>(a.batch * a.dim * (nseg - 1) * (a.dstate + 1)) * sizeof(float);
 }
 
 hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {
@@ -558,18 +92,20 @@ hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {
     }
     return hipGetLastError();
   }
-  ScanParams p;
+  fwd::ScanParams p;
   p.u = a.u; p.delta = a.delta; p.z = a.z; p.B = a.B; p.C = a.C;
   p.A = a.A; p.D = a.D; p.bias = a.delta_bias; p.h0 = a.h0; p.last_state = a.last_state;
   p.out = a.out;
   p.usb = a.u_batch_stride; p.usd = a.u_dim_stride;
   p.dsb = a.delta_batch_stride; p.dsd = a.delta_dim_stride;
   p.zsb = a.z_batch_stride; p.zsd = a.z_dim_stride;
-  p.Bsb = a.B_batch_stride; p.Bsn = a.B_state_stride;
-  p.Csb = a.C_batch_stride; p.Csn = a.C_state_stride;
+  p.Bsb = a.B_batch_stride; p.Bsg = a.B_group_stride; p.Bsn = a.B_state_stride;
+  p.Csb = a.C_batch_stride; p.Csg = a.C_group_stride; p.Csn = a.C_state_stride;
   p.Asd = a.A_dim_stride; p.Asn = a.A_state_stride;
   p.osb = a.out_batch_stride; p.osd = a.out_dim_stride;
   p.batch = a.batch; p.dim = a.dim; p.L = static_cast<int>(a.seqlen);
+  p.N = static_cast<int>(a.dstate);
+  p.cpg = a.dim / ngroups_of(a);
   p.cgroups = (a.dim + kCh - 1) / kCh;
 
   // Segmenting needs the caller's workspace; without enough of it the whole
@@ -591,12 +127,16 @@ hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {
   p.conv_silu = a.conv_silu;
   p.nbk = static_cast<int>((a.seqlen + kT - 1) / kT);
 
-  if (p.nseg > 1) {
-    const dim3 g1((unsigned)(groups * (p.nseg - 1)));
-    launch<Mode::kAggregate>(a.io_dtype == SSM_BF16, a.delta_softplus != 0, p.K, g1, p, stream);
-  }
-  const dim3 g2((unsigned)(groups * p.nseg));
-  launch<Mode::kScan>(a.io_dtype == SSM_BF16, a.delta_softplus != 0, p.K, g2, p, stream);
+  const bool bf16 = a.io_dtype == SSM_BF16, sp = a.delta_softplus != 0, lane = lane_bc(a);
+  auto run = [&](bool aggregate, dim3 grid) {
+    switch (slots(a.dstate)) {
+      case 1: fwd::launch_slots<1>(aggregate, lane, bf16, sp, p.K, grid, p, stream); break;
+      case 2: fwd::launch_slots<2>(aggregate, lane, bf16, sp, p.K, grid, p, stream); break;
+      default: fwd::launch_slots<4>(aggregate, lane, bf16, sp, p.K, grid, p, stream); break;
+    }
+  };
+  if (p.nseg > 1) run(true, dim3((unsigned)(groups * (p.nseg - 1))));
+  run(false, dim3((unsigned)(groups * p.nseg)));
   return hipGetLastError();
 }
 

@@ -1,0 +1,629 @@
+// scan_fwd_kernel.h -- the prefill selective-scan kernel for gfx950, as a
+// template instantiated by scan_fwd_s1/s2/s4.hip (one translation unit per
+// number of states a lane holds, so that the variants compile in parallel).
+//
+// Computes, per batch row b, channel d and state n (Mamba model notes sections
+// 2.2, 4.1 and 4.4; Mamba paper notes section 2.3 for the discretisation):
+//   Delta_t = softplus(delta_t + bias[d])
+//   h_t[n]  = exp(Delta_t A[d,n]) h_{t-1}[n] + Delta_t B[b,g,n,t] u_t
+//   out_t   = (sum_n C[b,g,n,t] h_t[n] + D[d] u_t) * silu(z_t)
+// with g the B/C group of channel d (one group: B and C shared by every
+// channel of the batch row).
+//
+// Work decomposition.  A workgroup is 4 wavefronts; a wavefront is 4
+// channels of one batch row, each a 16-lane row whose lane c holds the fp32
+// states n = c, c + 16, ... (S of them, S = 1, 2 or 4 for up to 16, 32 or 64
+// states; states past dstate are padding that stays exactly zero) in
+// registers for the whole sequence.  The workgroup walks its token range in
+// blocks of 16:
+//   owner role  lane (row r, col j) loads u/delta/z of token t0+j of channel r
+//               and computes Delta and Delta*u once; a DPP row_newbcast:j
+//               inside the consuming VALU op hands them to the 16 state lanes
+//               of the same row.
+//   B/C         shared mode (all 16 channels of the workgroup in one group):
+//               every 2 blocks the workgroup loads the next 16S x 32 tile of
+//               B and of C (one state row per 16 lanes, coalesced) into a
+//               double-buffered LDS tile and synchronises once; every lane
+//               then reads back its states' rows for each block.
+//               lane mode (groups smaller than a workgroup, down to one
+//               channel per group): each lane loads the 16 tokens of its own
+//               group's rows for each block straight from memory; no LDS
+//               tile and no barrier.
+//   readout     each state lane leaves sum_s C_n h_n per token in its
+//               wavefront's LDS; one block later the owner of the token sums
+//               the 16 partials, adds D*u, applies the gate and stores.
+// Apart from the B/C tile, LDS is private to a wavefront, whose LDS operations
+// complete in issue order, so the per-block exchange needs no barrier.  Every
+// global access goes through a buffer descriptor whose window ends where the
+// wavefront's data ends: lanes of a partial last block that reach past it
+// read zero instead of touching memory, so no lane clamps its address; the
+// B/C rows of padding states and the checkpoint stores of padding states
+// start at the window's end and read zero / are dropped the same way (the
+// host keeps every window 256 bytes short of 4 GiB, so these offsets plus a
+// block's reach never wrap).
+//
+// Long sequences with few channels.  The recurrence is linear in the state
+// (Mamba paper notes, sections 5.3/5.4: a long input can be cut into chunks
+// with the state handed from one chunk to the next), so the sequence may be
+// cut into G segments processed by different workgroups:
+//   pass 1 (aggregate)  segments 0..G-2 run from a zero state and record their
+//                       end state b_g and the sum of their step sizes S_g;
+//   pass 2 (scan)       segment g starts from
+//                       h_in = fold_{i<g} (exp(A S_i) h + b_i) applied to h0,
+//                       then runs exactly like the single-segment scan.
+// The exact state entering segment g is exp(A S_{g-1}) h_in(g-1) + b_{g-1},
+// so the fold reproduces the sequential result up to fp32 rounding.
+#pragma once
+
+#include <algorithm>
+
+#include "ssm_internal.h"
+
+namespace ssm {
+namespace fwd {
+
+constexpr int kN = 16;              // lanes per channel row (states per slot)
+constexpr int kRows = 4;            // channels per wavefront
+constexpr int kWaves = 4;           // wavefronts per workgroup
+constexpr int kCh = kRows * kWaves; // channels per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kT = 16;              // tokens per block
+constexpr int kGB = 2;              // blocks per B/C staging group
+constexpr int kGT = kT * kGB;       // tokens per group
+static_assert(4 % kGB == 0, "the steady-state loop runs four blocks at a time");
+constexpr int kGPitch = kGT + 4;    // LDS pitch (floats) of one state's group of B / C
+constexpr int kPitch = 20;          // LDS pitch (floats) of one state's readout partials
+constexpr int kPartRow = kN * kPitch + 16;  // floats per channel of readout partials
+
+enum class Mode { kScan, kAggregate };
+
+struct ScanParams {
+  const void* u;
+  const void* delta;
+  const void* z;
+  const void* B;
+  const void* C;
+  const float* A;
+  const float* D;
+  const float* bias;
+  const float* h0;
+  float* last_state;
+  void* out;
+  float* agg;      // [batch * dim][nseg - 1][N + 1] segment aggregates (nseg > 1)
+  float* ckpt;     // [batch][dim][nbk][N] states entering each block, or NULL
+  const float* conv_w;      // [dim][K] conv weights (the conv path only)
+  const float* conv_b;      // [dim] or NULL
+  const float* conv_in;     // [batch][dim][K] inputs before the sequence, or NULL
+  float* conv_stout;        // [batch][dim][K] last K inputs, or NULL
+  void* conv_out;           // (batch, dim, L) SSM input u, or NULL
+  int64_t usb, usd, dsb, dsd, zsb, zsd, Bsb, Bsg, Bsn, Csb, Csg, Csn, Asd, Asn, osb, osd,
+      cosb, cosd;
+  int K;                    // conv width
+  int conv_silu;
+  int N;                    // states per channel (dstate)
+  int64_t cpg;              // channels per B/C group
+  int64_t batch, dim;
+  int L;
+  int seg_len;     // tokens per segment (multiple of kGT)
+  int nseg;        // segments per sequence
+  int nbk;         // blocks per sequence, ceil(L / kT)
+  int64_t cgroups; // ceil(dim / kCh)
+};
+
+// Owner role raw inputs of one block: token t0 + col of the lane's channel
+// (bit patterns, widened where they are used); with the conv path, u holds
+// the conv input x.
+struct Raw {
+  uint32_t u, dt, z;
+};
+
+// Shared mode, stage role raw inputs of one group: B and C of states
+// 4w + row + 16s at tokens tg + col + 16i.
+template <int S>
+struct GroupRaw {
+  uint32_t b[S][kGB], c[S][kGB];
+};
+
+// Lane (J - m) mod 16 of the 16-lane row (DPP row_ror:m).
+template <int M>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + M, 0xf, 0xf, true));
+}
+
+template <typename T, Mode M, bool kSoftplus, int KP, int S, bool kLane>
+struct Wave {
+  const ScanParams& p;
+  int wave, row, col;
+  int t_beg, t_end, nblk, ngrp;
+  Window wu, wdt, wz, wB, wC, wout, wck;
+  uint32_t ou, odt, oz, oout;       // per-lane byte offsets inside the windows
+  // per state slot; B/C offsets of padding states (n >= dstate) point past
+  // their window, so those loads read zero
+  uint32_t oB[S], oC[S], ock[S];
+  uint32_t ckstep;    // checkpoint bytes per block of a channel row (0: none kept)
+  int blk0;           // global index of this segment's first block
+  float a2[S], bias, Dd;
+  // conv path (KP > 0: the width padded to KP): tap weights by lag m,
+  // wl[m] multiplies x_{t-m} (zero past the real width), and the bias
+  float wl[KP > 0 ? KP : 1], cb;
+  bool silu_in;
+  Window wco;                 // conv_out window (empty when not wanted)
+  uint32_t oco;
+  float (*sB)[kN * S][kGPitch];   // [2][16S][kGPitch], shared by the workgroup
+  float (*sC)[kN * S][kGPitch];
+  float (*sP)[kPartRow];          // this wavefront's [kRows][kPartRow]
+
+  static constexpr int E = Elem<T>::kSize;
+
+  __device__ __forceinline__ uint32_t skip(int k) const {
+    return static_cast<uint32_t>(t_beg + k * kT) * E;
+  }
+
+  // Owner raw inputs of block k; blocks past the last one reload the last one
+  // (the pipeline prefetches two blocks ahead and never uses those).
+  __device__ __forceinline__ Raw load(int k) const {
+    Raw r;
+    const uint32_t s = skip(min(k, nblk - 1));
+    r.u = Elem<T>::load(wu.at(s), ou);
+    r.dt = Elem<T>::load(wdt.at(s), odt);
+    // without a gate the z window is u's: the load is a cache hit, never used
+    r.z = M == Mode::kScan ? Elem<T>::load(wz.at(s), oz) : 0u;
+    return r;
+  }
+
+  // Shared mode, stage raw inputs of group g (clamped to the last group like
+  // load()).
+  __device__ __forceinline__ GroupRaw<S> load_group(int g) const {
+    GroupRaw<S> r;
+    const uint32_t s = skip(min(g, ngrp - 1) * kGB);
+    const __amdgpu_buffer_rsrc_t rb = wB.at(s);
+    const __amdgpu_buffer_rsrc_t rc = wC.at(s);
+#pragma unroll
+    for (int q = 0; q < S; ++q) {
+#pragma unroll
+      for (int i = 0; i < kGB; ++i) {
+        r.b[q][i] = Elem<T>::load(rb, oB[q] + i * kT * E);
+        r.c[q][i] = M == Mode::kScan ? Elem<T>::load(rc, oC[q] + i * kT * E) : 0u;
+      }
+    }
+    return r;
+  }
+
+  // Shared mode, stage role: group g's B (and C) into LDS buffer g & 1.  B of
+  // tokens past the end is zeroed so that a non-finite value read from
+  // beyond a row cannot reach h; rows of padding states load as zero.
+  __device__ __forceinline__ void stage(int g, const GroupRaw<S>& r) const {
+    const int st = kRows * wave + row;
+    const int t = t_beg + g * kGT + col;
+#pragma unroll
+    for (int q = 0; q < S; ++q) {
+#pragma unroll
+      for (int i = 0; i < kGB; ++i) {
+        const float bv = Elem<T>::f32(r.b[q][i]);
+        sB[g & 1][st + kN * q][col + i * kT] = t + i * kT < t_end ? bv : 0.0f;
+        if (M == Mode::kScan) sC[g & 1][st + kN * q][col + i * kT] = Elem<T>::f32(r.c[q][i]);
+      }
+    }
+  }
+
+  // B and C of state slot q for the 16 tokens of block k: from the LDS tile
+  // (shared mode) or from this lane's own rows (lane mode; tokens past the
+  // end read as zero B).
+  template <bool kMask>
+  __device__ __forceinline__ void bc(int k, int q, float (&bv)[kT], float (&cv)[kT]) const {
+    if constexpr (!kLane) {
+      const int buf = (k / kGB) & 1;
+      const int tb = (k % kGB) * kT;
+#pragma unroll
+      for (int i = 0; i < kT / 4; ++i) {
+        const float4 x = *reinterpret_cast<const float4*>(&sB[buf][col + kN * q][tb + 4 * i]);
+        bv[4 * i] = x.x; bv[4 * i + 1] = x.y; bv[4 * i + 2] = x.z; bv[4 * i + 3] = x.w;
+        if (M == Mode::kScan) {
+          const float4 y = *reinterpret_cast<const float4*>(&sC[buf][col + kN * q][tb + 4 * i]);
+          cv[4 * i] = y.x; cv[4 * i + 1] = y.y; cv[4 * i + 2] = y.z; cv[4 * i + 3] = y.w;
+        }
+      }
+    } else {
+      const uint32_t s = skip(k);
+      const __amdgpu_buffer_rsrc_t rb = wB.at(s);
+      const __amdgpu_buffer_rsrc_t rc = wC.at(s);
+      const int tleft = t_end - (t_beg + k * kT);
+#pragma unroll
+      for (int j = 0; j < kT; ++j) {
+        const float b = Elem<T>::f32(Elem<T>::load(rb, oB[q] + j * E));
+        bv[j] = !kMask || j < tleft ? b : 0.0f;
+        if (M == Mode::kScan) cv[j] = Elem<T>::f32(Elem<T>::load(rc, oC[q] + j * E));
+      }
+    }
+  }
+
+  // Owner role: readout of block k (y = the sum of its 16 partials, uv its
+  // SSM input), skip term, gate, store.  Rows past dim repeat the last channel bit for bit, so in full
+  // blocks every lane may store (duplicates write identical values); with
+  // kMask only tokens before the end are stored.
+  template <bool kMask>
+  __device__ __forceinline__ void finish(int k, const Raw& r, float uv, float y) const {
+    y = fmaf(Dd, uv, y);
+    const float g = silu_f32(Elem<T>::f32(r.z));
+    y *= p.z ? g : 1.0f;  // a select, not a branch
+    const __amdgpu_buffer_rsrc_t ro = wout.at(skip(k));
+    if (!kMask || t_beg + k * kT + col < t_end) Elem<T>::store(ro, oout, y);
+  }
+
+  // Iteration k.  Buffers: P = block k-1 (finish), Q = block k (scan),
+  // R = block k+2 (load target); G holds the next group's B/C.
+  // kMask = false is the steady state, valid when blocks k-1 and k are full:
+  // it has no branch, so the scan's DPP broadcasts stay fused into the ops
+  // that use them.  kEnd (steady state only) marks the last block of a group,
+  // after which the next group is staged and the workgroup synchronises; in
+  // the masked form that is decided at run time.
+  template <bool kMask, bool kEnd>
+  __device__ __forceinline__ void iter(int k, float (&h)[S], double& ssum, const Raw& P,
+                                       const Raw& Q, Raw& R, GroupRaw<S>& G, float& uprev,
+                                       float& xprev) const {
+    // B/C of the first state slot and the previous block's partials first
+    float bv[kT], cv[kT];
+    bc<kMask>(k, 0, bv, cv);
+    float ysum = 0.0f;
+    if (M == Mode::kScan) {
+      // unconditional: at k = 0 the value is never used; summed right away so
+      // that one register, not sixteen, lives across the scan
+      float part[kN];
+#pragma unroll
+      for (int n = 0; n < kN; ++n) part[n] = sP[row][n * kPitch + col];
+#pragma unroll
+      for (int n = 0; n < kN; ++n) ysum += part[n];
+    }
+    R = load(k + 2);
+
+    // owner role: the SSM input u of this token (through the causal conv on
+    // the conv path), Delta and Delta*u (zero past the end)
+    float uv;
+    if constexpr (KP > 0) {
+      // x_{t-m} is lane col-m of this block for m <= col, else lane col-m+16
+      // of the previous one: a DPP row rotation of each and a select
+      const float xc = Elem<T>::f32(Q.u);
+      float pre = fmaf(wl[0], xc, cb);
+      static_for<1, KP>([&](auto Mm) {
+        constexpr int m = decltype(Mm)::value;
+        const float xcur = row_ror<m>(xc), xold = row_ror<m>(xprev);
+        pre = fmaf(wl[m], col >= m ? xcur : xold, pre);
+      });
+      const float act = silu_f32(pre);
+      uv = silu_in ? act : pre;  // a select, not a branch
+      xprev = xc;
+      if (M == Mode::kScan && (!kMask || t_beg + k * kT + col < t_end))
+        Elem<T>::store(wco.at(p.conv_out ? skip(k) : 0u), oco, uv);
+    } else {
+      uv = Elem<T>::f32(Q.u);
+    }
+    const float x = Elem<T>::f32(Q.dt) + bias;
+    float dl = kSoftplus ? softplus_f32(x) : x;
+    float du = dl * uv;
+    if (kMask) {
+      const bool own = t_beg + k * kT + col < t_end;
+      dl = own ? dl : 0.0f;
+      du = own ? du : 0.0f;
+    }
+    if (M == Mode::kAggregate) ssum += static_cast<double>(dl);
+
+    // checkpoint: the states entering this block (an empty window when none
+    // are kept, and an offset past the window for padding slots, so the
+    // stores are dropped without a branch)
+    if (M == Mode::kScan) {
+#pragma unroll
+      for (int q = 0; q < S; ++q) Elem<float>::store(wck.at((blk0 + k) * ckstep), ock[q], h[q]);
+    }
+
+    // state role: 16 sequential steps of each state slot; the readout
+    // partials sum_q C_n h_n go to LDS four tokens at a time after the last
+    // slot
+    // one slot: a rolling 4-register buffer; several: one sum per token
+    float pk[S == 1 ? 4 : kT];
+    static_for<0, S>([&](auto Qs) {
+      constexpr int q = decltype(Qs)::value;
+      if constexpr (q > 0) {
+        // compiler-only fence: one slot's B/C live at a time, not all S
+        asm volatile("" ::: "memory");
+        bc<kMask>(k, q, bv, cv);
+      }
+      static_for<0, kT>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        const float e = __builtin_amdgcn_exp2f(row_bcast<j>(dl) * a2[q]);  // Abar = exp(Delta A)
+        const float w = row_bcast<j>(du) * bv[j];                          // Bbar u = Delta u B
+        h[q] = fmaf(e, h[q], w);
+        if (M == Mode::kScan) {
+          constexpr int i = S == 1 ? j % 4 : j;
+          pk[i] = q == 0 ? cv[j] * h[q] : fmaf(cv[j], h[q], pk[i]);        // C_n h_n
+          if (q == S - 1 && j % 4 == 3)
+            *reinterpret_cast<float4*>(&sP[row][col * kPitch + j - 3]) =
+                make_float4(pk[i - 3], pk[i - 2], pk[i - 1], pk[i]);
+        }
+      });
+    });
+    if (M == Mode::kScan) {
+      if (!kMask) finish<false>(k - 1, P, uprev, ysum);
+      else if (k > 0) finish<true>(k - 1, P, uprev, ysum);
+    }
+    uprev = uv;
+    // Compiler-only fence: keep this block's LDS traffic in program order with
+    // the next block's (the hardware already keeps one wavefront's in order).
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    if constexpr (!kLane) {
+      if (kMask ? (k % kGB == kGB - 1 && k + 1 < nblk) : kEnd) {
+        // Group (k+1)/kGB into the other buffer.  Every wavefront finished
+        // reading that buffer before the previous barrier.
+        const int g = k / kGB + 1;
+        stage(g, G);
+        __syncthreads();
+        G = load_group(g + 1);
+      }
+    }
+  }
+};
+
+template <typename T, Mode M, bool kSoftplus, int KP, int S, bool kLane>
+__global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
+  constexpr int kTile = kLane ? 1 : 2;
+  __shared__ __align__(16) float sB[kTile][kN * S][kGPitch];
+  __shared__ __align__(16) float sC[M == Mode::kScan ? kTile : 1][kN * S][kGPitch];
+  __shared__ __align__(16) float sP[M == Mode::kScan ? kWaves : 1][kRows][kPartRow];
+  __shared__ double sSum[M == Mode::kScan ? 1 : kWaves][kRows][kT];
+
+  // wavefront index, made visibly uniform so that windows stay in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = (threadIdx.x >> 4) & 3;
+  const int col = threadIdx.x & 15;
+  // blockIdx.x = (b * cgroups + cg) * nseg_grid + g; the aggregate pass skips
+  // the last segment (its end state is never needed by a later segment)
+  const int nseg_grid = M == Mode::kScan ? p.nseg : p.nseg - 1;
+  const int g = static_cast<int>(blockIdx.x % nseg_grid);
+  const int64_t bc = blockIdx.x / nseg_grid;
+  const int64_t b = bc / p.cgroups;
+  const int64_t d = (bc % p.cgroups) * kCh + kRows * wave + row;
+  const bool vrow = d < p.dim;
+  // rows past dim repeat the last channel exactly (same inputs, same state)
+  const int64_t dc = vrow ? d : p.dim - 1;
+  // this wavefront's first and last (clamped) rows
+  const int64_t dw0 = std::min<int64_t>((bc % p.cgroups) * kCh + kRows * wave, p.dim - 1);
+  const int64_t dw3 = std::min<int64_t>(dw0 + kRows - 1, p.dim - 1);
+  const int N = p.N;
+  const int aggs = N + 1;  // floats per (channel, segment) aggregate: b[N], S
+
+  constexpr int E = Elem<T>::kSize;
+  Wave<T, M, kSoftplus, KP, S, kLane> w{p};
+  w.wave = wave; w.row = row; w.col = col;
+  w.t_beg = g * p.seg_len;
+  w.t_end = std::min(p.L, w.t_beg + p.seg_len);
+  w.nblk = (w.t_end - w.t_beg + kT - 1) / kT;
+  w.ngrp = (w.nblk + kGB - 1) / kGB;
+
+  // Windows run from this wavefront's first row to the end of its last row.
+  auto rows_window = [&](const void* base, int64_t sb, int64_t sd, uint32_t& off) {
+    off = static_cast<uint32_t>(((dc - dw0) * sd + col) * E);
+    return Window{static_cast<const char*>(base) + (b * sb + dw0 * sd) * E,
+                  static_cast<uint32_t>(((dw3 - dw0) * sd + p.L) * E)};
+  };
+  w.wu = rows_window(p.u, p.usb, p.usd, w.ou);
+  w.wdt = rows_window(p.delta, p.dsb, p.dsd, w.odt);
+  if (p.z) {
+    w.wz = rows_window(p.z, p.zsb, p.zsd, w.oz);
+  } else {
+    w.wz = w.wu;
+    w.oz = w.ou;
+  }
+  w.wout = rows_window(p.out, p.osb, p.osd, w.oout);
+  // checkpoints: rows of nbk * N floats, [b][d][block][n]
+  const int64_t ckrow = static_cast<int64_t>(p.nbk) * N;
+  w.blk0 = w.t_beg / kT;
+  w.ckstep = p.ckpt ? N * 4 : 0;
+  w.wck = Window{reinterpret_cast<const char*>(p.ckpt ? p.ckpt + (b * p.dim + dw0) * ckrow : nullptr),
+                 p.ckpt ? static_cast<uint32_t>((dw3 - dw0 + 1) * ckrow * 4) : 0u};
+#pragma unroll
+  for (int q = 0; q < S; ++q) {
+    const int n = col + kN * q;
+    w.ock[q] = n < N ? static_cast<uint32_t>(((dc - dw0) * ckrow + n) * 4) : w.wck.bytes;
+  }
+  if constexpr (!kLane) {
+    // B/C: the workgroup's group; this lane stages states 4 wave + row + 16q
+    // of tokens col, col + 16 of each staging group
+    const int64_t grp = ((bc % p.cgroups) * kCh) / p.cpg;
+    const int st = kRows * wave + row;
+    w.wB = Window{static_cast<const char*>(p.B) + (b * p.Bsb + grp * p.Bsg) * E,
+                  static_cast<uint32_t>(((N - 1) * p.Bsn + p.L) * E)};
+    w.wC = Window{static_cast<const char*>(p.C) + (b * p.Csb + grp * p.Csg) * E,
+                  static_cast<uint32_t>(((N - 1) * p.Csn + p.L) * E)};
+#pragma unroll
+    for (int q = 0; q < S; ++q) {
+      const int n = st + kN * q;
+      w.oB[q] = n < N ? static_cast<uint32_t>((n * p.Bsn + col) * E) : w.wB.bytes;
+      w.oC[q] = n < N ? static_cast<uint32_t>((n * p.Csn + col) * E) : w.wC.bytes;
+    }
+  } else {
+    // B/C: this lane reads its own states' rows in its channel's group; the
+    // window spans the groups of the wavefront's four rows
+    const int64_t g0 = dw0 / p.cpg, g3 = dw3 / p.cpg, gl = dc / p.cpg;
+    w.wB = Window{static_cast<const char*>(p.B) + (b * p.Bsb + g0 * p.Bsg) * E,
+                  static_cast<uint32_t>(((g3 - g0) * p.Bsg + (N - 1) * p.Bsn + p.L) * E)};
+    w.wC = Window{static_cast<const char*>(p.C) + (b * p.Csb + g0 * p.Csg) * E,
+                  static_cast<uint32_t>(((g3 - g0) * p.Csg + (N - 1) * p.Csn + p.L) * E)};
+#pragma unroll
+    for (int q = 0; q < S; ++q) {
+      const int n = col + kN * q;
+      w.oB[q] = n < N ? static_cast<uint32_t>(((gl - g0) * p.Bsg + n * p.Bsn) * E) : w.wB.bytes;
+      w.oC[q] = n < N ? static_cast<uint32_t>(((gl - g0) * p.Csg + n * p.Csn) * E) : w.wC.bytes;
+    }
+  }
+
+#pragma unroll
+  for (int q = 0; q < S; ++q) {
+    const int n = col + kN * q;
+    w.a2[q] = n < N ? p.A[dc * p.Asd + n * p.Asn] * kLog2e : 0.0f;
+  }
+  w.bias = p.bias ? p.bias[dc] : 0.0f;
+  w.Dd = p.D ? p.D[dc] : 0.0f;
+  w.sB = sB; w.sC = sC; w.sP = sP[M == Mode::kScan ? wave : 0];
+
+  // conv path: tap weights by lag, bias, the inputs just before this
+  // segment (x_{t_beg-16+col}: from the conv state at the sequence start,
+  // else from x itself), and the conv_out window
+  float xprev = 0.0f;
+  if constexpr (KP > 0) {
+    const int K = p.K;
+#pragma unroll
+    for (int m = 0; m < KP; ++m) w.wl[m] = m < K ? p.conv_w[dc * K + (K - 1 - m)] : 0.0f;
+    w.cb = p.conv_b ? p.conv_b[dc] : 0.0f;
+    w.silu_in = p.conv_silu != 0;
+    if (w.t_beg == 0) {
+      const int t = col - kT;  // token index before the sequence, -16 .. -1
+      xprev = (p.conv_in && t >= -K) ? p.conv_in[(b * p.dim + dc) * K + K + t] : 0.0f;
+    } else {
+      xprev = Elem<T>::f32(Elem<T>::load(w.wu.at(static_cast<uint32_t>(w.t_beg - kT) * E), w.ou));
+    }
+    if (p.conv_out) {
+      w.wco = rows_window(p.conv_out, p.cosb, p.cosd, w.oco);
+    } else {
+      w.wco = Window{nullptr, 0u};
+      w.oco = 0;
+    }
+  }
+  float uprev = 0.0f;
+
+  // Initial state: zero for an aggregate segment; otherwise h0 (or zero) carried
+  // through the aggregates of every earlier segment.
+  float h[S];
+#pragma unroll
+  for (int q = 0; q < S; ++q) {
+    const int n = col + kN * q;
+    h[q] = 0.0f;
+    if (M == Mode::kScan && n < N) {
+      h[q] = p.h0 ? p.h0[(b * p.dim + dc) * N + n] : 0.0f;
+      if (g > 0) {
+        const float* ag = p.agg + ((b * p.dim + dc) * (p.nseg - 1)) * aggs;
+        for (int i = 0; i < g; ++i) {
+          const float decay = __builtin_amdgcn_exp2f(w.a2[q] * ag[i * aggs + N]);
+          h[q] = fmaf(decay, h[q], ag[i * aggs + n]);
+        }
+      }
+    }
+  }
+
+  double ssum = 0.0;
+  // group 0 staged before the loop, group 1 in flight; block j's owner inputs
+  // live in buffer j % 4 and iteration k loads block k + 2
+  GroupRaw<S> grp;
+  if constexpr (!kLane) grp = w.load_group(0);
+  Raw buf0 = w.load(0), buf1 = w.load(1), buf2 = buf0, buf3 = buf0;
+  if constexpr (!kLane) {
+    w.stage(0, grp);
+    grp = w.load_group(1);
+    __syncthreads();
+  }
+
+  // Steady state: iterations 1 .. nfull-1 (blocks k-1 and k full), four at a
+  // time so that buffer j % 4 is a fixed set of registers; a group ends at
+  // k % kGB == kGB - 1.  The first iteration and the last few take the masked
+  // form.
+  const int nblk = w.nblk;
+  const int nfull = (w.t_end - w.t_beg) / kT;
+  w.template iter<true, false>(0, h, ssum, buf3, buf0, buf2, grp, uprev, xprev);
+  int k = 1;
+  for (; k + 4 <= nfull; k += 4) {
+    // k % 4 == 1 here, and 4 is a multiple of kGB
+    w.template iter<false, (1 % kGB == kGB - 1)>(k + 0, h, ssum, buf0, buf1, buf3, grp, uprev, xprev);
+    w.template iter<false, (2 % kGB == kGB - 1)>(k + 1, h, ssum, buf1, buf2, buf0, grp, uprev, xprev);
+    w.template iter<false, (3 % kGB == kGB - 1)>(k + 2, h, ssum, buf2, buf3, buf1, grp, uprev, xprev);
+    w.template iter<false, (4 % kGB == kGB - 1)>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev);
+  }
+  if (k < nblk) w.template iter<true, false>(k, h, ssum, buf0, buf1, buf3, grp, uprev, xprev);
+  if (k + 1 < nblk) w.template iter<true, false>(k + 1, h, ssum, buf1, buf2, buf0, grp, uprev, xprev);
+  if (k + 2 < nblk) w.template iter<true, false>(k + 2, h, ssum, buf2, buf3, buf1, grp, uprev, xprev);
+  if (k + 3 < nblk) w.template iter<true, false>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev);
+
+  if (M == Mode::kScan) {
+    // finish the last block: its partials are in LDS, its raw inputs in buffer
+    // (nblk - 1) % 4
+    const int kl = nblk - 1;
+    const int r = kl & 3;
+    const Raw last = r == 0 ? buf0 : r == 1 ? buf1 : r == 2 ? buf2 : buf3;
+    float ysum = 0.0f;
+#pragma unroll
+    for (int n = 0; n < kN; ++n) ysum += w.sP[row][n * kPitch + col];
+    w.template finish<true>(kl, last, uprev, ysum);
+    if (vrow && p.last_state && g == p.nseg - 1) {
+#pragma unroll
+      for (int q = 0; q < S; ++q) {
+        const int n = col + kN * q;
+        if (n < N) p.last_state[(b * p.dim + d) * N + n] = h[q];
+      }
+    }
+    if constexpr (KP > 0) {
+      // the last K inputs, for the decode update to continue from
+      const int K = p.K;
+      if (vrow && p.conv_stout && g == p.nseg - 1 && col < K) {
+        const int t = p.L - K + col;
+        float v;
+        if (t >= 0) {
+          const uint32_t orow = w.ou - static_cast<uint32_t>(col * E);
+          v = Elem<T>::f32(Elem<T>::load(w.wu.at(0), orow + static_cast<uint32_t>(t * E)));
+        } else {
+          v = p.conv_in ? p.conv_in[(b * p.dim + d) * K + K + t] : 0.0f;
+        }
+        p.conv_stout[(b * p.dim + d) * K + col] = v;
+      }
+    }
+  } else {
+    // segment aggregate: end state from zero and the step-size sum (fp64 partial
+    // sums of the 16 owner lanes of each channel, added in a fixed order)
+    sSum[wave][row][col] = ssum;
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    float* ag = p.agg + ((b * p.dim + dc) * (p.nseg - 1) + g) * aggs;
+    if (vrow) {
+#pragma unroll
+      for (int q = 0; q < S; ++q) {
+        const int n = col + kN * q;
+        if (n < N) ag[n] = h[q];
+      }
+    }
+    if (vrow && col == 0) {
+      double s = 0.0;
+      for (int j = 0; j < kT; ++j) s += sSum[wave][row][j];
+      ag[N] = static_cast<float>(s);
+    }
+  }
+}
+
+// Launch of one variant family: the dtype, softplus and conv width choose
+// among the instantiations with S state slots per lane and the B/C mode.
+template <Mode M, int KP, int S, bool kLane>
+void launch_kp(bool bf16, bool softplus, dim3 grid, const ScanParams& p, hipStream_t stream) {
+  const dim3 block(kThreads);
+  if (bf16) {
+    if (softplus) scan_fwd_kernel<uint16_t, M, true, KP, S, kLane><<<grid, block, 0, stream>>>(p);
+    else scan_fwd_kernel<uint16_t, M, false, KP, S, kLane><<<grid, block, 0, stream>>>(p);
+  } else {
+    if (softplus) scan_fwd_kernel<float, M, true, KP, S, kLane><<<grid, block, 0, stream>>>(p);
+    else scan_fwd_kernel<float, M, false, KP, S, kLane><<<grid, block, 0, stream>>>(p);
+  }
+}
+
+// The conv width is padded to 4 or 8 taps (zero weights); only the
+// one-slot shared-B/C kernels, the common Mamba-1 shape, get the 4-tap form.
+template <Mode M, int S, bool kLane>
+void launch_mode(bool bf16, bool softplus, int K, dim3 grid, const ScanParams& p,
+                 hipStream_t stream) {
+  if (K == 0) launch_kp<M, 0, S, kLane>(bf16, softplus, grid, p, stream);
+  else if (K <= 4 && S == 1 && !kLane) launch_kp<M, 4, S, kLane>(bf16, softplus, grid, p, stream);
+  else launch_kp<M, 8, S, kLane>(bf16, softplus, grid, p, stream);
+}
+
+// Both passes' launches for S state slots per lane (defined in
+// scan_fwd_s<S>.hip).
+template <int S>
+void launch_slots(bool aggregate, bool lane, bool bf16, bool softplus, int K, dim3 grid,
+                  const ScanParams& p, hipStream_t stream);
+
+}  // namespace fwd
+}  // namespace ssm

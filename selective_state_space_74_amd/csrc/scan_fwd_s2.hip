@@ -1,0 +1,21 @@
+// scan_fwd_s2.hip -- instantiations of the prefill scan with 2 state slot(s)
+// per lane (dstate up to 32); the kernel is in scan_fwd_kernel.h.
+#include "scan_fwd_kernel.h"
+
+namespace ssm {
+namespace fwd {
+
+template <>
+void launch_slots<2>(bool aggregate, bool lane, bool bf16, bool softplus, int K, dim3 grid,
+                      const ScanParams& p, hipStream_t stream) {
+  if (aggregate) {
+    if (lane) launch_mode<Mode::kAggregate, 2, true>(bf16, softplus, K, grid, p, stream);
+    else launch_mode<Mode::kAggregate, 2, false>(bf16, softplus, K, grid, p, stream);
+  } else {
+    if (lane) launch_mode<Mode::kScan, 2, true>(bf16, softplus, K, grid, p, stream);
+    else launch_mode<Mode::kScan, 2, false>(bf16, softplus, K, grid, p, stream);
+  }
+}
+
+}  // namespace fwd
+}  // namespace ssm

@@ -29,6 +29,22 @@ Span span3(const void* p, int64_t n0, int64_t s0, int64_t n1, int64_t s1, int64_
 
 Span span1(const void* p, int64_t n, int64_t esz) { return span3(p, 1, 0, 1, 0, n, esz); }
 
+// Bytes touched by a (n0, n1, n2, n3) tensor with strides (s0, s1, s2, 1).
+Span span4(const void* p, int64_t n0, int64_t s0, int64_t n1, int64_t s1, int64_t n2,
+           int64_t s2, int64_t n3, int64_t esz) {
+  Span s;
+  if (!p || n0 <= 0 || n1 <= 0 || n2 <= 0 || n3 <= 0) return s;
+  s.lo = reinterpret_cast<uintptr_t>(p);
+  s.hi = s.lo + static_cast<uintptr_t>(((n0 - 1) * s0 + (n1 - 1) * s1 + (n2 - 1) * s2 + n3) * esz);
+  return s;
+}
+
+// B/C groups: 0 or 1 is one group; otherwise it must divide dim.
+int64_t groups_of(int64_t ngroups) { return ngroups > 1 ? ngroups : 1; }
+bool bad_groups(int64_t ngroups, int64_t dim) {
+  return ngroups < 0 || (dim > 0 && dim % groups_of(ngroups) != 0);
+}
+
 bool misaligned(const void* p, int64_t align) {
   return p && (reinterpret_cast<uintptr_t>(p) % static_cast<uintptr_t>(align)) != 0;
 }
@@ -49,7 +65,7 @@ size_t ssm_scan_bwd_args_size(void) { return sizeof(ssm_scan_bwd_args); }
 size_t ssm_update_args_size(void) { return sizeof(ssm_update_args); }
 
 size_t ssm_scan_workspace_size(const ssm_scan_args* a) {
-  if (!a || a->dstate != 16 || a->seqlen > kMaxSeqlen) return 0;
+  if (!a || a->dstate < 1 || a->dstate > SSM_MAX_DSTATE || a->seqlen > kMaxSeqlen) return 0;
   return ssm::scan_workspace_bytes(*a);
 }
 
@@ -57,12 +73,12 @@ const char* ssm_status_string(int status) {
   switch (status) {
     case SSM_OK: return "ok";
     case SSM_ERR_NULL: return "a required pointer is NULL";
-    case SSM_ERR_SHAPE: return "invalid size (negative, or dstate < 1)";
+    case SSM_ERR_SHAPE: return "invalid size (negative, dstate < 1, or ngroups not dividing dim)";
     case SSM_ERR_STRIDE: return "invalid stride (negative)";
     case SSM_ERR_DTYPE: return "io_dtype must be SSM_F32 or SSM_BF16";
     case SSM_ERR_ALIGN: return "pointer not aligned to its element size";
     case SSM_ERR_ALIAS: return "an output overlaps an input";
-    case SSM_ERR_UNSUPPORTED: return "unsupported configuration (dstate != 16, or a size past the limits in ssm.h)";
+    case SSM_ERR_UNSUPPORTED: return "unsupported configuration (dstate or B/C groups outside what is built, or a size past the limits in ssm.h)";
     case SSM_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
   }
@@ -71,11 +87,13 @@ const char* ssm_status_string(int status) {
 int ssm_validate_scan(const ssm_scan_args* a) {
   if (!a) return SSM_ERR_NULL;
   if (a->batch < 0 || a->dim < 0 || a->seqlen < 0 || a->dstate < 1) return SSM_ERR_SHAPE;
+  if (bad_groups(a->ngroups, a->dim)) return SSM_ERR_SHAPE;
   if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
-  if (a->dstate != 16) return SSM_ERR_UNSUPPORTED;
+  if (a->dstate > SSM_MAX_DSTATE) return SSM_ERR_UNSUPPORTED;
   if (a->seqlen > kMaxSeqlen) return SSM_ERR_UNSUPPORTED;
   if (a->batch == 0 || a->dim == 0) return SSM_OK;
   const int64_t B = a->batch, Dm = a->dim, L = a->seqlen, N = a->dstate;
+  const int64_t G = groups_of(a->ngroups);
   const int64_t esz = io_size(a->io_dtype);
   if (L > 0) {
     if (!a->u || !a->delta || !a->B || !a->C || !a->A || !a->out) return SSM_ERR_NULL;
@@ -83,7 +101,8 @@ int ssm_validate_scan(const ssm_scan_args* a) {
                                a->delta_dim_stride, a->B_batch_stride, a->B_state_stride,
                                a->C_batch_stride, a->C_state_stride, a->A_dim_stride,
                                a->A_state_stride, a->out_batch_stride, a->out_dim_stride,
-                               a->z ? a->z_batch_stride : 0, a->z ? a->z_dim_stride : 0};
+                               a->z ? a->z_batch_stride : 0, a->z ? a->z_dim_stride : 0,
+                               G > 1 ? a->B_group_stride : 0, G > 1 ? a->C_group_stride : 0};
     for (int64_t s : strides)
       if (s < 0) return SSM_ERR_STRIDE;
     if (misaligned(a->u, esz) || misaligned(a->delta, esz) || misaligned(a->z, esz) ||
@@ -120,8 +139,8 @@ int ssm_validate_scan(const ssm_scan_args* a) {
       span3(a->u, B, a->u_batch_stride, Dm, a->u_dim_stride, L, esz),
       span3(a->delta, B, a->delta_batch_stride, Dm, a->delta_dim_stride, L, esz),
       span3(a->z, B, a->z_batch_stride, Dm, a->z_dim_stride, L, esz),
-      span3(a->B, B, a->B_batch_stride, N, a->B_state_stride, L, esz),
-      span3(a->C, B, a->C_batch_stride, N, a->C_state_stride, L, esz),
+      span4(a->B, B, a->B_batch_stride, G, a->B_group_stride, N, a->B_state_stride, L, esz),
+      span4(a->C, B, a->C_batch_stride, G, a->C_group_stride, N, a->C_state_stride, L, esz),
       sA, span1(a->D, Dm, 4), span1(a->delta_bias, Dm, 4), sh0,
       span1(a->conv_weight, Dm * K, 4), span1(a->conv_bias, Dm, 4),
       span1(a->conv_state_in, B * Dm * K, 4)};
@@ -148,12 +167,17 @@ int ssm_validate_scan(const ssm_scan_args* a) {
 int ssm_validate_scan_bwd(const ssm_scan_bwd_args* a) {
   if (!a) return SSM_ERR_NULL;
   if (a->batch < 0 || a->dim < 0 || a->seqlen < 0 || a->dstate < 1) return SSM_ERR_SHAPE;
+  if (bad_groups(a->ngroups, a->dim)) return SSM_ERR_SHAPE;
   if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
   if (a->dstate != 16) return SSM_ERR_UNSUPPORTED;
+  // every block of 16 channels must sit in one group
+  if (groups_of(a->ngroups) > 1 && (a->dim / groups_of(a->ngroups)) % 16 != 0)
+    return SSM_ERR_UNSUPPORTED;
   if (a->seqlen > kMaxSeqlen) return SSM_ERR_UNSUPPORTED;
   if (a->batch == 0 || a->dim == 0) return SSM_OK;
   if (!a->A || !a->dA) return SSM_ERR_NULL;
   const int64_t B = a->batch, Dm = a->dim, L = a->seqlen, N = a->dstate;
+  const int64_t G = groups_of(a->ngroups);
   const int64_t esz = io_size(a->io_dtype);
   if (L > 0) {
     if (!a->u || !a->delta || !a->B || !a->C || !a->checkpoints || !a->dout || !a->du ||
@@ -166,7 +190,8 @@ int ssm_validate_scan_bwd(const ssm_scan_bwd_args* a) {
                                a->du_batch_stride, a->du_dim_stride, a->ddelta_batch_stride,
                                a->ddelta_dim_stride, a->z ? a->z_batch_stride : 0,
                                a->z ? a->z_dim_stride : 0, a->z ? a->dz_batch_stride : 0,
-                               a->z ? a->dz_dim_stride : 0};
+                               a->z ? a->dz_dim_stride : 0, G > 1 ? a->B_group_stride : 0,
+                               G > 1 ? a->C_group_stride : 0};
     for (int64_t s : strides)
       if (s < 0) return SSM_ERR_STRIDE;
     if (misaligned(a->u, esz) || misaligned(a->delta, esz) || misaligned(a->z, esz) ||
@@ -185,8 +210,8 @@ int ssm_validate_scan_bwd(const ssm_scan_bwd_args* a) {
       span3(a->u, B, a->u_batch_stride, Dm, a->u_dim_stride, L, esz),
       span3(a->delta, B, a->delta_batch_stride, Dm, a->delta_dim_stride, L, esz),
       span3(a->z, B, a->z_batch_stride, Dm, a->z_dim_stride, L, esz),
-      span3(a->B, B, a->B_batch_stride, N, a->B_state_stride, L, esz),
-      span3(a->C, B, a->C_batch_stride, N, a->C_state_stride, L, esz),
+      span4(a->B, B, a->B_batch_stride, G, a->B_group_stride, N, a->B_state_stride, L, esz),
+      span4(a->C, B, a->C_batch_stride, G, a->C_group_stride, N, a->C_state_stride, L, esz),
       L > 0 ? Span{reinterpret_cast<uintptr_t>(a->A),
                    reinterpret_cast<uintptr_t>(a->A) +
                        static_cast<uintptr_t>(((Dm - 1) * a->A_dim_stride +
@@ -200,7 +225,7 @@ int ssm_validate_scan_bwd(const ssm_scan_bwd_args* a) {
       span3(a->du, B, a->du_batch_stride, Dm, a->du_dim_stride, L, esz),
       span3(a->ddelta, B, a->ddelta_batch_stride, Dm, a->ddelta_dim_stride, L, esz),
       a->z ? span3(a->dz, B, a->dz_batch_stride, Dm, a->dz_dim_stride, L, esz) : Span{},
-      span1(a->dB, B * N * L, 4), span1(a->dC, B * N * L, 4), span1(a->dA, Dm * N, 4),
+      span1(a->dB, B * G * N * L, 4), span1(a->dC, B * G * N * L, 4), span1(a->dA, Dm * N, 4),
       span1(a->dD, Dm, 4), span1(a->ddelta_bias, Dm, 4), span1(a->dh0, B * Dm * N, 4)};
   for (const Span& o : outputs) {
     for (const Span& i : inputs)
@@ -214,15 +239,18 @@ int ssm_validate_scan_bwd(const ssm_scan_bwd_args* a) {
 int ssm_validate_update(const ssm_update_args* a) {
   if (!a) return SSM_ERR_NULL;
   if (a->batch < 0 || a->dim < 0 || a->dstate < 1) return SSM_ERR_SHAPE;
+  if (bad_groups(a->ngroups, a->dim)) return SSM_ERR_SHAPE;
   if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
-  if (a->dstate != 16) return SSM_ERR_UNSUPPORTED;
+  if (a->dstate > SSM_MAX_DSTATE) return SSM_ERR_UNSUPPORTED;
   if (a->batch > 65535) return SSM_ERR_UNSUPPORTED;
   if (a->batch == 0 || a->dim == 0) return SSM_OK;
   if (!a->state || !a->x || !a->dt || !a->B || !a->C || !a->A || !a->out) return SSM_ERR_NULL;
   const int64_t strides[] = {a->state_batch_stride, a->state_dim_stride, a->x_batch_stride,
                              a->dt_batch_stride, a->z ? a->z_batch_stride : 0,
                              a->B_batch_stride, a->C_batch_stride, a->A_dim_stride,
-                             a->out_batch_stride};
+                             a->out_batch_stride,
+                             a->ngroups > 1 ? a->B_group_stride : 0,
+                             a->ngroups > 1 ? a->C_group_stride : 0};
   for (int64_t s : strides)
     if (s < 0) return SSM_ERR_STRIDE;
   const int64_t esz = io_size(a->io_dtype);
@@ -237,8 +265,9 @@ int ssm_validate_update(const ssm_update_args* a) {
   const Span sx = span3(a->x, 1, 0, B, a->x_batch_stride, Dm, esz);
   const Span sdt = span3(a->dt, 1, 0, B, a->dt_batch_stride, Dm, esz);
   const Span sz = span3(a->z, 1, 0, B, a->z_batch_stride, Dm, esz);
-  const Span sB = span3(a->B, 1, 0, B, a->B_batch_stride, N, esz);
-  const Span sC = span3(a->C, 1, 0, B, a->C_batch_stride, N, esz);
+  const int64_t G = groups_of(a->ngroups);
+  const Span sB = span3(a->B, B, a->B_batch_stride, G, a->B_group_stride, N, esz);
+  const Span sC = span3(a->C, B, a->C_batch_stride, G, a->C_group_stride, N, esz);
   const Span sA = span3(a->A, 1, 0, Dm, a->A_dim_stride, N, 4);
   const Span sD = span1(a->D, Dm, 4), sbias = span1(a->dt_bias, Dm, 4);
   const Span sout = span3(a->out, 1, 0, B, a->out_batch_stride, Dm, esz);

@@ -8,15 +8,17 @@
 //   s[n]  = exp(Delta A[d,n]) s[n] + Delta B[b,n] x        (in place)
 //   out   = (sum_n C[b,n] s[n] + D[d] x) * silu(z)
 //
-// The step is bound by memory traffic on the state (read + write 128 B per
-// channel).  Four consecutive lanes share one channel and own four states
-// each, so every state access of a wavefront is one contiguous 1 KiB run
-// (one lane per channel with 64 B per lane measured ~35% slower on gfx950).
-// The grid is (blocks of 64 channels, batch rows): no thread divides to find
-// its (batch, channel).  Aligned layouts (the usual contiguous ones) take a
-// branch-free instantiation with one 16-byte access per lane; others take the
-// element-wise one.  The readout is reduced over the quad with two DPP quad
-// permutations.
+// The step is bound by memory traffic on the state (read + write 8N bytes per
+// channel).  Four consecutive lanes share one channel and own R = N/4
+// consecutive states each (R rounded up to 1, 2, 4, 8 or 16 for N up to 64),
+// so every state access of a wavefront is one contiguous run (one lane per
+// channel with 64 B per lane measured ~35% slower on gfx950).  The grid is
+// (blocks of 64 channels, batch rows): no thread divides to find its (batch,
+// channel).  Aligned layouts with N = 4R (the usual contiguous ones) take a
+// branch-free instantiation with vector accesses; others take the
+// element-wise one, masked to the N real states.  The readout is reduced
+// over the quad with two DPP quad permutations.  B and C are those of the
+// channel's group (one group: shared by every channel of the batch row).
 #include "ssm_internal.h"
 
 namespace ssm {
@@ -37,8 +39,9 @@ struct UpdateParams {
   const float* D;
   const float* bias;
   void* out;
-  int64_t ssb, ssd, xsb, dtsb, zsb, Bsb, Csb, Asd, osb;
-  int64_t batch, dim;
+  int64_t ssb, ssd, xsb, dtsb, zsb, Bsb, Bsg, Csb, Csg, Asd, osb;
+  int64_t batch, dim, cpg;
+  int N;
   int softplus;
   // fused conv branch: [batch][dim][K] state shifted in place, [dim][K]
   // weights, [dim] bias (or NULL)
@@ -49,38 +52,64 @@ struct UpdateParams {
   int conv_silu;
 };
 
-template <typename T> struct Vec4;
-template <> struct Vec4<float> {
-  __device__ static __forceinline__ void load(const float* p, float (&v)[4]) {
-    const float4 q = *reinterpret_cast<const float4*>(p);
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-  }
-};
-template <> struct Vec4<uint16_t> {
-  __device__ static __forceinline__ void load(const uint16_t* p, float (&v)[4]) {
-    const uint2 q = *reinterpret_cast<const uint2*>(p);
-    v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
-    v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
-  }
-};
-
-template <typename T, bool VEC>
-__device__ __forceinline__ void load4(const T* p, float (&v)[4]) {
-  if constexpr (VEC) {
-    Vec4<T>::load(p, v);
+// R consecutive values from p as fp32: vector accesses (VEC: all R real and
+// aligned to min(R, 4) elements) or element-wise ones masked to the first
+// nvalid.
+template <typename T, bool VEC, int R>
+__device__ __forceinline__ void loadR(const T* p, float (&v)[R], int nvalid) {
+  if constexpr (VEC && R >= 4) {
+#pragma unroll
+    for (int c = 0; c < R / 4; ++c) {
+      if constexpr (sizeof(T) == 4) {
+        const float4 q = reinterpret_cast<const float4*>(p)[c];
+        v[4 * c] = q.x; v[4 * c + 1] = q.y; v[4 * c + 2] = q.z; v[4 * c + 3] = q.w;
+      } else {
+        const uint2 q = reinterpret_cast<const uint2*>(p)[c];
+        v[4 * c] = __uint_as_float(q.x << 16); v[4 * c + 1] = __uint_as_float(q.x & 0xffff0000u);
+        v[4 * c + 2] = __uint_as_float(q.y << 16); v[4 * c + 3] = __uint_as_float(q.y & 0xffff0000u);
+      }
+    }
+  } else if constexpr (VEC && R == 2) {
+    if constexpr (sizeof(T) == 4) {
+      const float2 q = *reinterpret_cast<const float2*>(p);
+      v[0] = q.x; v[1] = q.y;
+    } else {
+      const uint32_t q = *reinterpret_cast<const uint32_t*>(p);
+      v[0] = __uint_as_float(q << 16); v[1] = __uint_as_float(q & 0xffff0000u);
+    }
+  } else if constexpr (VEC) {
+    v[0] = io<T>::load(p);
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = io<T>::load(p + i);
+    for (int i = 0; i < R; ++i) v[i] = i < nvalid ? io<T>::load(p + i) : 0.0f;
   }
 }
 
-// VEC: state rows, A rows and B/C quads are aligned for one vector access each.
+template <bool VEC, int R>
+__device__ __forceinline__ void storeR(float* p, const float (&v)[R], int nvalid) {
+  if constexpr (VEC && R >= 4) {
+#pragma unroll
+    for (int c = 0; c < R / 4; ++c)
+      reinterpret_cast<float4*>(p)[c] = make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+  } else if constexpr (VEC && R == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  } else if constexpr (VEC) {
+    *p = v[0];
+  } else {
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      if (i < nvalid) p[i] = v[i];
+  }
+}
+
+// VEC: N == 4R and state rows, A rows and B/C rows are aligned for vector
+// accesses.
 // CONV: x is the conv input.  CONV == 1 (width <= 4): lane q of the channel's
 // quad holds conv state element q, takes element q+1 from its neighbour by a
 // DPP quad permute (the newest, x, at q = K-1), and the quad sums the four
 // weighted taps.  CONV == 2 (width 5..8): every lane of the quad forms the
 // whole sum and lane q writes back the elements k = q, q + 4.
-template <typename T, bool VEC, int CONV>
+template <typename T, bool VEC, int CONV, int R>
 __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p) {
   const int q = threadIdx.x & 3;
   const int64_t b = blockIdx.y;
@@ -88,12 +117,16 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p) 
   const bool ok = d0 < p.dim;
   const int64_t d = ok ? d0 : p.dim - 1;   // clamped: loads stay in bounds
 
-  float* sp = p.state + b * p.ssb + d * p.ssd + 4 * q;
-  float s[4], a[4], bb[4], cc[4];
-  load4<float, VEC>(sp, s);
-  load4<float, VEC>(p.A + d * p.Asd + 4 * q, a);
-  load4<T, VEC>(static_cast<const T*>(p.B) + b * p.Bsb + 4 * q, bb);
-  load4<T, VEC>(static_cast<const T*>(p.C) + b * p.Csb + 4 * q, cc);
+  const int nv = min(R, max(0, p.N - R * q));   // real states of this lane
+  // B/C group of the channel (a uniform branch: no division with one group)
+  int64_t g = 0;
+  if (p.cpg != p.dim) g = d / p.cpg;
+  float* sp = p.state + b * p.ssb + d * p.ssd + R * q;
+  float s[R], a[R], bb[R], cc[R];
+  loadR<float, VEC, R>(sp, s, nv);
+  loadR<float, VEC, R>(p.A + d * p.Asd + R * q, a, nv);
+  loadR<T, VEC, R>(static_cast<const T*>(p.B) + b * p.Bsb + g * p.Bsg + R * q, bb, nv);
+  loadR<T, VEC, R>(static_cast<const T*>(p.C) + b * p.Csb + g * p.Csg + R * q, cc, nv);
   float xv = io<T>::load(static_cast<const T*>(p.x) + b * p.xsb + d);
   if constexpr (CONV == 1) {
     // causal conv of the block's conv branch: shift in x, then the weighted
@@ -140,19 +173,12 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p) 
   const float dlx = dl * xv;
   float y = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < R; ++i) {
     const float e = __builtin_amdgcn_exp2f(dl * (a[i] * kLog2e));
     s[i] = fmaf(e, s[i], dlx * bb[i]);
-    y = fmaf(cc[i], s[i], y);
+    y = fmaf(cc[i], s[i], y);   // padding states are 0 with C = 0
   }
-  if (ok) {
-    if constexpr (VEC) {
-      *reinterpret_cast<float4*>(sp) = make_float4(s[0], s[1], s[2], s[3]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sp[i] = s[i];
-    }
-  }
+  if (ok) storeR<VEC, R>(sp, s, nv);
   // quad sum: lanes (0,1,2,3) <- (1,0,3,2), then <- (2,3,0,1)
   y += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xf, 0xf, true));
   y += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0x4E, 0xf, 0xf, true));
@@ -163,17 +189,29 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p) 
   }
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, int R>
 void launch_v(int conv, dim3 grid, dim3 block, const UpdateParams& p, hipStream_t stream) {
-  if (conv == 0) state_update_kernel<T, VEC, 0><<<grid, block, 0, stream>>>(p);
-  else if (conv == 1) state_update_kernel<T, VEC, 1><<<grid, block, 0, stream>>>(p);
-  else state_update_kernel<T, VEC, 2><<<grid, block, 0, stream>>>(p);
+  if (conv == 0) state_update_kernel<T, VEC, 0, R><<<grid, block, 0, stream>>>(p);
+  else if (conv == 1) state_update_kernel<T, VEC, 1, R><<<grid, block, 0, stream>>>(p);
+  else state_update_kernel<T, VEC, 2, R><<<grid, block, 0, stream>>>(p);
+}
+
+template <typename T, int R>
+void launch_r(bool vec, int conv, dim3 grid, dim3 block, const UpdateParams& p, hipStream_t stream) {
+  if (vec) launch_v<T, true, R>(conv, grid, block, p, stream);
+  else launch_v<T, false, R>(conv, grid, block, p, stream);
 }
 
 template <typename T>
-void launch_t(bool vec, int conv, dim3 grid, dim3 block, const UpdateParams& p, hipStream_t stream) {
-  if (vec) launch_v<T, true>(conv, grid, block, p, stream);
-  else launch_v<T, false>(conv, grid, block, p, stream);
+void launch_t(int r, bool vec, int conv, dim3 grid, dim3 block, const UpdateParams& p,
+              hipStream_t stream) {
+  switch (r) {
+    case 1: launch_r<T, 1>(vec, conv, grid, block, p, stream); break;
+    case 2: launch_r<T, 2>(vec, conv, grid, block, p, stream); break;
+    case 4: launch_r<T, 4>(vec, conv, grid, block, p, stream); break;
+    case 8: launch_r<T, 8>(vec, conv, grid, block, p, stream); break;
+    default: launch_r<T, 16>(vec, conv, grid, block, p, stream); break;
+  }
 }
 
 }  // namespace
@@ -187,14 +225,24 @@ hipError_t launch_state_update(const ssm_update_args& a, hipStream_t stream) {
   p.Bsb = a.B_batch_stride; p.Csb = a.C_batch_stride; p.Asd = a.A_dim_stride;
   p.osb = a.out_batch_stride;
   p.batch = a.batch; p.dim = a.dim;
+  const int64_t G = a.ngroups > 1 ? a.ngroups : 1;
+  p.cpg = a.dim / G;
+  p.Bsg = G > 1 ? a.B_group_stride : 0;
+  p.Csg = G > 1 ? a.C_group_stride : 0;
+  p.N = static_cast<int>(a.dstate);
   p.softplus = a.dt_softplus ? 1 : 0;
+  // states per lane: N / 4 rounded up to a power of two
+  int r = 1;
+  while (4 * r < a.dstate) r *= 2;
   const int esz = a.io_dtype == SSM_BF16 ? 2 : 4;
-  const bool vec = (reinterpret_cast<uintptr_t>(a.state) % 16 == 0) &&
-                   (a.state_batch_stride % 4 == 0) && (a.state_dim_stride % 4 == 0) &&
-                   (reinterpret_cast<uintptr_t>(a.A) % 16 == 0) && (a.A_dim_stride % 4 == 0) &&
-                   (reinterpret_cast<uintptr_t>(a.B) % (4 * esz) == 0) &&
-                   (reinterpret_cast<uintptr_t>(a.C) % (4 * esz) == 0) &&
-                   (a.B_batch_stride % 4 == 0) && (a.C_batch_stride % 4 == 0);
+  const int64_t w = r < 4 ? r : 4;   // elements per vector access
+  auto al = [&](const void* ptr, int64_t bytes) {
+    return reinterpret_cast<uintptr_t>(ptr) % static_cast<uintptr_t>(bytes) == 0;
+  };
+  const bool vec = a.dstate == 4 * r && al(a.state, 4 * w) && a.state_batch_stride % w == 0 &&
+                   a.state_dim_stride % w == 0 && al(a.A, 4 * w) && a.A_dim_stride % w == 0 &&
+                   al(a.B, esz * w) && al(a.C, esz * w) && a.B_batch_stride % w == 0 &&
+                   a.C_batch_stride % w == 0 && p.Bsg % w == 0 && p.Csg % w == 0;
   p.conv_state = a.conv_weight ? a.conv_state : nullptr;
   p.conv_w = a.conv_weight; p.conv_b = a.conv_bias;
   p.K = a.conv_weight ? a.d_conv : 0;
@@ -204,8 +252,8 @@ hipError_t launch_state_update(const ssm_update_args& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(xblocks), static_cast<unsigned>(a.batch));
   const dim3 block(kThreads);
   const int conv = a.conv_weight == nullptr ? 0 : (a.d_conv <= 4 ? 1 : 2);
-  if (a.io_dtype == SSM_BF16) launch_t<uint16_t>(vec, conv, grid, block, p, stream);
-  else launch_t<float>(vec, conv, grid, block, p, stream);
+  if (a.io_dtype == SSM_BF16) launch_t<uint16_t>(r, vec, conv, grid, block, p, stream);
+  else launch_t<float>(r, vec, conv, grid, block, p, stream);
   return hipGetLastError();
 }
 

@@ -102,15 +102,17 @@ def channel_params(dim: int, dstate: int, rng: np.random.Generator):
 
 
 def scan_inputs(batch: int, dim: int, seqlen: int, dstate: int = DSTATE,
-                io_dtype: str = "f32", seed: int = 0) -> dict:
+                io_dtype: str = "f32", seed: int = 0, ngroups: int = 0) -> dict:
     """Host (numpy) inputs for one prefill scan; IO tensors are fp32 arrays
-    whose values are exact in io_dtype."""
+    whose values are exact in io_dtype.  B and C are (batch, dstate, L), or
+    (batch, ngroups, dstate, L) when ngroups >= 1."""
     rng = np.random.default_rng(seed)
     u = rng.standard_normal((batch, dim, seqlen), dtype=np.float32)
     z = rng.standard_normal((batch, dim, seqlen), dtype=np.float32)
     dt = np.float32(0.1) * rng.standard_normal((batch, dim, seqlen), dtype=np.float32)
-    B = rng.standard_normal((batch, dstate, seqlen), dtype=np.float32)
-    C = rng.standard_normal((batch, dstate, seqlen), dtype=np.float32)
+    bc = (batch, ngroups, dstate, seqlen) if ngroups else (batch, dstate, seqlen)
+    B = rng.standard_normal(bc, dtype=np.float32)
+    C = rng.standard_normal(bc, dtype=np.float32)
     A, D, bias = channel_params(dim, dstate, rng)
     return dict(u=_to_io(u, io_dtype), z=_to_io(z, io_dtype), delta=_to_io(dt, io_dtype),
                 B=_to_io(B, io_dtype), C=_to_io(C, io_dtype), A=A, D=D, delta_bias=bias,
@@ -212,17 +214,20 @@ def decode_inputs_device(cfg: DecodeConfig, steps: int | None = None, device="cu
 
 
 def decode_inputs_host(batch: int, dim: int, dstate: int = DSTATE, io_dtype: str = "bf16",
-                       steps: int = 1, seed: int = 0, random_state: bool = False) -> dict:
+                       steps: int = 1, seed: int = 0, random_state: bool = False,
+                       ngroups: int = 0) -> dict:
     """Small host-drawn decode inputs (numpy), for parity tests.
 
-    x, dt, z: (steps, batch, dim); B, C: (steps, batch, dstate).  With
-    random_state the initial state is N(0, 1), else zero."""
+    x, dt, z: (steps, batch, dim); B, C: (steps, batch, dstate), or (steps,
+    batch, ngroups, dstate) when ngroups >= 1.  With random_state the initial
+    state is N(0, 1), else zero."""
     rng = np.random.default_rng(seed)
     x = rng.standard_normal((steps, batch, dim), dtype=np.float32)
     z = rng.standard_normal((steps, batch, dim), dtype=np.float32)
     dt = np.float32(0.1) * rng.standard_normal((steps, batch, dim), dtype=np.float32)
-    B = rng.standard_normal((steps, batch, dstate), dtype=np.float32)
-    C = rng.standard_normal((steps, batch, dstate), dtype=np.float32)
+    bc = (steps, batch, ngroups, dstate) if ngroups else (steps, batch, dstate)
+    B = rng.standard_normal(bc, dtype=np.float32)
+    C = rng.standard_normal(bc, dtype=np.float32)
     A, D, bias = channel_params(dim, dstate, rng)
     state = (rng.standard_normal((batch, dim, dstate), dtype=np.float32) if random_state
              else np.zeros((batch, dim, dstate), dtype=np.float32))

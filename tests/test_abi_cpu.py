@@ -36,12 +36,12 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_struct_layout():
     L = ssm.lib()
-    assert L.ssm_abi_version() == ssm.SSM_ABI_VERSION == 3
+    assert L.ssm_abi_version() == ssm.SSM_ABI_VERSION == 4
     assert L.ssm_scan_args_size() == ctypes.sizeof(ssm.ScanArgs)
     assert L.ssm_scan_bwd_args_size() == ctypes.sizeof(ssm.ScanBwdArgs)
     assert L.ssm_update_args_size() == ctypes.sizeof(ssm.UpdateArgs)
     header = open(HEADER).read()
-    assert "#define SSM_ABI_VERSION 3" in header
+    assert "#define SSM_ABI_VERSION 4" in header
     assert f"#define SSM_MAX_CONV {ssm.MAX_CONV}" in header
     assert f"#define SSM_CHECKPOINT_TOKENS {ssm.CHECKPOINT_TOKENS}" in header
 
@@ -124,7 +124,8 @@ def test_scan_optional_pointers(field):
 
 @pytest.mark.parametrize("field,value,code", [
     ("batch", -1, SHAPE), ("dim", -3, SHAPE), ("seqlen", -1, SHAPE), ("dstate", 0, SHAPE),
-    ("dstate", 8, UNSUP), ("dstate", 32, UNSUP), ("io_dtype", 2, DTYPE), ("io_dtype", -1, DTYPE),
+    ("dstate", 65, UNSUP), ("dstate", 128, UNSUP), ("io_dtype", 2, DTYPE), ("io_dtype", -1, DTYPE),
+    ("ngroups", 3, SHAPE), ("ngroups", -1, SHAPE), ("ngroups", 64, SHAPE),
     ("u_dim_stride", -1, STRIDE), ("B_state_stride", -64, STRIDE), ("out_batch_stride", -1, STRIDE),
     ("A_state_stride", -1, STRIDE),
 ])
@@ -136,11 +137,13 @@ def test_scan_bad_fields(field, value, code):
 
 def test_scan_window_limits():
     """The kernel reads 4 channel rows (u/delta/z/out) and 16 state rows (B/C)
-    through 32-bit byte windows; spans past 2^32 bytes are unsupported."""
+    through 32-bit byte windows; spans within 256 bytes of 2^32 or past it
+    are unsupported."""
     L = 64
     for field, rows in (("u_dim_stride", 3), ("delta_dim_stride", 3), ("z_dim_stride", 3),
                         ("out_dim_stride", 3), ("B_state_stride", 15), ("C_state_stride", 15)):
-        limit = ((1 << 32) // 4 - L) // rows        # largest stride whose span fits (fp32)
+        # largest stride whose span fits (fp32; windows stay 256 bytes short of 4 GiB)
+        limit = (((1 << 32) - 256) // 4 - L) // rows
         a = good_scan(L=L)
         setattr(a, field, limit + 1)
         assert ssm.validate_scan(a) == UNSUP, field
@@ -219,7 +222,8 @@ def test_update_required_pointers(field):
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("batch", -1, SHAPE), ("dim", -1, SHAPE), ("dstate", 0, SHAPE), ("dstate", 64, UNSUP),
+    ("batch", -1, SHAPE), ("dim", -1, SHAPE), ("dstate", 0, SHAPE), ("dstate", 65, UNSUP),
+    ("ngroups", 5, SHAPE), ("ngroups", -2, SHAPE),
     ("io_dtype", 7, DTYPE), ("state_dim_stride", -16, STRIDE), ("x_batch_stride", -1, STRIDE),
 ])
 def test_update_bad_fields(field, value, code):
@@ -300,7 +304,8 @@ def test_bwd_optional_pointers(field):
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("dstate", 8, UNSUP), ("io_dtype", 3, DTYPE), ("seqlen", -2, SHAPE),
+    ("dstate", 8, UNSUP), ("dstate", 32, UNSUP), ("io_dtype", 3, DTYPE), ("seqlen", -2, SHAPE),
+    ("ngroups", 3, SHAPE), ("ngroups", 4, UNSUP), ("ngroups", 32, UNSUP),
     ("dout_dim_stride", -1, STRIDE), ("du_batch_stride", -1, STRIDE),
 ])
 def test_bwd_bad_fields(field, value, code):
@@ -355,3 +360,87 @@ def test_conv_fields_validated():
     assert ssm.validate_update(u) == OK
     u.conv_state = u.state
     assert ssm.validate_update(u) == ALIAS
+
+
+def grouped_scan(G, N=16, dim=32, L=64, batch=2):
+    """A valid block with B/C as (batch, G, N, L), contiguous."""
+    a = good_scan(batch=batch, dim=dim, L=L, N=N)
+    for name in ("B", "C"):
+        setattr(a, f"{name}_batch_stride", G * N * L)
+        setattr(a, f"{name}_group_stride", N * L)
+        setattr(a, f"{name}_state_stride", L)
+    a.A_dim_stride = N
+    a.ngroups = G
+    return a
+
+
+@pytest.mark.parametrize("N", [1, 8, 16, 33, 64])
+@pytest.mark.parametrize("G", [0, 1, 2, 8, 32])
+def test_scan_any_dstate_and_groups_pass(N, G):
+    assert ssm.validate_scan(grouped_scan(G, N)) == OK
+
+
+def test_scan_group_stride_validated():
+    a = grouped_scan(4)
+    a.B_group_stride = -1
+    assert ssm.validate_scan(a) == STRIDE
+    # with one group the group stride is never read
+    a = grouped_scan(1)
+    a.B_group_stride = -1
+    assert ssm.validate_scan(a) == OK
+
+
+def test_scan_grouped_b_overlapping_output_is_an_alias():
+    a = grouped_scan(4)
+    a.out = a.B + 3 * 16 * 64 * 4          # inside group 3 of batch row 0
+    assert ssm.validate_scan(a) == ALIAS
+
+
+def test_scan_lane_mode_window_counts_group_stride():
+    """With groups smaller than 16 channels a wavefront's window spans up to
+    four groups: 3 * group_stride + (dstate - 1) * state_stride + L elements."""
+    L, N = 64, 16
+    limit = (((1 << 32) - 256) // 4 - L - (N - 1) * L) // 3
+    a = grouped_scan(32, N=N, L=L)           # one channel per group: lane mode
+    a.B_group_stride = limit + 1
+    a.B_batch_stride = 0
+    assert ssm.validate_scan(a) == UNSUP
+    a.B_group_stride = limit - 1
+    assert ssm.validate_scan(a) != UNSUP
+    # groups of 16 channels read one group per workgroup: the stride is free
+    # (the huge stride makes B's span cover the other fake tensors: not UNSUP,
+    # but an alias)
+    a = grouped_scan(2, N=N, L=L)
+    a.B_group_stride = limit + 1
+    a.B_batch_stride = 0
+    assert ssm.validate_scan(a) == ALIAS
+
+
+def test_workspace_grows_with_dstate():
+    a = grouped_scan(1, N=16, dim=16, L=1 << 20, batch=1)
+    b = grouped_scan(1, N=64, dim=16, L=1 << 20, batch=1)
+    ws16, ws64 = ssm.scan_workspace_size(a), ssm.scan_workspace_size(b)
+    assert ws16 > 0 and ws64 * 17 == ws16 * 65
+
+
+def test_update_any_dstate_and_groups_pass():
+    for N in (1, 5, 8, 16, 32, 64):
+        for G in (0, 1, 4, 64):
+            a = good_update(N=N)
+            a.A_dim_stride = N
+            a.B_batch_stride = a.C_batch_stride = max(G, 1) * N
+            a.ngroups = G
+            if G > 1:
+                a.B_group_stride = a.C_group_stride = N
+            assert ssm.validate_update(a) == OK, (N, G)
+
+
+def test_bwd_groups_of_sixteen_channels_pass():
+    a = good_bwd()
+    for name in ("B", "C"):
+        setattr(a, f"{name}_batch_stride", 2 * 16 * 64)
+        setattr(a, f"{name}_group_stride", 16 * 64)
+    a.ngroups = 2                         # 32 channels: two groups of 16
+    assert ssm.validate_scan_bwd(a) == OK
+    a.dC = a.dB + 2 * 2 * 16 * 64 * 4 - 4  # dB is (batch, 2, 16, L): overlap by one float
+    assert ssm.validate_scan_bwd(a) == ALIAS

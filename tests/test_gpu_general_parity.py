@@ -1,0 +1,240 @@
+"""GPU parity of the generalised Mamba-1 path (through the C ABI) against the
+fp64 oracle: state sizes over the pages' range (Mamba training/inference
+guide, parameter table: d_state 8 to 64), B/C in groups of channels (one
+group shared by every channel, groups of 16+ channels read per workgroup,
+smaller groups down to one per channel read per lane), and A of either sign.
+Bars as in tests/parity.py: row-normwise max relative error 1e-4 (fp32 IO),
+2e-2 (bf16 IO)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth_inputs as si
+from parity import TOL, gpu_scan, oracle_scan, row_rel_err, to_np
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU machines only to be skipped
+    pytest.skip("no GPU", allow_module_level=True)
+
+import selective_state_space_74_amd as ssm  # noqa: E402
+
+DEV = "cuda"
+
+
+def state_err(got, ref):
+    """last_state error: rows over n (a channel's state vector) from 16
+    states up; with fewer, rows over the batch row's whole state, since a row
+    of one or a few values makes the measure elementwise, ill-posed where a
+    state sums to near zero."""
+    got, ref = np.asarray(got), np.asarray(ref)
+    if ref.shape[-1] < 16:
+        got, ref = got.reshape(got.shape[0], -1), ref.reshape(ref.shape[0], -1)
+    return row_rel_err(got, ref)
+
+
+def check(inp, io, label, h0=None, twin=True):
+    out, last = gpu_scan(inp, h0=h0)
+    ref, rlast = oracle_scan(inp, h0=h0)
+    e_out, e_last = row_rel_err(to_np(out), ref), state_err(to_np(last), rlast)
+    msg = f"[{label}] err_out={e_out:.3e} err_last={e_last:.3e}"
+    if twin:
+        out2, _ = gpu_scan(inp, D=False, z=False, h0=h0)
+        ref2, _ = oracle_scan(inp, D=False, z=False, h0=h0)
+        e2 = row_rel_err(to_np(out2), ref2)
+        msg += f" err_ssm_only={e2:.3e}"
+    print(msg, flush=True)
+    assert e_out <= TOL[io] and e_last <= TOL[io]
+    if twin:
+        assert e2 <= TOL[io]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("G", [0, 3, 12, 48])
+@pytest.mark.parametrize("N", [1, 8, 24, 33, 64])
+def test_dstate_and_groups(N, G, io):
+    """dim 48: G = 3 keeps 16 channels per group (one group per workgroup);
+    G = 12 (4 channels) and G = 48 (one channel) read B/C per lane."""
+    inp = si.scan_inputs(2, 48, 300, dstate=N, io_dtype=io, seed=N * 100 + G, ngroups=G)
+    h0 = np.random.default_rng(N + G).standard_normal((2, 48, N)).astype(np.float32)
+    check(inp, io, f"N{N} G{G} {io}", h0=h0 if N in (8, 64) else None)
+
+
+@pytest.mark.parametrize("N,G", [(16, 0), (64, 2), (40, 20)])
+def test_A_of_either_sign(N, G):
+    """A drawn from [-1, 0.3]: growing modes too (bounded over 96 tokens)."""
+    inp = si.scan_inputs(2, 40, 96, dstate=N, seed=11 + N, ngroups=G)
+    inp["A"] = np.random.default_rng(N).uniform(-1.0, 0.3, inp["A"].shape).astype(np.float32)
+    check(inp, "f32", f"signed A N{N} G{G}")
+
+
+@pytest.mark.parametrize("N,G,io", [(64, 0, "bf16"), (32, 16, "f32"), (12, 4, "bf16")])
+def test_long_sequence_segmented(N, G, io):
+    """Few channels and a long sequence: cut into segments (two passes)."""
+    inp = si.scan_inputs(1, 16, 3 * 8192 + 77, dstate=N, io_dtype=io, seed=N + G, ngroups=G)
+    h0 = np.random.default_rng(5).standard_normal((1, 16, N)).astype(np.float32)
+    check(inp, io, f"segmented N{N} G{G} {io}", h0=h0, twin=False)
+
+
+def test_ragged_channels_lane_mode():
+    """dim 37 per-channel B/C (lane mode) with a partial last workgroup."""
+    inp = si.scan_inputs(2, 37, 131, dstate=20, seed=3, ngroups=37)
+    check(inp, "f32", "ragged lane mode")
+
+
+@pytest.mark.parametrize("N,G", [(40, 8), (64, 0)])
+def test_checkpoints_any_dstate(N, G):
+    batch, dim, L = 2, 32, 100
+    inp = si.scan_inputs(batch, dim, L, dstate=N, seed=N, ngroups=G)
+    h0 = np.random.default_rng(N).standard_normal((batch, dim, N)).astype(np.float32)
+    t = si.to_torch(inp, DEV)
+    ck = torch.empty(ssm.checkpoint_shape(batch, dim, L, N), dtype=torch.float32, device=DEV)
+    ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                           delta_bias=t["delta_bias"], h0=torch.from_numpy(h0).to(DEV),
+                           checkpoints=ck)
+    torch.cuda.synchronize()
+    ckn = to_np(ck)
+    assert np.array_equal(ckn[:, :, 0, :], h0.astype(np.float64))
+    for k in (1, 4, 6):
+        cut = {key: (np.ascontiguousarray(v[..., :16 * k]) if key in ("u", "delta", "z", "B", "C")
+                     else v) for key, v in inp.items()}
+        _, last = oracle_scan(cut, h0=h0)
+        e = state_err(ckn[:, :, k, :], last)
+        print(f"[checkpoint N{N} G{G} k{k}] err={e:.2e}", flush=True)
+        assert e <= 1e-4
+
+
+def test_grouped_equals_broadcast_one_group():
+    """Every group holding the same B/C gives the one-group result bit for bit
+    in shared mode (same kernel arithmetic, only the addressing differs)."""
+    inp = si.scan_inputs(2, 64, 200, seed=9)
+    g = dict(inp)
+    g["B"] = np.ascontiguousarray(np.repeat(inp["B"][:, None], 4, axis=1))
+    g["C"] = np.ascontiguousarray(np.repeat(inp["C"][:, None], 4, axis=1))
+    o1, l1 = gpu_scan(inp)
+    o4, l4 = gpu_scan(g)
+    assert torch.equal(o1, o4) and torch.equal(l1, l4)
+
+
+def test_conv_branch_with_large_state_and_lane_groups():
+    """The conv path on the S = 4 slot, lane-mode kernel (width 4 padded to 8)."""
+    batch, dim, L, N, K = 2, 24, 150, 64, 4
+    inp = si.scan_inputs(batch, dim, L, dstate=N, seed=17, ngroups=24)
+    rng = np.random.default_rng(17)
+    w = (rng.standard_normal((dim, K)) / 2).astype(np.float32)
+    cb = rng.standard_normal(dim).astype(np.float32)
+    t = si.to_torch(inp, DEV)
+    out, last = ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"],
+                                       z=t["z"], delta_bias=t["delta_bias"], return_last_state=True,
+                                       conv_weight=torch.from_numpy(w).to(DEV),
+                                       conv_bias=torch.from_numpy(cb).to(DEV))
+    torch.cuda.synchronize()
+    uc = oracle.causal_conv1d(inp["u"], w, cb)
+    ref, rlast = oracle.selective_scan(uc, inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"],
+                                       z=inp["z"], delta_bias=inp["delta_bias"],
+                                       return_last_state=True)
+    e, el = row_rel_err(to_np(out), ref), state_err(to_np(last), rlast)
+    print(f"[conv N64 lane] err_out={e:.2e} err_last={el:.2e}", flush=True)
+    assert e <= TOL["f32"] and el <= TOL["f32"]
+
+
+# ---------------------------------------------------------------------------- decode
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("G", [0, 4, 40])
+@pytest.mark.parametrize("N", [1, 5, 8, 16, 32, 64])
+def test_decode_dstate_and_groups(N, G, io):
+    d = si.decode_inputs_host(3, 40, dstate=N, io_dtype=io, seed=N + G, random_state=True,
+                              ngroups=G)
+    t = si.to_torch(d, DEV)
+    state = t["state"].clone()
+    out = ssm.selective_state_update(state, t["x"][0], t["dt"][0], t["A"], t["B"][0], t["C"][0],
+                                     D=t["D"], z=t["z"][0], dt_bias=t["dt_bias"])
+    torch.cuda.synchronize()
+    ref, rstate = oracle.state_update(d["state"], d["x"][0], d["dt"][0], d["A"], d["B"][0],
+                                      d["C"][0], D=d["D"], z=d["z"][0], dt_bias=d["dt_bias"])
+    e = row_rel_err(to_np(out)[None], ref[None])
+    es = state_err(to_np(state), rstate)
+    print(f"[decode N{N} G{G} {io}] err_out={e:.2e} err_state={es:.2e}", flush=True)
+    assert e <= TOL[io] and es <= TOL[io]
+
+
+def test_decode_padded_state_rows():
+    """State rows with a gap (state_dim_stride > dstate): the element-wise
+    instantiation; the gap is never written."""
+    N, batch, dim = 32, 2, 24
+    d = si.decode_inputs_host(batch, dim, dstate=N, io_dtype="f32", seed=4, random_state=True,
+                              ngroups=3)
+    t = si.to_torch(d, DEV)
+    big = torch.full((batch, dim, N + 3), 7.0, device=DEV)
+    big[..., :N] = t["state"]
+    view = big[..., :N]
+    out = ssm.selective_state_update(view, t["x"][0], t["dt"][0], t["A"], t["B"][0], t["C"][0],
+                                     D=t["D"], z=t["z"][0], dt_bias=t["dt_bias"])
+    torch.cuda.synchronize()
+    ref, rstate = oracle.state_update(d["state"], d["x"][0], d["dt"][0], d["A"], d["B"][0],
+                                      d["C"][0], D=d["D"], z=d["z"][0], dt_bias=d["dt_bias"])
+    assert row_rel_err(to_np(out)[None], ref[None]) <= 1e-4
+    assert state_err(to_np(view), rstate) <= 1e-4
+    assert torch.all(big[..., N:] == 7.0)
+
+
+def test_decode_steps_equal_scan_grouped():
+    N, G, batch, dim, L = 64, 4, 2, 32, 12
+    inp = si.scan_inputs(batch, dim, L, dstate=N, seed=23, ngroups=G)
+    t = si.to_torch(inp, DEV)
+    out, last = ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"],
+                                       z=t["z"], delta_bias=t["delta_bias"], return_last_state=True)
+    state = torch.zeros((batch, dim, N), device=DEV)
+    steps = []
+    for s in range(L):
+        steps.append(ssm.selective_state_update(
+            state, t["u"][..., s].contiguous(), t["delta"][..., s].contiguous(), t["A"],
+            t["B"][..., s].contiguous(), t["C"][..., s].contiguous(), D=t["D"],
+            z=t["z"][..., s].contiguous(), dt_bias=t["delta_bias"]))
+    torch.cuda.synchronize()
+    dec = torch.stack(steps, dim=-1)
+    e = row_rel_err(to_np(dec), to_np(out))
+    es = row_rel_err(to_np(state), to_np(last))
+    print(f"[decode==scan N64 G4] err={e:.2e} err_state={es:.2e}", flush=True)
+    assert e <= 1e-4 and es <= 1e-4
+
+
+# -------------------------------------------------------------------------- backward
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_backward_groups_of_sixteen(io):
+    batch, dim, L, G = 2, 64, 100, 4
+    inp = si.scan_inputs(batch, dim, L, io_dtype=io, seed=31, ngroups=G)
+    rng = np.random.default_rng(31)
+    dout = rng.standard_normal((batch, dim, L)).astype(np.float32)
+    if io == "bf16":
+        dout = si.bf16_round(dout)
+    t = si.to_torch(inp, DEV)
+    ck = torch.empty(ssm.checkpoint_shape(batch, dim, L), dtype=torch.float32, device=DEV)
+    kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"])
+    ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], checkpoints=ck, **kw)
+    g = ssm.selective_scan_bwd(torch.from_numpy(dout).to(DEV).to(t["u"].dtype), t["u"], t["delta"],
+                               t["A"], t["B"], t["C"], ck, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan_bwd(dout, inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                    D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"])
+    errs = {}
+    for k, r in ref.items():
+        got = to_np(g[k])
+        assert got.shape == r.shape, k
+        errs[k] = row_rel_err(got[None], r[None]) if k in ("dD", "ddelta_bias") else row_rel_err(got, r)
+    print("[bwd G4 " + io + "] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= TOL[io], (k, v)
+
+
+@pytest.mark.parametrize("N,G", [(32, 0), (16, 8)])
+def test_backward_unsupported_shapes_raise(N, G):
+    inp = si.scan_inputs(1, 64, 20, dstate=N, seed=1, ngroups=G)
+    t = si.to_torch(inp, DEV)
+    ck = torch.zeros(ssm.checkpoint_shape(1, 64, 20, N), dtype=torch.float32, device=DEV)
+    with pytest.raises(ssm.SSMError) as ei:
+        ssm.selective_scan_bwd(t["u"], t["u"], t["delta"], t["A"], t["B"], t["C"], ck)
+    assert ei.value.status == 7

@@ -205,8 +205,8 @@ def test_nan_propagates_within_its_row():
 
 def test_binding_raises_on_unsupported_state_size():
     u = torch.zeros((1, 16, 8), device=DEV)
-    A = -torch.ones((16, 8), device=DEV)
-    Bm = torch.zeros((1, 8, 8), device=DEV)
+    A = -torch.ones((16, 65), device=DEV)
+    Bm = torch.zeros((1, 65, 8), device=DEV)
     with pytest.raises(ssm.SSMError) as ei:
         ssm.selective_scan_fwd(u, u, A, Bm, Bm)
     assert ei.value.status == 7
