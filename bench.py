@@ -18,6 +18,7 @@ Prints ONE JSON line on stdout.  Progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -32,6 +33,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 METRIC = "selective-scan GB/s and channel·tokens/s (1 GPU); % of HBM roofline"
 SCAN_KERNEL_SRC = ["selective_state_space_74_amd/csrc/scan_fwd.hip",
+                   "selective_state_space_74_amd/csrc/scan_fwd_kernel.h",
+                   "selective_state_space_74_amd/csrc/scan_fwd_s1.hip",
                    "selective_state_space_74_amd/csrc/ssm_internal.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_fwd_mamba130m_f32_traffic.json")
 
@@ -40,10 +43,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def scan_bytes(batch, dim, L, N, esz, last_state=True, h0=False, gate=True):
+def scan_bytes(batch, dim, L, N, esz, last_state=True, h0=False, gate=True, ngroups=0):
     """Algorithmic bytes of one prefill scan."""
     io = batch * dim * L * esz * (3 + (1 if gate else 0))   # u, delta, out (+ z)
-    bc = 2 * batch * N * L * esz                            # B, C once per (batch, token)
+    bc = 2 * batch * max(ngroups, 1) * N * L * esz          # B, C once per (batch, group, token)
     params = dim * N * 4 + 2 * dim * 4                      # A, D, bias
     st = batch * dim * N * 4 * ((1 if last_state else 0) + (1 if h0 else 0))
     return io + bc + params + st
@@ -98,7 +101,7 @@ def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2, conv=0):
     dev = "cuda"
     sets = []
     for r in range(rotate):
-        if cfg.seqlen * cfg.dim * cfg.batch > 200_000_000:
+        if cfg.seqlen * cfg.batch * (cfg.dim + 2 * max(cfg.ngroups, 1) * cfg.dstate) > 200_000_000:
             t = si.scan_inputs_device(cfg, dev)
         else:
             t = si.to_torch(si.scan_inputs_for(cfg), dev)
@@ -134,7 +137,7 @@ def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2, conv=0):
     wall = time.perf_counter() - t0
     kern_ms, kern_min = timed_launches(step, max(10, min(steps, 200)), torch)
     esz = 2 if io == torch.bfloat16 else 4
-    nbytes = scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, esz)
+    nbytes = scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, esz, ngroups=cfg.ngroups)
     if conv:
         nbytes += cfg.dim * conv * 4 + cfg.dim * 4              # conv weights and bias
     ms_step = wall / steps * 1e3
@@ -347,6 +350,14 @@ def main():
         secondary[key] = bench_scan(c1, max(20, args.steps // 4), 5, torch, ssm, si, conv=4)
         log(f"[bench] {key} {secondary[key]['gbps']:.1f} GB/s, "
             f"kernel {secondary[key]['kernel_ms'] * 1e3:.1f} us")
+        # the generalised kernel: 64 states (four slots per lane), and B/C of
+        # its own per channel (lane mode)
+        for cg in (dataclasses.replace(c1, name=f"{c1.name}-dstate64", dstate=64),
+                   dataclasses.replace(c1, name=f"{c1.name}-bc-per-channel", ngroups=c1.dim)):
+            log(f"[bench] secondary {cg.name}")
+            secondary[cg.name] = bench_scan(cg, max(20, args.steps // 10), 5, torch, ssm, si)
+            log(f"[bench] {cg.name} {secondary[cg.name]['gbps']:.1f} GB/s, "
+                f"kernel {secondary[cg.name]['kernel_ms'] * 1e3:.1f} us")
         for cid in (1, 2):
             cb = si.SCAN_CONFIGS[cid]
             key = f"{cb.name}-backward"

@@ -42,6 +42,7 @@ class ScanConfig:
     io_dtype: str  # "f32" or "bf16"
     seed: int
     last_state: bool = True
+    ngroups: int = 0   # B/C groups: 0 = (batch, N, L), else (batch, ngroups, N, L)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -120,7 +121,8 @@ def scan_inputs(batch: int, dim: int, seqlen: int, dstate: int = DSTATE,
 
 
 def scan_inputs_for(cfg: ScanConfig) -> dict:
-    return scan_inputs(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, cfg.io_dtype, cfg.seed)
+    return scan_inputs(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, cfg.io_dtype, cfg.seed,
+                       cfg.ngroups)
 
 
 def torch_io_dtype(io_dtype: str):
@@ -173,8 +175,10 @@ def scan_inputs_device(cfg: ScanConfig, device="cuda", chunk: int = 1 << 22) -> 
     u = draw(shp)
     z = draw(shp)
     dt = draw(shp, 0.1)
-    B = draw((cfg.batch, cfg.dstate, cfg.seqlen))
-    C = draw((cfg.batch, cfg.dstate, cfg.seqlen))
+    bc = ((cfg.batch, cfg.ngroups, cfg.dstate, cfg.seqlen) if cfg.ngroups
+          else (cfg.batch, cfg.dstate, cfg.seqlen))
+    B = draw(bc)
+    C = draw(bc)
     rng = np.random.default_rng(cfg.seed)
     A, D, bias = channel_params(cfg.dim, cfg.dstate, rng)
     return dict(u=u, z=z, delta=dt, B=B, C=C, A=torch.from_numpy(A).to(device),
