@@ -54,6 +54,9 @@ def _load():
                                                  P, P, ctypes.c_int]
         lib.oracle_conv_state_update_f64.restype = ctypes.c_int
         lib.oracle_conv_state_update_f64.argtypes = [I64, I64, I64, P, P, P, P, ctypes.c_int, P]
+        lib.oracle_ssd_scan_f64.restype = ctypes.c_int
+        lib.oracle_ssd_scan_f64.argtypes = [I64] * 6 + [P] * 8 + [ctypes.c_int, P, P, P,
+                                                                  ctypes.c_int]
         lib.oracle_softplus.restype = ctypes.c_double
         lib.oracle_softplus.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
@@ -222,3 +225,27 @@ def conv_state_update(state, x, weight, bias=None, silu=True):
     lib.oracle_conv_state_update_f64(batch, dim, K, _ptr(s), _ptr(x), _ptr(weight), _ptr(bias),
                                      int(bool(silu)), _ptr(u))
     return u, s
+
+
+def ssd_scan(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True, h0=None,
+             return_last_state=False, nthreads=0):
+    """Mamba-2 SSM (SSD layer) in fp64, recurrent form.
+
+    x, z: (batch, L, H, P); dt: (batch, L, H); B, C: (batch, L, G, N) with
+    head h reading group h // (H // G); A, D, dt_bias: (H,); h0: (batch, H,
+    P, N).  Returns out (batch, L, H, P) and, with return_last_state, the
+    final state (batch, H, P, N)."""
+    lib = _load()
+    x, dt, z, B, C, A, D, dt_bias, h0 = map(_f64, (x, dt, z, B, C, A, D, dt_bias, h0))
+    batch, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt.shape == (batch, L, H) and (z is None or z.shape == x.shape)
+    assert B.shape == (batch, L, G, N) and C.shape == B.shape and H % G == 0
+    assert A.shape == (H,) and (h0 is None or h0.shape == (batch, H, P, N))
+    out = np.empty_like(x)
+    last = np.empty((batch, H, P, N)) if return_last_state else None
+    used = lib.oracle_ssd_scan_f64(batch, L, H, P, G, N, _ptr(x), _ptr(dt), _ptr(z), _ptr(B),
+                                   _ptr(C), _ptr(A), _ptr(D), _ptr(dt_bias), int(bool(dt_softplus)),
+                                   _ptr(h0), _ptr(out), _ptr(last), int(nthreads))
+    ssd_scan.last_threads = used
+    return (out, last) if return_last_state else out

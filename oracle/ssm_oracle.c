@@ -416,3 +416,82 @@ int oracle_conv_state_update_f64(int64_t batch, int64_t dim, int64_t K, double* 
   }
   return 1;
 }
+
+/* ------------------------------------------------------------------------ *
+ * Mamba-2 SSM (the SSD layer), recurrent form, in fp64.
+ *
+ * Mamba-2 is multi-head (Mamba-2 section of the mamba_ssm notes and the
+ * skill page's Mamba-2 configuration: headdim, ngroups): the inner width is
+ * H heads of P channels, and the block's printed parameter count (6,468,320
+ * for d_model 1024, d_state 64) has one A, one D and one step bias per head
+ * and 2 * ngroups * d_state B/C numbers per token.  So for batch b, head h,
+ * channel p of the head and state n, with g = h / (H / G) the head's group:
+ *   Delta_t   = softplus(dt[b,t,h] + bias[h])        (one step per head)
+ *   S_t[p,n]  = exp(Delta_t A[h]) S_{t-1}[p,n] + Delta_t B[b,t,g,n] x[b,t,h,p]
+ *   y[b,t,h,p]= sum_n C[b,t,g,n] S_t[p,n] + D[h] x[b,t,h,p],  times silu(z)
+ * starting from S_{-1} = h0[b,h] (or zero) and returning S_{L-1}.  The
+ * structured-matrix (attention-like) view the pages call state space
+ * duality is the same map written as y = M x; the pins check the two agree.
+ *
+ * Layouts (contiguous, row-major): x, z, out (batch, L, H, P); dt (batch,
+ * L, H); Bm, Cm (batch, L, G, N); A, Dv, bias (H); h0, last (batch, H, P, N).
+ * ------------------------------------------------------------------------ */
+static void ssd_head(int64_t b, int64_t h, int64_t L, int64_t H, int64_t P, int64_t G,
+                     int64_t N, const double* x, const double* dt, const double* z,
+                     const double* Bm, const double* Cm, const double* A, const double* Dv,
+                     const double* bias, int softplus, const double* h0, double* out,
+                     double* last, double* S) {
+  const int64_t g = h / (H / G);                      /* the head's B/C group */
+  for (int64_t i = 0; i < P * N; ++i) S[i] = h0 ? h0[(b * H + h) * P * N + i] : 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    const double step = step_size(dt[(b * L + t) * H + h], bias, h, softplus);
+    const double decay = exp(step * A[h]);            /* scalar decay per head */
+    const double* Bt = Bm + ((b * L + t) * G + g) * N;
+    const double* Ct = Cm + ((b * L + t) * G + g) * N;
+    for (int64_t p = 0; p < P; ++p) {
+      const int64_t xi = ((b * L + t) * H + h) * P + p;
+      const double xv = x[xi];
+      double y = 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        S[p * N + n] = decay * S[p * N + n] + step * Bt[n] * xv;
+        y += Ct[n] * S[p * N + n];
+      }
+      if (Dv) y += Dv[h] * xv;
+      if (z) y *= oracle_silu(z[xi]);
+      out[xi] = y;
+    }
+  }
+  if (last)
+    for (int64_t i = 0; i < P * N; ++i) last[(b * H + h) * P * N + i] = S[i];
+}
+
+int oracle_ssd_scan_f64(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t ngroups, int64_t dstate, const double* x, const double* dt,
+                        const double* z, const double* Bm, const double* Cm, const double* A,
+                        const double* Dv, const double* bias, int softplus, const double* h0,
+                        double* out, double* last, int nthreads) {
+  int used = 1;
+  const int64_t PN = headdim * dstate > 0 ? headdim * dstate : 1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+  {
+#pragma omp single
+    used = omp_get_num_threads();
+    double* S = (double*)malloc(sizeof(double) * (size_t)PN);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < batch * nheads; ++r)
+      ssd_head(r / nheads, r % nheads, seqlen, nheads, headdim, ngroups, dstate, x, dt, z, Bm,
+               Cm, A, Dv, bias, softplus, h0, out, last, S);
+    free(S);
+  }
+#else
+  (void)nthreads;
+  double* S = (double*)malloc(sizeof(double) * (size_t)PN);
+  for (int64_t r = 0; r < batch * nheads; ++r)
+    ssd_head(r / nheads, r % nheads, seqlen, nheads, headdim, ngroups, dstate, x, dt, z, Bm, Cm,
+             A, Dv, bias, softplus, h0, out, last, S);
+  free(S);
+#endif
+  return used;
+}

@@ -189,3 +189,45 @@ def test_group_pins_catch_planted_mistake(name, old, new, tmp_path):
     with oracle.use_library(str(lib)):
         caught = [i for i, fn in enumerate(GROUP_PINS) if _fails_call(fn)]
     assert caught, f"no pin caught mutant {name}"
+
+
+# Planted mistakes in the Mamba-2 (SSD layer) oracle, each to be caught by a
+# pin in test_oracle_ssd_pins.py.
+import test_oracle_ssd_pins as spins  # noqa: E402
+
+SSD_PINS = [
+    lambda: [spins.test_equals_mamba1_oracle_with_shared_head_parameters_bit_exact(*s)
+             for s in ((4, 3, 2, 5), (6, 1, 3, 8))],
+    lambda: [spins.test_structured_matrix_form(4, 3, 2, 5, 20, sp) for sp in (True, False)],
+    spins.test_single_token_closed_form,
+    spins.test_zero_input_decays_every_state_by_the_head_scalar,
+]
+
+SSD_MUTANTS = [
+    ("ssd-group-interleaved", "const int64_t g = h / (H / G);                      /* the head's B/C group */",
+     "const int64_t g = h % G;"),
+    ("ssd-step-of-another-head", "const double step = step_size(dt[(b * L + t) * H + h], bias, h, softplus);",
+     "const double step = step_size(dt[(b * L + t) * H + (h + 1) % H], bias, h, softplus);"),
+    ("ssd-drop-skip", "if (Dv) y += Dv[h] * xv;", ";"),
+    ("ssd-input-not-scaled-by-step", "S[p * N + n] = decay * S[p * N + n] + step * Bt[n] * xv;",
+     "S[p * N + n] = decay * S[p * N + n] + Bt[n] * xv;"),
+    ("ssd-ignore-h0", "S[i] = h0 ? h0[(b * H + h) * P * N + i] : 0.0;", "S[i] = 0.0;"),
+    ("ssd-readout-before-update",
+     "        S[p * N + n] = decay * S[p * N + n] + step * Bt[n] * xv;\n        y += Ct[n] * S[p * N + n];",
+     "        y += Ct[n] * S[p * N + n];\n        S[p * N + n] = decay * S[p * N + n] + step * Bt[n] * xv;"),
+    ("ssd-swap-B-C", "const double* Bt = Bm + ((b * L + t) * G + g) * N;",
+     "const double* Bt = Cm + ((b * L + t) * G + g) * N;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", SSD_MUTANTS, ids=[m[0] for m in SSD_MUTANTS])
+def test_ssd_pins_catch_planted_mistake(name, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    path = tmp_path / "mut.c"
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", str(lib), str(path), "-lm"])
+    with oracle.use_library(str(lib)):
+        caught = [i for i, fn in enumerate(SSD_PINS) if _fails_call(fn)]
+    assert caught, f"no pin caught mutant {name}"
