@@ -234,6 +234,55 @@ def bench_decode(cfg, torch, ssm, si, warmup=20, conv=0):
     return res
 
 
+def ssd_bytes(batch, L, H, P, G, N, esz, gate=True, last_state=True):
+    """Algorithmic bytes of one Mamba-2 SSM prefill: x, out (+ z) and dt read
+    or written once, B and C once per (batch, token, group), the per-head
+    parameters, and the final state."""
+    io = batch * L * H * P * esz * (2 + (1 if gate else 0))
+    dt = batch * L * H * esz
+    bc = 2 * batch * L * G * N * esz
+    params = 3 * H * 4
+    st = batch * H * P * N * 4 if last_state else 0
+    return io + dt + bc + params + st
+
+
+def bench_ssd(cfg, steps, torch, ssm, si):
+    """Times the Mamba-2 SSM prefill on device-drawn inputs (two input sets
+    in rotation)."""
+    sets = [si.ssd_inputs_device(cfg, "cuda")]
+    sets.append({k: v.clone() for k, v in sets[0].items()})
+    outs = [torch.empty_like(s["x"]) for s in sets]
+    lasts = [torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), device="cuda")
+             for _ in sets]
+
+    def step(i):
+        k = i % 2
+        s = sets[k]
+        ssm.ssd_scan_fwd(s["x"], s["dt"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
+                         dt_bias=s["dt_bias"], out=outs[k], last_state=lasts[k])
+
+    for i in range(5):
+        step(i)
+    torch.cuda.synchronize()
+    kern_ms, kern_min = timed_launches(step, steps, torch)
+    esz = 2 if cfg.io_dtype == "bf16" else 4
+    nbytes = ssd_bytes(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, esz)
+    # matrix-core work of the chunked form: per (batch, head, 64-token chunk),
+    # the causal half of the Q x Q scores (k = N), the intra-chunk product,
+    # the state product and the state update (k = Q), each 2 flops per MAC
+    Q = 64
+    chunks = cfg.batch * cfg.nheads * ((cfg.seqlen + Q - 1) // Q)
+    macs = chunks * (Q * (Q + 16) // 2 * cfg.dstate + Q * (Q + 16) // 2 * cfg.headdim
+                     + 2 * Q * cfg.dstate * cfg.headdim)
+    res = dict(kernel_ms=kern_ms, kernel_ms_min=kern_min, bytes=nbytes,
+               gbps=nbytes / (kern_ms * 1e-3) / 1e9, mfma_tflops=2 * macs / (kern_ms * 1e-3) / 1e12,
+               token_heads_per_s=cfg.batch * cfg.seqlen * cfg.nheads / (kern_ms * 1e-3))
+    res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBS
+    del sets, outs, lasts
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cfg, si, max_s=30.0):
     """The fp64 oracle, as it stands, on the host cores, over the headline
     workload (whole batch rows at full length).  It runs batch row 0 first and
@@ -358,6 +407,12 @@ def main():
             secondary[cg.name] = bench_scan(cg, max(20, args.steps // 10), 5, torch, ssm, si)
             log(f"[bench] {cg.name} {secondary[cg.name]['gbps']:.1f} GB/s, "
                 f"kernel {secondary[cg.name]['kernel_ms'] * 1e3:.1f} us")
+        cs = si.SSD_CONFIG
+        log(f"[bench] secondary {cs.name}")
+        secondary[cs.name] = bench_ssd(cs, 100, torch, ssm, si)
+        log(f"[bench] {cs.name} {secondary[cs.name]['gbps']:.1f} GB/s, "
+            f"{secondary[cs.name]['kernel_ms'] * 1e3:.1f} us, "
+            f"{secondary[cs.name]['mfma_tflops']:.1f} TFLOP/s on the matrix cores")
         for cid in (1, 2):
             cb = si.SCAN_CONFIGS[cid]
             key = f"{cb.name}-backward"

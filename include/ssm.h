@@ -1,7 +1,7 @@
 /*
  * ssm.h -- C ABI of libssm.so, the gfx950 (MI355X) selective-scan library.
  *
- * Three operations, all from the Mamba pages (cited by page title and section):
+ * Four operations, all from the Mamba pages (cited by page title and section):
  *
  *   ssm_selective_scan_fwd  -- prefill.  For every batch row b, channel d and
  *     state index n, with Delta_t = softplus(delta_t + bias[d]) (Mamba paper
@@ -23,6 +23,8 @@
  *     checkpointing, state passed at chunk edges), the forward keeps only one
  *     state per 16-token chunk and the backward recomputes the steps between.
  *
+ *   ssm_ssd_scan_fwd -- the Mamba-2 SSM (multi-head, scalar decay per head,
+ *     the SSD layer) prefill; see ssm_ssd_args.
  *   ssm_selective_state_update -- decode: the same recurrence for a single
  *     token, reading and writing a resident fp32 state (Mamba paper notes,
  *     section 4.3: inference keeps one fixed-size state and updates it once
@@ -55,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 
 /* Tokens between two state checkpoints (see ssm_scan_args.checkpoints). */
 #define SSM_CHECKPOINT_TOKENS 16
@@ -265,6 +267,60 @@ typedef struct ssm_update_args {
   int64_t B_group_stride, C_group_stride;
 } ssm_update_args;
 
+/* Arguments of the Mamba-2 SSM (the SSD layer) prefill.  The Mamba-2
+ * section of the mamba_ssm notes and the skill page's Mamba-2 configuration
+ * make the block multi-head (nheads heads of headdim channels, ngroups B/C
+ * groups), and its printed parameter count has one A, one D and one step bias
+ * per head.  For batch row b, head h (reading B/C group g = h / (nheads /
+ * ngroups)), head channel p and state n:
+ *     Delta_t  = softplus(dt[b,t,h] + dt_bias[h])      (identity without softplus)
+ *     S_t[p,n] = exp(Delta_t * A[h]) * S_{t-1}[p,n] + Delta_t * B[b,t,g,n] * x[b,t,h,p]
+ *     out[b,t,h,p] = (sum_n C[b,t,g,n] * S_t[p,n] + D[h] * x[b,t,h,p]) * silu(z[b,t,h,p])
+ * from S_{-1} = h0[b,h] (or zero), optionally returning S_{L-1}.  The kernel
+ * evaluates it in chunks of 64 tokens through the equivalent structured
+ * matrix form (state space duality) on the matrix cores.
+ *   x, z, out   : (batch, seqlen, nheads, headdim), headdim stride 1;
+ *                 element (b, t, h, p) at ptr[b * *_batch_stride +
+ *                 t * *_seq_stride + h * *_head_stride + p].
+ *   dt          : (batch, seqlen, nheads), head stride 1, io_dtype.
+ *   B, C        : (batch, seqlen, ngroups, dstate), state stride 1.
+ *   A, D, dt_bias : (nheads) fp32; D and dt_bias NULL mean 0.
+ *   h0, last_state : (batch, nheads, headdim, dstate) fp32, contiguous; h0
+ *                 NULL is a zero initial state, last_state NULL: not wanted.
+ *   z NULL      : no gate.
+ * Sizes: batch, seqlen >= 0 (zero is a no-op; seqlen 0 with last_state
+ * copies h0, or zeros); nheads, headdim, dstate >= 1; ngroups 0 or 1 (one
+ * group) or a divisor of nheads; seqlen below 2^31 - 64; dstate at most 128
+ * for bf16 IO and 64 for fp32 IO (SSM_ERR_UNSUPPORTED past that); batch *
+ * nheads * ceil(headdim / 16) below 2^31.  The kernel reaches 64 tokens of a
+ * (batch, head) slice of x, z, dt and out and of a (batch, group) slice of B
+ * and C through 31-bit byte windows: (63 * seq_stride + inner size) * element
+ * size must stay below 2^31 (inner size headdim, 1 for dt, dstate for B/C);
+ * larger strides return SSM_ERR_UNSUPPORTED.
+ * Precision: fp32 accumulation throughout and an fp32 state.  With bf16 IO the
+ * products run on bf16 operands, so the masked chunk scores, B weighted by
+ * the decays and the state entering each chunk are rounded to bf16 where
+ * they enter a product (the state itself stays fp32); with fp32 IO every
+ * product is fp32.
+ * Aliasing: out must not overlap any input; last_state must not overlap any
+ * input except that it may be exactly h0. */
+typedef struct ssm_ssd_args {
+  int64_t batch, seqlen, nheads, headdim, ngroups, dstate;
+  int32_t io_dtype;      /* ssm_dtype */
+  int32_t dt_softplus;   /* bool */
+  const void* x;   int64_t x_batch_stride, x_seq_stride, x_head_stride;
+  const void* dt;  int64_t dt_batch_stride, dt_seq_stride;
+  const void* z;   int64_t z_batch_stride, z_seq_stride, z_head_stride;
+  const void* B;   int64_t B_batch_stride, B_seq_stride, B_group_stride;
+  const void* C;   int64_t C_batch_stride, C_seq_stride, C_group_stride;
+  const float* A;
+  const float* D;
+  const float* dt_bias;
+  const float* h0;
+  float* last_state;
+  void* out;       int64_t out_batch_stride, out_seq_stride, out_head_stride;
+} ssm_ssd_args;
+
 /* ABI version of the loaded library (SSM_ABI_VERSION at build time). */
 int ssm_abi_version(void);
 
@@ -272,6 +328,7 @@ int ssm_abi_version(void);
 size_t ssm_scan_args_size(void);
 size_t ssm_scan_bwd_args_size(void);
 size_t ssm_update_args_size(void);
+size_t ssm_ssd_args_size(void);
 
 /* Workspace bytes the scan can use for this argument block (0 when it would
  * run single-segment anyway).  Reads only sizes; pure host code. */
@@ -285,6 +342,7 @@ const char* ssm_status_string(int status);
 int ssm_validate_scan(const ssm_scan_args* args);
 int ssm_validate_scan_bwd(const ssm_scan_bwd_args* args);
 int ssm_validate_update(const ssm_update_args* args);
+int ssm_validate_ssd(const ssm_ssd_args* args);
 
 /* Prefill scan (see ssm_scan_args).  Validates, then launches on `stream`. */
 int ssm_selective_scan_fwd(const ssm_scan_args* args, void* stream);
@@ -295,6 +353,10 @@ int ssm_selective_scan_bwd(const ssm_scan_bwd_args* args, void* stream);
 
 /* Decode update (see ssm_update_args).  Validates, then launches on `stream`. */
 int ssm_selective_state_update(const ssm_update_args* args, void* stream);
+
+/* Mamba-2 SSM prefill (see ssm_ssd_args).  Validates, then launches on
+ * `stream`. */
+int ssm_ssd_scan_fwd(const ssm_ssd_args* args, void* stream);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssm.so")
 
-SSM_ABI_VERSION = 4
+SSM_ABI_VERSION = 5
 CHECKPOINT_TOKENS = 16
 MAX_CONV = 8
 SSM_F32, SSM_BF16 = 0, 1
@@ -105,6 +105,21 @@ class UpdateArgs(ctypes.Structure):
                 ("ngroups", _I64), ("B_group_stride", _I64), ("C_group_stride", _I64)]
 
 
+class SsdArgs(ctypes.Structure):
+    """Mirror of ssm_ssd_args."""
+    _fields_ = [("batch", _I64), ("seqlen", _I64), ("nheads", _I64), ("headdim", _I64),
+                ("ngroups", _I64), ("dstate", _I64),
+                ("io_dtype", _I32), ("dt_softplus", _I32),
+                ("x", _P), ("x_batch_stride", _I64), ("x_seq_stride", _I64), ("x_head_stride", _I64),
+                ("dt", _P), ("dt_batch_stride", _I64), ("dt_seq_stride", _I64),
+                ("z", _P), ("z_batch_stride", _I64), ("z_seq_stride", _I64), ("z_head_stride", _I64),
+                ("B", _P), ("B_batch_stride", _I64), ("B_seq_stride", _I64), ("B_group_stride", _I64),
+                ("C", _P), ("C_batch_stride", _I64), ("C_seq_stride", _I64), ("C_group_stride", _I64),
+                ("A", _P), ("D", _P), ("dt_bias", _P), ("h0", _P), ("last_state", _P),
+                ("out", _P), ("out_batch_stride", _I64), ("out_seq_stride", _I64),
+                ("out_head_stride", _I64)]
+
+
 class SSMError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -126,10 +141,11 @@ def lib():
         L.ssm_scan_args_size.restype = ctypes.c_size_t
         L.ssm_scan_bwd_args_size.restype = ctypes.c_size_t
         L.ssm_update_args_size.restype = ctypes.c_size_t
+        L.ssm_ssd_args_size.restype = ctypes.c_size_t
         L.ssm_status_string.restype = ctypes.c_char_p
         L.ssm_status_string.argtypes = [ctypes.c_int]
         for name, T in (("ssm_validate_scan", ScanArgs), ("ssm_validate_update", UpdateArgs),
-                        ("ssm_validate_scan_bwd", ScanBwdArgs)):
+                        ("ssm_validate_scan_bwd", ScanBwdArgs), ("ssm_validate_ssd", SsdArgs)):
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.POINTER(T)]
@@ -141,11 +157,14 @@ def lib():
         L.ssm_selective_scan_bwd.argtypes = [ctypes.POINTER(ScanBwdArgs), _P]
         L.ssm_selective_state_update.restype = ctypes.c_int
         L.ssm_selective_state_update.argtypes = [ctypes.POINTER(UpdateArgs), _P]
+        L.ssm_ssd_scan_fwd.restype = ctypes.c_int
+        L.ssm_ssd_scan_fwd.argtypes = [ctypes.POINTER(SsdArgs), _P]
         if L.ssm_abi_version() != SSM_ABI_VERSION:
             raise ImportError(f"libssm.so ABI {L.ssm_abi_version()} != {SSM_ABI_VERSION}")
         if (L.ssm_scan_args_size() != ctypes.sizeof(ScanArgs)
                 or L.ssm_scan_bwd_args_size() != ctypes.sizeof(ScanBwdArgs)
-                or L.ssm_update_args_size() != ctypes.sizeof(UpdateArgs)):
+                or L.ssm_update_args_size() != ctypes.sizeof(UpdateArgs)
+                or L.ssm_ssd_args_size() != ctypes.sizeof(SsdArgs)):
             raise ImportError("libssm.so argument struct layout differs from the binding")
         _lib = L
     return _lib
@@ -173,6 +192,14 @@ def scan_workspace_size(args: ScanArgs) -> int:
 
 def scan_fwd_raw(args: ScanArgs, stream: int = 0) -> int:
     return lib().ssm_selective_scan_fwd(ctypes.byref(args), _P(stream or None))
+
+
+def validate_ssd(args: SsdArgs) -> int:
+    return lib().ssm_validate_ssd(ctypes.byref(args))
+
+
+def ssd_fwd_raw(args: SsdArgs, stream: int = 0) -> int:
+    return lib().ssm_ssd_scan_fwd(ctypes.byref(args), ctypes.c_void_p(stream))
 
 
 def scan_bwd_raw(args: ScanBwdArgs, stream: int = 0) -> int:
@@ -497,3 +524,61 @@ def selective_scan_bwd(dout, u, delta, A, B, C, checkpoints, D=None, z=None, del
     if st != 0:
         raise SSMError(st, "ssm_selective_scan_bwd")
     return g
+
+
+def ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True, h0=None,
+                 return_last_state=False, out=None, last_state=None, stream=None):
+    """Mamba-2 SSM (SSD layer) prefill on the GPU.
+
+    x, z: (batch, L, nheads, headdim) with headdim stride 1; dt: (batch, L,
+    nheads) with head stride 1 (IO dtype); B, C: (batch, L, ngroups, dstate)
+    with state stride 1; A, D, dt_bias: (nheads,) fp32; h0: (batch, nheads,
+    headdim, dstate) fp32.  Returns out (like x) or (out, last_state)."""
+    torch = _torch()
+    if x.dim() != 4:
+        raise ValueError("x must be (batch, L, nheads, headdim)")
+    batch, L, H, P = x.shape
+    dev, io = x.device, x.dtype
+    code = _io_code(x)
+    for name, t in (("dt", dt), ("z", z), ("B", B), ("C", C)):
+        _check_dev(name, t, dev, io)
+    for name, t in (("A", A), ("D", D), ("dt_bias", dt_bias), ("h0", h0),
+                    ("last_state", last_state)):
+        _check_dev(name, t, dev, torch.float32)
+    if B.dim() != 4 or tuple(B.shape) != tuple(C.shape) or tuple(B.shape[:2]) != (batch, L):
+        raise ValueError("B and C must be (batch, L, ngroups, dstate)")
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (batch, L, H) or (z is not None and tuple(z.shape) != tuple(x.shape)):
+        raise ValueError("dt must be (batch, L, nheads) and z shaped like x")
+    for name, t in (("x", x), ("z", z), ("dt", dt), ("B", B), ("C", C)):
+        if t is not None and t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError(f"{name} must have a unit innermost stride")
+    _contig_f32("A", A, (H,))
+    _contig_f32("D", D, (H,))
+    _contig_f32("dt_bias", dt_bias, (H,))
+    _contig_f32("h0", h0, (batch, H, P, N))
+    if out is None:
+        out = torch.empty_like(x)
+    _check_dev("out", out, dev, io)
+    if tuple(out.shape) != tuple(x.shape) or (P > 1 and out.stride(-1) != 1):
+        raise ValueError("out must be shaped like x with headdim stride 1")
+    if return_last_state and last_state is None:
+        last_state = torch.empty((batch, H, P, N), dtype=torch.float32, device=dev)
+    if last_state is not None:
+        _contig_f32("last_state", last_state, (batch, H, P, N))
+    a = SsdArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.ngroups, a.dstate = batch, L, H, P, G, N
+    a.io_dtype, a.dt_softplus = code, int(bool(dt_softplus))
+    a.x, (a.x_batch_stride, a.x_seq_stride, a.x_head_stride) = _ptr(x), x.stride()[:3]
+    a.dt, (a.dt_batch_stride, a.dt_seq_stride) = _ptr(dt), dt.stride()[:2]
+    if z is not None:
+        a.z, (a.z_batch_stride, a.z_seq_stride, a.z_head_stride) = _ptr(z), z.stride()[:3]
+    a.B, (a.B_batch_stride, a.B_seq_stride, a.B_group_stride) = _ptr(B), B.stride()[:3]
+    a.C, (a.C_batch_stride, a.C_seq_stride, a.C_group_stride) = _ptr(C), C.stride()[:3]
+    a.A, a.D, a.dt_bias, a.h0 = _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(h0)
+    a.last_state = _ptr(last_state)
+    a.out, (a.out_batch_stride, a.out_seq_stride, a.out_head_stride) = _ptr(out), out.stride()[:3]
+    st = ssd_fwd_raw(a, _stream(stream))
+    if st != 0:
+        raise SSMError(st, "ssm_ssd_scan_fwd")
+    return (out, last_state) if return_last_state else out

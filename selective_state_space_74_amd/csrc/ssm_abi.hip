@@ -63,6 +63,7 @@ int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 size_t ssm_scan_args_size(void) { return sizeof(ssm_scan_args); }
 size_t ssm_scan_bwd_args_size(void) { return sizeof(ssm_scan_bwd_args); }
 size_t ssm_update_args_size(void) { return sizeof(ssm_update_args); }
+size_t ssm_ssd_args_size(void) { return sizeof(ssm_ssd_args); }
 
 size_t ssm_scan_workspace_size(const ssm_scan_args* a) {
   if (!a || a->dstate < 1 || a->dstate > SSM_MAX_DSTATE || a->seqlen > kMaxSeqlen) return 0;
@@ -291,6 +292,68 @@ int ssm_validate_update(const ssm_update_args* a) {
   return SSM_OK;
 }
 
+int ssm_validate_ssd(const ssm_ssd_args* a) {
+  if (!a) return SSM_ERR_NULL;
+  if (a->batch < 0 || a->seqlen < 0 || a->nheads < 1 || a->headdim < 1 || a->dstate < 1 ||
+      a->ngroups < 0)
+    return SSM_ERR_SHAPE;
+  const int64_t G = groups_of(a->ngroups);
+  if (a->nheads % G != 0) return SSM_ERR_SHAPE;
+  if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
+  if (a->dstate > (a->io_dtype == SSM_BF16 ? 128 : 64)) return SSM_ERR_UNSUPPORTED;
+  if (a->seqlen > kMaxSeqlen) return SSM_ERR_UNSUPPORTED;
+  if (a->batch * a->nheads * ((a->headdim + 15) / 16) > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
+  if (a->batch == 0) return SSM_OK;
+  const int64_t Bt = a->batch, L = a->seqlen, H = a->nheads, P = a->headdim, N = a->dstate;
+  const int64_t esz = io_size(a->io_dtype);
+  if (!a->A) return SSM_ERR_NULL;
+  if (L > 0) {
+    if (!a->x || !a->dt || !a->B || !a->C || !a->out) return SSM_ERR_NULL;
+    const int64_t strides[] = {a->x_batch_stride, a->x_seq_stride, a->x_head_stride,
+                               a->dt_batch_stride, a->dt_seq_stride,
+                               a->B_batch_stride, a->B_seq_stride, G > 1 ? a->B_group_stride : 0,
+                               a->C_batch_stride, a->C_seq_stride, G > 1 ? a->C_group_stride : 0,
+                               a->out_batch_stride, a->out_seq_stride, a->out_head_stride,
+                               a->z ? a->z_batch_stride : 0, a->z ? a->z_seq_stride : 0,
+                               a->z ? a->z_head_stride : 0};
+    for (int64_t s : strides)
+      if (s < 0) return SSM_ERR_STRIDE;
+    if (misaligned(a->x, esz) || misaligned(a->dt, esz) || misaligned(a->z, esz) ||
+        misaligned(a->B, esz) || misaligned(a->C, esz) || misaligned(a->out, esz))
+      return SSM_ERR_ALIGN;
+    // the kernel reads a chunk (64 tokens) of x, dt, B and C through 31-bit
+    // byte windows
+    auto fits = [&](int64_t seq_stride, int64_t inner) {
+      return (63 * seq_stride + inner) * esz < (int64_t{1} << 31);
+    };
+    if (!fits(a->x_seq_stride, P) || !fits(a->dt_seq_stride, 1) || !fits(a->B_seq_stride, N) ||
+        !fits(a->C_seq_stride, N) || !fits(a->out_seq_stride, P) ||
+        (a->z && !fits(a->z_seq_stride, P)))
+      return SSM_ERR_UNSUPPORTED;
+  }
+  if (misaligned(a->A, 4) || misaligned(a->D, 4) || misaligned(a->dt_bias, 4) ||
+      misaligned(a->h0, 4) || misaligned(a->last_state, 4))
+    return SSM_ERR_ALIGN;
+  const Span sh0 = span1(a->h0, Bt * H * P * N, 4);
+  const Span inputs[] = {
+      span4(a->x, Bt, a->x_batch_stride, L, a->x_seq_stride, H, a->x_head_stride, P, esz),
+      span3(a->dt, Bt, a->dt_batch_stride, L, a->dt_seq_stride, H, esz),
+      span4(a->z, Bt, a->z_batch_stride, L, a->z_seq_stride, H, a->z_head_stride, P, esz),
+      span4(a->B, Bt, a->B_batch_stride, L, a->B_seq_stride, G, a->B_group_stride, N, esz),
+      span4(a->C, Bt, a->C_batch_stride, L, a->C_seq_stride, G, a->C_group_stride, N, esz),
+      span1(a->A, H, 4), span1(a->D, H, 4), span1(a->dt_bias, H, 4), sh0};
+  const Span sout = span4(a->out, Bt, a->out_batch_stride, L, a->out_seq_stride, H,
+                          a->out_head_stride, P, esz);
+  const Span slast = span1(a->last_state, Bt * H * P * N, 4);
+  for (const Span& i : inputs) {
+    if (overlap(sout, i)) return SSM_ERR_ALIAS;
+    if (&i == &inputs[8] && a->last_state == a->h0) continue;
+    if (overlap(slast, i)) return SSM_ERR_ALIAS;
+  }
+  if (overlap(sout, slast)) return SSM_ERR_ALIAS;
+  return SSM_OK;
+}
+
 int ssm_selective_scan_fwd(const ssm_scan_args* a, void* stream) {
   const int st = ssm_validate_scan(a);
   if (st != SSM_OK) return st;
@@ -306,6 +369,14 @@ int ssm_selective_scan_bwd(const ssm_scan_bwd_args* a, void* stream) {
   if (a->batch == 0 || a->dim == 0) return SSM_OK;
   if (ssm::launch_scan_bwd(*a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return SSM_ERR_HIP;
+  return SSM_OK;
+}
+
+int ssm_ssd_scan_fwd(const ssm_ssd_args* a, void* stream) {
+  const int st = ssm_validate_ssd(a);
+  if (st != SSM_OK) return st;
+  if (a->batch == 0) return SSM_OK;
+  if (ssm::launch_ssd_fwd(*a, static_cast<hipStream_t>(stream)) != hipSuccess) return SSM_ERR_HIP;
   return SSM_OK;
 }
 

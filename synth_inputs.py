@@ -238,3 +238,81 @@ def decode_inputs_host(batch: int, dim: int, dstate: int = DSTATE, io_dtype: str
     return dict(x=_to_io(x, io_dtype), z=_to_io(z, io_dtype), dt=_to_io(dt, io_dtype),
                 B=_to_io(B, io_dtype), C=_to_io(C, io_dtype), A=A, D=D, dt_bias=bias,
                 state=state, io_dtype=io_dtype)
+
+
+# ---------------------------------------------------------------------------
+# Mamba-2 (SSD layer) inputs.  Same distributions as above, per head: x, z ~
+# N(0, 1); dt ~ 0.1 N(0, 1); B, C ~ N(0, 1); per-head step bias = inverse
+# softplus of Delta0 log-uniform in [1e-3, 1e-1]; A[h] = -exp(U(0, ln 16)),
+# i.e. decays spread over [-16, -1] like the Mamba-1 recipe's -(n+1); D = 1.
+# Draw order: x, z, dt, B, C, then per head Delta0 and A.
+
+@dataclasses.dataclass(frozen=True)
+class SsdConfig:
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    dstate: int
+    io_dtype: str
+    seed: int
+
+
+# The page's Mamba2(d_model=1024, d_state=64, expand=2, headdim 64) block:
+# d_inner 2048 = 32 heads of 64, at the 130m-like layer's batch and length.
+SSD_CONFIG = SsdConfig("mamba2-d1024-layer-bf16", 8, 2048, 32, 64, 1, 64, "bf16", 5)
+
+
+def head_params(nheads: int, rng: np.random.Generator):
+    lo, hi = math.log(1e-3), math.log(1e-1)
+    delta0 = np.exp(rng.uniform(lo, hi, size=nheads))
+    A = -np.exp(rng.uniform(0.0, math.log(16.0), size=nheads)).astype(np.float32)
+    D = np.ones(nheads, dtype=np.float32)
+    return A, D, delta_bias_from_delta0(delta0)
+
+
+def ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, ngroups: int, dstate: int,
+               io_dtype: str = "f32", seed: int = 0) -> dict:
+    """Host (numpy) inputs of one Mamba-2 SSM prefill: x, z (batch, L, H, P);
+    dt (batch, L, H); B, C (batch, L, G, N); A, D, dt_bias (H)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((batch, seqlen, nheads, headdim), dtype=np.float32)
+    z = rng.standard_normal((batch, seqlen, nheads, headdim), dtype=np.float32)
+    dt = np.float32(0.1) * rng.standard_normal((batch, seqlen, nheads), dtype=np.float32)
+    B = rng.standard_normal((batch, seqlen, ngroups, dstate), dtype=np.float32)
+    C = rng.standard_normal((batch, seqlen, ngroups, dstate), dtype=np.float32)
+    A, D, bias = head_params(nheads, rng)
+    return dict(x=_to_io(x, io_dtype), z=_to_io(z, io_dtype), dt=_to_io(dt, io_dtype),
+                B=_to_io(B, io_dtype), C=_to_io(C, io_dtype), A=A, D=D, dt_bias=bias,
+                io_dtype=io_dtype)
+
+
+def ssd_inputs_device(cfg: SsdConfig, device="cuda", chunk: int = 1 << 22) -> dict:
+    """Device-drawn (torch Philox) inputs of the Mamba-2 layer config."""
+    import torch
+    io = torch_io_dtype(cfg.io_dtype)
+    g = torch.Generator(device=device)
+    g.manual_seed(cfg.seed)
+
+    def draw(shape, scale=1.0):
+        t = torch.empty(shape, dtype=io, device=device)
+        flat = t.view(-1)
+        for s in range(0, flat.numel(), chunk):
+            e = min(flat.numel(), s + chunk)
+            v = torch.randn(e - s, generator=g, device=device, dtype=torch.float32)
+            if scale != 1.0:
+                v.mul_(scale)
+            flat[s:e].copy_(v)
+        return t
+
+    xs = (cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim)
+    x = draw(xs)
+    z = draw(xs)
+    dt = draw((cfg.batch, cfg.seqlen, cfg.nheads), 0.1)
+    B = draw((cfg.batch, cfg.seqlen, cfg.ngroups, cfg.dstate))
+    C = draw((cfg.batch, cfg.seqlen, cfg.ngroups, cfg.dstate))
+    A, D, bias = head_params(cfg.nheads, np.random.default_rng(cfg.seed))
+    return dict(x=x, z=z, dt=dt, B=B, C=C, A=torch.from_numpy(A).to(device),
+                D=torch.from_numpy(D).to(device), dt_bias=torch.from_numpy(bias).to(device))

@@ -36,12 +36,12 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_struct_layout():
     L = ssm.lib()
-    assert L.ssm_abi_version() == ssm.SSM_ABI_VERSION == 4
+    assert L.ssm_abi_version() == ssm.SSM_ABI_VERSION == 5
     assert L.ssm_scan_args_size() == ctypes.sizeof(ssm.ScanArgs)
     assert L.ssm_scan_bwd_args_size() == ctypes.sizeof(ssm.ScanBwdArgs)
     assert L.ssm_update_args_size() == ctypes.sizeof(ssm.UpdateArgs)
     header = open(HEADER).read()
-    assert "#define SSM_ABI_VERSION 4" in header
+    assert "#define SSM_ABI_VERSION 5" in header
     assert f"#define SSM_MAX_CONV {ssm.MAX_CONV}" in header
     assert f"#define SSM_CHECKPOINT_TOKENS {ssm.CHECKPOINT_TOKENS}" in header
 
