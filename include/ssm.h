@@ -298,7 +298,7 @@ typedef struct ssm_update_args {
  * size must stay below 2^31 (inner size headdim, 1 for dt, dstate for B/C);
  * larger strides return SSM_ERR_UNSUPPORTED.
  * Precision: fp32 accumulation throughout and an fp32 state.  With bf16 IO the
- * products run on bf16 operands, so the masked chunk scores, B weighted by
+ * products run on bf16 operands, so the masked chunk scores, x weighted by
  * the decays and the state entering each chunk are rounded to bf16 where
  * they enter a product (the state itself stays fp32); with fp32 IO every
  * product is fp32.

@@ -18,7 +18,8 @@
 //   scores  G[s][t]  = sum_n B_s[n] C_t[n]                      (Q x Q, k = N)
 //   intra   Y1[t][p] = sum_s M[t][s] x_s[p],  M = G^T * decay mask * Delta
 //   state   Y2[t][p] = exp(a_t) sum_n C_t[n] H_in[n][p]         (k = N)
-//   update  H_out^T[p][n] = exp(a_{Q-1}) H_in^T + sum_s x_s[p] Bw_s[n]   (k = Q)
+//   update  H_out^T[p][n] = exp(a_{Q-1}) H_in^T + sum_s w_s x_s[p] B_s[n]  (k = Q),
+//           w_s = exp(a_{Q-1} - a_s) Delta_s
 //
 // Work decomposition.  A workgroup (4 wavefronts) owns one (batch, head,
 // block of 16 head channels) and walks the sequence chunk by chunk, keeping
@@ -32,7 +33,7 @@
 // never leave registers.  B, C and x of a chunk are staged in LDS by the
 // whole workgroup; the state goes through LDS once per chunk for the state
 // product.  bf16 IO uses v_mfma_f32_16x16x16_bf16 (fp32 accumulation; the
-// masked scores, the weighted B and the state operand are rounded to bf16);
+// masked scores, the decay-weighted x and the state operand are rounded to bf16);
 // fp32 IO uses v_mfma_f32_16x16x4_f32 four times per 16-wide k block, each
 // lane supplying the same four consecutive k values one per instruction.
 #include <algorithm>
@@ -85,19 +86,17 @@ template <> struct Lds<uint16_t> {
   }
 };
 
-// One 16x16 output tile step over a 16-wide k block: each lane supplies four
-// consecutive k values (k = 4 (l/16) + i) of its A row and B column.
+// A lane's operand fragment of one 16x16 tile step over a 16-wide k block:
+// four consecutive k values (k = 4 (l/16) + i) of its A row or B column, as
+// the product instruction takes them (four bf16, or four fp32).
+template <typename T> struct Frag;
+template <> struct Frag<uint16_t> { using V = v4s; };
+template <> struct Frag<float> { using V = v4f; };
+
 template <typename T>
-__device__ __forceinline__ v4f mma16(const typename Lds<T>::E (&a)[4],
-                                     const typename Lds<T>::E (&b)[4], v4f c) {
-  if constexpr (sizeof(typename Lds<T>::E) == 2) {
-    v4s av, bv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      av[i] = static_cast<short>(a[i]);
-      bv[i] = static_cast<short>(b[i]);
-    }
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, c, 0, 0, 0);
+__device__ __forceinline__ v4f mma16(typename Frag<T>::V a, typename Frag<T>::V b, v4f c) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
@@ -105,16 +104,38 @@ __device__ __forceinline__ v4f mma16(const typename Lds<T>::E (&a)[4],
   }
 }
 
-// Four consecutive LDS elements (8 or 16 bytes, aligned).
-template <typename E>
-__device__ __forceinline__ void lds4(const E* p, E (&v)[4]) {
-  if constexpr (sizeof(E) == 2) {
-    const uint2 q = *reinterpret_cast<const uint2*>(p);
-    v[0] = static_cast<E>(q.x & 0xffff); v[1] = static_cast<E>(q.x >> 16);
-    v[2] = static_cast<E>(q.y & 0xffff); v[3] = static_cast<E>(q.y >> 16);
+// Four consecutive LDS elements (8 or 16 bytes, aligned) as a fragment.
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::V ldsf(const typename Lds<T>::E* p) {
+  return *reinterpret_cast<const typename Frag<T>::V*>(p);
+}
+
+// Four LDS elements (already in the fragment's element type) as a fragment.
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::V tofrag_bits(typename Lds<T>::E a, typename Lds<T>::E b,
+                                                           typename Lds<T>::E c, typename Lds<T>::E d) {
+  if constexpr (sizeof(T) == 2) {
+    v4s v;
+    v[0] = static_cast<short>(a); v[1] = static_cast<short>(b);
+    v[2] = static_cast<short>(c); v[3] = static_cast<short>(d);
+    return v;
   } else {
-    const float4 q = *reinterpret_cast<const float4*>(p);
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    return v4f{a, b, c, d};
+  }
+}
+
+// Four fp32 values as a fragment (rounded to bf16 for bf16 IO).
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::V tofrag(float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    v4s v;
+    v[0] = __builtin_bit_cast(short, static_cast<__bf16>(a));
+    v[1] = __builtin_bit_cast(short, static_cast<__bf16>(b));
+    v[2] = __builtin_bit_cast(short, static_cast<__bf16>(c));
+    v[3] = __builtin_bit_cast(short, static_cast<__bf16>(d));
+    return v;
+  } else {
+    return v4f{a, b, c, d};
   }
 }
 
@@ -133,10 +154,10 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
   __shared__ __align__(16) E sB[kQ][NP];       // B_s[n]
   __shared__ __align__(16) E sC[kQ][NP];       // C_t[n]
   __shared__ __align__(16) E sXT[kPB][QP];     // x_s[p], transposed
+  __shared__ __align__(16) E sXW[kPB][QP];     // exp(a_{Q-1} - a_s) Delta_s x_s[p], transposed
   __shared__ __align__(16) E sHT[kPB][NP];     // H_in^T[p][n] (operand copy)
-  __shared__ float sDl[kQ];                    // Delta_s (0 past the end)
-  __shared__ float sLa[kQ];                    // a_t * log2(e)
-  __shared__ float sW[kQ];                     // exp(a_{Q-1} - a_s) Delta_s
+  __shared__ __align__(16) float sDl[kQ];      // Delta_s (0 past the end)
+  __shared__ __align__(16) float sLa[kQ];      // a_t * log2(e)
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -275,42 +296,10 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * kQ;
     const int nv = std::min(kQ, p.L - t0);
-    // ---- B, C, x^T and the step sizes of this chunk into LDS ----
+    // ---- the chunk's step sizes: every wavefront runs the 64-token scan
+    // (lane = token), so that each staging thread has the weight of its row
+    float w_row;
     {
-      const bool tv = srow < nv;
-      if constexpr (kVec) {
-        // a whole quarter row is real or padding (dstate % (NMAX/4) == 0)
-        const uint32_t m = (tv && squart * kQn < N) ? 0xffffffffu : 0u;
-#pragma unroll
-        for (int k = 0; k < kQw / 4; ++k) {
-          *reinterpret_cast<uint4*>(&sB[srow][squart * kQn + k * (16 / ES)]) =
-              make_uint4(st.b[4 * k] & m, st.b[4 * k + 1] & m, st.b[4 * k + 2] & m, st.b[4 * k + 3] & m);
-          *reinterpret_cast<uint4*>(&sC[srow][squart * kQn + k * (16 / ES)]) =
-              make_uint4(st.c[4 * k] & m, st.c[4 * k + 1] & m, st.c[4 * k + 2] & m, st.c[4 * k + 3] & m);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int pp = 4 * squart + k;
-          const uint32_t v = ES == 2 ? (st.x[k / 2] >> (16 * (k % 2))) : st.x[k % kXw];
-          sXT[pp][srow] = raw(v, tv && p0 + pp < p.P);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < kQn; ++k) {
-          const int n = squart * kQn + k;
-          const bool ok = tv && n < N;
-          sB[srow][n] = raw(st.b[k], ok);
-          sC[srow][n] = raw(st.c[k], ok);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int pp = 4 * squart + k;
-          sXT[pp][srow] = raw(st.x[k], tv && p0 + pp < p.P);
-        }
-      }
-    }
-    if (wave == 0) {
-      // step sizes, their running sum inside the chunk, decays
       const bool tv = lane < nv;
       const float x = Elem<T>::f32(st.dt) + bias;
       float dl = kSoftplus ? softplus_f32(x) : x;
@@ -323,9 +312,51 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
       }
       const float la = cum * a2;
       const float last = __shfl(la, 63, 64);
-      sDl[lane] = dl;
-      sLa[lane] = la;
-      sW[lane] = __builtin_amdgcn_exp2f(last - la) * dl;
+      const float w = __builtin_amdgcn_exp2f(last - la) * dl;   // exp(a_{Q-1} - a_s) Delta_s
+      w_row = __shfl(w, srow, 64);
+      if (wave == 0) {
+        sDl[lane] = dl;
+        sLa[lane] = la;
+      }
+    }
+    // ---- B (raw and decay-weighted), C, x^T of this chunk into LDS ----
+    {
+      const bool tv = srow < nv;
+      if constexpr (kVec) {
+        // a whole quarter row is real or padding (dstate % (NMAX/4) == 0)
+        const uint32_t m = (tv && squart * kQn < N) ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int k = 0; k < kQw / 4; ++k) {
+          const int col = squart * kQn + k * (16 / ES);
+          *reinterpret_cast<uint4*>(&sB[srow][col]) =
+              make_uint4(st.b[4 * k] & m, st.b[4 * k + 1] & m, st.b[4 * k + 2] & m, st.b[4 * k + 3] & m);
+          *reinterpret_cast<uint4*>(&sC[srow][col]) =
+              make_uint4(st.c[4 * k] & m, st.c[4 * k + 1] & m, st.c[4 * k + 2] & m, st.c[4 * k + 3] & m);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int pp = 4 * squart + k;
+          const uint32_t v = ES == 2 ? (st.x[k / 2] >> (16 * (k % 2))) : st.x[k % kXw];
+          const E xv = raw(v, tv && p0 + pp < p.P);
+          sXT[pp][srow] = xv;
+          sXW[pp][srow] = L::from(L::f(xv) * w_row);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < kQn; ++k) {
+          const int n = squart * kQn + k;
+          const bool ok = tv && n < N;
+          sB[srow][n] = raw(st.b[k], ok);
+          sC[srow][n] = raw(st.c[k], ok);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int pp = 4 * squart + k;
+          const E xv = raw(st.x[k], tv && p0 + pp < p.P);
+          sXT[pp][srow] = xv;
+          sXW[pp][srow] = L::from(L::f(xv) * w_row);
+        }
+      }
     }
     __syncthreads();
     // this chunk's gate, then the next chunk's loads fly while this one is
@@ -345,43 +376,38 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
         // k = n), B operand = C^T (k = n, column t)
         v4f sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          E av[4], bv[4];
-          lds4<E>(&sB[16 * sbk + lr][16 * nb + 4 * lq], av);
-          lds4<E>(&sC[tb + lr][16 * nb + 4 * lq], bv);
-          sc = mma16<T>(av, bv, sc);
-        }
+        for (int nb = 0; nb < NB; ++nb)
+          sc = mma16<T>(ldsf<T>(&sB[16 * sbk + lr][16 * nb + 4 * lq]),
+                        ldsf<T>(&sC[tb + lr][16 * nb + 4 * lq]), sc);
         // mask and scale: lane holds s = 16 sbk + 4 lq + i, t = tb + lr
-        E mv[4], xv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int s = 16 * sbk + 4 * lq + i;
-          const float m = sc[i] * __builtin_amdgcn_exp2f(la_t - sLa[s]) * sDl[s];
-          mv[i] = L::from(s <= tb + lr ? m : 0.0f);
-        }
+        const int s0 = 16 * sbk + 4 * lq;
+        const float4 la_s = *reinterpret_cast<const float4*>(&sLa[s0]);
+        const float4 dl_s = *reinterpret_cast<const float4*>(&sDl[s0]);
+        const int t = tb + lr;
+        const float m0 = s0 + 0 <= t ? sc[0] * __builtin_amdgcn_exp2f(la_t - la_s.x) * dl_s.x : 0.0f;
+        const float m1 = s0 + 1 <= t ? sc[1] * __builtin_amdgcn_exp2f(la_t - la_s.y) * dl_s.y : 0.0f;
+        const float m2 = s0 + 2 <= t ? sc[2] * __builtin_amdgcn_exp2f(la_t - la_s.z) * dl_s.z : 0.0f;
+        const float m3 = s0 + 3 <= t ? sc[3] * __builtin_amdgcn_exp2f(la_t - la_s.w) * dl_s.w : 0.0f;
         // intra: A = M (row t, k = s), B operand = x (k = s, column p)
-        lds4<E>(&sXT[lr][16 * sbk + 4 * lq], xv);
-        y1 = mma16<T>(mv, xv, y1);
+        y1 = mma16<T>(tofrag<T>(m0, m1, m2, m3), ldsf<T>(&sXT[lr][s0]), y1);
       }
       // state: A = C (row t, k = n), B operand = H_in (k = n, column p)
       v4f y2 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        E av[4], bv[4];
-        lds4<E>(&sC[tb + lr][16 * nb + 4 * lq], av);
-        lds4<E>(&sHT[lr][16 * nb + 4 * lq], bv);
-        y2 = mma16<T>(av, bv, y2);
-      }
+      for (int nb = 0; nb < NB; ++nb)
+        y2 = mma16<T>(ldsf<T>(&sC[tb + lr][16 * nb + 4 * lq]), ldsf<T>(&sHT[lr][16 * nb + 4 * lq]), y2);
       // lane holds t = tb + 4 lq + i, p = lr; stores of tokens past the end
       // or channels past headdim go past the window's end and are dropped
       const __amdgpu_buffer_rsrc_t ro = window(og, p.osl, p.P - p0, t0);
       const uint32_t oend = static_cast<uint32_t>(
           (static_cast<int64_t>(std::min(p.L - 1 - t0, kQ - 1)) * p.osl + (p.P - p0)) * ES);
+      const float4 la_o = *reinterpret_cast<const float4*>(&sLa[tb + 4 * lq]);
+      const float lav[4] = {la_o.x, la_o.y, la_o.z, la_o.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tl = tb + 4 * lq + i;
         const float xval = L::f(sXT[lr][tl]);
-        float y = y1[i] + __builtin_amdgcn_exp2f(sLa[tl]) * y2[i];
+        float y = y1[i] + __builtin_amdgcn_exp2f(lav[i]) * y2[i];
         y = fmaf(Dh, xval, y);
         const float gz = silu_f32(Elem<T>::f32(zr[i]));
         y *= zg ? gz : 1.0f;
@@ -391,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
       }
     }
 
-    // ---- state update: H_out^T = exp(a_last) H_in^T + x^T Bw ----
+    // ---- state update: H_out^T = exp(a_last) H_in^T + (w x)^T B ----
     {
       const float decay = __builtin_amdgcn_exp2f(sLa[kQ - 1]);
 #pragma unroll
@@ -401,15 +427,11 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
           v4f acc = Hs[j] * decay;
 #pragma unroll
           for (int sbk = 0; sbk < kQ / 16; ++sbk) {
-            // A = x^T (row p, k = s); B operand = Bw (k = s, column n)
-            E av[4], bv[4];
-            lds4<E>(&sXT[lr][16 * sbk + 4 * lq], av);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int s = 16 * sbk + 4 * lq + i;
-              bv[i] = L::from(L::f(sB[s][16 * m + lr]) * sW[s]);
-            }
-            acc = mma16<T>(av, bv, acc);
+            // A = (w x)^T (row p, k = s); B operand = B (k = s, column n)
+            const int s0 = 16 * sbk + 4 * lq, n = 16 * m + lr;
+            acc = mma16<T>(ldsf<T>(&sXW[lr][s0]),
+                           tofrag_bits<T>(sB[s0][n], sB[s0 + 1][n], sB[s0 + 2][n], sB[s0 + 3][n]),
+                           acc);
           }
           Hs[j] = acc;
         }
