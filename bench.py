@@ -191,12 +191,15 @@ def bench_bwd(cfg, steps, torch, ssm, si):
     return res
 
 
-def bench_decode(cfg, torch, ssm, si, warmup=20, conv=0):
+def bench_decode(cfg, torch, ssm, si, warmup=20, conv=0, state_sets=1):
     """1000 consecutive decode steps with per-step inputs pre-resident (with
-    conv > 0 the conv branch's state update of that width is fused in)."""
+    conv > 0 the conv branch's state update of that width is fused in).
+    With state_sets > 1, step s updates state set s % state_sets: the sets
+    together (84 MB each here) exceed the 256 MB Infinity Cache, so every
+    step's state comes from HBM (the cold cross-check)."""
     dev = "cuda"
     d = si.decode_inputs_device(cfg, device=dev)
-    state = torch.zeros((cfg.batch, cfg.dim, cfg.dstate), device=dev)
+    states = [torch.zeros((cfg.batch, cfg.dim, cfg.dstate), device=dev) for _ in range(state_sets)]
     out = torch.empty((cfg.steps, cfg.batch, cfg.dim), dtype=d["x"].dtype, device=dev)
     ckw = {}
     if conv:
@@ -205,12 +208,14 @@ def bench_decode(cfg, torch, ssm, si, warmup=20, conv=0):
                    conv_bias=torch.zeros(cfg.dim, device=dev))
 
     def step(s):
-        ssm.selective_state_update(state, d["x"][s], d["dt"][s], d["A"], d["B"][s], d["C"][s],
-                                   D=d["D"], z=d["z"][s], dt_bias=d["dt_bias"], out=out[s], **ckw)
+        ssm.selective_state_update(states[s % state_sets], d["x"][s], d["dt"][s], d["A"], d["B"][s],
+                                   d["C"][s], D=d["D"], z=d["z"][s], dt_bias=d["dt_bias"],
+                                   out=out[s], **ckw)
 
     for s in range(warmup):
         step(s)
-    state.zero_()
+    for st in states:
+        st.zero_()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(cfg.steps):
@@ -229,7 +234,8 @@ def bench_decode(cfg, torch, ssm, si, warmup=20, conv=0):
                kernel_gbps=nbytes / (kern_ms * 1e-3) / 1e9,
                channel_tokens_per_s=cfg.batch * cfg.dim / (ms_step * 1e-3))
     res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBS
-    del d, out, state
+    res["state_sets"] = state_sets
+    del d, out, states
     torch.cuda.empty_cache()
     return res
 
@@ -389,6 +395,10 @@ def main():
         log(f"[bench] secondary {si.DECODE_CONFIG.name}")
         secondary[si.DECODE_CONFIG.name] = bench_decode(si.DECODE_CONFIG, torch, ssm, si)
         log(f"[bench] decode {secondary[si.DECODE_CONFIG.name]['gbps']:.1f} GB/s")
+        key = f"{si.DECODE_CONFIG.name}-cold-4-state-sets"
+        log(f"[bench] secondary {key}")
+        secondary[key] = bench_decode(si.DECODE_CONFIG, torch, ssm, si, state_sets=4)
+        log(f"[bench] {key} {secondary[key]['gbps']:.1f} GB/s")
         key = f"{si.DECODE_CONFIG.name}-conv4-fused"
         log(f"[bench] secondary {key}")
         secondary[key] = bench_decode(si.DECODE_CONFIG, torch, ssm, si, conv=4)
