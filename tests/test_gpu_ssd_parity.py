@@ -4,7 +4,7 @@ against the fp64 oracle (oracle.ssd_scan) on the same seeded inputs.
 Bars (row-normwise max relative error; a row is one (batch, head, channel)
 sequence over t, or one state vector over n): 1e-4 for fp32 IO and 2e-2 for
 bf16 IO.  With bf16 IO the kernel rounds the masked chunk scores, the
-decay-weighted B and the chunk-entry state to bf16 where they enter a matrix
+decay-weighted x and the chunk-entry state to bf16 where they enter a matrix
 product (fp32 accumulation), so its error is of the order of bf16 rounding;
 the printed errors show the margin."""
 import numpy as np
@@ -185,3 +185,36 @@ def test_ssd_rejects_unsupported_state_size():
     with pytest.raises(ssm.SSMError) as ei:
         ssm.ssd_scan_fwd(x, dt, -torch.ones(2, device=DEV), Bm, Bm)
     assert ei.value.status == 7
+
+
+def test_mamba2_decode_is_the_mamba1_step_with_head_broadcast():
+    """A Mamba-2 decode step through ssm_selective_state_update: channel
+    d = h * P + p, A[d, n] = A[h] for every n, the head's step and bias
+    repeated over its P channels, D repeated, B/C in G groups (channel d reads
+    group d / (H P / G) = h / (H / G)).  Checked against the SSD oracle one
+    token at a time, starting from a random state."""
+    batch, H, P, G, N, steps = 2, 4, 16, 2, 64, 5
+    inp = si.ssd_inputs(batch, steps, H, P, G, N, io_dtype="f32", seed=44)
+    state0 = np.random.default_rng(44).standard_normal((batch, H, P, N)).astype(np.float32)
+    dev = {k: torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for k, v in inp.items()
+           if k != "io_dtype"}
+    A1 = dev["A"].repeat_interleave(P)[:, None].expand(H * P, N).contiguous()
+    D1 = dev["D"].repeat_interleave(P)
+    bias1 = dev["dt_bias"].repeat_interleave(P)
+    state = torch.from_numpy(state0.reshape(batch, H * P, N)).to(DEV)
+    ref_state = state0.astype(np.float64)
+    for t in range(steps):
+        x = dev["x"][:, t].reshape(batch, H * P).contiguous()
+        z = dev["z"][:, t].reshape(batch, H * P).contiguous()
+        dt = dev["dt"][:, t].repeat_interleave(P, dim=1).contiguous()
+        out = ssm.selective_state_update(state, x, dt, A1, dev["B"][:, t].contiguous(),
+                                         dev["C"][:, t].contiguous(), D=D1, z=z, dt_bias=bias1)
+        torch.cuda.synchronize()
+        one = {k: (v[:, t:t + 1] if k in ("x", "z", "dt", "B", "C") else v) for k, v in inp.items()}
+        ref, ref_state = oracle.ssd_scan(one["x"], one["dt"], one["A"], one["B"], one["C"], D=one["D"],
+                                         z=one["z"], dt_bias=one["dt_bias"], h0=ref_state,
+                                         return_last_state=True)
+        e = row_rel_err(to_np(out).reshape(batch, H, P), ref[:, 0])
+        es = row_rel_err(to_np(state).reshape(batch, H, P, N), ref_state)
+        print(f"[mamba2 decode step {t}] err_out={e:.2e} err_state={es:.2e}", flush=True)
+        assert e <= 1e-4 and es <= 1e-4
