@@ -298,10 +298,10 @@ typedef struct ssm_update_args {
  * size must stay below 2^31 (inner size headdim, 1 for dt, dstate for B/C);
  * larger strides return SSM_ERR_UNSUPPORTED.
  * Precision: fp32 accumulation throughout and an fp32 state.  With bf16 IO the
- * products run on bf16 operands, so the masked chunk scores, x weighted by
- * the decays and the state entering each chunk are rounded to bf16 where
- * they enter a product (the state itself stays fp32); with fp32 IO every
- * product is fp32.
+ * products run on bf16 operands, so the masked chunk scores and x weighted
+ * by the decays are rounded to bf16 where they enter a product, and the fp32
+ * state entering each chunk enters as a bf16 value plus its bf16 remainder
+ * (two products); with fp32 IO every product is fp32.
  * Aliasing: out must not overlap any input; last_state must not overlap any
  * input except that it may be exactly h0. */
 typedef struct ssm_ssd_args {

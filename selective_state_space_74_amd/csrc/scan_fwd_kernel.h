@@ -335,7 +335,7 @@ struct Wave {
         if (M == Mode::kScan) {
           constexpr int i = S == 1 ? j % 4 : j;
           pk[i] = q == 0 ? cv[j] * h[q] : fmaf(cv[j], h[q], pk[i]);        // C_n h_n
-          if (q == S - 1 && j % 4 == 3)
+          if constexpr (q == S - 1 && j % 4 == 3)
             *reinterpret_cast<float4*>(&sP[row][col * kPitch + j - 3]) =
                 make_float4(pk[i - 3], pk[i - 2], pk[i - 1], pk[i]);
         }

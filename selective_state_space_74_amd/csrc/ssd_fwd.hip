@@ -33,7 +33,8 @@
 // never leave registers.  B, C and x of a chunk are staged in LDS by the
 // whole workgroup; the state goes through LDS once per chunk for the state
 // product.  bf16 IO uses v_mfma_f32_16x16x16_bf16 (fp32 accumulation; the
-// masked scores, the decay-weighted x and the state operand are rounded to bf16);
+// masked scores and the decay-weighted x are rounded to bf16, and the state
+// operand is split into a bf16 value and its bf16 remainder);
 // fp32 IO uses v_mfma_f32_16x16x4_f32 four times per 16-wide k block, each
 // lane supplying the same four consecutive k values one per instruction.
 #include <algorithm>
@@ -156,6 +157,9 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
   __shared__ __align__(16) E sXT[kPB][QP];     // x_s[p], transposed
   __shared__ __align__(16) E sXW[kPB][QP];     // exp(a_{Q-1} - a_s) Delta_s x_s[p], transposed
   __shared__ __align__(16) E sHT[kPB][NP];     // H_in^T[p][n] (operand copy)
+  // bf16: the rounding remainder H - bf16(H), so that the state product
+  // carries the fp32 state to about 16 bits (two bf16 products)
+  __shared__ __align__(16) E sHL[sizeof(E) == 2 ? kPB : 1][sizeof(E) == 2 ? NP : 1];
   __shared__ __align__(16) float sDl[kQ];      // Delta_s (0 past the end)
   __shared__ __align__(16) float sLa[kQ];      // a_t * log2(e)
 
@@ -201,7 +205,11 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
       const int m = wave + kWaves * j;
       if (m < NB) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sHT[4 * lq + i][16 * m + lr] = L::from(Hs[j][i]);
+        for (int i = 0; i < 4; ++i) {
+          const E hi = L::from(Hs[j][i]);
+          sHT[4 * lq + i][16 * m + lr] = hi;
+          if constexpr (sizeof(E) == 2) sHL[4 * lq + i][16 * m + lr] = L::from(Hs[j][i] - L::f(hi));
+        }
       }
     }
   };
@@ -395,7 +403,11 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
       v4f y2 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        y2 = mma16<T>(ldsf<T>(&sC[tb + lr][16 * nb + 4 * lq]), ldsf<T>(&sHT[lr][16 * nb + 4 * lq]), y2);
+      {
+        const auto cf = ldsf<T>(&sC[tb + lr][16 * nb + 4 * lq]);
+        y2 = mma16<T>(cf, ldsf<T>(&sHT[lr][16 * nb + 4 * lq]), y2);
+        if constexpr (sizeof(E) == 2) y2 = mma16<T>(cf, ldsf<T>(&sHL[lr][16 * nb + 4 * lq]), y2);
+      }
       // lane holds t = tb + 4 lq + i, p = lr; stores of tokens past the end
       // or channels past headdim go past the window's end and are dropped
       const __amdgpu_buffer_rsrc_t ro = window(og, p.osl, p.P - p0, t0);

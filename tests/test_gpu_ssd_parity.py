@@ -3,10 +3,11 @@ against the fp64 oracle (oracle.ssd_scan) on the same seeded inputs.
 
 Bars (row-normwise max relative error; a row is one (batch, head, channel)
 sequence over t, or one state vector over n): 1e-4 for fp32 IO and 2e-2 for
-bf16 IO.  With bf16 IO the kernel rounds the masked chunk scores, the
-decay-weighted x and the chunk-entry state to bf16 where they enter a matrix
-product (fp32 accumulation), so its error is of the order of bf16 rounding;
-the printed errors show the margin."""
+bf16 IO.  With bf16 IO the kernel rounds the masked chunk scores and the
+decay-weighted x to bf16 where they enter a matrix product (fp32
+accumulation; the chunk-entry state enters as a bf16 value plus its bf16
+remainder), so its error is of the order of bf16 rounding; the printed
+errors show the margin."""
 import numpy as np
 import pytest
 
