@@ -127,7 +127,17 @@ hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {
   p.conv_silu = a.conv_silu;
   p.nbk = static_cast<int>((a.seqlen + kT - 1) / kT);
 
-  const bool bf16 = a.io_dtype == SSM_BF16, sp = a.delta_softplus != 0, lane = lane_bc(a);
+  const bool bf16 = a.io_dtype == SSM_BF16, sp = a.delta_softplus != 0;
+  // lane mode with 16-byte aligned B/C rows and blocks: vector loads.  The
+  // rows' ends are 16-byte aligned too (seqlen a multiple of the vector
+  // width), so no load straddles the end of a buffer window.
+  const int64_t vw = bf16 ? 8 : 4;
+  auto al16 = [](const void* ptr) { return reinterpret_cast<uintptr_t>(ptr) % 16 == 0; };
+  const bool lvec = al16(a.B) && al16(a.C) && a.seqlen % vw == 0 && a.B_batch_stride % vw == 0 &&
+                    a.B_group_stride % vw == 0 && a.B_state_stride % vw == 0 &&
+                    a.C_batch_stride % vw == 0 && a.C_group_stride % vw == 0 &&
+                    a.C_state_stride % vw == 0;
+  const int lane = lane_bc(a) ? (lvec ? 2 : 1) : 0;
   auto run = [&](bool aggregate, dim3 grid) {
     switch (slots(a.dstate)) {
       case 1: fwd::launch_slots<1>(aggregate, lane, bf16, sp, p.K, grid, p, stream); break;

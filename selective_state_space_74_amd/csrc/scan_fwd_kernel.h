@@ -27,8 +27,8 @@
 //               then reads back its states' rows for each block.
 //               lane mode (groups smaller than a workgroup, down to one
 //               channel per group): each lane loads the 16 tokens of its own
-//               group's rows for each block straight from memory; no LDS
-//               tile and no barrier.
+//               group's rows for each block straight from memory (16-byte
+//               loads when the rows are aligned); no LDS tile and no barrier.
 //   readout     each state lane leaves sum_s C_n h_n per token in its
 //               wavefront's LDS; one block later the owner of the token sums
 //               the 16 partials, adds D*u, applies the gate and stores.
@@ -130,7 +130,7 @@ __device__ __forceinline__ float row_ror(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + M, 0xf, 0xf, true));
 }
 
-template <typename T, Mode M, bool kSoftplus, int KP, int S, bool kLane>
+template <typename T, Mode M, bool kSoftplus, int KP, int S, int kLane>
 struct Wave {
   const ScanParams& p;
   int wave, row, col;
@@ -228,11 +228,41 @@ struct Wave {
       const __amdgpu_buffer_rsrc_t rb = wB.at(s);
       const __amdgpu_buffer_rsrc_t rc = wC.at(s);
       const int tleft = t_end - (t_beg + k * kT);
+      if constexpr (kLane == 2) {
+        // 16-byte aligned rows: the block's 16 tokens in 16-byte loads
+        constexpr int kV = kT * E / 16;  // loads per tensor
+        uint32_t rbw[kT * E / 4], rcw[kT * E / 4];
 #pragma unroll
-      for (int j = 0; j < kT; ++j) {
-        const float b = Elem<T>::f32(Elem<T>::load(rb, oB[q] + j * E));
-        bv[j] = !kMask || j < tleft ? b : 0.0f;
-        if (M == Mode::kScan) cv[j] = Elem<T>::f32(Elem<T>::load(rc, oC[q] + j * E));
+        for (int v = 0; v < kV; ++v) {
+          const auto xb = __builtin_amdgcn_raw_buffer_load_b128(rb, oB[q] + 16 * v, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rbw[4 * v + i] = xb[i];
+          if (M == Mode::kScan) {
+            const auto xc = __builtin_amdgcn_raw_buffer_load_b128(rc, oC[q] + 16 * v, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rcw[4 * v + i] = xc[i];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kT; ++j) {
+          float b, cc = 0.0f;
+          if constexpr (E == 2) {
+            b = __uint_as_float(j % 2 ? rbw[j / 2] & 0xffff0000u : rbw[j / 2] << 16);
+            if (M == Mode::kScan) cc = __uint_as_float(j % 2 ? rcw[j / 2] & 0xffff0000u : rcw[j / 2] << 16);
+          } else {
+            b = __uint_as_float(rbw[j]);
+            if (M == Mode::kScan) cc = __uint_as_float(rcw[j]);
+          }
+          bv[j] = !kMask || j < tleft ? b : 0.0f;
+          if (M == Mode::kScan) cv[j] = cc;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kT; ++j) {
+          const float b = Elem<T>::f32(Elem<T>::load(rb, oB[q] + j * E));
+          bv[j] = !kMask || j < tleft ? b : 0.0f;
+          if (M == Mode::kScan) cv[j] = Elem<T>::f32(Elem<T>::load(rc, oC[q] + j * E));
+        }
       }
     }
   }
@@ -363,7 +393,7 @@ struct Wave {
   }
 };
 
-template <typename T, Mode M, bool kSoftplus, int KP, int S, bool kLane>
+template <typename T, Mode M, bool kSoftplus, int KP, int S, int kLane>
 __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   constexpr int kTile = kLane ? 1 : 2;
   __shared__ __align__(16) float sB[kTile][kN * S][kGPitch];
@@ -597,7 +627,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
 
 // Launch of one variant family: the dtype, softplus and conv width choose
 // among the instantiations with S state slots per lane and the B/C mode.
-template <Mode M, int KP, int S, bool kLane>
+template <Mode M, int KP, int S, int kLane>
 void launch_kp(bool bf16, bool softplus, dim3 grid, const ScanParams& p, hipStream_t stream) {
   const dim3 block(kThreads);
   if (bf16) {
@@ -611,18 +641,27 @@ void launch_kp(bool bf16, bool softplus, dim3 grid, const ScanParams& p, hipStre
 
 // The conv width is padded to 4 or 8 taps (zero weights); only the
 // one-slot shared-B/C kernels, the common Mamba-1 shape, get the 4-tap form.
-template <Mode M, int S, bool kLane>
-void launch_mode(bool bf16, bool softplus, int K, dim3 grid, const ScanParams& p,
+// B/C modes: 0 shared tile, 1 per-lane element loads, 2 per-lane 16-byte
+// loads (aligned rows; without the conv branch).
+template <Mode M, int S>
+void launch_mode(int lane, bool bf16, bool softplus, int K, dim3 grid, const ScanParams& p,
                  hipStream_t stream) {
-  if (K == 0) launch_kp<M, 0, S, kLane>(bf16, softplus, grid, p, stream);
-  else if (K <= 4 && S == 1 && !kLane) launch_kp<M, 4, S, kLane>(bf16, softplus, grid, p, stream);
-  else launch_kp<M, 8, S, kLane>(bf16, softplus, grid, p, stream);
+  if (lane == 0) {
+    if (K == 0) launch_kp<M, 0, S, 0>(bf16, softplus, grid, p, stream);
+    else if (K <= 4 && S == 1) launch_kp<M, 4, S, 0>(bf16, softplus, grid, p, stream);
+    else launch_kp<M, 8, S, 0>(bf16, softplus, grid, p, stream);
+  } else if (lane == 2 && K == 0) {
+    launch_kp<M, 0, S, 2>(bf16, softplus, grid, p, stream);
+  } else {
+    if (K == 0) launch_kp<M, 0, S, 1>(bf16, softplus, grid, p, stream);
+    else launch_kp<M, 8, S, 1>(bf16, softplus, grid, p, stream);
+  }
 }
 
 // Both passes' launches for S state slots per lane (defined in
 // scan_fwd_s<S>.hip).
 template <int S>
-void launch_slots(bool aggregate, bool lane, bool bf16, bool softplus, int K, dim3 grid,
+void launch_slots(bool aggregate, int lane, bool bf16, bool softplus, int K, dim3 grid,
                   const ScanParams& p, hipStream_t stream);
 
 }  // namespace fwd

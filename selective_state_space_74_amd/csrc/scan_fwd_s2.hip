@@ -6,15 +6,10 @@ namespace ssm {
 namespace fwd {
 
 template <>
-void launch_slots<2>(bool aggregate, bool lane, bool bf16, bool softplus, int K, dim3 grid,
+void launch_slots<2>(bool aggregate, int lane, bool bf16, bool softplus, int K, dim3 grid,
                       const ScanParams& p, hipStream_t stream) {
-  if (aggregate) {
-    if (lane) launch_mode<Mode::kAggregate, 2, true>(bf16, softplus, K, grid, p, stream);
-    else launch_mode<Mode::kAggregate, 2, false>(bf16, softplus, K, grid, p, stream);
-  } else {
-    if (lane) launch_mode<Mode::kScan, 2, true>(bf16, softplus, K, grid, p, stream);
-    else launch_mode<Mode::kScan, 2, false>(bf16, softplus, K, grid, p, stream);
-  }
+  if (aggregate) launch_mode<Mode::kAggregate, 2>(lane, bf16, softplus, K, grid, p, stream);
+  else launch_mode<Mode::kScan, 2>(lane, bf16, softplus, K, grid, p, stream);
 }
 
 }  // namespace fwd

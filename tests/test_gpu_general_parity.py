@@ -77,6 +77,16 @@ def test_long_sequence_segmented(N, G, io):
     check(inp, io, f"segmented N{N} G{G} {io}", h0=h0, twin=False)
 
 
+@pytest.mark.parametrize("io,N", [("bf16", 16), ("bf16", 64), ("f32", 33)])
+def test_lane_mode_vector_loads(io, N):
+    """Per-channel B/C with rows 16-byte aligned and L a multiple of the
+    vector width: the lane mode's 16-byte loads (two segments for bf16)."""
+    L = 8192 * 2 + 512 if io == "bf16" else 320
+    inp = si.scan_inputs(1 if io == "bf16" else 2, 32, L, dstate=N, io_dtype=io, seed=N + L,
+                         ngroups=32)
+    check(inp, io, f"lane vector {io} N{N} L{L}", twin=False)
+
+
 def test_ragged_channels_lane_mode():
     """dim 37 per-channel B/C (lane mode) with a partial last workgroup."""
     inp = si.scan_inputs(2, 37, 131, dstate=20, seed=3, ngroups=37)
