@@ -22,9 +22,11 @@
 //           w_s = exp(a_{Q-1} - a_s) Delta_s
 //
 // Work decomposition.  A workgroup (4 wavefronts) owns one (batch, head,
-// block of 16 head channels) and walks the sequence chunk by chunk, keeping
-// the fp32 state H^T (16 channels x N states) in MFMA accumulator registers:
-// wavefront w holds state columns n in blocks w, w+4, ... .  Wavefront w also
+// PB blocks of 16 head channels) and walks the sequence chunk by chunk,
+// keeping the fp32 state H^T (16 PB channels x N states) in MFMA accumulator
+// registers: wavefront w holds state columns n in blocks w, w+4, ... .  The
+// chunk's step scan, B/C staging, score tiles and masks are formed once and
+// used for all PB channel blocks.  Wavefront w also
 // owns output tokens 16w..16w+15 of each chunk: it forms the score tiles for
 // source blocks 0..w (causal), masks them, and feeds them straight into the
 // next product: the accumulator layout of a 16x16 tile (lane l holds rows
@@ -45,7 +47,7 @@ namespace ssm {
 namespace {
 
 constexpr int kQ = 64;          // tokens per chunk
-constexpr int kPB = 16;         // head channels per workgroup
+constexpr int kPB = 16;         // head channels per channel block
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
@@ -68,7 +70,7 @@ struct SsdParams {
   void* out;
   int64_t xsb, xsl, xsh, dsb, dsl, zsb, zsl, zsh, Bsb, Bsl, Bsg, Csb, Csl, Csg, osb, osl, osh;
   int L, H, P, G, N;
-  int pblocks;   // ceil(P / 16)
+  int pblocks;   // workgroups per head: ceil(P / (16 PB))
 };
 
 // Storage of one IO element in LDS and its widening.
@@ -140,11 +142,21 @@ __device__ __forceinline__ typename Frag<T>::V tofrag(float a, float b, float c,
   }
 }
 
+// The one-block bf16 kernel with 64 states and vector staging fits four
+// wavefronts per SIMD (128 registers) without spilling; asking for that keeps
+// a grid of 4 x 256 workgroups in one wave of residency.
+template <typename T, int NMAX, bool kVec, int PB>
+constexpr bool kFourWaves() { return sizeof(T) == 2 && NMAX == 64 && kVec && PB == 1; }
+
 // kVec: B/C rows, x rows and their strides are 16-byte (x: 8-byte for bf16)
 // aligned and dstate is a multiple of NMAX / 4, so staging uses vector loads
-// and 16-byte LDS stores; otherwise element-wise loads.
-template <typename T, int NMAX, bool kSoftplus, bool kVec>
-__global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
+// and 16-byte LDS stores; otherwise element-wise loads.  PB: blocks of 16
+// head channels per workgroup (the score tiles, masks and B/C staging of a
+// chunk are shared by all of them).
+template <typename T, int NMAX, bool kSoftplus, bool kVec, int PB>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kFourWaves<T, NMAX, kVec, PB>() ? 4 : 1)))
+void ssd_fwd_kernel(SsdParams p) {
   using L = Lds<T>;
   using E = typename L::E;
   constexpr int kPadE = 16 / sizeof(E);        // 16 bytes of padding per row
@@ -152,14 +164,16 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
   constexpr int QP = kQ + kPadE;               // LDS pitch of an x^T row
   constexpr int NB = NMAX / 16;                // 16-wide state blocks
   constexpr int NBW = (NB + kWaves - 1) / kWaves;  // state blocks per wavefront
+  constexpr int PC = kPB * PB;                 // head channels per workgroup
+  constexpr bool kBF = sizeof(E) == 2;
   __shared__ __align__(16) E sB[kQ][NP];       // B_s[n]
   __shared__ __align__(16) E sC[kQ][NP];       // C_t[n]
-  __shared__ __align__(16) E sXT[kPB][QP];     // x_s[p], transposed
-  __shared__ __align__(16) E sXW[kPB][QP];     // exp(a_{Q-1} - a_s) Delta_s x_s[p], transposed
-  __shared__ __align__(16) E sHT[kPB][NP];     // H_in^T[p][n] (operand copy)
+  __shared__ __align__(16) E sXT[PC][QP];      // x_s[p], transposed
+  __shared__ __align__(16) E sXW[PC][QP];      // exp(a_{Q-1} - a_s) Delta_s x_s[p], transposed
+  __shared__ __align__(16) E sHT[PC][NP];      // H_in^T[p][n] (operand copy)
   // bf16: the rounding remainder H - bf16(H), so that the state product
   // carries the fp32 state to about 16 bits (two bf16 products)
-  __shared__ __align__(16) E sHL[sizeof(E) == 2 ? kPB : 1][sizeof(E) == 2 ? NP : 1];
+  __shared__ __align__(16) E sHL[kBF ? PC : 1][kBF ? NP : 1];
   __shared__ __align__(16) float sDl[kQ];      // Delta_s (0 past the end)
   __shared__ __align__(16) float sLa[kQ];      // a_t * log2(e)
 
@@ -171,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
   const int h = (blockIdx.x / p.pblocks) % p.H;
   const int64_t b = blockIdx.x / (static_cast<int64_t>(p.pblocks) * p.H);
   const int g = h / (p.H / p.G);
-  const int p0 = pb * kPB;
+  const int p0 = pb * PC;
   const int N = p.N;
   const float a2 = p.A[h] * kLog2e;
   const float bias = p.bias ? p.bias[h] : 0.0f;
@@ -185,30 +199,37 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
   const T* Cg = static_cast<const T*>(p.C) + b * p.Csb + static_cast<int64_t>(g) * p.Csg;
   T* og = static_cast<T*>(p.out) + b * p.osb + static_cast<int64_t>(h) * p.osh + p0;
 
-  // State H^T tiles: lane holds H^T[p = 4 lq + i][n = 16 m + lr], m = wave + 4 j.
-  v4f Hs[NBW];
+  // State H^T tiles: lane holds H^T[p = 16 q + 4 lq + i][n = 16 m + lr] for
+  // channel block q and state block m = wave + 4 j.
+  v4f Hs[NBW][PB];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     const int n = 16 * (wave + kWaves * j) + lr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pp = 4 * lq + i;
-      Hs[j][i] = (p.h0 && n < N && p0 + pp < p.P)
-                     ? p.h0[((b * p.H + h) * p.P + p0 + pp) * static_cast<int64_t>(N) + n]
-                     : 0.0f;
+    for (int q = 0; q < PB; ++q) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pp = p0 + kPB * q + 4 * lq + i;
+        Hs[j][q][i] = (p.h0 && n < N && pp < p.P)
+                          ? p.h0[((b * p.H + h) * p.P + pp) * static_cast<int64_t>(N) + n]
+                          : 0.0f;
+      }
     }
   }
-  // operand copy of the initial state
+  // operand copy of the state (bf16: value and remainder)
   auto store_ht = [&]() {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const int m = wave + kWaves * j;
       if (m < NB) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const E hi = L::from(Hs[j][i]);
-          sHT[4 * lq + i][16 * m + lr] = hi;
-          if constexpr (sizeof(E) == 2) sHL[4 * lq + i][16 * m + lr] = L::from(Hs[j][i] - L::f(hi));
+        for (int q = 0; q < PB; ++q) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const E hi = L::from(Hs[j][q][i]);
+            sHT[kPB * q + 4 * lq + i][16 * m + lr] = hi;
+            if constexpr (kBF) sHL[kPB * q + 4 * lq + i][16 * m + lr] = L::from(Hs[j][q][i] - L::f(hi));
+          }
         }
       }
     }
@@ -216,10 +237,11 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
   store_ht();
 
   // Staging of one chunk.  Thread tid covers B/C row s = tid / 4, quarter
-  // (tid % 4) of the NMAX states, and x row s, channels 4 (tid % 4) .. +3;
-  // the threads of wavefront 0 also load the step of token tid.  Every load
-  // goes through a buffer window that starts at the chunk and ends where the
-  // tensor's (batch, head or group) slice ends, so the loads are issued
+  // (tid % 4) of the NMAX states, and x row s, channels 16 q + 4 (tid % 4)
+  // .. +3 of each channel block q; every thread also loads the step of token
+  // (tid % 64) for its wavefront's scan.  Every load goes through a buffer
+  // window that starts at the chunk and ends where the chunk's rows of the
+  // tensor's (batch, head or group) slice end, so the loads are issued
   // unconditionally (past the end they read zero) and all at once; validity
   // is applied by selects when the values are written to LDS.
   const int srow = tid >> 2, squart = tid & 3;
@@ -230,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
   constexpr int kXw = 4 * ES / 4;              // dwords of a thread's 4 x values
   struct Stage {
     // element bits (scalar path) or packed dwords (vector path)
-    uint32_t b[kVec ? kQw : kQn], c[kVec ? kQw : kQn], x[kVec ? kXw : 4], dt, z[4];
+    uint32_t b[kVec ? kQw : kQn], c[kVec ? kQw : kQn], x[PB][kVec ? kXw : 4], dt, z[PB][4];
   };
   auto window = [&](const T* base, int64_t seq_stride, int inner, int t0) {
     // bytes from token t0's row to the end of the chunk's last row (at most
@@ -250,7 +272,6 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
     const __amdgpu_buffer_rsrc_t rd = window(dtg, p.dsl, 1, t0);
     const uint32_t ob = static_cast<uint32_t>((srow * p.Bsl + squart * kQn) * ES);
     const uint32_t oc = static_cast<uint32_t>((srow * p.Csl + squart * kQn) * ES);
-    const uint32_t ox = static_cast<uint32_t>((srow * p.xsl + 4 * squart) * ES);
     if constexpr (kVec) {
 #pragma unroll
       for (int k = 0; k < kQw / 4; ++k) {
@@ -262,14 +283,18 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
           st.c[4 * k + j] = vc[j];
         }
       }
-      if constexpr (kXw == 4) {
-        const v4u vx = __builtin_amdgcn_raw_buffer_load_b128(rx, ox, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) st.x[j] = vx[j];
-      } else {
-        const v2u vx = __builtin_amdgcn_raw_buffer_load_b64(rx, ox, 0, 0);
-        st.x[0] = vx[0];
-        st.x[1] = vx[1];
+      for (int q = 0; q < PB; ++q) {
+        const uint32_t ox = static_cast<uint32_t>((srow * p.xsl + kPB * q + 4 * squart) * ES);
+        if constexpr (kXw == 4) {
+          const v4u vx = __builtin_amdgcn_raw_buffer_load_b128(rx, ox, 0, 0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) st.x[q][j] = vx[j];
+        } else {
+          const v2u vx = __builtin_amdgcn_raw_buffer_load_b64(rx, ox, 0, 0);
+          st.x[q][0] = vx[0];
+          st.x[q][1] = vx[1];
+        }
       }
     } else {
 #pragma unroll
@@ -278,18 +303,28 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
         st.c[k] = Elem<T>::load(rc, oc + k * ES);
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) st.x[k] = Elem<T>::load(rx, ox + k * ES);
+      for (int q = 0; q < PB; ++q) {
+        const uint32_t ox = static_cast<uint32_t>((srow * p.xsl + kPB * q + 4 * squart) * ES);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) st.x[q][k] = Elem<T>::load(rx, ox + k * ES);
+      }
     }
     st.dt = Elem<T>::load(rd, static_cast<uint32_t>(lane * p.dsl * ES));
-    // the gate at this lane's output positions (t = 16 w + 4 lq + i, p = lr)
+    // the gate at this lane's output positions (t = 16 w + 4 lq + i,
+    // p = 16 q + lr)
     if (zg) {
       const __amdgpu_buffer_rsrc_t rz = window(zg, p.zsl, p.P - p0, t0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        st.z[i] = Elem<T>::load(rz, static_cast<uint32_t>(((16 * wave + 4 * lq + i) * p.zsl + lr) * ES));
+      for (int q = 0; q < PB; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          st.z[q][i] = Elem<T>::load(
+              rz, static_cast<uint32_t>(((16 * wave + 4 * lq + i) * p.zsl + kPB * q + lr) * ES));
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st.z[i] = 0u;
+      for (int q = 0; q < PB; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.z[q][i] = 0u;
     }
     return st;
   };
@@ -327,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
         sLa[lane] = la;
       }
     }
-    // ---- B (raw and decay-weighted), C, x^T of this chunk into LDS ----
+    // ---- B, C, x^T (raw and decay-weighted) of this chunk into LDS ----
     {
       const bool tv = srow < nv;
       if constexpr (kVec) {
@@ -341,14 +376,6 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
           *reinterpret_cast<uint4*>(&sC[srow][col]) =
               make_uint4(st.c[4 * k] & m, st.c[4 * k + 1] & m, st.c[4 * k + 2] & m, st.c[4 * k + 3] & m);
         }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int pp = 4 * squart + k;
-          const uint32_t v = ES == 2 ? (st.x[k / 2] >> (16 * (k % 2))) : st.x[k % kXw];
-          const E xv = raw(v, tv && p0 + pp < p.P);
-          sXT[pp][srow] = xv;
-          sXW[pp][srow] = L::from(L::f(xv) * w_row);
-        }
       } else {
 #pragma unroll
         for (int k = 0; k < kQn; ++k) {
@@ -357,10 +384,16 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
           sB[srow][n] = raw(st.b[k], ok);
           sC[srow][n] = raw(st.c[k], ok);
         }
+      }
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int pp = 4 * squart + k;
-          const E xv = raw(st.x[k], tv && p0 + pp < p.P);
+          const int pp = kPB * q + 4 * squart + k;
+          uint32_t v;
+          if constexpr (kVec) v = ES == 2 ? (st.x[q][k / 2] >> (16 * (k % 2))) : st.x[q][k % kXw];
+          else v = st.x[q][k];
+          const E xv = raw(v, tv && p0 + pp < p.P);
           sXT[pp][srow] = xv;
           sXW[pp][srow] = L::from(L::f(xv) * w_row);
         }
@@ -369,16 +402,20 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
     __syncthreads();
     // this chunk's gate, then the next chunk's loads fly while this one is
     // computed
-    uint32_t zr[4];
+    uint32_t zr[PB][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) zr[i] = st.z[i];
+    for (int q = 0; q < PB; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zr[q][i] = st.z[q][i];
     if (c + 1 < nchunks) st = load_stage(c + 1);
 
     // ---- outputs of tokens 16 w .. 16 w + 15 ----
     {
       const int tb = 16 * wave;
       const float la_t = sLa[tb + lr];
-      v4f y1 = {0.0f, 0.0f, 0.0f, 0.0f};
+      v4f y1[PB];
+#pragma unroll
+      for (int q = 0; q < PB; ++q) y1[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
       for (int sbk = 0; sbk <= wave; ++sbk) {
         // scores G[s][t] for s in block sbk, t in block wave: A = B (row s,
         // k = n), B operand = C^T (k = n, column t)
@@ -396,36 +433,49 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
         const float m1 = s0 + 1 <= t ? sc[1] * __builtin_amdgcn_exp2f(la_t - la_s.y) * dl_s.y : 0.0f;
         const float m2 = s0 + 2 <= t ? sc[2] * __builtin_amdgcn_exp2f(la_t - la_s.z) * dl_s.z : 0.0f;
         const float m3 = s0 + 3 <= t ? sc[3] * __builtin_amdgcn_exp2f(la_t - la_s.w) * dl_s.w : 0.0f;
-        // intra: A = M (row t, k = s), B operand = x (k = s, column p)
-        y1 = mma16<T>(tofrag<T>(m0, m1, m2, m3), ldsf<T>(&sXT[lr][s0]), y1);
+        // intra: A = M (row t, k = s), B operand = x (k = s, column p) of
+        // every channel block
+        const auto mf = tofrag<T>(m0, m1, m2, m3);
+#pragma unroll
+        for (int q = 0; q < PB; ++q) y1[q] = mma16<T>(mf, ldsf<T>(&sXT[kPB * q + lr][s0]), y1[q]);
       }
       // state: A = C (row t, k = n), B operand = H_in (k = n, column p)
-      v4f y2 = {0.0f, 0.0f, 0.0f, 0.0f};
+      v4f y2[PB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-      {
+      for (int q = 0; q < PB; ++q) y2[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
         const auto cf = ldsf<T>(&sC[tb + lr][16 * nb + 4 * lq]);
-        y2 = mma16<T>(cf, ldsf<T>(&sHT[lr][16 * nb + 4 * lq]), y2);
-        if constexpr (sizeof(E) == 2) y2 = mma16<T>(cf, ldsf<T>(&sHL[lr][16 * nb + 4 * lq]), y2);
+#pragma unroll
+        for (int q = 0; q < PB; ++q) {
+          y2[q] = mma16<T>(cf, ldsf<T>(&sHT[kPB * q + lr][16 * nb + 4 * lq]), y2[q]);
+          if constexpr (kBF) y2[q] = mma16<T>(cf, ldsf<T>(&sHL[kPB * q + lr][16 * nb + 4 * lq]), y2[q]);
+        }
       }
-      // lane holds t = tb + 4 lq + i, p = lr; stores of tokens past the end
-      // or channels past headdim go past the window's end and are dropped
+      // lane holds t = tb + 4 lq + i, p = 16 q + lr; stores of tokens past
+      // the end or channels past headdim go past the window's end and are
+      // dropped
       const __amdgpu_buffer_rsrc_t ro = window(og, p.osl, p.P - p0, t0);
       const uint32_t oend = static_cast<uint32_t>(
           (static_cast<int64_t>(std::min(p.L - 1 - t0, kQ - 1)) * p.osl + (p.P - p0)) * ES);
       const float4 la_o = *reinterpret_cast<const float4*>(&sLa[tb + 4 * lq]);
-      const float lav[4] = {la_o.x, la_o.y, la_o.z, la_o.w};
+      const float ea[4] = {__builtin_amdgcn_exp2f(la_o.x), __builtin_amdgcn_exp2f(la_o.y),
+                           __builtin_amdgcn_exp2f(la_o.z), __builtin_amdgcn_exp2f(la_o.w)};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tl = tb + 4 * lq + i;
-        const float xval = L::f(sXT[lr][tl]);
-        float y = y1[i] + __builtin_amdgcn_exp2f(lav[i]) * y2[i];
-        y = fmaf(Dh, xval, y);
-        const float gz = silu_f32(Elem<T>::f32(zr[i]));
-        y *= zg ? gz : 1.0f;
-        const bool ok = tl < nv && p0 + lr < p.P;
-        const uint32_t off = ok ? static_cast<uint32_t>((tl * p.osl + lr) * ES) : oend;
-        Elem<T>::store(ro, off, y);
+      for (int q = 0; q < PB; ++q) {
+        const int pl = kPB * q + lr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tl = tb + 4 * lq + i;
+          const float xval = L::f(sXT[pl][tl]);
+          float y = fmaf(ea[i], y2[q][i], y1[q][i]);
+          y = fmaf(Dh, xval, y);
+          const float gz = silu_f32(Elem<T>::f32(zr[q][i]));
+          y *= zg ? gz : 1.0f;
+          const bool ok = tl < nv && p0 + pl < p.P;
+          const uint32_t off = ok ? static_cast<uint32_t>((tl * p.osl + pl) * ES) : oend;
+          Elem<T>::store(ro, off, y);
+        }
       }
     }
 
@@ -436,16 +486,19 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
       for (int j = 0; j < NBW; ++j) {
         const int m = wave + kWaves * j;
         if (m < NB) {
-          v4f acc = Hs[j] * decay;
+          v4f acc[PB];
+#pragma unroll
+          for (int q = 0; q < PB; ++q) acc[q] = Hs[j][q] * decay;
 #pragma unroll
           for (int sbk = 0; sbk < kQ / 16; ++sbk) {
             // A = (w x)^T (row p, k = s); B operand = B (k = s, column n)
             const int s0 = 16 * sbk + 4 * lq, n = 16 * m + lr;
-            acc = mma16<T>(ldsf<T>(&sXW[lr][s0]),
-                           tofrag_bits<T>(sB[s0][n], sB[s0 + 1][n], sB[s0 + 2][n], sB[s0 + 3][n]),
-                           acc);
+            const auto bf = tofrag_bits<T>(sB[s0][n], sB[s0 + 1][n], sB[s0 + 2][n], sB[s0 + 3][n]);
+#pragma unroll
+            for (int q = 0; q < PB; ++q) acc[q] = mma16<T>(ldsf<T>(&sXW[kPB * q + lr][s0]), bf, acc[q]);
           }
-          Hs[j] = acc;
+#pragma unroll
+          for (int q = 0; q < PB; ++q) Hs[j][q] = acc[q];
         }
       }
     }
@@ -459,10 +512,13 @@ __global__ __launch_bounds__(kThreads) void ssd_fwd_kernel(SsdParams p) {
     for (int j = 0; j < NBW; ++j) {
       const int n = 16 * (wave + kWaves * j) + lr;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pp = 4 * lq + i;
-        if (n < N && p0 + pp < p.P)
-          p.last[((b * p.H + h) * p.P + p0 + pp) * static_cast<int64_t>(N) + n] = Hs[j][i];
+      for (int q = 0; q < PB; ++q) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pp = p0 + kPB * q + 4 * lq + i;
+          if (n < N && pp < p.P)
+            p.last[((b * p.H + h) * p.P + pp) * static_cast<int64_t>(N) + n] = Hs[j][q][i];
+        }
       }
     }
   }
@@ -474,14 +530,35 @@ __global__ void ssd_copy_state_kernel(const float* h0, float* last, int64_t n) {
   if (i < n) last[i] = h0 ? h0[i] : 0.0f;
 }
 
-template <typename T, int NMAX>
+// Blocks of 16 head channels per workgroup: up to the whole head, as far as
+// 64 KB of LDS allows (four with 64 bf16 states, else two), while the grid
+// still holds kMinGroups workgroups.
+#ifndef SSD_PB_FORCE
+constexpr int64_t kMinGroups = 512;
+int choose_pb(int P, int nmax, bool bf, int64_t heads) {
+  const int cap = (bf && nmax == 64) ? 4 : 2;
+  const int full = (P + kPB - 1) / kPB;
+  int pb = 1;
+  while (2 * pb <= cap && pb < full &&
+         heads * ((P + 2 * pb * kPB - 1) / (2 * pb * kPB)) >= kMinGroups)
+    pb *= 2;
+  return pb;
+}
+#else
+int choose_pb(int P, int nmax, bool bf, int64_t) {
+  const int cap = (bf && nmax == 64) ? 4 : 2;
+  return std::min(SSD_PB_FORCE, cap);
+}
+#endif
+
+template <typename T, int NMAX, int PB>
 void launch_n(bool softplus, bool vec, dim3 grid, const SsdParams& p, hipStream_t stream) {
   if (vec) {
-    if (softplus) ssd_fwd_kernel<T, NMAX, true, true><<<grid, dim3(kThreads), 0, stream>>>(p);
-    else ssd_fwd_kernel<T, NMAX, false, true><<<grid, dim3(kThreads), 0, stream>>>(p);
+    if (softplus) ssd_fwd_kernel<T, NMAX, true, true, PB><<<grid, dim3(kThreads), 0, stream>>>(p);
+    else ssd_fwd_kernel<T, NMAX, false, true, PB><<<grid, dim3(kThreads), 0, stream>>>(p);
   } else {
-    if (softplus) ssd_fwd_kernel<T, NMAX, true, false><<<grid, dim3(kThreads), 0, stream>>>(p);
-    else ssd_fwd_kernel<T, NMAX, false, false><<<grid, dim3(kThreads), 0, stream>>>(p);
+    if (softplus) ssd_fwd_kernel<T, NMAX, true, false, PB><<<grid, dim3(kThreads), 0, stream>>>(p);
+    else ssd_fwd_kernel<T, NMAX, false, false, PB><<<grid, dim3(kThreads), 0, stream>>>(p);
   }
 }
 
@@ -508,13 +585,14 @@ hipError_t launch_ssd_fwd(const ssm_ssd_args& a, hipStream_t stream) {
   p.L = static_cast<int>(a.seqlen); p.H = static_cast<int>(a.nheads);
   p.P = static_cast<int>(a.headdim); p.G = static_cast<int>(a.ngroups > 1 ? a.ngroups : 1);
   p.N = static_cast<int>(a.dstate);
-  p.pblocks = (p.P + kPB - 1) / kPB;
-  const int64_t nblocks = a.batch * a.nheads * p.pblocks;
-  if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const dim3 grid(static_cast<unsigned>(nblocks));
   const bool sp = a.dt_softplus != 0;
   const bool bf = a.io_dtype == SSM_BF16;
   const int nmax = (bf && a.dstate > 64) ? 128 : 64;
+  const int pbk = choose_pb(p.P, nmax, bf, a.batch * a.nheads);
+  p.pblocks = (p.P + kPB * pbk - 1) / (kPB * pbk);
+  const int64_t nblocks = a.batch * a.nheads * p.pblocks;
+  if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(nblocks));
   // vector staging: 16-byte B/C row quarters, 8- (bf16) or 16-byte (fp32) x
   // rows of four channels
   const int esz = bf ? 2 : 4;
@@ -529,11 +607,18 @@ hipError_t launch_ssd_fwd(const ssm_ssd_args& a, hipStream_t stream) {
                    a.C_seq_stride % bw == 0 && (G == 1 || a.C_group_stride % bw == 0) &&
                    al(a.x, xw * esz) && a.x_batch_stride % xw == 0 && a.x_seq_stride % xw == 0 &&
                    a.x_head_stride % xw == 0 && a.headdim % xw == 0;
-  if (bf) {
-    if (nmax == 64) launch_n<uint16_t, 64>(sp, vec, grid, p, stream);
-    else launch_n<uint16_t, 128>(sp, vec, grid, p, stream);
+  if (bf && nmax == 64) {
+    switch (pbk) {
+      case 4: launch_n<uint16_t, 64, 4>(sp, vec, grid, p, stream); break;
+      case 2: launch_n<uint16_t, 64, 2>(sp, vec, grid, p, stream); break;
+      default: launch_n<uint16_t, 64, 1>(sp, vec, grid, p, stream); break;
+    }
+  } else if (bf) {
+    if (pbk == 2) launch_n<uint16_t, 128, 2>(sp, vec, grid, p, stream);
+    else launch_n<uint16_t, 128, 1>(sp, vec, grid, p, stream);
   } else {
-    launch_n<float, 64>(sp, vec, grid, p, stream);
+    if (pbk == 2) launch_n<float, 64, 2>(sp, vec, grid, p, stream);
+    else launch_n<float, 64, 1>(sp, vec, grid, p, stream);
   }
   return hipGetLastError();
 }

@@ -86,6 +86,21 @@ def test_ssd_matches_oracle(batch, L, H, P, G, N, io):
     check(inp, io, f"b{batch} L{L} H{H} P{P} G{G} N{N} {io} no h0")
 
 
+@pytest.mark.parametrize("batch,L,H,P,G,N,io", [
+    (2, 100, 256, 48, 4, 64, "bf16"),   # four blocks, the last one masked
+    (2, 70, 256, 64, 2, 128, "bf16"),   # two blocks, 128 states
+    (2, 90, 256, 40, 1, 64, "f32"),     # two blocks, the second ragged
+    (2, 66, 256, 32, 4, 40, "f32"),     # two blocks, element-wise staging
+])
+def test_ssd_channel_blocks_per_workgroup(batch, L, H, P, G, N, io):
+    """Enough (batch, head) pairs (512) that a workgroup takes several blocks
+    of 16 head channels (sharing the chunk's scores and B/C staging), with
+    head sizes that leave channel blocks partly or wholly past headdim."""
+    inp = si.ssd_inputs(batch, L, H, P, G, N, io_dtype=io, seed=L + P + N)
+    h0 = np.random.default_rng(P).standard_normal((batch, H, P, N)).astype(np.float32)
+    check(inp, io, f"blocks b{batch} L{L} H{H} P{P} G{G} N{N} {io}", h0=h0)
+
+
 @pytest.mark.parametrize("gate,skip,bias,softplus", [
     (False, False, False, True), (True, True, True, False), (False, True, False, True)])
 def test_ssd_optional_inputs(gate, skip, bias, softplus):
