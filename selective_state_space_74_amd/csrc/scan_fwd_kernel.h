@@ -73,6 +73,7 @@ constexpr int kGT = kT * kGB;       // tokens per group
 static_assert(4 % kGB == 0, "the steady-state loop runs four blocks at a time");
 constexpr int kGPitch = kGT + 4;    // LDS pitch (floats) of one state's group of B / C
 constexpr int kPitch = 20;          // LDS pitch (floats) of one state's readout partials
+constexpr int kCPitch = kN + 4;     // LDS pitch (floats) of one token's C (token-major tile)
 constexpr int kPartRow = kN * kPitch + 16;  // floats per channel of readout partials
 
 enum class Mode { kScan, kAggregate };
@@ -151,9 +152,15 @@ struct Wave {
   uint32_t oco;
   float (*sB)[kN * S][kGPitch];   // [2][16S][kGPitch], shared by the workgroup
   float (*sC)[kN * S][kGPitch];
+  float (*sCt)[kGT][kCPitch];     // [2][kGT][kCPitch] token-major C (kOwnerC)
   float (*sP)[kPartRow];          // this wavefront's [kRows][kPartRow]
 
   static constexpr int E = Elem<T>::kSize;
+  // One state slot with the shared tile: the state lanes hand their h to
+  // LDS and the owner of each token contracts it with the token's C column
+  // (16 FMAs in place of 16 products on the state lanes and a 15-add sum);
+  // C is then staged token-major.
+  static constexpr bool kOwnerC = S == 1 && !kLane && M == Mode::kScan;
 
   __device__ __forceinline__ uint32_t skip(int k) const {
     return static_cast<uint32_t>(t_beg + k * kT) * E;
@@ -201,7 +208,8 @@ struct Wave {
       for (int i = 0; i < kGB; ++i) {
         const float bv = Elem<T>::f32(r.b[q][i]);
         sB[g & 1][st + kN * q][col + i * kT] = t + i * kT < t_end ? bv : 0.0f;
-        if (M == Mode::kScan) sC[g & 1][st + kN * q][col + i * kT] = Elem<T>::f32(r.c[q][i]);
+        if constexpr (kOwnerC) sCt[g & 1][col + i * kT][st] = Elem<T>::f32(r.c[q][i]);
+        else if (M == Mode::kScan) sC[g & 1][st + kN * q][col + i * kT] = Elem<T>::f32(r.c[q][i]);
       }
     }
   }
@@ -218,7 +226,7 @@ struct Wave {
       for (int i = 0; i < kT / 4; ++i) {
         const float4 x = *reinterpret_cast<const float4*>(&sB[buf][col + kN * q][tb + 4 * i]);
         bv[4 * i] = x.x; bv[4 * i + 1] = x.y; bv[4 * i + 2] = x.z; bv[4 * i + 3] = x.w;
-        if (M == Mode::kScan) {
+        if (M == Mode::kScan && !kOwnerC) {
           const float4 y = *reinterpret_cast<const float4*>(&sC[buf][col + kN * q][tb + 4 * i]);
           cv[4 * i] = y.x; cv[4 * i + 1] = y.y; cv[4 * i + 2] = y.z; cv[4 * i + 3] = y.w;
         }
@@ -295,7 +303,7 @@ struct Wave {
     float bv[kT], cv[kT];
     bc<kMask>(k, 0, bv, cv);
     float ysum = 0.0f;
-    if (M == Mode::kScan) {
+    if (M == Mode::kScan && !kOwnerC) {
       // unconditional: at k = 0 the value is never used; summed right away so
       // that one register, not sixteen, lives across the scan
       float part[kN];
@@ -364,14 +372,31 @@ struct Wave {
         h[q] = fmaf(e, h[q], w);
         if (M == Mode::kScan) {
           constexpr int i = S == 1 ? j % 4 : j;
-          pk[i] = q == 0 ? cv[j] * h[q] : fmaf(cv[j], h[q], pk[i]);        // C_n h_n
+          if constexpr (kOwnerC) pk[i] = h[q];                               // h_n
+          else pk[i] = q == 0 ? cv[j] * h[q] : fmaf(cv[j], h[q], pk[i]);   // C_n h_n
           if constexpr (q == S - 1 && j % 4 == 3)
             *reinterpret_cast<float4*>(&sP[row][col * kPitch + j - 3]) =
                 make_float4(pk[i - 3], pk[i - 2], pk[i - 1], pk[i]);
         }
       });
     });
-    if (M == Mode::kScan) {
+    if constexpr (kOwnerC) {
+      // this block's readout right away: y = sum_n C_n h_n from the h the
+      // state lanes just left in LDS and this token's C column of the tile
+      // (still this group's buffer: the other one is staged next)
+      const float* cc = &sCt[(k / kGB) & 1][(k % kGB) * kT + col][0];
+      float cl[kN], part[kN];
+#pragma unroll
+      for (int i = 0; i < kN / 4; ++i) {
+        const float4 y = *reinterpret_cast<const float4*>(cc + 4 * i);
+        cl[4 * i] = y.x; cl[4 * i + 1] = y.y; cl[4 * i + 2] = y.z; cl[4 * i + 3] = y.w;
+      }
+#pragma unroll
+      for (int n = 0; n < kN; ++n) part[n] = sP[row][n * kPitch + col];
+#pragma unroll
+      for (int n = 0; n < kN; ++n) ysum = fmaf(cl[n], part[n], ysum);
+      finish<kMask>(k, Q, uv, ysum);
+    } else if (M == Mode::kScan) {
       if (!kMask) finish<false>(k - 1, P, uprev, ysum);
       else if (k > 0) finish<true>(k - 1, P, uprev, ysum);
     }
@@ -397,7 +422,9 @@ template <typename T, Mode M, bool kSoftplus, int KP, int S, int kLane>
 __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   constexpr int kTile = kLane ? 1 : 2;
   __shared__ __align__(16) float sB[kTile][kN * S][kGPitch];
-  __shared__ __align__(16) float sC[M == Mode::kScan ? kTile : 1][kN * S][kGPitch];
+  constexpr bool kOC = Wave<T, M, kSoftplus, KP, S, kLane>::kOwnerC;
+  __shared__ __align__(16) float sC[M == Mode::kScan && !kOC ? kTile : 1][kN * S][kGPitch];
+  __shared__ __align__(16) float sCt[kOC ? 2 : 1][kOC ? kGT : 1][kCPitch];
   __shared__ __align__(16) float sP[M == Mode::kScan ? kWaves : 1][kRows][kPartRow];
   __shared__ double sSum[M == Mode::kScan ? 1 : kWaves][kRows][kT];
 
@@ -494,6 +521,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   w.bias = p.bias ? p.bias[dc] : 0.0f;
   w.Dd = p.D ? p.D[dc] : 0.0f;
   w.sB = sB; w.sC = sC; w.sP = sP[M == Mode::kScan ? wave : 0];
+  w.sCt = reinterpret_cast<float (*)[kGT][kCPitch]>(&sCt[0][0][0]);
 
   // conv path: tap weights by lag, bias, the inputs just before this
   // segment (x_{t_beg-16+col}: from the conv state at the sequence start,
@@ -572,15 +600,17 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   if (k + 3 < nblk) w.template iter<true, false>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev);
 
   if (M == Mode::kScan) {
-    // finish the last block: its partials are in LDS, its raw inputs in buffer
-    // (nblk - 1) % 4
-    const int kl = nblk - 1;
-    const int r = kl & 3;
-    const Raw last = r == 0 ? buf0 : r == 1 ? buf1 : r == 2 ? buf2 : buf3;
-    float ysum = 0.0f;
+    if constexpr (!kOC) {
+      // finish the last block: its partials are in LDS, its raw inputs in
+      // buffer (nblk - 1) % 4
+      const int kl = nblk - 1;
+      const int r = kl & 3;
+      const Raw last = r == 0 ? buf0 : r == 1 ? buf1 : r == 2 ? buf2 : buf3;
+      float ysum = 0.0f;
 #pragma unroll
-    for (int n = 0; n < kN; ++n) ysum += w.sP[row][n * kPitch + col];
-    w.template finish<true>(kl, last, uprev, ysum);
+      for (int n = 0; n < kN; ++n) ysum += w.sP[row][n * kPitch + col];
+      w.template finish<true>(kl, last, uprev, ysum);
+    }
     if (vrow && p.last_state && g == p.nseg - 1) {
 #pragma unroll
       for (int q = 0; q < S; ++q) {
