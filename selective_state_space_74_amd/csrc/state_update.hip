@@ -13,8 +13,10 @@
 // consecutive states each (R rounded up to 1, 2, 4, 8 or 16 for N up to 64),
 // so every state access of a wavefront is one contiguous run (one lane per
 // channel with 64 B per lane measured ~35% slower on gfx950).  The grid is
-// (blocks of 64 channels, batch rows): no thread divides to find its (batch,
-// channel).  Aligned layouts with N = 4R (the usual contiguous ones) take a
+// (blocks of 64 channels, batch rows or pairs of them): no thread divides to
+// find its (batch, channel).  With a large enough grid a thread takes two
+// batch rows of its channel: A, bias and D are loaded once for both, and
+// both rows' state and inputs are in flight together.  Aligned layouts with N = 4R (the usual contiguous ones) take a
 // branch-free instantiation with vector accesses; others take the
 // element-wise one, masked to the N real states.  The readout is reduced
 // over the quad with two DPP quad permutations.  B and C are those of the
@@ -27,6 +29,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChannelsPerBlock = kThreads / 4;
 constexpr int kMaxConv = SSM_MAX_CONV;
+// batch rows per thread for the plain update (vector path, up to 16 states
+// per channel), when the grid keeps enough workgroups
+constexpr int kRowsPerThread = 2;
+constexpr int64_t kMinBlocksRows = 2048;
 
 struct UpdateParams {
   float* state;
@@ -109,10 +115,15 @@ __device__ __forceinline__ void storeR(float* p, const float (&v)[R], int nvalid
 // DPP quad permute (the newest, x, at q = K-1), and the quad sums the four
 // weighted taps.  CONV == 2 (width 5..8): every lane of the quad forms the
 // whole sum and lane q writes back the elements k = q, q + 4.
-template <typename T, bool VEC, int CONV, int R>
+// NBB: batch rows per thread (without the conv branch).  The channel's A,
+// bias and D are loaded once for all of them, and every row's loads are
+// issued before the first row is computed, so a wavefront keeps NBB times
+// the bytes in flight.
+template <typename T, bool VEC, int CONV, int R, int NBB>
 __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p) {
+  static_assert(CONV == 0 || NBB == 1, "the conv branch runs one batch row per thread");
   const int q = threadIdx.x & 3;
-  const int64_t b = blockIdx.y;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.y) * NBB;
   const int64_t d0 = static_cast<int64_t>(blockIdx.x) * kChannelsPerBlock + (threadIdx.x >> 2);
   const bool ok = d0 < p.dim;
   const int64_t d = ok ? d0 : p.dim - 1;   // clamped: loads stay in bounds
@@ -121,39 +132,47 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p) 
   // B/C group of the channel (a uniform branch: no division with one group)
   int64_t g = 0;
   if (p.cpg != p.dim) g = d / p.cpg;
-  float* sp = p.state + b * p.ssb + d * p.ssd + R * q;
-  float s[R], a[R], bb[R], cc[R];
-  loadR<float, VEC, R>(sp, s, nv);
+  float a[R];
   loadR<float, VEC, R>(p.A + d * p.Asd + R * q, a, nv);
-  loadR<T, VEC, R>(static_cast<const T*>(p.B) + b * p.Bsb + g * p.Bsg + R * q, bb, nv);
-  loadR<T, VEC, R>(static_cast<const T*>(p.C) + b * p.Csb + g * p.Csg + R * q, cc, nv);
-  float xv = io<T>::load(static_cast<const T*>(p.x) + b * p.xsb + d);
+  const float bias = p.bias ? p.bias[d] : 0.0f;
+  const float Dd = p.D ? p.D[d] : 0.0f;
+  float s[NBB][R], bb[NBB][R], cc[NBB][R], xv[NBB], dtv[NBB], zv[NBB];
+#pragma unroll
+  for (int i = 0; i < NBB; ++i) {
+    const int64_t b = min(b0 + i, p.batch - 1);   // rows past the batch repeat the last
+    loadR<float, VEC, R>(p.state + b * p.ssb + d * p.ssd + R * q, s[i], nv);
+    loadR<T, VEC, R>(static_cast<const T*>(p.B) + b * p.Bsb + g * p.Bsg + R * q, bb[i], nv);
+    loadR<T, VEC, R>(static_cast<const T*>(p.C) + b * p.Csb + g * p.Csg + R * q, cc[i], nv);
+    xv[i] = io<T>::load(static_cast<const T*>(p.x) + b * p.xsb + d);
+    dtv[i] = io<T>::load(static_cast<const T*>(p.dt) + b * p.dtsb + d);
+    zv[i] = p.z ? io<T>::load(static_cast<const T*>(p.z) + b * p.zsb + d) : 0.0f;
+  }
   if constexpr (CONV == 1) {
     // causal conv of the block's conv branch: shift in x, then the weighted
     // sum of the K newest inputs (Mamba model notes, section 4.3)
     const int K = p.K;
-    float* cs = p.conv_state + (b * p.dim + d) * K;
+    float* cs = p.conv_state + (b0 * p.dim + d) * K;
     const int qk = min(q, K - 1);                     // lanes past K stay in the row
     const float old = cs[qk];
     const float nb = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(old), 0xF9, 0xf, 0xf, true));
-    const float nv = q == K - 1 ? xv : nb;            // element q of the shifted state
-    float acc = q < K ? p.conv_w[d * K + q] * nv : 0.0f;
+    const float nvx = q == K - 1 ? xv[0] : nb;        // element q of the shifted state
+    float acc = q < K ? p.conv_w[d * K + q] * nvx : 0.0f;
     acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xf, 0xf, true));
     acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xf, 0xf, true));
     if (p.conv_b) acc += p.conv_b[d];
-    if (ok && q < K) cs[q] = nv;
-    xv = p.conv_silu ? silu_f32(acc) : acc;
+    if (ok && q < K) cs[q] = nvx;
+    xv[0] = p.conv_silu ? silu_f32(acc) : acc;
   } else if constexpr (CONV == 2) {
     const int K = p.K;
-    float* cs = p.conv_state + (b * p.dim + d) * K;
+    float* cs = p.conv_state + (b0 * p.dim + d) * K;
     const float* cw = p.conv_w + d * K;
     float acc = p.conv_b ? p.conv_b[d] : 0.0f;
-    float nv[kMaxConv];
+    float nvx[kMaxConv];
 #pragma unroll
     for (int k = 0; k < kMaxConv; ++k) {
       if (k < K) {
-        nv[k] = k + 1 < K ? cs[k + 1] : xv;
-        acc = fmaf(cw[k], nv[k], acc);
+        nvx[k] = k + 1 < K ? cs[k + 1] : xv[0];
+        acc = fmaf(cw[k], nvx[k], acc);
       }
     }
     // all four lanes have read the old state before any lane writes
@@ -161,56 +180,71 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p) 
     if (ok) {
 #pragma unroll
       for (int k = 0; k < kMaxConv; ++k)
-        if (k < K && (k & 3) == q) cs[k] = nv[k];
+        if (k < K && (k & 3) == q) cs[k] = nvx[k];
     }
-    xv = p.conv_silu ? silu_f32(acc) : acc;
+    xv[0] = p.conv_silu ? silu_f32(acc) : acc;
   }
-  const float dtv = io<T>::load(static_cast<const T*>(p.dt) + b * p.dtsb + d);
-  const float zv = p.z ? io<T>::load(static_cast<const T*>(p.z) + b * p.zsb + d) : 0.0f;
 
-  float dl = dtv + (p.bias ? p.bias[d] : 0.0f);
-  if (p.softplus) dl = softplus_f32(dl);
-  const float dlx = dl * xv;
-  float y = 0.0f;
 #pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const float e = __builtin_amdgcn_exp2f(dl * (a[i] * kLog2e));
-    s[i] = fmaf(e, s[i], dlx * bb[i]);
-    y = fmaf(cc[i], s[i], y);   // padding states are 0 with C = 0
-  }
-  if (ok) storeR<VEC, R>(sp, s, nv);
-  // quad sum: lanes (0,1,2,3) <- (1,0,3,2), then <- (2,3,0,1)
-  y += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xf, 0xf, true));
-  y += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0x4E, 0xf, 0xf, true));
-  if (ok && q == 0) {
-    if (p.D) y = fmaf(p.D[d], xv, y);
-    if (p.z) y *= silu_f32(zv);
-    io<T>::store(static_cast<T*>(p.out) + b * p.osb + d, y);
+  for (int i = 0; i < NBB; ++i) {
+    const int64_t b = b0 + i;
+    float dl = dtv[i] + bias;
+    if (p.softplus) dl = softplus_f32(dl);
+    const float dlx = dl * xv[i];
+    float y = 0.0f;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float e = __builtin_amdgcn_exp2f(dl * (a[j] * kLog2e));
+      s[i][j] = fmaf(e, s[i][j], dlx * bb[i][j]);
+      y = fmaf(cc[i][j], s[i][j], y);   // padding states are 0 with C = 0
+    }
+    const bool okb = ok && b < p.batch;
+    if (okb) storeR<VEC, R>(p.state + b * p.ssb + d * p.ssd + R * q, s[i], nv);
+    // quad sum: lanes (0,1,2,3) <- (1,0,3,2), then <- (2,3,0,1)
+    y += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0xB1, 0xf, 0xf, true));
+    y += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y), 0x4E, 0xf, 0xf, true));
+    if (okb && q == 0) {
+      y = fmaf(Dd, xv[i], y);
+      if (p.z) y *= silu_f32(zv[i]);
+      io<T>::store(static_cast<T*>(p.out) + b * p.osb + d, y);
+    }
   }
 }
 
 template <typename T, bool VEC, int R>
-void launch_v(int conv, dim3 grid, dim3 block, const UpdateParams& p, hipStream_t stream) {
-  if (conv == 0) state_update_kernel<T, VEC, 0, R><<<grid, block, 0, stream>>>(p);
-  else if (conv == 1) state_update_kernel<T, VEC, 1, R><<<grid, block, 0, stream>>>(p);
-  else state_update_kernel<T, VEC, 2, R><<<grid, block, 0, stream>>>(p);
+void launch_v(int conv, bool rows, dim3 grid, dim3 block, const UpdateParams& p,
+              hipStream_t stream) {
+  if (conv == 0) {
+    if constexpr (VEC && R <= 4) {
+      if (rows) {
+        state_update_kernel<T, VEC, 0, R, kRowsPerThread><<<grid, block, 0, stream>>>(p);
+        return;
+      }
+    }
+    state_update_kernel<T, VEC, 0, R, 1><<<grid, block, 0, stream>>>(p);
+  } else if (conv == 1) {
+    state_update_kernel<T, VEC, 1, R, 1><<<grid, block, 0, stream>>>(p);
+  } else {
+    state_update_kernel<T, VEC, 2, R, 1><<<grid, block, 0, stream>>>(p);
+  }
 }
 
 template <typename T, int R>
-void launch_r(bool vec, int conv, dim3 grid, dim3 block, const UpdateParams& p, hipStream_t stream) {
-  if (vec) launch_v<T, true, R>(conv, grid, block, p, stream);
-  else launch_v<T, false, R>(conv, grid, block, p, stream);
+void launch_r(bool vec, int conv, bool rows, dim3 grid, dim3 block, const UpdateParams& p,
+              hipStream_t stream) {
+  if (vec) launch_v<T, true, R>(conv, rows, grid, block, p, stream);
+  else launch_v<T, false, R>(conv, rows, grid, block, p, stream);
 }
 
 template <typename T>
-void launch_t(int r, bool vec, int conv, dim3 grid, dim3 block, const UpdateParams& p,
-              hipStream_t stream) {
+void launch_t(int r, bool vec, int conv, bool rows, dim3 grid, dim3 block,
+              const UpdateParams& p, hipStream_t stream) {
   switch (r) {
-    case 1: launch_r<T, 1>(vec, conv, grid, block, p, stream); break;
-    case 2: launch_r<T, 2>(vec, conv, grid, block, p, stream); break;
-    case 4: launch_r<T, 4>(vec, conv, grid, block, p, stream); break;
-    case 8: launch_r<T, 8>(vec, conv, grid, block, p, stream); break;
-    default: launch_r<T, 16>(vec, conv, grid, block, p, stream); break;
+    case 1: launch_r<T, 1>(vec, conv, rows, grid, block, p, stream); break;
+    case 2: launch_r<T, 2>(vec, conv, rows, grid, block, p, stream); break;
+    case 4: launch_r<T, 4>(vec, conv, rows, grid, block, p, stream); break;
+    case 8: launch_r<T, 8>(vec, conv, rows, grid, block, p, stream); break;
+    default: launch_r<T, 16>(vec, conv, rows, grid, block, p, stream); break;
   }
 }
 
@@ -249,11 +283,14 @@ hipError_t launch_state_update(const ssm_update_args& a, hipStream_t stream) {
   p.conv_silu = a.conv_silu;
   const int64_t xblocks = (a.dim + kChannelsPerBlock - 1) / kChannelsPerBlock;
   if (xblocks > 0x7fffffff || a.batch > 65535) return hipErrorInvalidConfiguration;
-  const dim3 grid(static_cast<unsigned>(xblocks), static_cast<unsigned>(a.batch));
+  const bool rows = a.conv_weight == nullptr && vec && r <= 4 &&
+                    xblocks * ((a.batch + kRowsPerThread - 1) / kRowsPerThread) >= kMinBlocksRows;
+  const int64_t ybl = rows ? (a.batch + kRowsPerThread - 1) / kRowsPerThread : a.batch;
+  const dim3 grid(static_cast<unsigned>(xblocks), static_cast<unsigned>(ybl));
   const dim3 block(kThreads);
   const int conv = a.conv_weight == nullptr ? 0 : (a.d_conv <= 4 ? 1 : 2);
-  if (a.io_dtype == SSM_BF16) launch_t<uint16_t>(r, vec, conv, grid, block, p, stream);
-  else launch_t<float>(r, vec, conv, grid, block, p, stream);
+  if (a.io_dtype == SSM_BF16) launch_t<uint16_t>(r, vec, conv, rows, grid, block, p, stream);
+  else launch_t<float>(r, vec, conv, rows, grid, block, p, stream);
   return hipGetLastError();
 }
 

@@ -238,6 +238,27 @@ def test_decode_single_step_random_state(io):
     assert e <= TOL[io] and es <= TOL[io]
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_decode_batch_rows_per_thread_ragged(io):
+    """A grid large enough that each thread takes two batch rows (odd batch:
+    the last pair has one row; dim not a multiple of the 64-channel block),
+    two steps from a random state."""
+    h = si.decode_inputs_host(51, 5100, io_dtype=io, steps=2, seed=23, random_state=True)
+    d = si.to_torch(h, DEV)
+    state = d["state"].clone()
+    outs = gpu_decode_steps(d, 2, state)
+    rstate = h["state"]
+    for s in range(2):
+        ref, rstate = oracle.state_update(rstate, h["x"][s], h["dt"][s], h["A"], h["B"][s],
+                                          h["C"][s], D=h["D"], z=h["z"][s], dt_bias=h["dt_bias"])
+        e = row_rel_err(to_np(outs[s]), ref, axis=1)
+        print(f"[decode rows {io} step {s}] err_out={e:.3e}", flush=True)
+        assert e <= TOL[io]
+    es = row_rel_err(to_np(state), rstate)
+    print(f"[decode rows {io}] err_state={es:.3e}", flush=True)
+    assert es <= TOL[io]
+
+
 def test_decode_equals_scan_on_gpu():
     """L decode steps reproduce the scan's outputs and final state (both HIP)."""
     inp = si.scan_inputs(2, 48, 64, io_dtype="f32", seed=31)
