@@ -21,15 +21,16 @@ __global__ void copy_state_kernel(const float* h0, float* last, int64_t n) {
 }
 
 // Segments per sequence: cut only when the batch x channel groups alone leave
-// the machine short of wavefronts, and keep segments long enough that the
-// extra aggregate pass and the fold stay small.
-constexpr int64_t kTargetGroups = 768;    // 3 wavefronts per SIMD on 256 CUs
+// the machine short of wavefronts, as many as fit one residency round of the
+// one-slot kernels (5 workgroups per CU), and keep segments long enough that
+// the extra aggregate pass and the fold stay small.
+constexpr int64_t kTargetGroups = 1280;   // 5 wavefronts per SIMD on 256 CUs
 constexpr int64_t kMinSegLen = 8192;
 constexpr int kMaxSeg = 64;
 
 int choose_segments(int64_t groups, int64_t L) {
   if (groups >= kTargetGroups / 2) return 1;
-  int64_t g = (kTargetGroups + groups - 1) / groups;
+  int64_t g = kTargetGroups / groups;
   g = std::min<int64_t>(g, std::max<int64_t>(1, L / kMinSegLen));
   return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(g, kMaxSeg)));
 }
