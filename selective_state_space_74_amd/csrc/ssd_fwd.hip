@@ -68,7 +68,10 @@ struct SsdParams {
   const float* h0;
   float* last;
   void* out;
-  int64_t xsb, xsl, xsh, dsb, dsl, zsb, zsl, zsh, Bsb, Bsl, Bsg, Csb, Csl, Csg, osb, osl, osh;
+  int64_t xsb, xsh, dsb, zsb, zsh, Bsb, Bsg, Csb, Csg, osb, osh;
+  // byte strides between consecutive tokens (a chunk's 64 rows span less
+  // than 2^31 bytes, so these and every in-chunk offset are 32-bit)
+  uint32_t xsl, dsl, zsl, Bsl, Csl, osl;
   int L, H, P, G, N;
   int pblocks;   // workgroups per head: ceil(P / (16 PB))
 };
@@ -254,15 +257,22 @@ void ssd_fwd_kernel(SsdParams p) {
     // element bits (scalar path) or packed dwords (vector path)
     uint32_t b[kVec ? kQw : kQn], c[kVec ? kQw : kQn], x[PB][kVec ? kXw : 4], dt, z[PB][4];
   };
-  auto window = [&](const T* base, int64_t seq_stride, int inner, int t0) {
+  auto window = [&](const T* base, uint32_t seq_bytes, int inner, int t0) {
     // bytes from token t0's row to the end of the chunk's last row (at most
     // 64 rows; the host keeps that below 2^31); empty past the sequence
-    const int64_t rows = std::min(p.L - 1 - t0, kQ - 1);
-    const int64_t bytes = rows < 0 ? 0 : (rows * seq_stride + inner) * ES;
+    const int rows = std::min(p.L - 1 - t0, kQ - 1);
+    const uint32_t bytes = rows < 0 ? 0u : static_cast<uint32_t>(rows) * seq_bytes + inner * ES;
     return __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<T*>(base + static_cast<int64_t>(t0) * seq_stride), 0,
-        static_cast<int>(bytes), kRsrcWord3);
+        const_cast<char*>(reinterpret_cast<const char*>(base) + static_cast<int64_t>(t0) * seq_bytes),
+        0, static_cast<int>(bytes), kRsrcWord3);
   };
+  // per-lane byte offsets inside a chunk's windows (the same every chunk)
+  const uint32_t ob = srow * p.Bsl + squart * kQn * ES;
+  const uint32_t oc = srow * p.Csl + squart * kQn * ES;
+  const uint32_t ox0 = srow * p.xsl + 4 * squart * ES;     // + 16 q ES for block q
+  const uint32_t odt = lane * p.dsl;
+  const uint32_t oz0 = (16 * wave + 4 * lq) * p.zsl + lr * ES;   // + i zsl + 16 q ES
+  const uint32_t oo0 = (16 * wave + 4 * lq) * p.osl + lr * ES;   // likewise for out
   auto load_stage = [&](int c) {
     Stage st;
     const int t0 = c * kQ;
@@ -270,8 +280,6 @@ void ssd_fwd_kernel(SsdParams p) {
     const __amdgpu_buffer_rsrc_t rc = window(Cg, p.Csl, N, t0);
     const __amdgpu_buffer_rsrc_t rx = window(xg, p.xsl, p.P - p0, t0);
     const __amdgpu_buffer_rsrc_t rd = window(dtg, p.dsl, 1, t0);
-    const uint32_t ob = static_cast<uint32_t>((srow * p.Bsl + squart * kQn) * ES);
-    const uint32_t oc = static_cast<uint32_t>((srow * p.Csl + squart * kQn) * ES);
     if constexpr (kVec) {
 #pragma unroll
       for (int k = 0; k < kQw / 4; ++k) {
@@ -285,7 +293,7 @@ void ssd_fwd_kernel(SsdParams p) {
       }
 #pragma unroll
       for (int q = 0; q < PB; ++q) {
-        const uint32_t ox = static_cast<uint32_t>((srow * p.xsl + kPB * q + 4 * squart) * ES);
+        const uint32_t ox = ox0 + kPB * q * ES;
         if constexpr (kXw == 4) {
           const v4u vx = __builtin_amdgcn_raw_buffer_load_b128(rx, ox, 0, 0);
 #pragma unroll
@@ -304,12 +312,12 @@ void ssd_fwd_kernel(SsdParams p) {
       }
 #pragma unroll
       for (int q = 0; q < PB; ++q) {
-        const uint32_t ox = static_cast<uint32_t>((srow * p.xsl + kPB * q + 4 * squart) * ES);
+        const uint32_t ox = ox0 + kPB * q * ES;
 #pragma unroll
         for (int k = 0; k < 4; ++k) st.x[q][k] = Elem<T>::load(rx, ox + k * ES);
       }
     }
-    st.dt = Elem<T>::load(rd, static_cast<uint32_t>(lane * p.dsl * ES));
+    st.dt = Elem<T>::load(rd, odt);
     // the gate at this lane's output positions (t = 16 w + 4 lq + i,
     // p = 16 q + lr)
     if (zg) {
@@ -318,8 +326,7 @@ void ssd_fwd_kernel(SsdParams p) {
       for (int q = 0; q < PB; ++q)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          st.z[q][i] = Elem<T>::load(
-              rz, static_cast<uint32_t>(((16 * wave + 4 * lq + i) * p.zsl + kPB * q + lr) * ES));
+          st.z[q][i] = Elem<T>::load(rz, oz0 + i * p.zsl + kPB * q * ES);
     } else {
 #pragma unroll
       for (int q = 0; q < PB; ++q)
@@ -456,8 +463,8 @@ void ssd_fwd_kernel(SsdParams p) {
       // the end or channels past headdim go past the window's end and are
       // dropped
       const __amdgpu_buffer_rsrc_t ro = window(og, p.osl, p.P - p0, t0);
-      const uint32_t oend = static_cast<uint32_t>(
-          (static_cast<int64_t>(std::min(p.L - 1 - t0, kQ - 1)) * p.osl + (p.P - p0)) * ES);
+      const uint32_t oend = static_cast<uint32_t>(std::min(p.L - 1 - t0, kQ - 1)) * p.osl +
+                            (p.P - p0) * ES;
       const float4 la_o = *reinterpret_cast<const float4*>(&sLa[tb + 4 * lq]);
       const float ea[4] = {__builtin_amdgcn_exp2f(la_o.x), __builtin_amdgcn_exp2f(la_o.y),
                            __builtin_amdgcn_exp2f(la_o.z), __builtin_amdgcn_exp2f(la_o.w)};
@@ -473,7 +480,7 @@ void ssd_fwd_kernel(SsdParams p) {
           const float gz = silu_f32(Elem<T>::f32(zr[q][i]));
           y *= zg ? gz : 1.0f;
           const bool ok = tl < nv && p0 + pl < p.P;
-          const uint32_t off = ok ? static_cast<uint32_t>((tl * p.osl + pl) * ES) : oend;
+          const uint32_t off = ok ? oo0 + i * p.osl + kPB * q * ES : oend;
           Elem<T>::store(ro, off, y);
         }
       }
@@ -576,12 +583,14 @@ hipError_t launch_ssd_fwd(const ssm_ssd_args& a, hipStream_t stream) {
   SsdParams p;
   p.x = a.x; p.dt = a.dt; p.z = a.z; p.B = a.B; p.C = a.C;
   p.A = a.A; p.D = a.D; p.bias = a.dt_bias; p.h0 = a.h0; p.last = a.last_state; p.out = a.out;
-  p.xsb = a.x_batch_stride; p.xsl = a.x_seq_stride; p.xsh = a.x_head_stride;
-  p.dsb = a.dt_batch_stride; p.dsl = a.dt_seq_stride;
-  p.zsb = a.z_batch_stride; p.zsl = a.z_seq_stride; p.zsh = a.z_head_stride;
-  p.Bsb = a.B_batch_stride; p.Bsl = a.B_seq_stride; p.Bsg = a.B_group_stride;
-  p.Csb = a.C_batch_stride; p.Csl = a.C_seq_stride; p.Csg = a.C_group_stride;
-  p.osb = a.out_batch_stride; p.osl = a.out_seq_stride; p.osh = a.out_head_stride;
+  const int64_t es = a.io_dtype == SSM_BF16 ? 2 : 4;
+  auto seqb = [&](int64_t stride) { return static_cast<uint32_t>(stride * es); };
+  p.xsb = a.x_batch_stride; p.xsl = seqb(a.x_seq_stride); p.xsh = a.x_head_stride;
+  p.dsb = a.dt_batch_stride; p.dsl = seqb(a.dt_seq_stride);
+  p.zsb = a.z_batch_stride; p.zsl = seqb(a.z_seq_stride); p.zsh = a.z_head_stride;
+  p.Bsb = a.B_batch_stride; p.Bsl = seqb(a.B_seq_stride); p.Bsg = a.B_group_stride;
+  p.Csb = a.C_batch_stride; p.Csl = seqb(a.C_seq_stride); p.Csg = a.C_group_stride;
+  p.osb = a.out_batch_stride; p.osl = seqb(a.out_seq_stride); p.osh = a.out_head_stride;
   p.L = static_cast<int>(a.seqlen); p.H = static_cast<int>(a.nheads);
   p.P = static_cast<int>(a.headdim); p.G = static_cast<int>(a.ngroups > 1 ? a.ngroups : 1);
   p.N = static_cast<int>(a.dstate);
