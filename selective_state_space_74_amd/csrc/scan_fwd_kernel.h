@@ -161,6 +161,10 @@ struct Wave {
   // (16 FMAs in place of 16 products on the state lanes and a 15-add sum);
   // C is then staged token-major.
   static constexpr bool kOwnerC = S == 1 && !kLane && M == Mode::kScan;
+  // token of the scan after which the owner's C column is read, so that the
+  // read is in flight during the rest of the scan rather than exposed at the
+  // end of the block
+  static constexpr int kCRead = 7;
 
   __device__ __forceinline__ uint32_t skip(int k) const {
     return static_cast<uint32_t>(t_beg + k * kT) * E;
@@ -358,6 +362,7 @@ struct Wave {
     // slot
     // one slot: a rolling 4-register buffer; several: one sum per token
     float pk[S == 1 ? 4 : kT];
+    float cl[kN];   // kOwnerC: this token's C column (this group's tile buffer)
     static_for<0, S>([&](auto Qs) {
       constexpr int q = decltype(Qs)::value;
       if constexpr (q > 0) {
@@ -378,19 +383,22 @@ struct Wave {
             *reinterpret_cast<float4*>(&sP[row][col * kPitch + j - 3]) =
                 make_float4(pk[i - 3], pk[i - 2], pk[i - 1], pk[i]);
         }
+        if constexpr (kOwnerC && j == kCRead) {
+          const float* cc = &sCt[(k / kGB) & 1][(k % kGB) * kT + col][0];
+#pragma unroll
+          for (int ii = 0; ii < kN / 4; ++ii) {
+            const float4 c4 = *reinterpret_cast<const float4*>(cc + 4 * ii);
+            cl[4 * ii] = c4.x; cl[4 * ii + 1] = c4.y; cl[4 * ii + 2] = c4.z; cl[4 * ii + 3] = c4.w;
+          }
+        }
       });
     });
     if constexpr (kOwnerC) {
       // this block's readout right away: y = sum_n C_n h_n from the h the
       // state lanes just left in LDS and this token's C column of the tile
-      // (still this group's buffer: the other one is staged next)
-      const float* cc = &sCt[(k / kGB) & 1][(k % kGB) * kT + col][0];
-      float cl[kN], part[kN];
-#pragma unroll
-      for (int i = 0; i < kN / 4; ++i) {
-        const float4 y = *reinterpret_cast<const float4*>(cc + 4 * i);
-        cl[4 * i] = y.x; cl[4 * i + 1] = y.y; cl[4 * i + 2] = y.z; cl[4 * i + 3] = y.w;
-      }
+      // (read during the scan; still this group's buffer: the other one is
+      // staged next)
+      float part[kN];
 #pragma unroll
       for (int n = 0; n < kN; ++n) part[n] = sP[row][n * kPitch + col];
 #pragma unroll
