@@ -115,13 +115,13 @@ __device__ __forceinline__ void storeR(float* p, const float (&v)[R], int nvalid
 // DPP quad permute (the newest, x, at q = K-1), and the quad sums the four
 // weighted taps.  CONV == 2 (width 5..8): every lane of the quad forms the
 // whole sum and lane q writes back the elements k = q, q + 4.
-// NBB: batch rows per thread (without the conv branch).  The channel's A,
-// bias and D are loaded once for all of them, and every row's loads are
-// issued before the first row is computed, so a wavefront keeps NBB times
-// the bytes in flight.
+// NBB: batch rows per thread (without the conv branch or with a width of at
+// most 4).  The channel's A, bias, D and conv weights are loaded once for
+// all of them, and every row's loads are issued before the first row is
+// computed, so a wavefront keeps NBB times the bytes in flight.
 template <typename T, bool VEC, int CONV, int R, int NBB>
 __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p) {
-  static_assert(CONV == 0 || NBB == 1, "the conv branch runs one batch row per thread");
+  static_assert(CONV != 2 || NBB == 1, "widths above 4 run one batch row per thread");
   const int q = threadIdx.x & 3;
   const int64_t b0 = static_cast<int64_t>(blockIdx.y) * NBB;
   const int64_t d0 = static_cast<int64_t>(blockIdx.x) * kChannelsPerBlock + (threadIdx.x >> 2);
@@ -151,17 +151,24 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p) 
     // causal conv of the block's conv branch: shift in x, then the weighted
     // sum of the K newest inputs (Mamba model notes, section 4.3)
     const int K = p.K;
-    float* cs = p.conv_state + (b0 * p.dim + d) * K;
     const int qk = min(q, K - 1);                     // lanes past K stay in the row
-    const float old = cs[qk];
-    const float nb = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(old), 0xF9, 0xf, 0xf, true));
-    const float nvx = q == K - 1 ? xv[0] : nb;        // element q of the shifted state
-    float acc = q < K ? p.conv_w[d * K + q] * nvx : 0.0f;
-    acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xf, 0xf, true));
-    acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xf, 0xf, true));
-    if (p.conv_b) acc += p.conv_b[d];
-    if (ok && q < K) cs[q] = nvx;
-    xv[0] = p.conv_silu ? silu_f32(acc) : acc;
+    const float wq = q < K ? p.conv_w[d * K + q] : 0.0f;
+    const float cb = p.conv_b ? p.conv_b[d] : 0.0f;
+    float old[NBB];
+#pragma unroll
+    for (int i = 0; i < NBB; ++i)
+      old[i] = p.conv_state[(min(b0 + i, p.batch - 1) * p.dim + d) * K + qk];
+#pragma unroll
+    for (int i = 0; i < NBB; ++i) {
+      const float nb = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(old[i]), 0xF9, 0xf, 0xf, true));
+      const float nvx = q == K - 1 ? xv[i] : nb;      // element q of the shifted state
+      float acc = q < K ? wq * nvx : 0.0f;
+      acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0xB1, 0xf, 0xf, true));
+      acc += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(acc), 0x4E, 0xf, 0xf, true));
+      acc += cb;
+      if (ok && b0 + i < p.batch && q < K) p.conv_state[((b0 + i) * p.dim + d) * K + q] = nvx;
+      xv[i] = p.conv_silu ? silu_f32(acc) : acc;
+    }
   } else if constexpr (CONV == 2) {
     const int K = p.K;
     float* cs = p.conv_state + (b0 * p.dim + d) * K;
@@ -223,6 +230,12 @@ void launch_v(int conv, bool rows, dim3 grid, dim3 block, const UpdateParams& p,
     }
     state_update_kernel<T, VEC, 0, R, 1><<<grid, block, 0, stream>>>(p);
   } else if (conv == 1) {
+    if constexpr (VEC && R <= 4) {
+      if (rows) {
+        state_update_kernel<T, VEC, 1, R, kRowsPerThread><<<grid, block, 0, stream>>>(p);
+        return;
+      }
+    }
     state_update_kernel<T, VEC, 1, R, 1><<<grid, block, 0, stream>>>(p);
   } else {
     state_update_kernel<T, VEC, 2, R, 1><<<grid, block, 0, stream>>>(p);
@@ -283,7 +296,7 @@ hipError_t launch_state_update(const ssm_update_args& a, hipStream_t stream) {
   p.conv_silu = a.conv_silu;
   const int64_t xblocks = (a.dim + kChannelsPerBlock - 1) / kChannelsPerBlock;
   if (xblocks > 0x7fffffff || a.batch > 65535) return hipErrorInvalidConfiguration;
-  const bool rows = a.conv_weight == nullptr && vec && r <= 4 &&
+  const bool rows = (a.conv_weight == nullptr || a.d_conv <= 4) && vec && r <= 4 &&
                     xblocks * ((a.batch + kRowsPerThread - 1) / kRowsPerThread) >= kMinBlocksRows;
   const int64_t ybl = rows ? (a.batch + kRowsPerThread - 1) / kRowsPerThread : a.batch;
   const dim3 grid(static_cast<unsigned>(xblocks), static_cast<unsigned>(ybl));

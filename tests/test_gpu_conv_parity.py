@@ -120,12 +120,16 @@ def test_chunked_prefill_hands_over_both_states():
     assert np.array_equal(to_np(s2), ref_st)
 
 
-@pytest.mark.parametrize("io,K", [("f32", 4), ("bf16", 4), ("f32", 2), ("bf16", 7)])
-def test_decode_with_conv_continues_the_prefill(io, K):
+@pytest.mark.parametrize("io,K,batch,dim,L,S", [
+    ("f32", 4, 3, 40, 48, 6), ("bf16", 4, 3, 40, 48, 6), ("f32", 2, 3, 40, 48, 6),
+    ("bf16", 7, 3, 40, 48, 6),
+    # a grid large enough that each decode thread takes two batch rows (odd
+    # batch, a partial last channel block)
+    ("bf16", 4, 51, 5100, 8, 3), ("f32", 3, 51, 5100, 8, 3)])
+def test_decode_with_conv_continues_the_prefill(io, K, batch, dim, L, S):
     """Prefill L tokens, then decode S tokens one at a time from the returned
     SSM and conv states: the decode outputs equal the last S outputs of one
     prefill over L + S tokens."""
-    batch, dim, L, S = 3, 40, 48, 6
     inp = si.scan_inputs(batch, dim, L + S, io_dtype=io, seed=31 + K)
     w, b, st = conv_params(dim, K, 31, batch)
     st = as_io(st, io)
