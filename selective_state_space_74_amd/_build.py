@@ -21,6 +21,17 @@ HIPCC_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall",
                "-I", INCLUDE, "-I", CSRC]
 
 
+# Per-source extra flags.  The SSD kernel keeps its matrix-product
+# accumulators in the ordinary VGPR file (the VGPR form of the MFMA
+# instructions) instead of the accumulation registers, which saves the
+# copies between the two files.
+SOURCE_FLAGS = {"ssd_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
+def flags_for(src: str) -> list:
+    return HIPCC_FLAGS + SOURCE_FLAGS.get(os.path.basename(src), [])
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
@@ -52,7 +63,7 @@ def build(verbose: bool = False) -> str:
     with tempfile.TemporaryDirectory(prefix="ssm_build_") as d:
         objs = [os.path.join(d, os.path.basename(src) + ".o") for src in sources()]
         with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-            list(ex.map(lambda so: _run([hipcc(), *HIPCC_FLAGS, "-c", "-o", so[1], so[0]], verbose),
+            list(ex.map(lambda so: _run([hipcc(), *flags_for(so[0]), "-c", "-o", so[1], so[0]], verbose),
                         zip(sources(), objs)))
         _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
@@ -62,7 +73,7 @@ def build(verbose: bool = False) -> str:
 def assembly(out_path: str, src: str | None = None) -> str:
     """Device assembly of one source (for inspecting the generated ISA)."""
     src = src or os.path.join(CSRC, "scan_fwd.hip")
-    cmd = [hipcc(), *HIPCC_FLAGS, "--cuda-device-only", "-S", "-o", out_path, src]
+    cmd = [hipcc(), *flags_for(src), "--cuda-device-only", "-S", "-o", out_path, src]
     subprocess.run(cmd, check=True, capture_output=True)
     return out_path
 
