@@ -112,7 +112,7 @@ def test_backward_config1_full_size():
     """The 130m-like layer (batch 8, d_inner 1536, L 2048, fp32) end to end."""
     cfg = si.SCAN_CONFIGS[1]
     errs, *_ = run(cfg.batch, cfg.dim, cfg.seqlen, "f32", seed=cfg.seed, h0=False, dlast=False)
-    check(errs, "f32", "cfg1")
+    check(errs, "f32", "130m-like layer")
 
 
 def test_backward_zero_length():

@@ -43,7 +43,7 @@ def check_scan(inp, io, rows=None, twin=True, h0=None, label=""):
 
 def test_config0_tiny_f32():
     cfg = si.SCAN_CONFIGS[0]
-    check_scan(si.scan_inputs_for(cfg), "f32", label="cfg0")
+    check_scan(si.scan_inputs_for(cfg), "f32", label="tiny")
 
 
 @pytest.mark.parametrize("batch,dim,L,io", [
@@ -86,7 +86,7 @@ def test_initial_state_and_split_sequence():
 
 def test_config1_full_f32():
     cfg = si.SCAN_CONFIGS[1]
-    check_scan(si.scan_inputs_for(cfg), "f32", label="cfg1")
+    check_scan(si.scan_inputs_for(cfg), "f32", label="130m-like layer")
 
 
 def test_config2_bf16_sampled_rows():
@@ -94,7 +94,7 @@ def test_config2_bf16_sampled_rows():
     inp = si.scan_inputs_for(cfg)
     rng = np.random.default_rng(2)
     rows = (np.arange(cfg.batch), np.sort(rng.choice(cfg.dim, 64, replace=False)))
-    check_scan(inp, "bf16", rows=rows, label="cfg2")
+    check_scan(inp, "bf16", rows=rows, label="2.8b-like layer")
 
 
 def test_config3_long_context_16_channels():
@@ -113,7 +113,7 @@ def test_config3_long_context_16_channels():
                                        return_last_state=True)
     e = row_rel_err(sel(out), ref)
     el = row_rel_err(to_np(last)[:, ch], rlast)
-    print(f"[cfg3] err_out={e:.3e} err_last={el:.3e}", flush=True)
+    print(f"[1M tokens] err_out={e:.3e} err_last={el:.3e}", flush=True)
     assert e <= TOL["bf16"] and el <= TOL["bf16"]
     del t, out, last
     torch.cuda.empty_cache()
@@ -275,7 +275,7 @@ def test_decode_equals_scan_on_gpu():
     assert e <= TOL["f32"] and es <= TOL["f32"]
 
 
-def test_decode_config4_1000_steps_sampled():
+def test_decode_b256_d5120_1000_steps_sampled():
     cfg = si.DECODE_CONFIG
     d = si.decode_inputs_device(cfg, device=DEV)
     state = torch.zeros((cfg.batch, cfg.dim, cfg.dstate), device=DEV)
@@ -298,7 +298,7 @@ def test_decode_config4_1000_steps_sampled():
     got = to_np(outs.index_select(1, tb).index_select(2, td))
     e = row_rel_err(np.moveaxis(got, 0, -1), np.moveaxis(ref, 0, -1))
     es = row_rel_err(to_np(state)[np.ix_(bi, di)], rstate)
-    print(f"[cfg4 decode 1000 steps] err_out={e:.3e} err_state={es:.3e}", flush=True)
+    print(f"[decode b256 d5120, 1000 steps] err_out={e:.3e} err_state={es:.3e}", flush=True)
     assert e <= TOL["bf16"] and es <= TOL["bf16"]
     del d, outs
     torch.cuda.empty_cache()
