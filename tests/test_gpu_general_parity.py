@@ -170,6 +170,25 @@ def test_decode_dstate_and_groups(N, G, io):
     assert e <= TOL[io] and es <= TOL[io]
 
 
+@pytest.mark.parametrize("N,G,io", [(16, 4, "bf16"), (8, 5100, "f32"), (4, 0, "bf16")])
+def test_decode_paired_rows_with_groups(N, G, io):
+    """A grid large enough that each thread takes two batch rows (odd batch,
+    partial last channel block), with B/C groups and fewer than 16 states."""
+    d = si.decode_inputs_host(51, 5100, dstate=N, io_dtype=io, seed=N + G + 7,
+                              random_state=True, ngroups=G)
+    t = si.to_torch(d, DEV)
+    state = t["state"].clone()
+    out = ssm.selective_state_update(state, t["x"][0], t["dt"][0], t["A"], t["B"][0], t["C"][0],
+                                     D=t["D"], z=t["z"][0], dt_bias=t["dt_bias"])
+    torch.cuda.synchronize()
+    ref, rstate = oracle.state_update(d["state"], d["x"][0], d["dt"][0], d["A"], d["B"][0],
+                                      d["C"][0], D=d["D"], z=d["z"][0], dt_bias=d["dt_bias"])
+    e = row_rel_err(to_np(out)[None], ref[None])
+    es = state_err(to_np(state), rstate)
+    print(f"[decode paired N{N} G{G} {io}] err_out={e:.2e} err_state={es:.2e}", flush=True)
+    assert e <= TOL[io] and es <= TOL[io]
+
+
 def test_decode_padded_state_rows():
     """State rows with a gap (state_dim_stride > dstate): the element-wise
     instantiation; the gap is never written."""
