@@ -1,0 +1,139 @@
+"""Seeded random-shape parity sweep of every entry point against the fp64
+oracle, through the C ABI: shapes off every tile grid (channels, tokens,
+states, heads, head sizes), optional inputs switched on and off at random,
+B/C groups, strided views.  The cases are drawn from a fixed seed, so the
+sweep is the same on every run.  Bars as in tests/parity.py: row-normwise
+max relative error 1e-4 (fp32 IO), 2e-2 (bf16 IO)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth_inputs as si
+from parity import TOL, row_rel_err, to_np
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU machines only to be skipped
+    pytest.skip("no GPU", allow_module_level=True)
+
+import selective_state_space_74_amd as ssm  # noqa: E402
+
+DEV = "cuda"
+
+
+def state_err(got, ref):
+    """Rows over n from 16 states up; with fewer, rows over the batch row."""
+    got, ref = np.asarray(got), np.asarray(ref)
+    if ref.shape[-1] < 16:
+        got, ref = got.reshape(got.shape[0], -1), ref.reshape(ref.shape[0], -1)
+    return row_rel_err(got, ref)
+
+
+def divisor(rng, n):
+    ds = [d for d in range(1, n + 1) if n % d == 0]
+    return int(rng.choice(ds))
+
+
+def scan_case(i):
+    rng = np.random.default_rng(1000 + i)
+    io = "f32" if i % 2 == 0 else "bf16"
+    batch, dim = int(rng.integers(1, 4)), int(rng.integers(1, 71))
+    L, N = int(rng.integers(1, 301)), int(rng.integers(1, 65))
+    G = 0 if rng.random() < 0.4 else divisor(rng, dim)
+    return dict(io=io, batch=batch, dim=dim, L=L, N=N, G=G, D=bool(rng.random() < 0.7),
+                z=bool(rng.random() < 0.7), bias=bool(rng.random() < 0.7),
+                softplus=bool(rng.random() < 0.8), h0=bool(rng.random() < 0.5),
+                view=bool(rng.random() < 0.3), seed=2000 + i)
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_scan_random_shapes(i):
+    c = scan_case(i)
+    inp = si.scan_inputs(c["batch"], c["dim"], c["L"], dstate=c["N"], io_dtype=c["io"],
+                         seed=c["seed"], ngroups=c["G"])
+    if not c["softplus"]:   # a positive step taken as is
+        inp["delta"] = si._to_io(np.abs(inp["delta"].astype(np.float32)) + np.float32(0.01), c["io"])
+        inp["delta_bias"] = np.zeros_like(inp["delta_bias"])
+    h0 = (np.random.default_rng(c["seed"]).standard_normal((c["batch"], c["dim"], c["N"]))
+          .astype(np.float32) if c["h0"] else None)
+    t = si.to_torch(inp, DEV)
+    u = t["u"]
+    if c["view"]:   # u as a channel slice of a wider tensor (free channel stride)
+        wide = torch.zeros((c["batch"], c["dim"] + 5, c["L"]), dtype=u.dtype, device=DEV)
+        wide[:, 2:2 + c["dim"]] = u
+        u = wide[:, 2:2 + c["dim"]]
+    out, last = ssm.selective_scan_fwd(
+        u, t["delta"], t["A"], t["B"], t["C"], D=t["D"] if c["D"] else None,
+        z=t["z"] if c["z"] else None, delta_bias=t["delta_bias"] if c["bias"] else None,
+        delta_softplus=c["softplus"], h0=None if h0 is None else torch.from_numpy(h0).to(DEV),
+        return_last_state=True)
+    torch.cuda.synchronize()
+    ref, rlast = oracle.selective_scan(
+        inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"], D=inp["D"] if c["D"] else None,
+        z=inp["z"] if c["z"] else None, delta_bias=inp["delta_bias"] if c["bias"] else None,
+        delta_softplus=c["softplus"], h0=h0, return_last_state=True)
+    e, el = row_rel_err(to_np(out), ref), state_err(to_np(last), rlast)
+    print(f"[fuzz scan {i} {c}] err_out={e:.2e} err_last={el:.2e}", flush=True)
+    assert e <= TOL[c["io"]] and el <= TOL[c["io"]]
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_decode_random_shapes(i):
+    rng = np.random.default_rng(3000 + i)
+    io = "f32" if i % 2 == 0 else "bf16"
+    batch, dim, N = int(rng.integers(1, 6)), int(rng.integers(1, 201)), int(rng.integers(1, 65))
+    G = 0 if rng.random() < 0.4 else divisor(rng, dim)
+    d = si.decode_inputs_host(batch, dim, dstate=N, io_dtype=io, steps=2, seed=4000 + i,
+                              random_state=True, ngroups=G)
+    t = si.to_torch(d, DEV)
+    state = t["state"].clone()
+    outs = []
+    for s in range(2):
+        outs.append(ssm.selective_state_update(state, t["x"][s], t["dt"][s], t["A"], t["B"][s],
+                                               t["C"][s], D=t["D"], z=t["z"][s],
+                                               dt_bias=t["dt_bias"]))
+    torch.cuda.synchronize()
+    rstate = d["state"]
+    errs = []
+    for s in range(2):
+        ref, rstate = oracle.state_update(rstate, d["x"][s], d["dt"][s], d["A"], d["B"][s],
+                                          d["C"][s], D=d["D"], z=d["z"][s], dt_bias=d["dt_bias"])
+        errs.append(row_rel_err(to_np(outs[s])[None], ref[None]))
+    es = state_err(to_np(state), rstate)
+    print(f"[fuzz decode {i} b{batch} d{dim} N{N} G{G} {io}] err_out={max(errs):.2e} "
+          f"err_state={es:.2e}", flush=True)
+    assert max(errs) <= TOL[io] and es <= TOL[io]
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_ssd_random_shapes(i):
+    rng = np.random.default_rng(5000 + i)
+    io = "f32" if i % 2 == 0 else "bf16"
+    batch, L = int(rng.integers(1, 3)), int(rng.integers(1, 201))
+    H, P = int(rng.integers(1, 9)), int(rng.integers(1, 73))
+    G = divisor(rng, H)
+    N = int(rng.integers(1, 65))
+    inp = si.ssd_inputs(batch, L, H, P, G, N, io_dtype=io, seed=6000 + i)
+    gate, skip, h0 = bool(rng.random() < 0.7), bool(rng.random() < 0.7), bool(rng.random() < 0.5)
+    h0v = (np.random.default_rng(i).standard_normal((batch, H, P, N)).astype(np.float32)
+           if h0 else None)
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    tt = {k: torch.from_numpy(np.ascontiguousarray(v)).to(DEV) for k, v in inp.items()
+          if k != "io_dtype"}
+    for k in ("x", "z", "dt", "B", "C"):
+        tt[k] = tt[k].to(dt)
+    out, last = ssm.ssd_scan_fwd(tt["x"], tt["dt"], tt["A"], tt["B"], tt["C"],
+                                 D=tt["D"] if skip else None, z=tt["z"] if gate else None,
+                                 dt_bias=tt["dt_bias"],
+                                 h0=None if h0v is None else torch.from_numpy(h0v).to(DEV),
+                                 return_last_state=True)
+    torch.cuda.synchronize()
+    ref, rlast = oracle.ssd_scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                                 D=inp["D"] if skip else None, z=inp["z"] if gate else None,
+                                 dt_bias=inp["dt_bias"], h0=h0v, return_last_state=True)
+    e = row_rel_err(np.moveaxis(to_np(out), 1, -1), np.moveaxis(ref, 1, -1))
+    el = state_err(to_np(last).reshape(batch, -1, N), rlast.reshape(batch, -1, N))
+    print(f"[fuzz ssd {i} b{batch} L{L} H{H} P{P} G{G} N{N} {io} gate{gate} skip{skip} "
+          f"h0{h0}] err_out={e:.2e} err_last={el:.2e}", flush=True)
+    assert e <= TOL[io] and el <= TOL[io]
