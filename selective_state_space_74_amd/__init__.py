@@ -582,3 +582,32 @@ def ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True,
     if st != 0:
         raise SSMError(st, "ssm_ssd_scan_fwd")
     return (out, last_state) if return_last_state else out
+
+
+def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True):
+    """selective_scan_fwd as a differentiable torch op: the forward keeps the
+    state checkpoints and the backward runs ssm_selective_scan_bwd on them.
+    Gradients flow to u, delta, A, B, C and, when given, D, z and delta_bias
+    (d_state 16; B/C shared or in groups that keep 16-channel blocks whole)."""
+    torch = _torch()
+
+    class _Scan(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, u, delta, A, B, C, D, z, delta_bias):
+            batch, dim, L = u.shape
+            ck = torch.empty(checkpoint_shape(batch, dim, L, A.shape[1]), dtype=torch.float32,
+                             device=u.device)
+            out = selective_scan_fwd(u, delta, A, B, C, D=D, z=z, delta_bias=delta_bias,
+                                     delta_softplus=delta_softplus, checkpoints=ck)
+            ctx.save_for_backward(u, delta, A, B, C, D, z, delta_bias, ck)
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            u, delta, A, B, C, D, z, delta_bias, ck = ctx.saved_tensors
+            g = selective_scan_bwd(dout.contiguous(), u, delta, A, B, C, ck, D=D, z=z,
+                                   delta_bias=delta_bias, delta_softplus=delta_softplus)
+            return (g["du"], g["ddelta"], g["dA"], g["dB"].to(B.dtype), g["dC"].to(C.dtype),
+                    g.get("dD"), g.get("dz"), g.get("ddelta_bias"))
+
+    return _Scan.apply(u, delta, A, B, C, D, z, delta_bias)
