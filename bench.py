@@ -383,6 +383,8 @@ def main():
     ap.add_argument("--profile", action="store_true",
                     help="only the headline scan (10 launches) and a 1 GiB copy kernel "
                          "(10 launches) that calibrates the HBM byte counters; for rocprofv3")
+    ap.add_argument("--profile-ssd", action="store_true",
+                    help="only the Mamba-2 SSD layer (10 launches); for rocprofv3")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -403,6 +405,16 @@ def main():
     head = si.SCAN_CONFIGS[1]
     if args.profile:
         profile_run(head, torch, ssm, si)
+        return
+    if args.profile_ssd:
+        cs = si.SSD_CONFIG
+        t = si.ssd_inputs_device(cs, "cuda")
+        out = torch.empty_like(t["x"])
+        for _ in range(10):
+            ssm.ssd_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                             dt_bias=t["dt_bias"], out=out)
+        torch.cuda.synchronize()
+        log(f"[profile] 10 launches of the SSD layer {cs.name}")
         return
     log(f"[bench] headline {head.name}: warmup {args.warmup}, steps {args.steps}")
     r = bench_scan(head, args.steps, args.warmup, torch, ssm, si)
