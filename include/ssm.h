@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 5
+#define SSM_ABI_VERSION 6
 
 /* Tokens between two state checkpoints (see ssm_scan_args.checkpoints). */
 #define SSM_CHECKPOINT_TOKENS 16
@@ -192,10 +192,18 @@ typedef struct ssm_scan_args {
  * The sums over channels (dB, dC) and over batch rows (dA, dD, ddelta_bias)
  * are accumulated with device atomics, so their last bits can vary from run
  * to run; every other output is deterministic.  Outputs must not overlap
- * each other or any input.  The backward runs every sequence as one segment
- * (no workspace).  It is built for dstate == 16 and for B/C groups that
- * keep each block of 16 consecutive channels in one group (one group, or
- * dim / ngroups a multiple of 16); other shapes return SSM_ERR_UNSUPPORTED. */
+ * each other or any input.  The backward runs every sequence as one segment.
+ * It is built for dstate == 16 and for B/C groups that keep each block of 16
+ * consecutive channels in one group (one group, or dim / ngroups a multiple
+ * of 16); other shapes return SSM_ERR_UNSUPPORTED.
+ * Workspace (optional): device scratch owned by the caller, 4-byte aligned,
+ * of at least ssm_scan_bwd_workspace_size() bytes, not overlapping any
+ * tensor.  With many channel blocks per group the library then writes each
+ * block's dB/dC partial sums there with plain stores and sums them in a
+ * second pass, instead of adding into dB/dC with device atomics (whose
+ * throughput bounds the backward at that size); dB and dC are then
+ * deterministic.  With workspace NULL or too small the atomics are used.
+ * Its contents are scratch on return. */
 typedef struct ssm_scan_bwd_args {
   int64_t batch, dim, seqlen, dstate;
   int32_t io_dtype;       /* ssm_dtype */
@@ -223,6 +231,7 @@ typedef struct ssm_scan_bwd_args {
   float* dh0;
   int64_t ngroups;    /* B/C groups; 0 or 1: one group */
   int64_t B_group_stride, C_group_stride;
+  void* workspace;    size_t workspace_bytes;
 } ssm_scan_bwd_args;
 
 /* Arguments of the single-token decode update.
@@ -333,6 +342,10 @@ size_t ssm_ssd_args_size(void);
 /* Workspace bytes the scan can use for this argument block (0 when it would
  * run single-segment anyway).  Reads only sizes; pure host code. */
 size_t ssm_scan_workspace_size(const ssm_scan_args* args);
+
+/* Workspace bytes the backward can use for this argument block (0 when it
+ * adds dB/dC with atomics anyway).  Reads only sizes; pure host code. */
+size_t ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args* args);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* ssm_status_string(int status);

@@ -32,7 +32,7 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssm.so")
 
-SSM_ABI_VERSION = 5
+SSM_ABI_VERSION = 6
 CHECKPOINT_TOKENS = 16
 MAX_CONV = 8
 SSM_F32, SSM_BF16 = 0, 1
@@ -84,7 +84,8 @@ class ScanBwdArgs(ctypes.Structure):
                 ("dz", _P), ("dz_batch_stride", _I64), ("dz_dim_stride", _I64),
                 ("dB", _P), ("dC", _P), ("dA", _P), ("dD", _P), ("ddelta_bias", _P),
                 ("dh0", _P),
-                ("ngroups", _I64), ("B_group_stride", _I64), ("C_group_stride", _I64)]
+                ("ngroups", _I64), ("B_group_stride", _I64), ("C_group_stride", _I64),
+                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class UpdateArgs(ctypes.Structure):
@@ -151,6 +152,8 @@ def lib():
             f.argtypes = [ctypes.POINTER(T)]
         L.ssm_scan_workspace_size.restype = ctypes.c_size_t
         L.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs)]
+        L.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
+        L.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ScanBwdArgs)]
         L.ssm_selective_scan_fwd.restype = ctypes.c_int
         L.ssm_selective_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _P]
         L.ssm_selective_scan_bwd.restype = ctypes.c_int
@@ -188,6 +191,10 @@ def validate_update(args: UpdateArgs) -> int:
 
 def scan_workspace_size(args: ScanArgs) -> int:
     return lib().ssm_scan_workspace_size(ctypes.byref(args))
+
+
+def scan_bwd_workspace_size(args: "ScanBwdArgs") -> int:
+    return lib().ssm_scan_bwd_workspace_size(ctypes.byref(args))
 
 
 def scan_fwd_raw(args: ScanArgs, stream: int = 0) -> int:
@@ -456,14 +463,22 @@ def selective_state_update(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, 
     return out
 
 
+# the backward's workspace is allocated automatically only up to this size
+BWD_WORKSPACE_AUTO_MAX = 2 << 30
+
+
 def selective_scan_bwd(dout, u, delta, A, B, C, checkpoints, D=None, z=None, delta_bias=None,
-                       delta_softplus=True, h0=None, dlast=None, stream=None):
+                       delta_softplus=True, h0=None, dlast=None, stream=None, workspace=None):
     """Gradients of selective_scan_fwd for the upstream gradient dout on out
     (and dlast on last_state), from the checkpoints that forward wrote.
     Returns a dict: du, ddelta (IO dtype, shaped like u), dB, dC (fp32, like
     B), dA (fp32, like A) and, for the inputs that were given, dz, dD,
-    ddelta_bias, dh0 (fp32).  dB, dC, dA, dD and ddelta_bias are summed with
-    device atomics (their last bits may vary between runs)."""
+    ddelta_bias, dh0 (fp32).  dA, dD and ddelta_bias are summed with device
+    atomics (their last bits may vary between runs); so are dB and dC unless
+    the library sums per-block partials in a workspace.
+    `workspace`: a device tensor reused across calls; None allocates one of
+    the size the library asks for (up to BWD_WORKSPACE_AUTO_MAX bytes);
+    False passes none (dB/dC then always by atomics)."""
     torch = _torch()
     if u.dim() != 3:
         raise ValueError("u must be (batch, dim, L)")
@@ -520,6 +535,15 @@ def selective_scan_bwd(dout, u, delta, A, B, C, checkpoints, D=None, z=None, del
     a.ddelta, (a.ddelta_batch_stride, a.ddelta_dim_stride) = _ptr(g["ddelta"]), g["ddelta"].stride()[:2]
     a.dB, a.dC, a.dA = _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dA"])
     a.dD, a.ddelta_bias, a.dh0 = _ptr(g.get("dD")), _ptr(g.get("ddelta_bias")), _ptr(g.get("dh0"))
+    need = scan_bwd_workspace_size(a) if workspace is not False else 0
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = (torch.empty(need, dtype=torch.uint8, device=dev)
+                         if need <= BWD_WORKSPACE_AUTO_MAX else None)
+        if workspace is not None:
+            _check_dev("workspace", workspace, dev)
+            a.workspace = _ptr(workspace)
+            a.workspace_bytes = workspace.numel() * workspace.element_size()
     st = scan_bwd_raw(a, _stream(stream))
     if st != 0:
         raise SSMError(st, "ssm_selective_scan_bwd")

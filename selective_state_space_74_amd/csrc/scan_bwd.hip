@@ -74,6 +74,7 @@ struct BwdParams {
   float* dD;
   float* dbias;
   float* dh0;
+  float* part;          // [batch][cgroups][2][kN][L] dB/dC partial sums, or NULL (atomics)
   int64_t usb, usd, dsb, dsd, zsb, zsd, Bsb, Bsn, Csb, Csn, Asd, Asn, gsb, gsd;
   int64_t dusb, dusd, ddsb, ddsd, dzsb, dzsd;
   int64_t Bsg, Csg;     // B/C group strides
@@ -103,6 +104,7 @@ struct BwdWave {
   uint32_t ou, odt, oz, og, odu, odd, odz, oB, oC, ock;
   float a, a2, bias, Dd;
   bool gate;
+  bool partials;      // dB/dC sums stored to this workgroup's slots, not added
   int nvalid;         // channels of this workgroup below dim
   float (*sB)[kN][kGPitch];   // [2][kN][kGPitch], shared
   float (*sC)[kN][kGPitch];
@@ -275,7 +277,13 @@ struct BwdWave {
         float sum = 0.0f;
         for (int c = 0; c < nvalid; ++c) sum += sR[ten][c][n][t];  // rows past dim: repeats
         const uint32_t off = static_cast<uint32_t>((n * p.L + t0 + 8 * h8 + t) * 4);
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(sum, ten ? wdC.at(0) : wdB.at(0), off, 0, 0);
+        // (a uniform branch).  Tokens past the end store or add exact zeros:
+        // into the next state's row, which the sequence's first block
+        // rewrites later (blocks run last to first), or past the window.
+        if (partials)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), ten ? wdC.at(0) : wdB.at(0), off, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(sum, ten ? wdC.at(0) : wdB.at(0), off, 0, 0);
         __syncthreads();
       }
     });
@@ -338,10 +346,15 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   w.ock = static_cast<uint32_t>(((dc - dw0) * ckrow + col) * 4);
   w.wck = Window{reinterpret_cast<const char*>(p.ckpt + (b * p.dim + dw0) * ckrow),
                  static_cast<uint32_t>((dw3 - dw0 + 1) * ckrow * 4)};
-  w.wdB = Window{reinterpret_cast<const char*>(p.dB + (b * p.ngroups + grp) * kN * p.L),
-                 static_cast<uint32_t>(kN * p.L * 4)};
-  w.wdC = Window{reinterpret_cast<const char*>(p.dC + (b * p.ngroups + grp) * kN * p.L),
-                 static_cast<uint32_t>(kN * p.L * 4)};
+  // dB/dC: this workgroup's slots of the partial sums, or the group's rows
+  // of dB/dC themselves (atomics)
+  const float* pB = p.part ? p.part + ((b * p.cgroups + cg) * 2 + 0) * kN * p.L
+                           : p.dB + (b * p.ngroups + grp) * kN * p.L;
+  const float* pC = p.part ? p.part + ((b * p.cgroups + cg) * 2 + 1) * kN * p.L
+                           : p.dC + (b * p.ngroups + grp) * kN * p.L;
+  w.wdB = Window{reinterpret_cast<const char*>(pB), static_cast<uint32_t>(kN * p.L * 4)};
+  w.wdC = Window{reinterpret_cast<const char*>(pC), static_cast<uint32_t>(kN * p.L * 4)};
+  w.partials = p.part != nullptr;
 
   w.a = p.A[dc * p.Asd + col * p.Asn];
   w.a2 = w.a * kLog2e;
@@ -387,6 +400,24 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   }
 }
 
+// dB/dC from the partial sums: element i of group g's (n, t) plane is the
+// sum over the group's channel blocks, in block order.
+__global__ void partial_sum_kernel(const float* part, float* dB, float* dC, int64_t NL,
+                                   int64_t cgroups, int64_t G) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= NL) return;
+  const int64_t bg = blockIdx.y;   // b * G + g
+  const int64_t b = bg / G, g = bg % G, per = cgroups / G;
+  float sb = 0.0f, sc = 0.0f;
+  for (int64_t cg = g * per; cg < (g + 1) * per; ++cg) {
+    const float* q = part + (b * cgroups + cg) * 2 * NL + i;
+    sb += q[0];
+    sc += q[NL];
+  }
+  dB[bg * NL + i] = sb;
+  dC[bg * NL + i] = sc;
+}
+
 // Zero the outputs that are accumulated with atomics (a plain kernel, not a
 // memset, so the launch sequence can be captured in a graph).
 __global__ void zero_kernel(float* p0, int64_t n0, float* p1, int64_t n1, float* p2, int64_t n2,
@@ -420,13 +451,28 @@ bool scan_bwd_windows_fit(const ssm_scan_bwd_args& a) {
   return ok;
 }
 
+// Channel blocks per B/C group from which the partial-sum path beats the
+// device atomics: measured A/B, 96 blocks per group (the 130m-like layer)
+// faster with atomics, 320 (the 2.8b-like layer) with partial sums.
+constexpr int64_t kPartialMinBlocks = 160;
+
+size_t scan_bwd_workspace_bytes(const ssm_scan_bwd_args& a) {
+  const int64_t G = a.ngroups > 1 ? a.ngroups : 1;
+  const int64_t cgroups = (a.dim + kCh - 1) / kCh;
+  if (a.batch <= 0 || a.dim <= 0 || a.seqlen <= 0 || cgroups / G < kPartialMinBlocks) return 0;
+  return static_cast<size_t>(a.batch * cgroups * 2 * kN * a.seqlen) * sizeof(float);
+}
+
 hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
-  // zero what the kernel accumulates into
+  // zero what the kernel accumulates into (dB/dC only when added atomically)
   const int64_t G = a.ngroups > 1 ? a.ngroups : 1;
   const int64_t nbc = a.batch * G * a.dstate * a.seqlen;
-  const int64_t nmax = std::max<int64_t>(nbc, a.dim * a.dstate);
+  const size_t wneed = scan_bwd_workspace_bytes(a);
+  const bool partials = wneed > 0 && a.workspace && a.workspace_bytes >= wneed;
+  const int64_t nz = partials ? 0 : nbc;
+  const int64_t nmax = std::max<int64_t>(nz, a.dim * a.dstate);
   zero_kernel<<<dim3(static_cast<unsigned>((nmax + 255) / 256)), dim3(256), 0, stream>>>(
-      a.dB, nbc, a.dC, nbc, a.dA, a.dim * a.dstate, a.dD, a.dim, a.ddelta_bias, a.dim);
+      a.dB, nz, a.dC, nz, a.dA, a.dim * a.dstate, a.dD, a.dim, a.ddelta_bias, a.dim);
   if (a.seqlen == 0) {
     // no token: the gradient reaching h0 is dlast itself
     if (a.dh0) {
@@ -445,6 +491,7 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
   p.dout = a.dout; p.dlast = a.dlast;
   p.du = a.du; p.ddelta = a.ddelta; p.dz = a.dz;
   p.dB = a.dB; p.dC = a.dC; p.dA = a.dA; p.dD = a.dD; p.dbias = a.ddelta_bias; p.dh0 = a.dh0;
+  p.part = partials ? static_cast<float*>(a.workspace) : nullptr;
   p.usb = a.u_batch_stride; p.usd = a.u_dim_stride;
   p.dsb = a.delta_batch_stride; p.dsd = a.delta_dim_stride;
   p.zsb = a.z_batch_stride; p.zsd = a.z_dim_stride;
@@ -468,6 +515,11 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
   } else {
     if (sp) scan_bwd_kernel<float, true><<<grid, block, 0, stream>>>(p);
     else scan_bwd_kernel<float, false><<<grid, block, 0, stream>>>(p);
+  }
+  if (partials) {
+    const int64_t NL = kN * a.seqlen;
+    partial_sum_kernel<<<dim3(static_cast<unsigned>((NL + 255) / 256), static_cast<unsigned>(a.batch * G)),
+                         dim3(256), 0, stream>>>(p.part, a.dB, a.dC, NL, p.cgroups, G);
   }
   return hipGetLastError();
 }

@@ -70,6 +70,13 @@ size_t ssm_scan_workspace_size(const ssm_scan_args* a) {
   return ssm::scan_workspace_bytes(*a);
 }
 
+size_t ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args* a) {
+  if (!a || a->dstate != 16 || a->seqlen > kMaxSeqlen || a->batch < 0 || a->dim < 0 ||
+      a->seqlen < 0)
+    return 0;
+  return ssm::scan_bwd_workspace_bytes(*a);
+}
+
 const char* ssm_status_string(int status) {
   switch (status) {
     case SSM_OK: return "ok";
@@ -204,7 +211,8 @@ int ssm_validate_scan_bwd(const ssm_scan_bwd_args* a) {
   if (misaligned(a->A, 4) || misaligned(a->D, 4) || misaligned(a->delta_bias, 4) ||
       misaligned(a->h0, 4) || misaligned(a->checkpoints, 4) || misaligned(a->dlast, 4) ||
       misaligned(a->dB, 4) || misaligned(a->dC, 4) || misaligned(a->dA, 4) ||
-      misaligned(a->dD, 4) || misaligned(a->ddelta_bias, 4) || misaligned(a->dh0, 4))
+      misaligned(a->dD, 4) || misaligned(a->ddelta_bias, 4) || misaligned(a->dh0, 4) ||
+      misaligned(a->workspace, 4))
     return SSM_ERR_ALIGN;
   const int64_t nbk = (L + kCkptTokens - 1) / kCkptTokens;
   const Span inputs[] = {
@@ -227,7 +235,8 @@ int ssm_validate_scan_bwd(const ssm_scan_bwd_args* a) {
       span3(a->ddelta, B, a->ddelta_batch_stride, Dm, a->ddelta_dim_stride, L, esz),
       a->z ? span3(a->dz, B, a->dz_batch_stride, Dm, a->dz_dim_stride, L, esz) : Span{},
       span1(a->dB, B * G * N * L, 4), span1(a->dC, B * G * N * L, 4), span1(a->dA, Dm * N, 4),
-      span1(a->dD, Dm, 4), span1(a->ddelta_bias, Dm, 4), span1(a->dh0, B * Dm * N, 4)};
+      span1(a->dD, Dm, 4), span1(a->ddelta_bias, Dm, 4), span1(a->dh0, B * Dm * N, 4),
+      span1(a->workspace, static_cast<int64_t>(a->workspace_bytes), 1)};
   for (const Span& o : outputs) {
     for (const Span& i : inputs)
       if (overlap(o, i)) return SSM_ERR_ALIAS;

@@ -36,12 +36,12 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_struct_layout():
     L = ssm.lib()
-    assert L.ssm_abi_version() == ssm.SSM_ABI_VERSION == 5
+    assert L.ssm_abi_version() == ssm.SSM_ABI_VERSION == 6
     assert L.ssm_scan_args_size() == ctypes.sizeof(ssm.ScanArgs)
     assert L.ssm_scan_bwd_args_size() == ctypes.sizeof(ssm.ScanBwdArgs)
     assert L.ssm_update_args_size() == ctypes.sizeof(ssm.UpdateArgs)
     header = open(HEADER).read()
-    assert "#define SSM_ABI_VERSION 5" in header
+    assert "#define SSM_ABI_VERSION 6" in header
     assert f"#define SSM_MAX_CONV {ssm.MAX_CONV}" in header
     assert f"#define SSM_CHECKPOINT_TOKENS {ssm.CHECKPOINT_TOKENS}" in header
 
@@ -280,6 +280,30 @@ def good_bwd(batch=2, dim=32, L=64, N=16, io=0, z=True):
     a.dB, a.dC, a.dA, a.dD, a.ddelta_bias, a.dh0 = (addr(16), addr(17), addr(18), addr(19),
                                                     addr(20), addr(21))
     return a
+
+
+def test_bwd_workspace_size():
+    """The partial-sum workspace is asked for only from 160 blocks of 16
+    channels per B/C group: batch * blocks * 2 * 16 * L fp32 values."""
+    assert ssm.scan_bwd_workspace_size(good_bwd(batch=2, dim=96 * 16, L=64)) == 0
+    a = good_bwd(batch=2, dim=320 * 16, L=64)
+    assert ssm.scan_bwd_workspace_size(a) == 2 * 320 * 2 * 16 * 64 * 4
+    a.ngroups, a.B_group_stride, a.C_group_stride = 2, 16 * 64, 16 * 64
+    assert ssm.scan_bwd_workspace_size(a) == 2 * 320 * 2 * 16 * 64 * 4   # 160 per group
+    a.ngroups = 4
+    assert ssm.scan_bwd_workspace_size(a) == 0          # 80 per group: atomics
+    assert ssm.scan_bwd_workspace_size(good_bwd(dim=320 * 16, L=0)) == 0
+    assert ssm.scan_bwd_workspace_size(good_bwd(dim=320 * 16, N=32)) == 0
+
+
+def test_bwd_workspace_alias_and_alignment():
+    a = good_bwd()
+    a.workspace, a.workspace_bytes = addr(22), 1 << 20
+    assert ssm.validate_scan_bwd(a) == OK
+    a.workspace = addr(16)                               # over dB
+    assert ssm.validate_scan_bwd(a) == ALIAS
+    a.workspace = addr(22) + 2
+    assert ssm.validate_scan_bwd(a) == ALIGN
 
 
 def test_bwd_valid_block_passes():

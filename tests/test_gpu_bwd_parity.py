@@ -157,3 +157,37 @@ def test_autograd_op_matches_oracle_gradients(io):
     # B and C are bf16 leaves in the bf16 case: their gradients are rounded
     # to bf16 on the way back, so they get the bf16 bar
     check(errs, io, f"autograd {io}")
+
+
+@pytest.mark.parametrize("dim,G,L,io", [(2576, 0, 40, "f32"), (2576, 0, 33, "bf16"),
+                                        (5120, 2, 24, "f32")])
+def test_backward_partial_sums_match_oracle(dim, G, L, io):
+    """At least 160 blocks of 16 channels per B/C group: dB and dC come from
+    per-block partial sums in the workspace and a second summing pass, not
+    from atomics.  Checked against the oracle, and dB/dC against the atomic
+    path (workspace=False) on the same inputs."""
+    inp = si.scan_inputs(1, dim, L, io_dtype=io, seed=dim + L, ngroups=G)
+    rng = np.random.default_rng(dim)
+    dout = rng.standard_normal((1, dim, L)).astype(np.float32)
+    if io == "bf16":
+        dout = si.bf16_round(dout)
+    t = si.to_torch(inp, DEV)
+    ck = torch.empty(ssm.checkpoint_shape(1, dim, L), dtype=torch.float32, device=DEV)
+    kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"])
+    ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], checkpoints=ck, **kw)
+    dt = torch.from_numpy(dout).to(DEV).to(t["u"].dtype)
+    g = ssm.selective_scan_bwd(dt, t["u"], t["delta"], t["A"], t["B"], t["C"], ck, **kw)
+    ga = ssm.selective_scan_bwd(dt, t["u"], t["delta"], t["A"], t["B"], t["C"], ck,
+                                workspace=False, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan_bwd(dout, inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                    D=inp["D"], z=inp["z"], delta_bias=inp["delta_bias"])
+    errs = {}
+    for k, r in ref.items():
+        got = to_np(g[k])
+        errs[k] = row_rel_err(got[None], r[None]) if k in ("dD", "ddelta_bias") else row_rel_err(got, r)
+    check(errs, io, f"partial sums dim{dim} G{G} {io}")
+    for k in ("dB", "dC"):
+        e = row_rel_err(to_np(g[k]), to_np(ga[k]))
+        print(f"[bwd partial vs atomic {k}] {e:.2e}", flush=True)
+        assert e <= 1e-5
