@@ -172,9 +172,14 @@ def bench_bwd(cfg, steps, torch, ssm, si):
     kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"])
     ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], checkpoints=ck, **kw)
     dout = torch.randn_like(t["u"], dtype=torch.float32).to(t["u"].dtype)
+    # the dB/dC partial-sum workspace, allocated once outside the timed region
+    a = ssm.ScanBwdArgs()
+    a.batch, a.dim, a.seqlen, a.dstate = cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate
+    ws = torch.empty(max(1, ssm.scan_bwd_workspace_size(a)), dtype=torch.uint8, device=dev)
 
     def step(i):
-        ssm.selective_scan_bwd(dout, t["u"], t["delta"], t["A"], t["B"], t["C"], ck, **kw)
+        ssm.selective_scan_bwd(dout, t["u"], t["delta"], t["A"], t["B"], t["C"], ck, workspace=ws,
+                               **kw)
 
     for i in range(5):
         step(i)
@@ -186,7 +191,8 @@ def bench_bwd(cfg, steps, torch, ssm, si):
                gbps=nbytes / (kern_ms * 1e-3) / 1e9,
                channel_tokens_per_s=cfg.batch * cfg.dim * cfg.seqlen / (kern_ms * 1e-3))
     res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBS
-    del t, ck, dout
+    res["dBdC"] = "per-block partial sums" if ws.numel() > 1 else "device atomics"
+    del t, ck, dout, ws
     torch.cuda.empty_cache()
     return res
 

@@ -198,11 +198,13 @@ typedef struct ssm_scan_args {
  * of 16); other shapes return SSM_ERR_UNSUPPORTED.
  * Workspace (optional): device scratch owned by the caller, 4-byte aligned,
  * of at least ssm_scan_bwd_workspace_size() bytes, not overlapping any
- * tensor.  With many channel blocks per group the library then writes each
- * block's dB/dC partial sums there with plain stores and sums them in a
- * second pass, instead of adding into dB/dC with device atomics (whose
- * throughput bounds the backward at that size); dB and dC are then
- * deterministic.  With workspace NULL or too small the atomics are used.
+ * tensor.  The library then writes each block of 16 channels' dB/dC partial
+ * sums there with plain stores and adds them in a second pass, instead of
+ * adding into dB/dC with device atomics; dB and dC are then deterministic,
+ * and the time no longer depends on where dB and dC sit (the atomics on
+ * dB(n, t) and dC(n, t) are issued together and at some offsets between the
+ * two buffers share memory channels).  With workspace NULL or too small the
+ * atomics are used.
  * Its contents are scratch on return. */
 typedef struct ssm_scan_bwd_args {
   int64_t batch, dim, seqlen, dstate;
@@ -343,8 +345,10 @@ size_t ssm_ssd_args_size(void);
  * run single-segment anyway).  Reads only sizes; pure host code. */
 size_t ssm_scan_workspace_size(const ssm_scan_args* args);
 
-/* Workspace bytes the backward can use for this argument block (0 when it
- * adds dB/dC with atomics anyway).  Reads only sizes; pure host code. */
+/* Workspace bytes the backward can use for this argument block:
+ * batch * ceil(dim / 16) * 2 * 16 * seqlen fp32 values (0 for an empty
+ * sequence or when batch * ngroups exceeds 65535, where it adds dB/dC with
+ * atomics anyway).  Reads only sizes; pure host code. */
 size_t ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args* args);
 
 /* Static, NUL-terminated description of a status code (never NULL). */

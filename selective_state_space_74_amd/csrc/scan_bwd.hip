@@ -270,16 +270,18 @@ struct BwdWave {
           // the store is dropped
           Elem<T>::store(wdz.at(gate ? skip(k) : 0u), odz, dzv);
         }
-        // dB, dC: thread (tensor, n, t) sums the workgroup's channels (tokens
-        // past the end add exact zeros or fall outside the window)
+        // dB, dC: thread (tensor, n, t) sums the workgroup's channels
         const int tid = threadIdx.x;
         const int ten = tid >> 7, n = (tid >> 3) & 15, t = tid & 7;
         float sum = 0.0f;
         for (int c = 0; c < nvalid; ++c) sum += sR[ten][c][n][t];  // rows past dim: repeats
-        const uint32_t off = static_cast<uint32_t>((n * p.L + t0 + 8 * h8 + t) * 4);
-        // (a uniform branch).  Tokens past the end store or add exact zeros:
-        // into the next state's row, which the sequence's first block
-        // rewrites later (blocks run last to first), or past the window.
+        // Tokens past the end address the window's end, where the store or
+        // atomic is dropped: their offsets would otherwise reach into later
+        // states' rows, and a plain store there (the partial sums) races with
+        // the real value when the sequence is shorter than a block.
+        const int tok = t0 + 8 * h8 + t;
+        const uint32_t off = static_cast<uint32_t>((tok < p.L ? n * p.L + tok : kN * p.L) * 4);
+        // (a uniform branch)
         if (partials)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), ten ? wdC.at(0) : wdB.at(0), off, 0, 0);
         else
@@ -401,21 +403,45 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 }
 
 // dB/dC from the partial sums: element i of group g's (n, t) plane is the
-// sum over the group's channel blocks, in block order.
-__global__ void partial_sum_kernel(const float* part, float* dB, float* dC, int64_t NL,
-                                   int64_t cgroups, int64_t G) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= NL) return;
+// sum over the group's channel blocks.  V consecutive elements per thread
+// (float4 when the buffers are 16-byte aligned); the four thread rows of a
+// workgroup each sum a quarter of the blocks in block order, and row 0 adds
+// the quarters in row order, so the result does not depend on scheduling.
+constexpr int kSumCols = 64, kSumRows = 4;
+
+template <typename V>
+__global__ __launch_bounds__(kSumCols* kSumRows) void partial_sum_kernel(
+    const float* part, float* dB, float* dC, int64_t NL, int64_t cgroups, int64_t G) {
+  constexpr int kV = sizeof(V) / sizeof(float);
+  __shared__ V sB[kSumRows - 1][kSumCols], sC[kSumRows - 1][kSumCols];
+  const int x = threadIdx.x, q = threadIdx.y;
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * kSumCols + x) * kV;
   const int64_t bg = blockIdx.y;   // b * G + g
   const int64_t b = bg / G, g = bg % G, per = cgroups / G;
-  float sb = 0.0f, sc = 0.0f;
-  for (int64_t cg = g * per; cg < (g + 1) * per; ++cg) {
-    const float* q = part + (b * cgroups + cg) * 2 * NL + i;
-    sb += q[0];
-    sc += q[NL];
+  const int64_t lo = g * per + q * per / kSumRows, hi = g * per + (q + 1) * per / kSumRows;
+  V sb{}, sc{};
+  if (i < NL) {
+#pragma unroll 4
+    for (int64_t cg = lo; cg < hi; ++cg) {
+      const float* r = part + (b * cgroups + cg) * 2 * NL + i;
+      sb += *reinterpret_cast<const V*>(r);
+      sc += *reinterpret_cast<const V*>(r + NL);
+    }
   }
-  dB[bg * NL + i] = sb;
-  dC[bg * NL + i] = sc;
+  if (q > 0) {
+    sB[q - 1][x] = sb;
+    sC[q - 1][x] = sc;
+  }
+  __syncthreads();
+  if (q == 0 && i < NL) {
+#pragma unroll
+    for (int r = 0; r < kSumRows - 1; ++r) {
+      sb += sB[r][x];
+      sc += sC[r][x];
+    }
+    *reinterpret_cast<V*>(dB + bg * NL + i) = sb;
+    *reinterpret_cast<V*>(dC + bg * NL + i) = sc;
+  }
 }
 
 // Zero the outputs that are accumulated with atomics (a plain kernel, not a
@@ -451,15 +477,18 @@ bool scan_bwd_windows_fit(const ssm_scan_bwd_args& a) {
   return ok;
 }
 
-// Channel blocks per B/C group from which the partial-sum path beats the
-// device atomics: measured A/B, 96 blocks per group (the 130m-like layer)
-// faster with atomics, 320 (the 2.8b-like layer) with partial sums.
-constexpr int64_t kPartialMinBlocks = 160;
-
+// The partial-sum path is taken whenever the caller gives a workspace.  The
+// atomics' speed depends on where dB and dC sit relative to each other:
+// every workgroup adds into dB(n, t) and dC(n, t) at the same moment, and at
+// some offsets between the two buffers those addresses share memory channels
+// (measured on the 130m-like layer: 561 us at 1 or 3 MiB apart, 713-729 us
+// at 2 or 8 MiB or 1 MiB + 4 KiB; the partial sums take 605 us at every
+// offset, and on the 2.8b-like layer they beat the atomics at any offset).
 size_t scan_bwd_workspace_bytes(const ssm_scan_bwd_args& a) {
   const int64_t G = a.ngroups > 1 ? a.ngroups : 1;
   const int64_t cgroups = (a.dim + kCh - 1) / kCh;
-  if (a.batch <= 0 || a.dim <= 0 || a.seqlen <= 0 || cgroups / G < kPartialMinBlocks) return 0;
+  if (a.batch <= 0 || a.dim <= 0 || a.seqlen <= 0) return 0;
+  if (a.batch * G > 65535) return 0;   // the sum pass runs one grid row per (batch, group)
   return static_cast<size_t>(a.batch * cgroups * 2 * kN * a.seqlen) * sizeof(float);
 }
 
@@ -517,9 +546,19 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
     else scan_bwd_kernel<float, false><<<grid, block, 0, stream>>>(p);
   }
   if (partials) {
+    // NL = 16 * seqlen: a multiple of 4, so float4 only needs aligned bases
     const int64_t NL = kN * a.seqlen;
-    partial_sum_kernel<<<dim3(static_cast<unsigned>((NL + 255) / 256), static_cast<unsigned>(a.batch * G)),
-                         dim3(256), 0, stream>>>(p.part, a.dB, a.dC, NL, p.cgroups, G);
+    auto al16 = [](const void* ptr) { return reinterpret_cast<uintptr_t>(ptr) % 16 == 0; };
+    const dim3 sblock(kSumCols, kSumRows);
+    if (al16(p.part) && al16(a.dB) && al16(a.dC)) {
+      const int64_t cols = (NL / 4 + kSumCols - 1) / kSumCols;
+      partial_sum_kernel<float4><<<dim3(static_cast<unsigned>(cols), static_cast<unsigned>(a.batch * G)),
+                                   sblock, 0, stream>>>(p.part, a.dB, a.dC, NL, p.cgroups, G);
+    } else {
+      const int64_t cols = (NL + kSumCols - 1) / kSumCols;
+      partial_sum_kernel<float><<<dim3(static_cast<unsigned>(cols), static_cast<unsigned>(a.batch * G)),
+                                  sblock, 0, stream>>>(p.part, a.dB, a.dC, NL, p.cgroups, G);
+    }
   }
   return hipGetLastError();
 }

@@ -29,7 +29,7 @@ TOL_BWD = {"f32": 1e-4, "bf16": 2e-2}
 
 
 def run(batch, dim, L, io, seed, gate=True, skip=True, bias=True, softplus=True, h0=True,
-        dlast=True):
+        dlast=True, workspace=None):
     inp = si.scan_inputs(batch, dim, L, io_dtype=io, seed=seed)
     if not softplus:
         # Delta = delta + bias taken as is: keep it positive (a negative step
@@ -50,7 +50,8 @@ def run(batch, dim, L, io, seed, gate=True, skip=True, bias=True, softplus=True,
     ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], checkpoints=ck, **kw)
     g = ssm.selective_scan_bwd(torch.from_numpy(dout).to(DEV).to(tio), t["u"], t["delta"], t["A"],
                                t["B"], t["C"], ck,
-                               dlast=None if dl is None else torch.from_numpy(dl).to(DEV), **kw)
+                               dlast=None if dl is None else torch.from_numpy(dl).to(DEV),
+                               workspace=workspace, **kw)
     torch.cuda.synchronize()
     ref = oracle.selective_scan_bwd(dout, inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
                                     D=inp["D"] if skip else None, z=inp["z"] if gate else None,
@@ -76,9 +77,13 @@ def check(errs, io, label):
     (2, 32, 64, "f32"), (1, 37, 37, "f32"), (2, 13, 100, "f32"), (1, 16, 1000, "f32"),
     (2, 16, 64, "bf16"), (1, 33, 300, "bf16"), (3, 20, 1, "f32"), (2, 5, 17, "bf16"),
 ])
-def test_backward_matches_oracle(batch, dim, L, io):
-    errs, *_ = run(batch, dim, L, io, seed=7 + L + dim)
-    check(errs, io, f"b{batch} d{dim} L{L} {io}")
+@pytest.mark.parametrize("path", ["partials", "atomics"])
+def test_backward_matches_oracle(batch, dim, L, io, path):
+    """dB/dC from per-block partial sums (the binding's default workspace) and
+    from device atomics (workspace=False)."""
+    errs, *_ = run(batch, dim, L, io, seed=7 + L + dim,
+                   workspace=None if path == "partials" else False)
+    check(errs, io, f"b{batch} d{dim} L{L} {io} {path}")
 
 
 @pytest.mark.parametrize("gate,skip,bias,softplus,h0,dlast", [
@@ -108,11 +113,13 @@ def test_forward_checkpoints_are_the_block_entry_states():
         assert e <= 1e-4
 
 
-def test_backward_config1_full_size():
+@pytest.mark.parametrize("path", ["partials", "atomics"])
+def test_backward_config1_full_size(path):
     """The 130m-like layer (batch 8, d_inner 1536, L 2048, fp32) end to end."""
     cfg = si.SCAN_CONFIGS[1]
-    errs, *_ = run(cfg.batch, cfg.dim, cfg.seqlen, "f32", seed=cfg.seed, h0=False, dlast=False)
-    check(errs, "f32", "130m-like layer")
+    errs, *_ = run(cfg.batch, cfg.dim, cfg.seqlen, "f32", seed=cfg.seed, h0=False, dlast=False,
+                   workspace=None if path == "partials" else False)
+    check(errs, "f32", f"130m-like layer {path}")
 
 
 def test_backward_zero_length():
@@ -162,10 +169,10 @@ def test_autograd_op_matches_oracle_gradients(io):
 @pytest.mark.parametrize("dim,G,L,io", [(2576, 0, 40, "f32"), (2576, 0, 33, "bf16"),
                                         (5120, 2, 24, "f32")])
 def test_backward_partial_sums_match_oracle(dim, G, L, io):
-    """At least 160 blocks of 16 channels per B/C group: dB and dC come from
-    per-block partial sums in the workspace and a second summing pass, not
-    from atomics.  Checked against the oracle, and dB/dC against the atomic
-    path (workspace=False) on the same inputs."""
+    """Many blocks of 16 channels per B/C group: dB and dC come from per-block
+    partial sums in the workspace and a second summing pass.  Checked against
+    the oracle, and dB/dC against the atomic path (workspace=False) on the
+    same inputs."""
     inp = si.scan_inputs(1, dim, L, io_dtype=io, seed=dim + L, ngroups=G)
     rng = np.random.default_rng(dim)
     dout = rng.standard_normal((1, dim, L)).astype(np.float32)
