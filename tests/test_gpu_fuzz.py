@@ -1,4 +1,4 @@
-"""Seeded random-shape parity sweep of every entry point against the fp64
+"""Seeded random-shape parity sweep of every entry point (the backward too) against the fp64
 oracle, through the C ABI: shapes off every tile grid (channels, tokens,
 states, heads, head sizes), optional inputs switched on and off at random,
 B/C groups, strided views.  The cases are drawn from a fixed seed, so the
@@ -137,3 +137,59 @@ def test_ssd_random_shapes(i):
     print(f"[fuzz ssd {i} b{batch} L{L} H{H} P{P} G{G} N{N} {io} gate{gate} skip{skip} "
           f"h0{h0}] err_out={e:.2e} err_last={el:.2e}", flush=True)
     assert e <= TOL[io] and el <= TOL[io]
+
+
+TOL_BWD = {"f32": 1e-4, "bf16": 2e-2}   # the backward's bars, as in test_gpu_bwd_parity
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_backward_random_shapes(i):
+    """The scan backward at random shapes (d_state 16; B/C groups of whole
+    16-channel blocks), optional inputs on and off, dB/dC from partial sums
+    or from atomics, after the forward that writes its checkpoints."""
+    rng = np.random.default_rng(7000 + i)
+    io = "f32" if i % 2 == 0 else "bf16"
+    batch = int(rng.integers(1, 4))
+    L = int(rng.integers(1, 8)) if rng.random() < 0.2 else int(rng.integers(1, 301))
+    if rng.random() < 0.35:   # G groups of 16 or 32 channels
+        G = int(rng.integers(2, 5))
+        dim = 16 * G * int(rng.integers(1, 3))
+    else:
+        G, dim = 0, int(rng.integers(1, 81))
+    gate, skip, bias = (bool(rng.random() < 0.7) for _ in range(3))
+    softplus, h0, dlast = bool(rng.random() < 0.8), bool(rng.random() < 0.5), bool(rng.random() < 0.5)
+    path = "partials" if rng.random() < 0.5 else "atomics"
+    inp = si.scan_inputs(batch, dim, L, io_dtype=io, seed=8000 + i, ngroups=G)
+    if not softplus:   # a positive step taken as is
+        inp["delta"] = si._to_io(np.abs(inp["delta"].astype(np.float32)) + np.float32(0.01), io)
+        inp["delta_bias"] = np.zeros_like(inp["delta_bias"])
+    h0v = rng.standard_normal((batch, dim, 16)).astype(np.float32) if h0 else None
+    dl = rng.standard_normal((batch, dim, 16)).astype(np.float32) if dlast else None
+    dout = rng.standard_normal((batch, dim, L)).astype(np.float32)
+    if io == "bf16":
+        dout = si.bf16_round(dout)
+    t = si.to_torch(inp, DEV)
+    ck = torch.empty(ssm.checkpoint_shape(batch, dim, L), dtype=torch.float32, device=DEV)
+    kw = dict(D=t["D"] if skip else None, z=t["z"] if gate else None,
+              delta_bias=t["delta_bias"] if bias else None, delta_softplus=softplus,
+              h0=None if h0v is None else torch.from_numpy(h0v).to(DEV))
+    ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], checkpoints=ck, **kw)
+    g = ssm.selective_scan_bwd(torch.from_numpy(dout).to(DEV).to(t["u"].dtype), t["u"], t["delta"],
+                               t["A"], t["B"], t["C"], ck,
+                               dlast=None if dl is None else torch.from_numpy(dl).to(DEV),
+                               workspace=None if path == "partials" else False, **kw)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan_bwd(dout, inp["u"], inp["delta"], inp["A"], inp["B"], inp["C"],
+                                    D=inp["D"] if skip else None, z=inp["z"] if gate else None,
+                                    delta_bias=inp["delta_bias"] if bias else None,
+                                    delta_softplus=softplus, h0=h0v, dlast=dl)
+    errs = {}
+    for k, r in ref.items():
+        got = to_np(g[k])
+        assert got.shape == r.shape, k
+        errs[k] = row_rel_err(got[None], r[None]) if k in ("dD", "ddelta_bias") else row_rel_err(got, r)
+    print(f"[fuzz bwd {i} b{batch} d{dim} L{L} G{G} {io} gate{gate} skip{skip} bias{bias} "
+          f"sp{softplus} h0{h0} dlast{dlast} {path}] "
+          + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= TOL_BWD[io], (k, v)
