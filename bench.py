@@ -391,6 +391,8 @@ def main():
                          "(10 launches) that calibrates the HBM byte counters; for rocprofv3")
     ap.add_argument("--profile-ssd", action="store_true",
                     help="only the Mamba-2 SSD layer (10 launches); for rocprofv3")
+    ap.add_argument("--profile-bwd", action="store_true",
+                    help="only the scan backward of the 130m-like layer (10 launches); for rocprofv3")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -421,6 +423,18 @@ def main():
                              dt_bias=t["dt_bias"], out=out)
         torch.cuda.synchronize()
         log(f"[profile] 10 launches of the SSD layer {cs.name}")
+        return
+    if args.profile_bwd:
+        t = si.to_torch(si.scan_inputs_for(head), "cuda")
+        ck = torch.empty(ssm.checkpoint_shape(head.batch, head.dim, head.seqlen),
+                         dtype=torch.float32, device="cuda")
+        kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"])
+        ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], checkpoints=ck, **kw)
+        dout = torch.randn_like(t["u"])
+        for _ in range(10):
+            ssm.selective_scan_bwd(dout, t["u"], t["delta"], t["A"], t["B"], t["C"], ck, **kw)
+        torch.cuda.synchronize()
+        log(f"[profile] 10 launches of the scan backward on {head.name}")
         return
     log(f"[bench] headline {head.name}: warmup {args.warmup}, steps {args.steps}")
     r = bench_scan(head, args.steps, args.warmup, torch, ssm, si)

@@ -53,6 +53,20 @@ constexpr int kGPitch = kGT + 4;     // LDS pitch (floats) of one state's tile r
 constexpr int kPitch = 20;           // LDS pitch (floats) of one state's 16 token terms
 constexpr int kPartRow = kN * kPitch + 16;  // floats per channel of per-token terms
 
+// Sums over the four 16-lane rows of a wavefront by lane swaps (no LDS).
+// swap_add32(a, b): rows 0..3 hold a0+a2, a1+a3, b0+b2, b1+b3.
+__device__ __forceinline__ float swap_add32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// swap_add16(x, y): rows 0..3 hold x0+x1, y0+y1, x2+x3, y2+y3.  Applied to
+// x = swap_add32(a, b) and y = swap_add32(c, d) it leaves the four-row sums
+// of a, c, b, d in rows 0, 1, 2, 3.
+__device__ __forceinline__ float swap_add16(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 struct BwdParams {
   const void* u;
   const void* delta;
@@ -110,7 +124,9 @@ struct BwdWave {
   float (*sC)[kN][kGPitch];
   float (*sX)[kPartRow];      // this wavefront's [kRows][kPartRow]: readout, then the
                               // per-state du/ddelta terms of half a block
-  float (*sR)[kCh][kN][kT / 2];  // [2][kCh][kN][kT/2], shared: dB, dC terms per channel
+  float (*sQ)[kRows][kN][4];   // [kWaves][kRows][kN][4], shared: dB/dC terms of half a
+                              // block summed over each wavefront's channels; row r
+                              // holds tensor r / 2 (dB, dC), tokens 4 (r % 2) + 0..3
 
   static constexpr int E = Elem<T>::kSize;
 
@@ -217,10 +233,14 @@ struct BwdWave {
     // each broadcast folds into its one consumer).  After each half: the
     // owners of its 8 tokens finish du/ddelta from the per-state terms, and
     // the workgroup's 256 threads sum the dB/dC terms over its channels.
-    const float dl2 = opaque_copy(dl), du2 = opaque_copy(du), dy2 = opaque_copy(dy);
+    // channels past dim (their rows repeat the last channel) add nothing to
+    // dB/dC: their Delta u and dy copies for those terms are zero
+    const bool rv = kRows * wave + row < nvalid;
+    const float dl2 = opaque_copy(dl), du2 = opaque_copy(rv ? du : 0.0f),
+                dy2 = opaque_copy(rv ? dy : 0.0f);
     float sxm = 0.0f;  // softplus'(x) for this owner's token
     if (kSoftplus) sxm = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
-    float s1[4], s2[4], rb[4], rc[4];
+    float s1[4], s2[4], yq[4], rq[4];
     static_for<0, kT>([&](auto J) {
       constexpr int j = kT - 1 - decltype(J)::value;
       constexpr int h8 = j / 8;          // which half
@@ -231,8 +251,12 @@ struct BwdWave {
       const float q = adj * (e[j] * hp);
       s1[j % 4] = adj * bv[j];                                     // -> du, ddelta
       s2[j % 4] = q * a;                                           // -> ddelta
-      rb[j % 4] = row_bcast<j>(du2) * adj;                         // -> dB
-      rc[j % 4] = row_bcast<j>(dy2) * hs[j];                       // -> dC
+      const float rb = row_bcast<j>(du2) * adj;                    // -> dB
+      const float rc = row_bcast<j>(dy2) * hs[j];                  // -> dC
+      // summed over the wavefront's four channels as they come: tokens 4..7
+      // of the half pair with tokens 0..3 (row layout of sQ)
+      if constexpr (jj >= 4) yq[jj - 4] = swap_add32(rb, rc);
+      else rq[jj] = swap_add16(swap_add32(rb, rc), yq[jj]);
       dA = fmaf(row_bcast<j>(dl2), q, dA);
       g = e[j] * adj;                                              // adjoint of h_{t-1}
       if constexpr (j % 4 == 0) {
@@ -240,12 +264,9 @@ struct BwdWave {
         *reinterpret_cast<float4*>(&sX[row][col * kPitch + jj]) = make_float4(s1[0], s1[1], s1[2], s1[3]);
         *reinterpret_cast<float4*>(&sX[row][col * kPitch + 8 + jj]) =
             make_float4(s2[0], s2[1], s2[2], s2[3]);
-        *reinterpret_cast<float4*>(&sR[0][kRows * wave + row][col][jj]) =
-            make_float4(rb[0], rb[1], rb[2], rb[3]);
-        *reinterpret_cast<float4*>(&sR[1][kRows * wave + row][col][jj]) =
-            make_float4(rc[0], rc[1], rc[2], rc[3]);
       }
       if constexpr (jj == 0) {
+        *reinterpret_cast<float4*>(&sQ[wave][row][col][0]) = make_float4(rq[0], rq[1], rq[2], rq[3]);
         __syncthreads();
         // owners of tokens 8 h8 .. 8 h8 + 7: du, ddelta (lanes of the other
         // half compute and discard)
@@ -273,8 +294,10 @@ struct BwdWave {
         // dB, dC: thread (tensor, n, t) sums the workgroup's channels
         const int tid = threadIdx.x;
         const int ten = tid >> 7, n = (tid >> 3) & 15, t = tid & 7;
-        float sum = 0.0f;
-        for (int c = 0; c < nvalid; ++c) sum += sR[ten][c][n][t];  // rows past dim: repeats
+        const int qr = 2 * ten + (t >> 2), qt = t & 3;
+        float sum = sQ[0][qr][n][qt];
+#pragma unroll
+        for (int v = 1; v < kWaves; ++v) sum += sQ[v][qr][n][qt];
         // Tokens past the end address the window's end, where the store or
         // atomic is dropped: their offsets would otherwise reach into later
         // states' rows, and a plain store there (the partial sums) races with
@@ -297,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   __shared__ __align__(16) float sB[2][kN][kGPitch];
   __shared__ __align__(16) float sC[2][kN][kGPitch];
   __shared__ __align__(16) float sX[kWaves][kRows][kPartRow];
-  __shared__ __align__(16) float sR[2][kCh][kN][kT / 2];
+  __shared__ __align__(16) float sQ[kWaves][kRows][kN][4];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = (threadIdx.x >> 4) & 3;
@@ -362,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   w.a2 = w.a * kLog2e;
   w.bias = p.bias ? p.bias[dc] : 0.0f;
   w.Dd = p.D ? p.D[dc] : 0.0f;
-  w.sB = sB; w.sC = sC; w.sX = sX[wave]; w.sR = sR;
+  w.sB = sB; w.sC = sC; w.sX = sX[wave]; w.sQ = sQ;
 
   float g = p.dlast ? p.dlast[(b * p.dim + dc) * kN + col] : 0.0f;
   float dA = 0.0f, dDs = 0.0f, dbs = 0.0f;
