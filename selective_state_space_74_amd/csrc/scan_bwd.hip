@@ -53,6 +53,11 @@ constexpr int kGPitch = kGT + 4;     // LDS pitch (floats) of one state's tile r
 constexpr int kPitch = 20;           // LDS pitch (floats) of one state's 16 token terms
 constexpr int kPartRow = kN * kPitch + 16;  // floats per channel of per-token terms
 
+// The value held by lane col ^ 8 of the same 16-lane row (DPP row_ror:8).
+__device__ __forceinline__ float row_swap8(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, true));
+}
+
 // Sums over the four 16-lane rows of a wavefront by lane swaps (no LDS).
 // swap_add32(a, b): rows 0..3 hold a0+a2, a1+a3, b0+b2, b1+b3.
 __device__ __forceinline__ float swap_add32(float a, float b) {
@@ -268,17 +273,21 @@ struct BwdWave {
       if constexpr (jj == 0) {
         *reinterpret_cast<float4*>(&sQ[wave][row][col][0]) = make_float4(rq[0], rq[1], rq[2], rq[3]);
         __syncthreads();
-        // owners of tokens 8 h8 .. 8 h8 + 7: du, ddelta (lanes of the other
-        // half compute and discard)
+        // owners of tokens 8 h8 .. 8 h8 + 7: du, ddelta.  The sums over the
+        // 16 states for token ti: lanes col and col ^ 8 each add 8 states'
+        // terms and then exchange, so both hold the sum (the owner is the
+        // one in this half; the other discards it)
         const int tj = col - 8 * h8;
         const bool mine = own && tj >= 0 && tj < 8;
-        const int ti = tj & 7;
+        const int ti = col & 7, n0 = col & 8;
         float S1 = 0.0f, S2 = 0.0f;
 #pragma unroll
-        for (int n = 0; n < kN; ++n) {
-          S1 += sX[row][n * kPitch + ti];
-          S2 += sX[row][n * kPitch + 8 + ti];
+        for (int n = 0; n < kN / 2; ++n) {
+          S1 += sX[row][(n0 + n) * kPitch + ti];
+          S2 += sX[row][(n0 + n) * kPitch + 8 + ti];
         }
+        S1 += row_swap8(S1);
+        S2 += row_swap8(S2);
         const float duv = fmaf(dl, S1, dy * Dd);
         float dx = fmaf(uv, S1, S2);
         if (kSoftplus) dx *= sxm;
