@@ -190,8 +190,9 @@ typedef struct ssm_scan_args {
  *   dD, ddelta_bias : (dim) fp32 (summed over batch, time); NULL: not wanted.
  *   dh0             : (batch, dim, dstate) fp32, contiguous; NULL: not wanted.
  * The sums over channels (dB, dC) and over batch rows (dA, dD, ddelta_bias)
- * are accumulated with device atomics, so their last bits can vary from run
- * to run; every other output is deterministic.  Outputs must not overlap
+ * are accumulated with device atomics when no workspace is given, so their
+ * last bits can vary from run to run; with a workspace every output is
+ * deterministic.  Outputs must not overlap
  * each other or any input.  The backward runs every sequence as one segment.
  * It is built for dstate == 16 and for B/C groups that keep each block of 16
  * consecutive channels in one group (one group, or dim / ngroups a multiple
@@ -199,8 +200,9 @@ typedef struct ssm_scan_args {
  * Workspace (optional): device scratch owned by the caller, 4-byte aligned,
  * of at least ssm_scan_bwd_workspace_size() bytes, not overlapping any
  * tensor.  The library then writes each block of 16 channels' dB/dC partial
- * sums there with plain stores and adds them in a second pass, instead of
- * adding into dB/dC with device atomics; dB and dC are then deterministic,
+ * sums, and each batch row's dA, dD and ddelta_bias, there with plain
+ * stores and adds them in fixed order in second passes, instead of adding
+ * into the outputs with device atomics: every output is then deterministic,
  * and the time no longer depends on where dB and dC sit (the atomics on
  * dB(n, t) and dC(n, t) are issued together and at some offsets between the
  * two buffers share memory channels).  With workspace NULL or too small the
@@ -346,7 +348,8 @@ size_t ssm_ssd_args_size(void);
 size_t ssm_scan_workspace_size(const ssm_scan_args* args);
 
 /* Workspace bytes the backward can use for this argument block:
- * batch * ceil(dim / 16) * 2 * 16 * seqlen fp32 values (0 for an empty
+ * batch * ceil(dim / 16) * 2 * 16 * seqlen + batch * dim * 18 fp32 values
+ * (0 for an empty
  * sequence or when batch * ngroups exceeds 65535, where it adds dB/dC with
  * atomics anyway).  Reads only sizes; pure host code. */
 size_t ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args* args);

@@ -473,9 +473,10 @@ def selective_scan_bwd(dout, u, delta, A, B, C, checkpoints, D=None, z=None, del
     (and dlast on last_state), from the checkpoints that forward wrote.
     Returns a dict: du, ddelta (IO dtype, shaped like u), dB, dC (fp32, like
     B), dA (fp32, like A) and, for the inputs that were given, dz, dD,
-    ddelta_bias, dh0 (fp32).  dA, dD and ddelta_bias are summed with device
-    atomics (their last bits may vary between runs); dB and dC are summed
-    from per-block partials in a workspace, or with atomics without one.
+    ddelta_bias, dh0 (fp32).  The sums over channels (dB, dC) and batch rows
+    (dA, dD, ddelta_bias) are formed from partials in a workspace, in fixed
+    order (deterministic), or with device atomics without one (their last
+    bits may then vary between runs).
     `workspace`: a device tensor reused across calls; None allocates one of
     the size the library asks for (up to BWD_WORKSPACE_AUTO_MAX bytes);
     False passes none (dB/dC then always by atomics)."""

@@ -94,6 +94,9 @@ struct BwdParams {
   float* dbias;
   float* dh0;
   float* part;          // [batch][cgroups][2][kN][L] dB/dC partial sums, or NULL (atomics)
+  float* pdA;           // with part: [batch][dim][kN] dA, [batch][dim] dD and bias
+  float* pdD;           // gradient per batch row, summed over rows by a second
+  float* pdb;           // kernel (NULL: device atomics into dA, dD, dbias)
   int64_t usb, usd, dsb, dsd, zsb, zsd, Bsb, Bsn, Csb, Csn, Asd, Asn, gsb, gsd;
   int64_t dusb, dusd, ddsb, ddsd, dzsb, dzsd;
   int64_t Bsg, Csg;     // B/C group strides
@@ -421,7 +424,10 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   }
 
   if (vrow && p.dh0) p.dh0[(b * p.dim + d) * kN + col] = g;
-  if (vrow) atomicAdd(&p.dA[d * kN + col], dA);
+  if (vrow) {
+    if (p.pdA) p.pdA[(b * p.dim + d) * kN + col] = dA;
+    else atomicAdd(&p.dA[d * kN + col], dA);
+  }
   // dD and the bias gradient: sum the 16 owner lanes of the row
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) {
@@ -429,8 +435,34 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     dbs += __shfl_xor(dbs, m, 16);
   }
   if (vrow && col == 0) {
-    if (p.dD) atomicAdd(&p.dD[d], dDs);
-    if (p.dbias) atomicAdd(&p.dbias[d], dbs);
+    if (p.pdA) {
+      p.pdD[b * p.dim + d] = dDs;
+      p.pdb[b * p.dim + d] = dbs;
+    } else {
+      if (p.dD) atomicAdd(&p.dD[d], dDs);
+      if (p.dbias) atomicAdd(&p.dbias[d], dbs);
+    }
+  }
+}
+
+// dA, dD and the bias gradient from the per-batch-row partials, summed over
+// the rows in row order.
+__global__ void param_sum_kernel(const float* pdA, const float* pdD, const float* pdb, float* dA,
+                                 float* dD, float* dbias, int64_t batch, int64_t dim) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < dim * kN) {
+    float s = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) s += pdA[b * dim * kN + i];
+    dA[i] = s;
+  }
+  if (i < dim) {
+    float sd = 0.0f, sb = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) {
+      sd += pdD[b * dim + i];
+      sb += pdb[b * dim + i];
+    }
+    if (dD) dD[i] = sd;
+    if (dbias) dbias[i] = sb;
   }
 }
 
@@ -521,19 +553,23 @@ size_t scan_bwd_workspace_bytes(const ssm_scan_bwd_args& a) {
   const int64_t cgroups = (a.dim + kCh - 1) / kCh;
   if (a.batch <= 0 || a.dim <= 0 || a.seqlen <= 0) return 0;
   if (a.batch * G > 65535) return 0;   // the sum pass runs one grid row per (batch, group)
-  return static_cast<size_t>(a.batch * cgroups * 2 * kN * a.seqlen) * sizeof(float);
+  // dB/dC partials per channel block, then dA, dD and the bias gradient per batch row
+  return static_cast<size_t>(a.batch * cgroups * 2 * kN * a.seqlen + a.batch * a.dim * (kN + 2)) *
+         sizeof(float);
 }
 
 hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
-  // zero what the kernel accumulates into (dB/dC only when added atomically)
   const int64_t G = a.ngroups > 1 ? a.ngroups : 1;
   const int64_t nbc = a.batch * G * a.dstate * a.seqlen;
   const size_t wneed = scan_bwd_workspace_bytes(a);
   const bool partials = wneed > 0 && a.workspace && a.workspace_bytes >= wneed;
-  const int64_t nz = partials ? 0 : nbc;
-  const int64_t nmax = std::max<int64_t>(nz, a.dim * a.dstate);
-  zero_kernel<<<dim3(static_cast<unsigned>((nmax + 255) / 256)), dim3(256), 0, stream>>>(
-      a.dB, nz, a.dC, nz, a.dA, a.dim * a.dstate, a.dD, a.dim, a.ddelta_bias, a.dim);
+  // Without the workspace, zero what the kernel adds into with atomics (with
+  // it, every output is written whole by plain stores).
+  if (!partials) {
+    const int64_t nmax = std::max<int64_t>(nbc, a.dim * a.dstate);
+    zero_kernel<<<dim3(static_cast<unsigned>((nmax + 255) / 256)), dim3(256), 0, stream>>>(
+        a.dB, nbc, a.dC, nbc, a.dA, a.dim * a.dstate, a.dD, a.dim, a.ddelta_bias, a.dim);
+  }
   if (a.seqlen == 0) {
     // no token: the gradient reaching h0 is dlast itself
     if (a.dh0) {
@@ -553,6 +589,9 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
   p.du = a.du; p.ddelta = a.ddelta; p.dz = a.dz;
   p.dB = a.dB; p.dC = a.dC; p.dA = a.dA; p.dD = a.dD; p.dbias = a.ddelta_bias; p.dh0 = a.dh0;
   p.part = partials ? static_cast<float*>(a.workspace) : nullptr;
+  p.pdA = partials ? p.part + a.batch * ((a.dim + kCh - 1) / kCh) * 2 * kN * a.seqlen : nullptr;
+  p.pdD = partials ? p.pdA + a.batch * a.dim * kN : nullptr;
+  p.pdb = partials ? p.pdD + a.batch * a.dim : nullptr;
   p.usb = a.u_batch_stride; p.usd = a.u_dim_stride;
   p.dsb = a.delta_batch_stride; p.dsd = a.delta_dim_stride;
   p.zsb = a.z_batch_stride; p.zsd = a.z_dim_stride;
@@ -591,6 +630,8 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
       partial_sum_kernel<float><<<dim3(static_cast<unsigned>(cols), static_cast<unsigned>(a.batch * G)),
                                   sblock, 0, stream>>>(p.part, a.dB, a.dC, NL, p.cgroups, G);
     }
+    param_sum_kernel<<<dim3(static_cast<unsigned>((a.dim * kN + 255) / 256)), dim3(256), 0, stream>>>(
+        p.pdA, p.pdD, p.pdb, a.dA, a.dD, a.ddelta_bias, a.batch, a.dim);
   }
   return hipGetLastError();
 }

@@ -283,15 +283,19 @@ def good_bwd(batch=2, dim=32, L=64, N=16, io=0, z=True):
 
 
 def test_bwd_workspace_size():
-    """The partial-sum workspace: batch * blocks of 16 channels * 2 * 16 * L
-    fp32 values, for any grouping; none for an empty sequence, for more than
-    65535 (batch, group) rows, or for shapes the backward does not take."""
-    assert ssm.scan_bwd_workspace_size(good_bwd(batch=2, dim=96 * 16, L=64)) == 2 * 96 * 2 * 16 * 64 * 4
-    assert ssm.scan_bwd_workspace_size(good_bwd(batch=1, dim=5, L=3)) == 1 * 1 * 2 * 16 * 3 * 4
+    """The backward workspace: the dB/dC partials (batch * blocks of 16
+    channels * 2 * 16 * L fp32 values) and the per-batch-row dA, dD and bias
+    gradients (batch * dim * 18), for any grouping; none for an empty
+    sequence, for more than 65535 (batch, group) rows, or for shapes the
+    backward does not take."""
+    def want(batch, dim, L):
+        return (batch * -(-dim // 16) * 2 * 16 * L + batch * dim * 18) * 4
+    assert ssm.scan_bwd_workspace_size(good_bwd(batch=2, dim=96 * 16, L=64)) == want(2, 96 * 16, 64)
+    assert ssm.scan_bwd_workspace_size(good_bwd(batch=1, dim=5, L=3)) == want(1, 5, 3)
     a = good_bwd(batch=2, dim=320 * 16, L=64)
-    assert ssm.scan_bwd_workspace_size(a) == 2 * 320 * 2 * 16 * 64 * 4
+    assert ssm.scan_bwd_workspace_size(a) == want(2, 320 * 16, 64)
     a.ngroups, a.B_group_stride, a.C_group_stride = 4, 16 * 64, 16 * 64
-    assert ssm.scan_bwd_workspace_size(a) == 2 * 320 * 2 * 16 * 64 * 4
+    assert ssm.scan_bwd_workspace_size(a) == want(2, 320 * 16, 64)
     assert ssm.scan_bwd_workspace_size(good_bwd(batch=70000, dim=16, L=4)) == 0
     assert ssm.scan_bwd_workspace_size(good_bwd(dim=320 * 16, L=0)) == 0
     assert ssm.scan_bwd_workspace_size(good_bwd(dim=320 * 16, N=32)) == 0
