@@ -27,6 +27,11 @@ __global__ void copy_state_kernel(const float* h0, float* last, int64_t n) {
 constexpr int64_t kTargetGroups = 1280;   // 5 wavefronts per SIMD on 256 CUs
 constexpr int64_t kMinSegLen = 8192;
 constexpr int kMaxSeg = 64;
+// Grids of at most this many workgroups leave three wavefronts per SIMD on
+// 256 CUs whatever a kernel's register count; there the one-slot scan takes
+// the deferred owner-C readout (more registers, the LDS round trip of the
+// readout covered).  Larger grids keep the compact form's occupancy.
+constexpr int64_t kDeferMaxGroups = 768;
 
 int choose_segments(int64_t groups, int64_t L) {
   if (groups >= kTargetGroups / 2) return 1;
@@ -139,11 +144,12 @@ hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {
                     a.C_batch_stride % vw == 0 && a.C_group_stride % vw == 0 &&
                     a.C_state_stride % vw == 0;
   const int lane = lane_bc(a) ? (lvec ? 2 : 1) : 0;
+  const bool defer = groups * p.nseg <= kDeferMaxGroups;
   auto run = [&](bool aggregate, dim3 grid) {
     switch (slots(a.dstate)) {
-      case 1: fwd::launch_slots<1>(aggregate, lane, bf16, sp, p.K, grid, p, stream); break;
-      case 2: fwd::launch_slots<2>(aggregate, lane, bf16, sp, p.K, grid, p, stream); break;
-      default: fwd::launch_slots<4>(aggregate, lane, bf16, sp, p.K, grid, p, stream); break;
+      case 1: fwd::launch_slots<1>(aggregate, lane, bf16, sp, p.K, defer, grid, p, stream); break;
+      case 2: fwd::launch_slots<2>(aggregate, lane, bf16, sp, p.K, defer, grid, p, stream); break;
+      default: fwd::launch_slots<4>(aggregate, lane, bf16, sp, p.K, defer, grid, p, stream); break;
     }
   };
   if (p.nseg > 1) run(true, dim3((unsigned)(groups * (p.nseg - 1))));

@@ -131,7 +131,7 @@ __device__ __forceinline__ float row_ror(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + M, 0xf, 0xf, true));
 }
 
-template <typename T, Mode M, bool kSoftplus, int KP, int S, int kLane>
+template <typename T, Mode M, bool kSoftplus, int KP, int S, int kLane, bool kDefer>
 struct Wave {
   const ScanParams& p;
   int wave, row, col;
@@ -162,9 +162,15 @@ struct Wave {
   // C is then staged token-major.
   static constexpr bool kOwnerC = S == 1 && !kLane && M == Mode::kScan;
   // token of the scan after which the owner's C column is read, so that the
-  // read is in flight during the rest of the scan rather than exposed at the
-  // end of the block
+  // read is in flight during the rest of the scan
   static constexpr int kCRead = 7;
+  // Owner-C readout deferred to the top of the next block (kDefer): the
+  // block's states are read back from LDS there and contracted after the
+  // next block's owner work, which covers the LDS round trip; the C column
+  // is carried in registers across the block boundary.  Costs about 30
+  // VGPRs (128), so it is launched only where the grid leaves three
+  // wavefronts per SIMD anyway.
+  static_assert(!kDefer || kOwnerC, "the deferred readout is an owner-C form");
 
   __device__ __forceinline__ uint32_t skip(int k) const {
     return static_cast<uint32_t>(t_beg + k * kT) * E;
@@ -302,19 +308,24 @@ struct Wave {
   template <bool kMask, bool kEnd>
   __device__ __forceinline__ void iter(int k, float (&h)[S], double& ssum, const Raw& P,
                                        const Raw& Q, Raw& R, GroupRaw<S>& G, float& uprev,
-                                       float& xprev) const {
+                                       float& xprev, float (&cl)[kN]) const {
     // B/C of the first state slot and the previous block's partials first
     float bv[kT], cv[kT];
     bc<kMask>(k, 0, bv, cv);
     float ysum = 0.0f;
-    if (M == Mode::kScan && !kOwnerC) {
-      // unconditional: at k = 0 the value is never used; summed right away so
-      // that one register, not sixteen, lives across the scan
-      float part[kN];
+    float part[kN];
+    if (M == Mode::kScan && (!kOwnerC || kDefer)) {
+      // The previous block's readout inputs from this wavefront's LDS region,
+      // read before this block's own stores there (a wavefront's LDS
+      // operations complete in order); unconditional: at k = 0 they are never
+      // used.  Without owner-C they are summed right away so that one
+      // register, not sixteen, lives across the scan.
 #pragma unroll
       for (int n = 0; n < kN; ++n) part[n] = sP[row][n * kPitch + col];
+      if constexpr (!kOwnerC) {
 #pragma unroll
-      for (int n = 0; n < kN; ++n) ysum += part[n];
+        for (int n = 0; n < kN; ++n) ysum += part[n];
+      }
     }
     R = load(k + 2);
 
@@ -348,6 +359,13 @@ struct Wave {
       du = own ? du : 0.0f;
     }
     if (M == Mode::kAggregate) ssum += static_cast<double>(dl);
+    if constexpr (kDefer) {
+      // the previous block's readout: its states (read above) against its
+      // token's C column (read during its scan), after this block's owner
+      // work so that the LDS reads above are not waited on right away
+#pragma unroll
+      for (int n = 0; n < kN; ++n) ysum = fmaf(cl[n], part[n], ysum);
+    }
 
     // checkpoint: the states entering this block (an empty window when none
     // are kept, and an offset past the window for padding slots, so the
@@ -362,7 +380,6 @@ struct Wave {
     // slot
     // one slot: a rolling 4-register buffer; several: one sum per token
     float pk[S == 1 ? 4 : kT];
-    float cl[kN];   // kOwnerC: this token's C column (this group's tile buffer)
     static_for<0, S>([&](auto Qs) {
       constexpr int q = decltype(Qs)::value;
       if constexpr (q > 0) {
@@ -393,12 +410,11 @@ struct Wave {
         }
       });
     });
-    if constexpr (kOwnerC) {
+    if constexpr (kOwnerC && !kDefer) {
       // this block's readout right away: y = sum_n C_n h_n from the h the
       // state lanes just left in LDS and this token's C column of the tile
       // (read during the scan; still this group's buffer: the other one is
       // staged next)
-      float part[kN];
 #pragma unroll
       for (int n = 0; n < kN; ++n) part[n] = sP[row][n * kPitch + col];
 #pragma unroll
@@ -426,11 +442,12 @@ struct Wave {
   }
 };
 
-template <typename T, Mode M, bool kSoftplus, int KP, int S, int kLane>
+template <typename T, Mode M, bool kSoftplus, int KP, int S, int kLane, bool kDefer>
 __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   constexpr int kTile = kLane ? 1 : 2;
   __shared__ __align__(16) float sB[kTile][kN * S][kGPitch];
-  constexpr bool kOC = Wave<T, M, kSoftplus, KP, S, kLane>::kOwnerC;
+  using W = Wave<T, M, kSoftplus, KP, S, kLane, kDefer>;
+  constexpr bool kOC = W::kOwnerC;
   __shared__ __align__(16) float sC[M == Mode::kScan && !kOC ? kTile : 1][kN * S][kGPitch];
   __shared__ __align__(16) float sCt[kOC ? 2 : 1][kOC ? kGT : 1][kCPitch];
   __shared__ __align__(16) float sP[M == Mode::kScan ? kWaves : 1][kRows][kPartRow];
@@ -457,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   const int aggs = N + 1;  // floats per (channel, segment) aggregate: b[N], S
 
   constexpr int E = Elem<T>::kSize;
-  Wave<T, M, kSoftplus, KP, S, kLane> w{p};
+  W w{p};
   w.wave = wave; w.row = row; w.col = col;
   w.t_beg = g * p.seg_len;
   w.t_end = std::min(p.L, w.t_beg + p.seg_len);
@@ -593,30 +610,38 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   // form.
   const int nblk = w.nblk;
   const int nfull = (w.t_end - w.t_beg) / kT;
-  w.template iter<true, false>(0, h, ssum, buf3, buf0, buf2, grp, uprev, xprev);
+  // owner-C: the C column of each block's token, read during the block's scan
+  // (deferred form: used in the next block's readout)
+  float cl[kN];
+#pragma unroll
+  for (int n = 0; n < kN; ++n) cl[n] = 0.0f;
+  w.template iter<true, false>(0, h, ssum, buf3, buf0, buf2, grp, uprev, xprev, cl);
   int k = 1;
   for (; k + 4 <= nfull; k += 4) {
     // k % 4 == 1 here, and 4 is a multiple of kGB
-    w.template iter<false, (1 % kGB == kGB - 1)>(k + 0, h, ssum, buf0, buf1, buf3, grp, uprev, xprev);
-    w.template iter<false, (2 % kGB == kGB - 1)>(k + 1, h, ssum, buf1, buf2, buf0, grp, uprev, xprev);
-    w.template iter<false, (3 % kGB == kGB - 1)>(k + 2, h, ssum, buf2, buf3, buf1, grp, uprev, xprev);
-    w.template iter<false, (4 % kGB == kGB - 1)>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev);
+    w.template iter<false, (1 % kGB == kGB - 1)>(k + 0, h, ssum, buf0, buf1, buf3, grp, uprev, xprev, cl);
+    w.template iter<false, (2 % kGB == kGB - 1)>(k + 1, h, ssum, buf1, buf2, buf0, grp, uprev, xprev, cl);
+    w.template iter<false, (3 % kGB == kGB - 1)>(k + 2, h, ssum, buf2, buf3, buf1, grp, uprev, xprev, cl);
+    w.template iter<false, (4 % kGB == kGB - 1)>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev, cl);
   }
-  if (k < nblk) w.template iter<true, false>(k, h, ssum, buf0, buf1, buf3, grp, uprev, xprev);
-  if (k + 1 < nblk) w.template iter<true, false>(k + 1, h, ssum, buf1, buf2, buf0, grp, uprev, xprev);
-  if (k + 2 < nblk) w.template iter<true, false>(k + 2, h, ssum, buf2, buf3, buf1, grp, uprev, xprev);
-  if (k + 3 < nblk) w.template iter<true, false>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev);
+  if (k < nblk) w.template iter<true, false>(k, h, ssum, buf0, buf1, buf3, grp, uprev, xprev, cl);
+  if (k + 1 < nblk) w.template iter<true, false>(k + 1, h, ssum, buf1, buf2, buf0, grp, uprev, xprev, cl);
+  if (k + 2 < nblk) w.template iter<true, false>(k + 2, h, ssum, buf2, buf3, buf1, grp, uprev, xprev, cl);
+  if (k + 3 < nblk) w.template iter<true, false>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev, cl);
 
   if (M == Mode::kScan) {
-    if constexpr (!kOC) {
-      // finish the last block: its partials are in LDS, its raw inputs in
-      // buffer (nblk - 1) % 4
+    if constexpr (!kOC || kDefer) {
+      // finish the last block: its partials (owner-C: states) are in LDS, its
+      // raw inputs in buffer (nblk - 1) % 4
       const int kl = nblk - 1;
       const int r = kl & 3;
       const Raw last = r == 0 ? buf0 : r == 1 ? buf1 : r == 2 ? buf2 : buf3;
       float ysum = 0.0f;
 #pragma unroll
-      for (int n = 0; n < kN; ++n) ysum += w.sP[row][n * kPitch + col];
+      for (int n = 0; n < kN; ++n) {
+        const float v = w.sP[row][n * kPitch + col];
+        ysum = kOC ? fmaf(cl[n], v, ysum) : ysum + v;
+      }
       w.template finish<true>(kl, last, uprev, ysum);
     }
     if (vrow && p.last_state && g == p.nseg - 1) {
@@ -665,25 +690,34 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
 
 // Launch of one variant family: the dtype, softplus and conv width choose
 // among the instantiations with S state slots per lane and the B/C mode.
-template <Mode M, int KP, int S, int kLane>
+template <Mode M, int KP, int S, int kLane, bool kDefer = false>
 void launch_kp(bool bf16, bool softplus, dim3 grid, const ScanParams& p, hipStream_t stream) {
   const dim3 block(kThreads);
   if (bf16) {
-    if (softplus) scan_fwd_kernel<uint16_t, M, true, KP, S, kLane><<<grid, block, 0, stream>>>(p);
-    else scan_fwd_kernel<uint16_t, M, false, KP, S, kLane><<<grid, block, 0, stream>>>(p);
+    if (softplus) scan_fwd_kernel<uint16_t, M, true, KP, S, kLane, kDefer><<<grid, block, 0, stream>>>(p);
+    else scan_fwd_kernel<uint16_t, M, false, KP, S, kLane, kDefer><<<grid, block, 0, stream>>>(p);
   } else {
-    if (softplus) scan_fwd_kernel<float, M, true, KP, S, kLane><<<grid, block, 0, stream>>>(p);
-    else scan_fwd_kernel<float, M, false, KP, S, kLane><<<grid, block, 0, stream>>>(p);
+    if (softplus) scan_fwd_kernel<float, M, true, KP, S, kLane, kDefer><<<grid, block, 0, stream>>>(p);
+    else scan_fwd_kernel<float, M, false, KP, S, kLane, kDefer><<<grid, block, 0, stream>>>(p);
   }
 }
 
 // The conv width is padded to 4 or 8 taps (zero weights); only the
 // one-slot shared-B/C kernels, the common Mamba-1 shape, get the 4-tap form.
 // B/C modes: 0 shared tile, 1 per-lane element loads, 2 per-lane 16-byte
-// loads (aligned rows; without the conv branch).
+// loads (aligned rows; without the conv branch).  `defer` picks the
+// deferred owner-C readout for the one-slot shared-tile scan (no conv or the
+// 4-tap one).
 template <Mode M, int S>
-void launch_mode(int lane, bool bf16, bool softplus, int K, dim3 grid, const ScanParams& p,
-                 hipStream_t stream) {
+void launch_mode(int lane, bool bf16, bool softplus, int K, bool defer, dim3 grid,
+                 const ScanParams& p, hipStream_t stream) {
+  if constexpr (M == Mode::kScan && S == 1) {
+    if (defer && lane == 0 && K <= 4) {
+      if (K == 0) launch_kp<M, 0, S, 0, true>(bf16, softplus, grid, p, stream);
+      else launch_kp<M, 4, S, 0, true>(bf16, softplus, grid, p, stream);
+      return;
+    }
+  }
   if (lane == 0) {
     if (K == 0) launch_kp<M, 0, S, 0>(bf16, softplus, grid, p, stream);
     else if (K <= 4 && S == 1) launch_kp<M, 4, S, 0>(bf16, softplus, grid, p, stream);
@@ -699,7 +733,7 @@ void launch_mode(int lane, bool bf16, bool softplus, int K, dim3 grid, const Sca
 // Both passes' launches for S state slots per lane (defined in
 // scan_fwd_s<S>.hip).
 template <int S>
-void launch_slots(bool aggregate, int lane, bool bf16, bool softplus, int K, dim3 grid,
+void launch_slots(bool aggregate, int lane, bool bf16, bool softplus, int K, bool defer, dim3 grid,
                   const ScanParams& p, hipStream_t stream);
 
 }  // namespace fwd

@@ -6,10 +6,10 @@ namespace ssm {
 namespace fwd {
 
 template <>
-void launch_slots<2>(bool aggregate, int lane, bool bf16, bool softplus, int K, dim3 grid,
-                      const ScanParams& p, hipStream_t stream) {
-  if (aggregate) launch_mode<Mode::kAggregate, 2>(lane, bf16, softplus, K, grid, p, stream);
-  else launch_mode<Mode::kScan, 2>(lane, bf16, softplus, K, grid, p, stream);
+void launch_slots<2>(bool aggregate, int lane, bool bf16, bool softplus, int K, bool defer,
+                      dim3 grid, const ScanParams& p, hipStream_t stream) {
+  if (aggregate) launch_mode<Mode::kAggregate, 2>(lane, bf16, softplus, K, false, grid, p, stream);
+  else launch_mode<Mode::kScan, 2>(lane, bf16, softplus, K, defer, grid, p, stream);
 }
 
 }  // namespace fwd

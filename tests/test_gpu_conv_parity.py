@@ -73,6 +73,14 @@ def check(inp, io, K, seed, silu=True, st=True, label=""):
     assert np.array_equal(to_np(got[2]), ref[2])
 
 
+@pytest.mark.parametrize("blocks", [768, 769])
+def test_conv4_readout_forms_either_side_of_the_grid_switch(blocks):
+    """The width-4 conv scan with the deferred readout (up to 768 workgroups)
+    and with the end-of-block readout (above)."""
+    inp = si.scan_inputs(1, 16 * blocks, 37, io_dtype="f32", seed=blocks)
+    check(inp, "f32", 4, seed=blocks, label=f"{blocks} workgroups")
+
+
 @pytest.mark.parametrize("batch,dim,L,io,K", [
     (2, 32, 64, "f32", 4), (1, 37, 37, "f32", 4), (2, 13, 100, "bf16", 3), (2, 16, 1000, "f32", 4),
     (1, 20, 50, "f32", 1), (1, 20, 50, "f32", 2), (2, 24, 70, "f32", 5), (2, 24, 70, "bf16", 8),

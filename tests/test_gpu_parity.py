@@ -97,6 +97,16 @@ def test_config2_bf16_sampled_rows():
     check_scan(inp, "bf16", rows=rows, label="2.8b-like layer")
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("blocks", [768, 769])
+def test_readout_forms_either_side_of_the_grid_switch(blocks, io):
+    """Up to 768 workgroups (3 wavefronts per SIMD) the one-slot scan defers
+    each block's readout to the next block; above, it reads out at the end of
+    the block.  One batch row of `blocks` 16-channel blocks, ragged length."""
+    inp = si.scan_inputs(1, 16 * blocks, 45, io_dtype=io, seed=blocks)
+    check_scan(inp, io, label=f"{blocks} workgroups {io}")
+
+
 def test_config3_long_context_16_channels():
     cfg = si.SCAN_CONFIGS[3]
     t = si.scan_inputs_device(cfg, DEV)
