@@ -706,15 +706,15 @@ void launch_kp(bool bf16, bool softplus, dim3 grid, const ScanParams& p, hipStre
 // one-slot shared-B/C kernels, the common Mamba-1 shape, get the 4-tap form.
 // B/C modes: 0 shared tile, 1 per-lane element loads, 2 per-lane 16-byte
 // loads (aligned rows; without the conv branch).  `defer` picks the
-// deferred owner-C readout for the one-slot shared-tile scan (no conv or the
-// 4-tap one).
+// deferred owner-C readout for the one-slot shared-tile scan without the
+// conv branch (with it the form measured slower: 137 -> 149 us on the
+// 130m-like layer, at 146-151 VGPRs).
 template <Mode M, int S>
 void launch_mode(int lane, bool bf16, bool softplus, int K, bool defer, dim3 grid,
                  const ScanParams& p, hipStream_t stream) {
   if constexpr (M == Mode::kScan && S == 1) {
-    if (defer && lane == 0 && K <= 4) {
-      if (K == 0) launch_kp<M, 0, S, 0, true>(bf16, softplus, grid, p, stream);
-      else launch_kp<M, 4, S, 0, true>(bf16, softplus, grid, p, stream);
+    if (defer && lane == 0 && K == 0) {
+      launch_kp<M, 0, S, 0, true>(bf16, softplus, grid, p, stream);
       return;
     }
   }

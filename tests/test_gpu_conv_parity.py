@@ -75,8 +75,9 @@ def check(inp, io, K, seed, silu=True, st=True, label=""):
 
 @pytest.mark.parametrize("blocks", [768, 769])
 def test_conv4_readout_forms_either_side_of_the_grid_switch(blocks):
-    """The width-4 conv scan with the deferred readout (up to 768 workgroups)
-    and with the end-of-block readout (above)."""
+    """The width-4 conv scan on both sides of the 768-workgroup switch (the
+    conv path keeps the end-of-block readout on both; the plain scan changes
+    form there)."""
     inp = si.scan_inputs(1, 16 * blocks, 37, io_dtype="f32", seed=blocks)
     check(inp, "f32", 4, seed=blocks, label=f"{blocks} workgroups")
 
