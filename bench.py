@@ -96,8 +96,12 @@ def timed_launches(fn, iters, torch):
     return float(np.mean(ms)), float(np.min(ms))
 
 
-def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2, conv=0):
-    """Times `steps` full scans; returns a dict of measurements."""
+def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2, conv=0, graph=False):
+    """Times `steps` full scans; returns a dict of measurements.  With graph,
+    the `steps` launches are captured once into a HIP graph (torch.cuda.graph,
+    a private stream at default priority) and the timed region is one replay
+    of it, after an untimed one: back-to-back launches without the host's
+    per-call dispatch between them."""
     dev = "cuda"
     sets = []
     for r in range(rotate):
@@ -130,11 +134,24 @@ def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2, conv=0):
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        del g
+    else:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     kern_ms, kern_min = timed_launches(step, max(10, min(steps, 200)), torch)
     esz = 2 if io == torch.bfloat16 else 4
     nbytes = scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, esz, ngroups=cfg.ngroups)
@@ -145,7 +162,8 @@ def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2, conv=0):
                gbps=nbytes / (ms_step * 1e-3) / 1e9,
                kernel_gbps=nbytes / (kern_ms * 1e-3) / 1e9,
                channel_tokens_per_s=cfg.batch * cfg.dim * cfg.seqlen / (ms_step * 1e-3),
-               io_dtype="bf16" if esz == 2 else "f32")
+               io_dtype="bf16" if esz == 2 else "f32",
+               launch="one HIP graph of the timed steps" if graph else "eager launches")
     res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBS
     del sets, outs, lasts
     torch.cuda.empty_cache()
@@ -392,6 +410,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--all", action="store_true", help="also time the 1M-token scan")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the headline's steps as eager launches, not one HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="only the headline scan (10 launches) and a 1 GiB copy kernel "
@@ -444,7 +464,7 @@ def main():
         log(f"[profile] 10 launches of the scan backward on {head.name}")
         return
     log(f"[bench] headline {head.name}: warmup {args.warmup}, steps {args.steps}")
-    r = bench_scan(head, args.steps, args.warmup, torch, ssm, si)
+    r = bench_scan(head, args.steps, args.warmup, torch, ssm, si, graph=not args.no_graph)
     log(f"[bench] headline {r['gbps']:.1f} GB/s, kernel {r['kernel_ms'] * 1e3:.1f} us")
 
     secondary = {}
@@ -527,6 +547,7 @@ def main():
                    "dstate": head.dstate},
         "channel_tokens_per_s": r["channel_tokens_per_s"],
         "hbm_frac": round(r["hbm_frac"], 4),
+        "launch": r["launch"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "scan_fwd_kernel<float>",

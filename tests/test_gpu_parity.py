@@ -164,6 +164,42 @@ def test_deterministic_bitwise():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_graph_replay_matches_eager(io):
+    """The scan captured in a HIP graph (as bench.py times it): three launches
+    over two input sets, replayed several times with eager scans and
+    synchronisations between the replays; every replay equals the eager
+    result bit for bit (outputs cleared before each replay)."""
+    sets = [si.to_torch(si.scan_inputs(2, 96, 300, io_dtype=io, seed=s), DEV) for s in (5, 6)]
+    outs = [torch.empty_like(t["u"]) for t in sets]
+    lasts = [torch.empty((2, 96, 16), device=DEV) for _ in sets]
+
+    def step(i):
+        t = sets[i % 2]
+        ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                               delta_bias=t["delta_bias"], out=outs[i % 2], last_state=lasts[i % 2])
+
+    for i in range(2):
+        step(i)
+    torch.cuda.synchronize()
+    ref = [(o.clone(), l.clone()) for o, l in zip(outs, lasts)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(3):
+            step(i)
+    for r in range(4):
+        for o, l in zip(outs, lasts):
+            o.zero_()
+            l.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for (o, l), (ro, rl) in zip(zip(outs, lasts), ref):
+            assert torch.equal(o, ro) and torch.equal(l, rl), r
+        eager = gpu_scan(si.scan_inputs(1, 20, 50, io_dtype=io, seed=r))   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(eager[0].float()).all()
+
+
 def test_strided_views():
     batch, dim, L = 2, 40, 96
     inp = si.scan_inputs(batch, dim, L, io_dtype="bf16", seed=5)
