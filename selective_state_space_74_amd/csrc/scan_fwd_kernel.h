@@ -303,8 +303,9 @@ struct Wave {
   // kMask = false is the steady state, valid when blocks k-1 and k are full:
   // it has no branch, so the scan's DPP broadcasts stay fused into the ops
   // that use them.  kEnd (steady state only) marks the last block of a group,
-  // after which the next group is staged and the workgroup synchronises; in
-  // the masked form that is decided at run time.
+  // after which the workgroup synchronises; the other blocks are first blocks
+  // (two per group), after which the next group is staged.  In the masked
+  // form both are decided at run time.
   template <bool kMask, bool kEnd>
   __device__ __forceinline__ void iter(int k, float (&h)[S], double& ssum, const Raw& P,
                                        const Raw& Q, Raw& R, GroupRaw<S>& G, float& uprev,
@@ -430,14 +431,22 @@ struct Wave {
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
     if constexpr (!kLane) {
-      if (kMask ? (k % kGB == kGB - 1 && k + 1 < nblk) : kEnd) {
-        // Group (k+1)/kGB into the other buffer.  Every wavefront finished
-        // reading that buffer before the previous barrier.
-        const int g = k / kGB + 1;
+      // Group g + 1 goes into the other buffer at the end of group g's first
+      // block: that buffer held group g - 1, which every wavefront finished
+      // reading before the barrier that closed group g - 1.  The barrier at
+      // the end of group g's last block orders these stores before group
+      // g + 1's reads; issued a block earlier, they no longer hold it up.
+      static_assert(kGB == 2, "each block is the first or the last of its group");
+      const bool first = kMask ? (k % kGB == 0) : !kEnd;
+      const bool last = kMask ? (k % kGB == kGB - 1) : kEnd;
+      const int g = k / kGB + 1;
+      // (the steady state may stage one group past the end: clamped data into
+      // a buffer that nothing reads again)
+      if (kMask ? first && g < ngrp : first) {
         stage(g, G);
-        __syncthreads();
         G = load_group(g + 1);
       }
+      if (last && k + 1 < nblk) __syncthreads();
     }
   }
 };
