@@ -346,30 +346,9 @@ void ssd_fwd_kernel(SsdParams p) {
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = c * kQ;
     const int nv = std::min(kQ, p.L - t0);
-    // ---- the chunk's step sizes: every wavefront runs the 64-token scan
-    // (lane = token), so that each staging thread has the weight of its row
-    float w_row;
-    {
-      const bool tv = lane < nv;
-      const float x = Elem<T>::f32(st.dt) + bias;
-      float dl = kSoftplus ? softplus_f32(x) : x;
-      dl = tv ? dl : 0.0f;
-      float cum = dl;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(cum, off, 64);
-        cum += lane >= off ? o : 0.0f;
-      }
-      const float la = cum * a2;
-      const float last = __shfl(la, 63, 64);
-      const float w = __builtin_amdgcn_exp2f(last - la) * dl;   // exp(a_{Q-1} - a_s) Delta_s
-      w_row = __shfl(w, srow, 64);
-      if (wave == 0) {
-        sDl[lane] = dl;
-        sLa[lane] = la;
-      }
-    }
-    // ---- B, C, x^T (raw and decay-weighted) of this chunk into LDS ----
+    // ---- B, C and x^T of this chunk into LDS, before the step-size scan so
+    // that the stores are under way while it runs (the barrier closing the
+    // previous chunk freed these buffers) ----
     {
       const bool tv = srow < nv;
       if constexpr (kVec) {
@@ -402,6 +381,44 @@ void ssd_fwd_kernel(SsdParams p) {
           else v = st.x[q][k];
           const E xv = raw(v, tv && p0 + pp < p.P);
           sXT[pp][srow] = xv;
+        }
+      }
+    }
+    // ---- the chunk's step sizes: every wavefront runs the 64-token scan
+    // (lane = token), so that each staging thread has the weight of its row
+    float w_row;
+    {
+      const bool tv = lane < nv;
+      const float x = Elem<T>::f32(st.dt) + bias;
+      float dl = kSoftplus ? softplus_f32(x) : x;
+      dl = tv ? dl : 0.0f;
+      float cum = dl;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float o = __shfl_up(cum, off, 64);
+        cum += lane >= off ? o : 0.0f;
+      }
+      const float la = cum * a2;
+      const float last = __shfl(la, 63, 64);
+      const float w = __builtin_amdgcn_exp2f(last - la) * dl;   // exp(a_{Q-1} - a_s) Delta_s
+      w_row = __shfl(w, srow, 64);
+      if (wave == 0) {
+        sDl[lane] = dl;
+        sLa[lane] = la;
+      }
+    }
+    // ---- decay-weighted x^T (needs the step sizes) ----
+    {
+      const bool tv = srow < nv;
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int pp = kPB * q + 4 * squart + k;
+          uint32_t v;
+          if constexpr (kVec) v = ES == 2 ? (st.x[q][k / 2] >> (16 * (k % 2))) : st.x[q][k % kXw];
+          else v = st.x[q][k];
+          const E xv = raw(v, tv && p0 + pp < p.P);
           sXW[pp][srow] = L::from(L::f(xv) * w_row);
         }
       }
