@@ -423,7 +423,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the scan shards by batch/channel with no communication; see the design notes)",
+              "(the scan would shard by batch rows and channel blocks, with no communication between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -29,7 +29,7 @@
  *     (the decode form below).
  *   - Mamba paper notes, section 5.5: the state starts at zero.
  *
- * Readings where the pages are silent (listed in the design notes too):
+ * Readings where the pages are silent:
  *   softplus is exact (max(x,0) + log1p(exp(-|x|))), no threshold; the
  *   initial state is h0 when given, else zero; out = (sum_n C h + D u) * silu(z).
  *
