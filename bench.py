@@ -422,7 +422,7 @@ def main():
                     help="only the scan backward of the 130m-like layer (10 launches); for rocprofv3")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the scan would shard by batch rows and channel blocks, with no communication between GPUs)",
               file=sys.stderr)
         sys.exit(2)
