@@ -1,17 +1,30 @@
 #!/usr/bin/env python3
 """Benchmark of the gfx950 selective scan.
 
-Headline: the Mamba-130m-like layer scan (batch 8, d_inner 1536, L 2048,
-d_state 16, fp32 IO, silu gate, last_state returned).  One step = one full
-prefill scan over the batch with inputs already resident in HBM.  Throughput is
-algorithmic bytes per second (every input element read once, B and C once per
-(batch, token), every output written once, the state never touching HBM) and
-channel*tokens per second; the HBM fraction is against MI355X's 8 TB/s.
+Headline: the long-context scan, the largest single-GPU workload (batch 1,
+d_inner 1536, L 1,048,576, d_state 16, bf16 IO with fp32 state, silu gate,
+last_state returned).  One step = one full prefill scan of the sequence with
+inputs already resident in HBM: both launches of the segmented scan (pass 1
+over every segment, pass 2 over the segments' heads while the incoming state
+still counts).  Throughput is algorithmic bytes per second (every input
+element read once, B and C once per (batch, token), every output written
+once, the state never touching HBM) and channel*tokens per second; the HBM
+fraction is against MI355X's 8 TB/s.  The scan is bound by vector
+arithmetic (one exp and four fp32 operations per token and state, plus the
+per-token softplus and silu), so the line also reports the fraction of the
+chip's vector issue rate and of the measured arithmetic ceiling (a
+register-only kernel with the same instruction mix, libssm_micro.so), and
+names the binding one.
 
-Also measured (secondary, same JSON line): the bf16 2.8b-like layer scan, the
-1000-step decode update, the headline scan with the width-4 causal conv of the
-block's conv branch fused in front, and the scan backward on the two layer
-shapes; with --all also the 1M-token scan.
+Before timing, every workload runs untimed launches for at least 200 ms
+beyond the requested warm-up steps, so that the clocks have settled; kernel
+durations are medians of per-launch HIP events on the launching stream.
+
+Also measured (secondary, same JSON line): the Mamba-130m-like fp32 layer
+scan, the bf16 2.8b-like layer scan, the 1000-step decode update, the
+130m-like scan with the width-4 causal conv of the block's conv branch fused
+in front, with d_state 64 and with per-channel B/C, the Mamba-2 SSD layer,
+and the scan backward on the two layer shapes.
 
 Prints ONE JSON line on stdout.  Progress goes to stderr.
 """
@@ -34,9 +47,20 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 METRIC = "selective-scan GB/s and channel·tokens/s (1 GPU); % of HBM roofline"
 SCAN_KERNEL_SRC = ["selective_state_space_74_amd/csrc/scan_fwd.hip",
                    "selective_state_space_74_amd/csrc/scan_fwd_kernel.h",
-                   "selective_state_space_74_amd/csrc/scan_fwd_s1.hip",
+                   "selective_state_space_74_amd/csrc/scan_fwd_seg_s1.hip",
                    "selective_state_space_74_amd/csrc/ssm_internal.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_fwd_mamba130m_f32_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_fwd_long_context_bf16_traffic.json")
+# Vector issue rate of MI355X from its unit counts and clock: 256 CUs x 4
+# SIMDs x 16 lanes x 2.4 GHz = one fp32 VALU lane-instruction per lane per
+# clock (the 157.3 TFLOP/s fp32 figure counts packed FMAs, 2 lanes x 2 flops,
+# which this build does not generate).
+ALU_PEAK_T = 256 * 64 * 2.4e9 / 1e12     # T lane-instructions / s
+# Algorithmic lane-instructions per (token, state) step: 2 multiplies, 1 exp,
+# 2 FMAs (state, readout), plus per token the delta bias add, softplus
+# (4 VALU + 2 transcendentals), silu (3 + 2), Delta*u, D*u, the gate, and one
+# per loaded input (u, delta, z), spread over the token's 16 states.
+ALU_OPS_PER_STEP = 5 + (11 + 4) / 16
+WARM_MS = 200.0                # untimed launches before any timing, at least
 
 
 def log(*a):
@@ -83,7 +107,8 @@ def measured_traffic():
 
 
 def timed_launches(fn, iters, torch):
-    """Average kernel duration with HIP events on the launching stream."""
+    """Per-launch durations (ms) with HIP events on the launching stream:
+    (median, min, mean)."""
     stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
@@ -93,7 +118,21 @@ def timed_launches(fn, iters, torch):
         ends[i].record(stream)
     torch.cuda.synchronize()
     ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return float(np.mean(ms)), float(np.min(ms))
+    return float(np.median(ms)), float(np.min(ms)), float(np.mean(ms))
+
+
+def warm(fn, n, torch, min_ms=WARM_MS):
+    """n untimed launches, then more until at least min_ms have elapsed (the
+    clocks settle under sustained load).  Returns (launches, ms)."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < n or (time.perf_counter() - t0) * 1e3 < min_ms:
+        fn(i)
+        i += 1
+        if i >= n:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i, (time.perf_counter() - t0) * 1e3
 
 
 def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2, conv=0, graph=False):
@@ -115,6 +154,11 @@ def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2, conv=0, graph=False
     io = sets[0]["u"].dtype
     outs = [torch.empty_like(s["u"]) for s in sets]
     lasts = [torch.empty((cfg.batch, cfg.dim, cfg.dstate), device=dev) for _ in sets]
+    # the segment workspace, allocated once outside the timed region
+    a = ssm.ScanArgs()
+    a.batch, a.dim, a.seqlen, a.dstate = cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate
+    nws = ssm.scan_workspace_size(a)
+    ws = torch.empty(max(1, nws), dtype=torch.uint8, device=dev) if nws else False
 
     ckw = {}
     if conv:
@@ -129,11 +173,9 @@ def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2, conv=0, graph=False
         s = sets[k]
         ssm.selective_scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
                                delta_bias=s["delta_bias"], out=outs[k], last_state=lasts[k],
-                               **ckw)
+                               workspace=ws, **ckw)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
+    wl, wms = warm(step, warmup, torch)
     if graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -147,25 +189,29 @@ def bench_scan(cfg, steps, warmup, torch, ssm, si, rotate=2, conv=0, graph=False
         wall = time.perf_counter() - t0
         del g
     else:
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             step(i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-    kern_ms, kern_min = timed_launches(step, max(10, min(steps, 200)), torch)
+    kern_ms, kern_min, kern_mean = timed_launches(step, max(10, min(steps, 200)), torch)
     esz = 2 if io == torch.bfloat16 else 4
     nbytes = scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, esz, ngroups=cfg.ngroups)
     if conv:
         nbytes += cfg.dim * conv * 4 + cfg.dim * 4              # conv weights and bias
     ms_step = wall / steps * 1e3
-    res = dict(ms_per_step=ms_step, kernel_ms=kern_ms, kernel_ms_min=kern_min, bytes=nbytes,
+    res = dict(ms_per_step=ms_step, kernel_ms=kern_ms, kernel_ms_min=kern_min,
+               kernel_ms_mean=kern_mean, bytes=nbytes,
                gbps=nbytes / (ms_step * 1e-3) / 1e9,
                kernel_gbps=nbytes / (kern_ms * 1e-3) / 1e9,
                channel_tokens_per_s=cfg.batch * cfg.dim * cfg.seqlen / (ms_step * 1e-3),
                io_dtype="bf16" if esz == 2 else "f32",
-               launch="one HIP graph of the timed steps" if graph else "eager launches")
+               launch="one HIP graph of the timed steps" if graph else "eager launches",
+               warmup_launches=wl, warmup_ms=round(wms, 1),
+               segment_workspace_bytes=nws)
     res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBS
-    del sets, outs, lasts
+    del sets, outs, lasts, ws
     torch.cuda.empty_cache()
     return res
 
@@ -199,15 +245,14 @@ def bench_bwd(cfg, steps, torch, ssm, si):
         ssm.selective_scan_bwd(dout, t["u"], t["delta"], t["A"], t["B"], t["C"], ck, workspace=ws,
                                **kw)
 
-    for i in range(5):
-        step(i)
-    torch.cuda.synchronize()
-    kern_ms, kern_min = timed_launches(step, steps, torch)
+    wl, wms = warm(step, 5, torch)
+    kern_ms, kern_min, kern_mean = timed_launches(step, steps, torch)
     esz = 2 if t["u"].dtype == torch.bfloat16 else 4
     nbytes = scan_bwd_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, esz)
-    res = dict(kernel_ms=kern_ms, kernel_ms_min=kern_min, bytes=nbytes,
+    res = dict(kernel_ms=kern_ms, kernel_ms_min=kern_min, kernel_ms_mean=kern_mean, bytes=nbytes,
                gbps=nbytes / (kern_ms * 1e-3) / 1e9,
-               channel_tokens_per_s=cfg.batch * cfg.dim * cfg.seqlen / (kern_ms * 1e-3))
+               channel_tokens_per_s=cfg.batch * cfg.dim * cfg.seqlen / (kern_ms * 1e-3),
+               warmup_launches=wl, warmup_ms=round(wms, 1))
     res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBS
     res["dBdC"] = "per-block partial sums" if ws.numel() > 1 else "device atomics"
     del t, ck, dout, ws
@@ -231,13 +276,13 @@ def bench_decode(cfg, torch, ssm, si, warmup=20, conv=0, state_sets=1):
                    conv_weight=torch.full((cfg.dim, conv), 1.0 / conv, device=dev),
                    conv_bias=torch.zeros(cfg.dim, device=dev))
 
-    def step(s):
-        ssm.selective_state_update(states[s % state_sets], d["x"][s], d["dt"][s], d["A"], d["B"][s],
+    def step(i):
+        s = i % cfg.steps
+        ssm.selective_state_update(states[i % state_sets], d["x"][s], d["dt"][s], d["A"], d["B"][s],
                                    d["C"][s], D=d["D"], z=d["z"][s], dt_bias=d["dt_bias"],
                                    out=out[s], **ckw)
 
-    for s in range(warmup):
-        step(s)
+    wl, wms = warm(step, warmup, torch)
     for st in states:
         st.zero_()
     torch.cuda.synchronize()
@@ -246,14 +291,15 @@ def bench_decode(cfg, torch, ssm, si, warmup=20, conv=0, state_sets=1):
         step(s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms, kern_min = timed_launches(step, 200, torch)
+    kern_ms, kern_min, kern_mean = timed_launches(step, 200, torch)
     esz = 2 if d["x"].dtype == torch.bfloat16 else 4
     nbytes = decode_bytes(cfg.batch, cfg.dim, cfg.dstate, esz)
     if conv:
         nbytes += 2 * cfg.batch * cfg.dim * conv * 4 + cfg.dim * (conv + 1) * 4
     ms_step = wall / cfg.steps * 1e3
     res = dict(steps=cfg.steps, ms_total=wall * 1e3, ms_per_step=ms_step, kernel_ms=kern_ms,
-               kernel_ms_min=kern_min, bytes_per_step=nbytes,
+               kernel_ms_min=kern_min, kernel_ms_mean=kern_mean, bytes_per_step=nbytes,
+               warmup_launches=wl, warmup_ms=round(wms, 1),
                gbps=nbytes / (ms_step * 1e-3) / 1e9,
                kernel_gbps=nbytes / (kern_ms * 1e-3) / 1e9,
                channel_tokens_per_s=cfg.batch * cfg.dim / (ms_step * 1e-3))
@@ -291,10 +337,8 @@ def bench_ssd(cfg, steps, torch, ssm, si):
         ssm.ssd_scan_fwd(s["x"], s["dt"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
                          dt_bias=s["dt_bias"], out=outs[k], last_state=lasts[k])
 
-    for i in range(5):
-        step(i)
-    torch.cuda.synchronize()
-    kern_ms, kern_min = timed_launches(step, steps, torch)
+    wl, wms = warm(step, 5, torch)
+    kern_ms, kern_min, kern_mean = timed_launches(step, steps, torch)
     esz = 2 if cfg.io_dtype == "bf16" else 4
     nbytes = ssd_bytes(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate, esz)
     # matrix-core work of the chunked form: per (batch, head, 64-token chunk),
@@ -304,9 +348,10 @@ def bench_ssd(cfg, steps, torch, ssm, si):
     chunks = cfg.batch * cfg.nheads * ((cfg.seqlen + Q - 1) // Q)
     macs = chunks * (Q * (Q + 16) // 2 * cfg.dstate + Q * (Q + 16) // 2 * cfg.headdim
                      + 2 * Q * cfg.dstate * cfg.headdim)
-    res = dict(kernel_ms=kern_ms, kernel_ms_min=kern_min, bytes=nbytes,
+    res = dict(kernel_ms=kern_ms, kernel_ms_min=kern_min, kernel_ms_mean=kern_mean, bytes=nbytes,
                gbps=nbytes / (kern_ms * 1e-3) / 1e9, mfma_tflops=2 * macs / (kern_ms * 1e-3) / 1e12,
-               token_heads_per_s=cfg.batch * cfg.seqlen * cfg.nheads / (kern_ms * 1e-3))
+               token_heads_per_s=cfg.batch * cfg.seqlen * cfg.nheads / (kern_ms * 1e-3),
+               warmup_launches=wl, warmup_ms=round(wms, 1))
     res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBS
     del sets, outs, lasts
     torch.cuda.empty_cache()
@@ -314,11 +359,11 @@ def bench_ssd(cfg, steps, torch, ssm, si):
 
 
 def cpu_baseline(cfg, si, max_s=30.0):
-    """The fp64 oracle, as it stands, on the host cores, over the headline
-    workload (whole batch rows at full length).  It runs batch row 0 first and
-    adds further batch rows while the projected total stays under max_s; when
-    the whole workload takes under 2 s it is repeated (up to 5 s in all) and
-    the median run is reported."""
+    """The fp64 oracle, as it stands, on the host cores, over a layer workload
+    (whole batch rows at full length).  It runs batch row 0 first and adds
+    further batch rows while the projected total stays under max_s; when the
+    whole workload takes under 2 s it is repeated (up to 5 s in all) and the
+    median run is reported."""
     import oracle
     inp = si.scan_inputs_for(cfg)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
@@ -340,12 +385,83 @@ def cpu_baseline(cfg, si, max_s=30.0):
         dt = float(np.median([dt] + [run(k) for _ in range(reps - 1)]))
     used = oracle.selective_scan.last_threads
     rows = k * cfg.dim
-    nbytes = scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, 4) * k / cfg.batch
+    esz = 2 if cfg.io_dtype == "bf16" else 4
+    nbytes = scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, esz) * k / cfg.batch
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
             "channel_tokens_per_s": rows * cfg.seqlen / dt, "seconds": round(dt, 3),
-            "sample": f"{k} of {cfg.batch} batch rows ({rows} channel rows) of the headline "
-                      f"workload at full L={cfg.seqlen}; fp64 oracle with {used} OpenMP threads; "
+            "sample": f"{k} of {cfg.batch} batch rows ({rows} channel rows) of {cfg.name} "
+                      f"at full L={cfg.seqlen}; fp64 oracle with {used} OpenMP threads; "
                       f"median of {reps} run(s)"}
+
+
+def cpu_baseline_channels(cfg, si, torch, channels=128, target_s=10.0):
+    """The fp64 oracle, as it stands, on the host cores, over a seeded sample
+    of `channels` channels of a single-sequence workload at its full length
+    (the device-drawn inputs of those channels, read back).  The sample is
+    run repeatedly until about target_s seconds of CPU work have been done;
+    the median run is reported, scaled to the workload's bytes per
+    channel-token."""
+    import oracle
+    t = si.scan_inputs_device(cfg, "cuda")
+    ch = np.sort(np.random.default_rng(cfg.seed).choice(cfg.dim, channels, replace=False))
+    idx = torch.from_numpy(ch).to("cuda")
+    host = lambda x: x.float().cpu().numpy()
+    sel = lambda x: host(x.index_select(1, idx))
+    u, dl, z = sel(t["u"]), sel(t["delta"]), sel(t["z"])
+    B, C = host(t["B"]), host(t["C"])
+    A, D, bias = host(t["A"])[ch], host(t["D"])[ch], host(t["delta_bias"])[ch]
+    del t
+    torch.cuda.empty_cache()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
+
+    def run():
+        t0 = time.perf_counter()
+        oracle.selective_scan(u, dl, A, B, C, D=D, z=z, delta_bias=bias, nthreads=threads,
+                              return_last_state=True)
+        return time.perf_counter() - t0
+
+    runs = [run()]
+    while sum(runs) < target_s and len(runs) < 50:
+        runs.append(run())
+    dt = float(np.median(runs))
+    used = oracle.selective_scan.last_threads
+    ct = cfg.batch * channels * cfg.seqlen
+    esz = 2 if cfg.io_dtype == "bf16" else 4
+    nbytes = scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, esz) * channels / cfg.dim
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
+            "channel_tokens_per_s": ct / dt, "seconds": round(dt, 3),
+            "sample": f"{channels} of {cfg.dim} channels (seeded choice) of {cfg.name} at its full "
+                      f"L={cfg.seqlen}, bytes scaled by {channels}/{cfg.dim}; fp64 oracle with "
+                      f"{used} OpenMP threads; median of {len(runs)} run(s), "
+                      f"{sum(runs):.1f} s of CPU work"}
+
+
+def valu_ceiling(torch, lanes=2048 * 256, blocks=4096, reps=10):
+    """(token, state) steps per second of the register-only kernel that
+    executes the scan's unavoidable instruction mix (libssm_micro.so), median
+    of `reps` timed launches after a >= 200 ms warm-up."""
+    import ctypes
+    path = os.path.join(ROOT, "selective_state_space_74_amd", "libssm_micro.so")
+    lib = ctypes.CDLL(path)
+    lib.ssm_micro_valu_mix.restype = ctypes.c_int
+    lib.ssm_micro_valu_mix.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_void_p]
+    out = torch.empty(lanes, device="cuda")
+
+    def step(i):
+        st = lib.ssm_micro_valu_mix(ctypes.c_void_p(out.data_ptr()), lanes, blocks,
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"ssm_micro_valu_mix: hip error {st}")
+
+    warm(step, 3, torch)
+    ms, mn, _ = timed_launches(step, reps, torch)
+    steps = lanes * blocks * 16
+    del out
+    return {"steps_per_s": steps / (ms * 1e-3), "kernel_ms": round(ms, 4),
+            "steps": steps, "what": "register-only kernel, per 16 (token, state) steps of a lane: "
+                                    "16 x (2 mul, exp, 2 fma) + the per-token softplus, silu, "
+                                    "Delta*u, D*u, gate and input operations; 8 waves per SIMD"}
 
 
 def stream_copy(torch, reps=10):
@@ -370,10 +486,48 @@ def stream_copy(torch, reps=10):
     return 2 * 4 * n / (ms * 1e-3) / 1e9
 
 
-def profile_run(cfg, torch, ssm, si, launches=10):
-    """Headline scan launches, decode steps on the decode workload, and a plain
-    copy kernel of known size (reads 1 GiB, writes 1 GiB) so that the
-    FETCH_SIZE / WRITE_SIZE counters can be scaled to bytes."""
+def calibration_copy(torch, launches):
+    """A plain copy kernel of known size (reads 1 GiB, writes 1 GiB) so that
+    the FETCH_SIZE / WRITE_SIZE counters can be scaled to bytes."""
+    n = (1 << 30) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for i in range(launches):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def profile_long(cfg, torch, ssm, si, launches=5):
+    """The headline scan (both passes) after a >= 200 ms warm-up, then the
+    calibration copy; for rocprofv3."""
+    t = si.scan_inputs_device(cfg, "cuda")
+    out = torch.empty_like(t["u"])
+    last = torch.empty((cfg.batch, cfg.dim, cfg.dstate), device="cuda")
+    a = ssm.ScanArgs()
+    a.batch, a.dim, a.seqlen, a.dstate = cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate
+    ws = torch.empty(max(1, ssm.scan_workspace_size(a)), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                               delta_bias=t["delta_bias"], out=out, last_state=last, workspace=ws)
+
+    wl, _ = warm(step, 1, torch)
+    kern_ms, _, _ = timed_launches(step, launches, torch)
+    del t, out, last, ws
+    torch.cuda.empty_cache()
+    calibration_copy(torch, launches)
+    esz = 2 if cfg.io_dtype == "bf16" else 4
+    log(f"[profile] {wl} warm-up + {launches} timed scans of {cfg.name} "
+        f"({scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, esz)} algorithmic bytes each; "
+        f"HIP events median {kern_ms:.3f} ms per scan, both passes), {launches} copy launches "
+        f"(1 GiB read + 1 GiB write)")
+
+
+def profile_layer(cfg, torch, ssm, si, launches=10):
+    """Layer scan launches, decode steps on the decode workload, and the
+    calibration copy; for rocprofv3."""
     t = si.to_torch(si.scan_inputs_for(cfg), "cuda")
     out = torch.empty_like(t["u"])
     last = torch.empty((cfg.batch, cfg.dim, cfg.dstate), device="cuda")
@@ -391,12 +545,7 @@ def profile_run(cfg, torch, ssm, si, launches=10):
                                    D=d["D"], z=d["z"][s], dt_bias=d["dt_bias"], out=dout)
     torch.cuda.synchronize()
     del d, state, dout
-    n = (1 << 30) // 4
-    src = torch.ones(n, device="cuda")
-    dst = torch.empty_like(src)
-    for i in range(launches):
-        torch.mul(src, 1.0, out=dst)
-    torch.cuda.synchronize()
+    calibration_copy(torch, launches)
     log(f"[profile] {launches} scan launches ({scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, 4)}"
         f" algorithmic bytes each), {launches} decode steps "
         f"({decode_bytes(dc.batch, dc.dim, dc.dstate, 2)} bytes each), {launches} copy launches "
@@ -406,16 +555,16 @@ def profile_run(cfg, torch, ssm, si, launches=10):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--all", action="store_true", help="also time the 1M-token scan")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="time the headline's steps as eager launches, not one HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true",
-                    help="only the headline scan (10 launches) and a 1 GiB copy kernel "
-                         "(10 launches) that calibrates the HBM byte counters; for rocprofv3")
+                    help="only the headline scan (warm-up, then 5 scans) and a 1 GiB copy kernel "
+                         "(5 launches) that calibrates the HBM byte counters; for rocprofv3")
+    ap.add_argument("--profile-layer", action="store_true",
+                    help="only the 130m-like layer scan (10 launches), 10 decode steps and the "
+                         "calibration copy; for rocprofv3")
     ap.add_argument("--profile-ssd", action="store_true",
                     help="only the Mamba-2 SSD layer (10 launches); for rocprofv3")
     ap.add_argument("--profile-bwd", action="store_true",
@@ -437,9 +586,13 @@ def main():
     ssm.lib()
     torch.cuda.init()
 
-    head = si.SCAN_CONFIGS[1]
+    head = si.SCAN_CONFIGS[3]           # the long-context scan: the largest single-GPU workload
+    layer = si.SCAN_CONFIGS[1]
     if args.profile:
-        profile_run(head, torch, ssm, si)
+        profile_long(head, torch, ssm, si)
+        return
+    if args.profile_layer:
+        profile_layer(layer, torch, ssm, si)
         return
     if args.profile_ssd:
         cs = si.SSD_CONFIG
@@ -452,8 +605,8 @@ def main():
         log(f"[profile] 10 launches of the SSD layer {cs.name}")
         return
     if args.profile_bwd:
-        t = si.to_torch(si.scan_inputs_for(head), "cuda")
-        ck = torch.empty(ssm.checkpoint_shape(head.batch, head.dim, head.seqlen),
+        t = si.to_torch(si.scan_inputs_for(layer), "cuda")
+        ck = torch.empty(ssm.checkpoint_shape(layer.batch, layer.dim, layer.seqlen),
                          dtype=torch.float32, device="cuda")
         kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"])
         ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], checkpoints=ck, **kw)
@@ -461,18 +614,27 @@ def main():
         for _ in range(10):
             ssm.selective_scan_bwd(dout, t["u"], t["delta"], t["A"], t["B"], t["C"], ck, **kw)
         torch.cuda.synchronize()
-        log(f"[profile] 10 launches of the scan backward on {head.name}")
+        log(f"[profile] 10 launches of the scan backward on {layer.name}")
         return
-    log(f"[bench] headline {head.name}: warmup {args.warmup}, steps {args.steps}")
-    r = bench_scan(head, args.steps, args.warmup, torch, ssm, si, graph=not args.no_graph)
-    log(f"[bench] headline {r['gbps']:.1f} GB/s, kernel {r['kernel_ms'] * 1e3:.1f} us")
+    log(f"[bench] headline {head.name}: warmup {args.warmup} (+ >= {WARM_MS:.0f} ms), "
+        f"steps {args.steps}")
+    r = bench_scan(head, args.steps, args.warmup, torch, ssm, si, rotate=1)
+    log(f"[bench] headline {r['gbps']:.1f} GB/s, kernel median {r['kernel_ms']:.3f} ms")
+    ceiling = valu_ceiling(torch)
+    log(f"[bench] measured arithmetic ceiling {ceiling['steps_per_s'] / 1e12:.3f} T steps/s")
 
     secondary = {}
     if not args.no_secondary:
+        log(f"[bench] secondary {layer.name}")
+        secondary[layer.name] = bench_scan(layer, max(20, args.steps), args.warmup, torch, ssm, si,
+                                           graph=True)
+        log(f"[bench] {layer.name} {secondary[layer.name]['gbps']:.1f} GB/s, "
+            f"kernel median {secondary[layer.name]['kernel_ms'] * 1e3:.1f} us")
         c2 = si.SCAN_CONFIGS[2]
         log(f"[bench] secondary {c2.name}")
-        secondary[c2.name] = bench_scan(c2, max(20, args.steps // 4), 5, torch, ssm, si)
-        log(f"[bench] {c2.name} {secondary[c2.name]['gbps']:.1f} GB/s")
+        secondary[c2.name] = bench_scan(c2, max(20, args.steps), 5, torch, ssm, si)
+        log(f"[bench] {c2.name} {secondary[c2.name]['gbps']:.1f} GB/s, "
+            f"kernel median {secondary[c2.name]['kernel_ms'] * 1e3:.1f} us")
         log(f"[bench] secondary {si.DECODE_CONFIG.name}")
         secondary[si.DECODE_CONFIG.name] = bench_decode(si.DECODE_CONFIG, torch, ssm, si)
         log(f"[bench] decode {secondary[si.DECODE_CONFIG.name]['gbps']:.1f} GB/s")
@@ -484,18 +646,17 @@ def main():
         log(f"[bench] secondary {key}")
         secondary[key] = bench_decode(si.DECODE_CONFIG, torch, ssm, si, conv=4)
         log(f"[bench] {key} {secondary[key]['gbps']:.1f} GB/s")
-        c1 = si.SCAN_CONFIGS[1]
-        key = f"{c1.name}-conv4-fused"
+        key = f"{layer.name}-conv4-fused"
         log(f"[bench] secondary {key}")
-        secondary[key] = bench_scan(c1, max(20, args.steps // 4), 5, torch, ssm, si, conv=4)
+        secondary[key] = bench_scan(layer, max(20, args.steps), 5, torch, ssm, si, conv=4)
         log(f"[bench] {key} {secondary[key]['gbps']:.1f} GB/s, "
             f"kernel {secondary[key]['kernel_ms'] * 1e3:.1f} us")
         # the generalised kernel: 64 states (four slots per lane), and B/C of
         # its own per channel (lane mode)
-        for cg in (dataclasses.replace(c1, name=f"{c1.name}-dstate64", dstate=64),
-                   dataclasses.replace(c1, name=f"{c1.name}-bc-per-channel", ngroups=c1.dim)):
+        for cg in (dataclasses.replace(layer, name=f"{layer.name}-dstate64", dstate=64),
+                   dataclasses.replace(layer, name=f"{layer.name}-bc-per-channel", ngroups=layer.dim)):
             log(f"[bench] secondary {cg.name}")
-            secondary[cg.name] = bench_scan(cg, max(20, args.steps // 10), 5, torch, ssm, si)
+            secondary[cg.name] = bench_scan(cg, 20, 5, torch, ssm, si)
             log(f"[bench] {cg.name} {secondary[cg.name]['gbps']:.1f} GB/s, "
                 f"kernel {secondary[cg.name]['kernel_ms'] * 1e3:.1f} us")
         cs = si.SSD_CONFIG
@@ -511,22 +672,31 @@ def main():
             secondary[key] = bench_bwd(cb, 20, torch, ssm, si)
             log(f"[bench] {key} {secondary[key]['gbps']:.1f} GB/s, "
                 f"{secondary[key]['kernel_ms'] * 1e3:.1f} us")
-        if args.all:
-            c3 = si.SCAN_CONFIGS[3]
-            log(f"[bench] secondary {c3.name}")
-            secondary[c3.name] = bench_scan(c3, 3, 1, torch, ssm, si, rotate=1)
-            log(f"[bench] {c3.name} {secondary[c3.name]['gbps']:.1f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
-        cpu = cpu_baseline(head, si)
+        cpu = cpu_baseline_channels(head, si, torch)
         log(f"[bench] cpu baseline {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
 
     traffic = measured_traffic()
-    achieved = r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+    steps_tn = head.batch * head.dim * head.seqlen * head.dstate
+    ksec = r["kernel_ms"] * 1e-3
+    hbm_ach = r["bytes"] / ksec / 1e9
+    alu_ach = steps_tn * ALU_OPS_PER_STEP / ksec / 1e12
+    hbm_frac, alu_frac = hbm_ach / HBM_PEAK_GBS, alu_ach / ALU_PEAK_T
+    valu_frac = (steps_tn / ceiling["steps_per_s"]) / ksec
     copy_gbps = stream_copy(torch)
     log(f"[bench] device copy {copy_gbps:.1f} GB/s")
+    alu = {"achieved": round(alu_ach, 3), "peak": round(ALU_PEAK_T, 3),
+           "unit": "T lane-instructions/s", "frac": round(alu_frac, 4),
+           "ops_per_token_state": ALU_OPS_PER_STEP,
+           "what": "algorithmic fp32 VALU lane-instructions (each exp or log counted once) "
+                   "against 256 CUs x 64 lanes x 2.4 GHz"}
+    hbm = {"achieved": round(hbm_ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(hbm_frac, 4)}
+    bound = "alu" if alu_frac >= hbm_frac else "hbm"
+    main_ = alu if bound == "alu" else hbm
     line = {
         "metric": METRIC,
         "value": round(r["gbps"], 2),
@@ -539,23 +709,34 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded numpy PCG64: u,z~N(0,1), dt~0.1N(0,1), B,C~N(0,1), "
+        "data": "synthetic (seeded torch Philox on the device: u,z~N(0,1), dt~0.1N(0,1), "
+                "B,C~N(0,1), rounded to bf16; numpy PCG64 parameters: "
                 "bias=inv-softplus(logU[1e-3,1e-1]), A=-(n+1), D=1)",
-        "config": {"workload": "selective scan fwd, mamba-130m-like layer: batch 8, d_inner 1536, "
-                               "L 2048, d_state 16, fp32 IO, silu gate, last_state",
+        "config": {"workload": "selective scan fwd, long context: batch 1, d_inner 1536, "
+                               "L 1048576, d_state 16, bf16 IO, fp32 state and arithmetic, "
+                               "silu gate, last_state; both passes of the segmented scan",
                    "batch": head.batch, "dim": head.dim, "seqlen": head.seqlen,
-                   "dstate": head.dstate},
+                   "dstate": head.dstate, "io_dtype": "bf16"},
         "channel_tokens_per_s": r["channel_tokens_per_s"],
         "hbm_frac": round(r["hbm_frac"], 4),
         "launch": r["launch"],
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "scan_fwd_kernel<float>",
+        "warmup_launches": r["warmup_launches"],
+        "warmup_ms": r["warmup_ms"],
+        "roofline": {"bound": bound, "achieved": main_["achieved"], "peak": main_["peak"],
+                     "unit": main_["unit"], "frac": main_["frac"], "traffic": traffic,
+                     "kernel": "scan_fwd_kernel<bf16> pass 1 (kSeg) + pass 2 (kFix)",
                      "kernel_ms": round(r["kernel_ms"], 5),
-                     "algorithmic_bytes_per_launch": r["bytes"]},
+                     "kernel_ms_min": round(r["kernel_ms_min"], 5),
+                     "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
+                     "timing": "median of per-step HIP events around both launches",
+                     "algorithmic_bytes_per_launch": r["bytes"],
+                     "token_state_steps_per_launch": steps_tn,
+                     "hbm": hbm, "alu": alu,
+                     "valu_frac_of_measured_ceiling": round(valu_frac, 4),
+                     "measured_ceiling": ceiling},
         "cpu_baseline": cpu,
         "stream": {"copy_gbps": round(copy_gbps, 1),
-                   "frac_of_copy": round(achieved / copy_gbps, 4),
+                   "frac_of_copy": round(hbm_ach / copy_gbps, 4),
                    "what": "device copy, 1 GiB read + 1 GiB written, HIP events"},
         "secondary": secondary,
     }

@@ -79,7 +79,8 @@ class use_library:
         lib = ctypes.CDLL(self.path)
         for name in ("oracle_selective_scan_f64", "oracle_state_update_f64",
                      "oracle_selective_scan_bwd_f64", "oracle_causal_conv1d_f64",
-                     "oracle_conv_state_update_f64", "oracle_softplus", "oracle_silu"):
+                     "oracle_conv_state_update_f64", "oracle_ssd_scan_f64", "oracle_softplus",
+                     "oracle_silu"):
             src = getattr(self.saved, name)
             dst = getattr(lib, name)
             dst.restype, dst.argtypes = src.restype, src.argtypes

@@ -13,6 +13,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssm.so")
+# The arithmetic-ceiling micro-benchmark that bench.py times (not part of the
+# libssm.so boundary).
+MICRO_SRC = os.path.join(PKG, "micro", "valu_mix.hip")
+MICRO_LIB = os.path.join(PKG, "libssm_micro.so")
 ARCH = "gfx950"
 
 # Packed fp32 (v_pk_*_f32) is kept out of the generated code.
@@ -56,8 +60,9 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every csrc/*.hip into libssm.so (always recompiles).  The
-    sources compile in parallel into a temporary directory, then link."""
+    """Compile every csrc/*.hip into libssm.so (always recompiles), and the
+    micro-benchmark into libssm_micro.so.  The library sources compile in
+    parallel into a temporary directory, then link."""
     tmp = LIB + ".tmp"
     jobs = max(1, min(len(sources()), os.cpu_count() or 1, 16))
     with tempfile.TemporaryDirectory(prefix="ssm_build_") as d:
@@ -66,7 +71,10 @@ def build(verbose: bool = False) -> str:
             list(ex.map(lambda so: _run([hipcc(), *flags_for(so[0]), "-c", "-o", so[1], so[0]], verbose),
                         zip(sources(), objs)))
         _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs], verbose)
+        mtmp = MICRO_LIB + ".tmp"
+        _run([hipcc(), *flags_for(MICRO_SRC), "-shared", "-o", mtmp, MICRO_SRC], verbose)
     os.replace(tmp, LIB)
+    os.replace(mtmp, MICRO_LIB)
     return LIB
 
 

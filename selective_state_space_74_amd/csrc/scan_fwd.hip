@@ -23,7 +23,8 @@ __global__ void copy_state_kernel(const float* h0, float* last, int64_t n) {
 // Segments per sequence: cut only when the batch x channel groups alone leave
 // the machine short of wavefronts, as many as fit one residency round of the
 // one-slot kernels (5 workgroups per CU), and keep segments long enough that
-// the extra aggregate pass and the fold stay small.
+// the second pass (bounded by the decay of the incoming state, not by the
+// segment length) and the fold stay small next to them.
 constexpr int64_t kTargetGroups = 1280;   // 5 wavefronts per SIMD on 256 CUs
 constexpr int64_t kMinSegLen = 8192;
 constexpr int kMaxSeg = 64;
@@ -80,7 +81,7 @@ size_t scan_workspace_bytes(const ssm_scan_args& a) {
   const int64_t groups = a.batch * ((a.dim + kCh - 1) / kCh);
   const int nseg = choose_segments(groups, a.seqlen);
   if (nseg <= 1) return 0;
-  return static_cast<size_t>(a.batch * a.dim * (nseg - 1) * (a.dstate + 1)) * sizeof(float);
+  return static_cast<size_t>(a.batch * a.dim * nseg * (a.dstate + 1)) * sizeof(float);
 }
 
 hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {
@@ -144,16 +145,23 @@ hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {
                     a.C_batch_stride % vw == 0 && a.C_group_stride % vw == 0 &&
                     a.C_state_stride % vw == 0;
   const int lane = lane_bc(a) ? (lvec ? 2 : 1) : 0;
-  const bool defer = groups * p.nseg <= kDeferMaxGroups;
-  auto run = [&](bool aggregate, dim3 grid) {
+  const bool defer = p.nseg == 1 && groups <= kDeferMaxGroups;
+  auto run = [&](int pass, dim3 grid) {
     switch (slots(a.dstate)) {
-      case 1: fwd::launch_slots<1>(aggregate, lane, bf16, sp, p.K, defer, grid, p, stream); break;
-      case 2: fwd::launch_slots<2>(aggregate, lane, bf16, sp, p.K, defer, grid, p, stream); break;
-      default: fwd::launch_slots<4>(aggregate, lane, bf16, sp, p.K, defer, grid, p, stream); break;
+      case 1: fwd::launch_slots<1>(pass, lane, bf16, sp, p.K, defer, grid, p, stream); break;
+      case 2: fwd::launch_slots<2>(pass, lane, bf16, sp, p.K, defer, grid, p, stream); break;
+      default: fwd::launch_slots<4>(pass, lane, bf16, sp, p.K, defer, grid, p, stream); break;
     }
   };
-  if (p.nseg > 1) run(true, dim3((unsigned)(groups * (p.nseg - 1))));
-  run(false, dim3((unsigned)(groups * p.nseg)));
+  if (p.nseg > 1) {
+    // pass 1: every segment from zero (segment 0 from h0), with aggregates;
+    // pass 2: segments 1.. from their folded incoming state, until it has
+    // decayed.  Stream order puts pass 1's aggregates before pass 2.
+    run(1, dim3((unsigned)(groups * p.nseg)));
+    run(2, dim3((unsigned)(groups * (p.nseg - 1))));
+  } else {
+    run(0, dim3((unsigned)groups));
+  }
   return hipGetLastError();
 }
 

@@ -45,14 +45,23 @@
 // Long sequences with few channels.  The recurrence is linear in the state
 // (Mamba paper notes, sections 5.3/5.4: a long input can be cut into chunks
 // with the state handed from one chunk to the next), so the sequence may be
-// cut into G segments processed by different workgroups:
-//   pass 1 (aggregate)  segments 0..G-2 run from a zero state and record their
-//                       end state b_g and the sum of their step sizes S_g;
-//   pass 2 (scan)       segment g starts from
-//                       h_in = fold_{i<g} (exp(A S_i) h + b_i) applied to h0,
-//                       then runs exactly like the single-segment scan.
-// The exact state entering segment g is exp(A S_{g-1}) h_in(g-1) + b_{g-1},
-// so the fold reproduces the sequential result up to fp32 rounding.
+// cut into G segments processed by different workgroups, in two launches:
+//   pass 1  every segment runs the full scan (outputs, checkpoints) from a
+//           zero state (segment 0 from h0) and records its end state b_g and
+//           the sum of its step sizes S_g;
+//   pass 2  segment g >= 1 folds the exact state entering it,
+//           h_in = fold_{i<g} (exp(A S_i) h + b_i), with the associative
+//           combine (a1,b1).(a2,b2) = (a1 a2, a2 b1 + b2) kept in factored
+//           form, and scans again from h_in, rewriting outputs and
+//           checkpoints, only while that state's contribution still counts.
+// Pass 1's state inside segment g differs from the exact one by
+// d_t = exp(A (S_0 + ... + S_t)) h_in (the free response of h_in), so once
+// |d_t| falls below fp32 resolution of the state (2^-24 max_n |h_t[n]|, over
+// each channel's states) pass 1's values are the sequential result up to
+// rounding, and pass 2 stops: with A < 0 the contribution decays, and a
+// workgroup stops when all 16 of its channels are there (checked every 64
+// tokens).  With A >= 0 it never decays and pass 2 runs the whole segment.
+// The last segment's workgroups write last_state = exp(A S_g) h_in + b_g.
 #pragma once
 
 #include <algorithm>
@@ -76,7 +85,9 @@ constexpr int kPitch = 20;          // LDS pitch (floats) of one state's readout
 constexpr int kCPitch = kN + 4;     // LDS pitch (floats) of one token's C (token-major tile)
 constexpr int kPartRow = kN * kPitch + 16;  // floats per channel of readout partials
 
-enum class Mode { kScan, kAggregate };
+// kScan: one segment per sequence.  kSeg, kFix: passes 1 and 2 of a
+// segmented sequence.
+enum class Mode { kScan, kSeg, kFix };
 
 struct ScanParams {
   const void* u;
@@ -90,7 +101,7 @@ struct ScanParams {
   const float* h0;
   float* last_state;
   void* out;
-  float* agg;      // [batch * dim][nseg - 1][N + 1] segment aggregates (nseg > 1)
+  float* agg;      // [batch * dim][nseg][N + 1] segment aggregates (nseg > 1)
   float* ckpt;     // [batch][dim][nbk][N] states entering each block, or NULL
   const float* conv_w;      // [dim][K] conv weights (the conv path only)
   const float* conv_b;      // [dim] or NULL
@@ -160,7 +171,9 @@ struct Wave {
   // LDS and the owner of each token contracts it with the token's C column
   // (16 FMAs in place of 16 products on the state lanes and a 15-add sum);
   // C is then staged token-major.
-  static constexpr bool kOwnerC = S == 1 && !kLane && M == Mode::kScan;
+  static constexpr bool kOwnerC = S == 1 && !kLane;
+  static constexpr bool kSegm = M != Mode::kScan;
+  static constexpr bool kFixp = M == Mode::kFix;
   // token of the scan after which the owner's C column is read, so that the
   // read is in flight during the rest of the scan
   static constexpr int kCRead = 7;
@@ -170,10 +183,35 @@ struct Wave {
   // is carried in registers across the block boundary.  Costs about 30
   // VGPRs (128), so it is launched only where the grid leaves three
   // wavefronts per SIMD anyway.
-  static_assert(!kDefer || kOwnerC, "the deferred readout is an owner-C form");
+  static_assert(!kDefer || (kOwnerC && !kSegm),
+                "the deferred readout is an owner-C form of the one-segment scan");
 
   __device__ __forceinline__ uint32_t skip(int k) const {
     return static_cast<uint32_t>(t_beg + k * kT) * E;
+  }
+
+  // Pass 2 of a segmented sequence: has the free response of the incoming
+  // state, |h_in[n]| exp(A[n] S) with S the step sizes of the tokens done so
+  // far, fallen to 2^-24 max_n |h[n]| or below in every channel of the
+  // workgroup?  (ssum: this owner's share of S; a non-finite state or
+  // h_in never compares true.)  Every wavefront of the workgroup calls it
+  // at the same point: it ends with a workgroup barrier.
+  __device__ __forceinline__ bool converged(const float (&h)[S], const float (&hin)[S],
+                                            double ssum) const {
+    float sacc = static_cast<float>(ssum);
+    float hm = 0.0f;
+#pragma unroll
+    for (int q = 0; q < S; ++q) hm = fmaxf(hm, fabsf(h[q]));
+#pragma unroll
+    for (int m = 1; m < kN; m <<= 1) {
+      sacc += __shfl_xor(sacc, m, kN);
+      hm = fmaxf(hm, __shfl_xor(hm, m, kN));
+    }
+    bool ok = true;
+#pragma unroll
+    for (int q = 0; q < S; ++q)
+      ok = ok && __builtin_amdgcn_exp2f(a2[q] * sacc) * hin[q] <= 0x1p-24f * hm;
+    return __syncthreads_and(ok) != 0;
   }
 
   // Owner raw inputs of block k; blocks past the last one reload the last one
@@ -184,7 +222,7 @@ struct Wave {
     r.u = Elem<T>::load(wu.at(s), ou);
     r.dt = Elem<T>::load(wdt.at(s), odt);
     // without a gate the z window is u's: the load is a cache hit, never used
-    r.z = M == Mode::kScan ? Elem<T>::load(wz.at(s), oz) : 0u;
+    r.z = Elem<T>::load(wz.at(s), oz);
     return r;
   }
 
@@ -200,7 +238,7 @@ struct Wave {
 #pragma unroll
       for (int i = 0; i < kGB; ++i) {
         r.b[q][i] = Elem<T>::load(rb, oB[q] + i * kT * E);
-        r.c[q][i] = M == Mode::kScan ? Elem<T>::load(rc, oC[q] + i * kT * E) : 0u;
+        r.c[q][i] = Elem<T>::load(rc, oC[q] + i * kT * E);
       }
     }
     return r;
@@ -219,7 +257,7 @@ struct Wave {
         const float bv = Elem<T>::f32(r.b[q][i]);
         sB[g & 1][st + kN * q][col + i * kT] = t + i * kT < t_end ? bv : 0.0f;
         if constexpr (kOwnerC) sCt[g & 1][col + i * kT][st] = Elem<T>::f32(r.c[q][i]);
-        else if (M == Mode::kScan) sC[g & 1][st + kN * q][col + i * kT] = Elem<T>::f32(r.c[q][i]);
+        else sC[g & 1][st + kN * q][col + i * kT] = Elem<T>::f32(r.c[q][i]);
       }
     }
   }
@@ -236,7 +274,7 @@ struct Wave {
       for (int i = 0; i < kT / 4; ++i) {
         const float4 x = *reinterpret_cast<const float4*>(&sB[buf][col + kN * q][tb + 4 * i]);
         bv[4 * i] = x.x; bv[4 * i + 1] = x.y; bv[4 * i + 2] = x.z; bv[4 * i + 3] = x.w;
-        if (M == Mode::kScan && !kOwnerC) {
+        if constexpr (!kOwnerC) {
           const float4 y = *reinterpret_cast<const float4*>(&sC[buf][col + kN * q][tb + 4 * i]);
           cv[4 * i] = y.x; cv[4 * i + 1] = y.y; cv[4 * i + 2] = y.z; cv[4 * i + 3] = y.w;
         }
@@ -253,33 +291,32 @@ struct Wave {
 #pragma unroll
         for (int v = 0; v < kV; ++v) {
           const auto xb = __builtin_amdgcn_raw_buffer_load_b128(rb, oB[q] + 16 * v, 0, 0);
+          const auto xc = __builtin_amdgcn_raw_buffer_load_b128(rc, oC[q] + 16 * v, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) rbw[4 * v + i] = xb[i];
-          if (M == Mode::kScan) {
-            const auto xc = __builtin_amdgcn_raw_buffer_load_b128(rc, oC[q] + 16 * v, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rcw[4 * v + i] = xc[i];
+          for (int i = 0; i < 4; ++i) {
+            rbw[4 * v + i] = xb[i];
+            rcw[4 * v + i] = xc[i];
           }
         }
 #pragma unroll
         for (int j = 0; j < kT; ++j) {
-          float b, cc = 0.0f;
+          float b, cc;
           if constexpr (E == 2) {
             b = __uint_as_float(j % 2 ? rbw[j / 2] & 0xffff0000u : rbw[j / 2] << 16);
-            if (M == Mode::kScan) cc = __uint_as_float(j % 2 ? rcw[j / 2] & 0xffff0000u : rcw[j / 2] << 16);
+            cc = __uint_as_float(j % 2 ? rcw[j / 2] & 0xffff0000u : rcw[j / 2] << 16);
           } else {
             b = __uint_as_float(rbw[j]);
-            if (M == Mode::kScan) cc = __uint_as_float(rcw[j]);
+            cc = __uint_as_float(rcw[j]);
           }
           bv[j] = !kMask || j < tleft ? b : 0.0f;
-          if (M == Mode::kScan) cv[j] = cc;
+          cv[j] = cc;
         }
       } else {
 #pragma unroll
         for (int j = 0; j < kT; ++j) {
           const float b = Elem<T>::f32(Elem<T>::load(rb, oB[q] + j * E));
           bv[j] = !kMask || j < tleft ? b : 0.0f;
-          if (M == Mode::kScan) cv[j] = Elem<T>::f32(Elem<T>::load(rc, oC[q] + j * E));
+          cv[j] = Elem<T>::f32(Elem<T>::load(rc, oC[q] + j * E));
         }
       }
     }
@@ -315,7 +352,7 @@ struct Wave {
     bc<kMask>(k, 0, bv, cv);
     float ysum = 0.0f;
     float part[kN];
-    if (M == Mode::kScan && (!kOwnerC || kDefer)) {
+    if constexpr (!kOwnerC || kDefer) {
       // The previous block's readout inputs from this wavefront's LDS region,
       // read before this block's own stores there (a wavefront's LDS
       // operations complete in order); unconditional: at k = 0 they are never
@@ -346,7 +383,7 @@ struct Wave {
       const float act = silu_f32(pre);
       uv = silu_in ? act : pre;  // a select, not a branch
       xprev = xc;
-      if (M == Mode::kScan && (!kMask || t_beg + k * kT + col < t_end))
+      if (!kMask || t_beg + k * kT + col < t_end)
         Elem<T>::store(wco.at(p.conv_out ? skip(k) : 0u), oco, uv);
     } else {
       uv = Elem<T>::f32(Q.u);
@@ -359,7 +396,8 @@ struct Wave {
       dl = own ? dl : 0.0f;
       du = own ? du : 0.0f;
     }
-    if (M == Mode::kAggregate) ssum += static_cast<double>(dl);
+    // segmented: the step sizes of this owner's tokens, summed in fp64
+    if constexpr (kSegm) ssum += static_cast<double>(dl);
     if constexpr (kDefer) {
       // the previous block's readout: its states (read above) against its
       // token's C column (read during its scan), after this block's owner
@@ -371,10 +409,8 @@ struct Wave {
     // checkpoint: the states entering this block (an empty window when none
     // are kept, and an offset past the window for padding slots, so the
     // stores are dropped without a branch)
-    if (M == Mode::kScan) {
 #pragma unroll
-      for (int q = 0; q < S; ++q) Elem<float>::store(wck.at((blk0 + k) * ckstep), ock[q], h[q]);
-    }
+    for (int q = 0; q < S; ++q) Elem<float>::store(wck.at((blk0 + k) * ckstep), ock[q], h[q]);
 
     // state role: 16 sequential steps of each state slot; the readout
     // partials sum_q C_n h_n go to LDS four tokens at a time after the last
@@ -393,7 +429,7 @@ struct Wave {
         const float e = __builtin_amdgcn_exp2f(row_bcast<j>(dl) * a2[q]);  // Abar = exp(Delta A)
         const float w = row_bcast<j>(du) * bv[j];                          // Bbar u = Delta u B
         h[q] = fmaf(e, h[q], w);
-        if (M == Mode::kScan) {
+        {
           constexpr int i = S == 1 ? j % 4 : j;
           if constexpr (kOwnerC) pk[i] = h[q];                               // h_n
           else pk[i] = q == 0 ? cv[j] * h[q] : fmaf(cv[j], h[q], pk[i]);   // C_n h_n
@@ -421,7 +457,7 @@ struct Wave {
 #pragma unroll
       for (int n = 0; n < kN; ++n) ysum = fmaf(cl[n], part[n], ysum);
       finish<kMask>(k, Q, uv, ysum);
-    } else if (M == Mode::kScan) {
+    } else {
       if (!kMask) finish<false>(k - 1, P, uprev, ysum);
       else if (k > 0) finish<true>(k - 1, P, uprev, ysum);
     }
@@ -430,19 +466,7 @@ struct Wave {
     // the next block's (the hardware already keeps one wavefront's in order).
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
-    if constexpr (!kLane && M == Mode::kAggregate) {
-      // The aggregate pass (short blocks: no readout) stores group g + 1 at
-      // the end of group g's last block, just before the barrier (storing it
-      // a block earlier measured 5.46 -> 6.67 ms on the 1M-token pass).
-      // Every wavefront finished reading that buffer before the previous
-      // barrier.
-      if (kMask ? (k % kGB == kGB - 1 && k + 1 < nblk) : kEnd) {
-        const int g = k / kGB + 1;
-        stage(g, G);
-        __syncthreads();
-        G = load_group(g + 1);
-      }
-    } else if constexpr (!kLane) {
+    if constexpr (!kLane) {
       // Group g + 1 goes into the other buffer at the end of group g's first
       // block: that buffer held group g - 1, which every wavefront finished
       // reading before the barrier that closed group g - 1.  The barrier at
@@ -469,19 +493,21 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   __shared__ __align__(16) float sB[kTile][kN * S][kGPitch];
   using W = Wave<T, M, kSoftplus, KP, S, kLane, kDefer>;
   constexpr bool kOC = W::kOwnerC;
-  __shared__ __align__(16) float sC[M == Mode::kScan && !kOC ? kTile : 1][kN * S][kGPitch];
+  constexpr bool kSegm = W::kSegm;
+  __shared__ __align__(16) float sC[!kOC ? kTile : 1][kN * S][kGPitch];
   __shared__ __align__(16) float sCt[kOC ? 2 : 1][kOC ? kGT : 1][kCPitch];
-  __shared__ __align__(16) float sP[M == Mode::kScan ? kWaves : 1][kRows][kPartRow];
-  __shared__ double sSum[M == Mode::kScan ? 1 : kWaves][kRows][kT];
+  __shared__ __align__(16) float sP[kWaves][kRows][kPartRow];
+  __shared__ double sSum[kSegm ? kWaves : 1][kRows][kT];
 
   // wavefront index, made visibly uniform so that windows stay in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = (threadIdx.x >> 4) & 3;
   const int col = threadIdx.x & 15;
-  // blockIdx.x = (b * cgroups + cg) * nseg_grid + g; the aggregate pass skips
-  // the last segment (its end state is never needed by a later segment)
-  const int nseg_grid = M == Mode::kScan ? p.nseg : p.nseg - 1;
-  const int g = static_cast<int>(blockIdx.x % nseg_grid);
+  // blockIdx.x = (b * cgroups + cg) * nseg_grid + g'; pass 2 of a segmented
+  // sequence skips segment 0 (it started from the exact state): g = g' + 1
+  constexpr bool fix = W::kFixp;
+  const int nseg_grid = fix ? p.nseg - 1 : p.nseg;
+  const int g = static_cast<int>(blockIdx.x % nseg_grid) + (fix ? 1 : 0);
   const int64_t bc = blockIdx.x / nseg_grid;
   const int64_t b = bc / p.cgroups;
   const int64_t d = (bc % p.cgroups) * kCh + kRows * wave + row;
@@ -566,7 +592,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   }
   w.bias = p.bias ? p.bias[dc] : 0.0f;
   w.Dd = p.D ? p.D[dc] : 0.0f;
-  w.sB = sB; w.sC = sC; w.sP = sP[M == Mode::kScan ? wave : 0];
+  w.sB = sB; w.sC = sC; w.sP = sP[wave];
   w.sCt = reinterpret_cast<float (*)[kGT][kCPitch]>(&sCt[0][0][0]);
 
   // conv path: tap weights by lag, bias, the inputs just before this
@@ -594,23 +620,34 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   }
   float uprev = 0.0f;
 
-  // Initial state: zero for an aggregate segment; otherwise h0 (or zero) carried
-  // through the aggregates of every earlier segment.
-  float h[S];
+  // Initial state: h0 (or zero) for the one segment of kScan and for segment
+  // 0 of pass 1; zero for the other segments of pass 1; in pass 2, the exact
+  // state entering segment g, folded from the aggregates of segments 0..g-1
+  // (segment 0's end state already includes h0).  Pass 2's last segment also
+  // folds its own aggregate into last_state right away.
+  float h[S], hin[S];
+  const size_t arow = static_cast<size_t>(b * p.dim + dc) * p.nseg;  // aggregates of this channel
 #pragma unroll
   for (int q = 0; q < S; ++q) {
     const int n = col + kN * q;
     h[q] = 0.0f;
-    if (M == Mode::kScan && n < N) {
-      h[q] = p.h0 ? p.h0[(b * p.dim + dc) * N + n] : 0.0f;
-      if (g > 0) {
-        const float* ag = p.agg + ((b * p.dim + dc) * (p.nseg - 1)) * aggs;
-        for (int i = 0; i < g; ++i) {
+    if (n < N) {
+      if constexpr (!fix) {
+        if (g == 0 && p.h0) h[q] = p.h0[(b * p.dim + dc) * N + n];
+      } else {
+        const float* ag = p.agg + arow * aggs;
+        h[q] = ag[n];
+        for (int i = 1; i < g; ++i) {
           const float decay = __builtin_amdgcn_exp2f(w.a2[q] * ag[i * aggs + N]);
           h[q] = fmaf(decay, h[q], ag[i * aggs + n]);
         }
+        if (vrow && p.last_state && g == p.nseg - 1) {
+          const float decay = __builtin_amdgcn_exp2f(w.a2[q] * ag[g * aggs + N]);
+          p.last_state[(b * p.dim + d) * N + n] = fmaf(decay, h[q], ag[g * aggs + n]);
+        }
       }
     }
+    hin[q] = fabsf(h[q]);
   }
 
   double ssum = 0.0;
@@ -628,7 +665,8 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   // Steady state: iterations 1 .. nfull-1 (blocks k-1 and k full), four at a
   // time so that buffer j % 4 is a fixed set of registers; a group ends at
   // k % kGB == kGB - 1.  The first iteration and the last few take the masked
-  // form.
+  // form.  Pass 2 checks at the top of each four-block round whether it can
+  // stop (block k - 1 is then the last one done).
   const int nblk = w.nblk;
   const int nfull = (w.t_end - w.t_beg) / kT;
   // owner-C: the C column of each block's token, read during the block's scan
@@ -638,62 +676,73 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   for (int n = 0; n < kN; ++n) cl[n] = 0.0f;
   w.template iter<true, false>(0, h, ssum, buf3, buf0, buf2, grp, uprev, xprev, cl);
   int k = 1;
+  bool done = false;
   for (; k + 4 <= nfull; k += 4) {
+    if constexpr (fix) {
+      if (w.converged(h, hin, ssum)) {
+        done = true;
+        break;
+      }
+    }
     // k % 4 == 1 here, and 4 is a multiple of kGB
     w.template iter<false, (1 % kGB == kGB - 1)>(k + 0, h, ssum, buf0, buf1, buf3, grp, uprev, xprev, cl);
     w.template iter<false, (2 % kGB == kGB - 1)>(k + 1, h, ssum, buf1, buf2, buf0, grp, uprev, xprev, cl);
     w.template iter<false, (3 % kGB == kGB - 1)>(k + 2, h, ssum, buf2, buf3, buf1, grp, uprev, xprev, cl);
     w.template iter<false, (4 % kGB == kGB - 1)>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev, cl);
   }
-  if (k < nblk) w.template iter<true, false>(k, h, ssum, buf0, buf1, buf3, grp, uprev, xprev, cl);
-  if (k + 1 < nblk) w.template iter<true, false>(k + 1, h, ssum, buf1, buf2, buf0, grp, uprev, xprev, cl);
-  if (k + 2 < nblk) w.template iter<true, false>(k + 2, h, ssum, buf2, buf3, buf1, grp, uprev, xprev, cl);
-  if (k + 3 < nblk) w.template iter<true, false>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev, cl);
+  if (!done) {
+    if (k < nblk) w.template iter<true, false>(k, h, ssum, buf0, buf1, buf3, grp, uprev, xprev, cl);
+    if (k + 1 < nblk) w.template iter<true, false>(k + 1, h, ssum, buf1, buf2, buf0, grp, uprev, xprev, cl);
+    if (k + 2 < nblk) w.template iter<true, false>(k + 2, h, ssum, buf2, buf3, buf1, grp, uprev, xprev, cl);
+    if (k + 3 < nblk) w.template iter<true, false>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev, cl);
+  }
 
-  if (M == Mode::kScan) {
-    if constexpr (!kOC || kDefer) {
-      // finish the last block: its partials (owner-C: states) are in LDS, its
-      // raw inputs in buffer (nblk - 1) % 4
-      const int kl = nblk - 1;
-      const int r = kl & 3;
-      const Raw last = r == 0 ? buf0 : r == 1 ? buf1 : r == 2 ? buf2 : buf3;
-      float ysum = 0.0f;
+  if constexpr (!kOC || kDefer) {
+    // finish the last block done: its partials (owner-C: states) are in LDS,
+    // its raw inputs in buffer kl % 4 (block k - 1 after an early stop:
+    // buffer 0)
+    const int kl = done ? k - 1 : nblk - 1;
+    const int r = kl & 3;
+    const Raw last = r == 0 ? buf0 : r == 1 ? buf1 : r == 2 ? buf2 : buf3;
+    float ysum = 0.0f;
 #pragma unroll
-      for (int n = 0; n < kN; ++n) {
-        const float v = w.sP[row][n * kPitch + col];
-        ysum = kOC ? fmaf(cl[n], v, ysum) : ysum + v;
-      }
-      w.template finish<true>(kl, last, uprev, ysum);
+    for (int n = 0; n < kN; ++n) {
+      const float v = w.sP[row][n * kPitch + col];
+      ysum = kOC ? fmaf(cl[n], v, ysum) : ysum + v;
     }
-    if (vrow && p.last_state && g == p.nseg - 1) {
+    w.template finish<true>(kl, last, uprev, ysum);
+  }
+  if constexpr (fix) return;
+  if (vrow && p.last_state && !kSegm) {
 #pragma unroll
-      for (int q = 0; q < S; ++q) {
-        const int n = col + kN * q;
-        if (n < N) p.last_state[(b * p.dim + d) * N + n] = h[q];
-      }
+    for (int q = 0; q < S; ++q) {
+      const int n = col + kN * q;
+      if (n < N) p.last_state[(b * p.dim + d) * N + n] = h[q];
     }
-    if constexpr (KP > 0) {
-      // the last K inputs, for the decode update to continue from
-      const int K = p.K;
-      if (vrow && p.conv_stout && g == p.nseg - 1 && col < K) {
-        const int t = p.L - K + col;
-        float v;
-        if (t >= 0) {
-          const uint32_t orow = w.ou - static_cast<uint32_t>(col * E);
-          v = Elem<T>::f32(Elem<T>::load(w.wu.at(0), orow + static_cast<uint32_t>(t * E)));
-        } else {
-          v = p.conv_in ? p.conv_in[(b * p.dim + d) * K + K + t] : 0.0f;
-        }
-        p.conv_stout[(b * p.dim + d) * K + col] = v;
+  }
+  if constexpr (KP > 0) {
+    // the last K inputs, for the decode update to continue from
+    const int K = p.K;
+    if (vrow && p.conv_stout && g == p.nseg - 1 && col < K) {
+      const int t = p.L - K + col;
+      float v;
+      if (t >= 0) {
+        const uint32_t orow = w.ou - static_cast<uint32_t>(col * E);
+        v = Elem<T>::f32(Elem<T>::load(w.wu.at(0), orow + static_cast<uint32_t>(t * E)));
+      } else {
+        v = p.conv_in ? p.conv_in[(b * p.dim + d) * K + K + t] : 0.0f;
       }
+      p.conv_stout[(b * p.dim + d) * K + col] = v;
     }
-  } else {
-    // segment aggregate: end state from zero and the step-size sum (fp64 partial
-    // sums of the 16 owner lanes of each channel, added in a fixed order)
+  }
+  if constexpr (kSegm) {
+    // pass 1: segment aggregate, the end state and the step-size sum (fp64
+    // partial sums of the 16 owner lanes of each channel, added in a fixed
+    // order)
     sSum[wave][row][col] = ssum;
     __builtin_amdgcn_wave_barrier();
     asm volatile("" ::: "memory");
-    float* ag = p.agg + ((b * p.dim + dc) * (p.nseg - 1) + g) * aggs;
+    float* ag = p.agg + (arow + g) * aggs;
     if (vrow) {
 #pragma unroll
       for (int q = 0; q < S; ++q) {
@@ -751,11 +800,15 @@ void launch_mode(int lane, bool bf16, bool softplus, int K, bool defer, dim3 gri
   }
 }
 
-// Both passes' launches for S state slots per lane (defined in
-// scan_fwd_s<S>.hip).
+// Launches for S state slots per lane (defined in scan_fwd_s<S>.hip): pass 0
+// is the one-segment scan, passes 1 and 2 those of a segmented sequence.
 template <int S>
-void launch_slots(bool aggregate, int lane, bool bf16, bool softplus, int K, bool defer, dim3 grid,
+void launch_slots(int pass, int lane, bool bf16, bool softplus, int K, bool defer, dim3 grid,
                   const ScanParams& p, hipStream_t stream);
+// Passes 1 and 2 of a segmented sequence (defined in scan_fwd_seg_s<S>.hip).
+template <int S>
+void launch_slots_seg(int pass, int lane, bool bf16, bool softplus, int K, dim3 grid,
+                      const ScanParams& p, hipStream_t stream);
 
 }  // namespace fwd
 }  // namespace ssm

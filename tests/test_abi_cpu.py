@@ -445,6 +445,16 @@ def test_scan_lane_mode_window_counts_group_stride():
     assert ssm.validate_scan(a) == ALIAS
 
 
+def test_segmented_workspace_size():
+    """The segmented scan keeps one aggregate (end state and step-size sum,
+    dstate + 1 floats) per channel and segment; the 1M-token config (96
+    channel groups) is cut into 13 segments.  Layer shapes with enough
+    channel groups run as one segment and need none."""
+    a = grouped_scan(1, N=16, dim=1536, L=1 << 20, batch=1)
+    assert ssm.scan_workspace_size(a) == 1536 * 13 * 17 * 4
+    assert ssm.scan_workspace_size(grouped_scan(1, N=16, dim=1536, L=2048, batch=8)) == 0
+
+
 def test_workspace_grows_with_dstate():
     a = grouped_scan(1, N=16, dim=16, L=1 << 20, batch=1)
     b = grouped_scan(1, N=64, dim=16, L=1 << 20, batch=1)
