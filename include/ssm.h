@@ -32,7 +32,9 @@
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
- *     library never allocates, never frees and holds no global state.
+ *     library never allocates and never frees; its only global state is the
+ *     static scratch of ssm_selective_scan_fwd_noalloc (and the per-device
+ *     address of it), which no other entry point touches.
  *   - Strides are in ELEMENTS and must be >= 0.  The innermost (time, or
  *     state for decode) stride is implicitly 1.
  *   - io_dtype (SSM_F32 or SSM_BF16) is the dtype of u/delta/z/B/C/out in the
@@ -45,7 +47,8 @@
  *     itself; a device fault shows up at the caller's next synchronisation.
  *   - No exception crosses the ABI; errors are ssm_status codes, explained by
  *     ssm_status_string().  On any error nothing is launched.
- *   - The library is re-entrant and thread-safe (no mutable global state).
+ *   - The library is re-entrant and thread-safe (the no-allocation scan's
+ *     shared scratch excepted, see there).
  */
 #ifndef SSM_H_
 #define SSM_H_
@@ -57,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 6
+#define SSM_ABI_VERSION 7
 
 /* Tokens between two state checkpoints (see ssm_scan_args.checkpoints). */
 #define SSM_CHECKPOINT_TOKENS 16
@@ -68,6 +71,9 @@ extern "C" {
 /* Largest state size of the scan and the decode update (the Mamba training
  * and inference guide's parameter table puts d_state between 8 and 64). */
 #define SSM_MAX_DSTATE 64
+
+/* Size of the static device scratch of ssm_selective_scan_fwd_noalloc. */
+#define SSM_NOALLOC_SCRATCH_BYTES (2u << 20)
 
 typedef enum ssm_status {
   SSM_OK = 0,
@@ -84,7 +90,9 @@ typedef enum ssm_status {
                               32-bit token indices (>= 2^31 - 64), or row
                               spans past the 32-bit windows (see
                               ssm_scan_args)                                   */
-  SSM_ERR_HIP = 8          /* the HIP runtime rejected the launch              */
+  SSM_ERR_HIP = 8,         /* the HIP runtime rejected the launch              */
+  SSM_ERR_SCRATCH = 9      /* ssm_selective_scan_fwd_noalloc: the segment
+                              aggregates exceed SSM_NOALLOC_SCRATCH_BYTES      */
 } ssm_status;
 
 typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
@@ -366,6 +374,23 @@ int ssm_validate_ssd(const ssm_ssd_args* args);
 
 /* Prefill scan (see ssm_scan_args).  Validates, then launches on `stream`. */
 int ssm_selective_scan_fwd(const ssm_scan_args* args, void* stream);
+
+/* The prefill scan for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and kernels as ssm_selective_scan_fwd, and it calls no
+ * allocating routine.  args->workspace and args->workspace_bytes are ignored;
+ * long sequences with few channels are cut into segments with their
+ * aggregates kept in a static device buffer of SSM_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every device it runs on until the process ends (its
+ * address is looked up on the first call on each device).  That is enough
+ * for every argument block with dstate <= 16 (at most 1.4 MB are needed);
+ * with more states, blocks whose aggregates, ssm_scan_workspace_size(args)
+ * bytes, exceed it return SSM_ERR_SCRATCH and launch nothing.  Every call on
+ * a device shares that device's buffer: calls on one device that may
+ * overlap in time (different streams, no ordering between them) race on it
+ * and must be serialised by the caller.  The buffer holds no state between
+ * calls that needs clearing.  Returns an ssm_status. */
+int ssm_selective_scan_fwd_noalloc(const ssm_scan_args* args, void* stream);
 
 /* Scan backward (see ssm_scan_bwd_args).  Validates, then launches on
  * `stream`. */

@@ -32,13 +32,14 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssm.so")
 
-SSM_ABI_VERSION = 6
+SSM_ABI_VERSION = 7
 CHECKPOINT_TOKENS = 16
 MAX_CONV = 8
 SSM_F32, SSM_BF16 = 0, 1
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_STRIDE",
           4: "SSM_ERR_DTYPE", 5: "SSM_ERR_ALIGN", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_UNSUPPORTED",
-          8: "SSM_ERR_HIP"}
+          8: "SSM_ERR_HIP", 9: "SSM_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 2 << 20
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -156,6 +157,8 @@ def lib():
         L.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ScanBwdArgs)]
         L.ssm_selective_scan_fwd.restype = ctypes.c_int
         L.ssm_selective_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _P]
+        L.ssm_selective_scan_fwd_noalloc.restype = ctypes.c_int
+        L.ssm_selective_scan_fwd_noalloc.argtypes = [ctypes.POINTER(ScanArgs), _P]
         L.ssm_selective_scan_bwd.restype = ctypes.c_int
         L.ssm_selective_scan_bwd.argtypes = [ctypes.POINTER(ScanBwdArgs), _P]
         L.ssm_selective_state_update.restype = ctypes.c_int
@@ -199,6 +202,10 @@ def scan_bwd_workspace_size(args: "ScanBwdArgs") -> int:
 
 def scan_fwd_raw(args: ScanArgs, stream: int = 0) -> int:
     return lib().ssm_selective_scan_fwd(ctypes.byref(args), _P(stream or None))
+
+
+def scan_fwd_noalloc_raw(args: ScanArgs, stream: int = 0) -> int:
+    return lib().ssm_selective_scan_fwd_noalloc(ctypes.byref(args), _P(stream or None))
 
 
 def validate_ssd(args: SsdArgs) -> int:
@@ -302,7 +309,8 @@ def _stream(stream):
 def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_softplus=True,
                        h0=None, return_last_state=False, out=None, last_state=None, stream=None,
                        workspace=None, checkpoints=None, conv_weight=None, conv_bias=None,
-                       conv_state_in=None, conv_state_out=None, conv_out=None, conv_silu=True):
+                       conv_state_in=None, conv_state_out=None, conv_out=None, conv_silu=True,
+                       noalloc=False):
     """Prefill selective scan on the GPU (see the module docstring).
 
     `workspace` (optional): a device tensor reused across calls; when None,
@@ -315,7 +323,11 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
     x) (no SiLU with conv_silu=False).  conv_state_in (batch, dim, d_conv)
     fp32 holds the inputs before the sequence; conv_state_out (same shape,
     filled with the last d_conv inputs) and conv_out (like u, the SSM
-    input) are optional output tensors."""
+    input) are optional output tensors.
+    `noalloc=True` calls ssm_selective_scan_fwd_noalloc, which keeps the
+    segment aggregates in the library's static device scratch (no workspace
+    is passed or allocated; pass `out` and `last_state` to allocate
+    nothing at all)."""
     torch = _torch()
     if u.dim() != 3:
         raise ValueError("u must be (batch, dim, L)")
@@ -385,6 +397,11 @@ def selective_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta
                 raise ValueError("conv_out must be (batch, dim, L) with time stride 1")
             a.conv_out = _ptr(conv_out)
             a.conv_out_batch_stride, a.conv_out_dim_stride = conv_out.stride()[:2]
+    if noalloc:
+        st = scan_fwd_noalloc_raw(a, _stream(stream))
+        if st != 0:
+            raise SSMError(st, "ssm_selective_scan_fwd_noalloc")
+        return (out, last_state) if return_last_state else out
     need = scan_workspace_size(a) if workspace is not False else 0
     if need:
         if workspace is None or workspace.numel() * workspace.element_size() < need:

@@ -1,9 +1,17 @@
 // scan_fwd.hip -- host side of the prefill selective scan: segment choice,
-// B/C mode, workspace, window limits and the launches.  The kernel itself is
+// B/C mode, workspace, window limits and the launches, and the static
+// segment scratch of the no-allocation entry point.  The kernel itself is
 // in scan_fwd_kernel.h (instantiated by scan_fwd_s1/s2/s4.hip).
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "scan_fwd_kernel.h"
+
+// The no-allocation entry point's segment scratch: one copy per device, held
+// until the process ends.  Host code never uses this name as an address; it
+// takes the device address from hipGetSymbolAddress once per device.
+static __device__ __align__(256) float scratch[SSM_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace ssm {
 namespace {
@@ -82,6 +90,53 @@ size_t scan_workspace_bytes(const ssm_scan_args& a) {
   const int nseg = choose_segments(groups, a.seqlen);
   if (nseg <= 1) return 0;
   return static_cast<size_t>(a.batch * a.dim * nseg * (a.dstate + 1)) * sizeof(float);
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The device address of the current device's copy of `scratch`, looked up
+// on the first call on that device (with it current) and kept.
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!ptr) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return hipSuccess;
+}
+
+}  // namespace
+
+// The scan with the segment aggregates in `scratch` instead of a caller
+// workspace.  Pass 1 writes every aggregate that pass 2 reads, so nothing in
+// the scratch needs clearing between calls.
+int scan_fwd_noalloc(const ssm_scan_args& a, hipStream_t stream) {
+  if (scan_workspace_bytes(a) > SSM_NOALLOC_SCRATCH_BYTES) return SSM_ERR_SCRATCH;
+  ssm_scan_args b = a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (scan_workspace_bytes(a) > 0) {
+    void* ptr = nullptr;
+    if (scratch_address(&ptr) != hipSuccess) return SSM_ERR_HIP;
+    b.workspace = ptr;
+    b.workspace_bytes = SSM_NOALLOC_SCRATCH_BYTES;
+  }
+  return launch_scan_fwd(b, stream) == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {

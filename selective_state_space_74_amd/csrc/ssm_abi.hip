@@ -88,6 +88,7 @@ const char* ssm_status_string(int status) {
     case SSM_ERR_ALIAS: return "an output overlaps an input";
     case SSM_ERR_UNSUPPORTED: return "unsupported configuration (dstate or B/C groups outside what is built, or a size past the limits in ssm.h)";
     case SSM_ERR_HIP: return "HIP runtime error at launch";
+    case SSM_ERR_SCRATCH: return "the scan needs more segment scratch than the no-allocation entry point's static buffer (SSM_NOALLOC_SCRATCH_BYTES) holds";
     default: return "unknown status";
   }
 }
@@ -370,6 +371,18 @@ int ssm_selective_scan_fwd(const ssm_scan_args* a, void* stream) {
   if (ssm::launch_scan_fwd(*a, static_cast<hipStream_t>(stream)) != hipSuccess)
     return SSM_ERR_HIP;
   return SSM_OK;
+}
+
+int ssm_selective_scan_fwd_noalloc(const ssm_scan_args* a, void* stream) {
+  if (!a) return SSM_ERR_NULL;
+  // the caller's workspace is not used: validate without it
+  ssm_scan_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  const int st = ssm_validate_scan(&b);
+  if (st != SSM_OK) return st;
+  if (b.batch == 0 || b.dim == 0) return SSM_OK;
+  return ssm::scan_fwd_noalloc(b, static_cast<hipStream_t>(stream));
 }
 
 int ssm_selective_scan_bwd(const ssm_scan_bwd_args* a, void* stream) {

@@ -10,6 +10,9 @@ namespace ssm {
 
 // Launches; arguments already validated by the ABI layer.
 hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream);
+// The same scan with its segment scratch in the library's static device
+// buffer (validated arguments; returns an ssm_status).
+int scan_fwd_noalloc(const ssm_scan_args& a, hipStream_t stream);
 size_t scan_workspace_bytes(const ssm_scan_args& a);
 // The scan addresses each wavefront's rows through 32-bit byte windows.
 bool scan_windows_fit(const ssm_scan_args& a);

@@ -36,18 +36,20 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_struct_layout():
     L = ssm.lib()
-    assert L.ssm_abi_version() == ssm.SSM_ABI_VERSION == 6
+    assert L.ssm_abi_version() == ssm.SSM_ABI_VERSION == 7
     assert L.ssm_scan_args_size() == ctypes.sizeof(ssm.ScanArgs)
     assert L.ssm_scan_bwd_args_size() == ctypes.sizeof(ssm.ScanBwdArgs)
     assert L.ssm_update_args_size() == ctypes.sizeof(ssm.UpdateArgs)
     header = open(HEADER).read()
-    assert "#define SSM_ABI_VERSION 6" in header
+    assert "#define SSM_ABI_VERSION 7" in header
+    assert f"#define SSM_NOALLOC_SCRATCH_BYTES (2u << 20)" in header
+    assert ssm.NOALLOC_SCRATCH_BYTES == 2 << 20
     assert f"#define SSM_MAX_CONV {ssm.MAX_CONV}" in header
     assert f"#define SSM_CHECKPOINT_TOKENS {ssm.CHECKPOINT_TOKENS}" in header
 
 
 def test_status_strings():
-    for code in range(9):
+    for code in range(10):
         s = ssm.status_string(code)
         assert isinstance(s, str) and s
     assert ssm.status_string(123) == "unknown status"
@@ -105,6 +107,7 @@ def test_null_block():
     assert L.ssm_validate_scan(None) == NULL
     assert L.ssm_validate_update(None) == NULL
     assert L.ssm_selective_scan_fwd(None, None) == NULL
+    assert L.ssm_selective_scan_fwd_noalloc(None, None) == NULL
     assert L.ssm_selective_state_update(None, None) == NULL
 
 
@@ -483,3 +486,45 @@ def test_bwd_groups_of_sixteen_channels_pass():
     assert ssm.validate_scan_bwd(a) == OK
     a.dC = a.dB + 2 * 2 * 16 * 64 * 4 - 4  # dB is (batch, 2, 16, L): overlap by one float
     assert ssm.validate_scan_bwd(a) == ALIAS
+
+
+SCRATCH = 9
+
+
+def spaced_scan(batch, dim, L, N, io=1):
+    """A valid scan block whose tensors sit 4 GiB apart (fake addresses)."""
+    a = ssm.ScanArgs()
+    a.batch, a.dim, a.seqlen, a.dstate = batch, dim, L, N
+    a.io_dtype, a.delta_softplus = io, 1
+    far = lambda i: BASE + i * (1 << 32)
+    for i, name in enumerate(("u", "delta", "z", "out")):
+        setattr(a, name, far(i))
+        setattr(a, f"{name}_batch_stride", dim * L)
+        setattr(a, f"{name}_dim_stride", L)
+    for i, name in enumerate(("B", "C")):
+        setattr(a, name, far(4 + i))
+        setattr(a, f"{name}_batch_stride", N * L)
+        setattr(a, f"{name}_state_stride", L)
+    a.A, a.A_dim_stride, a.A_state_stride = far(6), N, 1
+    a.D, a.delta_bias, a.h0, a.last_state = far(7), far(8), far(9), far(10)
+    return a
+
+
+def test_noalloc_scratch_limit_is_checked_on_the_host():
+    """The no-allocation scan validates like the workspace entry point and
+    rejects, before any HIP call, a block whose segment aggregates exceed
+    its static scratch (64 states, 96 channel groups, 13 segments: 5.2 MB);
+    with 16 states every shape fits (at most 16 x 1280 channel-segments of
+    17 floats)."""
+    L = ssm.lib()
+    big = spaced_scan(1, 1536, 13 * 8192, 64)
+    assert ssm.validate_scan(big) == OK
+    assert ssm.scan_workspace_size(big) > ssm.NOALLOC_SCRATCH_BYTES
+    assert L.ssm_selective_scan_fwd_noalloc(ctypes.byref(big), None) == SCRATCH
+    assert "SSM_NOALLOC_SCRATCH_BYTES" in ssm.status_string(SCRATCH)
+    for dim in (16, 100, 1536, 5000, 10000):
+        a = spaced_scan(1, dim, 1 << 21, 16)
+        assert ssm.scan_workspace_size(a) <= 16 * 1280 * 17 * 4 <= ssm.NOALLOC_SCRATCH_BYTES
+    bad = spaced_scan(1, 16, 64, 16)
+    bad.seqlen = -1
+    assert L.ssm_selective_scan_fwd_noalloc(ctypes.byref(bad), None) == SHAPE
