@@ -68,8 +68,8 @@ extern "C" {
 /* Largest width of the fused causal conv (see ssm_scan_args.conv_weight). */
 #define SSM_MAX_CONV 8
 
-/* Largest state size of the scan and the decode update (the Mamba training
- * and inference guide's parameter table puts d_state between 8 and 64). */
+/* Largest state size of the scan and the decode update (the Mamba paper
+ * notes, section 3.2, put d_state between 8 and 64). */
 #define SSM_MAX_DSTATE 64
 
 /* Size of the static device scratch of ssm_selective_scan_fwd_noalloc. */
