@@ -497,7 +497,6 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   __shared__ __align__(16) float sC[!kOC ? kTile : 1][kN * S][kGPitch];
   __shared__ __align__(16) float sCt[kOC ? 2 : 1][kOC ? kGT : 1][kCPitch];
   __shared__ __align__(16) float sP[kWaves][kRows][kPartRow];
-  __shared__ double sSum[kSegm ? kWaves : 1][kRows][kT];
 
   // wavefront index, made visibly uniform so that windows stay in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -736,12 +735,12 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
     }
   }
   if constexpr (kSegm) {
-    // pass 1: segment aggregate, the end state and the step-size sum (fp64
-    // partial sums of the 16 owner lanes of each channel, added in a fixed
-    // order)
-    sSum[wave][row][col] = ssum;
-    __builtin_amdgcn_wave_barrier();
-    asm volatile("" ::: "memory");
+    // pass 1: segment aggregate, the end state and the step-size sum (the
+    // fp64 partial sums of the 16 owner lanes of each channel, added by a
+    // lane butterfly in registers: the workgroup's LDS stays that of the
+    // one-segment scan, five workgroups per CU)
+#pragma unroll
+    for (int m = 1; m < kN; m <<= 1) ssum += __shfl_xor(ssum, m, kN);
     float* ag = p.agg + (arow + g) * aggs;
     if (vrow) {
 #pragma unroll
@@ -750,11 +749,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
         if (n < N) ag[n] = h[q];
       }
     }
-    if (vrow && col == 0) {
-      double s = 0.0;
-      for (int j = 0; j < kT; ++j) s += sSum[wave][row][j];
-      ag[N] = static_cast<float>(s);
-    }
+    if (vrow && col == 0) ag[N] = static_cast<float>(ssum);
   }
 }
 

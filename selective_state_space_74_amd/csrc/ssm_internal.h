@@ -50,16 +50,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|), on the hardware
-// exp2/log2/rcp.  log1p(y) for y in (0, 1] uses the exact-rounding correction
-// log1p(y) = log(1 + y) * y / ((1 + y) - 1), which keeps full relative accuracy
-// for small y (Delta around 1e-3 sits there); when 1 + y rounds to 1 the
-// answer is y itself.
+// exp2/log2/rcp.  log1p(y) for y in (0, 1] is log(u) for u = 1 + y rounded,
+// plus the part of y that the rounding dropped, e = y - (u - 1) (exact), over
+// u: log1p(y) = log(u) + log(1 + e/u), and |e/u| <= 2^-24 leaves only the
+// first-order term.  This keeps full relative accuracy for small y (Delta
+// around 1e-3 sits there), and when 1 + y rounds to 1 it gives y itself.
 __device__ __forceinline__ float softplus_f32(float x) {
   const float y = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
   const float u = 1.0f + y;
-  const float d = u - 1.0f;
-  const float l = __builtin_amdgcn_logf(u) * kLn2;
-  const float lp = d == 0.0f ? y : l * (y * __builtin_amdgcn_rcpf(d));
+  const float e = y - (u - 1.0f);
+  const float lp = fmaf(__builtin_amdgcn_logf(u), kLn2, e * __builtin_amdgcn_rcpf(u));
   return fmaxf(x, 0.0f) + lp;
 }
 
