@@ -626,8 +626,7 @@ def main():
     secondary = {}
     if not args.no_secondary:
         log(f"[bench] secondary {layer.name}")
-        secondary[layer.name] = bench_scan(layer, max(20, args.steps), args.warmup, torch, ssm, si,
-                                           graph=True)
+        secondary[layer.name] = bench_scan(layer, max(20, args.steps), args.warmup, torch, ssm, si)
         log(f"[bench] {layer.name} {secondary[layer.name]['gbps']:.1f} GB/s, "
             f"kernel median {secondary[layer.name]['kernel_ms'] * 1e3:.1f} us")
         c2 = si.SCAN_CONFIGS[2]

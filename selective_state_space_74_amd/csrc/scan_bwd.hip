@@ -28,12 +28,16 @@
 //   3. state lanes run the adjoint from token 15 down to 0, accumulating dA in
 //      a register and leaving per-token terms in LDS: g B and g A e h_{t-1}
 //      (summed over n by the owners, who finish du and ddelta), g Delta u and
-//      dy h_t (summed over the workgroup's 16 channels, then added to dB and
-//      dC with one device atomic per (n, t) and workgroup); this runs in two
+//      dy h_t (summed over the workgroup's 16 channels); this runs in two
 //      halves of 8 tokens so that the LDS holds half a block of terms.
-// dA, dD and the bias gradient are summed over batch rows with device atomics
-// at the end.  B/C tiles are staged as in the forward (16 states x 32 tokens,
-// double buffered), walking backwards.
+// The workgroup's dB/dC sums go, with a caller workspace (the default of the
+// binding), to the workgroup's own slot of a partial-sum buffer that a second
+// kernel adds up per group in a fixed order (deterministic); without one,
+// they are added into dB and dC with one device atomic per (n, t) and
+// workgroup.  dA, dD and the bias gradient are summed over batch rows the
+// same way: per-row slots and an ordered sum with the workspace, device
+// atomics without.  B/C tiles are staged as in the forward (16 states x 32
+// tokens, double buffered), walking backwards.
 #include <algorithm>
 
 #include "ssm_internal.h"
