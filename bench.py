@@ -228,14 +228,19 @@ def scan_bwd_bytes(batch, dim, L, N, esz, gate=True):
 
 
 def bench_bwd(cfg, steps, torch, ssm, si):
-    """Times the scan backward (from the forward's checkpoints)."""
+    """Times the scan backward (from the forward's checkpoints); long
+    sequences with few channels run segmented (the workspace holds the
+    segments' adjoint aggregates)."""
     dev = "cuda"
-    t = si.to_torch(si.scan_inputs_for(cfg), dev)
+    big = cfg.seqlen * cfg.batch * cfg.dim > 200_000_000
+    t = si.scan_inputs_device(cfg, dev) if big else si.to_torch(si.scan_inputs_for(cfg), dev)
     ck = torch.empty(ssm.checkpoint_shape(cfg.batch, cfg.dim, cfg.seqlen), dtype=torch.float32,
                      device=dev)
     kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"])
     ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], checkpoints=ck, **kw)
-    dout = torch.randn_like(t["u"], dtype=torch.float32).to(t["u"].dtype)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    dout = torch.randn(t["u"].shape, generator=gen, device=dev).to(t["u"].dtype)
     # the dB/dC partial-sum workspace, allocated once outside the timed region
     a = ssm.ScanBwdArgs()
     a.batch, a.dim, a.seqlen, a.dstate = cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate
@@ -664,7 +669,7 @@ def main():
         log(f"[bench] {cs.name} {secondary[cs.name]['gbps']:.1f} GB/s, "
             f"{secondary[cs.name]['kernel_ms'] * 1e3:.1f} us, "
             f"{secondary[cs.name]['mfma_tflops']:.1f} TFLOP/s on the matrix cores")
-        for cid in (1, 2):
+        for cid in (1, 2, 3):
             cb = si.SCAN_CONFIGS[cid]
             key = f"{cb.name}-backward"
             log(f"[bench] secondary {key}")

@@ -201,14 +201,19 @@ typedef struct ssm_scan_args {
  * are accumulated with device atomics when no workspace is given, so their
  * last bits can vary from run to run; with a workspace every output is
  * deterministic.  Outputs must not overlap
- * each other or any input.  The backward runs every sequence as one segment.
+ * each other or any input.  With the workspace, long sequences with few
+ * channels are cut into segments: a pass over segments 1..G-1 records the
+ * adjoint leaving each segment at its start (the adjoint recurrence needs no
+ * forward state), and every segment then runs the full backward from the
+ * exact adjoint entering it (Mamba paper notes, section 5.4: state passed at
+ * chunk edges); without it, each sequence is one segment.
  * It is built for dstate == 16 and for B/C groups that keep each block of 16
  * consecutive channels in one group (one group, or dim / ngroups a multiple
  * of 16); other shapes return SSM_ERR_UNSUPPORTED.
  * Workspace (optional): device scratch owned by the caller, 4-byte aligned,
  * of at least ssm_scan_bwd_workspace_size() bytes, not overlapping any
  * tensor.  The library then writes each block of 16 channels' dB/dC partial
- * sums, and each batch row's dA, dD and ddelta_bias, there with plain
+ * sums, and each segment's and batch row's dA, dD and ddelta_bias, there with plain
  * stores and adds them in fixed order in second passes, instead of adding
  * into the outputs with device atomics: every output is then deterministic,
  * and the time no longer depends on where dB and dC sit (the atomics on
@@ -356,8 +361,9 @@ size_t ssm_ssd_args_size(void);
 size_t ssm_scan_workspace_size(const ssm_scan_args* args);
 
 /* Workspace bytes the backward can use for this argument block:
- * batch * ceil(dim / 16) * 2 * 16 * seqlen + batch * dim * 18 fp32 values
- * (0 for an empty
+ * batch * ceil(dim / 16) * 2 * 16 * seqlen + G * batch * dim * 18 fp32
+ * values, plus batch * dim * G * 17 for the adjoint aggregates when the
+ * sequence is cut into G > 1 segments (0 for an empty
  * sequence or when batch * ngroups exceeds 65535, where it adds dB/dC with
  * atomics anyway).  Reads only sizes; pure host code. */
 size_t ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args* args);

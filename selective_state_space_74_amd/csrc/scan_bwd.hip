@@ -38,6 +38,18 @@
 // same way: per-row slots and an ordered sum with the workspace, device
 // atomics without.  B/C tiles are staged as in the forward (16 states x 32
 // tokens, double buffered), walking backwards.
+//
+// Long sequences with few channels (with the workspace) are cut into
+// segments, as the forward does.  The adjoint recurrence
+// g_{t-1} = e_t (dy_t C_t + g_t) is linear in g and needs no forward state, so
+//   pass 1 (bwd_aggregate_kernel) runs it over segments 1..G-1 from a zero
+//          adjoint and records what leaves each segment at its start,
+//          alpha_s, and the segment's step-size sum S_s;
+//   pass 2 (scan_bwd_kernel) runs the full backward of segment s from the
+//          exact adjoint entering it from the right,
+//          K_s = alpha_{s+1} + exp(A S_{s+1}) K_{s+1},  K_{G-1} = dlast,
+//          with dA, dD and the bias gradient in per-segment slots.
+// Every output is then the single-segment result up to fp32 rounding.
 #include <algorithm>
 
 #include "ssm_internal.h"
@@ -98,9 +110,12 @@ struct BwdParams {
   float* dbias;
   float* dh0;
   float* part;          // [batch][cgroups][2][kN][L] dB/dC partial sums, or NULL (atomics)
-  float* pdA;           // with part: [batch][dim][kN] dA, [batch][dim] dD and bias
-  float* pdD;           // gradient per batch row, summed over rows by a second
-  float* pdb;           // kernel (NULL: device atomics into dA, dD, dbias)
+  float* pdA;           // with part: [nseg][batch][dim][kN] dA, [nseg][batch][dim] dD and
+  float* pdD;           // bias gradient per segment and batch row, summed over both
+  float* pdb;           // by a second kernel (NULL: device atomics into dA, dD, dbias)
+  float* agg;           // segmented: [batch][dim][nseg][kN + 1] adjoint aggregates
+  int seg_len;          // tokens per segment (a multiple of kGT)
+  int nseg;             // segments per sequence (1: the whole sequence)
   int64_t usb, usd, dsb, dsd, zsb, zsd, Bsb, Bsn, Csb, Csn, Asd, Asn, gsb, gsd;
   int64_t dusb, dusd, ddsb, ddsd, dzsb, dzsd;
   int64_t Bsg, Csg;     // B/C group strides
@@ -341,8 +356,11 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = (threadIdx.x >> 4) & 3;
   const int col = threadIdx.x & 15;
-  const int64_t b = blockIdx.x / p.cgroups;
-  const int64_t cg = blockIdx.x % p.cgroups;
+  // blockIdx.x = (b * cgroups + cg) * nseg + seg
+  const int seg = static_cast<int>(blockIdx.x % p.nseg);
+  const int64_t bcg = blockIdx.x / p.nseg;
+  const int64_t b = bcg / p.cgroups;
+  const int64_t cg = bcg % p.cgroups;
   const int64_t d = cg * kCh + kRows * wave + row;
   const bool vrow = d < p.dim;
   const int64_t dc = vrow ? d : p.dim - 1;
@@ -403,21 +421,33 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   w.Dd = p.D ? p.D[dc] : 0.0f;
   w.sB = sB; w.sC = sC; w.sX = sX[wave]; w.sQ = sQ;
 
+  // The adjoint entering the segment from the right: dlast, folded with the
+  // aggregates of the later segments (segment i turns K into
+  // alpha_i + exp(A S_i) K).
   float g = p.dlast ? p.dlast[(b * p.dim + dc) * kN + col] : 0.0f;
+  if (seg < p.nseg - 1) {
+    const float* ag = p.agg + (b * p.dim + dc) * p.nseg * (kN + 1);
+    for (int i = p.nseg - 1; i > seg; --i)
+      g = fmaf(__builtin_amdgcn_exp2f(w.a2 * ag[i * (kN + 1) + kN]), g, ag[i * (kN + 1) + col]);
+  }
   float dA = 0.0f, dDs = 0.0f, dbs = 0.0f;
 
+  // this segment's blocks [kbeg, kend), walked from the last; segment
+  // starts are multiples of a tile
+  const int kbeg = seg * (p.seg_len / kT);
+  const int kend = std::min(p.nbk, kbeg + p.seg_len / kT);
   // the last tile first; owner inputs of block k in buffer k % 2, the next
   // (earlier) one loading meanwhile
-  const int nbk = p.nbk;
-  TileRaw tile = w.load_tile(w.ntile - 1);
-  w.stage(w.ntile - 1, tile);
-  tile = w.load_tile(w.ntile - 2);
+  const int tl = (kend - 1) / kGB;
+  TileRaw tile = w.load_tile(tl);
+  w.stage(tl, tile);
+  tile = w.load_tile(tl - 1);
   __syncthreads();
-  Raw cur = w.load(nbk - 1);
-  for (int k = nbk - 1; k >= 0; --k) {
+  Raw cur = w.load(kend - 1);
+  for (int k = kend - 1; k >= kbeg; --k) {
     const Raw next = w.load(k - 1);
     w.block(k, cur, g, dA, dDs, dbs);
-    if (k % kGB == 0 && k > 0) {
+    if (k % kGB == 0 && k > kbeg) {
       // tile (k / kGB) - 1 into the other buffer; every wavefront finished
       // reading it before the barrier at the end of the previous block
       w.stage(k / kGB - 1, tile);
@@ -427,9 +457,10 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     cur = next;
   }
 
-  if (vrow && p.dh0) p.dh0[(b * p.dim + d) * kN + col] = g;
+  if (vrow && p.dh0 && seg == 0) p.dh0[(b * p.dim + d) * kN + col] = g;
+  const int64_t slot = seg * p.batch * p.dim + b * p.dim + d;   // per segment and batch row
   if (vrow) {
-    if (p.pdA) p.pdA[(b * p.dim + d) * kN + col] = dA;
+    if (p.pdA) p.pdA[slot * kN + col] = dA;
     else atomicAdd(&p.dA[d * kN + col], dA);
   }
   // dD and the bias gradient: sum the 16 owner lanes of the row
@@ -440,8 +471,8 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   }
   if (vrow && col == 0) {
     if (p.pdA) {
-      p.pdD[b * p.dim + d] = dDs;
-      p.pdb[b * p.dim + d] = dbs;
+      p.pdD[slot] = dDs;
+      p.pdb[slot] = dbs;
     } else {
       if (p.dD) atomicAdd(&p.dD[d], dDs);
       if (p.dbias) atomicAdd(&p.dbias[d], dbs);
@@ -449,19 +480,137 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   }
 }
 
-// dA, dD and the bias gradient from the per-batch-row partials, summed over
-// the rows in row order.
+// Pass 1 of a segmented backward: the adjoint recurrence alone over segment
+// s (1..nseg-1) from a zero adjoint at its end.  Lane (row c, col n) carries
+// the adjoint of state n of channel c; owner lane (row c, col j) forms dy
+// (dout through the gate) and Delta of token j of each block, handed to the
+// state lanes by DPP row broadcasts; C comes through the same double-buffered
+// LDS tiles as in the full backward.  Per token t, walking down:
+// g <- exp(Delta_t A) (dy_t C_t + g).  What leaves the segment at its start,
+// alpha_s = g, and the step-size sum S_s (fp64 per owner, summed by a lane
+// butterfly) go to agg[b][d][s].
+template <typename T, bool kSoftplus>
+__global__ __launch_bounds__(kThreads) void bwd_aggregate_kernel(BwdParams p) {
+  __shared__ __align__(16) float sC[2][kN][kGPitch];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = (threadIdx.x >> 4) & 3;
+  const int col = threadIdx.x & 15;
+  // blockIdx.x = (b * cgroups + cg) * (nseg - 1) + seg - 1
+  const int seg = 1 + static_cast<int>(blockIdx.x % (p.nseg - 1));
+  const int64_t bcg = blockIdx.x / (p.nseg - 1);
+  const int64_t b = bcg / p.cgroups;
+  const int64_t cg = bcg % p.cgroups;
+  const int64_t d = cg * kCh + kRows * wave + row;
+  const bool vrow = d < p.dim;
+  const int64_t dc = vrow ? d : p.dim - 1;
+  const int64_t dw0 = std::min<int64_t>(cg * kCh + kRows * wave, p.dim - 1);
+  const int64_t dw3 = std::min<int64_t>(dw0 + kRows - 1, p.dim - 1);
+  constexpr int E = Elem<T>::kSize;
+  const bool gate = p.z != nullptr;
+
+  auto rows_window = [&](const void* base, int64_t sb, int64_t sd, uint32_t& off) {
+    off = static_cast<uint32_t>(((dc - dw0) * sd + col) * E);
+    return Window{static_cast<const char*>(base) + (b * sb + dw0 * sd) * E,
+                  static_cast<uint32_t>(((dw3 - dw0) * sd + p.L) * E)};
+  };
+  uint32_t odt, oz, og;
+  const Window wdt = rows_window(p.delta, p.dsb, p.dsd, odt);
+  const Window wg = rows_window(p.dout, p.gsb, p.gsd, og);
+  const Window wz = gate ? rows_window(p.z, p.zsb, p.zsd, oz) : wdt;
+  if (!gate) oz = odt;   // loaded, never used
+  const int64_t grp = (cg * kCh) / p.cpg;
+  const int st = kRows * wave + row;
+  const uint32_t oC = static_cast<uint32_t>((st * p.Csn + col) * E);
+  const Window wC{static_cast<const char*>(p.C) + (b * p.Csb + grp * p.Csg) * E,
+                  static_cast<uint32_t>(((kN - 1) * p.Csn + p.L) * E)};
+  const float a2 = p.A[dc * p.Asd + col * p.Asn] * kLog2e;
+  const float bias = p.bias ? p.bias[dc] : 0.0f;
+
+  auto skip = [](int k) { return static_cast<uint32_t>(k * kT) * E; };
+  struct In { uint32_t dt, z, go; };
+  auto load = [&](int k) {
+    const uint32_t s = skip(max(k, 0));
+    return In{Elem<T>::load(wdt.at(s), odt), Elem<T>::load(wz.at(s), oz),
+              Elem<T>::load(wg.at(s), og)};
+  };
+  auto load_tile = [&](int t, uint32_t (&c)[kGB]) {
+    const __amdgpu_buffer_rsrc_t rc = wC.at(skip(max(t, 0) * kGB));
+#pragma unroll
+    for (int i = 0; i < kGB; ++i) c[i] = Elem<T>::load(rc, oC + i * kT * E);
+  };
+  auto stage = [&](int t, const uint32_t (&c)[kGB]) {
+#pragma unroll
+    for (int i = 0; i < kGB; ++i) sC[t & 1][st][col + i * kT] = Elem<T>::f32(c[i]);
+  };
+
+  const int kbeg = seg * (p.seg_len / kT);
+  const int kend = std::min(p.nbk, kbeg + p.seg_len / kT);
+  const int tl = (kend - 1) / kGB;
+  uint32_t tile[kGB];
+  load_tile(tl, tile);
+  stage(tl, tile);
+  load_tile(tl - 1, tile);
+  __syncthreads();
+  float g = 0.0f;
+  double ssum = 0.0;
+  In cur = load(kend - 1);
+  for (int k = kend - 1; k >= kbeg; --k) {
+    const In next = load(k - 1);
+    const int t0 = k * kT;
+    const int buf = (k / kGB) & 1;
+    const int tb = (k % kGB) * kT;
+    float cv[kT];
+#pragma unroll
+    for (int q = 0; q < kT / 4; ++q) {
+      const float4 y = *reinterpret_cast<const float4*>(&sC[buf][col][tb + 4 * q]);
+      cv[4 * q] = y.x; cv[4 * q + 1] = y.y; cv[4 * q + 2] = y.z; cv[4 * q + 3] = y.w;
+    }
+    // owner: Delta (zero past the end: softplus(-inf) = 0) and dy
+    const bool own = t0 + col < p.L;
+    const float x = Elem<T>::f32(cur.dt) + bias;
+    const float xm = own ? x : (kSoftplus ? -__builtin_inff() : 0.0f);
+    const float dl = kSoftplus ? softplus_f32(xm) : xm;
+    const float zv = Elem<T>::f32(cur.z);
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zv * kLog2e));
+    const float go = own ? Elem<T>::f32(cur.go) : 0.0f;
+    const float dy = gate ? go * zv * sg : go;
+    ssum += static_cast<double>(dl);
+    static_for<0, kT>([&](auto J) {
+      constexpr int j = kT - 1 - decltype(J)::value;
+      const float adj = fmaf(row_bcast<j>(dy), cv[j], g);
+      g = __builtin_amdgcn_exp2f(row_bcast<j>(dl) * a2) * adj;
+    });
+    if (k % kGB == 0 && k > kbeg) {
+      // the other buffer held tile k / kGB + 1, which every wavefront
+      // finished before the barrier that followed the previous staging
+      stage(k / kGB - 1, tile);
+      load_tile(k / kGB - 2, tile);
+      __syncthreads();
+    }
+    cur = next;
+  }
+#pragma unroll
+  for (int m = 1; m < kN; m <<= 1) ssum += __shfl_xor(ssum, m, kN);
+  if (vrow) {
+    float* ag = p.agg + ((b * p.dim + d) * p.nseg + seg) * (kN + 1);
+    ag[col] = g;
+    if (col == 0) ag[kN] = static_cast<float>(ssum);
+  }
+}
+
+// dA, dD and the bias gradient from the partials per segment and batch row
+// (`rows` = nseg * batch of them), summed in slot order.
 __global__ void param_sum_kernel(const float* pdA, const float* pdD, const float* pdb, float* dA,
-                                 float* dD, float* dbias, int64_t batch, int64_t dim) {
+                                 float* dD, float* dbias, int64_t rows, int64_t dim) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < dim * kN) {
     float s = 0.0f;
-    for (int64_t b = 0; b < batch; ++b) s += pdA[b * dim * kN + i];
+    for (int64_t b = 0; b < rows; ++b) s += pdA[b * dim * kN + i];
     dA[i] = s;
   }
   if (i < dim) {
     float sd = 0.0f, sb = 0.0f;
-    for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t b = 0; b < rows; ++b) {
       sd += pdD[b * dim + i];
       sb += pdb[b * dim + i];
     }
@@ -552,13 +701,35 @@ bool scan_bwd_windows_fit(const ssm_scan_bwd_args& a) {
 // (measured on the 130m-like layer: 561 us at 1 or 3 MiB apart, 713-729 us
 // at 2 or 8 MiB or 1 MiB + 4 KiB; the partial sums take 605 us at every
 // offset, and on the 2.8b-like layer they beat the atomics at any offset).
+namespace {
+
+// Segments of the backward: as in the forward, cut only when the batch x
+// channel groups leave the machine short of workgroups, here as many as fill
+// one residency round of the backward kernel (three workgroups of 4 waves
+// per CU at its register count), with segments of at least 8192 tokens.
+constexpr int64_t kBwdTargetGroups = 768;
+constexpr int64_t kBwdMinSegLen = 8192;
+constexpr int kBwdMaxSeg = 64;
+
+int bwd_segments(int64_t groups, int64_t L) {
+  if (groups >= kBwdTargetGroups / 2) return 1;
+  int64_t g = std::min<int64_t>(kBwdTargetGroups / groups, std::max<int64_t>(1, L / kBwdMinSegLen));
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(g, kBwdMaxSeg)));
+}
+
+}  // namespace
+
 size_t scan_bwd_workspace_bytes(const ssm_scan_bwd_args& a) {
   const int64_t G = a.ngroups > 1 ? a.ngroups : 1;
   const int64_t cgroups = (a.dim + kCh - 1) / kCh;
   if (a.batch <= 0 || a.dim <= 0 || a.seqlen <= 0) return 0;
   if (a.batch * G > 65535) return 0;   // the sum pass runs one grid row per (batch, group)
-  // dB/dC partials per channel block, then dA, dD and the bias gradient per batch row
-  return static_cast<size_t>(a.batch * cgroups * 2 * kN * a.seqlen + a.batch * a.dim * (kN + 2)) *
+  const int64_t nseg = bwd_segments(a.batch * cgroups, a.seqlen);
+  // dB/dC partials per channel block, then dA, dD and the bias gradient per
+  // segment and batch row, then (segmented) the adjoint aggregates
+  return static_cast<size_t>(a.batch * cgroups * 2 * kN * a.seqlen +
+                             nseg * a.batch * a.dim * (kN + 2) +
+                             (nseg > 1 ? a.batch * a.dim * nseg * (kN + 1) : 0)) *
          sizeof(float);
 }
 
@@ -593,9 +764,19 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
   p.du = a.du; p.ddelta = a.ddelta; p.dz = a.dz;
   p.dB = a.dB; p.dC = a.dC; p.dA = a.dA; p.dD = a.dD; p.dbias = a.ddelta_bias; p.dh0 = a.dh0;
   p.part = partials ? static_cast<float*>(a.workspace) : nullptr;
-  p.pdA = partials ? p.part + a.batch * ((a.dim + kCh - 1) / kCh) * 2 * kN * a.seqlen : nullptr;
-  p.pdD = partials ? p.pdA + a.batch * a.dim * kN : nullptr;
-  p.pdb = partials ? p.pdD + a.batch * a.dim : nullptr;
+  const int64_t cgroups = (a.dim + kCh - 1) / kCh;
+  // segments only with the workspace (the aggregates and per-segment
+  // partial sums live there); without it, one segment and atomics
+  p.nseg = partials ? bwd_segments(a.batch * cgroups, a.seqlen) : 1;
+  {
+    const int64_t seg = (a.seqlen + p.nseg - 1) / p.nseg;
+    p.seg_len = static_cast<int>((seg + kGT - 1) / kGT * kGT);
+    p.nseg = static_cast<int>((a.seqlen + p.seg_len - 1) / p.seg_len);
+  }
+  p.pdA = partials ? p.part + a.batch * cgroups * 2 * kN * a.seqlen : nullptr;
+  p.pdD = partials ? p.pdA + p.nseg * a.batch * a.dim * kN : nullptr;
+  p.pdb = partials ? p.pdD + p.nseg * a.batch * a.dim : nullptr;
+  p.agg = partials && p.nseg > 1 ? p.pdb + p.nseg * a.batch * a.dim : nullptr;
   p.usb = a.u_batch_stride; p.usd = a.u_dim_stride;
   p.dsb = a.delta_batch_stride; p.dsd = a.delta_dim_stride;
   p.zsb = a.z_batch_stride; p.zsd = a.z_dim_stride;
@@ -611,8 +792,19 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
   p.batch = a.batch; p.dim = a.dim; p.L = static_cast<int>(a.seqlen);
   p.nbk = static_cast<int>((a.seqlen + kT - 1) / kT);
   p.cgroups = (a.dim + kCh - 1) / kCh;
-  const dim3 grid(static_cast<unsigned>(a.batch * p.cgroups)), block(kThreads);
+  const dim3 grid(static_cast<unsigned>(a.batch * p.cgroups * p.nseg)), block(kThreads);
   const bool sp = a.delta_softplus != 0;
+  if (p.nseg > 1) {
+    // pass 1: the adjoint aggregates of segments 1..nseg-1
+    const dim3 agrid(static_cast<unsigned>(a.batch * p.cgroups * (p.nseg - 1)));
+    if (a.io_dtype == SSM_BF16) {
+      if (sp) bwd_aggregate_kernel<uint16_t, true><<<agrid, block, 0, stream>>>(p);
+      else bwd_aggregate_kernel<uint16_t, false><<<agrid, block, 0, stream>>>(p);
+    } else {
+      if (sp) bwd_aggregate_kernel<float, true><<<agrid, block, 0, stream>>>(p);
+      else bwd_aggregate_kernel<float, false><<<agrid, block, 0, stream>>>(p);
+    }
+  }
   if (a.io_dtype == SSM_BF16) {
     if (sp) scan_bwd_kernel<uint16_t, true><<<grid, block, 0, stream>>>(p);
     else scan_bwd_kernel<uint16_t, false><<<grid, block, 0, stream>>>(p);
@@ -635,7 +827,7 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
                                   sblock, 0, stream>>>(p.part, a.dB, a.dC, NL, p.cgroups, G);
     }
     param_sum_kernel<<<dim3(static_cast<unsigned>((a.dim * kN + 255) / 256)), dim3(256), 0, stream>>>(
-        p.pdA, p.pdD, p.pdb, a.dA, a.dD, a.ddelta_bias, a.batch, a.dim);
+        p.pdA, p.pdD, p.pdb, a.dA, a.dD, a.ddelta_bias, p.nseg * a.batch, a.dim);
   }
   return hipGetLastError();
 }

@@ -224,3 +224,60 @@ def test_backward_with_workspace_is_deterministic(io):
     for k in g1:
         assert torch.isfinite(g1[k].float()).all(), k
         assert torch.equal(g1[k], g2[k]), k
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("batch,dim,L", [(1, 16, 3 * 8192 + 100), (2, 40, 2 * 8192 + 48)])
+def test_backward_segmented_long_sequence(batch, dim, L, io):
+    """Few channels and a long sequence: with the workspace the backward cuts
+    the sequence into segments (an adjoint-aggregate pass, then the full
+    backward of every segment from its folded incoming adjoint).  Checked
+    against the oracle on every gradient, with h0 and dlast, and against the
+    single-segment run (no workspace: device atomics)."""
+    a = ssm.ScanBwdArgs()
+    a.batch, a.dim, a.seqlen, a.dstate = batch, dim, L, 16
+    # the workspace holds the aggregates and per-segment slots: segmented
+    assert ssm.scan_bwd_workspace_size(a) > 4 * (batch * ((dim + 15) // 16) * 32 * L + batch * dim * 18)
+    errs, g, *_ = run(batch, dim, L, io, seed=51 + dim)
+    check(errs, io, f"segmented b{batch} d{dim} L{L} {io}")
+    errs1, g1, *_ = run(batch, dim, L, io, seed=51 + dim, workspace=False)
+    check(errs1, io, f"single segment b{batch} d{dim} L{L} {io}")
+    for k in ("du", "ddelta", "dz", "dB", "dC", "dA", "dh0"):
+        e = row_rel_err(to_np(g[k]), to_np(g1[k]))
+        assert e <= TOL_BWD[io], (k, e)
+
+
+def test_backward_long_context_16_channels():
+    """The long-context workload's backward on its 16-channel sample (the
+    channels the forward parity uses) at the full 1,048,576 tokens, bf16 IO:
+    the sampled channels as a 16-channel problem, so that every gradient,
+    dB and dC included, has an oracle value.  64 segments."""
+    cfg = si.SCAN_CONFIGS[3]
+    t = si.scan_inputs_device(cfg, DEV)
+    ch = np.sort(np.random.default_rng(3).choice(cfg.dim, 16, replace=False))
+    idx = torch.from_numpy(ch).to(DEV)
+    sub = {k: t[k].index_select(1, idx).contiguous() for k in ("u", "delta", "z")}
+    sub.update(B=t["B"], C=t["C"], A=t["A"][idx].contiguous(), D=t["D"][idx].contiguous(),
+               delta_bias=t["delta_bias"][idx].contiguous())
+    del t
+    torch.cuda.empty_cache()
+    L = cfg.seqlen
+    g0 = torch.Generator(device=DEV)
+    g0.manual_seed(33)
+    dout = torch.randn((1, 16, L), generator=g0, device=DEV).to(torch.bfloat16)
+    dlast = torch.randn((1, 16, 16), generator=g0, device=DEV)
+    ck = torch.empty(ssm.checkpoint_shape(1, 16, L), dtype=torch.float32, device=DEV)
+    kw = dict(D=sub["D"], z=sub["z"], delta_bias=sub["delta_bias"])
+    ssm.selective_scan_fwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], checkpoints=ck, **kw)
+    g = ssm.selective_scan_bwd(dout, sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], ck,
+                               dlast=dlast, **kw)
+    torch.cuda.synchronize()
+    h = {k: to_np(v) for k, v in sub.items()}
+    ref = oracle.selective_scan_bwd(to_np(dout), h["u"], h["delta"], h["A"], h["B"], h["C"],
+                                    D=h["D"], z=h["z"], delta_bias=h["delta_bias"],
+                                    dlast=to_np(dlast))
+    errs = {k: (row_rel_err(to_np(g[k])[None], r[None]) if k in ("dD", "ddelta_bias")
+                else row_rel_err(to_np(g[k]), r)) for k, r in ref.items()}
+    check(errs, "bf16", "1M tokens, 16 channels")
+    del g, ck, dout, sub
+    torch.cuda.empty_cache()
