@@ -304,6 +304,24 @@ def test_bwd_workspace_size():
     assert ssm.scan_bwd_workspace_size(good_bwd(dim=320 * 16, N=32)) == 0
 
 
+def test_bwd_segmented_workspace_size():
+    """Long sequences with few channel blocks are cut into G segments (up to
+    768 workgroups, segments of at least 8192 tokens, at most 64): the
+    per-row parameter slots are per segment, and the adjoint aggregates
+    (17 floats per channel and segment) follow."""
+    def want(batch, dim, L, G):
+        return (batch * -(-dim // 16) * 2 * 16 * L + G * batch * dim * 18 +
+                (batch * dim * G * 17 if G > 1 else 0)) * 4
+    L = 3 * 8192 + 100
+    assert ssm.scan_bwd_workspace_size(good_bwd(batch=1, dim=16, L=L)) == want(1, 16, L, 3)
+    assert ssm.scan_bwd_workspace_size(good_bwd(batch=1, dim=1536, L=1 << 20)) == \
+        want(1, 1536, 1 << 20, 8)
+    assert ssm.scan_bwd_workspace_size(good_bwd(batch=1, dim=16, L=1 << 20)) == \
+        want(1, 16, 1 << 20, 64)
+    assert ssm.scan_bwd_workspace_size(good_bwd(batch=8, dim=1536, L=1 << 16)) == \
+        want(8, 1536, 1 << 16, 1)
+
+
 def test_bwd_workspace_alias_and_alignment():
     a = good_bwd()
     a.workspace, a.workspace_bytes = addr(22), 1 << 20
