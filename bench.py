@@ -441,6 +441,87 @@ def cpu_baseline_channels(cfg, si, torch, channels=128, target_s=10.0):
                       f"{sum(runs):.1f} s of CPU work"}
 
 
+def oracle_timings(si, torch):
+    """The fp64 oracle on the other workloads, as it stands: the tiny and the
+    130m-like configs single-threaded (one batch row of the latter), the
+    long-context config's 16-channel parity sample at its full length, and
+    the decode workload on every channel for its first 100 steps."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count() or 1
+    res = {}
+
+    def timed(fn, min_s=1.0):
+        runs = []
+        while not runs or (sum(runs) < min_s and len(runs) < 20):
+            t0 = time.perf_counter()
+            fn()
+            runs.append(time.perf_counter() - t0)
+        return float(np.median(runs)), len(runs)
+
+    for cid, rows in ((0, None), (1, 1)):
+        cfg = si.SCAN_CONFIGS[cid]
+        inp = si.scan_inputs_for(cfg)
+        k = cfg.batch if rows is None else rows
+        sl = lambda x: x[:k]
+        dt, n = timed(lambda: oracle.selective_scan(sl(inp["u"]), sl(inp["delta"]), inp["A"],
+                                                    sl(inp["B"]), sl(inp["C"]), D=inp["D"],
+                                                    z=sl(inp["z"]), delta_bias=inp["delta_bias"],
+                                                    nthreads=1, return_last_state=True))
+        ct = k * cfg.dim * cfg.seqlen
+        res[f"{cfg.name}-1-thread"] = {"channel_tokens_per_s": ct / dt, "seconds": round(dt, 4),
+                                       "sample": f"{k} of {cfg.batch} batch rows, median of {n}"}
+    c3 = si.SCAN_CONFIGS[3]
+    t = si.scan_inputs_device(c3, "cuda")
+    ch = np.sort(np.random.default_rng(3).choice(c3.dim, 16, replace=False))
+    idx = torch.from_numpy(ch).to("cuda")
+    host = lambda x: x.float().cpu().numpy()
+    sel = lambda x: host(x.index_select(1, idx))
+    u, dl, z, B, C = sel(t["u"]), sel(t["delta"]), sel(t["z"]), host(t["B"]), host(t["C"])
+    A, D, bias = host(t["A"])[ch], host(t["D"])[ch], host(t["delta_bias"])[ch]
+    del t
+    torch.cuda.empty_cache()
+    dt, n = timed(lambda: oracle.selective_scan(u, dl, A, B, C, D=D, z=z, delta_bias=bias,
+                                                nthreads=threads, return_last_state=True))
+    res[f"{c3.name}-16-channel-sample"] = {
+        "channel_tokens_per_s": 16 * c3.seqlen / dt, "seconds": round(dt, 4),
+        "threads": oracle.selective_scan.last_threads,
+        "sample": f"the 16 parity channels over L={c3.seqlen}, median of {n}"}
+    del u, dl, z, B, C
+    dc = si.DECODE_CONFIG
+    d = si.decode_inputs_device(dc, steps=100, device="cuda")
+    steps = [{k: host(d[k][s]) for k in ("x", "dt", "z", "B", "C")} for s in range(100)]
+    A, D, bias = host(d["A"]), host(d["D"]), host(d["dt_bias"])
+    del d
+    torch.cuda.empty_cache()
+
+    def dec():
+        st = np.zeros((dc.batch, dc.dim, dc.dstate))
+        for v in steps:
+            _, st = oracle.state_update(st, v["x"], v["dt"], A, v["B"], v["C"], D=D, z=v["z"],
+                                        dt_bias=bias, nthreads=threads)
+    dt, n = timed(dec, min_s=0.1)
+    res[f"{dc.name}-100-steps"] = {
+        "channel_tokens_per_s": 100 * dc.batch * dc.dim / dt, "seconds": round(dt, 4),
+        "ms_per_step": round(dt * 10, 3),
+        "sample": f"every channel, the first 100 steps, {threads} threads, median of {n}"}
+    return res
+
+
+def length_sweep(torch, ssm, si, lengths=(1024, 2048, 4096, 8192, 16384)):
+    """The scan of the pages' length sweep shape: one sequence of the
+    Mamba(d_model=1024, d_state=16, expand=2) block, d_inner 2048, fp32, at
+    doubling lengths; kernel medians after the >= 200 ms warm-up."""
+    out = {}
+    for L in lengths:
+        cfg = si.ScanConfig(f"sweep-L{L}", 1, 2048, L, 16, "f32", 10 + L)
+        r = bench_scan(cfg, 50, 5, torch, ssm, si, rotate=1)
+        out[str(L)] = round(r["kernel_ms"] * 1e3, 2)
+    ls = sorted(out, key=int)
+    return {"what": "batch 1, d_inner 2048, d_state 16, fp32: kernel median us per length",
+            "kernel_us": out,
+            "ratio_per_doubling": [round(out[b] / out[a], 3) for a, b in zip(ls, ls[1:])]}
+
+
 def valu_ceiling(torch, lanes=2048 * 256, blocks=4096, reps=10):
     """(token, state) steps per second of the register-only kernel that
     executes the scan's unavoidable instruction mix (libssm_micro.so), median
@@ -677,11 +758,19 @@ def main():
             log(f"[bench] {key} {secondary[key]['gbps']:.1f} GB/s, "
                 f"{secondary[key]['kernel_ms'] * 1e3:.1f} us")
 
+    if not args.no_secondary:
+        log("[bench] length sweep")
+        secondary["length-sweep-d2048-f32"] = length_sweep(torch, ssm, si)
+        log(f"[bench] length sweep {secondary['length-sweep-d2048-f32']['kernel_us']}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle)")
         cpu = cpu_baseline_channels(head, si, torch)
         log(f"[bench] cpu baseline {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
+        if not args.no_secondary:
+            log("[bench] oracle on the other workloads")
+            secondary["oracle"] = oracle_timings(si, torch)
 
     traffic = measured_traffic()
     steps_tn = head.batch * head.dim * head.seqlen * head.dstate

@@ -33,8 +33,14 @@ __global__ void copy_state_kernel(const float* h0, float* last, int64_t n) {
 // one-slot kernels (5 workgroups per CU), and keep segments long enough that
 // the second pass (bounded by the decay of the incoming state, not by the
 // segment length) and the fold stay small next to them.
+// The minimum segment length keeps pass 2 well inside each segment: its
+// rescan of a segment's head runs until the incoming state has decayed,
+// about 17 / (Delta |A|) tokens for the slowest state (17,000 at Delta 1e-3,
+// A = -1), and on segments not much longer than that the two passes cost
+// more than one (at batch 1, d_inner 2048: 8192-token segments took L 16,384
+// from 265 us at 8192 tokens to 624 us).
 constexpr int64_t kTargetGroups = 1280;   // 5 wavefronts per SIMD on 256 CUs
-constexpr int64_t kMinSegLen = 8192;
+constexpr int64_t kMinSegLen = 32768;
 constexpr int kMaxSeg = 64;
 // Grids of at most this many workgroups leave three wavefronts per SIMD on
 // 256 CUs whatever a kernel's register count; there the one-slot scan takes

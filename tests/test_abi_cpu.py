@@ -535,7 +535,7 @@ def test_noalloc_scratch_limit_is_checked_on_the_host():
     with 16 states every shape fits (at most 16 x 1280 channel-segments of
     17 floats)."""
     L = ssm.lib()
-    big = spaced_scan(1, 1536, 13 * 8192, 64)
+    big = spaced_scan(1, 1536, 13 * 32768, 64)
     assert ssm.validate_scan(big) == OK
     assert ssm.scan_workspace_size(big) > ssm.NOALLOC_SCRATCH_BYTES
     assert L.ssm_selective_scan_fwd_noalloc(ctypes.byref(big), None) == SCRATCH

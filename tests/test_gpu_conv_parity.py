@@ -105,7 +105,7 @@ def test_fused_conv_config1_layer():
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_fused_conv_segmented_long_sequence(io):
-    L = 3 * 8192 + 100
+    L = 3 * 32768 + 100
     inp = si.scan_inputs(1, 16, L, io_dtype=io, seed=88)
     check(inp, io, 4, seed=88, label=f"segmented {io}")
 

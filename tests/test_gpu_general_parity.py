@@ -72,7 +72,7 @@ def test_A_of_either_sign(N, G):
 @pytest.mark.parametrize("N,G,io", [(64, 0, "bf16"), (32, 16, "f32"), (12, 4, "bf16")])
 def test_long_sequence_segmented(N, G, io):
     """Few channels and a long sequence: cut into segments (two passes)."""
-    inp = si.scan_inputs(1, 16, 3 * 8192 + 77, dstate=N, io_dtype=io, seed=N + G, ngroups=G)
+    inp = si.scan_inputs(1, 16, 3 * 32768 + 77, dstate=N, io_dtype=io, seed=N + G, ngroups=G)
     h0 = np.random.default_rng(5).standard_normal((1, 16, N)).astype(np.float32)
     check(inp, io, f"segmented N{N} G{G} {io}", h0=h0, twin=False)
 
@@ -81,7 +81,7 @@ def test_long_sequence_segmented(N, G, io):
 def test_lane_mode_vector_loads(io, N):
     """Per-channel B/C with rows 16-byte aligned and L a multiple of the
     vector width: the lane mode's 16-byte loads (two segments for bf16)."""
-    L = 8192 * 2 + 512 if io == "bf16" else 320
+    L = 32768 * 2 + 512 if io == "bf16" else 320
     inp = si.scan_inputs(1 if io == "bf16" else 2, 32, L, dstate=N, io_dtype=io, seed=N + L,
                          ngroups=32)
     check(inp, io, f"lane vector {io} N{N} L{L}", twin=False)

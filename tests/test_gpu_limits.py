@@ -36,8 +36,8 @@ import selective_state_space_74_amd as ssm  # noqa: E402
 
 DEV = "cuda"
 # (batch, dim, L): one segment per sequence, and a shape the library cuts into
-# segments (one 16-channel group, L past 2 x 8192)
-SHAPES = [(2, 40, 2000 + 7), (1, 16, 3 * 8192 + 100)]
+# segments (one 16-channel group, L past 2 x 32768)
+SHAPES = [(2, 40, 2000 + 7), (1, 16, 3 * 32768 + 100)]
 
 
 def _io(x, io):
@@ -138,7 +138,7 @@ def test_zero_A_is_a_prefix_sum(shape, io):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("shape", [(2, 40, 2048 + 9), (1, 16, 3 * 8192 + 100)])
+@pytest.mark.parametrize("shape", [(2, 40, 2048 + 9), (1, 16, 3 * 32768 + 100)])
 def test_time_invariant_case(shape, io):
     batch, dim, L = shape
     inp = si.scan_inputs(batch, dim, L, io_dtype=io, seed=305)
@@ -151,7 +151,7 @@ def test_segmented_in_place_carry():
     """last_state == h0 (the state carried in place, as chunked prefill
     does) on a length the library cuts into segments: the state entering
     the sequence is read before any workgroup writes the final one."""
-    batch, dim, L = 1, 16, 3 * 8192 + 100
+    batch, dim, L = 1, 16, 3 * 32768 + 100
     inp = si.scan_inputs(batch, dim, L, io_dtype="f32", seed=306)
     h0 = _h0(batch, dim, 306)
     a = ssm.ScanArgs()

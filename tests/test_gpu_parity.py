@@ -55,7 +55,7 @@ def test_ragged_shapes(batch, dim, L, io):
     check_scan(inp, io, label=f"ragged b{batch} d{dim} L{L} {io}")
 
 
-@pytest.mark.parametrize("batch,dim,L,io", [(1, 37, 50, "f32"), (2, 13, 3 * 8192 + 5, "bf16")])
+@pytest.mark.parametrize("batch,dim,L,io", [(1, 37, 50, "f32"), (2, 13, 3 * 32768 + 5, "bf16")])
 def test_ragged_channels_with_initial_state(batch, dim, L, io):
     """Channel counts that leave a partial last channel group, with h0 and
     last_state (the second case is also cut into segments)."""
@@ -133,7 +133,7 @@ def test_segmented_long_sequence(io):
     """Few channels and a long sequence: the library cuts the sequence into
     segments (aggregate pass + scan pass).  Checked against the oracle on all
     channels, and against the same call run as one segment."""
-    L = 3 * 8192 + 100
+    L = 3 * 32768 + 100
     inp = si.scan_inputs(1, 16, L, io_dtype=io, seed=77)
     t = si.to_torch(inp, DEV)
     rng = np.random.default_rng(77)

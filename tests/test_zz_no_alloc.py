@@ -49,8 +49,8 @@ def _pair(batch, dim, L, io, seed):
 
 
 def test_noalloc_two_calls_second_smaller():
-    _pair(1, 48, 5 * 8192 + 77, "bf16", 401)
-    _pair(1, 16, 3 * 8192 + 5, "f32", 402)
+    _pair(1, 48, 5 * 32768 + 77, "bf16", 401)
+    _pair(1, 16, 3 * 32768 + 5, "f32", 402)
 
 
 def test_noalloc_one_segment_shape():
@@ -70,7 +70,7 @@ def test_noalloc_rejects_oversized_scratch():
     """64 states over 96 channel groups of a long sequence: the aggregates
     (5.2 MB) exceed the static scratch; the call returns SSM_ERR_SCRATCH and
     launches nothing (out keeps its contents)."""
-    dim, L, N = 1536, 13 * 8192, 64
+    dim, L, N = 1536, 13 * 32768, 64
     u = torch.zeros((1, dim, L), dtype=torch.bfloat16, device=DEV)
     Bm = torch.zeros((1, N, L), dtype=torch.bfloat16, device=DEV)
     A = -torch.ones((dim, N), device=DEV)
