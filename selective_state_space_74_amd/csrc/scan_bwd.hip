@@ -356,9 +356,10 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = (threadIdx.x >> 4) & 3;
   const int col = threadIdx.x & 15;
-  // blockIdx.x = (b * cgroups + cg) * nseg + seg
-  const int seg = static_cast<int>(blockIdx.x % p.nseg);
-  const int64_t bcg = blockIdx.x / p.nseg;
+  // logical workgroup wg = (b * cgroups + cg) * nseg + seg
+  const uint32_t wg = xcd_order(blockIdx.x, gridDim.x);
+  const int seg = static_cast<int>(wg % p.nseg);
+  const int64_t bcg = wg / p.nseg;
   const int64_t b = bcg / p.cgroups;
   const int64_t cg = bcg % p.cgroups;
   const int64_t d = cg * kCh + kRows * wave + row;
@@ -495,9 +496,10 @@ __global__ __launch_bounds__(kThreads) void bwd_aggregate_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = (threadIdx.x >> 4) & 3;
   const int col = threadIdx.x & 15;
-  // blockIdx.x = (b * cgroups + cg) * (nseg - 1) + seg - 1
-  const int seg = 1 + static_cast<int>(blockIdx.x % (p.nseg - 1));
-  const int64_t bcg = blockIdx.x / (p.nseg - 1);
+  // logical workgroup lw = (b * cgroups + cg) * (nseg - 1) + seg - 1
+  const uint32_t lw = xcd_order(blockIdx.x, gridDim.x);
+  const int seg = 1 + static_cast<int>(lw % (p.nseg - 1));
+  const int64_t bcg = lw / (p.nseg - 1);
   const int64_t b = bcg / p.cgroups;
   const int64_t cg = bcg % p.cgroups;
   const int64_t d = cg * kCh + kRows * wave + row;

@@ -487,15 +487,6 @@ struct Wave {
   }
 };
 
-// Logical workgroup of the i-th of n dispatched: XCD x = i % 8 receives
-// count(x) = n / 8 (+1 for x < n % 8) workgroups, slots i / 8 in order; they
-// become the logical range starting at the workgroups of the XCDs before it.
-constexpr uint32_t kXcds = 8;
-__device__ __forceinline__ uint32_t xcd_order(uint32_t i, uint32_t n) {
-  const uint32_t x = i % kXcds, slot = i / kXcds, q = n / kXcds, r = n % kXcds;
-  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + slot;
-}
-
 template <typename T, Mode M, bool kSoftplus, int KP, int S, int kLane, bool kDefer>
 __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   constexpr int kTile = kLane ? 1 : 2;
@@ -511,13 +502,11 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = (threadIdx.x >> 4) & 3;
   const int col = threadIdx.x & 15;
-  // Workgroup order.  The dispatcher hands workgroup i to XCD i % 8; the
-  // logical index wg gives each XCD a contiguous range of logical
-  // workgroups, so that one XCD's L2 and translation caches hold the rows
-  // of a few channel groups (and all segments of each) instead of pieces of
-  // all of them.  wg = (b * cgroups + cg) * nseg_grid + g'; pass 2 of a
-  // segmented sequence skips segment 0 (it started from the exact state):
-  // g = g' + 1.
+  // Logical workgroup (XCD-aware order, ssm_internal.h): one XCD's L2 and
+  // translation caches hold the rows of a few channel groups, all segments
+  // of each, instead of pieces of all of them.  wg = (b * cgroups + cg) *
+  // nseg_grid + g'; pass 2 of a segmented sequence skips segment 0 (it
+  // started from the exact state): g = g' + 1.
   constexpr bool fix = W::kFixp;
   const int nseg_grid = fix ? p.nseg - 1 : p.nseg;
   const uint32_t wg = xcd_order(blockIdx.x, gridDim.x);

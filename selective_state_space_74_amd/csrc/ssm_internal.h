@@ -68,6 +68,19 @@ __device__ __forceinline__ float silu_f32(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
+// Workgroup order.  The dispatcher hands the i-th workgroup of a launch to
+// XCD i % 8; xcd_order(i, n) is the logical workgroup that kernels work on,
+// chosen so that each XCD receives a contiguous logical range (XCD x gets
+// n / 8 workgroups, one more for x < n % 8, slots i / 8 in order, after the
+// ranges of the XCDs before it): neighbouring logical workgroups (channel
+// groups, segments of one group) then share one XCD's L2 and translation
+// caches.  A bijection of [0, n).
+constexpr uint32_t kXcds = 8;
+__device__ __forceinline__ uint32_t xcd_order(uint32_t i, uint32_t n) {
+  const uint32_t x = i % kXcds, slot = i / kXcds, q = n / kXcds, r = n % kXcds;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + slot;
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
