@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 7
+#define SSM_ABI_VERSION 8
 
 /* Tokens between two state checkpoints (see ssm_scan_args.checkpoints). */
 #define SSM_CHECKPOINT_TOKENS 16
@@ -73,7 +73,7 @@ extern "C" {
 #define SSM_MAX_DSTATE 64
 
 /* Size of the static device scratch of ssm_selective_scan_fwd_noalloc. */
-#define SSM_NOALLOC_SCRATCH_BYTES (2u << 20)
+#define SSM_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 typedef enum ssm_status {
   SSM_OK = 0,
@@ -92,7 +92,7 @@ typedef enum ssm_status {
                               ssm_scan_args)                                   */
   SSM_ERR_HIP = 8,         /* the HIP runtime rejected the launch              */
   SSM_ERR_SCRATCH = 9      /* ssm_selective_scan_fwd_noalloc: the segment
-                              aggregates exceed SSM_NOALLOC_SCRATCH_BYTES      */
+                              scratch exceeds SSM_NOALLOC_SCRATCH_BYTES        */
 } ssm_status;
 
 typedef enum ssm_dtype { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype;
@@ -357,7 +357,11 @@ size_t ssm_update_args_size(void);
 size_t ssm_ssd_args_size(void);
 
 /* Workspace bytes the scan can use for this argument block (0 when it would
- * run single-segment anyway).  Reads only sizes; pure host code. */
+ * run single-segment anyway): for G segments, with BD = batch * dim and
+ * each part rounded up to 256 bytes, the segment aggregates BD * G *
+ * (dstate + 1) floats, the records of the 10 windows of each segment's
+ * head BD * G * 10 * (dstate + 1) floats, and BD * G * 21 ints of work
+ * lists.  Reads only sizes; pure host code. */
 size_t ssm_scan_workspace_size(const ssm_scan_args* args);
 
 /* Workspace bytes the backward can use for this argument block:
@@ -386,12 +390,13 @@ int ssm_selective_scan_fwd(const ssm_scan_args* args, void* stream);
  * the same computation and kernels as ssm_selective_scan_fwd, and it calls no
  * allocating routine.  args->workspace and args->workspace_bytes are ignored;
  * long sequences with few channels are cut into segments with their
- * aggregates kept in a static device buffer of SSM_NOALLOC_SCRATCH_BYTES that
- * the library holds on every device it runs on until the process ends (its
- * address is looked up on the first call on each device).  That is enough
- * for every argument block with dstate <= 16 (at most 1.4 MB are needed);
- * with more states, blocks whose aggregates, ssm_scan_workspace_size(args)
- * bytes, exceed it return SSM_ERR_SCRATCH and launch nothing.  Every call on
+ * aggregates, window records and work lists kept in a static device buffer
+ * of SSM_NOALLOC_SCRATCH_BYTES that the library holds on every device it
+ * runs on until the process ends (its address is looked up on the first
+ * call on each device).  That is enough for every argument block with
+ * dstate <= 16 (at most 17 MB are needed); with more states, blocks whose
+ * segment scratch, ssm_scan_workspace_size(args) bytes, exceeds it return
+ * SSM_ERR_SCRATCH and launch nothing.  Every call on
  * a device shares that device's buffer: calls on one device that may
  * overlap in time (different streams, no ordering between them) race on it
  * and must be serialised by the caller.  The buffer holds no state between

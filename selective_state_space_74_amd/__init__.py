@@ -32,14 +32,14 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libssm.so")
 
-SSM_ABI_VERSION = 7
+SSM_ABI_VERSION = 8
 CHECKPOINT_TOKENS = 16
 MAX_CONV = 8
 SSM_F32, SSM_BF16 = 0, 1
 STATUS = {0: "SSM_OK", 1: "SSM_ERR_NULL", 2: "SSM_ERR_SHAPE", 3: "SSM_ERR_STRIDE",
           4: "SSM_ERR_DTYPE", 5: "SSM_ERR_ALIGN", 6: "SSM_ERR_ALIAS", 7: "SSM_ERR_UNSUPPORTED",
           8: "SSM_ERR_HIP", 9: "SSM_ERR_SCRATCH"}
-NOALLOC_SCRATCH_BYTES = 2 << 20
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64

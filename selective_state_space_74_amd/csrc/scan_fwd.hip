@@ -69,25 +69,200 @@ int slots(int64_t dstate) { return dstate <= 16 ? 1 : dstate <= 32 ? 2 : 4; }
 
 }  // namespace
 
-bool scan_windows_fit(const ssm_scan_args& a) {
-  // Per-wavefront byte windows (and the lane offsets inside them) are 32-bit,
-  // with a margin: lanes of padding states address from a window's end.
+namespace {
+
+// Per-wavefront byte windows (and the lane offsets inside them) are 32-bit,
+// with a margin: lanes of padding states address from a window's end.  A
+// wavefront's rows lie within `rows + 1` consecutive channels; with per-lane
+// B/C they reach `gspan + 1` groups.
+bool spans_fit(const ssm_scan_args& a, int64_t rows, int64_t gspan) {
   const int64_t esz = a.io_dtype == SSM_BF16 ? 2 : 4;
-  const int64_t rows = std::min<int64_t>(kRows, a.dim) - 1;
   const int64_t lim = (int64_t{1} << 32) - 256;
   auto fits = [&](int64_t span) { return span * esz < lim; };
-  // a wavefront's four rows reach at most four groups in lane mode
-  const int64_t gspan = lane_bc(a) ? std::min<int64_t>(3, ngroups_of(a) - 1) : 0;
   bool ok = fits(rows * a.u_dim_stride + a.seqlen) && fits(rows * a.delta_dim_stride + a.seqlen) &&
             fits(rows * a.out_dim_stride + a.seqlen) &&
             fits(gspan * a.B_group_stride + (a.dstate - 1) * a.B_state_stride + a.seqlen) &&
             fits(gspan * a.C_group_stride + (a.dstate - 1) * a.C_state_stride + a.seqlen);
   if (a.z) ok = ok && fits(rows * a.z_dim_stride + a.seqlen);
   if (a.conv_weight && a.conv_out) ok = ok && fits(rows * a.conv_out_dim_stride + a.seqlen);
-  // checkpoints: four rows of ceil(L / 16) * dstate floats
+  // checkpoints: rows + 1 rows of ceil(L / 16) * dstate floats
   if (a.checkpoints)
     ok = ok && (rows + 1) * ((a.seqlen + kT - 1) / kT) * a.dstate * 4 < lim;
   return ok;
+}
+
+// Pass 2 of the segmented scan gathers the channels of a window from a chunk
+// of `cw` consecutive channels of one B/C scope (the group with the shared
+// tile, the whole row with per-lane B/C): the widest chunk whose windows fit,
+// at least min(4, scope), which scan_windows_fit guarantees.
+int64_t chunk_width(const ssm_scan_args& a, int64_t scope) {
+  const int64_t cpg = a.dim / ngroups_of(a);
+  auto fit = [&](int64_t cw) {
+    // cw consecutive channels reach at most ceil((cw - 1) / cpg) + 1 groups
+    const int64_t gs = lane_bc(a) ? std::min<int64_t>((cw - 1 + cpg - 1) / cpg, ngroups_of(a) - 1) : 0;
+    return spans_fit(a, cw - 1, gs);
+  };
+  int64_t lo = std::min<int64_t>(kRows, scope), hi = scope;
+  if (fit(hi)) return hi;
+  while (hi - lo > 1) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (fit(mid)) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Workspace of a segmented scan (offsets in bytes, 256-byte aligned):
+// segment aggregates [B*D][G][N+1] and window records [G][kWin][B*D][N+1]
+// (fp32), then per (channel, segment) the number of windows to rescan, and
+// per (batch row, segment, window) the channel counts and lists.
+struct SegLayout {
+  size_t agg, rec, jst, cnt, lst, total;
+};
+
+SegLayout seg_layout(const ssm_scan_args& a, int nseg) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t bd = static_cast<size_t>(a.batch * a.dim), ns = static_cast<size_t>(nseg);
+  const size_t aggs = static_cast<size_t>(a.dstate + 1);
+  SegLayout l;
+  l.agg = 0;
+  l.rec = l.agg + al(bd * ns * aggs * 4);
+  l.jst = l.rec + al(ns * fwd::kWin * bd * aggs * 4);
+  l.cnt = l.jst + al(ns * bd * 4);
+  l.lst = l.cnt + al(ns * fwd::kWin * bd * 4);
+  l.total = l.lst + al(ns * fwd::kWin * bd * 4);
+  return l;
+}
+
+// Between the passes of a segmented scan, one 16-lane row per channel and
+// segment g >= 1 (lane c holds states c, c + 16, ...):
+//  - h_in, the exact state entering segment g, folded from the aggregates
+//    of segments 0..g-1 (segment 0's end state already includes h0), goes
+//    to window slot 0 (with S = 0); the last segment also folds its own
+//    aggregate into last_state;
+//  - each later window start's record (pass 1's state there) becomes the
+//    exact state, the record plus the free response exp(A S) h_in;
+//  - jst, the number of windows to rescan: up to the first window start
+//    where the free response is at most 2^-24 max_n |h[n]| in every state
+//    (a non-finite one never passes), else all of the segment's windows.
+struct PlanParams {
+  const float* agg;
+  float* rec;
+  int* jst;
+  float* last_state;
+  const float* A;
+  int64_t Asd, Asn, batch, dim;
+  int N, nseg, L, seg_len;
+};
+
+__global__ __launch_bounds__(256) void seg_plan_kernel(PlanParams q) {
+  const int64_t bd = q.batch * q.dim;
+  const int64_t item = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) / kN;
+  const int col = threadIdx.x % kN;
+  if (item >= bd * (q.nseg - 1)) return;  // whole rows
+  const int64_t c = item % bd;
+  const int g = static_cast<int>(item / bd) + 1;
+  const int64_t d = c % q.dim;
+  const int N = q.N, aggs = N + 1;
+  const int s0 = g * q.seg_len;
+  const int nw = fwd::seg_windows((min(q.L, s0 + q.seg_len) - s0) / kT);
+  const float* ag = q.agg + c * q.nseg * aggs;
+  float* slot0 = q.rec + (static_cast<size_t>(g) * fwd::kWin * bd + c) * aggs;
+  const size_t sstride = static_cast<size_t>(bd) * aggs;  // floats from one window slot to the next
+  float fr[fwd::kWin], hm[fwd::kWin];
+#pragma unroll
+  for (int j = 0; j < fwd::kWin; ++j) fr[j] = hm[j] = 0.0f;
+  for (int n = col; n < N; n += kN) {
+    const float a2 = q.A[d * q.Asd + n * q.Asn] * kLog2e;
+    float h = ag[n];
+    for (int i = 1; i < g; ++i)
+      h = fmaf(__builtin_amdgcn_exp2f(a2 * ag[i * aggs + N]), h, ag[i * aggs + n]);
+    if (q.last_state && g == q.nseg - 1)
+      q.last_state[c * N + n] = fmaf(__builtin_amdgcn_exp2f(a2 * ag[g * aggs + N]), h, ag[g * aggs + n]);
+    slot0[n] = h;
+#pragma unroll
+    for (int j = 1; j < fwd::kWin; ++j) {
+      if (j < nw) {
+        float* r = slot0 + j * sstride;
+        const float e = __builtin_amdgcn_exp2f(a2 * r[N]);
+        const float hx = fmaf(e, h, r[n]);
+        r[n] = hx;
+        const float f = e * fabsf(h);
+        fr[j] = fmaxf(fr[j], f == f ? f : __builtin_huge_valf());
+        hm[j] = fmaxf(hm[j], fabsf(hx));
+      }
+    }
+  }
+  if (col == 0) slot0[N] = 0.0f;
+  int js = nw;
+#pragma unroll
+  for (int j = fwd::kWin - 1; j >= 1; --j) {
+    float f = fr[j], m = hm[j];
+#pragma unroll
+    for (int o = 1; o < kN; o <<= 1) {
+      f = fmaxf(f, __shfl_xor(f, o, kN));
+      m = fmaxf(m, __shfl_xor(m, o, kN));
+    }
+    if (j < nw && f <= 0x1p-24f * m) js = j;
+  }
+  if (col == 0) q.jst[static_cast<size_t>(g) * bd + c] = js;
+}
+
+// Per (batch row, segment g >= 1, chunk): for each window j, the chunk's
+// channels with more than j windows to rescan, ascending, and their count
+// (a stable compaction: each thread takes a run of consecutive channels).
+struct ListParams {
+  const int* jst;
+  int* counts;
+  int* lists;
+  int64_t batch, dim, scope, cw, nchunk;
+  int nseg;
+};
+
+__global__ __launch_bounds__(256) void seg_list_kernel(ListParams q) {
+  __shared__ int wsum[4];
+  const int64_t bid = blockIdx.x;
+  const int64_t chunk = bid % q.nchunk;
+  const int g = static_cast<int>((bid / q.nchunk) % (q.nseg - 1)) + 1;
+  const int64_t b = bid / (q.nchunk * (q.nseg - 1));
+  const int64_t cps = (q.scope + q.cw - 1) / q.cw;
+  const int64_t c0 = (chunk / cps) * q.scope + (chunk % cps) * q.cw;
+  const int64_t c1 = std::min(c0 + q.cw, (chunk / cps + 1) * q.scope);
+  const int64_t per = (c1 - c0 + 255) / 256;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int64_t lo = std::min(c1, c0 + t * per), hi = std::min(c1, lo + per);
+  const int* js = q.jst + static_cast<size_t>(g) * q.batch * q.dim + b * q.dim;
+  for (int j = 0; j < fwd::kWin; ++j) {
+    int cnt = 0;
+    for (int64_t c = lo; c < hi; ++c) cnt += js[c] > j;
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int pos = incl - cnt, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (w < wv) pos += wsum[w];
+      total += wsum[w];
+    }
+    const int64_t key = ((b * q.nseg + g) * fwd::kWin + j) * q.dim + c0;
+    for (int64_t c = lo; c < hi; ++c)
+      if (js[c] > j) q.lists[key + pos++] = static_cast<int>(c);
+    if (t == 0) q.counts[key] = total;
+    __syncthreads();  // wsum is rewritten for the next window
+  }
+}
+
+}  // namespace
+
+bool scan_windows_fit(const ssm_scan_args& a) {
+  // a wavefront's four rows reach at most four groups in lane mode
+  const int64_t gspan = lane_bc(a) ? std::min<int64_t>(3, ngroups_of(a) - 1) : 0;
+  return spans_fit(a, std::min<int64_t>(kRows, a.dim) - 1, gspan);
 }
 
 size_t scan_workspace_bytes(const ssm_scan_args& a) {
@@ -95,7 +270,7 @@ size_t scan_workspace_bytes(const ssm_scan_args& a) {
   const int64_t groups = a.batch * ((a.dim + kCh - 1) / kCh);
   const int nseg = choose_segments(groups, a.seqlen);
   if (nseg <= 1) return 0;
-  return static_cast<size_t>(a.batch * a.dim * nseg * (a.dstate + 1)) * sizeof(float);
+  return seg_layout(a, nseg).total;
 }
 
 namespace {
@@ -186,7 +361,12 @@ hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {
   const int64_t seg = (a.seqlen + nseg - 1) / nseg;
   p.seg_len = static_cast<int>((seg + kGT - 1) / kGT * kGT);
   p.nseg = static_cast<int>((a.seqlen + p.seg_len - 1) / p.seg_len);
-  p.agg = p.nseg > 1 ? static_cast<float*>(a.workspace) : nullptr;
+  p.agg = nullptr;
+  p.rec = nullptr;
+  p.counts = nullptr;
+  p.lists = nullptr;
+  p.scope = p.cw = p.nchunk = 1;
+  p.maxi = 1;
   p.ckpt = a.checkpoints;
   p.K = a.conv_weight ? a.d_conv : 0;
   p.conv_w = a.conv_weight; p.conv_b = a.conv_bias; p.conv_in = a.conv_state_in;
@@ -215,11 +395,42 @@ hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {
     }
   };
   if (p.nseg > 1) {
-    // pass 1: every segment from zero (segment 0 from h0), with aggregates;
-    // pass 2: segments 1.. from their folded incoming state, until it has
-    // decayed.  Stream order puts pass 1's aggregates before pass 2.
+    // pass 1: every segment from zero (segment 0 from h0), with aggregates
+    // and window records; the plan: incoming and window start states, the
+    // windows each channel still needs, and per window the channels to
+    // rescan, gathered by chunk; pass 2: those windows from their exact
+    // start states, until the incoming state has decayed.  Stream order
+    // puts each launch's results before the next.
+    const SegLayout lay = seg_layout(a, p.nseg);
+    char* ws = static_cast<char*>(a.workspace);
+    p.agg = reinterpret_cast<float*>(ws + lay.agg);
+    p.rec = reinterpret_cast<float*>(ws + lay.rec);
+    int* jst = reinterpret_cast<int*>(ws + lay.jst);
+    int* counts = reinterpret_cast<int*>(ws + lay.cnt);
+    int* lists = reinterpret_cast<int*>(ws + lay.lst);
+    p.counts = counts;
+    p.lists = lists;
+    p.scope = lane ? a.dim : p.cpg;
+    p.cw = chunk_width(a, p.scope);
+    p.nchunk = (a.dim / p.scope) * ((p.scope + p.cw - 1) / p.cw);
+    p.maxi = static_cast<int>((p.cw + kCh - 1) / kCh);
     run(1, dim3((unsigned)(groups * p.nseg)));
-    run(2, dim3((unsigned)(groups * (p.nseg - 1))));
+
+    PlanParams pq;
+    pq.agg = p.agg; pq.rec = p.rec; pq.jst = jst; pq.last_state = a.last_state;
+    pq.A = a.A; pq.Asd = a.A_dim_stride; pq.Asn = a.A_state_stride;
+    pq.batch = a.batch; pq.dim = a.dim;
+    pq.N = p.N; pq.nseg = p.nseg; pq.L = p.L; pq.seg_len = p.seg_len;
+    const int64_t rows = a.batch * a.dim * (p.nseg - 1);
+    seg_plan_kernel<<<dim3((unsigned)((rows * kN + 255) / 256)), dim3(256), 0, stream>>>(pq);
+
+    ListParams lq;
+    lq.jst = jst; lq.counts = counts; lq.lists = lists;
+    lq.batch = a.batch; lq.dim = a.dim; lq.scope = p.scope; lq.cw = p.cw; lq.nchunk = p.nchunk;
+    lq.nseg = p.nseg;
+    seg_list_kernel<<<dim3((unsigned)(a.batch * (p.nseg - 1) * p.nchunk)), dim3(256), 0, stream>>>(lq);
+
+    run(2, dim3((unsigned)(fwd::kWin * a.batch * p.nchunk * (p.nseg - 1) * p.maxi)));
   } else {
     run(0, dim3((unsigned)groups));
   }

@@ -45,23 +45,33 @@
 // Long sequences with few channels.  The recurrence is linear in the state
 // (Mamba paper notes, sections 5.3/5.4: a long input can be cut into chunks
 // with the state handed from one chunk to the next), so the sequence may be
-// cut into G segments processed by different workgroups, in two launches:
+// cut into G segments processed by different workgroups:
 //   pass 1  every segment runs the full scan (outputs, checkpoints) from a
 //           zero state (segment 0 from h0) and records its end state b_g and
-//           the sum of its step sizes S_g;
-//   pass 2  segment g >= 1 folds the exact state entering it,
+//           the sum of its step sizes S_g, and, at the start of each window
+//           of its head (below), its state and the step sizes summed so far;
+//   plan    (scan_fwd.hip) the exact state entering segment g >= 1,
 //           h_in = fold_{i<g} (exp(A S_i) h + b_i), with the associative
 //           combine (a1,b1).(a2,b2) = (a1 a2, a2 b1 + b2) kept in factored
-//           form, and scans again from h_in, rewriting outputs and
-//           checkpoints, only while that state's contribution still counts.
+//           form; the exact state at each window start; and, per channel,
+//           the windows still to rescan;
+//   pass 2  one workgroup per 16 channels (of one B/C group) and window
+//           rescans the window from its exact start state, rewriting
+//           outputs and checkpoints, only while the incoming state's
+//           contribution still counts.
 // Pass 1's state inside segment g differs from the exact one by
 // d_t = exp(A (S_0 + ... + S_t)) h_in (the free response of h_in), so once
 // |d_t| falls below fp32 resolution of the state (2^-24 max_n |h_t[n]|, over
 // each channel's states) pass 1's values are the sequential result up to
-// rounding, and pass 2 stops: with A < 0 the contribution decays, and a
-// workgroup stops when all 16 of its channels are there (checked every 64
-// tokens).  With A >= 0 it never decays and pass 2 runs the whole segment.
-// The last segment's workgroups write last_state = exp(A S_g) h_in + b_g.
+// rounding.  With A < 0 the contribution decays: a channel's windows end at
+// the first window start where it holds, and a workgroup stops inside its
+// window once it holds for all 16 of its channels (checked every 64 tokens).
+// With A >= 0 it never decays and the whole segment is rescanned.  Windows
+// start 0, 528, 1040, 2064, ... tokens into a segment (win_blk), short at the
+// head where most channels drop out and longer behind it, so that both the
+// rescanned tokens and the longest window stay small; channels that need
+// the same window are gathered across the B/C group, so one slow channel
+// does not hold fifteen converged ones.
 #pragma once
 
 #include <algorithm>
@@ -85,6 +95,23 @@ constexpr int kPitch = 20;          // LDS pitch (floats) of one state's readout
 constexpr int kCPitch = kN + 4;     // LDS pitch (floats) of one token's C (token-major tile)
 constexpr int kPartRow = kN * kPitch + 16;  // floats per channel of readout partials
 
+// Segmented scan: the windows of a segment's head that pass 2 rescans.
+// Window j starts win_blk(j) blocks into the segment, at the top of a
+// steady-state round (1 mod 4 blocks), where pass 1 records its state; it
+// ends where the next window present starts, the last one present at the
+// segment's end.  Window j >= 1 is present when pass 1 runs that round:
+// win_blk(j) + 4 <= the segment's full blocks.
+constexpr int kWin = 10;
+__host__ __device__ constexpr int win_blk(int j) {
+  return j <= 0 ? 0 : j == 1 ? 33 : j == 2 ? 65 : j == 3 ? 129 : j == 4 ? 257
+       : j == 5 ? 385 : j == 6 ? 513 : j == 7 ? 769 : j == 8 ? 1025 : 1537;
+}
+__host__ __device__ constexpr int seg_windows(int nfull) {
+  int n = 1;
+  while (n < kWin && win_blk(n) + 4 <= nfull) ++n;
+  return n;
+}
+
 // kScan: one segment per sequence.  kSeg, kFix: passes 1 and 2 of a
 // segmented sequence.
 enum class Mode { kScan, kSeg, kFix };
@@ -101,7 +128,11 @@ struct ScanParams {
   const float* h0;
   float* last_state;
   void* out;
-  float* agg;      // [batch * dim][nseg][N + 1] segment aggregates (nseg > 1)
+  // segmented scan (nseg > 1)
+  float* agg;      // [batch * dim][nseg][N + 1] segment end states and step-size sums
+  float* rec;      // [nseg][kWin][batch * dim][N + 1] window start states and step sums
+  const int* counts;  // [batch][nseg][kWin][dim] channels to rescan, at each chunk's first
+  const int* lists;   // the same shape: those channels, ascending, from the chunk's first
   float* ckpt;     // [batch][dim][nbk][N] states entering each block, or NULL
   const float* conv_w;      // [dim][K] conv weights (the conv path only)
   const float* conv_b;      // [dim] or NULL
@@ -120,6 +151,10 @@ struct ScanParams {
   int nseg;        // segments per sequence
   int nbk;         // blocks per sequence, ceil(L / kT)
   int64_t cgroups; // ceil(dim / kCh)
+  int64_t scope;   // pass 2: channels per B/C scope, the group (shared tile) or dim
+  int64_t cw;      // pass 2: channels per chunk (a scope is cut into chunks of cw)
+  int64_t nchunk;  // pass 2: chunks per batch row
+  int maxi;        // pass 2: workgroups per chunk and window, ceil(cw / 16)
 };
 
 // Owner role raw inputs of one block: token t0 + col of the lane's channel
@@ -504,30 +539,74 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   const int col = threadIdx.x & 15;
   // Logical workgroup (XCD-aware order, ssm_internal.h): one XCD's L2 and
   // translation caches hold the rows of a few channel groups, all segments
-  // of each, instead of pieces of all of them.  wg = (b * cgroups + cg) *
-  // nseg_grid + g'; pass 2 of a segmented sequence skips segment 0 (it
-  // started from the exact state): g = g' + 1.
+  // of each (pass 2: the items of one window), instead of pieces of all.
   constexpr bool fix = W::kFixp;
-  const int nseg_grid = fix ? p.nseg - 1 : p.nseg;
-  const uint32_t wg = xcd_order(blockIdx.x, gridDim.x);
-  const int g = static_cast<int>(wg % nseg_grid) + (fix ? 1 : 0);
-  const int64_t bc = wg / nseg_grid;
-  const int64_t b = bc / p.cgroups;
-  const int64_t d = (bc % p.cgroups) * kCh + kRows * wave + row;
-  const bool vrow = d < p.dim;
-  // rows past dim repeat the last channel exactly (same inputs, same state)
-  const int64_t dc = vrow ? d : p.dim - 1;
-  // this wavefront's first and last (clamped) rows
-  const int64_t dw0 = std::min<int64_t>((bc % p.cgroups) * kCh + kRows * wave, p.dim - 1);
-  const int64_t dw3 = std::min<int64_t>(dw0 + kRows - 1, p.dim - 1);
   const int N = p.N;
-  const int aggs = N + 1;  // floats per (channel, segment) aggregate: b[N], S
+  const int aggs = N + 1;  // floats per aggregate and per window record: h[N], S
+  const int64_t BD = p.batch * p.dim;
+  int g, jw = 0, t_beg, t_end;
+  int64_t b, d, dc, dw0, dw3, grp_tile;
+  bool vrow;
+  if constexpr (!fix) {
+    // wg = (b * cgroups + cg) * nseg + g: 16 consecutive channels, one segment
+    const uint32_t wg = xcd_order(blockIdx.x, gridDim.x);
+    g = static_cast<int>(wg % p.nseg);
+    const int64_t bc = wg / p.nseg;
+    b = bc / p.cgroups;
+    const int64_t cg0 = (bc % p.cgroups) * kCh;
+    d = cg0 + kRows * wave + row;
+    vrow = d < p.dim;
+    // rows past dim repeat the last channel exactly (same inputs, same state)
+    dc = vrow ? d : p.dim - 1;
+    // this wavefront's first and last (clamped) rows
+    dw0 = std::min<int64_t>(cg0 + kRows * wave, p.dim - 1);
+    dw3 = std::min<int64_t>(dw0 + kRows - 1, p.dim - 1);
+    grp_tile = cg0 / p.cpg;
+    t_beg = g * p.seg_len;
+    t_end = std::min(p.L, t_beg + p.seg_len);
+  } else {
+    // Pass 2: wg = (((j * batch + b) * nchunk + chunk) * (nseg - 1) + g - 1)
+    // * maxi + i, the i-th 16 channels of the list of window j of segment g
+    // in one chunk of a batch row (windows outermost: the later ones, with
+    // few channels left, come last).  Lists are ascending, so a wavefront's
+    // rows lie between its first and its fourth; entries past the list
+    // repeat its last channel (identical values, identical stores).
+    uint32_t wg = xcd_order(blockIdx.x, gridDim.x);
+    const int i = static_cast<int>(wg % static_cast<uint32_t>(p.maxi));
+    wg /= static_cast<uint32_t>(p.maxi);
+    g = static_cast<int>(wg % static_cast<uint32_t>(p.nseg - 1)) + 1;
+    wg /= static_cast<uint32_t>(p.nseg - 1);
+    const int64_t chunk = wg % p.nchunk;
+    const int64_t wr = wg / p.nchunk;
+    b = wr % p.batch;
+    jw = static_cast<int>(wr / p.batch);
+    const int s0 = g * p.seg_len;
+    const int send = std::min(p.L, s0 + p.seg_len);
+    const int nwin = seg_windows((send - s0) / kT);
+    if (jw >= nwin) return;
+    const int64_t cps = (p.scope + p.cw - 1) / p.cw;  // chunks per scope
+    const int64_t c0 = (chunk / cps) * p.scope + (chunk % cps) * p.cw;
+    const int64_t key = ((b * p.nseg + g) * kWin + jw) * p.dim + c0;
+    const int cnt = __builtin_amdgcn_readfirstlane(p.counts[key]);
+    if (i * kCh >= cnt) return;
+    const int* lst = p.lists + key;
+    const int r0 = i * kCh + kRows * wave;
+    dc = lst[std::min(r0 + row, cnt - 1)];
+    dw0 = __builtin_amdgcn_readfirstlane(lst[std::min(r0, cnt - 1)]);
+    dw3 = __builtin_amdgcn_readfirstlane(lst[std::min(r0 + kRows - 1, cnt - 1)]);
+    d = dc;
+    vrow = true;
+    // shared tile: a chunk never straddles a group
+    grp_tile = dw0 / p.cpg;
+    t_beg = s0 + kT * win_blk(jw);
+    t_end = jw + 1 < nwin ? s0 + kT * win_blk(jw + 1) : send;
+  }
 
   constexpr int E = Elem<T>::kSize;
   W w{p};
   w.wave = wave; w.row = row; w.col = col;
-  w.t_beg = g * p.seg_len;
-  w.t_end = std::min(p.L, w.t_beg + p.seg_len);
+  w.t_beg = t_beg;
+  w.t_end = t_end;
   w.nblk = (w.t_end - w.t_beg + kT - 1) / kT;
   w.ngrp = (w.nblk + kGB - 1) / kGB;
 
@@ -560,11 +639,10 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   if constexpr (!kLane) {
     // B/C: the workgroup's group; this lane stages states 4 wave + row + 16q
     // of tokens col, col + 16 of each staging group
-    const int64_t grp = ((bc % p.cgroups) * kCh) / p.cpg;
     const int st = kRows * wave + row;
-    w.wB = Window{static_cast<const char*>(p.B) + (b * p.Bsb + grp * p.Bsg) * E,
+    w.wB = Window{static_cast<const char*>(p.B) + (b * p.Bsb + grp_tile * p.Bsg) * E,
                   static_cast<uint32_t>(((N - 1) * p.Bsn + p.L) * E)};
-    w.wC = Window{static_cast<const char*>(p.C) + (b * p.Csb + grp * p.Csg) * E,
+    w.wC = Window{static_cast<const char*>(p.C) + (b * p.Csb + grp_tile * p.Csg) * E,
                   static_cast<uint32_t>(((N - 1) * p.Csn + p.L) * E)};
 #pragma unroll
     for (int q = 0; q < S; ++q) {
@@ -624,33 +702,28 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   float uprev = 0.0f;
 
   // Initial state: h0 (or zero) for the one segment of kScan and for segment
-  // 0 of pass 1; zero for the other segments of pass 1; in pass 2, the exact
-  // state entering segment g, folded from the aggregates of segments 0..g-1
-  // (segment 0's end state already includes h0).  Pass 2's last segment also
-  // folds its own aggregate into last_state right away.
+  // 0 of pass 1; zero for the other segments of pass 1; in pass 2, the
+  // window's exact start state (written by the plan), and hin, the size of
+  // the incoming state's free response there, |h_in| exp(A S) with S the
+  // step sizes before the window (slot 0 holds h_in itself, with S = 0).
   float h[S], hin[S];
   const size_t arow = static_cast<size_t>(b * p.dim + dc) * p.nseg;  // aggregates of this channel
 #pragma unroll
   for (int q = 0; q < S; ++q) {
     const int n = col + kN * q;
     h[q] = 0.0f;
+    hin[q] = 0.0f;
     if (n < N) {
       if constexpr (!fix) {
         if (g == 0 && p.h0) h[q] = p.h0[(b * p.dim + dc) * N + n];
       } else {
-        const float* ag = p.agg + arow * aggs;
-        h[q] = ag[n];
-        for (int i = 1; i < g; ++i) {
-          const float decay = __builtin_amdgcn_exp2f(w.a2[q] * ag[i * aggs + N]);
-          h[q] = fmaf(decay, h[q], ag[i * aggs + n]);
-        }
-        if (vrow && p.last_state && g == p.nseg - 1) {
-          const float decay = __builtin_amdgcn_exp2f(w.a2[q] * ag[g * aggs + N]);
-          p.last_state[(b * p.dim + d) * N + n] = fmaf(decay, h[q], ag[g * aggs + n]);
-        }
+        const size_t c = static_cast<size_t>(b * p.dim + dc);
+        const float* rs = p.rec + ((static_cast<size_t>(g) * kWin + jw) * BD + c) * aggs;
+        const float* r0 = p.rec + (static_cast<size_t>(g) * kWin * BD + c) * aggs;
+        h[q] = rs[n];
+        hin[q] = fabsf(r0[n]) * __builtin_amdgcn_exp2f(w.a2[q] * rs[N]);
       }
     }
-    hin[q] = fabsf(h[q]);
   }
 
   double ssum = 0.0;
@@ -680,11 +753,33 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   w.template iter<true, false>(0, h, ssum, buf3, buf0, buf2, grp, uprev, xprev, cl);
   int k = 1;
   bool done = false;
+  // pass 1: the next window start to record (segment 0 needs none)
+  int rj = 1, rblk = g > 0 ? win_blk(1) : 0x7fffffff;
   for (; k + 4 <= nfull; k += 4) {
     if constexpr (fix) {
       if (w.converged(h, hin, ssum)) {
         done = true;
         break;
+      }
+    }
+    if constexpr (M == Mode::kSeg) {
+      if (k == rblk) {
+        // window rj starts at block k: the state entering it and the step
+        // sizes before it (this channel's 16 owner sums added up)
+        double sk = ssum;
+#pragma unroll
+        for (int m = 1; m < kN; m <<= 1) sk += __shfl_xor(sk, m, kN);
+        if (vrow) {
+          float* rs = p.rec + ((static_cast<size_t>(g) * kWin + rj) * BD + b * p.dim + d) * aggs;
+#pragma unroll
+          for (int q = 0; q < S; ++q) {
+            const int n = col + kN * q;
+            if (n < N) rs[n] = h[q];
+          }
+          if (col == 0) rs[N] = static_cast<float>(sk);
+        }
+        ++rj;
+        rblk = rj < kWin ? win_blk(rj) : 0x7fffffff;
       }
     }
     // k % 4 == 1 here, and 4 is a multiple of kGB

@@ -36,14 +36,14 @@ def test_exports_every_declared_function():
 
 def test_abi_version_and_struct_layout():
     L = ssm.lib()
-    assert L.ssm_abi_version() == ssm.SSM_ABI_VERSION == 7
+    assert L.ssm_abi_version() == ssm.SSM_ABI_VERSION == 8
     assert L.ssm_scan_args_size() == ctypes.sizeof(ssm.ScanArgs)
     assert L.ssm_scan_bwd_args_size() == ctypes.sizeof(ssm.ScanBwdArgs)
     assert L.ssm_update_args_size() == ctypes.sizeof(ssm.UpdateArgs)
     header = open(HEADER).read()
-    assert "#define SSM_ABI_VERSION 7" in header
-    assert f"#define SSM_NOALLOC_SCRATCH_BYTES (2u << 20)" in header
-    assert ssm.NOALLOC_SCRATCH_BYTES == 2 << 20
+    assert "#define SSM_ABI_VERSION 8" in header
+    assert f"#define SSM_NOALLOC_SCRATCH_BYTES (32u << 20)" in header
+    assert ssm.NOALLOC_SCRATCH_BYTES == 32 << 20
     assert f"#define SSM_MAX_CONV {ssm.MAX_CONV}" in header
     assert f"#define SSM_CHECKPOINT_TOKENS {ssm.CHECKPOINT_TOKENS}" in header
 
@@ -466,13 +466,24 @@ def test_scan_lane_mode_window_counts_group_stride():
     assert ssm.validate_scan(a) == ALIAS
 
 
+def seg_workspace(batch, dim, nseg, N):
+    """The segmented scan's scratch, each part rounded up to 256 bytes: one
+    aggregate (end state and step-size sum, N + 1 floats) per channel and
+    segment, the records of the 10 head windows of each segment (N + 1
+    floats each), and per channel and segment the window count plus, per
+    window, a list entry and a count slot (ints)."""
+    al = lambda x: (x + 255) // 256 * 256
+    bd = batch * dim
+    return (al(bd * nseg * (N + 1) * 4) + al(nseg * 10 * bd * (N + 1) * 4) + al(nseg * bd * 4)
+            + 2 * al(nseg * 10 * bd * 4))
+
+
 def test_segmented_workspace_size():
-    """The segmented scan keeps one aggregate (end state and step-size sum,
-    dstate + 1 floats) per channel and segment; the 1M-token config (96
-    channel groups) is cut into 13 segments.  Layer shapes with enough
-    channel groups run as one segment and need none."""
+    """The 1M-token config (96 channel groups) is cut into 13 segments.
+    Layer shapes with enough channel groups run as one segment and need no
+    workspace."""
     a = grouped_scan(1, N=16, dim=1536, L=1 << 20, batch=1)
-    assert ssm.scan_workspace_size(a) == 1536 * 13 * 17 * 4
+    assert ssm.scan_workspace_size(a) == seg_workspace(1, 1536, 13, 16)
     assert ssm.scan_workspace_size(grouped_scan(1, N=16, dim=1536, L=2048, batch=8)) == 0
 
 
@@ -480,7 +491,7 @@ def test_workspace_grows_with_dstate():
     a = grouped_scan(1, N=16, dim=16, L=1 << 20, batch=1)
     b = grouped_scan(1, N=64, dim=16, L=1 << 20, batch=1)
     ws16, ws64 = ssm.scan_workspace_size(a), ssm.scan_workspace_size(b)
-    assert ws16 > 0 and ws64 * 17 == ws16 * 65
+    assert ws16 == seg_workspace(1, 16, 32, 16) and ws64 == seg_workspace(1, 16, 32, 64)
 
 
 def test_update_any_dstate_and_groups_pass():
@@ -530,10 +541,9 @@ def spaced_scan(batch, dim, L, N, io=1):
 
 def test_noalloc_scratch_limit_is_checked_on_the_host():
     """The no-allocation scan validates like the workspace entry point and
-    rejects, before any HIP call, a block whose segment aggregates exceed
-    its static scratch (64 states, 96 channel groups, 13 segments: 5.2 MB);
-    with 16 states every shape fits (at most 16 x 1280 channel-segments of
-    17 floats)."""
+    rejects, before any HIP call, a block whose segment scratch exceeds its
+    static buffer (64 states, 96 channel groups, 13 segments: 57 MB); with
+    16 states every shape fits (at most 16 x 1280 channel-segments)."""
     L = ssm.lib()
     big = spaced_scan(1, 1536, 13 * 32768, 64)
     assert ssm.validate_scan(big) == OK
@@ -542,7 +552,7 @@ def test_noalloc_scratch_limit_is_checked_on_the_host():
     assert "SSM_NOALLOC_SCRATCH_BYTES" in ssm.status_string(SCRATCH)
     for dim in (16, 100, 1536, 5000, 10000):
         a = spaced_scan(1, dim, 1 << 21, 16)
-        assert ssm.scan_workspace_size(a) <= 16 * 1280 * 17 * 4 <= ssm.NOALLOC_SCRATCH_BYTES
+        assert ssm.scan_workspace_size(a) <= seg_workspace(1, 16 * 1280, 1, 16) <= ssm.NOALLOC_SCRATCH_BYTES
     bad = spaced_scan(1, 16, 64, 16)
     bad.seqlen = -1
     assert L.ssm_selective_scan_fwd_noalloc(ctypes.byref(bad), None) == SHAPE
