@@ -144,7 +144,11 @@ SegLayout seg_layout(const ssm_scan_args& a, int nseg) {
 //    exact state, the record plus the free response exp(A S) h_in;
 //  - jst, the number of windows to rescan: up to the first window start
 //    where the free response is at most 2^-24 max_n |h[n]| in every state
-//    (a non-finite one never passes), else all of the segment's windows.
+//    (a non-finite one never passes), else all of the segment's windows;
+//    and, in bits 8.., where in its last window the channel is expected to
+//    pass, 0..15 (log2 of the free response over that bound taken as
+//    linear between the window's start and the next start; 15 when the
+//    window runs to the segment's end): the lists' sort key.
 struct PlanParams {
   const float* agg;
   float* rec;
@@ -194,23 +198,42 @@ __global__ __launch_bounds__(256) void seg_plan_kernel(PlanParams q) {
     }
   }
   if (col == 0) slot0[N] = 0.0f;
-  int js = nw;
 #pragma unroll
-  for (int j = fwd::kWin - 1; j >= 1; --j) {
-    float f = fr[j], m = hm[j];
+  for (int j = 1; j < fwd::kWin; ++j) {
 #pragma unroll
     for (int o = 1; o < kN; o <<= 1) {
-      f = fmaxf(f, __shfl_xor(f, o, kN));
-      m = fmaxf(m, __shfl_xor(m, o, kN));
+      fr[j] = fmaxf(fr[j], __shfl_xor(fr[j], o, kN));
+      hm[j] = fmaxf(hm[j], __shfl_xor(hm[j], o, kN));
     }
-    if (j < nw && f <= 0x1p-24f * m) js = j;
   }
-  if (col == 0) q.jst[static_cast<size_t>(g) * bd + c] = js;
+  int js = nw;
+#pragma unroll
+  for (int j = fwd::kWin - 1; j >= 1; --j)
+    if (j < nw && fr[j] <= 0x1p-24f * hm[j]) js = j;
+  int tq = 15;
+  if (js < nw) {
+    // log2 of the free response over the bound: 24 at the segment start
+    // (h = h_in there), > 0 at the start of window js - 1, <= 0 at js's
+    float la = 24.0f, lb = 0.0f;
+#pragma unroll
+    for (int j = 1; j < fwd::kWin; ++j) {
+      const float l = __builtin_amdgcn_logf(fr[j]) - __builtin_amdgcn_logf(hm[j]) + 24.0f;
+      if (j == js - 1) la = l;
+      if (j == js) lb = l;
+    }
+    const float f = la / (la - lb);
+    tq = f == f ? static_cast<int>(fminf(fmaxf(16.0f * f, 0.0f), 15.0f)) : 15;
+  }
+  if (col == 0) q.jst[static_cast<size_t>(g) * bd + c] = js | tq << 8;
 }
 
-// Per (batch row, segment g >= 1, chunk): for each window j, the chunk's
-// channels with more than j windows to rescan, ascending, and their count
-// (a stable compaction: each thread takes a run of consecutive channels).
+// Per (batch row, segment g >= 1, chunk, window j): the chunk's channels
+// with more than j windows to rescan, and their count.  The list is sorted
+// by how far into the window a channel is expected to run (the whole
+// window unless it is the channel's last, else the plan's estimate), the
+// longest first, so that the 16 channels of a pass 2 workgroup stop at
+// about the same point; ties keep channel order (a stable counting sort:
+// each thread takes a run of consecutive channels, one scan per key).
 struct ListParams {
   const int* jst;
   int* counts;
@@ -222,9 +245,10 @@ struct ListParams {
 __global__ __launch_bounds__(256) void seg_list_kernel(ListParams q) {
   __shared__ int wsum[4];
   const int64_t bid = blockIdx.x;
-  const int64_t chunk = bid % q.nchunk;
-  const int g = static_cast<int>((bid / q.nchunk) % (q.nseg - 1)) + 1;
-  const int64_t b = bid / (q.nchunk * (q.nseg - 1));
+  const int j = static_cast<int>(bid % fwd::kWin);
+  const int64_t chunk = (bid / fwd::kWin) % q.nchunk;
+  const int g = static_cast<int>((bid / fwd::kWin / q.nchunk) % (q.nseg - 1)) + 1;
+  const int64_t b = bid / (fwd::kWin * q.nchunk * (q.nseg - 1));
   const int64_t cps = (q.scope + q.cw - 1) / q.cw;
   const int64_t c0 = (chunk / cps) * q.scope + (chunk % cps) * q.cw;
   const int64_t c1 = std::min(c0 + q.cw, (chunk / cps + 1) * q.scope);
@@ -232,9 +256,14 @@ __global__ __launch_bounds__(256) void seg_list_kernel(ListParams q) {
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int64_t lo = std::min(c1, c0 + t * per), hi = std::min(c1, lo + per);
   const int* js = q.jst + static_cast<size_t>(g) * q.batch * q.dim + b * q.dim;
-  for (int j = 0; j < fwd::kWin; ++j) {
+  const int64_t key = ((b * q.nseg + g) * fwd::kWin + j) * q.dim + c0;
+  // key of a channel in this window: 16 for the whole window, else the
+  // plan's 0..15; -1 when the channel is not rescanned here
+  auto skey = [&](int v) { return (v & 255) <= j ? -1 : (v & 255) > j + 1 ? 16 : v >> 8; };
+  int base = 0;
+  for (int sk = 16; sk >= 0; --sk) {
     int cnt = 0;
-    for (int64_t c = lo; c < hi; ++c) cnt += js[c] > j;
+    for (int64_t c = lo; c < hi; ++c) cnt += skey(js[c]) == sk;
     int incl = cnt;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -243,18 +272,18 @@ __global__ __launch_bounds__(256) void seg_list_kernel(ListParams q) {
     }
     if (lane == 63) wsum[wv] = incl;
     __syncthreads();
-    int pos = incl - cnt, total = 0;
+    int pos = base + incl - cnt, total = 0;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       if (w < wv) pos += wsum[w];
       total += wsum[w];
     }
-    const int64_t key = ((b * q.nseg + g) * fwd::kWin + j) * q.dim + c0;
     for (int64_t c = lo; c < hi; ++c)
-      if (js[c] > j) q.lists[key + pos++] = static_cast<int>(c);
-    if (t == 0) q.counts[key] = total;
-    __syncthreads();  // wsum is rewritten for the next window
+      if (skey(js[c]) == sk) q.lists[key + pos++] = static_cast<int>(c);
+    base += total;
+    __syncthreads();  // wsum is rewritten for the next key
   }
+  if (t == 0) q.counts[key] = base;
 }
 
 }  // namespace
@@ -428,7 +457,8 @@ hipError_t launch_scan_fwd(const ssm_scan_args& a, hipStream_t stream) {
     lq.jst = jst; lq.counts = counts; lq.lists = lists;
     lq.batch = a.batch; lq.dim = a.dim; lq.scope = p.scope; lq.cw = p.cw; lq.nchunk = p.nchunk;
     lq.nseg = p.nseg;
-    seg_list_kernel<<<dim3((unsigned)(a.batch * (p.nseg - 1) * p.nchunk)), dim3(256), 0, stream>>>(lq);
+    seg_list_kernel<<<dim3((unsigned)(a.batch * (p.nseg - 1) * p.nchunk * fwd::kWin)), dim3(256), 0,
+                      stream>>>(lq);
 
     run(2, dim3((unsigned)(fwd::kWin * a.batch * p.nchunk * (p.nseg - 1) * p.maxi)));
   } else {

@@ -565,12 +565,13 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
     t_beg = g * p.seg_len;
     t_end = std::min(p.L, t_beg + p.seg_len);
   } else {
-    // Pass 2: wg = (((j * batch + b) * nchunk + chunk) * (nseg - 1) + g - 1)
-    // * maxi + i, the i-th 16 channels of the list of window j of segment g
-    // in one chunk of a batch row (windows outermost: the later ones, with
-    // few channels left, come last).  Lists are ascending, so a wavefront's
-    // rows lie between its first and its fourth; entries past the list
-    // repeat its last channel (identical values, identical stores).
+    // Pass 2: wg = (((j' * batch + b) * nchunk + chunk) * (nseg - 1) + g - 1)
+    // * maxi + i, the i-th 16 channels of the list of window j = kWin-1-j'
+    // of segment g in one chunk of a batch row (windows outermost, the
+    // longest first, so that they do not trail the launch).  Entries past
+    // the list repeat its last channel (identical values, identical
+    // stores); a wavefront's windows run from the smallest to the largest
+    // channel of its rows, all in one chunk.
     uint32_t wg = xcd_order(blockIdx.x, gridDim.x);
     const int i = static_cast<int>(wg % static_cast<uint32_t>(p.maxi));
     wg /= static_cast<uint32_t>(p.maxi);
@@ -579,7 +580,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
     const int64_t chunk = wg % p.nchunk;
     const int64_t wr = wg / p.nchunk;
     b = wr % p.batch;
-    jw = static_cast<int>(wr / p.batch);
+    jw = kWin - 1 - static_cast<int>(wr / p.batch);
     const int s0 = g * p.seg_len;
     const int send = std::min(p.L, s0 + p.seg_len);
     const int nwin = seg_windows((send - s0) / kT);
@@ -589,11 +590,12 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
     const int64_t key = ((b * p.nseg + g) * kWin + jw) * p.dim + c0;
     const int cnt = __builtin_amdgcn_readfirstlane(p.counts[key]);
     if (i * kCh >= cnt) return;
-    const int* lst = p.lists + key;
-    const int r0 = i * kCh + kRows * wave;
-    dc = lst[std::min(r0 + row, cnt - 1)];
-    dw0 = __builtin_amdgcn_readfirstlane(lst[std::min(r0, cnt - 1)]);
-    dw3 = __builtin_amdgcn_readfirstlane(lst[std::min(r0 + kRows - 1, cnt - 1)]);
+    const int ch = p.lists[key + std::min(i * kCh + kRows * wave + row, cnt - 1)];
+    const int ch0 = __builtin_amdgcn_readlane(ch, 0), ch1 = __builtin_amdgcn_readlane(ch, 16);
+    const int ch2 = __builtin_amdgcn_readlane(ch, 32), ch3 = __builtin_amdgcn_readlane(ch, 48);
+    dw0 = std::min(std::min(ch0, ch1), std::min(ch2, ch3));
+    dw3 = std::max(std::max(ch0, ch1), std::max(ch2, ch3));
+    dc = ch;
     d = dc;
     vrow = true;
     // shared tile: a chunk never straddles a group
