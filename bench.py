@@ -327,20 +327,30 @@ def ssd_bytes(batch, L, H, P, G, N, esz, gate=True, last_state=True):
     return io + dt + bc + params + st
 
 
-def bench_ssd(cfg, steps, torch, ssm, si):
+def bench_ssd(cfg, steps, torch, ssm, si, segmented=True):
     """Times the Mamba-2 SSM prefill on device-drawn inputs (two input sets
-    in rotation)."""
+    in rotation; one for sequences of 1M tokens and more).  With
+    `segmented`, the library's workspace is allocated once outside the timed
+    region (long sequences with few heads then run as segments); without it
+    each sequence runs as one segment."""
     sets = [si.ssd_inputs_device(cfg, "cuda")]
-    sets.append({k: v.clone() for k, v in sets[0].items()})
+    if cfg.batch * cfg.seqlen < (1 << 20):
+        sets.append({k: v.clone() for k, v in sets[0].items()})
     outs = [torch.empty_like(s["x"]) for s in sets]
     lasts = [torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), device="cuda")
              for _ in sets]
+    a = ssm.SsdArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.ngroups, a.dstate = (
+        cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.ngroups, cfg.dstate)
+    a.io_dtype = ssm.SSM_BF16 if cfg.io_dtype == "bf16" else ssm.SSM_F32
+    nws = ssm.ssd_workspace_size(a) if segmented else 0
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else False
 
     def step(i):
-        k = i % 2
+        k = i % len(sets)
         s = sets[k]
         ssm.ssd_scan_fwd(s["x"], s["dt"], s["A"], s["B"], s["C"], D=s["D"], z=s["z"],
-                         dt_bias=s["dt_bias"], out=outs[k], last_state=lasts[k])
+                         dt_bias=s["dt_bias"], out=outs[k], last_state=lasts[k], workspace=ws)
 
     wl, wms = warm(step, 5, torch)
     kern_ms, kern_min, kern_mean = timed_launches(step, steps, torch)
@@ -356,9 +366,9 @@ def bench_ssd(cfg, steps, torch, ssm, si):
     res = dict(kernel_ms=kern_ms, kernel_ms_min=kern_min, kernel_ms_mean=kern_mean, bytes=nbytes,
                gbps=nbytes / (kern_ms * 1e-3) / 1e9, mfma_tflops=2 * macs / (kern_ms * 1e-3) / 1e12,
                token_heads_per_s=cfg.batch * cfg.seqlen * cfg.nheads / (kern_ms * 1e-3),
-               warmup_launches=wl, warmup_ms=round(wms, 1))
+               warmup_launches=wl, warmup_ms=round(wms, 1), segment_workspace_bytes=nws)
     res["hbm_frac"] = res["gbps"] / HBM_PEAK_GBS
-    del sets, outs, lasts
+    del sets, outs, lasts, ws
     torch.cuda.empty_cache()
     return res
 
@@ -750,6 +760,13 @@ def main():
         log(f"[bench] {cs.name} {secondary[cs.name]['gbps']:.1f} GB/s, "
             f"{secondary[cs.name]['kernel_ms'] * 1e3:.1f} us, "
             f"{secondary[cs.name]['mfma_tflops']:.1f} TFLOP/s on the matrix cores")
+        cl = si.SSD_LONG_CONFIG
+        for seg in (True, False):
+            key = cl.name if seg else f"{cl.name}-one-segment"
+            log(f"[bench] secondary {key}")
+            secondary[key] = bench_ssd(cl, 10, torch, ssm, si, segmented=seg)
+            log(f"[bench] {key} {secondary[key]['gbps']:.1f} GB/s, "
+                f"{secondary[key]['kernel_ms']:.2f} ms")
         for cid in (1, 2, 3):
             cb = si.SCAN_CONFIGS[cid]
             key = f"{cb.name}-backward"

@@ -329,7 +329,15 @@ typedef struct ssm_update_args {
  * state entering each chunk enters as a bf16 value plus its bf16 remainder
  * (two products); with fp32 IO every product is fp32.
  * Aliasing: out must not overlap any input; last_state must not overlap any
- * input except that it may be exactly h0. */
+ * input except that it may be exactly h0.
+ * Workspace: device scratch owned by the caller, 4-byte aligned, of at least
+ * ssm_ssd_workspace_size() bytes, not overlapping any tensor.  With it, a
+ * long sequence whose (batch, head) slices alone would leave the GPU idle is
+ * cut into segments scanned in parallel (Mamba paper notes, sections
+ * 5.3/5.4: chunks handing the state on), the state entering each segment
+ * folded from the end states of the earlier ones; the result is the
+ * one-segment result up to fp32 rounding.  With workspace NULL or too small
+ * each sequence is one segment.  Its contents are scratch on return. */
 typedef struct ssm_ssd_args {
   int64_t batch, seqlen, nheads, headdim, ngroups, dstate;
   int32_t io_dtype;      /* ssm_dtype */
@@ -345,6 +353,7 @@ typedef struct ssm_ssd_args {
   const float* h0;
   float* last_state;
   void* out;       int64_t out_batch_stride, out_seq_stride, out_head_stride;
+  void* workspace;    size_t workspace_bytes;
 } ssm_ssd_args;
 
 /* ABI version of the loaded library (SSM_ABI_VERSION at build time). */
@@ -363,6 +372,13 @@ size_t ssm_ssd_args_size(void);
  * head BD * G * 10 * (dstate + 1) floats, and BD * G * 21 ints of work
  * lists.  Reads only sizes; pure host code. */
 size_t ssm_scan_workspace_size(const ssm_scan_args* args);
+
+/* Workspace bytes the SSD prefill can use for this argument block (0 when
+ * it would run as one segment anyway): for G segments, the segment end
+ * states batch * nheads * G * headdim * dstate fp32 values (rounded up to
+ * 256 bytes) and their step-size sums, batch * nheads * G more.  Reads only
+ * sizes; pure host code. */
+size_t ssm_ssd_workspace_size(const ssm_ssd_args* args);
 
 /* Workspace bytes the backward can use for this argument block:
  * batch * ceil(dim / 16) * 2 * 16 * seqlen + G * batch * dim * 18 fp32

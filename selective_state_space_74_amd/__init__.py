@@ -119,7 +119,7 @@ class SsdArgs(ctypes.Structure):
                 ("C", _P), ("C_batch_stride", _I64), ("C_seq_stride", _I64), ("C_group_stride", _I64),
                 ("A", _P), ("D", _P), ("dt_bias", _P), ("h0", _P), ("last_state", _P),
                 ("out", _P), ("out_batch_stride", _I64), ("out_seq_stride", _I64),
-                ("out_head_stride", _I64)]
+                ("out_head_stride", _I64), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class SSMError(RuntimeError):
@@ -155,6 +155,8 @@ def lib():
         L.ssm_scan_workspace_size.argtypes = [ctypes.POINTER(ScanArgs)]
         L.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
         L.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ScanBwdArgs)]
+        L.ssm_ssd_workspace_size.restype = ctypes.c_size_t
+        L.ssm_ssd_workspace_size.argtypes = [ctypes.POINTER(SsdArgs)]
         L.ssm_selective_scan_fwd.restype = ctypes.c_int
         L.ssm_selective_scan_fwd.argtypes = [ctypes.POINTER(ScanArgs), _P]
         L.ssm_selective_scan_fwd_noalloc.restype = ctypes.c_int
@@ -210,6 +212,10 @@ def scan_fwd_noalloc_raw(args: ScanArgs, stream: int = 0) -> int:
 
 def validate_ssd(args: SsdArgs) -> int:
     return lib().ssm_validate_ssd(ctypes.byref(args))
+
+
+def ssd_workspace_size(args: SsdArgs) -> int:
+    return lib().ssm_ssd_workspace_size(ctypes.byref(args))
 
 
 def ssd_fwd_raw(args: SsdArgs, stream: int = 0) -> int:
@@ -569,13 +575,15 @@ def selective_scan_bwd(dout, u, delta, A, B, C, checkpoints, D=None, z=None, del
 
 
 def ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True, h0=None,
-                 return_last_state=False, out=None, last_state=None, stream=None):
+                 return_last_state=False, out=None, last_state=None, stream=None, workspace=None):
     """Mamba-2 SSM (SSD layer) prefill on the GPU.
 
     x, z: (batch, L, nheads, headdim) with headdim stride 1; dt: (batch, L,
     nheads) with head stride 1 (IO dtype); B, C: (batch, L, ngroups, dstate)
     with state stride 1; A, D, dt_bias: (nheads,) fp32; h0: (batch, nheads,
-    headdim, dstate) fp32.  Returns out (like x) or (out, last_state)."""
+    headdim, dstate) fp32.  Returns out (like x) or (out, last_state).
+    `workspace`: as for selective_scan_fwd (None allocates what the library
+    asks for, False passes none: each sequence then runs as one segment)."""
     torch = _torch()
     if x.dim() != 4:
         raise ValueError("x must be (batch, L, nheads, headdim)")
@@ -620,6 +628,12 @@ def ssd_scan_fwd(x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=True,
     a.A, a.D, a.dt_bias, a.h0 = _ptr(A), _ptr(D), _ptr(dt_bias), _ptr(h0)
     a.last_state = _ptr(last_state)
     a.out, (a.out_batch_stride, a.out_seq_stride, a.out_head_stride) = _ptr(out), out.stride()[:3]
+    need = ssd_workspace_size(a) if workspace is not False else 0
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        _check_dev("workspace", workspace, dev)
+        a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     st = ssd_fwd_raw(a, _stream(stream))
     if st != 0:
         raise SSMError(st, "ssm_ssd_scan_fwd")

@@ -39,6 +39,22 @@
 // operand is split into a bf16 value and its bf16 remainder);
 // fp32 IO uses v_mfma_f32_16x16x4_f32 four times per 16-wide k block, each
 // lane supplying the same four consecutive k values one per instruction.
+//
+// Long sequences with few heads.  The state recurrence is linear (Mamba paper
+// notes, sections 5.3/5.4: a long input is cut into chunks with the state
+// handed on), and a head's decay exp(Delta A) is one scalar per token, so
+// with a caller workspace the sequence is cut into G segments of whole
+// chunks, in two launches of this kernel:
+//   pass 1  every segment from a zero state (segment 0 from h0), writing
+//           every output, and recording its end state H_g and its step-size
+//           sum S_g;
+//   pass 2  segment g >= 1 from the exact state entering it, h_in =
+//           fold_{i<g} (exp(A S_i) h + H_i), rewriting outputs while the
+//           free response exp(A S) |h_in| (S: the step sizes since the
+//           segment start) exceeds 2^-24 of the largest state entry of the
+//           workgroup's channels, checked once per chunk; the last segment's
+//           workgroups also write last_state = exp(A S_g) h_in + H_g.
+// Past that point pass 1's values are the sequential result up to rounding.
 #include <algorithm>
 
 #include "ssm_internal.h"
@@ -74,6 +90,10 @@ struct SsdParams {
   uint32_t xsl, dsl, zsl, Bsl, Csl, osl;
   int L, H, P, G, N;
   int pblocks;   // workgroups per head: ceil(P / (16 PB))
+  // segmented sequences: mode 0 one segment, 1 and 2 the two passes
+  int mode, nseg, seg_chunks;   // segments, chunks per segment
+  float* aggH;   // [batch * H][nseg][P][N] segment end states (from a zero start)
+  float* aggS;   // [batch * H][nseg] segment step-size sums
 };
 
 // Storage of one IO element in LDS and its widening.
@@ -155,8 +175,9 @@ constexpr bool kFourWaves() { return sizeof(T) == 2 && NMAX == 64 && kVec && PB 
 // aligned and dstate is a multiple of NMAX / 4, so staging uses vector loads
 // and 16-byte LDS stores; otherwise element-wise loads.  PB: blocks of 16
 // head channels per workgroup (the score tiles, masks and B/C staging of a
-// chunk are shared by all of them).
-template <typename T, int NMAX, bool kSoftplus, bool kVec, int PB>
+// chunk are shared by all of them).  kSegd: the passes of a segmented
+// sequence (p.mode 1 or 2); without it, one segment and none of their code.
+template <typename T, int NMAX, bool kSoftplus, bool kVec, int PB, bool kSegd>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kFourWaves<T, NMAX, kVec, PB>() ? 4 : 1)))
 void ssd_fwd_kernel(SsdParams p) {
@@ -179,14 +200,23 @@ void ssd_fwd_kernel(SsdParams p) {
   __shared__ __align__(16) E sHL[kBF ? PC : 1][kBF ? NP : 1];
   __shared__ __align__(16) float sDl[kQ];      // Delta_s (0 past the end)
   __shared__ __align__(16) float sLa[kQ];      // a_t * log2(e)
+  // segmented passes (kept in LDS, not in registers across the chunk loop):
+  __shared__ float sRed[kWaves];               // per-wavefront state maxima (pass 2 check)
+  __shared__ float sHin[kWaves];               // per-wavefront maxima of |h_in| (pass 2)
+  __shared__ double sSum;                      // step sizes of the chunks done
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;    // row / column and k quarter
+  // workgroup = ((b * nseg' + seg') * H + h) * pblocks + pb; pass 2 skips
+  // segment 0 (seg = seg' + 1)
+  const int nsg = kSegd ? (p.mode == 2 ? p.nseg - 1 : p.nseg) : 1;
   const int pb = blockIdx.x % p.pblocks;
   const int h = (blockIdx.x / p.pblocks) % p.H;
-  const int64_t b = blockIdx.x / (static_cast<int64_t>(p.pblocks) * p.H);
+  const int64_t bs = blockIdx.x / (static_cast<int64_t>(p.pblocks) * p.H);
+  const int seg = kSegd ? static_cast<int>(bs % nsg) + (p.mode == 2 ? 1 : 0) : 0;
+  const int64_t b = bs / nsg;
   const int g = h / (p.H / p.G);
   const int p0 = pb * PC;
   const int N = p.N;
@@ -213,12 +243,52 @@ void ssd_fwd_kernel(SsdParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int pp = p0 + kPB * q + 4 * lq + i;
-        Hs[j][q][i] = (p.h0 && n < N && pp < p.P)
+        Hs[j][q][i] = (p.h0 && seg == 0 && n < N && pp < p.P)
                           ? p.h0[((b * p.H + h) * p.P + pp) * static_cast<int64_t>(N) + n]
                           : 0.0f;
       }
     }
   }
+  const int64_t bh = b * p.H + h;
+  // pass 2: the exact state entering the segment, folded from the end
+  // states of segments 0..seg-1 (segment 0's includes h0), and its largest
+  // entry over this workgroup's channels; the last segment also writes the
+  // final state
+  float hin_max = 0.0f;
+  if (kSegd && p.mode == 2) {
+    const float* aS = p.aggS + bh * p.nseg;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const int n = 16 * (wave + kWaves * j) + lr;
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pp = p0 + kPB * q + 4 * lq + i;
+          if (n < N && pp < p.P) {
+            const float* aH = p.aggH + (bh * p.nseg * p.P + pp) * static_cast<int64_t>(N) + n;
+            const int64_t sst = static_cast<int64_t>(p.P) * N;   // from one segment to the next
+            float hv = aH[0];
+            for (int k = 1; k < seg; ++k) hv = fmaf(__builtin_amdgcn_exp2f(a2 * aS[k]), hv, aH[k * sst]);
+            Hs[j][q][i] = hv;
+            // a non-finite entry never lets the rescan stop
+            hin_max = fmaxf(hin_max, hv == hv ? fabsf(hv) : __builtin_huge_valf());
+            if (p.last && seg == p.nseg - 1)
+              p.last[(bh * p.P + pp) * static_cast<int64_t>(N) + n] =
+                  fmaf(__builtin_amdgcn_exp2f(a2 * aS[seg]), hv, aH[seg * sst]);
+          }
+        }
+      }
+    }
+  }
+  if (kSegd && p.mode == 2) {
+    // per wavefront; the workgroup's maximum is taken where it is used (the
+    // chunk loop's barriers order these stores before those reads)
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) hin_max = fmaxf(hin_max, __shfl_xor(hin_max, m, 64));
+    if (lane == 0) sHin[wave] = hin_max;
+  }
+  if (kSegd && tid == 0) sSum = 0.0;
   // operand copy of the state (bf16: value and remainder)
   auto store_ht = [&]() {
 #pragma unroll
@@ -341,9 +411,32 @@ void ssd_fwd_kernel(SsdParams p) {
     if constexpr (sizeof(E) == 2) return static_cast<E>(m);
     else return __uint_as_float(m);
   };
+  // this segment's chunks
+  const int c_beg = kSegd ? seg * p.seg_chunks : 0;
+  const int c_end = kSegd ? std::min(nchunks, c_beg + p.seg_chunks) : nchunks;
   Stage st;
-  if (nchunks > 0) st = load_stage(0);
-  for (int c = 0; c < nchunks; ++c) {
+  if (c_beg < c_end) st = load_stage(c_beg);
+  for (int c = c_beg; c < c_end; ++c) {
+    if (kSegd && p.mode == 2 && c > c_beg) {
+      // pass 2: stop once the incoming state's free response is below fp32
+      // resolution of this workgroup's state (the chunk's loads in flight
+      // are simply dropped)
+      float hm = 0.0f;
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+#pragma unroll
+        for (int q = 0; q < PB; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hm = fmaxf(hm, fabsf(Hs[j][q][i]));
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) hm = fmaxf(hm, __shfl_xor(hm, m, 64));
+      if (lane == 0) sRed[wave] = hm;
+      __syncthreads();
+      hm = fmaxf(fmaxf(sRed[0], sRed[1]), fmaxf(sRed[2], sRed[3]));
+      const float hi = fmaxf(fmaxf(sHin[0], sHin[1]), fmaxf(sHin[2], sHin[3]));
+      const float fr = __builtin_amdgcn_exp2f(a2 * static_cast<float>(sSum)) * hi;
+      if (fr <= 0x1p-24f * hm) break;   // the same values in every thread
+    }
     const int t0 = c * kQ;
     const int nv = std::min(kQ, p.L - t0);
     // ---- B, C and x^T of this chunk into LDS, before the step-size scan so
@@ -400,6 +493,12 @@ void ssd_fwd_kernel(SsdParams p) {
       }
       const float la = cum * a2;
       const float last = __shfl(la, 63, 64);
+      if constexpr (kSegd) {
+        // segmented: read at the next chunk's top and after the loop, past
+        // this chunk's barriers
+        const float csum = __shfl(cum, 63, 64);
+        if (tid == 0) sSum += static_cast<double>(csum);
+      }
       const float w = __builtin_amdgcn_exp2f(last - la) * dl;   // exp(a_{Q-1} - a_s) Delta_s
       w_row = __shfl(w, srow, 64);
       if (wave == 0) {
@@ -431,7 +530,7 @@ void ssd_fwd_kernel(SsdParams p) {
     for (int q = 0; q < PB; ++q)
 #pragma unroll
       for (int i = 0; i < 4; ++i) zr[q][i] = st.z[q][i];
-    if (c + 1 < nchunks) st = load_stage(c + 1);
+    if (c + 1 < c_end) st = load_stage(c + 1);
 
     // ---- outputs of tokens 16 w .. 16 w + 15 ----
     {
@@ -530,8 +629,26 @@ void ssd_fwd_kernel(SsdParams p) {
     store_ht();
   }
 
-  // final state
-  if (p.last) {
+  // pass 1: the segment's end state from its start state and its
+  // step-size sum (equal in every workgroup of the head)
+  if (kSegd && p.mode == 1) {
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const int n = 16 * (wave + kWaves * j) + lr;
+#pragma unroll
+      for (int q = 0; q < PB; ++q) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pp = p0 + kPB * q + 4 * lq + i;
+          if (n < N && pp < p.P)
+            p.aggH[((bh * p.nseg + seg) * p.P + pp) * static_cast<int64_t>(N) + n] = Hs[j][q][i];
+        }
+      }
+    }
+    if (pb == 0 && tid == 0) p.aggS[bh * p.nseg + seg] = static_cast<float>(sSum);
+  }
+  // final state (one segment)
+  if (!kSegd && p.last) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const int n = 16 * (wave + kWaves * j) + lr;
@@ -575,18 +692,71 @@ int choose_pb(int P, int nmax, bool bf, int64_t) {
 }
 #endif
 
-template <typename T, int NMAX, int PB>
-void launch_n(bool softplus, bool vec, dim3 grid, const SsdParams& p, hipStream_t stream) {
+// Segments of a long sequence whose (batch, head, channel block) workgroups
+// leave the machine short: as many as bring the grid to about 512
+// workgroups (two per CU), each at least 32,768 tokens long (pass 2 rescans
+// a segment's head until the incoming state has decayed, about
+// 17 / (Delta |A|) tokens for the slowest head: 17,000 at Delta 1e-3,
+// A = -1), at most 64.
+constexpr int64_t kSsdTargetGroups = 512;
+constexpr int64_t kSsdMinSegLen = 32768;
+constexpr int kSsdMaxSeg = 64;
+
+struct SsdPlan {
+  int pbk, pblocks;   // channel blocks per workgroup, workgroups per head
+  int nseg, seg_chunks;
+};
+
+SsdPlan ssd_plan(const ssm_ssd_args& a) {
+  const bool bf = a.io_dtype == SSM_BF16;
+  const int nmax = (bf && a.dstate > 64) ? 128 : 64;
+  SsdPlan q;
+  q.pbk = choose_pb(static_cast<int>(a.headdim), nmax, bf, a.batch * a.nheads);
+  q.pblocks = static_cast<int>((a.headdim + kPB * q.pbk - 1) / (kPB * q.pbk));
+  const int64_t groups = a.batch * a.nheads * q.pblocks;
+  const int64_t nchunks = (a.seqlen + kQ - 1) / kQ;
+  int64_t g = 1;
+  if (groups > 0 && groups < kSsdTargetGroups / 2)
+    g = std::max<int64_t>(1, std::min<int64_t>({kSsdTargetGroups / groups, a.seqlen / kSsdMinSegLen,
+                                                int64_t{kSsdMaxSeg}}));
+  q.seg_chunks = static_cast<int>(std::max<int64_t>(1, (nchunks + g - 1) / g));
+  q.nseg = static_cast<int>(std::max<int64_t>(1, (nchunks + q.seg_chunks - 1) / q.seg_chunks));
+  return q;
+}
+
+// Workspace of a segmented sequence: the end states, [batch * H][nseg][P][N]
+// fp32, then the step-size sums [batch * H][nseg] (offset rounded to 256
+// bytes).
+size_t ssd_agg_offset(const ssm_ssd_args& a, int nseg) {
+  const size_t n = static_cast<size_t>(a.batch * a.nheads) * nseg * a.headdim * a.dstate * 4;
+  return (n + 255) / 256 * 256;
+}
+
+template <typename T, int NMAX, int PB, bool kSegd>
+void launch_s(bool softplus, bool vec, dim3 grid, const SsdParams& p, hipStream_t stream) {
   if (vec) {
-    if (softplus) ssd_fwd_kernel<T, NMAX, true, true, PB><<<grid, dim3(kThreads), 0, stream>>>(p);
-    else ssd_fwd_kernel<T, NMAX, false, true, PB><<<grid, dim3(kThreads), 0, stream>>>(p);
+    if (softplus) ssd_fwd_kernel<T, NMAX, true, true, PB, kSegd><<<grid, dim3(kThreads), 0, stream>>>(p);
+    else ssd_fwd_kernel<T, NMAX, false, true, PB, kSegd><<<grid, dim3(kThreads), 0, stream>>>(p);
   } else {
-    if (softplus) ssd_fwd_kernel<T, NMAX, true, false, PB><<<grid, dim3(kThreads), 0, stream>>>(p);
-    else ssd_fwd_kernel<T, NMAX, false, false, PB><<<grid, dim3(kThreads), 0, stream>>>(p);
+    if (softplus) ssd_fwd_kernel<T, NMAX, true, false, PB, kSegd><<<grid, dim3(kThreads), 0, stream>>>(p);
+    else ssd_fwd_kernel<T, NMAX, false, false, PB, kSegd><<<grid, dim3(kThreads), 0, stream>>>(p);
   }
 }
 
+template <typename T, int NMAX, int PB>
+void launch_n(bool softplus, bool vec, dim3 grid, const SsdParams& p, hipStream_t stream) {
+  if (p.mode != 0) launch_s<T, NMAX, PB, true>(softplus, vec, grid, p, stream);
+  else launch_s<T, NMAX, PB, false>(softplus, vec, grid, p, stream);
+}
+
 }  // namespace
+
+size_t ssd_workspace_bytes(const ssm_ssd_args& a) {
+  if (a.batch <= 0 || a.seqlen <= 0 || a.nheads <= 0 || a.headdim <= 0 || a.dstate <= 0) return 0;
+  const SsdPlan q = ssd_plan(a);
+  if (q.nseg <= 1) return 0;
+  return ssd_agg_offset(a, q.nseg) + static_cast<size_t>(a.batch * a.nheads) * q.nseg * 4;
+}
 
 hipError_t launch_ssd_fwd(const ssm_ssd_args& a, hipStream_t stream) {
   if (a.seqlen == 0) {
@@ -614,11 +784,21 @@ hipError_t launch_ssd_fwd(const ssm_ssd_args& a, hipStream_t stream) {
   const bool sp = a.dt_softplus != 0;
   const bool bf = a.io_dtype == SSM_BF16;
   const int nmax = (bf && a.dstate > 64) ? 128 : 64;
-  const int pbk = choose_pb(p.P, nmax, bf, a.batch * a.nheads);
-  p.pblocks = (p.P + kPB * pbk - 1) / (kPB * pbk);
-  const int64_t nblocks = a.batch * a.nheads * p.pblocks;
+  const SsdPlan q = ssd_plan(a);
+  const int pbk = q.pbk;
+  p.pblocks = q.pblocks;
+  // segments only with a workspace that holds their end states
+  const size_t need = ssd_workspace_bytes(a);
+  const bool segd = need > 0 && a.workspace && a.workspace_bytes >= need;
+  p.nseg = segd ? q.nseg : 1;
+  p.seg_chunks = segd ? q.seg_chunks : static_cast<int>((a.seqlen + kQ - 1) / kQ);
+  p.mode = segd ? 1 : 0;
+  p.aggH = segd ? static_cast<float*>(a.workspace) : nullptr;
+  p.aggS = segd ? reinterpret_cast<float*>(static_cast<char*>(a.workspace) + ssd_agg_offset(a, q.nseg))
+                : nullptr;
+  const int64_t nblocks = a.batch * a.nheads * p.pblocks * p.nseg;
   if (nblocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const dim3 grid(static_cast<unsigned>(nblocks));
+  dim3 grid(static_cast<unsigned>(nblocks));
   // vector staging: 16-byte B/C row quarters, 8- (bf16) or 16-byte (fp32) x
   // rows of four channels
   const int esz = bf ? 2 : 4;
@@ -633,18 +813,28 @@ hipError_t launch_ssd_fwd(const ssm_ssd_args& a, hipStream_t stream) {
                    a.C_seq_stride % bw == 0 && (G == 1 || a.C_group_stride % bw == 0) &&
                    al(a.x, xw * esz) && a.x_batch_stride % xw == 0 && a.x_seq_stride % xw == 0 &&
                    a.x_head_stride % xw == 0 && a.headdim % xw == 0;
-  if (bf && nmax == 64) {
-    switch (pbk) {
-      case 4: launch_n<uint16_t, 64, 4>(sp, vec, grid, p, stream); break;
-      case 2: launch_n<uint16_t, 64, 2>(sp, vec, grid, p, stream); break;
-      default: launch_n<uint16_t, 64, 1>(sp, vec, grid, p, stream); break;
+  auto run = [&](const SsdParams& pp, dim3 gr) {
+    if (bf && nmax == 64) {
+      switch (pbk) {
+        case 4: launch_n<uint16_t, 64, 4>(sp, vec, gr, pp, stream); break;
+        case 2: launch_n<uint16_t, 64, 2>(sp, vec, gr, pp, stream); break;
+        default: launch_n<uint16_t, 64, 1>(sp, vec, gr, pp, stream); break;
+      }
+    } else if (bf) {
+      if (pbk == 2) launch_n<uint16_t, 128, 2>(sp, vec, gr, pp, stream);
+      else launch_n<uint16_t, 128, 1>(sp, vec, gr, pp, stream);
+    } else {
+      if (pbk == 2) launch_n<float, 64, 2>(sp, vec, gr, pp, stream);
+      else launch_n<float, 64, 1>(sp, vec, gr, pp, stream);
     }
-  } else if (bf) {
-    if (pbk == 2) launch_n<uint16_t, 128, 2>(sp, vec, grid, p, stream);
-    else launch_n<uint16_t, 128, 1>(sp, vec, grid, p, stream);
-  } else {
-    if (pbk == 2) launch_n<float, 64, 2>(sp, vec, grid, p, stream);
-    else launch_n<float, 64, 1>(sp, vec, grid, p, stream);
+  };
+  run(p, grid);
+  if (segd) {
+    // pass 2: segments 1.. from their folded incoming states (stream order
+    // puts pass 1's end states, and its reads of h0, first)
+    SsdParams p2 = p;
+    p2.mode = 2;
+    run(p2, dim3(static_cast<unsigned>(a.batch * a.nheads * p.pblocks * (p.nseg - 1))));
   }
   return hipGetLastError();
 }

@@ -70,6 +70,11 @@ size_t ssm_scan_workspace_size(const ssm_scan_args* a) {
   return ssm::scan_workspace_bytes(*a);
 }
 
+size_t ssm_ssd_workspace_size(const ssm_ssd_args* a) {
+  if (!a || a->seqlen > kMaxSeqlen || a->batch < 0 || a->seqlen < 0) return 0;
+  return ssm::ssd_workspace_bytes(*a);
+}
+
 size_t ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args* a) {
   if (!a || a->dstate != 16 || a->seqlen > kMaxSeqlen || a->batch < 0 || a->dim < 0 ||
       a->seqlen < 0)
@@ -342,7 +347,7 @@ int ssm_validate_ssd(const ssm_ssd_args* a) {
       return SSM_ERR_UNSUPPORTED;
   }
   if (misaligned(a->A, 4) || misaligned(a->D, 4) || misaligned(a->dt_bias, 4) ||
-      misaligned(a->h0, 4) || misaligned(a->last_state, 4))
+      misaligned(a->h0, 4) || misaligned(a->last_state, 4) || misaligned(a->workspace, 4))
     return SSM_ERR_ALIGN;
   const Span sh0 = span1(a->h0, Bt * H * P * N, 4);
   const Span inputs[] = {
@@ -355,12 +360,13 @@ int ssm_validate_ssd(const ssm_ssd_args* a) {
   const Span sout = span4(a->out, Bt, a->out_batch_stride, L, a->out_seq_stride, H,
                           a->out_head_stride, P, esz);
   const Span slast = span1(a->last_state, Bt * H * P * N, 4);
+  const Span sws = span1(a->workspace, static_cast<int64_t>(a->workspace_bytes), 1);
   for (const Span& i : inputs) {
-    if (overlap(sout, i)) return SSM_ERR_ALIAS;
+    if (overlap(sout, i) || overlap(sws, i)) return SSM_ERR_ALIAS;
     if (&i == &inputs[8] && a->last_state == a->h0) continue;
     if (overlap(slast, i)) return SSM_ERR_ALIAS;
   }
-  if (overlap(sout, slast)) return SSM_ERR_ALIAS;
+  if (overlap(sout, slast) || overlap(sws, sout) || overlap(sws, slast)) return SSM_ERR_ALIAS;
   return SSM_OK;
 }
 

@@ -21,6 +21,7 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream);
 bool scan_bwd_windows_fit(const ssm_scan_bwd_args& a);
 size_t scan_bwd_workspace_bytes(const ssm_scan_bwd_args& a);
 hipError_t launch_ssd_fwd(const ssm_ssd_args& a, hipStream_t stream);
+size_t ssd_workspace_bytes(const ssm_ssd_args& a);
 
 // ---------------------------------------------------------------------------
 // Device helpers.

@@ -263,6 +263,8 @@ class SsdConfig:
 # The page's Mamba2(d_model=1024, d_state=64, expand=2, headdim 64) block:
 # d_inner 2048 = 32 heads of 64, at the 130m-like layer's batch and length.
 SSD_CONFIG = SsdConfig("mamba2-d1024-layer-bf16", 8, 2048, 32, 64, 1, 64, "bf16", 5)
+# a long-context Mamba-2 layer: one sequence of 1M tokens, 32 heads of 64
+SSD_LONG_CONFIG = SsdConfig("mamba2-long-context-bf16", 1, 1 << 20, 32, 64, 1, 64, "bf16", 6)
 
 
 def head_params(nheads: int, rng: np.random.Generator):

@@ -556,3 +556,67 @@ def test_noalloc_scratch_limit_is_checked_on_the_host():
     bad = spaced_scan(1, 16, 64, 16)
     bad.seqlen = -1
     assert L.ssm_selective_scan_fwd_noalloc(ctypes.byref(bad), None) == SHAPE
+
+
+def good_ssd(batch=2, L=128, H=4, P=32, G=1, N=64, io=0):
+    """A valid SSD prefill block at fake addresses (batch, L, H, P) rows."""
+    a = ssm.SsdArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.ngroups, a.dstate = batch, L, H, P, G, N
+    a.io_dtype, a.dt_softplus = io, 1
+    for i, name in enumerate(("x", "z", "out")):
+        setattr(a, name, addr(30 + i))
+        setattr(a, f"{name}_batch_stride", L * H * P)
+        setattr(a, f"{name}_seq_stride", H * P)
+        setattr(a, f"{name}_head_stride", P)
+    a.dt, a.dt_batch_stride, a.dt_seq_stride = addr(33), L * H, H
+    for i, name in enumerate(("B", "C")):
+        setattr(a, name, addr(34 + i))
+        setattr(a, f"{name}_batch_stride", L * G * N)
+        setattr(a, f"{name}_seq_stride", G * N)
+        setattr(a, f"{name}_group_stride", N)
+    a.A, a.D, a.dt_bias, a.h0, a.last_state = addr(36), addr(37), addr(38), addr(39), addr(40)
+    return a
+
+
+def test_ssd_struct_and_valid_block():
+    assert ssm.lib().ssm_ssd_args_size() == ctypes.sizeof(ssm.SsdArgs)
+    assert ssm.validate_ssd(good_ssd()) == OK
+    assert ssm.validate_ssd(good_ssd(io=1, N=128)) == OK
+    assert ssm.validate_ssd(good_ssd(N=128)) == UNSUP        # fp32 IO: at most 64 states
+
+
+def ssd_workspace(batch, H, P, N, nseg):
+    """The segmented SSD prefill's scratch: the segment end states (fp32,
+    rounded up to 256 bytes), then one step-size sum per (batch, head,
+    segment)."""
+    al = lambda x: (x + 255) // 256 * 256
+    return al(batch * H * nseg * P * N * 4) + batch * H * nseg * 4
+
+
+def test_ssd_workspace_size():
+    """Long sequences whose (batch, head, 16-channel block) workgroups are
+    few are cut into segments of whole 64-token chunks: up to about 512
+    workgroups, each segment at least 32,768 tokens, at most 64 segments.
+    Batch 1 with 32 heads of 64 channels (128 workgroups) at 1M tokens: 4
+    segments.  The benchmarked layer (batch 8, L 2048) and short sequences:
+    none."""
+    assert ssm.ssd_workspace_size(good_ssd(1, 1 << 20, 32, 64, 1, 64, io=1)) == \
+        ssd_workspace(1, 32, 64, 64, 4)
+    assert ssm.ssd_workspace_size(good_ssd(1, 3 * 32768 + 100, 2, 64, 1, 64)) == \
+        ssd_workspace(1, 2, 64, 64, 3)
+    assert ssm.ssd_workspace_size(good_ssd(1, 1 << 22, 1, 16, 1, 16)) == ssd_workspace(1, 1, 16, 16, 64)
+    assert ssm.ssd_workspace_size(good_ssd(8, 2048, 32, 64, 1, 64, io=1)) == 0
+    assert ssm.ssd_workspace_size(good_ssd(1, 32767, 1, 16, 1, 16)) == 0
+    assert ssm.ssd_workspace_size(good_ssd(1, 0, 1, 16, 1, 16)) == 0
+
+
+def test_ssd_workspace_alias_and_alignment():
+    a = good_ssd()
+    a.workspace, a.workspace_bytes = addr(41), 1 << 20
+    assert ssm.validate_ssd(a) == OK
+    a.workspace = addr(30)                               # over x
+    assert ssm.validate_ssd(a) == ALIAS
+    a.workspace = addr(32)                               # over out
+    assert ssm.validate_ssd(a) == ALIAS
+    a.workspace = addr(41) + 2
+    assert ssm.validate_ssd(a) == ALIGN

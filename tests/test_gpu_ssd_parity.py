@@ -125,6 +125,57 @@ def test_ssd_split_sequence_carries_the_state():
     assert e <= 1e-4 and el <= 1e-4
 
 
+def _ssd_args(batch, L, H, P, G, N):
+    a = ssm.SsdArgs()
+    a.batch, a.seqlen, a.nheads, a.headdim, a.ngroups, a.dstate = batch, L, H, P, G, N
+    return a
+
+
+@pytest.mark.parametrize("H,P,N,io", [(2, 64, 64, "f32"), (3, 40, 128, "bf16"), (2, 64, 64, "bf16")])
+def test_ssd_segmented_long_sequence(H, P, N, io):
+    """Few (batch, head) slices and a long sequence: with the workspace the
+    sequence is cut into segments (pass 1 from zero states, pass 2 rescanning
+    each segment's head from its folded incoming state).  Checked against the
+    oracle, with and without h0, next to the one-segment run (no workspace)."""
+    batch, L, G = 1, 3 * 32768 + 100, 1
+    assert ssm.ssd_workspace_size(_ssd_args(batch, L, H, P, G, N)) > 0
+    inp = si.ssd_inputs(batch, L, H, P, G, N, io_dtype=io, seed=H * 100 + N)
+    h0 = np.random.default_rng(N).standard_normal((batch, H, P, N)).astype(np.float32)
+    ref, rlast = run_oracle(inp, h0=h0)
+    t = to_dev(inp, io)
+    kw = dict(D=t["D"], z=t["z"], dt_bias=t["dt_bias"], h0=torch.from_numpy(h0).to(DEV),
+              return_last_state=True)
+    for ws in (None, False):
+        out, last = ssm.ssd_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], workspace=ws, **kw)
+        torch.cuda.synchronize()
+        e, el = errors(to_np(out), ref, to_np(last), rlast)
+        print(f"[ssd segmented={ws is None} H{H} P{P} N{N} {io}] err_out={e:.3e} err_last={el:.3e}",
+              flush=True)
+        assert e <= TOL[io] and el <= TOL[io], (e, el)
+    check(inp, io, f"segmented H{H} P{P} N{N} {io} no h0")
+
+
+def test_ssd_segmented_in_place_carry_and_no_decay():
+    """Segmented: the final state written over h0 (pass 1 reads h0 before
+    pass 2 writes it), and a head with A = 0 whose incoming state never
+    decays (pass 2 then rescans its whole segments)."""
+    batch, L, H, P, G, N = 1, 2 * 32768 + 640, 2, 32, 1, 64
+    assert ssm.ssd_workspace_size(_ssd_args(batch, L, H, P, G, N)) > 0
+    inp = si.ssd_inputs(batch, L, H, P, G, N, io_dtype="f32", seed=21)
+    inp["A"] = inp["A"].copy()
+    inp["A"][1] = 0.0
+    h0 = np.random.default_rng(21).standard_normal((batch, H, P, N)).astype(np.float32)
+    ref, rlast = run_oracle(inp, h0=h0)
+    t = to_dev(inp, "f32")
+    state = torch.from_numpy(h0).to(DEV)
+    out = ssm.ssd_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                           dt_bias=t["dt_bias"], h0=state, last_state=state)
+    torch.cuda.synchronize()
+    e, el = errors(to_np(out), ref, to_np(state), rlast)
+    print(f"[ssd segmented in-place, A=0 head] err_out={e:.3e} err_last={el:.3e}", flush=True)
+    assert e <= 1e-4 and el <= 1e-4
+
+
 def test_ssd_zero_length_copies_initial_state():
     H, P, N = 4, 16, 32
     x = torch.zeros((2, 0, H, P), device=DEV)
