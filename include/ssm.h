@@ -85,8 +85,8 @@ typedef enum ssm_status {
   SSM_ERR_ALIGN = 5,       /* pointer not aligned to its element size          */
   SSM_ERR_ALIAS = 6,       /* an output overlaps an input it must not overlap  */
   SSM_ERR_UNSUPPORTED = 7, /* valid but not built: dstate > SSM_MAX_DSTATE
-                              (backward: dstate != 16, or groups that split a
-                              block of 16 channels), seqlen too large for
+                              (backward: also groups that split a block of
+                              16 channels), seqlen too large for
                               32-bit token indices (>= 2^31 - 64), or row
                               spans past the 32-bit windows (see
                               ssm_scan_args)                                   */
@@ -207,9 +207,9 @@ typedef struct ssm_scan_args {
  * forward state), and every segment then runs the full backward from the
  * exact adjoint entering it (Mamba paper notes, section 5.4: state passed at
  * chunk edges); without it, each sequence is one segment.
- * It is built for dstate == 16 and for B/C groups that keep each block of 16
- * consecutive channels in one group (one group, or dim / ngroups a multiple
- * of 16); other shapes return SSM_ERR_UNSUPPORTED.
+ * It is built for dstate 1..SSM_MAX_DSTATE and for B/C groups that keep each
+ * block of 16 consecutive channels in one group (one group, or dim / ngroups
+ * a multiple of 16); other groupings return SSM_ERR_UNSUPPORTED.
  * Workspace (optional): device scratch owned by the caller, 4-byte aligned,
  * of at least ssm_scan_bwd_workspace_size() bytes, not overlapping any
  * tensor.  The library then writes each block of 16 channels' dB/dC partial
@@ -381,9 +381,9 @@ size_t ssm_scan_workspace_size(const ssm_scan_args* args);
 size_t ssm_ssd_workspace_size(const ssm_ssd_args* args);
 
 /* Workspace bytes the backward can use for this argument block:
- * batch * ceil(dim / 16) * 2 * 16 * seqlen + G * batch * dim * 18 fp32
- * values, plus batch * dim * G * 17 for the adjoint aggregates when the
- * sequence is cut into G > 1 segments (0 for an empty
+ * batch * ceil(dim / 16) * 2 * dstate * seqlen + G * batch * dim *
+ * (dstate + 2) fp32 values, plus batch * dim * G * (dstate + 1) for the
+ * adjoint aggregates when the sequence is cut into G > 1 segments (0 for an empty
  * sequence or when batch * ngroups exceeds 65535, where it adds dB/dC with
  * atomics anyway).  Reads only sizes; pure host code. */
 size_t ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args* args);

@@ -644,7 +644,7 @@ def selective_scan(u, delta, A, B, C, D=None, z=None, delta_bias=None, delta_sof
     """selective_scan_fwd as a differentiable torch op: the forward keeps the
     state checkpoints and the backward runs ssm_selective_scan_bwd on them.
     Gradients flow to u, delta, A, B, C and, when given, D, z and delta_bias
-    (d_state 16; B/C shared or in groups that keep 16-channel blocks whole)."""
+    (d_state 1..64; B/C shared or in groups that keep 16-channel blocks whole)."""
     torch = _torch()
 
     class _Scan(torch.autograd.Function):

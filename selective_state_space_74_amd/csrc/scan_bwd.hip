@@ -18,9 +18,11 @@
 // backward recomputes the 16 steps of a block from its checkpoint.
 //
 // Work decomposition (the forward's): a workgroup is 4 wavefronts x 4
-// channels of one batch row, lane (row c, col n) holds state n of channel c,
-// and lane (row c, col j), as owner, handles token j of each block.  Blocks
-// are walked from the last to the first; per block:
+// channels of one batch row, lane (row c, col n) holds states n, n + 16, ...
+// (S slots for up to 16 S states; states past dstate are padding that stays
+// zero) of channel c, and lane (row c, col j), as owner, handles token j of
+// each block.  Blocks are walked from the last to the first; per block (one
+// slot; with several, see block_slots):
 //   1. state lanes recompute e_t and h_t for the 16 tokens from the
 //      checkpoint (registers) and leave C_n h_t in LDS;
 //   2. owners sum those into y, form dy and dz (dy reaches the state lanes
@@ -57,7 +59,7 @@
 namespace ssm {
 namespace {
 
-constexpr int kN = 16;               // states per channel = lanes per row
+constexpr int kN = 16;               // lanes per row = states per slot
 constexpr int kRows = 4;             // channels per wavefront
 constexpr int kWaves = 4;            // wavefronts per workgroup
 constexpr int kCh = kRows * kWaves;  // channels per workgroup
@@ -67,7 +69,6 @@ constexpr int kGB = 2;               // blocks per B/C tile
 constexpr int kGT = kT * kGB;        // tokens per tile
 constexpr int kGPitch = kGT + 4;     // LDS pitch (floats) of one state's tile row
 constexpr int kPitch = 20;           // LDS pitch (floats) of one state's 16 token terms
-constexpr int kPartRow = kN * kPitch + 16;  // floats per channel of per-token terms
 
 // The value held by lane col ^ 8 of the same 16-lane row (DPP row_ror:8).
 __device__ __forceinline__ float row_swap8(float v) {
@@ -109,11 +110,11 @@ struct BwdParams {
   float* dD;
   float* dbias;
   float* dh0;
-  float* part;          // [batch][cgroups][2][kN][L] dB/dC partial sums, or NULL (atomics)
-  float* pdA;           // with part: [nseg][batch][dim][kN] dA, [nseg][batch][dim] dD and
+  float* part;          // [batch][cgroups][2][N][L] dB/dC partial sums, or NULL (atomics)
+  float* pdA;           // with part: [nseg][batch][dim][N] dA, [nseg][batch][dim] dD and
   float* pdD;           // bias gradient per segment and batch row, summed over both
   float* pdb;           // by a second kernel (NULL: device atomics into dA, dD, dbias)
-  float* agg;           // segmented: [batch][dim][nseg][kN + 1] adjoint aggregates
+  float* agg;           // segmented: [batch][dim][nseg][N + 1] adjoint aggregates
   int seg_len;          // tokens per segment (a multiple of kGT)
   int nseg;             // segments per sequence (1: the whole sequence)
   int64_t usb, usd, dsb, dsd, zsb, zsd, Bsb, Bsn, Csb, Csn, Asd, Asn, gsb, gsd;
@@ -122,6 +123,7 @@ struct BwdParams {
   int64_t ngroups, cpg; // groups, channels per group (a multiple of kCh, or dim)
   int64_t batch, dim;
   int L;
+  int N;            // states per channel (dstate)
   int nbk;          // ceil(L / kT)
   int64_t cgroups;  // ceil(dim / kCh)
 };
@@ -131,29 +133,41 @@ struct Raw {
   uint32_t u, dt, z, dout;
 };
 
-// Tile inputs: B and C of state 4 wave + row at tokens tg + col + 16 i.
+// Tile inputs: B and C of states 4 wave + row + 16 q at tokens tg + col + 16 i.
+template <int S>
 struct TileRaw {
-  uint32_t b[kGB], c[kGB];
+  uint32_t b[S][kGB], c[S][kGB];
 };
 
-template <typename T, bool kSoftplus>
+// LDS pitch (floats) of one state's per-token terms: 16 tokens (one slot:
+// readout partials, then half a block of g B and g A e h terms), or 32 (slots:
+// a whole block of both terms).
+template <int S>
+constexpr int kXPitch = S == 1 ? kPitch : 2 * kT + 4;
+template <int S>
+constexpr int kXRow = kN * kXPitch<S> + 16;   // floats per channel
+
+template <typename T, bool kSoftplus, int S>
 struct BwdWave {
   const BwdParams& p;
   int wave, row, col;
   int nbk, ntile;
   Window wu, wdt, wz, wg, wdu, wdd, wdz, wB, wC, wck, wdB, wdC;
-  uint32_t ou, odt, oz, og, odu, odd, odz, oB, oC, ock;
-  float a, a2, bias, Dd;
+  uint32_t ou, odt, oz, og, odu, odd, odz;
+  // per state slot; B/C and checkpoint offsets of padding states point past
+  // their window (loads read zero)
+  uint32_t oB[S], oC[S], ock[S];
+  float a[S], a2[S], bias, Dd;
   bool gate;
   bool partials;      // dB/dC sums stored to this workgroup's slots, not added
   int nvalid;         // channels of this workgroup below dim
-  float (*sB)[kN][kGPitch];   // [2][kN][kGPitch], shared
-  float (*sC)[kN][kGPitch];
-  float (*sX)[kPartRow];      // this wavefront's [kRows][kPartRow]: readout, then the
-                              // per-state du/ddelta terms of half a block
+  float (*sB)[kN * S][kGPitch];   // [2][kN S][kGPitch], shared
+  float (*sC)[kN * S][kGPitch];
+  float (*sX)[kXRow<S>];      // this wavefront's [kRows][kXRow]: readout, then the
+                              // per-state du/ddelta terms
   float (*sQ)[kRows][kN][4];   // [kWaves][kRows][kN][4], shared: dB/dC terms of half a
-                              // block summed over each wavefront's channels; row r
-                              // holds tensor r / 2 (dB, dC), tokens 4 (r % 2) + 0..3
+                              // block (one slot) summed over each wavefront's channels;
+                              // row r holds tensor r / 2 (dB, dC), tokens 4 (r % 2) + 0..3
 
   static constexpr int E = Elem<T>::kSize;
 
@@ -170,46 +184,92 @@ struct BwdWave {
     return r;
   }
 
-  __device__ __forceinline__ TileRaw load_tile(int g) const {
-    TileRaw r;
+  __device__ __forceinline__ TileRaw<S> load_tile(int g) const {
+    TileRaw<S> r;
     const uint32_t s = skip(max(g, 0) * kGB);
     const __amdgpu_buffer_rsrc_t rb = wB.at(s), rc = wC.at(s);
 #pragma unroll
-    for (int i = 0; i < kGB; ++i) {
-      r.b[i] = Elem<T>::load(rb, oB + i * kT * E);
-      r.c[i] = Elem<T>::load(rc, oC + i * kT * E);
+    for (int q = 0; q < S; ++q) {
+#pragma unroll
+      for (int i = 0; i < kGB; ++i) {
+        r.b[q][i] = Elem<T>::load(rb, oB[q] + i * kT * E);
+        r.c[q][i] = Elem<T>::load(rc, oC[q] + i * kT * E);
+      }
     }
     return r;
   }
 
   // Tile g into LDS buffer g & 1; B of tokens past the end is zeroed.
-  __device__ __forceinline__ void stage(int g, const TileRaw& r) const {
+  __device__ __forceinline__ void stage(int g, const TileRaw<S>& r) const {
     const int st = kRows * wave + row;
     const int t = g * kGT + col;
 #pragma unroll
-    for (int i = 0; i < kGB; ++i) {
-      sB[g & 1][st][col + i * kT] = t + i * kT < p.L ? Elem<T>::f32(r.b[i]) : 0.0f;
-      sC[g & 1][st][col + i * kT] = Elem<T>::f32(r.c[i]);
+    for (int q = 0; q < S; ++q) {
+#pragma unroll
+      for (int i = 0; i < kGB; ++i) {
+        sB[g & 1][st + kN * q][col + i * kT] = t + i * kT < p.L ? Elem<T>::f32(r.b[q][i]) : 0.0f;
+        sC[g & 1][st + kN * q][col + i * kT] = Elem<T>::f32(r.c[q][i]);
+      }
     }
   }
 
-  // Block k (all of it; k runs from nbk - 1 down to 0).  Q holds its owner
-  // inputs; g is the state lane's adjoint of the state leaving the block.
-  __device__ __forceinline__ void block(int k, const Raw& Q, float& g, float& dA, float& dDs,
-                                        float& dbs) const {
-    const int t0 = k * kT;
+  // B and C of slot q for the 16 tokens of block k, from the LDS tile.
+  __device__ __forceinline__ void tile_rows(int k, int q, float (&bv)[kT], float (&cv)[kT]) const {
     const int buf = (k / kGB) & 1;
     const int tb = (k % kGB) * kT;
-    float bv[kT], cv[kT];
 #pragma unroll
-    for (int q = 0; q < kT / 4; ++q) {
-      const float4 x = *reinterpret_cast<const float4*>(&sB[buf][col][tb + 4 * q]);
-      bv[4 * q] = x.x; bv[4 * q + 1] = x.y; bv[4 * q + 2] = x.z; bv[4 * q + 3] = x.w;
-      const float4 y = *reinterpret_cast<const float4*>(&sC[buf][col][tb + 4 * q]);
-      cv[4 * q] = y.x; cv[4 * q + 1] = y.y; cv[4 * q + 2] = y.z; cv[4 * q + 3] = y.w;
+    for (int i = 0; i < kT / 4; ++i) {
+      const float4 x = *reinterpret_cast<const float4*>(&sB[buf][col + kN * q][tb + 4 * i]);
+      bv[4 * i] = x.x; bv[4 * i + 1] = x.y; bv[4 * i + 2] = x.z; bv[4 * i + 3] = x.w;
+      const float4 y = *reinterpret_cast<const float4*>(&sC[buf][col + kN * q][tb + 4 * i]);
+      cv[4 * i] = y.x; cv[4 * i + 1] = y.y; cv[4 * i + 2] = y.z; cv[4 * i + 3] = y.w;
     }
-    const float hck = Elem<float>::f32(
-        __builtin_amdgcn_raw_buffer_load_b32(wck.at(static_cast<uint32_t>(k) * kN * 4), ock, 0, 0));
+  }
+
+  // The checkpoint of slot q: the state entering block k.
+  __device__ __forceinline__ float checkpoint(int k, int q) const {
+    return Elem<float>::f32(__builtin_amdgcn_raw_buffer_load_b32(
+        wck.at(static_cast<uint32_t>(k) * p.N * 4), ock[q], 0, 0));
+  }
+
+  // dB/dC of half h8 of block k, slot q: thread (tensor, n, t) sums the
+  // workgroup's channels from sQ (filled and synchronised by the caller) and
+  // stores or adds the sum.  Tokens past the end, and padding states,
+  // address the window's end, where the store or atomic is dropped: their
+  // offsets would otherwise reach into later states' rows, and a plain store
+  // there (the partial sums) races with the real value when the sequence is
+  // shorter than a block.
+  __device__ __forceinline__ void dbdc_sum(int k, int h8, int q) const {
+    const int tid = threadIdx.x;
+    const int ten = tid >> 7, n = (tid >> 3) & 15, t = tid & 7;
+    const int qr = 2 * ten + (t >> 2), qt = t & 3;
+    float sum = sQ[0][qr][n][qt];
+#pragma unroll
+    for (int v = 1; v < kWaves; ++v) sum += sQ[v][qr][n][qt];
+    const int tok = k * kT + 8 * h8 + t;
+    const int na = n + kN * q;
+    const uint32_t off =
+        static_cast<uint32_t>((tok < p.L && na < p.N ? na * p.L + tok : p.N * p.L) * 4);
+    // (a uniform branch)
+    if (partials)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), ten ? wdC.at(0) : wdB.at(0), off, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(sum, ten ? wdC.at(0) : wdB.at(0), off, 0, 0);
+  }
+
+  // Block k (all of it; k runs from nbk - 1 down to 0), one state slot.  Q
+  // holds its owner inputs; g is the state lane's adjoint of the state
+  // leaving the block.
+  __device__ __forceinline__ void block(int k, const Raw& Q, float (&ga)[S], float (&dAa)[S],
+                                        float& dDs, float& dbs) const {
+    static_assert(S == 1, "one state slot");
+    float& g = ga[0];
+    float& dA = dAa[0];
+    const float a = this->a[0], a2 = this->a2[0];
+    const int t0 = k * kT;
+    float bv[kT], cv[kT];
+    tile_rows(k, 0, bv, cv);
+    const float hck = checkpoint(k, 0);
 
     // owner: Delta, Delta u (zero past the end, so those steps are identities).
     // The mask is applied to the inputs (softplus(-inf) = 0) so that Delta
@@ -322,35 +382,176 @@ struct BwdWave {
           // the store is dropped
           Elem<T>::store(wdz.at(gate ? skip(k) : 0u), odz, dzv);
         }
-        // dB, dC: thread (tensor, n, t) sums the workgroup's channels
-        const int tid = threadIdx.x;
-        const int ten = tid >> 7, n = (tid >> 3) & 15, t = tid & 7;
-        const int qr = 2 * ten + (t >> 2), qt = t & 3;
-        float sum = sQ[0][qr][n][qt];
-#pragma unroll
-        for (int v = 1; v < kWaves; ++v) sum += sQ[v][qr][n][qt];
-        // Tokens past the end address the window's end, where the store or
-        // atomic is dropped: their offsets would otherwise reach into later
-        // states' rows, and a plain store there (the partial sums) races with
-        // the real value when the sequence is shorter than a block.
-        const int tok = t0 + 8 * h8 + t;
-        const uint32_t off = static_cast<uint32_t>((tok < p.L ? n * p.L + tok : kN * p.L) * 4);
-        // (a uniform branch)
-        if (partials)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), ten ? wdC.at(0) : wdB.at(0), off, 0, 0);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(sum, ten ? wdC.at(0) : wdB.at(0), off, 0, 0);
+        // dB, dC: summed over the workgroup's channels
+        dbdc_sum(k, h8, 0);
         __syncthreads();
       }
     });
   }
+
+  // Block k with several state slots.  The adjoint of each state needs every
+  // h_{t-1} and e_t of the block, 32 registers per slot, so the slots are
+  // taken one at a time (a loop that is not unrolled; the per-slot values
+  // rotate through index 0 of their arrays, so that every index stays
+  // static) and the forward is recomputed twice: once over all slots for the
+  // readout (y needs every state), once per slot right before its adjoint.
+  // The per-token sums over the states (for du and ddelta) accumulate over
+  // the slots in registers and go through LDS once per block; dB/dC go out
+  // per slot and half block as in the one-slot form.
+  template <typename V>
+  __device__ __forceinline__ static void rotate(V (&v)[S]) {
+    const V first = v[0];
+#pragma unroll
+    for (int q = 0; q + 1 < S; ++q) v[q] = v[q + 1];
+    v[S - 1] = first;
+  }
+
+  __device__ __forceinline__ void block_slots(int k, const Raw& Q, float (&g)[S], float (&dA)[S],
+                                              float& dDs, float& dbs) {
+    const int t0 = k * kT;
+    float hck[S];
+#pragma unroll
+    for (int q = 0; q < S; ++q) hck[q] = checkpoint(k, q);
+
+    // owner: Delta, Delta u (zero past the end, as in the one-slot form)
+    const bool own = t0 + col < p.L;
+    const float uv = own ? Elem<T>::f32(Q.u) : 0.0f;
+    const float x = Elem<T>::f32(Q.dt) + bias;
+    const float xm = own ? x : (kSoftplus ? -__builtin_inff() : 0.0f);
+    const float dl = kSoftplus ? softplus_f32(xm) : xm;
+    const float du = dl * uv;
+
+    // 1. readout partials sum_q C h_t of this lane's states, to LDS
+    {
+      float acc[kT];
+#pragma unroll
+      for (int j = 0; j < kT; ++j) acc[j] = 0.0f;
+#pragma unroll 1
+      for (int q = 0; q < S; ++q) {
+        float bv[kT], cv[kT];
+        tile_rows(k, q, bv, cv);
+        float h = hck[0];
+        static_for<0, kT>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          const float e = __builtin_amdgcn_exp2f(row_bcast<j>(dl) * a2[0]);
+          h = fmaf(e, h, row_bcast<j>(du) * bv[j]);
+          acc[j] = fmaf(cv[j], h, acc[j]);
+        });
+        rotate(hck);
+        rotate(a2);
+      }
+#pragma unroll
+      for (int i = 0; i < kT / 4; ++i)
+        *reinterpret_cast<float4*>(&sX[row][col * kXPitch<S> + 4 * i]) =
+            make_float4(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+
+    // 2. owner: y, dy, dz
+    float y = 0.0f;
+#pragma unroll
+    for (int n = 0; n < kN; ++n) y += sX[row][n * kXPitch<S> + col];
+    y = fmaf(Dd, uv, y);
+    const float zv = Elem<T>::f32(Q.z);
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zv * kLog2e));
+    const float go = own ? Elem<T>::f32(Q.dout) : 0.0f;
+    const float dy = gate ? go * zv * sg : go;
+    const float dzv = go * y * sg * fmaf(zv, 1.0f - sg, 1.0f);
+    dDs = fmaf(dy, uv, dDs);
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+
+    // 3. adjoint per slot, token 15 down to 0; channels past dim add nothing
+    // to dB/dC (their Delta u and dy copies for those terms are zero)
+    const bool rv = kRows * wave + row < nvalid;
+    const float du2 = rv ? du : 0.0f, dy2 = rv ? dy : 0.0f;
+    float s1[kT], s2[kT];   // sums over this lane's states of g B and g A e h_{t-1}
+#pragma unroll
+    for (int j = 0; j < kT; ++j) s1[j] = s2[j] = 0.0f;
+#pragma unroll 1
+    for (int q = 0; q < S; ++q) {
+      float bv[kT], cv[kT];
+      tile_rows(k, q, bv, cv);
+      float e[kT], hs[kT];
+      {
+        float h = hck[0];
+        static_for<0, kT>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          e[j] = __builtin_amdgcn_exp2f(row_bcast<j>(dl) * a2[0]);
+          h = fmaf(e[j], h, row_bcast<j>(du) * bv[j]);
+          hs[j] = h;
+        });
+      }
+      float yq[4], rq[4];
+      static_for<0, kT>([&](auto J) {
+        constexpr int j = kT - 1 - decltype(J)::value;
+        constexpr int h8 = j / 8;
+        constexpr int jj = j % 8;
+        const float adj = fmaf(row_bcast<j>(dy), cv[j], g[0]);           // adjoint of h_t
+        const float hp = j > 0 ? hs[j > 0 ? j - 1 : 0] : hck[0];          // h_{t-1}
+        const float qv = adj * (e[j] * hp);
+        s1[j] = fmaf(adj, bv[j], s1[j]);
+        s2[j] = fmaf(qv, a[0], s2[j]);
+        const float rb = row_bcast<j>(du2) * adj;                         // -> dB
+        const float rc = row_bcast<j>(dy2) * hs[j];                       // -> dC
+        if constexpr (jj >= 4) yq[jj - 4] = swap_add32(rb, rc);
+        else rq[jj] = swap_add16(swap_add32(rb, rc), yq[jj]);
+        dA[0] = fmaf(row_bcast<j>(dl), qv, dA[0]);
+        g[0] = e[j] * adj;                                                // adjoint of h_{t-1}
+        if constexpr (jj == 0) {
+          *reinterpret_cast<float4*>(&sQ[wave][row][col][0]) = make_float4(rq[0], rq[1], rq[2], rq[3]);
+          __syncthreads();
+          dbdc_sum(k, h8, q);
+          __syncthreads();
+        }
+      });
+      rotate(g);
+      rotate(dA);
+      rotate(hck);
+      rotate(a2);
+      rotate(a);
+    }
+
+    // 4. per-state terms of the 16 tokens to LDS ([c][n][0..15] g B,
+    // [c][n][16..31] g A e h_{t-1}); the owner of each token sums its 16
+    // lanes' terms into du and ddelta
+#pragma unroll
+    for (int i = 0; i < kT / 4; ++i) {
+      *reinterpret_cast<float4*>(&sX[row][col * kXPitch<S> + 4 * i]) =
+          make_float4(s1[4 * i], s1[4 * i + 1], s1[4 * i + 2], s1[4 * i + 3]);
+      *reinterpret_cast<float4*>(&sX[row][col * kXPitch<S> + kT + 4 * i]) =
+          make_float4(s2[4 * i], s2[4 * i + 1], s2[4 * i + 2], s2[4 * i + 3]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+    float S1 = 0.0f, S2 = 0.0f;
+#pragma unroll
+    for (int n = 0; n < kN; ++n) {
+      S1 += sX[row][n * kXPitch<S> + col];
+      S2 += sX[row][n * kXPitch<S> + kT + col];
+    }
+    const float duv = fmaf(dl, S1, dy * Dd);
+    float dx = fmaf(uv, S1, S2);
+    if (kSoftplus) dx *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+    dx = own ? dx : 0.0f;
+    dbs += dx;
+    if (own) {
+      Elem<T>::store(wdu.at(skip(k)), odu, duv);
+      Elem<T>::store(wdd.at(skip(k)), odd, dx);
+      Elem<T>::store(wdz.at(gate ? skip(k) : 0u), odz, dzv);
+    }
+    // the next block's readout rewrites sX
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+  }
 };
 
-template <typename T, bool kSoftplus>
+template <typename T, bool kSoftplus, int S>
 __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
-  __shared__ __align__(16) float sB[2][kN][kGPitch];
-  __shared__ __align__(16) float sC[2][kN][kGPitch];
-  __shared__ __align__(16) float sX[kWaves][kRows][kPartRow];
+  __shared__ __align__(16) float sB[2][kN * S][kGPitch];
+  __shared__ __align__(16) float sC[2][kN * S][kGPitch];
+  __shared__ __align__(16) float sX[kWaves][kRows][kXRow<S>];
   __shared__ __align__(16) float sQ[kWaves][kRows][kN][4];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -367,9 +568,10 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   const int64_t dc = vrow ? d : p.dim - 1;
   const int64_t dw0 = std::min<int64_t>(cg * kCh + kRows * wave, p.dim - 1);
   const int64_t dw3 = std::min<int64_t>(dw0 + kRows - 1, p.dim - 1);
+  const int N = p.N;
 
   constexpr int E = Elem<T>::kSize;
-  BwdWave<T, kSoftplus> w{p};
+  BwdWave<T, kSoftplus, S> w{p};
   w.wave = wave; w.row = row; w.col = col;
   w.nbk = p.nbk;
   w.ntile = (p.nbk + kGB - 1) / kGB;
@@ -396,28 +598,32 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   // the workgroup's 16 channels share one B/C group
   const int64_t grp = (cg * kCh) / p.cpg;
   const int st = kRows * wave + row;
-  w.oB = static_cast<uint32_t>((st * p.Bsn + col) * E);
   w.wB = Window{static_cast<const char*>(p.B) + (b * p.Bsb + grp * p.Bsg) * E,
-                static_cast<uint32_t>(((kN - 1) * p.Bsn + p.L) * E)};
-  w.oC = static_cast<uint32_t>((st * p.Csn + col) * E);
+                static_cast<uint32_t>(((N - 1) * p.Bsn + p.L) * E)};
   w.wC = Window{static_cast<const char*>(p.C) + (b * p.Csb + grp * p.Csg) * E,
-                static_cast<uint32_t>(((kN - 1) * p.Csn + p.L) * E)};
-  const int64_t ckrow = static_cast<int64_t>(p.nbk) * kN;
-  w.ock = static_cast<uint32_t>(((dc - dw0) * ckrow + col) * 4);
+                static_cast<uint32_t>(((N - 1) * p.Csn + p.L) * E)};
+  const int64_t ckrow = static_cast<int64_t>(p.nbk) * N;
   w.wck = Window{reinterpret_cast<const char*>(p.ckpt + (b * p.dim + dw0) * ckrow),
                  static_cast<uint32_t>((dw3 - dw0 + 1) * ckrow * 4)};
+#pragma unroll
+  for (int q = 0; q < S; ++q) {
+    const int ns = st + kN * q;     // the state this lane stages
+    w.oB[q] = ns < N ? static_cast<uint32_t>((ns * p.Bsn + col) * E) : w.wB.bytes;
+    w.oC[q] = ns < N ? static_cast<uint32_t>((ns * p.Csn + col) * E) : w.wC.bytes;
+    const int n = col + kN * q;     // the state this lane carries
+    w.ock[q] = n < N ? static_cast<uint32_t>(((dc - dw0) * ckrow + n) * 4) : w.wck.bytes;
+    w.a[q] = n < N ? p.A[dc * p.Asd + n * p.Asn] : 0.0f;
+    w.a2[q] = w.a[q] * kLog2e;
+  }
   // dB/dC: this workgroup's slots of the partial sums, or the group's rows
   // of dB/dC themselves (atomics)
-  const float* pB = p.part ? p.part + ((b * p.cgroups + cg) * 2 + 0) * kN * p.L
-                           : p.dB + (b * p.ngroups + grp) * kN * p.L;
-  const float* pC = p.part ? p.part + ((b * p.cgroups + cg) * 2 + 1) * kN * p.L
-                           : p.dC + (b * p.ngroups + grp) * kN * p.L;
-  w.wdB = Window{reinterpret_cast<const char*>(pB), static_cast<uint32_t>(kN * p.L * 4)};
-  w.wdC = Window{reinterpret_cast<const char*>(pC), static_cast<uint32_t>(kN * p.L * 4)};
+  const int64_t NL = static_cast<int64_t>(N) * p.L;
+  const float* pB = p.part ? p.part + ((b * p.cgroups + cg) * 2 + 0) * NL : p.dB + (b * p.ngroups + grp) * NL;
+  const float* pC = p.part ? p.part + ((b * p.cgroups + cg) * 2 + 1) * NL : p.dC + (b * p.ngroups + grp) * NL;
+  w.wdB = Window{reinterpret_cast<const char*>(pB), static_cast<uint32_t>(NL * 4)};
+  w.wdC = Window{reinterpret_cast<const char*>(pC), static_cast<uint32_t>(NL * 4)};
   w.partials = p.part != nullptr;
 
-  w.a = p.A[dc * p.Asd + col * p.Asn];
-  w.a2 = w.a * kLog2e;
   w.bias = p.bias ? p.bias[dc] : 0.0f;
   w.Dd = p.D ? p.D[dc] : 0.0f;
   w.sB = sB; w.sC = sC; w.sX = sX[wave]; w.sQ = sQ;
@@ -425,13 +631,22 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   // The adjoint entering the segment from the right: dlast, folded with the
   // aggregates of the later segments (segment i turns K into
   // alpha_i + exp(A S_i) K).
-  float g = p.dlast ? p.dlast[(b * p.dim + dc) * kN + col] : 0.0f;
-  if (seg < p.nseg - 1) {
-    const float* ag = p.agg + (b * p.dim + dc) * p.nseg * (kN + 1);
-    for (int i = p.nseg - 1; i > seg; --i)
-      g = fmaf(__builtin_amdgcn_exp2f(w.a2 * ag[i * (kN + 1) + kN]), g, ag[i * (kN + 1) + col]);
+  float g[S], dA[S];
+#pragma unroll
+  for (int q = 0; q < S; ++q) {
+    const int n = col + kN * q;
+    g[q] = 0.0f;
+    dA[q] = 0.0f;
+    if (n < N) {
+      g[q] = p.dlast ? p.dlast[(b * p.dim + dc) * N + n] : 0.0f;
+      if (seg < p.nseg - 1) {
+        const float* ag = p.agg + (b * p.dim + dc) * p.nseg * (N + 1);
+        for (int i = p.nseg - 1; i > seg; --i)
+          g[q] = fmaf(__builtin_amdgcn_exp2f(w.a2[q] * ag[i * (N + 1) + N]), g[q], ag[i * (N + 1) + n]);
+      }
+    }
   }
-  float dA = 0.0f, dDs = 0.0f, dbs = 0.0f;
+  float dDs = 0.0f, dbs = 0.0f;
 
   // this segment's blocks [kbeg, kend), walked from the last; segment
   // starts are multiples of a tile
@@ -440,14 +655,15 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   // the last tile first; owner inputs of block k in buffer k % 2, the next
   // (earlier) one loading meanwhile
   const int tl = (kend - 1) / kGB;
-  TileRaw tile = w.load_tile(tl);
+  TileRaw<S> tile = w.load_tile(tl);
   w.stage(tl, tile);
   tile = w.load_tile(tl - 1);
   __syncthreads();
   Raw cur = w.load(kend - 1);
   for (int k = kend - 1; k >= kbeg; --k) {
     const Raw next = w.load(k - 1);
-    w.block(k, cur, g, dA, dDs, dbs);
+    if constexpr (S == 1) w.block(k, cur, g, dA, dDs, dbs);
+    else w.block_slots(k, cur, g, dA, dDs, dbs);
     if (k % kGB == 0 && k > kbeg) {
       // tile (k / kGB) - 1 into the other buffer; every wavefront finished
       // reading it before the barrier at the end of the previous block
@@ -458,11 +674,15 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     cur = next;
   }
 
-  if (vrow && p.dh0 && seg == 0) p.dh0[(b * p.dim + d) * kN + col] = g;
   const int64_t slot = seg * p.batch * p.dim + b * p.dim + d;   // per segment and batch row
-  if (vrow) {
-    if (p.pdA) p.pdA[slot * kN + col] = dA;
-    else atomicAdd(&p.dA[d * kN + col], dA);
+#pragma unroll
+  for (int q = 0; q < S; ++q) {
+    const int n = col + kN * q;
+    if (vrow && n < N) {
+      if (p.dh0 && seg == 0) p.dh0[(b * p.dim + d) * N + n] = g[q];
+      if (p.pdA) p.pdA[slot * N + n] = dA[q];
+      else atomicAdd(&p.dA[d * N + n], dA[q]);
+    }
   }
   // dD and the bias gradient: sum the 16 owner lanes of the row
 #pragma unroll
@@ -483,16 +703,16 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 
 // Pass 1 of a segmented backward: the adjoint recurrence alone over segment
 // s (1..nseg-1) from a zero adjoint at its end.  Lane (row c, col n) carries
-// the adjoint of state n of channel c; owner lane (row c, col j) forms dy
-// (dout through the gate) and Delta of token j of each block, handed to the
-// state lanes by DPP row broadcasts; C comes through the same double-buffered
-// LDS tiles as in the full backward.  Per token t, walking down:
-// g <- exp(Delta_t A) (dy_t C_t + g).  What leaves the segment at its start,
-// alpha_s = g, and the step-size sum S_s (fp64 per owner, summed by a lane
-// butterfly) go to agg[b][d][s].
-template <typename T, bool kSoftplus>
+// the adjoints of states n, n + 16, ... of channel c; owner lane (row c, col
+// j) forms dy (dout through the gate) and Delta of token j of each block,
+// handed to the state lanes by DPP row broadcasts; C comes through the same
+// double-buffered LDS tiles as in the full backward.  Per token t, walking
+// down: g <- exp(Delta_t A) (dy_t C_t + g).  What leaves the segment at its
+// start, alpha_s = g, and the step-size sum S_s (fp64 per owner, summed by a
+// lane butterfly) go to agg[b][d][s].
+template <typename T, bool kSoftplus, int S>
 __global__ __launch_bounds__(kThreads) void bwd_aggregate_kernel(BwdParams p) {
-  __shared__ __align__(16) float sC[2][kN][kGPitch];
+  __shared__ __align__(16) float sC[2][kN * S][kGPitch];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = (threadIdx.x >> 4) & 3;
   const int col = threadIdx.x & 15;
@@ -509,6 +729,7 @@ __global__ __launch_bounds__(kThreads) void bwd_aggregate_kernel(BwdParams p) {
   const int64_t dw3 = std::min<int64_t>(dw0 + kRows - 1, p.dim - 1);
   constexpr int E = Elem<T>::kSize;
   const bool gate = p.z != nullptr;
+  const int N = p.N;
 
   auto rows_window = [&](const void* base, int64_t sb, int64_t sd, uint32_t& off) {
     off = static_cast<uint32_t>(((dc - dw0) * sd + col) * E);
@@ -522,10 +743,16 @@ __global__ __launch_bounds__(kThreads) void bwd_aggregate_kernel(BwdParams p) {
   if (!gate) oz = odt;   // loaded, never used
   const int64_t grp = (cg * kCh) / p.cpg;
   const int st = kRows * wave + row;
-  const uint32_t oC = static_cast<uint32_t>((st * p.Csn + col) * E);
   const Window wC{static_cast<const char*>(p.C) + (b * p.Csb + grp * p.Csg) * E,
-                  static_cast<uint32_t>(((kN - 1) * p.Csn + p.L) * E)};
-  const float a2 = p.A[dc * p.Asd + col * p.Asn] * kLog2e;
+                  static_cast<uint32_t>(((N - 1) * p.Csn + p.L) * E)};
+  uint32_t oC[S];
+  float a2[S];
+#pragma unroll
+  for (int q = 0; q < S; ++q) {
+    const int ns = st + kN * q, n = col + kN * q;
+    oC[q] = ns < N ? static_cast<uint32_t>((ns * p.Csn + col) * E) : wC.bytes;
+    a2[q] = n < N ? p.A[dc * p.Asd + n * p.Asn] * kLog2e : 0.0f;
+  }
   const float bias = p.bias ? p.bias[dc] : 0.0f;
 
   auto skip = [](int k) { return static_cast<uint32_t>(k * kT) * E; };
@@ -535,25 +762,31 @@ __global__ __launch_bounds__(kThreads) void bwd_aggregate_kernel(BwdParams p) {
     return In{Elem<T>::load(wdt.at(s), odt), Elem<T>::load(wz.at(s), oz),
               Elem<T>::load(wg.at(s), og)};
   };
-  auto load_tile = [&](int t, uint32_t (&c)[kGB]) {
+  auto load_tile = [&](int t, uint32_t (&c)[S][kGB]) {
     const __amdgpu_buffer_rsrc_t rc = wC.at(skip(max(t, 0) * kGB));
 #pragma unroll
-    for (int i = 0; i < kGB; ++i) c[i] = Elem<T>::load(rc, oC + i * kT * E);
-  };
-  auto stage = [&](int t, const uint32_t (&c)[kGB]) {
+    for (int q = 0; q < S; ++q)
 #pragma unroll
-    for (int i = 0; i < kGB; ++i) sC[t & 1][st][col + i * kT] = Elem<T>::f32(c[i]);
+      for (int i = 0; i < kGB; ++i) c[q][i] = Elem<T>::load(rc, oC[q] + i * kT * E);
+  };
+  auto stage = [&](int t, const uint32_t (&c)[S][kGB]) {
+#pragma unroll
+    for (int q = 0; q < S; ++q)
+#pragma unroll
+      for (int i = 0; i < kGB; ++i) sC[t & 1][st + kN * q][col + i * kT] = Elem<T>::f32(c[q][i]);
   };
 
   const int kbeg = seg * (p.seg_len / kT);
   const int kend = std::min(p.nbk, kbeg + p.seg_len / kT);
   const int tl = (kend - 1) / kGB;
-  uint32_t tile[kGB];
+  uint32_t tile[S][kGB];
   load_tile(tl, tile);
   stage(tl, tile);
   load_tile(tl - 1, tile);
   __syncthreads();
-  float g = 0.0f;
+  float g[S];
+#pragma unroll
+  for (int q = 0; q < S; ++q) g[q] = 0.0f;
   double ssum = 0.0;
   In cur = load(kend - 1);
   for (int k = kend - 1; k >= kbeg; --k) {
@@ -561,12 +794,6 @@ __global__ __launch_bounds__(kThreads) void bwd_aggregate_kernel(BwdParams p) {
     const int t0 = k * kT;
     const int buf = (k / kGB) & 1;
     const int tb = (k % kGB) * kT;
-    float cv[kT];
-#pragma unroll
-    for (int q = 0; q < kT / 4; ++q) {
-      const float4 y = *reinterpret_cast<const float4*>(&sC[buf][col][tb + 4 * q]);
-      cv[4 * q] = y.x; cv[4 * q + 1] = y.y; cv[4 * q + 2] = y.z; cv[4 * q + 3] = y.w;
-    }
     // owner: Delta (zero past the end: softplus(-inf) = 0) and dy
     const bool own = t0 + col < p.L;
     const float x = Elem<T>::f32(cur.dt) + bias;
@@ -577,10 +804,19 @@ __global__ __launch_bounds__(kThreads) void bwd_aggregate_kernel(BwdParams p) {
     const float go = own ? Elem<T>::f32(cur.go) : 0.0f;
     const float dy = gate ? go * zv * sg : go;
     ssum += static_cast<double>(dl);
-    static_for<0, kT>([&](auto J) {
-      constexpr int j = kT - 1 - decltype(J)::value;
-      const float adj = fmaf(row_bcast<j>(dy), cv[j], g);
-      g = __builtin_amdgcn_exp2f(row_bcast<j>(dl) * a2) * adj;
+    static_for<0, S>([&](auto Qs) {
+      constexpr int q = decltype(Qs)::value;
+      float cv[kT];
+#pragma unroll
+      for (int i = 0; i < kT / 4; ++i) {
+        const float4 y = *reinterpret_cast<const float4*>(&sC[buf][col + kN * q][tb + 4 * i]);
+        cv[4 * i] = y.x; cv[4 * i + 1] = y.y; cv[4 * i + 2] = y.z; cv[4 * i + 3] = y.w;
+      }
+      static_for<0, kT>([&](auto J) {
+        constexpr int j = kT - 1 - decltype(J)::value;
+        const float adj = fmaf(row_bcast<j>(dy), cv[j], g[q]);
+        g[q] = __builtin_amdgcn_exp2f(row_bcast<j>(dl) * a2[q]) * adj;
+      });
     });
     if (k % kGB == 0 && k > kbeg) {
       // the other buffer held tile k / kGB + 1, which every wavefront
@@ -594,20 +830,24 @@ __global__ __launch_bounds__(kThreads) void bwd_aggregate_kernel(BwdParams p) {
 #pragma unroll
   for (int m = 1; m < kN; m <<= 1) ssum += __shfl_xor(ssum, m, kN);
   if (vrow) {
-    float* ag = p.agg + ((b * p.dim + d) * p.nseg + seg) * (kN + 1);
-    ag[col] = g;
-    if (col == 0) ag[kN] = static_cast<float>(ssum);
+    float* ag = p.agg + ((b * p.dim + d) * p.nseg + seg) * (N + 1);
+#pragma unroll
+    for (int q = 0; q < S; ++q) {
+      const int n = col + kN * q;
+      if (n < N) ag[n] = g[q];
+    }
+    if (col == 0) ag[N] = static_cast<float>(ssum);
   }
 }
 
 // dA, dD and the bias gradient from the partials per segment and batch row
 // (`rows` = nseg * batch of them), summed in slot order.
 __global__ void param_sum_kernel(const float* pdA, const float* pdD, const float* pdb, float* dA,
-                                 float* dD, float* dbias, int64_t rows, int64_t dim) {
+                                 float* dD, float* dbias, int64_t rows, int64_t dim, int64_t N) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < dim * kN) {
+  if (i < dim * N) {
     float s = 0.0f;
-    for (int64_t b = 0; b < rows; ++b) s += pdA[b * dim * kN + i];
+    for (int64_t b = 0; b < rows; ++b) s += pdA[b * dim * N + i];
     dA[i] = s;
   }
   if (i < dim) {
@@ -688,9 +928,9 @@ bool scan_bwd_windows_fit(const ssm_scan_bwd_args& a) {
             fits(rows * a.dout_dim_stride + a.seqlen, esz) &&
             fits(rows * a.du_dim_stride + a.seqlen, esz) &&
             fits(rows * a.ddelta_dim_stride + a.seqlen, esz) &&
-            fits((kN - 1) * a.B_state_stride + a.seqlen, esz) &&
-            fits((kN - 1) * a.C_state_stride + a.seqlen, esz) &&
-            fits(kN * a.seqlen, 4) && fits((rows + 1) * nbk * kN, 4);
+            fits((a.dstate - 1) * a.B_state_stride + a.seqlen, esz) &&
+            fits((a.dstate - 1) * a.C_state_stride + a.seqlen, esz) &&
+            fits(a.dstate * a.seqlen, 4) && fits((rows + 1) * nbk * a.dstate, 4);
   if (a.z) ok = ok && fits(rows * a.z_dim_stride + a.seqlen, esz) &&
                 fits(rows * a.dz_dim_stride + a.seqlen, esz);
   return ok;
@@ -729,11 +969,39 @@ size_t scan_bwd_workspace_bytes(const ssm_scan_bwd_args& a) {
   const int64_t nseg = bwd_segments(a.batch * cgroups, a.seqlen);
   // dB/dC partials per channel block, then dA, dD and the bias gradient per
   // segment and batch row, then (segmented) the adjoint aggregates
-  return static_cast<size_t>(a.batch * cgroups * 2 * kN * a.seqlen +
-                             nseg * a.batch * a.dim * (kN + 2) +
-                             (nseg > 1 ? a.batch * a.dim * nseg * (kN + 1) : 0)) *
+  const int64_t N = a.dstate;
+  return static_cast<size_t>(a.batch * cgroups * 2 * N * a.seqlen +
+                             nseg * a.batch * a.dim * (N + 2) +
+                             (nseg > 1 ? a.batch * a.dim * nseg * (N + 1) : 0)) *
          sizeof(float);
 }
+
+namespace {
+
+// The backward (or, kAgg, its segment aggregate pass) with S state slots.
+template <int S, bool kAgg>
+void launch_bwd(bool bf16, bool softplus, dim3 grid, const BwdParams& p, hipStream_t stream) {
+  const dim3 block(kThreads);
+  if constexpr (kAgg) {
+    if (bf16) {
+      if (softplus) bwd_aggregate_kernel<uint16_t, true, S><<<grid, block, 0, stream>>>(p);
+      else bwd_aggregate_kernel<uint16_t, false, S><<<grid, block, 0, stream>>>(p);
+    } else {
+      if (softplus) bwd_aggregate_kernel<float, true, S><<<grid, block, 0, stream>>>(p);
+      else bwd_aggregate_kernel<float, false, S><<<grid, block, 0, stream>>>(p);
+    }
+  } else {
+    if (bf16) {
+      if (softplus) scan_bwd_kernel<uint16_t, true, S><<<grid, block, 0, stream>>>(p);
+      else scan_bwd_kernel<uint16_t, false, S><<<grid, block, 0, stream>>>(p);
+    } else {
+      if (softplus) scan_bwd_kernel<float, true, S><<<grid, block, 0, stream>>>(p);
+      else scan_bwd_kernel<float, false, S><<<grid, block, 0, stream>>>(p);
+    }
+  }
+}
+
+}  // namespace
 
 hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
   const int64_t G = a.ngroups > 1 ? a.ngroups : 1;
@@ -775,8 +1043,8 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
     p.seg_len = static_cast<int>((seg + kGT - 1) / kGT * kGT);
     p.nseg = static_cast<int>((a.seqlen + p.seg_len - 1) / p.seg_len);
   }
-  p.pdA = partials ? p.part + a.batch * cgroups * 2 * kN * a.seqlen : nullptr;
-  p.pdD = partials ? p.pdA + p.nseg * a.batch * a.dim * kN : nullptr;
+  p.pdA = partials ? p.part + a.batch * cgroups * 2 * a.dstate * a.seqlen : nullptr;
+  p.pdD = partials ? p.pdA + p.nseg * a.batch * a.dim * a.dstate : nullptr;
   p.pdb = partials ? p.pdD + p.nseg * a.batch * a.dim : nullptr;
   p.agg = partials && p.nseg > 1 ? p.pdb + p.nseg * a.batch * a.dim : nullptr;
   p.usb = a.u_batch_stride; p.usd = a.u_dim_stride;
@@ -792,34 +1060,29 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
   p.ddsb = a.ddelta_batch_stride; p.ddsd = a.ddelta_dim_stride;
   p.dzsb = a.dz_batch_stride; p.dzsd = a.dz_dim_stride;
   p.batch = a.batch; p.dim = a.dim; p.L = static_cast<int>(a.seqlen);
+  p.N = static_cast<int>(a.dstate);
   p.nbk = static_cast<int>((a.seqlen + kT - 1) / kT);
   p.cgroups = (a.dim + kCh - 1) / kCh;
   const dim3 grid(static_cast<unsigned>(a.batch * p.cgroups * p.nseg)), block(kThreads);
-  const bool sp = a.delta_softplus != 0;
+  const bool sp = a.delta_softplus != 0, bf = a.io_dtype == SSM_BF16;
+  const int S = a.dstate <= 16 ? 1 : a.dstate <= 32 ? 2 : 4;   // state slots per lane
   if (p.nseg > 1) {
     // pass 1: the adjoint aggregates of segments 1..nseg-1
     const dim3 agrid(static_cast<unsigned>(a.batch * p.cgroups * (p.nseg - 1)));
-    if (a.io_dtype == SSM_BF16) {
-      if (sp) bwd_aggregate_kernel<uint16_t, true><<<agrid, block, 0, stream>>>(p);
-      else bwd_aggregate_kernel<uint16_t, false><<<agrid, block, 0, stream>>>(p);
-    } else {
-      if (sp) bwd_aggregate_kernel<float, true><<<agrid, block, 0, stream>>>(p);
-      else bwd_aggregate_kernel<float, false><<<agrid, block, 0, stream>>>(p);
-    }
+    if (S == 1) launch_bwd<1, true>(bf, sp, agrid, p, stream);
+    else if (S == 2) launch_bwd<2, true>(bf, sp, agrid, p, stream);
+    else launch_bwd<4, true>(bf, sp, agrid, p, stream);
   }
-  if (a.io_dtype == SSM_BF16) {
-    if (sp) scan_bwd_kernel<uint16_t, true><<<grid, block, 0, stream>>>(p);
-    else scan_bwd_kernel<uint16_t, false><<<grid, block, 0, stream>>>(p);
-  } else {
-    if (sp) scan_bwd_kernel<float, true><<<grid, block, 0, stream>>>(p);
-    else scan_bwd_kernel<float, false><<<grid, block, 0, stream>>>(p);
-  }
+  if (S == 1) launch_bwd<1, false>(bf, sp, grid, p, stream);
+  else if (S == 2) launch_bwd<2, false>(bf, sp, grid, p, stream);
+  else launch_bwd<4, false>(bf, sp, grid, p, stream);
   if (partials) {
-    // NL = 16 * seqlen: a multiple of 4, so float4 only needs aligned bases
-    const int64_t NL = kN * a.seqlen;
+    // NL = dstate * seqlen; float4 when the bases are 16-byte aligned and NL
+    // is a multiple of 4
+    const int64_t NL = a.dstate * a.seqlen;
     auto al16 = [](const void* ptr) { return reinterpret_cast<uintptr_t>(ptr) % 16 == 0; };
     const dim3 sblock(kSumCols, kSumRows);
-    if (al16(p.part) && al16(a.dB) && al16(a.dC)) {
+    if (al16(p.part) && al16(a.dB) && al16(a.dC) && NL % 4 == 0) {
       const int64_t cols = (NL / 4 + kSumCols - 1) / kSumCols;
       partial_sum_kernel<float4><<<dim3(static_cast<unsigned>(cols), static_cast<unsigned>(a.batch * G)),
                                    sblock, 0, stream>>>(p.part, a.dB, a.dC, NL, p.cgroups, G);
@@ -828,8 +1091,8 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
       partial_sum_kernel<float><<<dim3(static_cast<unsigned>(cols), static_cast<unsigned>(a.batch * G)),
                                   sblock, 0, stream>>>(p.part, a.dB, a.dC, NL, p.cgroups, G);
     }
-    param_sum_kernel<<<dim3(static_cast<unsigned>((a.dim * kN + 255) / 256)), dim3(256), 0, stream>>>(
-        p.pdA, p.pdD, p.pdb, a.dA, a.dD, a.ddelta_bias, p.nseg * a.batch, a.dim);
+    param_sum_kernel<<<dim3(static_cast<unsigned>((a.dim * a.dstate + 255) / 256)), dim3(256), 0, stream>>>(
+        p.pdA, p.pdD, p.pdb, a.dA, a.dD, a.ddelta_bias, p.nseg * a.batch, a.dim, a.dstate);
   }
   return hipGetLastError();
 }

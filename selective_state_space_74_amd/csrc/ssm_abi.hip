@@ -76,8 +76,8 @@ size_t ssm_ssd_workspace_size(const ssm_ssd_args* a) {
 }
 
 size_t ssm_scan_bwd_workspace_size(const ssm_scan_bwd_args* a) {
-  if (!a || a->dstate != 16 || a->seqlen > kMaxSeqlen || a->batch < 0 || a->dim < 0 ||
-      a->seqlen < 0)
+  if (!a || a->dstate < 1 || a->dstate > SSM_MAX_DSTATE || a->seqlen > kMaxSeqlen || a->batch < 0 ||
+      a->dim < 0 || a->seqlen < 0)
     return 0;
   return ssm::scan_bwd_workspace_bytes(*a);
 }
@@ -183,7 +183,7 @@ int ssm_validate_scan_bwd(const ssm_scan_bwd_args* a) {
   if (a->batch < 0 || a->dim < 0 || a->seqlen < 0 || a->dstate < 1) return SSM_ERR_SHAPE;
   if (bad_groups(a->ngroups, a->dim)) return SSM_ERR_SHAPE;
   if (a->io_dtype != SSM_F32 && a->io_dtype != SSM_BF16) return SSM_ERR_DTYPE;
-  if (a->dstate != 16) return SSM_ERR_UNSUPPORTED;
+  if (a->dstate > SSM_MAX_DSTATE) return SSM_ERR_UNSUPPORTED;
   // every block of 16 channels must sit in one group
   if (groups_of(a->ngroups) > 1 && (a->dim / groups_of(a->ngroups)) % 16 != 0)
     return SSM_ERR_UNSUPPORTED;

@@ -287,12 +287,12 @@ def good_bwd(batch=2, dim=32, L=64, N=16, io=0, z=True):
 
 def test_bwd_workspace_size():
     """The backward workspace: the dB/dC partials (batch * blocks of 16
-    channels * 2 * 16 * L fp32 values) and the per-batch-row dA, dD and bias
-    gradients (batch * dim * 18), for any grouping; none for an empty
-    sequence, for more than 65535 (batch, group) rows, or for shapes the
-    backward does not take."""
-    def want(batch, dim, L):
-        return (batch * -(-dim // 16) * 2 * 16 * L + batch * dim * 18) * 4
+    channels * 2 * N * L fp32 values) and the per-batch-row dA, dD and bias
+    gradients (batch * dim * (N + 2)), for any grouping and state size; none
+    for an empty sequence, for more than 65535 (batch, group) rows, or for
+    state sizes the backward does not take."""
+    def want(batch, dim, L, N=16):
+        return (batch * -(-dim // 16) * 2 * N * L + batch * dim * (N + 2)) * 4
     assert ssm.scan_bwd_workspace_size(good_bwd(batch=2, dim=96 * 16, L=64)) == want(2, 96 * 16, 64)
     assert ssm.scan_bwd_workspace_size(good_bwd(batch=1, dim=5, L=3)) == want(1, 5, 3)
     a = good_bwd(batch=2, dim=320 * 16, L=64)
@@ -301,17 +301,19 @@ def test_bwd_workspace_size():
     assert ssm.scan_bwd_workspace_size(a) == want(2, 320 * 16, 64)
     assert ssm.scan_bwd_workspace_size(good_bwd(batch=70000, dim=16, L=4)) == 0
     assert ssm.scan_bwd_workspace_size(good_bwd(dim=320 * 16, L=0)) == 0
-    assert ssm.scan_bwd_workspace_size(good_bwd(dim=320 * 16, N=32)) == 0
+    assert ssm.scan_bwd_workspace_size(good_bwd(dim=320 * 16, N=32)) == want(2, 320 * 16, 64, 32)
+    assert ssm.scan_bwd_workspace_size(good_bwd(dim=320 * 16, N=5)) == want(2, 320 * 16, 64, 5)
+    assert ssm.scan_bwd_workspace_size(good_bwd(dim=320 * 16, N=65)) == 0
 
 
 def test_bwd_segmented_workspace_size():
     """Long sequences with few channel blocks are cut into G segments (up to
     768 workgroups, segments of at least 8192 tokens, at most 64): the
     per-row parameter slots are per segment, and the adjoint aggregates
-    (17 floats per channel and segment) follow."""
-    def want(batch, dim, L, G):
-        return (batch * -(-dim // 16) * 2 * 16 * L + G * batch * dim * 18 +
-                (batch * dim * G * 17 if G > 1 else 0)) * 4
+    (N + 1 floats per channel and segment) follow."""
+    def want(batch, dim, L, G, N=16):
+        return (batch * -(-dim // 16) * 2 * N * L + G * batch * dim * (N + 2) +
+                (batch * dim * G * (N + 1) if G > 1 else 0)) * 4
     L = 3 * 8192 + 100
     assert ssm.scan_bwd_workspace_size(good_bwd(batch=1, dim=16, L=L)) == want(1, 16, L, 3)
     assert ssm.scan_bwd_workspace_size(good_bwd(batch=1, dim=1536, L=1 << 20)) == \
@@ -320,6 +322,7 @@ def test_bwd_segmented_workspace_size():
         want(1, 16, 1 << 20, 64)
     assert ssm.scan_bwd_workspace_size(good_bwd(batch=8, dim=1536, L=1 << 16)) == \
         want(8, 1536, 1 << 16, 1)
+    assert ssm.scan_bwd_workspace_size(good_bwd(batch=1, dim=16, L=L, N=64)) == want(1, 16, L, 3, 64)
 
 
 def test_bwd_workspace_alias_and_alignment():
@@ -334,6 +337,8 @@ def test_bwd_workspace_alias_and_alignment():
 
 def test_bwd_valid_block_passes():
     assert ssm.validate_scan_bwd(good_bwd()) == OK
+    for N in (1, 8, 32, 64):
+        assert ssm.validate_scan_bwd(good_bwd(N=N)) == OK, N
     assert ssm.validate_scan_bwd(good_bwd(io=1)) == OK
     assert ssm.validate_scan_bwd(good_bwd(z=False)) == OK
 
@@ -354,7 +359,7 @@ def test_bwd_optional_pointers(field):
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("dstate", 8, UNSUP), ("dstate", 32, UNSUP), ("io_dtype", 3, DTYPE), ("seqlen", -2, SHAPE),
+    ("dstate", 65, UNSUP), ("dstate", 0, SHAPE), ("io_dtype", 3, DTYPE), ("seqlen", -2, SHAPE),
     ("ngroups", 3, SHAPE), ("ngroups", 4, UNSUP), ("ngroups", 32, UNSUP),
     ("dout_dim_stride", -1, STRIDE), ("du_batch_stride", -1, STRIDE),
 ])

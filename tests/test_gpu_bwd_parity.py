@@ -29,22 +29,22 @@ TOL_BWD = {"f32": 1e-4, "bf16": 2e-2}
 
 
 def run(batch, dim, L, io, seed, gate=True, skip=True, bias=True, softplus=True, h0=True,
-        dlast=True, workspace=None):
-    inp = si.scan_inputs(batch, dim, L, io_dtype=io, seed=seed)
+        dlast=True, workspace=None, N=16, G=0):
+    inp = si.scan_inputs(batch, dim, L, dstate=N, io_dtype=io, seed=seed, ngroups=G)
     if not softplus:
         # Delta = delta + bias taken as is: keep it positive (a negative step
         # makes exp(Delta A) grow without bound)
         inp["delta"] = np.abs(inp["delta"]) + np.float32(0.01)
         inp["delta_bias"] = np.abs(inp["delta_bias"]) * np.float32(0.01)
     rng = np.random.default_rng(seed + 1000)
-    h0v = rng.standard_normal((batch, dim, 16)).astype(np.float32) if h0 else None
+    h0v = rng.standard_normal((batch, dim, N)).astype(np.float32) if h0 else None
     dout = si.bf16_round(rng.standard_normal((batch, dim, L)).astype(np.float32)) if io == "bf16" \
         else rng.standard_normal((batch, dim, L)).astype(np.float32)
-    dl = rng.standard_normal((batch, dim, 16)).astype(np.float32) if dlast else None
+    dl = rng.standard_normal((batch, dim, N)).astype(np.float32) if dlast else None
     t = si.to_torch(inp, DEV)
     tio = t["u"].dtype
     h0t = None if h0v is None else torch.from_numpy(h0v).to(DEV)
-    ck = torch.empty(ssm.checkpoint_shape(batch, dim, L), dtype=torch.float32, device=DEV)
+    ck = torch.empty(ssm.checkpoint_shape(batch, dim, L, N), dtype=torch.float32, device=DEV)
     kw = dict(D=t["D"] if skip else None, z=t["z"] if gate else None,
               delta_bias=t["delta_bias"] if bias else None, delta_softplus=softplus, h0=h0t)
     ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], checkpoints=ck, **kw)
@@ -281,3 +281,27 @@ def test_backward_long_context_16_channels():
     check(errs, "bf16", "1M tokens, 16 channels")
     del g, ck, dout, sub
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("N,G,io", [(4, 0, "f32"), (12, 2, "bf16"), (32, 0, "f32"), (24, 2, "bf16"),
+                                    (64, 0, "f32"), (64, 0, "bf16"), (40, 2, "f32")])
+@pytest.mark.parametrize("path", ["partials", "atomics"])
+def test_backward_any_state_size(N, G, io, path):
+    """d_state below 16 (padding states in the one-slot kernel) and above it
+    (two or four state slots per lane: the forward recomputed per slot),
+    with one B/C group or two groups of 16 channels, against the oracle."""
+    errs, *_ = run(2, 32, 150, io, seed=N * 10 + G, N=N, G=G,
+                   workspace=None if path == "partials" else False)
+    check(errs, io, f"N{N} G{G} {io} {path}")
+
+
+@pytest.mark.parametrize("N,io", [(64, "f32"), (32, "bf16")])
+def test_backward_any_state_size_segmented(N, io):
+    """More states on a long sequence with few channels: the segmented
+    backward (adjoint aggregates per slot) against the oracle."""
+    a = ssm.ScanBwdArgs()
+    a.batch, a.dim, a.seqlen, a.dstate = 1, 16, 2 * 8192 + 48, N
+    # more than the one-segment size (dB/dC partials and one slot of dA, dD, dbias)
+    assert ssm.scan_bwd_workspace_size(a) > 4 * (2 * N * a.seqlen + 16 * (N + 2))
+    errs, *_ = run(1, 16, 2 * 8192 + 48, io, seed=N + 7, N=N)
+    check(errs, io, f"segmented N{N} {io}")
