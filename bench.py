@@ -621,17 +621,19 @@ def profile_long(cfg, torch, ssm, si, launches=5):
         f"(1 GiB read + 1 GiB write)")
 
 
-def profile_layer(cfg, torch, ssm, si, launches=10):
-    """Layer scan launches, decode steps on the decode workload, and the
-    calibration copy; for rocprofv3."""
-    t = si.to_torch(si.scan_inputs_for(cfg), "cuda")
-    out = torch.empty_like(t["u"])
-    last = torch.empty((cfg.batch, cfg.dim, cfg.dstate), device="cuda")
-    for i in range(launches):
-        ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
-                               delta_bias=t["delta_bias"], out=out, last_state=last)
-    torch.cuda.synchronize()
-    del t, out, last
+def profile_layer(cfg, torch, ssm, si, launches=10, cfg2=None):
+    """Layer scan launches (and, with cfg2, as many of a second layer
+    afterwards), decode steps on the decode workload, and the calibration
+    copy; for rocprofv3."""
+    for c in (cfg,) + ((cfg2,) if cfg2 is not None else ()):
+        t = si.to_torch(si.scan_inputs_for(c), "cuda")
+        out = torch.empty_like(t["u"])
+        last = torch.empty((c.batch, c.dim, c.dstate), device="cuda")
+        for i in range(launches):
+            ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                   delta_bias=t["delta_bias"], out=out, last_state=last)
+        torch.cuda.synchronize()
+        del t, out, last
     dc = si.DECODE_CONFIG
     d = si.decode_inputs_device(dc, steps=launches, device="cuda")
     state = torch.zeros((dc.batch, dc.dim, dc.dstate), device="cuda")
@@ -642,8 +644,12 @@ def profile_layer(cfg, torch, ssm, si, launches=10):
     torch.cuda.synchronize()
     del d, state, dout
     calibration_copy(torch, launches)
+    extra = ""
+    if cfg2 is not None:
+        extra = (f", then {launches} of {cfg2.name} "
+                 f"({scan_bytes(cfg2.batch, cfg2.dim, cfg2.seqlen, cfg2.dstate, 2)} bytes each)")
     log(f"[profile] {launches} scan launches ({scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, 4)}"
-        f" algorithmic bytes each), {launches} decode steps "
+        f" algorithmic bytes each){extra}, {launches} decode steps "
         f"({decode_bytes(dc.batch, dc.dim, dc.dstate, 2)} bytes each), {launches} copy launches "
         f"(1 GiB read + 1 GiB write)")
 
@@ -659,12 +665,17 @@ def main():
                     help="only the headline scan (warm-up, then 5 scans) and a 1 GiB copy kernel "
                          "(5 launches) that calibrates the HBM byte counters; for rocprofv3")
     ap.add_argument("--profile-layer", action="store_true",
-                    help="only the 130m-like layer scan (10 launches), 10 decode steps and the "
-                         "calibration copy; for rocprofv3")
+                    help="only the 130m-like and the 2.8b-like layer scans (10 launches each), "
+                         "10 decode steps and the calibration copy; for rocprofv3")
+    ap.add_argument("--profile-general", action="store_true",
+                    help="only the 130m-like layer with the width-4 conv fused, with 64 states "
+                         "and with per-channel B/C (10 launches each); for rocprofv3")
     ap.add_argument("--profile-ssd", action="store_true",
-                    help="only the Mamba-2 SSD layer (10 launches); for rocprofv3")
+                    help="only the Mamba-2 SSD layer (10 launches) and the long-context SSD "
+                         "layer (3 segmented launches); for rocprofv3")
     ap.add_argument("--profile-bwd", action="store_true",
-                    help="only the scan backward of the 130m-like layer (10 launches); for rocprofv3")
+                    help="only the scan backward of the 130m-like and the 2.8b-like layer "
+                         "(10 launches each); for rocprofv3")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -688,7 +699,28 @@ def main():
         profile_long(head, torch, ssm, si)
         return
     if args.profile_layer:
-        profile_layer(layer, torch, ssm, si)
+        profile_layer(layer, torch, ssm, si, cfg2=si.SCAN_CONFIGS[2])
+        return
+    if args.profile_general:
+        # the 130m-like layer with the width-4 conv fused, with 64 states, and
+        # with per-channel B/C (10 launches each)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(layer.seed)
+        for name, cg, conv in (("conv4", layer, 4),
+                               ("dstate64", dataclasses.replace(layer, dstate=64), 0),
+                               ("bc-per-channel", dataclasses.replace(layer, ngroups=layer.dim), 0)):
+            t = si.to_torch(si.scan_inputs_for(cg), "cuda")
+            kw = {}
+            if conv:
+                kw = dict(conv_weight=torch.randn(cg.dim, conv, device="cuda", generator=g) / conv ** 0.5,
+                          conv_bias=torch.zeros(cg.dim, device="cuda"))
+            out = torch.empty_like(t["u"])
+            for _ in range(10):
+                ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                       delta_bias=t["delta_bias"], out=out, **kw)
+            torch.cuda.synchronize()
+            del t, out
+            log(f"[profile] 10 launches of {layer.name} ({name})")
         return
     if args.profile_ssd:
         cs = si.SSD_CONFIG
@@ -698,19 +730,29 @@ def main():
             ssm.ssd_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
                              dt_bias=t["dt_bias"], out=out)
         torch.cuda.synchronize()
-        log(f"[profile] 10 launches of the SSD layer {cs.name}")
+        del t, out
+        cl = si.SSD_LONG_CONFIG
+        t = si.ssd_inputs_device(cl, "cuda")
+        out = torch.empty_like(t["x"])
+        for _ in range(3):   # segmented (the binding allocates the workspace)
+            ssm.ssd_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                             dt_bias=t["dt_bias"], out=out)
+        torch.cuda.synchronize()
+        log(f"[profile] 10 launches of the SSD layer {cs.name}, 3 of {cl.name} (segmented)")
         return
     if args.profile_bwd:
-        t = si.to_torch(si.scan_inputs_for(layer), "cuda")
-        ck = torch.empty(ssm.checkpoint_shape(layer.batch, layer.dim, layer.seqlen),
-                         dtype=torch.float32, device="cuda")
-        kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"])
-        ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], checkpoints=ck, **kw)
-        dout = torch.randn_like(t["u"])
-        for _ in range(10):
-            ssm.selective_scan_bwd(dout, t["u"], t["delta"], t["A"], t["B"], t["C"], ck, **kw)
-        torch.cuda.synchronize()
-        log(f"[profile] 10 launches of the scan backward on {layer.name}")
+        for cb in (layer, si.SCAN_CONFIGS[2]):
+            t = si.to_torch(si.scan_inputs_for(cb), "cuda")
+            ck = torch.empty(ssm.checkpoint_shape(cb.batch, cb.dim, cb.seqlen),
+                             dtype=torch.float32, device="cuda")
+            kw = dict(D=t["D"], z=t["z"], delta_bias=t["delta_bias"])
+            ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], checkpoints=ck, **kw)
+            dout = torch.randn_like(t["u"])
+            for _ in range(10):
+                ssm.selective_scan_bwd(dout, t["u"], t["delta"], t["A"], t["B"], t["C"], ck, **kw)
+            torch.cuda.synchronize()
+            del t, ck, dout
+            log(f"[profile] 10 launches of the scan backward on {cb.name}")
         return
     log(f"[bench] headline {head.name}: warmup {args.warmup} (+ >= {WARM_MS:.0f} ms), "
         f"steps {args.steps}")
