@@ -4,9 +4,9 @@
 Headline: the long-context scan, the largest single-GPU workload (batch 1,
 d_inner 1536, L 1,048,576, d_state 16, bf16 IO with fp32 state, silu gate,
 last_state returned).  One step = one full prefill scan of the sequence with
-inputs already resident in HBM: both launches of the segmented scan (pass 1
-over every segment, pass 2 over the segments' heads while the incoming state
-still counts).  Throughput is algorithmic bytes per second (every input
+inputs already resident in HBM: all four launches of the segmented scan
+(pass 1 over every segment, the plan and the work lists, pass 2 over the
+head windows of the segments while the incoming state still counts).  Throughput is algorithmic bytes per second (every input
 element read once, B and C once per (batch, token), every output written
 once, the state never touching HBM) and channel*tokens per second; the HBM
 fraction is against MI355X's 8 TB/s.  The scan is bound by vector
@@ -23,8 +23,10 @@ durations are medians of per-launch HIP events on the launching stream.
 Also measured (secondary, same JSON line): the Mamba-130m-like fp32 layer
 scan, the bf16 2.8b-like layer scan, the 1000-step decode update, the
 130m-like scan with the width-4 causal conv of the block's conv branch fused
-in front, with d_state 64 and with per-channel B/C, the Mamba-2 SSD layer,
-and the scan backward on the two layer shapes.
+in front, with d_state 64 and with per-channel B/C, the Mamba-2 SSD layer
+and its long-context form (segmented and as one segment), the scan backward
+on the two layer shapes and the long-context workload, a length sweep, and
+the oracle's rate on the other workloads.
 
 Prints ONE JSON line on stdout.  Progress goes to stderr.
 """
@@ -596,7 +598,7 @@ def calibration_copy(torch, launches):
 
 
 def profile_long(cfg, torch, ssm, si, launches=5):
-    """The headline scan (both passes) after a >= 200 ms warm-up, then the
+    """The headline scan (all its launches) after a >= 200 ms warm-up, then the
     calibration copy; for rocprofv3."""
     t = si.scan_inputs_device(cfg, "cuda")
     out = torch.empty_like(t["u"])
@@ -617,7 +619,7 @@ def profile_long(cfg, torch, ssm, si, launches=5):
     esz = 2 if cfg.io_dtype == "bf16" else 4
     log(f"[profile] {wl} warm-up + {launches} timed scans of {cfg.name} "
         f"({scan_bytes(cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate, esz)} algorithmic bytes each; "
-        f"HIP events median {kern_ms:.3f} ms per scan, both passes), {launches} copy launches "
+        f"HIP events median {kern_ms:.3f} ms per scan, all launches), {launches} copy launches "
         f"(1 GiB read + 1 GiB write)")
 
 
@@ -866,7 +868,7 @@ def main():
                 "bias=inv-softplus(logU[1e-3,1e-1]), A=-(n+1), D=1)",
         "config": {"workload": "selective scan fwd, long context: batch 1, d_inner 1536, "
                                "L 1048576, d_state 16, bf16 IO, fp32 state and arithmetic, "
-                               "silu gate, last_state; both passes of the segmented scan",
+                               "silu gate, last_state; all launches of the segmented scan",
                    "batch": head.batch, "dim": head.dim, "seqlen": head.seqlen,
                    "dstate": head.dstate, "io_dtype": "bf16"},
         "channel_tokens_per_s": r["channel_tokens_per_s"],
@@ -876,11 +878,11 @@ def main():
         "warmup_ms": r["warmup_ms"],
         "roofline": {"bound": bound, "achieved": main_["achieved"], "peak": main_["peak"],
                      "unit": main_["unit"], "frac": main_["frac"], "traffic": traffic,
-                     "kernel": "scan_fwd_kernel<bf16> pass 1 (kSeg) + pass 2 (kFix)",
+                     "kernel": "scan_fwd_kernel<bf16> pass 1 (kSeg) + seg_plan_kernel + seg_list_kernel + pass 2 (kFix)",
                      "kernel_ms": round(r["kernel_ms"], 5),
                      "kernel_ms_min": round(r["kernel_ms_min"], 5),
                      "kernel_ms_mean": round(r["kernel_ms_mean"], 5),
-                     "timing": "median of per-step HIP events around both launches",
+                     "timing": "median of per-step HIP events around all four launches",
                      "algorithmic_bytes_per_launch": r["bytes"],
                      "token_state_steps_per_launch": steps_tn,
                      "hbm": hbm, "alu": alu,
