@@ -571,8 +571,13 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
     // longest first, so that they do not trail the launch).  Entries past
     // the list repeat its last channel (identical values, identical
     // stores); a wavefront's windows run from the smallest to the largest
-    // channel of its rows, all in one chunk.
-    uint32_t wg = xcd_order(blockIdx.x, gridDim.x);
+    // channel of its rows, all in one chunk.  The workgroup index is taken
+    // as is, not in XCD order: the windows hold very different amounts of
+    // work (most list slots of the later windows are empty), and the
+    // dispatcher's round robin spreads each window over all XCDs, where
+    // contiguous ranges per XCD would give one XCD the later windows and
+    // another the dense first ones.
+    uint32_t wg = blockIdx.x;
     const int i = static_cast<int>(wg % static_cast<uint32_t>(p.maxi));
     wg /= static_cast<uint32_t>(p.maxi);
     g = static_cast<int>(wg % static_cast<uint32_t>(p.nseg - 1)) + 1;
