@@ -241,7 +241,10 @@ struct BwdWave {
   // shorter than a block.
   __device__ __forceinline__ void dbdc_sum(int k, int h8, int q) const {
     const int tid = threadIdx.x;
-    const int ten = tid >> 7, n = (tid >> 3) & 15, t = tid & 7;
+    // the tensor (dB, dC) is one per wavefront pair: made visibly uniform so
+    // that the buffer descriptor is selected in scalar registers
+    const int ten = __builtin_amdgcn_readfirstlane(tid >> 7);
+    const int n = (tid >> 3) & 15, t = tid & 7;
     const int qr = 2 * ten + (t >> 2), qt = t & 3;
     float sum = sQ[0][qr][n][qt];
 #pragma unroll
