@@ -128,6 +128,39 @@ def test_config3_long_context_16_channels():
     torch.cuda.empty_cache()
 
 
+def test_segmented_wide_fp32_gathers_windows_by_chunk():
+    """fp32, d_inner 1100, L 2^20 + 37: a B/C group's rows span 1100 rows of
+    4 MiB, more than a 32-bit buffer window can reach, so the segmented
+    scan's second pass gathers each window's channels from chunks of the
+    group (1023 channels, then 77) whose rows fit.  Checked against the
+    oracle on 24 channels taken from both chunks, with h0."""
+    cfg = si.ScanConfig("wide-fp32-long", 1, 1100, (1 << 20) + 37, 16, "f32", 9)
+    a = ssm.ScanArgs()
+    a.batch, a.dim, a.seqlen, a.dstate = cfg.batch, cfg.dim, cfg.seqlen, cfg.dstate
+    assert ssm.scan_workspace_size(a) > 0          # segmented
+    t = si.scan_inputs_device(cfg, DEV)
+    rng = np.random.default_rng(9)
+    h0 = torch.from_numpy(rng.standard_normal((1, cfg.dim, 16)).astype(np.float32)).to(DEV)
+    out, last = ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"],
+                                       z=t["z"], delta_bias=t["delta_bias"], h0=h0,
+                                       return_last_state=True)
+    torch.cuda.synchronize()
+    ch = np.sort(np.concatenate([rng.choice(1023, 12, replace=False),
+                                 1023 + rng.choice(77, 12, replace=False)]))
+    idx = torch.from_numpy(ch).to(DEV)
+    sel = lambda x: to_np(x.index_select(1, idx))
+    ref, rlast = oracle.selective_scan(sel(t["u"]), sel(t["delta"]), to_np(t["A"])[ch],
+                                       to_np(t["B"]), to_np(t["C"]), D=to_np(t["D"])[ch],
+                                       z=sel(t["z"]), delta_bias=to_np(t["delta_bias"])[ch],
+                                       h0=sel(h0), return_last_state=True)
+    e = row_rel_err(sel(out), ref)
+    el = row_rel_err(to_np(last)[:, ch], rlast)
+    print(f"[wide fp32 1M tokens, chunked windows] err_out={e:.3e} err_last={el:.3e}", flush=True)
+    assert e <= TOL["f32"] and el <= TOL["f32"]
+    del t, out, last
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_segmented_long_sequence(io):
     """Few channels and a long sequence: the library cuts the sequence into
