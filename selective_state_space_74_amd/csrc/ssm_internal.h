@@ -51,16 +51,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 // softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|), on the hardware
-// exp2/log2/rcp.  log1p(y) for y in (0, 1] is log(u) for u = 1 + y rounded,
-// plus the part of y that the rounding dropped, e = y - (u - 1) (exact), over
-// u: log1p(y) = log(u) + log(1 + e/u), and |e/u| <= 2^-24 leaves only the
-// first-order term.  This keeps full relative accuracy for small y (Delta
-// around 1e-3 sits there), and when 1 + y rounds to 1 it gives y itself.
+// exp2/log2.  log1p(y) for y in (0, 1] is log(u) for u = 1 + y rounded, plus
+// the part of y that the rounding dropped, e = y - (u - 1) (exact):
+// log1p(y) = log(u) + log(1 + e/u) = log(u) + e/u to first order, as
+// |e| <= 2^-24.  e is added in place of e/u: the two differ by e y / (1 + y),
+// under 2^-24 y / (1 + y), while log1p(y) >= y ln 2, so the result moves by
+// at most about one unit in its last place and no reciprocal is spent.  This
+// keeps full relative accuracy for small y (Delta around 1e-3 sits there), and
+// when 1 + y rounds to 1 it gives y itself.
 __device__ __forceinline__ float softplus_f32(float x) {
   const float y = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
   const float u = 1.0f + y;
   const float e = y - (u - 1.0f);
-  const float lp = fmaf(__builtin_amdgcn_logf(u), kLn2, e * __builtin_amdgcn_rcpf(u));
+  const float lp = fmaf(__builtin_amdgcn_logf(u), kLn2, e);
   return fmaxf(x, 0.0f) + lp;
 }
 
