@@ -560,7 +560,10 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = (threadIdx.x >> 4) & 3;
   const int col = threadIdx.x & 15;
-  // logical workgroup wg = (b * cgroups + cg) * nseg + seg
+  // logical workgroup wg = (b * cgroups + cg) * nseg + seg: channel-major
+  // (segment-major, which lets the channel groups of a segment share its B/C
+  // lines in one XCD's L2 as the forward does, measured 2.7% slower on the
+  // 1M-token backward)
   const uint32_t wg = xcd_order(blockIdx.x, gridDim.x);
   const int seg = static_cast<int>(wg % p.nseg);
   const int64_t bcg = wg / p.nseg;
@@ -1066,7 +1069,7 @@ hipError_t launch_scan_bwd(const ssm_scan_bwd_args& a, hipStream_t stream) {
   p.N = static_cast<int>(a.dstate);
   p.nbk = static_cast<int>((a.seqlen + kT - 1) / kT);
   p.cgroups = (a.dim + kCh - 1) / kCh;
-  const dim3 grid(static_cast<unsigned>(a.batch * p.cgroups * p.nseg)), block(kThreads);
+  const dim3 grid(static_cast<unsigned>(a.batch * p.cgroups * p.nseg));
   const bool sp = a.delta_softplus != 0, bf = a.io_dtype == SSM_BF16;
   const int S = a.dstate <= 16 ? 1 : a.dstate <= 32 ? 2 : 4;   // state slots per lane
   if (p.nseg > 1) {

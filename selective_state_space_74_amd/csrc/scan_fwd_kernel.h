@@ -537,9 +537,13 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = (threadIdx.x >> 4) & 3;
   const int col = threadIdx.x & 15;
-  // Logical workgroup (XCD-aware order, ssm_internal.h): one XCD's L2 and
-  // translation caches hold the rows of a few channel groups, all segments
-  // of each (pass 2: the items of one window), instead of pieces of all.
+  // Logical workgroup (XCD-aware order, ssm_internal.h), segment-major: one
+  // XCD runs every channel group of a few segments.  Those workgroups start
+  // together and walk the same tokens at about the same pace, so each line of
+  // a segment's B/C tile is fetched into that XCD's L2 once and read there by
+  // all of them; in channel-major order every XCD streamed the B/C of all
+  // segments once per channel group it held (at 1M tokens, 1.5x the input
+  // bytes read instead of 1.1x).
   constexpr bool fix = W::kFixp;
   const int N = p.N;
   const int aggs = N + 1;  // floats per aggregate and per window record: h[N], S
@@ -548,10 +552,12 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
   int64_t b, d, dc, dw0, dw3, grp_tile;
   bool vrow;
   if constexpr (!fix) {
-    // wg = (b * cgroups + cg) * nseg + g: 16 consecutive channels, one segment
+    // wg = g * (batch * cgroups) + b * cgroups + cg: 16 consecutive
+    // channels, one segment
     const uint32_t wg = xcd_order(blockIdx.x, gridDim.x);
-    g = static_cast<int>(wg % p.nseg);
-    const int64_t bc = wg / p.nseg;
+    const int64_t ncg = p.batch * p.cgroups;
+    g = static_cast<int>(wg / ncg);
+    const int64_t bc = wg % ncg;
     b = bc / p.cgroups;
     const int64_t cg0 = (bc % p.cgroups) * kCh;
     d = cg0 + kRows * wave + row;

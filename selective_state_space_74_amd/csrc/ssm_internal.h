@@ -76,9 +76,9 @@ __device__ __forceinline__ float silu_f32(float z) {
 // XCD i % 8; xcd_order(i, n) is the logical workgroup that kernels work on,
 // chosen so that each XCD receives a contiguous logical range (XCD x gets
 // n / 8 workgroups, one more for x < n % 8, slots i / 8 in order, after the
-// ranges of the XCDs before it): neighbouring logical workgroups (channel
-// groups, segments of one group) then share one XCD's L2 and translation
-// caches.  A bijection of [0, n).
+// ranges of the XCDs before it): neighbouring logical workgroups (the
+// channel groups of one segment, which read the same B/C tile) then share
+// one XCD's L2 and translation caches.  A bijection of [0, n).
 constexpr uint32_t kXcds = 8;
 __device__ __forceinline__ uint32_t xcd_order(uint32_t i, uint32_t n) {
   const uint32_t x = i % kXcds, slot = i / kXcds, q = n / kXcds, r = n % kXcds;
