@@ -470,8 +470,7 @@ def oracle_timings(si, torch):
             runs.append(time.perf_counter() - t0)
         return float(np.median(runs)), len(runs)
 
-    for cid, rows in ((0, None), (1, 1)):
-        cfg = si.SCAN_CONFIGS[cid]
+    for cfg, rows in ((si.TINY, None), (si.LAYER_130M, 1)):
         inp = si.scan_inputs_for(cfg)
         k = cfg.batch if rows is None else rows
         sl = lambda x: x[:k]
@@ -482,7 +481,7 @@ def oracle_timings(si, torch):
         ct = k * cfg.dim * cfg.seqlen
         res[f"{cfg.name}-1-thread"] = {"channel_tokens_per_s": ct / dt, "seconds": round(dt, 4),
                                        "sample": f"{k} of {cfg.batch} batch rows, median of {n}"}
-    c3 = si.SCAN_CONFIGS[3]
+    c3 = si.LONG_CONTEXT
     t = si.scan_inputs_device(c3, "cuda")
     ch = np.sort(np.random.default_rng(3).choice(c3.dim, 16, replace=False))
     idx = torch.from_numpy(ch).to("cuda")
@@ -695,13 +694,13 @@ def main():
     ssm.lib()
     torch.cuda.init()
 
-    head = si.SCAN_CONFIGS[3]           # the long-context scan: the largest single-GPU workload
-    layer = si.SCAN_CONFIGS[1]
+    head = si.LONG_CONTEXT           # the long-context scan: the largest single-GPU workload
+    layer = si.LAYER_130M
     if args.profile:
         profile_long(head, torch, ssm, si)
         return
     if args.profile_layer:
-        profile_layer(layer, torch, ssm, si, cfg2=si.SCAN_CONFIGS[2])
+        profile_layer(layer, torch, ssm, si, cfg2=si.LAYER_2P8B)
         return
     if args.profile_general:
         # the 130m-like layer with the width-4 conv fused, with 64 states, and
@@ -743,7 +742,7 @@ def main():
         log(f"[profile] 10 launches of the SSD layer {cs.name}, 3 of {cl.name} (segmented)")
         return
     if args.profile_bwd:
-        for cb in (layer, si.SCAN_CONFIGS[2]):
+        for cb in (layer, si.LAYER_2P8B):
             t = si.to_torch(si.scan_inputs_for(cb), "cuda")
             ck = torch.empty(ssm.checkpoint_shape(cb.batch, cb.dim, cb.seqlen),
                              dtype=torch.float32, device="cuda")
@@ -769,7 +768,7 @@ def main():
         secondary[layer.name] = bench_scan(layer, max(20, args.steps), args.warmup, torch, ssm, si)
         log(f"[bench] {layer.name} {secondary[layer.name]['gbps']:.1f} GB/s, "
             f"kernel median {secondary[layer.name]['kernel_ms'] * 1e3:.1f} us")
-        c2 = si.SCAN_CONFIGS[2]
+        c2 = si.LAYER_2P8B
         log(f"[bench] secondary {c2.name}")
         secondary[c2.name] = bench_scan(c2, max(20, args.steps), 5, torch, ssm, si)
         log(f"[bench] {c2.name} {secondary[c2.name]['gbps']:.1f} GB/s, "
@@ -811,8 +810,7 @@ def main():
             secondary[key] = bench_ssd(cl, 10, torch, ssm, si, segmented=seg)
             log(f"[bench] {key} {secondary[key]['gbps']:.1f} GB/s, "
                 f"{secondary[key]['kernel_ms']:.2f} ms")
-        for cid in (1, 2, 3):
-            cb = si.SCAN_CONFIGS[cid]
+        for cb in (si.LAYER_130M, si.LAYER_2P8B, si.LONG_CONTEXT):
             key = f"{cb.name}-backward"
             log(f"[bench] secondary {key}")
             secondary[key] = bench_bwd(cb, 20, torch, ssm, si)

@@ -64,6 +64,10 @@ SCAN_CONFIGS = {
     3: ScanConfig("long-context-bf16", 1, 1536, 1 << 20, DSTATE, "bf16", 3),
 }
 DECODE_CONFIG = DecodeConfig("decode-b256-d5120-bf16", 256, 5120, DSTATE, "bf16", 1000, 4)
+TINY = SCAN_CONFIGS[0]          # batch 2, d_inner 32, L 64, fp32
+LAYER_130M = SCAN_CONFIGS[1]    # batch 8, d_inner 1536, L 2048, fp32
+LAYER_2P8B = SCAN_CONFIGS[2]    # batch 4, d_inner 5120, L 4096, bf16
+LONG_CONTEXT = SCAN_CONFIGS[3]  # batch 1, d_inner 1536, L 1,048,576, bf16
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:

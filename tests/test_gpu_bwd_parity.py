@@ -116,7 +116,7 @@ def test_forward_checkpoints_are_the_block_entry_states():
 @pytest.mark.parametrize("path", ["partials", "atomics"])
 def test_backward_config1_full_size(path):
     """The 130m-like layer (batch 8, d_inner 1536, L 2048, fp32) end to end."""
-    cfg = si.SCAN_CONFIGS[1]
+    cfg = si.LAYER_130M
     errs, *_ = run(cfg.batch, cfg.dim, cfg.seqlen, "f32", seed=cfg.seed, h0=False, dlast=False,
                    workspace=None if path == "partials" else False)
     check(errs, "f32", f"130m-like layer {path}")
@@ -252,7 +252,7 @@ def test_backward_long_context_16_channels():
     channels the forward parity uses) at the full 1,048,576 tokens, bf16 IO:
     the sampled channels as a 16-channel problem, so that every gradient,
     dB and dC included, has an oracle value.  64 segments."""
-    cfg = si.SCAN_CONFIGS[3]
+    cfg = si.LONG_CONTEXT
     t = si.scan_inputs_device(cfg, DEV)
     ch = np.sort(np.random.default_rng(3).choice(cfg.dim, 16, replace=False))
     idx = torch.from_numpy(ch).to(DEV)

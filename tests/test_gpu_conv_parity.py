@@ -98,7 +98,7 @@ def test_fused_conv_without_silu_and_without_state():
 
 
 def test_fused_conv_config1_layer():
-    cfg = si.SCAN_CONFIGS[1]
+    cfg = si.LAYER_130M
     inp = si.scan_inputs_for(cfg)
     check(inp, "f32", 4, seed=1, label="130m-like layer")
 

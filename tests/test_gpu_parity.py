@@ -42,7 +42,7 @@ def check_scan(inp, io, rows=None, twin=True, h0=None, label=""):
 
 
 def test_config0_tiny_f32():
-    cfg = si.SCAN_CONFIGS[0]
+    cfg = si.TINY
     check_scan(si.scan_inputs_for(cfg), "f32", label="tiny")
 
 
@@ -85,14 +85,14 @@ def test_initial_state_and_split_sequence():
 
 
 def test_config1_full_f32():
-    cfg = si.SCAN_CONFIGS[1]
+    cfg = si.LAYER_130M
     check_scan(si.scan_inputs_for(cfg), "f32", label="130m-like layer")
 
 
 def test_config2_bf16_full():
     """The 2.8b-like layer (batch 4, d_inner 5120, L 4096, bf16 IO) on every
     channel: out, last_state and the SSM-only twin."""
-    cfg = si.SCAN_CONFIGS[2]
+    cfg = si.LAYER_2P8B
     check_scan(si.scan_inputs_for(cfg), "bf16", label="2.8b-like layer, all channels")
 
 
@@ -107,7 +107,7 @@ def test_readout_forms_either_side_of_the_grid_switch(blocks, io):
 
 
 def test_config3_long_context_16_channels():
-    cfg = si.SCAN_CONFIGS[3]
+    cfg = si.LONG_CONTEXT
     t = si.scan_inputs_device(cfg, DEV)
     out, last = ssm.selective_scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"],
                                        z=t["z"], delta_bias=t["delta_bias"],
