@@ -168,6 +168,27 @@ __device__ __forceinline__ typename Frag<T>::V tofrag(float a, float b, float c,
 // The one-block bf16 kernel with 64 states and vector staging fits four
 // wavefronts per SIMD (128 registers) without spilling; asking for that keeps
 // a grid of 4 x 256 workgroups in one wave of residency.
+// One DPP step on a float: lanes outside the row and bank masks, and lanes
+// whose source lies outside their row, read 0.
+template <int kCtrl, int kRowMask = 0xf>
+__device__ __forceinline__ float dpp0(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xf, true));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront in registers: row
+// shifts by 1, 2, 4 and 8 sum each 16-lane row, then row_bcast:15 adds row
+// 0's total to row 1 and row 2's to row 3, and row_bcast:31 adds lane 31's
+// (rows 0 and 1) to rows 2 and 3.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp0<0x111>(v);         // row_shr:1
+  v += dpp0<0x112>(v);         // row_shr:2
+  v += dpp0<0x114>(v);         // row_shr:4
+  v += dpp0<0x118>(v);         // row_shr:8
+  v += dpp0<0x142, 0xa>(v);    // row_bcast:15 into rows 1 and 3
+  v += dpp0<0x143, 0xc>(v);    // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 template <typename T, int NMAX, bool kVec, int PB>
 constexpr bool kFourWaves() { return sizeof(T) == 2 && NMAX == 64 && kVec && PB == 1; }
 
@@ -485,18 +506,13 @@ void ssd_fwd_kernel(SsdParams p) {
       const float x = Elem<T>::f32(st.dt) + bias;
       float dl = kSoftplus ? softplus_f32(x) : x;
       dl = tv ? dl : 0.0f;
-      float cum = dl;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float o = __shfl_up(cum, off, 64);
-        cum += lane >= off ? o : 0.0f;
-      }
+      const float cum = wave_prefix_sum(dl);
       const float la = cum * a2;
-      const float last = __shfl(la, 63, 64);
+      const float last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(la), 63));
       if constexpr (kSegd) {
         // segmented: read at the next chunk's top and after the loop, past
         // this chunk's barriers
-        const float csum = __shfl(cum, 63, 64);
+        const float csum = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), 63));
         if (tid == 0) sSum += static_cast<double>(csum);
       }
       const float w = __builtin_amdgcn_exp2f(last - la) * dl;   // exp(a_{Q-1} - a_s) Delta_s
