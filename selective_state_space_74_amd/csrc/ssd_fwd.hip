@@ -709,12 +709,14 @@ int choose_pb(int P, int nmax, bool bf, int64_t) {
 #endif
 
 // Segments of a long sequence whose (batch, head, channel block) workgroups
-// leave the machine short: as many as bring the grid to about 512
-// workgroups (two per CU), each at least 32,768 tokens long (pass 2 rescans
-// a segment's head until the incoming state has decayed, about
-// 17 / (Delta |A|) tokens for the slowest head: 17,000 at Delta 1e-3,
-// A = -1), at most 64.
-constexpr int64_t kSsdTargetGroups = 512;
+// leave the machine short: as many as bring the grid to about 2,048
+// workgroups (eight per CU, in rounds of what the kernel's registers let
+// reside), each at least 32,768 tokens long (pass 2 rescans a segment's head
+// until the incoming state has decayed, about 17 / (Delta |A|) tokens for
+// the slowest head: 17,000 at Delta 1e-3, A = -1), at most 64.  Measured on
+// batch 1, 32 heads of 64, L 1M (128 workgroups per segment): 13.9 ms at a
+// target of 512 (4 segments), 12.1 at 1,024, 11.8 at 2,048, 12.1 at 4,096.
+constexpr int64_t kSsdTargetGroups = 2048;
 constexpr int64_t kSsdMinSegLen = 32768;
 constexpr int kSsdMaxSeg = 64;
 
