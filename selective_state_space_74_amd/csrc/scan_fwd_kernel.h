@@ -279,18 +279,18 @@ struct Wave {
     return r;
   }
 
-  // Shared mode, stage role: group g's B (and C) into LDS buffer g & 1.  B of
-  // tokens past the end is zeroed so that a non-finite value read from
-  // beyond a row cannot reach h; rows of padding states load as zero.
+  // Shared mode, stage role: group g's B (and C) into LDS buffer g & 1, as
+  // loaded: tokens past the end hold whatever lies beyond them (the next
+  // segment, or the next state's row), which bc() keeps from h in the masked
+  // blocks, the only ones that reach past the end; rows of padding states
+  // load as zero.
   __device__ __forceinline__ void stage(int g, const GroupRaw<S>& r) const {
     const int st = kRows * wave + row;
-    const int t = t_beg + g * kGT + col;
 #pragma unroll
     for (int q = 0; q < S; ++q) {
 #pragma unroll
       for (int i = 0; i < kGB; ++i) {
-        const float bv = Elem<T>::f32(r.b[q][i]);
-        sB[g & 1][st + kN * q][col + i * kT] = t + i * kT < t_end ? bv : 0.0f;
+        sB[g & 1][st + kN * q][col + i * kT] = Elem<T>::f32(r.b[q][i]);
         if constexpr (kOwnerC) sCt[g & 1][col + i * kT][st] = Elem<T>::f32(r.c[q][i]);
         else sC[g & 1][st + kN * q][col + i * kT] = Elem<T>::f32(r.c[q][i]);
       }
@@ -298,8 +298,10 @@ struct Wave {
   }
 
   // B and C of state slot q for the 16 tokens of block k: from the LDS tile
-  // (shared mode) or from this lane's own rows (lane mode; tokens past the
-  // end read as zero B).
+  // (shared mode) or from this lane's own rows (lane mode).  In a masked
+  // block B of the tokens past the end reads as zero, so that a non-finite
+  // value lying beyond them cannot reach h (their step is then exactly the
+  // identity: Delta and Delta u are zero there).
   template <bool kMask>
   __device__ __forceinline__ void bc(int k, int q, float (&bv)[kT], float (&cv)[kT]) const {
     if constexpr (!kLane) {
@@ -313,6 +315,11 @@ struct Wave {
           const float4 y = *reinterpret_cast<const float4*>(&sC[buf][col + kN * q][tb + 4 * i]);
           cv[4 * i] = y.x; cv[4 * i + 1] = y.y; cv[4 * i + 2] = y.z; cv[4 * i + 3] = y.w;
         }
+      }
+      if constexpr (kMask) {
+        const int tleft = t_end - (t_beg + k * kT);
+#pragma unroll
+        for (int j = 0; j < kT; ++j) bv[j] = j < tleft ? bv[j] : 0.0f;
       }
     } else {
       const uint32_t s = skip(k);
@@ -378,8 +385,10 @@ struct Wave {
   // after which the workgroup synchronises; the other blocks are first blocks
   // (two per group), after which the next group is staged.  In the masked
   // form both are decided at run time.
-  template <bool kMask, bool kEnd>
-  __device__ __forceinline__ void iter(int k, float (&h)[S], double& ssum, const Raw& P,
+  // ssum: the owner's step-size sum, fp64 (masked blocks) or an fp32 sum of
+  // one steady-state round's four steps that the caller adds to it.
+  template <bool kMask, bool kEnd, typename Acc>
+  __device__ __forceinline__ void iter(int k, float (&h)[S], Acc& ssum, const Raw& P,
                                        const Raw& Q, Raw& R, GroupRaw<S>& G, float& uprev,
                                        float& xprev, float (&cl)[kN]) const {
     // B/C of the first state slot and the previous block's partials first
@@ -432,7 +441,7 @@ struct Wave {
       du = own ? du : 0.0f;
     }
     // segmented: the step sizes of this owner's tokens, summed in fp64
-    if constexpr (kSegm) ssum += static_cast<double>(dl);
+    if constexpr (kSegm) ssum += static_cast<Acc>(dl);
     if constexpr (kDefer) {
       // the previous block's readout: its states (read above) against its
       // token's C column (read during its scan), after this block's owner
@@ -795,11 +804,14 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p) {
         rblk = rj < kWin ? win_blk(rj) : 0x7fffffff;
       }
     }
-    // k % 4 == 1 here, and 4 is a multiple of kGB
-    w.template iter<false, (1 % kGB == kGB - 1)>(k + 0, h, ssum, buf0, buf1, buf3, grp, uprev, xprev, cl);
-    w.template iter<false, (2 % kGB == kGB - 1)>(k + 1, h, ssum, buf1, buf2, buf0, grp, uprev, xprev, cl);
-    w.template iter<false, (3 % kGB == kGB - 1)>(k + 2, h, ssum, buf2, buf3, buf1, grp, uprev, xprev, cl);
-    w.template iter<false, (4 % kGB == kGB - 1)>(k + 3, h, ssum, buf3, buf0, buf2, grp, uprev, xprev, cl);
+    // k % 4 == 1 here, and 4 is a multiple of kGB; the round's four step
+    // sizes are summed in fp32 and then added to the fp64 sum
+    float sq = 0.0f;
+    w.template iter<false, (1 % kGB == kGB - 1)>(k + 0, h, sq, buf0, buf1, buf3, grp, uprev, xprev, cl);
+    w.template iter<false, (2 % kGB == kGB - 1)>(k + 1, h, sq, buf1, buf2, buf0, grp, uprev, xprev, cl);
+    w.template iter<false, (3 % kGB == kGB - 1)>(k + 2, h, sq, buf2, buf3, buf1, grp, uprev, xprev, cl);
+    w.template iter<false, (4 % kGB == kGB - 1)>(k + 3, h, sq, buf3, buf0, buf2, grp, uprev, xprev, cl);
+    if constexpr (kSegm) ssum += static_cast<double>(sq);
   }
   if (!done) {
     if (k < nblk) w.template iter<true, false>(k, h, ssum, buf0, buf1, buf3, grp, uprev, xprev, cl);
