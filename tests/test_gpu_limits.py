@@ -164,3 +164,45 @@ def test_segmented_in_place_carry():
         print(f"[in-place carry, segmented, run {rep}] err_out={e:.3e} err_last={el:.3e}",
               flush=True)
         assert e <= TOL["f32"] and el <= TOL["f32"]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 40, 2000 + 7, 16), (8, 1536, 130 + 5, 16),
+                                   (4, 4096, 64 + 9, 16), (1, 16, 3 * 32768 + 100, 16),
+                                   (2, 40, 500 + 3, 40)])
+def test_non_finite_values_past_the_end_stay_out(shape, io):
+    """Every input is a view whose rows run on, past the sequence's end, into
+    NaN and Inf (the tail of a wider buffer): the ragged last block reads
+    those positions for its B tile and owner inputs, and none of them may
+    reach the state, the outputs or last_state.  Shapes: one segment with
+    the deferred readout (a grid of at most 768 workgroups), one segment
+    with the compact readout (1024 workgroups), a small grid, and a length
+    cut into segments (whose last segment ends in the ragged block); and 40
+    states (four state slots per lane, the last one part padding)."""
+    batch, dim, L, N = shape
+    inp = si.scan_inputs(batch, dim, L, dstate=N, io_dtype=io, seed=307)
+    t = si.to_torch(inp, DEV)
+
+    def poisoned(x, extra=23):
+        big = torch.empty(x.shape[:-1] + (x.shape[-1] + extra,), dtype=x.dtype, device=DEV)
+        big[..., : x.shape[-1]] = x
+        big[..., x.shape[-1]:: 2] = float("nan")
+        big[..., x.shape[-1] + 1:: 2] = float("inf")
+        return big[..., : x.shape[-1]]
+
+    u, dl, z, B, C = (poisoned(t[k]) for k in ("u", "delta", "z", "B", "C"))
+    h0 = np.random.default_rng(307).standard_normal((batch, dim, N)).astype(np.float32)
+    h0t = torch.from_numpy(h0).to(DEV)
+    out, last = ssm.selective_scan_fwd(u, dl, t["A"], B, C, D=t["D"], z=z,
+                                       delta_bias=t["delta_bias"], h0=h0t,
+                                       return_last_state=True)
+    torch.cuda.synchronize()
+    a = ssm.ScanArgs()
+    a.batch, a.dim, a.seqlen, a.dstate = batch, dim, L, N
+    seg = ssm.scan_workspace_size(a) > 0
+    assert torch.isfinite(out.float()).all() and torch.isfinite(last).all()
+    ref, rlast = oracle_scan(inp, h0=h0)
+    e, el = row_rel_err(to_np(out), ref), row_rel_err(to_np(last), rlast)
+    print(f"[non-finite past the end {shape} {io} segmented={seg}] err_out={e:.3e} "
+          f"err_last={el:.3e}", flush=True)
+    assert e <= TOL[io] and el <= TOL[io], (e, el)
