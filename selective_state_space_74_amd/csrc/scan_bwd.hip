@@ -146,6 +146,13 @@ template <int S>
 constexpr int kXPitch = S == 1 ? kPitch : 2 * kT + 4;
 template <int S>
 constexpr int kXRow = kN * kXPitch<S> + 16;   // floats per channel
+// Buffers of the dB/dC exchange (sQ): two, one per half block in turn, so
+// that one barrier per half orders both its writes before the sums and the
+// previous half's sums before the writes; one (and a second barrier per
+// half) with four slots, whose LDS would otherwise leave a single workgroup
+// per CU.
+template <int S>
+constexpr int kQBuf = S == 4 ? 1 : 2;
 
 template <typename T, bool kSoftplus, int S>
 struct BwdWave {
@@ -165,9 +172,10 @@ struct BwdWave {
   float (*sC)[kN * S][kGPitch];
   float (*sX)[kXRow<S>];      // this wavefront's [kRows][kXRow]: readout, then the
                               // per-state du/ddelta terms
-  float (*sQ)[kRows][kN][4];   // [kWaves][kRows][kN][4], shared: dB/dC terms of half a
-                              // block (one slot) summed over each wavefront's channels;
-                              // row r holds tensor r / 2 (dB, dC), tokens 4 (r % 2) + 0..3
+  float (*sQ)[kWaves][kRows][kN][4];  // [kQBuf][kWaves][kRows][kN][4], shared: dB/dC terms
+                              // of half a block (one slot) summed over each wavefront's
+                              // channels, half h8 in buffer h8 % kQBuf; row r holds
+                              // tensor r / 2 (dB, dC), tokens 4 (r % 2) + 0..3
 
   static constexpr int E = Elem<T>::kSize;
 
@@ -246,9 +254,10 @@ struct BwdWave {
     const int ten = __builtin_amdgcn_readfirstlane(tid >> 7);
     const int n = (tid >> 3) & 15, t = tid & 7;
     const int qr = 2 * ten + (t >> 2), qt = t & 3;
-    float sum = sQ[0][qr][n][qt];
+    const auto& sq = sQ[h8 % kQBuf<S>];
+    float sum = sq[0][qr][n][qt];
 #pragma unroll
-    for (int v = 1; v < kWaves; ++v) sum += sQ[v][qr][n][qt];
+    for (int v = 1; v < kWaves; ++v) sum += sq[v][qr][n][qt];
     const int tok = k * kT + 8 * h8 + t;
     const int na = n + kN * q;
     const uint32_t off =
@@ -356,7 +365,8 @@ struct BwdWave {
             make_float4(s2[0], s2[1], s2[2], s2[3]);
       }
       if constexpr (jj == 0) {
-        *reinterpret_cast<float4*>(&sQ[wave][row][col][0]) = make_float4(rq[0], rq[1], rq[2], rq[3]);
+        *reinterpret_cast<float4*>(&sQ[h8 % kQBuf<S>][wave][row][col][0]) =
+            make_float4(rq[0], rq[1], rq[2], rq[3]);
         __syncthreads();
         // owners of tokens 8 h8 .. 8 h8 + 7: du, ddelta.  The sums over the
         // 16 states for token ti: lanes col and col ^ 8 each add 8 states'
@@ -385,9 +395,12 @@ struct BwdWave {
           // the store is dropped
           Elem<T>::store(wdz.at(gate ? skip(k) : 0u), odz, dzv);
         }
-        // dB, dC: summed over the workgroup's channels
+        // dB, dC: summed over the workgroup's channels; the next half
+        // writes the other buffer, and the one after it this one again only
+        // past the next half's barrier, which every thread reaches after
+        // these reads
         dbdc_sum(k, h8, 0);
-        __syncthreads();
+        if constexpr (kQBuf<S> == 1) __syncthreads();
       }
     });
   }
@@ -503,10 +516,11 @@ struct BwdWave {
         dA[0] = fmaf(row_bcast<j>(dl), qv, dA[0]);
         g[0] = e[j] * adj;                                                // adjoint of h_{t-1}
         if constexpr (jj == 0) {
-          *reinterpret_cast<float4*>(&sQ[wave][row][col][0]) = make_float4(rq[0], rq[1], rq[2], rq[3]);
+          *reinterpret_cast<float4*>(&sQ[h8 % kQBuf<S>][wave][row][col][0]) =
+              make_float4(rq[0], rq[1], rq[2], rq[3]);
           __syncthreads();
           dbdc_sum(k, h8, q);
-          __syncthreads();
+          if constexpr (kQBuf<S> == 1) __syncthreads();
         }
       });
       rotate(g);
@@ -555,7 +569,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   __shared__ __align__(16) float sB[2][kN * S][kGPitch];
   __shared__ __align__(16) float sC[2][kN * S][kGPitch];
   __shared__ __align__(16) float sX[kWaves][kRows][kXRow<S>];
-  __shared__ __align__(16) float sQ[kWaves][kRows][kN][4];
+  __shared__ __align__(16) float sQ[kQBuf<S>][kWaves][kRows][kN][4];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = (threadIdx.x >> 4) & 3;
