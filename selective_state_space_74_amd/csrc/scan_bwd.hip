@@ -165,6 +165,9 @@ struct BwdWave {
   // their window (loads read zero)
   uint32_t oB[S], oC[S], ock[S];
   float a[S], a2[S], bias, Dd;
+  // one slot: A of the lane's channel at states (col & 8) + 0..7, the
+  // weights of the owner's half of the sum over states for ddelta
+  float ah[kN / 2];
   bool gate;
   bool partials;      // dB/dC sums stored to this workgroup's slots, not added
   int nvalid;         // channels of this workgroup below dim
@@ -277,7 +280,7 @@ struct BwdWave {
     static_assert(S == 1, "one state slot");
     float& g = ga[0];
     float& dA = dAa[0];
-    const float a = this->a[0], a2 = this->a2[0];
+    const float a2 = this->a2[0];
     const int t0 = k * kT;
     float bv[kT], cv[kT];
     tile_rows(k, 0, bv, cv);
@@ -340,16 +343,22 @@ struct BwdWave {
     float sxm = 0.0f;  // softplus'(x) for this owner's token
     if (kSoftplus) sxm = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
     float s1[4], s2[4], yq[4], rq[4];
+    // The adjoint of h_t itself is carried from token to token,
+    // adj_t = exp(Delta_{t+1} A) adj_{t+1} + dy_t C_t (the adjoint of the
+    // state leaving the block, g, enters at token 15 and leaves as
+    // exp(Delta_0 A) adj_0): one DPP-fused multiply and one FMA per token.
+    float adj = 0.0f;
     static_for<0, kT>([&](auto J) {
       constexpr int j = kT - 1 - decltype(J)::value;
       constexpr int h8 = j / 8;          // which half
       constexpr int jj = j % 8;          // token within the half
-      const float dyb = row_bcast<j>(dy);
-      const float adj = fmaf(dyb, cv[j], g);                       // adjoint of h_t
+      const float dyc = row_bcast<j>(dy) * cv[j];
+      if constexpr (j == kT - 1) adj = g + dyc;                    // adjoint of h_t
+      else adj = fmaf(e[j + 1], adj, dyc);
       const float hp = j > 0 ? hs[j > 0 ? j - 1 : 0] : hck;        // h_{t-1}
       const float q = adj * (e[j] * hp);
       s1[j % 4] = adj * bv[j];                                     // -> du, ddelta
-      s2[j % 4] = q * a;                                           // -> ddelta
+      s2[j % 4] = q;                                               // x A by the owner -> ddelta
       const float rb = row_bcast<j>(du2) * adj;                    // -> dB
       const float rc = row_bcast<j>(dy2) * hs[j];                  // -> dC
       // summed over the wavefront's four channels as they come: tokens 4..7
@@ -357,9 +366,9 @@ struct BwdWave {
       if constexpr (jj >= 4) yq[jj - 4] = swap_add32(rb, rc);
       else rq[jj] = swap_add16(swap_add32(rb, rc), yq[jj]);
       dA = fmaf(row_bcast<j>(dl2), q, dA);
-      g = e[j] * adj;                                              // adjoint of h_{t-1}
+      if constexpr (j == 0) g = e[0] * adj;                        // adjoint of h_{t-1}
       if constexpr (j % 4 == 0) {
-        // per-wave region: [c][n][0..7] g B, [c][n][8..15] g A e h_{t-1}
+        // per-wave region: [c][n][0..7] g B, [c][n][8..15] g e h_{t-1}
         *reinterpret_cast<float4*>(&sX[row][col * kPitch + jj]) = make_float4(s1[0], s1[1], s1[2], s1[3]);
         *reinterpret_cast<float4*>(&sX[row][col * kPitch + 8 + jj]) =
             make_float4(s2[0], s2[1], s2[2], s2[3]);
@@ -379,7 +388,7 @@ struct BwdWave {
 #pragma unroll
         for (int n = 0; n < kN / 2; ++n) {
           S1 += sX[row][(n0 + n) * kPitch + ti];
-          S2 += sX[row][(n0 + n) * kPitch + 8 + ti];
+          S2 = fmaf(ah[n], sX[row][(n0 + n) * kPitch + 8 + ti], S2);
         }
         S1 += row_swap8(S1);
         S2 += row_swap8(S2);
@@ -500,11 +509,16 @@ struct BwdWave {
         });
       }
       float yq[4], rq[4];
+      // the adjoint of h_t carried from token to token, as in the one-slot
+      // form
+      float adj = 0.0f;
       static_for<0, kT>([&](auto J) {
         constexpr int j = kT - 1 - decltype(J)::value;
         constexpr int h8 = j / 8;
         constexpr int jj = j % 8;
-        const float adj = fmaf(row_bcast<j>(dy), cv[j], g[0]);           // adjoint of h_t
+        const float dyc = row_bcast<j>(dy) * cv[j];
+        if constexpr (j == kT - 1) adj = g[0] + dyc;                      // adjoint of h_t
+        else adj = fmaf(e[j + 1], adj, dyc);
         const float hp = j > 0 ? hs[j > 0 ? j - 1 : 0] : hck[0];          // h_{t-1}
         const float qv = adj * (e[j] * hp);
         s1[j] = fmaf(adj, bv[j], s1[j]);
@@ -514,7 +528,7 @@ struct BwdWave {
         if constexpr (jj >= 4) yq[jj - 4] = swap_add32(rb, rc);
         else rq[jj] = swap_add16(swap_add32(rb, rc), yq[jj]);
         dA[0] = fmaf(row_bcast<j>(dl), qv, dA[0]);
-        g[0] = e[j] * adj;                                                // adjoint of h_{t-1}
+        if constexpr (j == 0) g[0] = e[0] * adj;                          // adjoint of h_{t-1}
         if constexpr (jj == 0) {
           *reinterpret_cast<float4*>(&sQ[h8 % kQBuf<S>][wave][row][col][0]) =
               make_float4(rq[0], rq[1], rq[2], rq[3]);
@@ -634,6 +648,13 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     w.ock[q] = n < N ? static_cast<uint32_t>(((dc - dw0) * ckrow + n) * 4) : w.wck.bytes;
     w.a[q] = n < N ? p.A[dc * p.Asd + n * p.Asn] : 0.0f;
     w.a2[q] = w.a[q] * kLog2e;
+  }
+  if constexpr (S == 1) {
+#pragma unroll
+    for (int n = 0; n < kN / 2; ++n) {
+      const int na = (col & 8) + n;
+      w.ah[n] = na < N ? p.A[dc * p.Asd + na * p.Asn] : 0.0f;
+    }
   }
   // dB/dC: this workgroup's slots of the partial sums, or the group's rows
   // of dB/dC themselves (atomics)
