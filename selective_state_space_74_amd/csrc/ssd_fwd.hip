@@ -136,6 +136,19 @@ __device__ __forceinline__ typename Frag<T>::V ldsf(const typename Lds<T>::E* p)
   return *reinterpret_cast<const typename Frag<T>::V*>(p);
 }
 
+// bf16 operand fragment through the LDS transpose read (ds_read_b64_tr_b16).
+// Within each group of 16 lanes, lane i receives element k from the chunk
+// (four consecutive elements) that lane 4k + i / 4 of the group addresses,
+// its element i % 4 (lane layout checked on the device with an in-bounds
+// probe).  So when lane r of group g addresses row 4g + r / 4, columns
+// 4 (r % 4) .. + 3 of a row-major tile X[k][c], lane 16 g + i receives
+// X[4g + k][i] for k = 0..3: the operand fragment of column i (k = 4g + k')
+// of a 16x16x16 product, equally the A fragment of row i of X^T.
+__device__ __forceinline__ v4s lds_tr(const uint16_t* row_chunk) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (v4s __attribute__((address_space(3)))*)(row_chunk));
+}
+
 // Four LDS elements (already in the fragment's element type) as a fragment.
 template <typename T>
 __device__ __forceinline__ typename Frag<T>::V tofrag_bits(typename Lds<T>::E a, typename Lds<T>::E b,
@@ -213,12 +226,21 @@ void ssd_fwd_kernel(SsdParams p) {
   constexpr bool kBF = sizeof(E) == 2;
   __shared__ __align__(16) E sB[kQ][NP];       // B_s[n]
   __shared__ __align__(16) E sC[kQ][NP];       // C_t[n]
-  __shared__ __align__(16) E sXT[PC][QP];      // x_s[p], transposed
-  __shared__ __align__(16) E sXW[PC][QP];      // exp(a_{Q-1} - a_s) Delta_s x_s[p], transposed
-  __shared__ __align__(16) E sHT[PC][NP];      // H_in^T[p][n] (operand copy)
+  // fp32: x, the decay-weighted x and the state operand stored transposed
+  // (the fragments then read four consecutive k values); bf16: stored as
+  // they are, [channel block][token or state][16 channels] (32-byte rows),
+  // with 8-byte stores, and read through the transpose read (lds_tr)
+  constexpr int kFP = kBF ? 1 : PC;
+  __shared__ __align__(16) E sXT[kFP][kBF ? 1 : QP];      // x_s[p], transposed
+  __shared__ __align__(16) E sXW[kFP][kBF ? 1 : QP];      // exp(a_{Q-1} - a_s) Delta_s x_s[p], transposed
+  __shared__ __align__(16) E sHT[kFP][kBF ? 1 : NP];      // H_in^T[p][n] (operand copy)
+  constexpr int kBP = kBF ? PB : 1;
+  __shared__ __align__(16) E sXb[kBP][kBF ? kQ : 1][kPB];     // x_s[p]
+  __shared__ __align__(16) E sXWb[kBP][kBF ? kQ : 1][kPB];    // exp(a_{Q-1} - a_s) Delta_s x_s[p]
+  __shared__ __align__(16) E sHb[kBP][kBF ? NMAX : 1][kPB];   // H_in[n][p], bf16 value
   // bf16: the rounding remainder H - bf16(H), so that the state product
   // carries the fp32 state to about 16 bits (two bf16 products)
-  __shared__ __align__(16) E sHL[kBF ? PC : 1][kBF ? NP : 1];
+  __shared__ __align__(16) E sHL[kBP][kBF ? NMAX : 1][kPB];
   __shared__ __align__(16) float sDl[kQ];      // Delta_s (0 past the end)
   __shared__ __align__(16) float sLa[kQ];      // a_t * log2(e)
   // segmented passes (kept in LDS, not in registers across the chunk loop):
@@ -318,11 +340,22 @@ void ssd_fwd_kernel(SsdParams p) {
       if (m < NB) {
 #pragma unroll
         for (int q = 0; q < PB; ++q) {
+          if constexpr (kBF) {
+            // lane holds H[n = 16 m + lr][p = 16 q + 4 lq + i], i = 0..3:
+            // one 8-byte store of the four values and one of the remainders
+            E hi[4], lo[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const E hi = L::from(Hs[j][q][i]);
-            sHT[kPB * q + 4 * lq + i][16 * m + lr] = hi;
-            if constexpr (kBF) sHL[kPB * q + 4 * lq + i][16 * m + lr] = L::from(Hs[j][q][i] - L::f(hi));
+            for (int i = 0; i < 4; ++i) {
+              hi[i] = L::from(Hs[j][q][i]);
+              lo[i] = L::from(Hs[j][q][i] - L::f(hi[i]));
+            }
+            *reinterpret_cast<uint2*>(&sHb[q][16 * m + lr][4 * lq]) =
+                make_uint2(hi[0] | static_cast<uint32_t>(hi[1]) << 16, hi[2] | static_cast<uint32_t>(hi[3]) << 16);
+            *reinterpret_cast<uint2*>(&sHL[q][16 * m + lr][4 * lq]) =
+                make_uint2(lo[0] | static_cast<uint32_t>(lo[1]) << 16, lo[2] | static_cast<uint32_t>(lo[3]) << 16);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sHT[kPB * q + 4 * lq + i][16 * m + lr] = L::from(Hs[j][q][i]);
           }
         }
       }
@@ -487,15 +520,20 @@ void ssd_fwd_kernel(SsdParams p) {
       }
 #pragma unroll
       for (int q = 0; q < PB; ++q) {
+        E xv[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int pp = kPB * q + 4 * squart + k;
           uint32_t v;
           if constexpr (kVec) v = ES == 2 ? (st.x[q][k / 2] >> (16 * (k % 2))) : st.x[q][k % kXw];
           else v = st.x[q][k];
-          const E xv = raw(v, tv && p0 + pp < p.P);
-          sXT[pp][srow] = xv;
+          xv[k] = raw(v, tv && p0 + pp < p.P);
+          if constexpr (!kBF) sXT[pp][srow] = xv[k];
         }
+        // bf16: row s, channels 4 squart .. + 3 of block q, one 8-byte store
+        if constexpr (kBF)
+          *reinterpret_cast<uint2*>(&sXb[q][srow][4 * squart]) =
+              make_uint2(xv[0] | static_cast<uint32_t>(xv[1]) << 16, xv[2] | static_cast<uint32_t>(xv[3]) << 16);
       }
     }
     // ---- the chunk's step sizes: every wavefront runs the 64-token scan
@@ -527,6 +565,7 @@ void ssd_fwd_kernel(SsdParams p) {
       const bool tv = srow < nv;
 #pragma unroll
       for (int q = 0; q < PB; ++q) {
+        E xw[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int pp = kPB * q + 4 * squart + k;
@@ -534,8 +573,12 @@ void ssd_fwd_kernel(SsdParams p) {
           if constexpr (kVec) v = ES == 2 ? (st.x[q][k / 2] >> (16 * (k % 2))) : st.x[q][k % kXw];
           else v = st.x[q][k];
           const E xv = raw(v, tv && p0 + pp < p.P);
-          sXW[pp][srow] = L::from(L::f(xv) * w_row);
+          xw[k] = L::from(L::f(xv) * w_row);
+          if constexpr (!kBF) sXW[pp][srow] = xw[k];
         }
+        if constexpr (kBF)
+          *reinterpret_cast<uint2*>(&sXWb[q][srow][4 * squart]) =
+              make_uint2(xw[0] | static_cast<uint32_t>(xw[1]) << 16, xw[2] | static_cast<uint32_t>(xw[3]) << 16);
       }
     }
     __syncthreads();
@@ -576,7 +619,10 @@ void ssd_fwd_kernel(SsdParams p) {
         // every channel block
         const auto mf = tofrag<T>(m0, m1, m2, m3);
 #pragma unroll
-        for (int q = 0; q < PB; ++q) y1[q] = mma16<T>(mf, ldsf<T>(&sXT[kPB * q + lr][s0]), y1[q]);
+        for (int q = 0; q < PB; ++q) {
+          if constexpr (kBF) y1[q] = mma16<T>(mf, lds_tr(&sXb[q][s0 + lr / 4][4 * (lr % 4)]), y1[q]);
+          else y1[q] = mma16<T>(mf, ldsf<T>(&sXT[kPB * q + lr][s0]), y1[q]);
+        }
       }
       // state: A = C (row t, k = n), B operand = H_in (k = n, column p)
       v4f y2[PB];
@@ -587,8 +633,13 @@ void ssd_fwd_kernel(SsdParams p) {
         const auto cf = ldsf<T>(&sC[tb + lr][16 * nb + 4 * lq]);
 #pragma unroll
         for (int q = 0; q < PB; ++q) {
-          y2[q] = mma16<T>(cf, ldsf<T>(&sHT[kPB * q + lr][16 * nb + 4 * lq]), y2[q]);
-          if constexpr (kBF) y2[q] = mma16<T>(cf, ldsf<T>(&sHL[kPB * q + lr][16 * nb + 4 * lq]), y2[q]);
+          if constexpr (kBF) {
+            const int hr = 16 * nb + 4 * lq + lr / 4;
+            y2[q] = mma16<T>(cf, lds_tr(&sHb[q][hr][4 * (lr % 4)]), y2[q]);
+            y2[q] = mma16<T>(cf, lds_tr(&sHL[q][hr][4 * (lr % 4)]), y2[q]);
+          } else {
+            y2[q] = mma16<T>(cf, ldsf<T>(&sHT[kPB * q + lr][16 * nb + 4 * lq]), y2[q]);
+          }
         }
       }
       // lane holds t = tb + 4 lq + i, p = 16 q + lr; stores of tokens past
@@ -606,7 +657,9 @@ void ssd_fwd_kernel(SsdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tl = tb + 4 * lq + i;
-          const float xval = L::f(sXT[pl][tl]);
+          float xval;
+          if constexpr (kBF) xval = L::f(sXb[q][tl][lr]);
+          else xval = L::f(sXT[pl][tl]);
           float y = fmaf(ea[i], y2[q][i], y1[q][i]);
           y = fmaf(Dh, xval, y);
           const float gz = silu_f32(Elem<T>::f32(zr[q][i]));
@@ -632,9 +685,16 @@ void ssd_fwd_kernel(SsdParams p) {
           for (int sbk = 0; sbk < kQ / 16; ++sbk) {
             // A = (w x)^T (row p, k = s); B operand = B (k = s, column n)
             const int s0 = 16 * sbk + 4 * lq, n = 16 * m + lr;
-            const auto bf = tofrag_bits<T>(sB[s0][n], sB[s0 + 1][n], sB[s0 + 2][n], sB[s0 + 3][n]);
+            if constexpr (kBF) {
+              const auto bf = lds_tr(&sB[s0 + lr / 4][16 * m + 4 * (lr % 4)]);
 #pragma unroll
-            for (int q = 0; q < PB; ++q) acc[q] = mma16<T>(ldsf<T>(&sXW[kPB * q + lr][s0]), bf, acc[q]);
+              for (int q = 0; q < PB; ++q)
+                acc[q] = mma16<T>(lds_tr(&sXWb[q][s0 + lr / 4][4 * (lr % 4)]), bf, acc[q]);
+            } else {
+              const auto bf = tofrag_bits<T>(sB[s0][n], sB[s0 + 1][n], sB[s0 + 2][n], sB[s0 + 3][n]);
+#pragma unroll
+              for (int q = 0; q < PB; ++q) acc[q] = mma16<T>(ldsf<T>(&sXW[kPB * q + lr][s0]), bf, acc[q]);
+            }
           }
 #pragma unroll
           for (int q = 0; q < PB; ++q) Hs[j][q] = acc[q];
