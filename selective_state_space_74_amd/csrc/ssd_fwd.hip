@@ -149,6 +149,13 @@ __device__ __forceinline__ v4s lds_tr(const uint16_t* row_chunk) {
       (v4s __attribute__((address_space(3)))*)(row_chunk));
 }
 
+// Two fp32 values rounded to bf16 (nearest even) in one word, a low.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const bf2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Four LDS elements (already in the fragment's element type) as a fragment.
 template <typename T>
 __device__ __forceinline__ typename Frag<T>::V tofrag_bits(typename Lds<T>::E a, typename Lds<T>::E b,
@@ -496,6 +503,7 @@ void ssd_fwd_kernel(SsdParams p) {
     // ---- B, C and x^T of this chunk into LDS, before the step-size scan so
     // that the stores are under way while it runs (the barrier closing the
     // previous chunk freed these buffers) ----
+    uint2 xm[PB];   // bf16 vector staging: the masked words of x, for the weighted copy
     {
       const bool tv = srow < nv;
       if constexpr (kVec) {
@@ -520,6 +528,16 @@ void ssd_fwd_kernel(SsdParams p) {
       }
 #pragma unroll
       for (int q = 0; q < PB; ++q) {
+        if constexpr (kBF && kVec) {
+          // the thread's four channels as loaded (two words), each half
+          // kept where its row and channel are real: one 8-byte store
+          const int vc = p.P - p0 - (kPB * q + 4 * squart);  // real channels from the first
+          const uint32_t m0 = !tv ? 0u : vc >= 2 ? 0xffffffffu : vc == 1 ? 0xffffu : 0u;
+          const uint32_t m1 = !tv ? 0u : vc >= 4 ? 0xffffffffu : vc == 3 ? 0xffffu : 0u;
+          xm[q] = make_uint2(st.x[q][0] & m0, st.x[q][1] & m1);
+          *reinterpret_cast<uint2*>(&sXb[q][srow][4 * squart]) = xm[q];
+          continue;
+        }
         E xv[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -565,6 +583,13 @@ void ssd_fwd_kernel(SsdParams p) {
       const bool tv = srow < nv;
 #pragma unroll
       for (int q = 0; q < PB; ++q) {
+        if constexpr (kBF && kVec) {
+          const uint2 v = xm[q];
+          *reinterpret_cast<uint2*>(&sXWb[q][srow][4 * squart]) = make_uint2(
+              pack_bf16x2(__uint_as_float(v.x << 16) * w_row, __uint_as_float(v.x & 0xffff0000u) * w_row),
+              pack_bf16x2(__uint_as_float(v.y << 16) * w_row, __uint_as_float(v.y & 0xffff0000u) * w_row));
+          continue;
+        }
         E xw[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -654,11 +679,14 @@ void ssd_fwd_kernel(SsdParams p) {
 #pragma unroll
       for (int q = 0; q < PB; ++q) {
         const int pl = kPB * q + lr;
+        // bf16: x at this lane's four tokens, one transpose read
+        v4s xq = {0, 0, 0, 0};
+        if constexpr (kBF) xq = lds_tr(&sXb[q][tb + 4 * lq + lr / 4][4 * (lr % 4)]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int tl = tb + 4 * lq + i;
           float xval;
-          if constexpr (kBF) xval = L::f(sXb[q][tl][lr]);
+          if constexpr (kBF) xval = L::f(static_cast<uint16_t>(xq[i]));
           else xval = L::f(sXT[pl][tl]);
           float y = fmaf(ea[i], y2[q][i], y1[q][i]);
           y = fmaf(Dh, xval, y);
