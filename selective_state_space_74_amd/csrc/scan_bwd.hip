@@ -831,6 +831,18 @@ __global__ __launch_bounds__(kThreads) void bwd_aggregate_kernel(BwdParams p) {
   double ssum = 0.0;
   In cur = load(kend - 1);
   for (int k = kend - 1; k >= kbeg; --k) {
+    if ((k + 1) % kGB == 0 && k + 1 > kbeg && k + 1 < kend) {
+      // tile (k + 1) / kGB - 1 (blocks k - 1, k) into the other buffer, at
+      // the top of block k, the first of them: that buffer held tile
+      // (k + 1) / kGB + 1, which every wavefront finished before the barrier
+      // that followed the previous staging.  (Staged here rather than after
+      // block k + 1, so that the block's token loop and the broadcasts that
+      // feed it stay in one basic block and the broadcasts fold into their
+      // multiplies.)
+      stage((k + 1) / kGB - 1, tile);
+      load_tile((k + 1) / kGB - 2, tile);
+      __syncthreads();
+    }
     const In next = load(k - 1);
     const int t0 = k * kT;
     const int buf = (k / kGB) & 1;
@@ -853,19 +865,19 @@ __global__ __launch_bounds__(kThreads) void bwd_aggregate_kernel(BwdParams p) {
         const float4 y = *reinterpret_cast<const float4*>(&sC[buf][col + kN * q][tb + 4 * i]);
         cv[4 * i] = y.x; cv[4 * i + 1] = y.y; cv[4 * i + 2] = y.z; cv[4 * i + 3] = y.w;
       }
+      // the adjoint of h_t carried from token to token (the backward's
+      // form): adj_t = exp(Delta_{t+1} A) adj_{t+1} + dy_t C_t, and what
+      // leaves the block is exp(Delta_0 A) adj_0; each broadcast folds into
+      // a two-operand multiply
+      float adj = 0.0f, enext = 1.0f;
       static_for<0, kT>([&](auto J) {
         constexpr int j = kT - 1 - decltype(J)::value;
-        const float adj = fmaf(row_bcast<j>(dy), cv[j], g[q]);
-        g[q] = __builtin_amdgcn_exp2f(row_bcast<j>(dl) * a2[q]) * adj;
+        const float dyc = row_bcast<j>(dy) * cv[j];
+        adj = j == kT - 1 ? g[q] + dyc : fmaf(enext, adj, dyc);
+        enext = __builtin_amdgcn_exp2f(row_bcast<j>(dl) * a2[q]);
       });
+      g[q] = enext * adj;
     });
-    if (k % kGB == 0 && k > kbeg) {
-      // the other buffer held tile k / kGB + 1, which every wavefront
-      // finished before the barrier that followed the previous staging
-      stage(k / kGB - 1, tile);
-      load_tile(k / kGB - 2, tile);
-      __syncthreads();
-    }
     cur = next;
   }
 #pragma unroll
