@@ -146,13 +146,15 @@ template <int S>
 constexpr int kXPitch = S == 1 ? kPitch : 2 * kT + 4;
 template <int S>
 constexpr int kXRow = kN * kXPitch<S> + 16;   // floats per channel
-// Buffers of the dB/dC exchange (sQ): two, one per half block in turn, so
-// that one barrier per half orders both its writes before the sums and the
-// previous half's sums before the writes; one (and a second barrier per
-// half) with four slots, whose LDS would otherwise leave a single workgroup
-// per CU.
+// Buffers of the dB/dC exchange (sQ).  One slot: four, a pair per block in
+// turn (half h8 of block k in buffer 2 (k % 2) + h8), so that one barrier
+// per block orders both halves' writes before their sums, and the previous
+// pair's sums before the next writes into it (one block later, past the
+// next block's barrier).  Two slots: two, one per half in turn, one barrier
+// per half.  Four slots: one, and a second barrier per half (more LDS would
+// leave a single workgroup per CU).
 template <int S>
-constexpr int kQBuf = S == 4 ? 1 : 2;
+constexpr int kQBuf = S == 1 ? 4 : S == 2 ? 2 : 1;
 
 template <typename T, bool kSoftplus, int S>
 struct BwdWave {
@@ -177,7 +179,7 @@ struct BwdWave {
                               // per-state du/ddelta terms
   float (*sQ)[kWaves][kRows][kN][4];  // [kQBuf][kWaves][kRows][kN][4], shared: dB/dC terms
                               // of half a block (one slot) summed over each wavefront's
-                              // channels, half h8 in buffer h8 % kQBuf; row r holds
+                              // channels (buffers: kQBuf); row r holds
                               // tensor r / 2 (dB, dC), tokens 4 (r % 2) + 0..3
 
   static constexpr int E = Elem<T>::kSize;
@@ -250,14 +252,14 @@ struct BwdWave {
   // offsets would otherwise reach into later states' rows, and a plain store
   // there (the partial sums) races with the real value when the sequence is
   // shorter than a block.
-  __device__ __forceinline__ void dbdc_sum(int k, int h8, int q) const {
+  __device__ __forceinline__ void dbdc_sum(int k, int h8, int q, int qb) const {
     const int tid = threadIdx.x;
     // the tensor (dB, dC) is one per wavefront pair: made visibly uniform so
     // that the buffer descriptor is selected in scalar registers
     const int ten = __builtin_amdgcn_readfirstlane(tid >> 7);
     const int n = (tid >> 3) & 15, t = tid & 7;
     const int qr = 2 * ten + (t >> 2), qt = t & 3;
-    const auto& sq = sQ[h8 % kQBuf<S>];
+    const auto& sq = sQ[qb];
     float sum = sq[0][qr][n][qt];
 #pragma unroll
     for (int v = 1; v < kWaves; ++v) sum += sq[v][qr][n][qt];
@@ -374,9 +376,11 @@ struct BwdWave {
             make_float4(s2[0], s2[1], s2[2], s2[3]);
       }
       if constexpr (jj == 0) {
-        *reinterpret_cast<float4*>(&sQ[h8 % kQBuf<S>][wave][row][col][0]) =
+        const int qb = 2 * (k & 1);   // this block's pair of exchange buffers
+        *reinterpret_cast<float4*>(&sQ[qb + h8][wave][row][col][0]) =
             make_float4(rq[0], rq[1], rq[2], rq[3]);
-        __syncthreads();
+        // one barrier per block, after both halves' stores
+        if constexpr (h8 == 0) __syncthreads();
         // owners of tokens 8 h8 .. 8 h8 + 7: du, ddelta.  The sums over the
         // 16 states for token ti: lanes col and col ^ 8 each add 8 states'
         // terms and then exchange, so both hold the sum (the owner is the
@@ -404,12 +408,14 @@ struct BwdWave {
           // the store is dropped
           Elem<T>::store(wdz.at(gate ? skip(k) : 0u), odz, dzv);
         }
-        // dB, dC: summed over the workgroup's channels; the next half
-        // writes the other buffer, and the one after it this one again only
-        // past the next half's barrier, which every thread reaches after
-        // these reads
-        dbdc_sum(k, h8, 0);
-        if constexpr (kQBuf<S> == 1) __syncthreads();
+        // dB, dC of both halves: summed over the workgroup's channels; the
+        // next block writes the other pair, and the block after it this pair
+        // again only past the next block's barrier, which every thread
+        // reaches after these reads
+        if constexpr (h8 == 0) {
+          dbdc_sum(k, 1, 0, qb + 1);
+          dbdc_sum(k, 0, 0, qb);
+        }
       }
     });
   }
@@ -533,7 +539,7 @@ struct BwdWave {
           *reinterpret_cast<float4*>(&sQ[h8 % kQBuf<S>][wave][row][col][0]) =
               make_float4(rq[0], rq[1], rq[2], rq[3]);
           __syncthreads();
-          dbdc_sum(k, h8, q);
+          dbdc_sum(k, h8, q, h8 % kQBuf<S>);
           if constexpr (kQBuf<S> == 1) __syncthreads();
         }
       });
