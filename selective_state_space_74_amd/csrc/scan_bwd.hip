@@ -709,14 +709,25 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
   Raw cur = w.load(kend - 1);
   for (int k = kend - 1; k >= kbeg; --k) {
     const Raw next = w.load(k - 1);
-    if constexpr (S == 1) w.block(k, cur, g, dA, dDs, dbs);
-    else w.block_slots(k, cur, g, dA, dDs, dbs);
-    if (k % kGB == 0 && k > kbeg) {
-      // tile (k / kGB) - 1 into the other buffer; every wavefront finished
-      // reading it before the barrier at the end of the previous block
-      w.stage(k / kGB - 1, tile);
-      tile = w.load_tile(k / kGB - 2);
-      __syncthreads();
+    if constexpr (S == 1) {
+      // one slot: tile (k / kGB) - 1 goes into the other buffer at the top
+      // of block k (every wavefront finished reading that buffer, tile
+      // k / kGB + 1, before the barrier at the end of block k + 1), and the
+      // barrier at the end of block k publishes it to block k - 1
+      if (k % kGB == 0 && k > kbeg) {
+        w.stage(k / kGB - 1, tile);
+        tile = w.load_tile(k / kGB - 2);
+      }
+      w.block(k, cur, g, dA, dDs, dbs);
+    } else {
+      w.block_slots(k, cur, g, dA, dDs, dbs);
+      if (k % kGB == 0 && k > kbeg) {
+        // tile (k / kGB) - 1 into the other buffer; every wavefront finished
+        // reading it before the barrier at the end of the previous block
+        w.stage(k / kGB - 1, tile);
+        tile = w.load_tile(k / kGB - 2);
+        __syncthreads();
+      }
     }
     cur = next;
   }
