@@ -210,8 +210,11 @@ struct Wave {
   static constexpr bool kSegm = M != Mode::kScan;
   static constexpr bool kFixp = M == Mode::kFix;
   // token of the scan after which the owner's C column is read, so that the
-  // read is in flight during the rest of the scan
-  static constexpr int kCRead = 7;
+  // read is in flight during the rest of the scan: at the top of the block
+  // in the compact one-segment form (its 84 registers still leave five
+  // wavefronts per SIMD), after token 7 where registers are tight (the
+  // segmented passes at 96) or the read is carried over (deferred form)
+  static constexpr int kCRead = (M == Mode::kScan && !kDefer) ? 0 : 7;
   // Owner-C readout deferred to the top of the next block (kDefer): the
   // block's states are read back from LDS there and contracted after the
   // next block's owner work, which covers the LDS round trip; the C column
