@@ -813,18 +813,32 @@ struct SsdPlan {
   int nseg, seg_chunks;
 };
 
-SsdPlan ssd_plan(const ssm_ssd_args& a) {
+// segments: whether the sequence may be cut (a workspace will hold the
+// segments' end states).  A cut sequence fills the machine with segments,
+// so it takes two channel blocks per workgroup where the head has them
+// (the chunk's staging, step scan and score tiles shared by both): on
+// batch 1, L 1M, 32 heads of 64, 11.05 ms with one block per workgroup in
+// 16 segments against 9.18 ms with two in 32 (same-box A/B).
+SsdPlan ssd_plan(const ssm_ssd_args& a, bool segments = true) {
   const bool bf = a.io_dtype == SSM_BF16;
   const int nmax = (bf && a.dstate > 64) ? 128 : 64;
-  SsdPlan q;
-  q.pbk = choose_pb(static_cast<int>(a.headdim), nmax, bf, a.batch * a.nheads);
-  q.pblocks = static_cast<int>((a.headdim + kPB * q.pbk - 1) / (kPB * q.pbk));
-  const int64_t groups = a.batch * a.nheads * q.pblocks;
   const int64_t nchunks = (a.seqlen + kQ - 1) / kQ;
+  SsdPlan q;
   int64_t g = 1;
-  if (groups > 0 && groups < kSsdTargetGroups / 2)
-    g = std::max<int64_t>(1, std::min<int64_t>({kSsdTargetGroups / groups, a.seqlen / kSsdMinSegLen,
-                                                int64_t{kSsdMaxSeg}}));
+  auto plan_with = [&](int pbk) {
+    q.pbk = pbk;
+    q.pblocks = static_cast<int>((a.headdim + kPB * q.pbk - 1) / (kPB * q.pbk));
+    const int64_t groups = a.batch * a.nheads * q.pblocks;
+    g = 1;
+    if (segments && groups > 0 && groups < kSsdTargetGroups / 2)
+      g = std::max<int64_t>(1, std::min<int64_t>({kSsdTargetGroups / groups, a.seqlen / kSsdMinSegLen,
+                                                  int64_t{kSsdMaxSeg}}));
+  };
+  plan_with(choose_pb(static_cast<int>(a.headdim), nmax, bf, a.batch * a.nheads));
+#ifndef SSD_PB_FORCE
+  const int full = static_cast<int>((a.headdim + kPB - 1) / kPB);
+  if (g > 1 && q.pbk < 2 && full >= 2) plan_with(2);
+#endif
   q.seg_chunks = static_cast<int>(std::max<int64_t>(1, (nchunks + g - 1) / g));
   q.nseg = static_cast<int>(std::max<int64_t>(1, (nchunks + q.seg_chunks - 1) / q.seg_chunks));
   return q;
@@ -890,12 +904,13 @@ hipError_t launch_ssd_fwd(const ssm_ssd_args& a, hipStream_t stream) {
   const bool sp = a.dt_softplus != 0;
   const bool bf = a.io_dtype == SSM_BF16;
   const int nmax = (bf && a.dstate > 64) ? 128 : 64;
-  const SsdPlan q = ssd_plan(a);
-  const int pbk = q.pbk;
-  p.pblocks = q.pblocks;
-  // segments only with a workspace that holds their end states
+  // segments only with a workspace that holds their end states; without
+  // one, the plan of a single segment
   const size_t need = ssd_workspace_bytes(a);
   const bool segd = need > 0 && a.workspace && a.workspace_bytes >= need;
+  const SsdPlan q = ssd_plan(a, segd);
+  const int pbk = q.pbk;
+  p.pblocks = q.pblocks;
   p.nseg = segd ? q.nseg : 1;
   p.seg_chunks = segd ? q.seg_chunks : static_cast<int>((a.seqlen + kQ - 1) / kQ);
   p.mode = segd ? 1 : 0;
