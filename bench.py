@@ -561,6 +561,35 @@ def valu_ceiling(torch, lanes=2048 * 256, blocks=4096, reps=10):
                                     "Delta*u, D*u, gate and input operations; 8 waves per SIMD"}
 
 
+def mfma_rate(torch, k, lanes=2048 * 256, iters=4096, reps=10):
+    """Dense bf16 matrix throughput of v_mfma_f32_16x16x{k}_bf16 (k 16 or
+    32) from a register-only kernel (libssm_micro.so; eight independent
+    accumulator chains per wavefront, 8 wavefronts per SIMD), median of
+    `reps` timed launches after a >= 200 ms warm-up."""
+    import ctypes
+    path = os.path.join(ROOT, "selective_state_space_74_amd", "libssm_micro.so")
+    lib = ctypes.CDLL(path)
+    lib.ssm_micro_mfma_rate.restype = ctypes.c_int
+    lib.ssm_micro_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_void_p]
+    out = torch.empty(lanes, device="cuda")
+
+    def step(i):
+        st = lib.ssm_micro_mfma_rate(ctypes.c_void_p(out.data_ptr()), lanes, iters, k,
+                                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"ssm_micro_mfma_rate: hip error {st}")
+
+    warm(step, 3, torch)
+    ms, _, _ = timed_launches(step, reps, torch)
+    instrs = lanes // 64 * iters * 8
+    flops = instrs * 2 * 16 * 16 * k
+    del out
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return {"k": k, "kernel_ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "instr_per_clk_per_cu_at_2p4ghz": round(instrs / (ms * 1e-3) / 2.4e9 / cus, 3)}
+
+
 def stream_copy(torch, reps=10):
     """Measured streaming bandwidth of the device: a plain 1 GiB -> 1 GiB
     device copy, timed with HIP events (the practical ceiling that a
@@ -674,6 +703,9 @@ def main():
     ap.add_argument("--profile-ssd", action="store_true",
                     help="only the Mamba-2 SSD layer (10 launches) and the long-context SSD "
                          "layer (3 segmented launches); for rocprofv3")
+    ap.add_argument("--micro-mfma", action="store_true",
+                    help="only the bf16 matrix-instruction rate micro-benchmark (k = 16 and k = 32); "
+                         "prints one JSON line")
     ap.add_argument("--profile-bwd", action="store_true",
                     help="only the scan backward of the 130m-like and the 2.8b-like layer "
                          "(10 launches each); for rocprofv3")
@@ -740,6 +772,9 @@ def main():
                              dt_bias=t["dt_bias"], out=out)
         torch.cuda.synchronize()
         log(f"[profile] 10 launches of the SSD layer {cs.name}, 3 of {cl.name} (segmented)")
+        return
+    if args.micro_mfma:
+        print(json.dumps({"mfma_bf16_16x16": [mfma_rate(torch, k) for k in (16, 32)]}), flush=True)
         return
     if args.profile_bwd:
         for cb in (layer, si.LAYER_2P8B):

@@ -13,9 +13,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libssm.so")
-# The arithmetic-ceiling micro-benchmark that bench.py times (not part of the
-# libssm.so boundary).
-MICRO_SRC = os.path.join(PKG, "micro", "valu_mix.hip")
+# The micro-benchmarks that bench.py times (the scan's arithmetic ceiling, the
+# matrix instructions' issue rate; not part of the libssm.so boundary).
+MICRO_SRCS = sorted(glob.glob(os.path.join(PKG, "micro", "*.hip")))
 MICRO_LIB = os.path.join(PKG, "libssm_micro.so")
 ARCH = "gfx950"
 
@@ -61,7 +61,7 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False) -> str:
     """Compile every csrc/*.hip into libssm.so (always recompiles), and the
-    micro-benchmark into libssm_micro.so.  The library sources compile in
+    micro-benchmarks into libssm_micro.so.  The library sources compile in
     parallel into a temporary directory, then link."""
     tmp = LIB + ".tmp"
     jobs = max(1, min(len(sources()), os.cpu_count() or 1, 16))
@@ -72,7 +72,7 @@ def build(verbose: bool = False) -> str:
                         zip(sources(), objs)))
         _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs], verbose)
         mtmp = MICRO_LIB + ".tmp"
-        _run([hipcc(), *flags_for(MICRO_SRC), "-shared", "-o", mtmp, MICRO_SRC], verbose)
+        _run([hipcc(), *HIPCC_FLAGS, "-shared", "-o", mtmp, *MICRO_SRCS], verbose)
     os.replace(tmp, LIB)
     os.replace(mtmp, MICRO_LIB)
     return LIB
