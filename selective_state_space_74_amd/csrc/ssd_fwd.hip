@@ -69,6 +69,8 @@ constexpr int kThreads = 64 * kWaves;
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 
@@ -128,6 +130,23 @@ __device__ __forceinline__ v4f mma16(typename Frag<T>::V a, typename Frag<T>::V 
     for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
     return c;
   }
+}
+
+// bf16, k = 32 (v_mfma_f32_16x16x32_bf16, twice the work of the k = 16 form
+// at the same issue rate on gfx950).  The instruction sums over its 32 k
+// slots, pairing slot v of A's lane 16 g + i with slot v of B's lane
+// 16 g + j, so any placement of the k values into (lane group, slot) that A
+// and B share gives the same sum: two k = 16 fragments side by side (slots
+// 0-3 and 4-7) give the sum of their two k = 16 products, and eight
+// consecutive k values per lane (slots 0-7 of lane group g holding k = 8 g
+// .. 8 g + 7) one 32-wide k block.
+__device__ __forceinline__ v4f mma32(v8s a, v8s b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b),
+                                                 c, 0, 0, 0);
+}
+__device__ __forceinline__ v4f mma32(v4s a0, v4s a1, v4s b0, v4s b1, v4f c) {
+  return mma32(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
+               __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), c);
 }
 
 // Four consecutive LDS elements (8 or 16 bytes, aligned) as a fragment.
@@ -627,10 +646,17 @@ void ssd_fwd_kernel(SsdParams p) {
         // scores G[s][t] for s in block sbk, t in block wave: A = B (row s,
         // k = n), B operand = C^T (k = n, column t)
         v4f sc = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (kBF) {   // 32-wide n blocks, eight consecutive n per lane
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          sc = mma16<T>(ldsf<T>(&sB[16 * sbk + lr][16 * nb + 4 * lq]),
-                        ldsf<T>(&sC[tb + lr][16 * nb + 4 * lq]), sc);
+          for (int nb = 0; nb < NB / 2; ++nb)
+            sc = mma32(*reinterpret_cast<const v8s*>(&sB[16 * sbk + lr][32 * nb + 8 * lq]),
+                       *reinterpret_cast<const v8s*>(&sC[tb + lr][32 * nb + 8 * lq]), sc);
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            sc = mma16<T>(ldsf<T>(&sB[16 * sbk + lr][16 * nb + 4 * lq]),
+                          ldsf<T>(&sC[tb + lr][16 * nb + 4 * lq]), sc);
+        }
         // mask and scale: lane holds s = 16 sbk + 4 lq + i, t = tb + lr
         const int s0 = 16 * sbk + 4 * lq;
         const float4 la_s = *reinterpret_cast<const float4*>(&sLa[s0]);
@@ -659,9 +685,8 @@ void ssd_fwd_kernel(SsdParams p) {
 #pragma unroll
         for (int q = 0; q < PB; ++q) {
           if constexpr (kBF) {
-            const int hr = 16 * nb + 4 * lq + lr / 4;
-            y2[q] = mma16<T>(cf, lds_tr(&sHb[q][hr][4 * (lr % 4)]), y2[q]);
-            y2[q] = mma16<T>(cf, lds_tr(&sHL[q][hr][4 * (lr % 4)]), y2[q]);
+            const int hr = 16 * nb + 4 * lq + lr / 4;   // C (H + H_lo) in one k = 32 product
+            y2[q] = mma32(cf, cf, lds_tr(&sHb[q][hr][4 * (lr % 4)]), lds_tr(&sHL[q][hr][4 * (lr % 4)]), y2[q]);
           } else {
             y2[q] = mma16<T>(cf, ldsf<T>(&sHT[kPB * q + lr][16 * nb + 4 * lq]), y2[q]);
           }
@@ -713,11 +738,16 @@ void ssd_fwd_kernel(SsdParams p) {
           for (int sbk = 0; sbk < kQ / 16; ++sbk) {
             // A = (w x)^T (row p, k = s); B operand = B (k = s, column n)
             const int s0 = 16 * sbk + 4 * lq, n = 16 * m + lr;
-            if constexpr (kBF) {
-              const auto bf = lds_tr(&sB[s0 + lr / 4][16 * m + 4 * (lr % 4)]);
+            if constexpr (kBF) {   // two 16-token blocks per k = 32 product
+              if (sbk % 2 == 0) {
+                const int s1 = s0 + 16;
+                const auto bf0 = lds_tr(&sB[s0 + lr / 4][16 * m + 4 * (lr % 4)]);
+                const auto bf1 = lds_tr(&sB[s1 + lr / 4][16 * m + 4 * (lr % 4)]);
 #pragma unroll
-              for (int q = 0; q < PB; ++q)
-                acc[q] = mma16<T>(lds_tr(&sXWb[q][s0 + lr / 4][4 * (lr % 4)]), bf, acc[q]);
+                for (int q = 0; q < PB; ++q)
+                  acc[q] = mma32(lds_tr(&sXWb[q][s0 + lr / 4][4 * (lr % 4)]),
+                                 lds_tr(&sXWb[q][s1 + lr / 4][4 * (lr % 4)]), bf0, bf1, acc[q]);
+              }
             } else {
               const auto bf = tofrag_bits<T>(sB[s0][n], sB[s0 + 1][n], sB[s0 + 2][n], sB[s0 + 3][n]);
 #pragma unroll
