@@ -34,9 +34,12 @@
 // 16x16x16 product (lane l supplies row l%16, k = 4(l/16)+i), so the scores
 // never leave registers.  B, C and x of a chunk are staged in LDS by the
 // whole workgroup; the state goes through LDS once per chunk for the state
-// product.  bf16 IO uses v_mfma_f32_16x16x16_bf16 (fp32 accumulation; the
-// masked scores and the decay-weighted x are rounded to bf16, and the state
-// operand is split into a bf16 value and its bf16 remainder);
+// product.  bf16 IO uses v_mfma_f32_16x16x32_bf16 where two 16-wide k blocks
+// pair up (the scores, the state product, the state update) and
+// v_mfma_f32_16x16x16_bf16 for the causal intra-chunk product (fp32
+// accumulation; the masked scores and the decay-weighted x are rounded to
+// bf16, and the state operand is split into a bf16 value and its bf16
+// remainder);
 // fp32 IO uses v_mfma_f32_16x16x4_f32 four times per 16-wide k block, each
 // lane supplying the same four consecutive k values one per instruction.
 //
