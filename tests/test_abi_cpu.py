@@ -601,12 +601,13 @@ def ssd_workspace(batch, H, P, N, nseg):
 def test_ssd_workspace_size():
     """Long sequences whose (batch, head, 16-channel block) workgroups are
     few are cut into segments of whole 64-token chunks: up to about 2,048
-    workgroups, each segment at least 32,768 tokens, at most 64 segments.
-    Batch 1 with 32 heads of 64 channels (128 workgroups) at 1M tokens: 16
-    segments.  The benchmarked layer (batch 8, L 2048) and short sequences:
+    workgroups, each segment at least 32,768 tokens, at most 64 segments;
+    a cut sequence takes two 16-channel blocks per workgroup where the head
+    has them.  Batch 1 with 32 heads of 64 channels (64 workgroups of two
+    blocks) at 1M tokens: 32 segments.  The benchmarked layer (batch 8, L 2048) and short sequences:
     none."""
     assert ssm.ssd_workspace_size(good_ssd(1, 1 << 20, 32, 64, 1, 64, io=1)) == \
-        ssd_workspace(1, 32, 64, 64, 16)
+        ssd_workspace(1, 32, 64, 64, 32)
     assert ssm.ssd_workspace_size(good_ssd(1, 3 * 32768 + 100, 2, 64, 1, 64)) == \
         ssd_workspace(1, 2, 64, 64, 3)
     assert ssm.ssd_workspace_size(good_ssd(1, 1 << 22, 1, 16, 1, 16)) == ssd_workspace(1, 1, 16, 16, 64)
