@@ -708,7 +708,7 @@ def main():
                          "prints one JSON line")
     ap.add_argument("--profile-bwd", action="store_true",
                     help="only the scan backward of the 130m-like and the 2.8b-like layer "
-                         "(10 launches each); for rocprofv3")
+                         "(10 launches each), then the calibration copy; for rocprofv3")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -788,7 +788,11 @@ def main():
                 ssm.selective_scan_bwd(dout, t["u"], t["delta"], t["A"], t["B"], t["C"], ck, **kw)
             torch.cuda.synchronize()
             del t, ck, dout
-            log(f"[profile] 10 launches of the scan backward on {cb.name}")
+            log(f"[profile] 10 launches of the scan backward on {cb.name} "
+                f"({scan_bwd_bytes(cb.batch, cb.dim, cb.seqlen, cb.dstate, 4 if cb.io_dtype == 'f32' else 2)}"
+                f" algorithmic bytes each)")
+        calibration_copy(torch, 10)
+        log("[profile] 10 copy launches (1 GiB read + 1 GiB write)")
         return
     log(f"[bench] headline {head.name}: warmup {args.warmup} (+ >= {WARM_MS:.0f} ms), "
         f"steps {args.steps}")
